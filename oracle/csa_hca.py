@@ -1,0 +1,218 @@
+"""Plain fp64 definition of the CSA / HCA attention step over a compressed KV cache.
+
+TEST INFRASTRUCTURE ONLY (see the package docstring).  Slow and literal on
+purpose: each function is the definition written out with numpy, no blocking,
+fusion or reordering beyond it.
+
+Page: "DeepSeek-V4: Towards Highly Efficient Million-Token Context Intelligence
+Review" (dimensionstp.github.io), abbreviated PAGE below.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+# --------------------------------------------------------------------------------------
+# bf16 storage <-> fp64 values
+
+
+def bf16_bits_to_f64(bits) -> np.ndarray:
+    """Exact value of bf16 bit patterns: a bf16 is the upper 16 bits of a float32."""
+    b = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
+    with np.errstate(invalid="ignore"):   # signalling-NaN patterns stay NaN
+        return b.view(np.float32).astype(np.float64)
+
+
+_BF16_MAX = float.fromhex("0x1.fep127")  # (2 - 2^-7) * 2^127
+
+
+def f64_to_bf16_bits(x) -> np.ndarray:
+    """Round fp64 values to bf16 (one rounding, to nearest, ties to even).
+
+    bf16 keeps 8 significant bits; below its smallest normal 2^-126 the spacing
+    is fixed at 2^-133.  The value is scaled by a power of two so that one bf16
+    spacing becomes 1, rounded with numpy's rint (ties to even) and scaled back;
+    values past the largest finite bf16 after rounding become infinities.
+    NaN maps to the quiet NaN 0x7FC0."""
+    x = np.asarray(x, dtype=np.float64)
+    _, e = np.frexp(x)                      # x = f * 2^e with 0.5 <= |f| < 1
+    shift = np.maximum(e.astype(np.int64) - 8, -133)
+    y = np.ldexp(np.rint(np.ldexp(x, -shift)), shift)
+    y = np.where(np.abs(y) > _BF16_MAX, np.copysign(np.inf, x), y)
+    bits = (y.astype(np.float32).view(np.uint32) >> np.uint32(16)).astype(np.uint16)
+    return np.where(np.isnan(x), np.uint16(0x7FC0), bits).astype(np.uint16)
+
+
+def to_bf16_values(x) -> np.ndarray:
+    """fp64 values after a round trip through bf16 storage."""
+    return bf16_bits_to_f64(f64_to_bf16_bits(x))
+
+
+# --------------------------------------------------------------------------------------
+# compression
+
+
+def kv_compress(x, c: int) -> np.ndarray:
+    """Sequence-direction compression: one entry per complete block of c tokens.
+
+    PAGE section 2-1 and section 3-2 item 2 (component table): CSA turns every 4
+    tokens into one compressed entry, HCA every 128 tokens; both models use the
+    ratios 4 and 128.  The page does not give the pooling operator; the workload
+    fixes the mean.  Entry j is the mean of tokens j*c .. j*c+c-1.  A tail of
+    T mod c tokens forms no entry: the page keeps tokens that are not yet ready
+    for compression in a separate state cache (section 3-2 item 4).
+
+    x: [T, D] values; returns [T // c, D] fp64 means (not yet rounded to bf16)."""
+    x = np.asarray(x, dtype=np.float64)
+    t, d = x.shape
+    n = t // c
+    return x[: n * c].reshape(n, c, d).mean(axis=1)
+
+
+def compress_to_cache(x, c: int) -> np.ndarray:
+    """Compressed entries as stored in the bf16 cache (bit patterns)."""
+    return f64_to_bf16_bits(kv_compress(x, c))
+
+
+# --------------------------------------------------------------------------------------
+# CSA selection
+
+
+def n_visible(pos: int, c: int, n_entries: int) -> int:
+    """Number of compressed entries a query at absolute position `pos` may see.
+
+    The workload states that a query sees only compressed blocks that end
+    before its position.  Block j spans tokens j*c .. j*c+c-1, so it ends
+    before `pos` iff j*c + c - 1 < pos, i.e. (j+1)*c <= pos; visible entries are
+    therefore 0 .. floor(pos/c)-1, capped by the entries the cache holds.  A
+    decoding query sits at position L after L context tokens and sees all
+    floor(L/c) entries."""
+    return int(min(pos // c, n_entries))
+
+
+def index_scores(q_idx, k_idx) -> np.ndarray:
+    """Indexer scores s_j = sum_d q[d] * k[j, d] in exact integer arithmetic.
+
+    PAGE section 3-2 item 4: CSA has an indexer whose Q.K path picks the
+    entries to attend (trained there with FP4 quantisation-aware training).
+    The workload fixes the form: int8 query and keys of width d_idx, dot
+    product accumulated exactly (int32 cannot overflow: |s| <= d * 127^2)."""
+    q = np.asarray(q_idx, dtype=np.int64)
+    k = np.asarray(k_idx, dtype=np.int64)
+    return k @ q
+
+
+def topk_select(scores, n_vis: int, k: int) -> np.ndarray:
+    """Indices of the top-k visible entries, returned in ascending index order.
+
+    PAGE section 3-2 item 2 (component table): CSA keeps a sparse top-k of the
+    compressed entries.  Entries are ranked by score, high first; among equal
+    scores the lower index ranks first (the workload's tie rule).  With k >=
+    n_vis every visible entry is kept."""
+    s = np.asarray(scores, dtype=np.int64)[:n_vis]
+    order = np.lexsort((np.arange(n_vis), -s))   # last key is the primary key
+    return np.sort(order[: min(k, n_vis)])
+
+
+# --------------------------------------------------------------------------------------
+# attention
+
+
+def attention(q, K, V, scale: float):
+    """Softmax attention of H query heads over n entries (one shared KV head).
+
+    PAGE sections 2-1 and 3-2 item 2: CSA runs sparse attention over the
+    selected compressed entries, HCA dense attention over all of them; both are
+    ordinary softmax attention over compressed K/V.  logits = scale * q K^T,
+    p = softmax(logits) per head, o = p V, lse = log sum exp(logits).
+
+    q: [H, D]; K, V: [n, D].  Returns (o [H, D], lse [H], p [H, n]).  With n = 0
+    the output is 0 and lse is -inf."""
+    q = np.asarray(q, dtype=np.float64)
+    K = np.asarray(K, dtype=np.float64)
+    V = np.asarray(V, dtype=np.float64)
+    h, d = q.shape
+    n = K.shape[0]
+    if n == 0:
+        return np.zeros((h, d)), np.full(h, -np.inf), np.zeros((h, 0))
+    logits = scale * (q @ K.T)
+    m = logits.max(axis=1, keepdims=True)
+    w = np.exp(logits - m)
+    l = w.sum(axis=1, keepdims=True)
+    p = w / l
+    o = p @ V
+    lse = m[:, 0] + np.log(l[:, 0])
+    return o, lse, p
+
+
+def csa_query(q, q_idx, pos: int, Kc, Vc, k_idx, c: int, topk: int, scale: float):
+    """One CSA query token: indexer scores -> top-k -> sparse attention.
+
+    Kc, Vc: compressed cache values [N, D]; k_idx: indexer keys [N, d_idx]."""
+    n_vis = n_visible(pos, c, Kc.shape[0])
+    scores = index_scores(q_idx, k_idx)
+    idx = topk_select(scores, n_vis, topk)
+    o, lse, p = attention(q, np.asarray(Kc)[idx], np.asarray(Vc)[idx], scale)
+    return {"o": o, "lse": lse, "p": p, "idx": idx, "scores": scores, "n_vis": n_vis}
+
+
+def hca_query(q, pos: int, Kc, Vc, m: int, scale: float):
+    """One HCA query token: dense attention over every visible entry.
+
+    PAGE section 3-2 item 2 (component table): HCA compresses 128 tokens per
+    entry and attends densely, with no selection."""
+    n_vis = n_visible(pos, m, Kc.shape[0])
+    o, lse, p = attention(q, np.asarray(Kc)[:n_vis], np.asarray(Vc)[:n_vis], scale)
+    return {"o": o, "lse": lse, "p": p, "n_vis": n_vis}
+
+
+# --------------------------------------------------------------------------------------
+# composed steps
+
+
+def csa_decode(q, q_idx, ctx_len: int, Kc, Vc, k_idx, c: int, topk: int, scale: float):
+    """Decode: the new token sits at position ctx_len and sees all floor(L/c) entries."""
+    return csa_query(q, q_idx, ctx_len, Kc, Vc, k_idx, c, topk, scale)
+
+
+def hca_decode(q, ctx_len: int, Kc, Vc, m: int, scale: float):
+    return hca_query(q, ctx_len, Kc, Vc, m, scale)
+
+
+def hybrid_decode(layers, ctx_len: int, scale: float):
+    """A stack of independent layers, CSA on even layers and HCA on odd ones.
+
+    PAGE section 3-2 item 2: CSA and HCA layers are interleaved.  The page
+    gives no projections, so layers do not feed one another here: each layer
+    attends its own cache with its own query.  `layers` is a list of dicts with
+    keys q, Kc, Vc and, for CSA layers, q_idx, k_idx, c, topk; HCA layers carry m."""
+    out = []
+    for li, L in enumerate(layers):
+        if li % 2 == 0:
+            out.append(csa_decode(L["q"], L["q_idx"], ctx_len, L["Kc"], L["Vc"], L["k_idx"],
+                                  L["c"], L["topk"], scale))
+        else:
+            out.append(hca_decode(L["q"], ctx_len, L["Kc"], L["Vc"], L["m"], scale))
+    return out
+
+
+def csa_prefill(q, q_idx, ctx_len: int, Kc_ctx, Vc_ctx, new_k, new_v, k_idx, c: int,
+                topk: int, scale: float, rows=None):
+    """Chunked prefill: compress the new tokens, append them, then run every new query.
+
+    New token i sits at position ctx_len + i.  The new raw tokens are mean-pooled
+    into floor(T_new / c) entries appended after the context entries (ctx_len
+    must be a multiple of c so that no block straddles the two).  Each query
+    then runs `csa_query` under the block visibility rule.  `rows` restricts the
+    queries evaluated (a sample); the appended entries are always returned.
+
+    Returns (new_entries_k_bits, new_entries_v_bits, per-query results)."""
+    assert ctx_len % c == 0
+    nk = compress_to_cache(new_k, c)
+    nv = compress_to_cache(new_v, c)
+    Kc = np.concatenate([np.asarray(Kc_ctx, np.float64), bf16_bits_to_f64(nk)], axis=0)
+    Vc = np.concatenate([np.asarray(Vc_ctx, np.float64), bf16_bits_to_f64(nv)], axis=0)
+    t = np.asarray(q).shape[0]
+    rows = range(t) if rows is None else rows
+    res = {int(i): csa_query(q[i], q_idx[i], ctx_len + int(i), Kc, Vc, k_idx, c, topk, scale)
+           for i in rows}
+    return nk, nv, res

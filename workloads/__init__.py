@@ -1,0 +1,23 @@
+"""Seeded synthetic inputs for the CSA/HCA compressed-KV attention step.
+
+This package holds the workload shapes and the seeded random generators that
+both the CPU oracle's tests and the GPU path's tests/bench draw from.  It holds
+none of the method's arithmetic: it only draws numbers and rounds the draws to
+the storage types (bf16 bit patterns, int8).
+"""
+from .configs import WORKLOADS, Workload, get
+from .gen import (
+    seed_of,
+    rng,
+    bf16_normal,
+    int8_uniform,
+    ragged_lengths,
+    bf16_bits_from_f32,
+    device_bf16_normal,
+    device_int8_uniform,
+)
+
+__all__ = [
+    "WORKLOADS", "Workload", "get", "seed_of", "rng", "bf16_normal", "int8_uniform",
+    "ragged_lengths", "bf16_bits_from_f32", "device_bf16_normal", "device_int8_uniform",
+]

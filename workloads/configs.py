@@ -1,0 +1,66 @@
+"""Workload shapes.
+
+The method ("DeepSeek-V4: Towards Highly Efficient Million-Token Context
+Intelligence Review", dimensionstp.github.io, section 3-2 item 2, component and
+config tables) fixes the compression ratios (4 tokens per CSA entry, 128 per
+HCA entry) and the interleaving of CSA and HCA layers.  Batch sizes, context
+lengths, head counts, top-k sizes, the pooling operator and the int8 indexer are
+synthetic choices of the workload specification, reproduced here as data.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+from typing import Optional, Tuple
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    cfg_id: int            # seed namespace
+    kind: str              # csa_decode | hca_decode | hybrid_decode | csa_prefill
+    batch: int
+    ctx_len: Optional[int]              # fixed context length (tokens) or None when ragged
+    ctx_range: Optional[Tuple[int, int]] = None   # inclusive range for ragged lengths
+    heads: int = 64
+    head_dim: int = 128
+    c: int = 4             # CSA compression ratio
+    m: int = 128           # HCA compression ratio
+    topk: int = 2048
+    d_idx: int = 64
+    n_layers: int = 1
+    new_tokens: int = 0    # prefill: query tokens appended after ctx_len
+    direct_entries: bool = False   # draw compressed entries directly (no raw tokens)
+    notes: str = field(default="", compare=False)
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / float(self.head_dim) ** 0.5
+
+
+WORKLOADS = {
+    # single-sequence CSA decode over an 8K context
+    "csa_decode_8k": Workload(
+        name="csa_decode_8k", cfg_id=0, kind="csa_decode", batch=1, ctx_len=8192,
+        heads=16, topk=256),
+    # HCA decode, 8 sequences of 128K tokens
+    "hca_decode_128k": Workload(
+        name="hca_decode_128k", cfg_id=1, kind="hca_decode", batch=8, ctx_len=131072,
+        heads=64),
+    # CSA decode, 4 sequences of 1M tokens
+    "csa_decode_1m": Workload(
+        name="csa_decode_1m", cfg_id=2, kind="csa_decode", batch=4, ctx_len=1048576,
+        heads=64, topk=2048),
+    # 8-layer hybrid stack (CSA on even layers, HCA on odd), 16 ragged sequences
+    "hybrid_decode_1m": Workload(
+        name="hybrid_decode_1m", cfg_id=3, kind="hybrid_decode", batch=16, ctx_len=None,
+        ctx_range=(65536, 1048576), heads=64, topk=2048, n_layers=8, direct_entries=True,
+        notes="compressed entries drawn directly as bf16 N(0, 1/ratio)"),
+    # CSA chunked prefill: 4096 new tokens after a 256K context
+    "csa_prefill_256k": Workload(
+        name="csa_prefill_256k", cfg_id=4, kind="csa_prefill", batch=1, ctx_len=262144,
+        heads=64, topk=2048, new_tokens=4096),
+}
+
+
+def get(name: str) -> Workload:
+    return WORKLOADS[name]

@@ -1,0 +1,96 @@
+"""Seeded generators.
+
+Every stream is keyed by (workload id, layer, tensor id) through numpy's
+SeedSequence, so any tensor can be regenerated on its own.  Tensor ids:
+
+    0 raw K tokens     1 raw V tokens     2 indexer keys      3 queries
+    4 indexer queries  5 context lengths  6 compressed K (direct)
+    7 compressed V (direct)  8 new raw K (prefill)  9 new raw V (prefill)
+
+Host generation (numpy PCG64) is exact and reproducible on any CPU; it is what
+the parity tests use.  The device generators (torch Philox on the GPU) exist
+for inputs of several GiB that numpy would take minutes to draw; they are
+seeded from the same SeedSequence and their values are read back to the host
+whenever the oracle needs them.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+T_RAW_K, T_RAW_V, T_KIDX, T_Q, T_QIDX, T_LEN, T_CMP_K, T_CMP_V, T_NEW_K, T_NEW_V = range(10)
+
+
+def seed_of(cfg_id: int, layer: int, tensor_id: int, replica: int = 0) -> int:
+    key = [cfg_id, layer, tensor_id] + ([replica] if replica else [])
+    return int(np.random.SeedSequence(key).generate_state(1, dtype=np.uint64)[0] >> 1)
+
+
+def rng(cfg_id: int, layer: int, tensor_id: int, replica: int = 0) -> np.random.Generator:
+    key = [cfg_id, layer, tensor_id] + ([replica] if replica else [])
+    return np.random.Generator(np.random.PCG64(np.random.SeedSequence(key)))
+
+
+def bf16_bits_from_f32(x: np.ndarray) -> np.ndarray:
+    """Round float32 draws to bf16 storage (round to nearest, ties to even).
+
+    Finite inputs only (the draws are Gaussian); returns uint16 bit patterns."""
+    b = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    b = b + 0x7FFF + ((b >> 16) & 1)
+    return (b >> 16).astype(np.uint16)
+
+
+def bf16_normal(gen: np.random.Generator, shape, std: float = 1.0) -> np.ndarray:
+    """bf16 bit patterns of N(0, std^2) draws."""
+    x = gen.standard_normal(size=shape, dtype=np.float32)
+    if std != 1.0:
+        x = (x.astype(np.float64) * std).astype(np.float32)
+    return bf16_bits_from_f32(x)
+
+
+def int8_uniform(gen: np.random.Generator, shape) -> np.ndarray:
+    """int8 uniform over the 255 integers -127..127 inclusive."""
+    return gen.integers(-127, 128, size=shape, dtype=np.int8)
+
+
+def ragged_lengths(gen: np.random.Generator, n: int, lo: int, hi: int) -> np.ndarray:
+    """n integers uniform over lo..hi inclusive."""
+    return gen.integers(lo, hi + 1, size=n, dtype=np.int64)
+
+
+# --------------------------------------------------------------------------------------
+# device-side generation for multi-GiB inputs
+
+
+def _torch_gen(seed: int, device):
+    import torch
+
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    return g
+
+
+def device_bf16_normal(shape, seed: int, std: float = 1.0, device="cuda", out=None):
+    """torch.bfloat16 tensor of N(0, std^2) draws made on the device (Philox).
+
+    Drawn in slabs so the float32 staging buffer stays small."""
+    import torch
+
+    g = _torch_gen(seed, device)
+    if out is None:
+        out = torch.empty(shape, dtype=torch.bfloat16, device=device)
+    flat = out.view(-1)
+    slab = 1 << 26
+    for s in range(0, flat.numel(), slab):
+        e = min(flat.numel(), s + slab)
+        tmp = torch.randn(e - s, generator=g, device=device, dtype=torch.float32)
+        if std != 1.0:
+            tmp.mul_(std)
+        flat[s:e].copy_(tmp)
+    return out
+
+
+def device_int8_uniform(shape, seed: int, device="cuda"):
+    import torch
+
+    g = _torch_gen(seed, device)
+    return torch.randint(-127, 128, shape, generator=g, device=device, dtype=torch.int8)

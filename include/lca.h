@@ -1,0 +1,215 @@
+/*
+ * lca.h — C ABI of the CSA / HCA compressed-KV attention library for gfx950.
+ *
+ * The operations follow "DeepSeek-V4: Towards Highly Efficient Million-Token
+ * Context Intelligence Review" (dimensionstp.github.io):
+ *   - section 2-1 and section 3-2 item 2 (component table): CSA compresses the KV
+ *     sequence 4 tokens per entry and runs sparse attention over a top-k of the
+ *     entries; HCA compresses 128 tokens per entry and attends densely; both
+ *     ratios are the same in both model sizes; CSA and HCA layers are interleaved.
+ *   - section 3-2 item 4: CSA's indexer has its own Q.K path; the compressed
+ *     cache is kept apart from a state cache holding the sliding window and the
+ *     tokens not yet ready for compression.
+ * The page leaves the pooling operator, the indexer form and the sizes open.
+ * This library implements mean pooling, an int8 indexer (d_idx = 64, exact
+ * int32 dot products), a top-k ranked by (score desc, index asc), and softmax
+ * attention with fp32 accumulation over bf16 K/V (head_dim = 128).
+ *
+ * Conventions shared by every call
+ *   Memory.   Every tensor pointer is DEVICE memory owned by the caller.  The
+ *             library allocates nothing and keeps no state besides a per-thread
+ *             error string.  Tensors are dense and row-major.  bf16 values are
+ *             passed as uint16_t bit patterns.  K/V/query rows and indexer rows
+ *             must be 16-byte aligned (else LCA_ERR_ALIGN).
+ *   Batches.  Sequences are packed.  ent_off[B+1] (device, int64) gives each
+ *             sequence's first compressed entry; q_off[B+1] (device, int64) its
+ *             first query row; q_pos[rows] (device, int64) the absolute token
+ *             position of each query row (a decoding query after L tokens sits at
+ *             L).  Host scalars max_q / max_entries bound the per-sequence counts
+ *             and size the launch grids; values beyond them are not processed.
+ *   Visibility. A query at position p sees entry j of a cache compressed at
+ *             ratio r iff the entry's block has ended before p: (j+1)*r <= p.
+ *   Streams.  `stream` is a hipStream_t passed as void* (NULL = default
+ *             stream).  Calls validate, enqueue and return; none synchronises.
+ *   Errors.   Every call returns an int32 status (below).  Validation happens
+ *             before anything is enqueued, so a failed call has no effect.
+ *             lca_last_error() returns a per-thread message for the last failure.
+ *             Faults inside a kernel surface at the caller's next synchronisation.
+ *   Workspace. Calls that need scratch memory take (ws, ws_bytes); the size comes
+ *             from the matching lca_*_workspace_bytes query.  A workspace must be
+ *             ZERO-FILLED by the caller before its first use; every call returns
+ *             it to that state (the kernels that consume counters and histograms
+ *             clear them), so one zeroed workspace serves any number of calls in
+ *             stream order.  Calls that share a workspace must not run
+ *             concurrently.  lca_workspace_reset() re-zeroes one on a stream.
+ *   Determinism. For a given launch shape every output is bitwise reproducible:
+ *             no result depends on the order in which work-groups finish.
+ */
+#ifndef LCA_H
+#define LCA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define LCA_ABI_VERSION 1
+
+enum lca_status {
+  LCA_OK = 0,
+  LCA_ERR_NULL = -1,        /* a required pointer is NULL */
+  LCA_ERR_SHAPE = -2,       /* a size is negative, zero where it must not be, or inconsistent */
+  LCA_ERR_ALIGN = -3,       /* a pointer is not 16-byte aligned */
+  LCA_ERR_UNSUPPORTED = -4, /* head_dim != 128, d_idx != 64, heads % 16 != 0, ... */
+  LCA_ERR_WORKSPACE = -5,   /* ws_bytes smaller than the query returned */
+  LCA_ERR_HIP = -6,         /* the HIP runtime reported an error at launch */
+  LCA_ERR_INTERNAL = -7
+};
+
+typedef uint16_t lca_bf16;
+
+int32_t lca_abi_version(void);
+const char* lca_last_error(void);
+/* Number of compute units of the current device (for callers sizing work); -1 on error. */
+int32_t lca_device_cu_count(void);
+/* Re-zero a workspace on `stream` (a fill kernel, not a memset node). */
+int32_t lca_workspace_reset(void* ws, size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * kv_compress — mean pooling of complete blocks of c tokens.
+ * Page section 3-2 item 2 (component table): CSA maps every 4 tokens to one
+ * compressed entry, HCA every 128; the pooling operator is the mean here.
+ *
+ *   x        [tok_off[B], head_dim] bf16 raw tokens, sequence b in rows
+ *            tok_off[b] .. tok_off[b+1]-1.
+ *   y        [*, head_dim] bf16; sequence b writes n_b = min(floor(T_b / c),
+ *            ent_off[b+1] - ent_off[b]) entries at rows ent_off[b] .. .
+ *            Entry j = mean of tokens j*c .. j*c+c-1 of its sequence, summed in
+ *            fp64 and rounded once to bf16 (to nearest, ties to even).  The
+ *            T_b mod c tail tokens form no entry.
+ *   max_tokens  host bound on T_b; head_dim % 8 == 0; 1 <= c <= 4096.
+ * ------------------------------------------------------------------------- */
+int32_t lca_kv_compress(const lca_bf16* x, const int64_t* tok_off, int32_t batch,
+                        int32_t max_tokens, int32_t head_dim, int32_t c, lca_bf16* y,
+                        const int64_t* ent_off, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * csa_index_score — indexer scores of every query row against its sequence's
+ * indexer keys.  Page section 3-2 item 4: CSA's indexer scores entries through
+ * a Q.K product of its own.  Here: int8 x int8 products summed exactly in
+ * int32 (|score| <= 64 * 127^2 < 2^20).
+ *
+ *   q_idx    [rows, d_idx] int8, one indexer query per query row.
+ *   k_idx    [ent_off[B], d_idx] int8 indexer keys, one per compressed entry.
+ *   scores   [rows, ld_scores] int32; row r of sequence b gets N_b values:
+ *            entries j < n_vis[r] hold the score, entries n_vis[r] <= j < N_b
+ *            hold INT32_MIN; columns >= N_b are not written.
+ *   n_vis    [rows] int32 out: min(floor(q_pos[r] / c), N_b).
+ *   ws       optional top-k workspace (lca_csa_topk_workspace_bytes for the same
+ *            rows, max_entries and k).  When given, the first radix pass of
+ *            the following lca_csa_topk_select is fused here; that call must
+ *            then pass LCA_TOPK_HIST_READY with the same workspace.
+ *   rows     = q_off[B] must not exceed batch * max_q.
+ *   d_idx == 64; ld_scores >= max_entries.
+ * ------------------------------------------------------------------------- */
+int32_t lca_csa_index_score(const int8_t* q_idx, const int64_t* q_off, const int64_t* q_pos,
+                            const int8_t* k_idx, const int64_t* ent_off, int32_t batch,
+                            int32_t max_q, int32_t max_entries, int32_t d_idx, int32_t c,
+                            int32_t* scores, int64_t ld_scores, int32_t* n_vis, void* ws,
+                            size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * csa_topk_select — per row, the top min(k, n_vis[r]) entries of
+ * scores[r, 0 .. n_vis[r]) ranked by (score desc, index asc).
+ * Page section 3-2 item 2 (component table): CSA keeps a sparse top-k of the
+ * compressed entries.  The tie rule (lower index first) is this library's.
+ *
+ *   scores   [rows, ld_scores] int32, values in [-2^20, 2^20) (what the int8
+ *            indexer with d_idx = 64 produces; others give unspecified sets).
+ *   n_vis    [rows] int32 visible entries per row (<= max_n).
+ *   idx      [rows, k] int32 out: selected entry indices in ascending order,
+ *            then -1 padding.    count [rows] int32 out: min(k, n_vis[r]).
+ *   flags    LCA_TOPK_HIST_READY if lca_csa_index_score already ran with ws.
+ *   Radix select over a 21-bit key in two levels (2048 then 1024 bins), with a
+ *   candidate list compacted in index order, so ties resolve deterministically.
+ * ------------------------------------------------------------------------- */
+#define LCA_TOPK_HIST_READY 1u
+size_t lca_csa_topk_workspace_bytes(int32_t rows, int32_t max_n, int32_t k);
+int32_t lca_csa_topk_select(const int32_t* scores, int64_t ld_scores, int32_t rows,
+                            int32_t max_n, const int32_t* n_vis, int32_t k, int32_t* idx,
+                            int32_t* count, void* ws, size_t ws_bytes, uint32_t flags,
+                            void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Attention over compressed entries (one shared KV head, H query heads).
+ * Page sections 2-1 and 3-2 item 2: CSA attends the selected entries, HCA all
+ * visible ones.  For each head h: logits = scale * q_h . K_j, p = softmax,
+ * o_h = sum_j p_j V_j; lse_h = log sum_j exp(logits_j).  bf16 inputs, fp32
+ * logits / softmax / accumulation, bf16 output (to nearest, ties to even).
+ * A row with no entries gets o = 0 and lse = -inf.
+ *
+ *   q        [rows, heads, 128] bf16;  out [rows, heads, 128] bf16
+ *   lse      [rows, heads] fp32 (nullable)
+ *   k_cmp, v_cmp  [ent_off[B], 128] bf16 compressed cache.
+ *   heads % 16 == 0, head_dim == 128.
+ *   splits   work-groups per (row, 64 heads) along the entries; 0 = automatic
+ *            (32 when max_q == 1, fewer as max_q grows, 1 from max_q >= 32).
+ *            The split of a row depends only on its own entry count and
+ *            `splits`, so a row's result does not depend on the rest of the batch.
+ * ------------------------------------------------------------------------- */
+size_t lca_attn_workspace_bytes(int32_t rows, int32_t heads, int32_t max_q, int32_t splits);
+
+/* Sparse (CSA): row r attends entries ent_off[b] + idx[r, j] for j < count[r]. */
+int32_t lca_csa_sparse_attn(const lca_bf16* q, const lca_bf16* k_cmp, const lca_bf16* v_cmp,
+                            const int64_t* ent_off, const int64_t* q_off, int32_t batch,
+                            int32_t max_q, const int32_t* idx, const int32_t* count, int32_t k,
+                            int32_t heads, int32_t head_dim, float scale, int32_t splits,
+                            lca_bf16* out, float* lse, void* ws, size_t ws_bytes, void* stream);
+
+/* Dense (HCA): row r attends entries 0 .. min(floor(q_pos[r] / m), N_b) - 1. */
+int32_t lca_hca_dense_attn(const lca_bf16* q, const lca_bf16* k_cmp, const lca_bf16* v_cmp,
+                           const int64_t* ent_off, const int64_t* q_off, const int64_t* q_pos,
+                           int32_t batch, int32_t max_q, int32_t max_entries, int32_t m,
+                           int32_t heads, int32_t head_dim, float scale, int32_t splits,
+                           lca_bf16* out, float* lse, void* ws, size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * hybrid_layer_step — a stack of independent attention layers over the same
+ * batch, CSA and HCA interleaved (page section 3-2 item 2).  Each layer has its
+ * own cache and queries; a CSA layer runs index_score -> topk_select ->
+ * sparse_attn, an HCA layer dense_attn, with the same kernels as the single
+ * calls.  Layers are independent, so the step may run them concurrently on
+ * internal streams forked from and joined back to `stream`.
+ * ------------------------------------------------------------------------- */
+enum lca_layer_kind { LCA_LAYER_CSA = 0, LCA_LAYER_HCA = 1 };
+
+typedef struct lca_layer {
+  int32_t kind;          /* LCA_LAYER_CSA or LCA_LAYER_HCA */
+  int32_t ratio;         /* compression ratio: c (CSA) or m (HCA) */
+  int32_t topk;          /* CSA only */
+  int32_t max_entries;   /* host bound on entries per sequence in this layer */
+  const lca_bf16* q;     /* [rows, heads, 128] */
+  const int8_t* q_idx;   /* CSA: [rows, 64] */
+  const lca_bf16* k_cmp; /* [ent_off[B], 128] */
+  const lca_bf16* v_cmp; /* [ent_off[B], 128] */
+  const int8_t* k_idx;   /* CSA: [ent_off[B], 64] */
+  const int64_t* ent_off;/* [B+1] device */
+  lca_bf16* out;         /* [rows, heads, 128] */
+  float* lse;            /* [rows, heads] or NULL */
+  int32_t* idx;          /* CSA out: [rows, topk] */
+  int32_t* count;        /* CSA out: [rows] */
+} lca_layer;
+
+size_t lca_hybrid_workspace_bytes(const lca_layer* layers, int32_t n_layers, int32_t batch,
+                                  int32_t max_q, int32_t heads);
+int32_t lca_hybrid_layer_step(const lca_layer* layers, int32_t n_layers, const int64_t* q_off,
+                              const int64_t* q_pos, int32_t batch, int32_t max_q, int32_t heads,
+                              int32_t head_dim, float scale, void* ws, size_t ws_bytes,
+                              void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* LCA_H */

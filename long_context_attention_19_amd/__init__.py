@@ -1,0 +1,176 @@
+"""Python binding of liblca.so, the gfx950 CSA/HCA compressed-KV attention library.
+
+Argument marshalling only: every function passes device pointers, sizes and
+the current HIP stream to the C ABI of the same name (include/lca.h) and
+raises LcaError on a non-zero status.  No step of the computation runs here.
+Importing this package fails loudly when liblca.so has not been built.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "liblca.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(
+        f"{LIB_PATH} is missing: build it with `python -m long_context_attention_19_amd.build_lib` "
+        "(or __graft_entry__.build()); there is no fallback implementation")
+
+_lib = ctypes.CDLL(LIB_PATH)
+
+_i32, _i64, _u32, _f32, _sz, _vp = (ctypes.c_int32, ctypes.c_int64, ctypes.c_uint32,
+                                    ctypes.c_float, ctypes.c_size_t, ctypes.c_void_p)
+
+LCA_LAYER_CSA = 0
+LCA_LAYER_HCA = 1
+LCA_TOPK_HIST_READY = 1
+
+
+class LcaLayer(ctypes.Structure):
+    _fields_ = [("kind", _i32), ("ratio", _i32), ("topk", _i32), ("max_entries", _i32),
+                ("q", _vp), ("q_idx", _vp), ("k_cmp", _vp), ("v_cmp", _vp), ("k_idx", _vp),
+                ("ent_off", _vp), ("out", _vp), ("lse", _vp), ("idx", _vp), ("count", _vp)]
+
+
+_SIGS = {
+    "lca_abi_version": (_i32, []),
+    "lca_last_error": (ctypes.c_char_p, []),
+    "lca_device_cu_count": (_i32, []),
+    "lca_workspace_reset": (_i32, [_vp, _sz, _vp]),
+    "lca_kv_compress": (_i32, [_vp, _vp, _i32, _i32, _i32, _i32, _vp, _vp, _vp]),
+    "lca_csa_index_score": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _vp,
+                                   _i64, _vp, _vp, _sz, _vp]),
+    "lca_csa_topk_workspace_bytes": (_sz, [_i32, _i32, _i32]),
+    "lca_csa_topk_select": (_i32, [_vp, _i64, _i32, _i32, _vp, _i32, _vp, _vp, _vp, _sz, _u32,
+                                   _vp]),
+    "lca_attn_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32]),
+    "lca_csa_sparse_attn": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _vp, _vp, _i32, _i32,
+                                   _i32, _f32, _i32, _vp, _vp, _vp, _sz, _vp]),
+    "lca_hca_dense_attn": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
+                                  _i32, _f32, _i32, _vp, _vp, _vp, _sz, _vp]),
+    "lca_hybrid_workspace_bytes": (_sz, [ctypes.POINTER(LcaLayer), _i32, _i32, _i32, _i32]),
+    "lca_hybrid_layer_step": (_i32, [ctypes.POINTER(LcaLayer), _i32, _vp, _vp, _i32, _i32, _i32,
+                                     _i32, _f32, _vp, _sz, _vp]),
+}
+for _name, (_res, _args) in _SIGS.items():
+    _fn = getattr(_lib, _name)
+    _fn.restype = _res
+    _fn.argtypes = _args
+
+EXPORTED = tuple(_SIGS)
+
+
+class LcaError(RuntimeError):
+    def __init__(self, name: str, status: int):
+        self.status = status
+        super().__init__(f"{name} failed with status {status}: {last_error()}")
+
+
+def last_error() -> str:
+    return (_lib.lca_last_error() or b"").decode()
+
+
+def abi_version() -> int:
+    return _lib.lca_abi_version()
+
+
+def device_cu_count() -> int:
+    return _lib.lca_device_cu_count()
+
+
+def _p(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _s(stream):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _check(name, st):
+    if st != 0:
+        raise LcaError(name, st)
+
+
+def _nb(t):
+    return 0 if t is None else t.numel() * t.element_size()
+
+
+# ------------------------------------------------------------------ workspaces
+def workspace(nbytes: int, device="cuda") -> torch.Tensor:
+    """A zero-filled device workspace (the library requires zero on first use)."""
+    return torch.zeros(max(int(nbytes), 16), dtype=torch.uint8, device=device)
+
+
+def workspace_reset(ws, stream=None):
+    _check("lca_workspace_reset", _lib.lca_workspace_reset(_p(ws), _nb(ws), _s(stream)))
+
+
+def csa_topk_workspace_bytes(rows, max_n, k) -> int:
+    return _lib.lca_csa_topk_workspace_bytes(rows, max_n, k)
+
+
+def attn_workspace_bytes(rows, heads, max_q, splits=0) -> int:
+    return _lib.lca_attn_workspace_bytes(rows, heads, max_q, splits)
+
+
+# ------------------------------------------------------------------ operations
+def kv_compress(x, tok_off, batch, max_tokens, c, y, ent_off, stream=None):
+    _check("lca_kv_compress", _lib.lca_kv_compress(
+        _p(x), _p(tok_off), batch, max_tokens, x.shape[-1], c, _p(y), _p(ent_off), _s(stream)))
+
+
+def csa_index_score(q_idx, q_off, q_pos, k_idx, ent_off, batch, max_q, max_entries, c, scores,
+                    n_vis, ws=None, stream=None):
+    _check("lca_csa_index_score", _lib.lca_csa_index_score(
+        _p(q_idx), _p(q_off), _p(q_pos), _p(k_idx), _p(ent_off), batch, max_q, max_entries,
+        q_idx.shape[-1], c, _p(scores), scores.stride(0), _p(n_vis), _p(ws), _nb(ws),
+        _s(stream)))
+
+
+def csa_topk_select(scores, rows, max_n, n_vis, k, idx, count, ws, hist_ready=False,
+                    stream=None):
+    _check("lca_csa_topk_select", _lib.lca_csa_topk_select(
+        _p(scores), scores.stride(0), rows, max_n, _p(n_vis), k, _p(idx), _p(count), _p(ws),
+        _nb(ws), LCA_TOPK_HIST_READY if hist_ready else 0, _s(stream)))
+
+
+def csa_sparse_attn(q, k_cmp, v_cmp, ent_off, q_off, batch, max_q, idx, count, k, scale, out,
+                    lse=None, ws=None, splits=0, stream=None):
+    _check("lca_csa_sparse_attn", _lib.lca_csa_sparse_attn(
+        _p(q), _p(k_cmp), _p(v_cmp), _p(ent_off), _p(q_off), batch, max_q, _p(idx), _p(count), k,
+        q.shape[-2], q.shape[-1], scale, splits, _p(out), _p(lse), _p(ws), _nb(ws), _s(stream)))
+
+
+def hca_dense_attn(q, k_cmp, v_cmp, ent_off, q_off, q_pos, batch, max_q, max_entries, m, scale,
+                   out, lse=None, ws=None, splits=0, stream=None):
+    _check("lca_hca_dense_attn", _lib.lca_hca_dense_attn(
+        _p(q), _p(k_cmp), _p(v_cmp), _p(ent_off), _p(q_off), _p(q_pos), batch, max_q,
+        max_entries, m, q.shape[-2], q.shape[-1], scale, splits, _p(out), _p(lse), _p(ws),
+        _nb(ws), _s(stream)))
+
+
+def make_layers(layers):
+    """ctypes array of lca_layer from dicts with tensor fields (see include/lca.h)."""
+    arr = (LcaLayer * len(layers))()
+    for i, L in enumerate(layers):
+        arr[i] = LcaLayer(L["kind"], L["ratio"], L.get("topk", 0), L["max_entries"],
+                          _p(L["q"]), _p(L.get("q_idx")), _p(L["k_cmp"]), _p(L["v_cmp"]),
+                          _p(L.get("k_idx")), _p(L["ent_off"]), _p(L["out"]), _p(L.get("lse")),
+                          _p(L.get("idx")), _p(L.get("count")))
+    return arr
+
+
+def hybrid_workspace_bytes(layer_arr, batch, max_q, heads) -> int:
+    return _lib.lca_hybrid_workspace_bytes(layer_arr, len(layer_arr), batch, max_q, heads)
+
+
+def hybrid_layer_step(layer_arr, q_off, q_pos, batch, max_q, heads, head_dim, scale, ws,
+                      stream=None):
+    _check("lca_hybrid_layer_step", _lib.lca_hybrid_layer_step(
+        layer_arr, len(layer_arr), _p(q_off), _p(q_pos), batch, max_q, heads, head_dim, scale,
+        _p(ws), _nb(ws), _s(stream)))

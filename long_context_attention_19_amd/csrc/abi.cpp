@@ -1,0 +1,322 @@
+// The C ABI declared in include/lca.h: argument validation, workspace carving
+// and kernel enqueue.  No call allocates or synchronises; validation happens
+// before any enqueue so a rejected call has no effect.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "lca.h"
+#include "lca_internal.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+int32_t fail(int32_t code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+int32_t ok() {
+  g_err.clear();
+  return LCA_OK;
+}
+
+bool al16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int32_t hip_status(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(LCA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+bool heads_supported(int32_t heads) {
+  if (heads <= 0 || heads % 16) return false;
+  if (heads < 64) return heads == 16 || heads == 32;
+  return heads % 64 == 0;
+}
+
+constexpr int kTopkChunk = 4096;
+
+size_t csa_layer_bytes(int rows, int max_entries, int topk, int heads, int splits) {
+  const int ld = (max_entries + 3) & ~3;
+  size_t b = lca::align256((size_t)rows * (size_t)std::max(ld, 4) * 4);   // scores
+  b += lca::align256((size_t)rows * 4);                                     // n_vis
+  b += lca::topk_ws_bytes(rows, max_entries, topk);
+  b += lca::attn_ws_bytes(rows, heads, splits);
+  return b;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t lca_abi_version(void) { return LCA_ABI_VERSION; }
+
+const char* lca_last_error(void) { return g_err.c_str(); }
+
+int32_t lca_device_cu_count(void) {
+  int dev = 0, cu = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return -1;
+  if (hipDeviceGetAttribute(&cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return -1;
+  return cu;
+}
+
+int32_t lca_workspace_reset(void* ws, size_t ws_bytes, void* stream) {
+  if (ws_bytes == 0) return ok();
+  if (!ws) return fail(LCA_ERR_NULL, "workspace_reset: ws is NULL");
+  if (!al16(ws)) return fail(LCA_ERR_ALIGN, "workspace_reset: ws not 16-byte aligned");
+  return hip_status(lca::launch_fill_zero(ws, ws_bytes, (hipStream_t)stream), "workspace_reset");
+}
+
+// ------------------------------------------------------------------ kv_compress
+int32_t lca_kv_compress(const lca_bf16* x, const int64_t* tok_off, int32_t batch,
+                        int32_t max_tokens, int32_t head_dim, int32_t c, lca_bf16* y,
+                        const int64_t* ent_off, void* stream) {
+  if (batch < 0 || max_tokens < 0) return fail(LCA_ERR_SHAPE, "kv_compress: negative batch or max_tokens");
+  if (head_dim <= 0 || head_dim % 8) return fail(LCA_ERR_UNSUPPORTED, "kv_compress: head_dim %d not a positive multiple of 8", head_dim);
+  if (c < 1 || c > 4096) return fail(LCA_ERR_SHAPE, "kv_compress: ratio c=%d outside 1..4096", c);
+  if (batch == 0 || max_tokens / c == 0) return ok();
+  if (!x || !tok_off || !y || !ent_off) return fail(LCA_ERR_NULL, "kv_compress: NULL pointer");
+  if (!al16(x) || !al16(y)) return fail(LCA_ERR_ALIGN, "kv_compress: x / y not 16-byte aligned");
+  return hip_status(lca::launch_kv_compress(x, tok_off, batch, max_tokens, head_dim, c, y, ent_off,
+                                            (hipStream_t)stream),
+                    "kv_compress launch");
+}
+
+// ------------------------------------------------------------------ index scores
+int32_t lca_csa_index_score(const int8_t* q_idx, const int64_t* q_off, const int64_t* q_pos,
+                            const int8_t* k_idx, const int64_t* ent_off, int32_t batch,
+                            int32_t max_q, int32_t max_entries, int32_t d_idx, int32_t c,
+                            int32_t* scores, int64_t ld_scores, int32_t* n_vis, void* ws,
+                            size_t ws_bytes, void* stream) {
+  if (d_idx != 64) return fail(LCA_ERR_UNSUPPORTED, "csa_index_score: d_idx=%d (only 64)", d_idx);
+  if (batch < 0 || max_q < 0 || max_entries < 0) return fail(LCA_ERR_SHAPE, "csa_index_score: negative size");
+  if (c < 1) return fail(LCA_ERR_SHAPE, "csa_index_score: ratio c=%d < 1", c);
+  if (ld_scores < max_entries || ld_scores % 4) return fail(LCA_ERR_SHAPE, "csa_index_score: ld_scores=%lld must be >= max_entries and a multiple of 4", (long long)ld_scores);
+  if (batch == 0 || max_q == 0) return ok();
+  if ((int64_t)batch * max_q > (1 << 30)) return fail(LCA_ERR_SHAPE, "csa_index_score: too many rows");
+  if (!q_idx || !q_off || !q_pos || !k_idx || !ent_off || !scores || !n_vis) return fail(LCA_ERR_NULL, "csa_index_score: NULL pointer");
+  if (!al16(q_idx) || !al16(k_idx) || !al16(scores)) return fail(LCA_ERR_ALIGN, "csa_index_score: q_idx / k_idx / scores not 16-byte aligned");
+  int32_t* hist = nullptr;
+  if (ws) {
+    const size_t need = (size_t)batch * max_q * 2048 * 4;
+    if (ws_bytes < need) return fail(LCA_ERR_WORKSPACE, "csa_index_score: ws_bytes %zu < %zu", ws_bytes, need);
+    if (!al16(ws)) return fail(LCA_ERR_ALIGN, "csa_index_score: ws not 16-byte aligned");
+    hist = reinterpret_cast<int32_t*>(ws);   // the histogram leads the top-k workspace
+  }
+  return hip_status(lca::launch_index_score(q_idx, q_off, q_pos, k_idx, ent_off, batch, max_q,
+                                            max_entries, c, scores, ld_scores, n_vis, hist,
+                                            (hipStream_t)stream),
+                    "csa_index_score launch");
+}
+
+// ------------------------------------------------------------------ top-k
+size_t lca_csa_topk_workspace_bytes(int32_t rows, int32_t max_n, int32_t k) {
+  if (rows <= 0 || max_n < 0 || k <= 0) return 0;
+  return lca::topk_ws_bytes(rows, max_n, k);
+}
+
+int32_t lca_csa_topk_select(const int32_t* scores, int64_t ld_scores, int32_t rows,
+                            int32_t max_n, const int32_t* n_vis, int32_t k, int32_t* idx,
+                            int32_t* count, void* ws, size_t ws_bytes, uint32_t flags,
+                            void* stream) {
+  if (rows < 0 || max_n < 0) return fail(LCA_ERR_SHAPE, "csa_topk_select: negative size");
+  if (k <= 0) return fail(LCA_ERR_SHAPE, "csa_topk_select: k=%d must be positive", k);
+  if ((int64_t)max_n > (int64_t)lca::topk_max_chunks() * kTopkChunk) return fail(LCA_ERR_UNSUPPORTED, "csa_topk_select: max_n=%d above %d", max_n, lca::topk_max_chunks() * kTopkChunk);
+  if (ld_scores < max_n || ld_scores % 4) return fail(LCA_ERR_SHAPE, "csa_topk_select: ld_scores must be >= max_n and a multiple of 4");
+  if (flags & ~LCA_TOPK_HIST_READY) return fail(LCA_ERR_SHAPE, "csa_topk_select: unknown flags 0x%x", flags);
+  if (rows == 0) return ok();
+  if (!scores || !n_vis || !idx || !count || !ws) return fail(LCA_ERR_NULL, "csa_topk_select: NULL pointer");
+  if (!al16(scores) || !al16(ws)) return fail(LCA_ERR_ALIGN, "csa_topk_select: scores / ws not 16-byte aligned");
+  const size_t need = lca::topk_ws_bytes(rows, max_n, k);
+  if (ws_bytes < need) return fail(LCA_ERR_WORKSPACE, "csa_topk_select: ws_bytes %zu < %zu", ws_bytes, need);
+  lca::TopkWs w = lca::topk_ws_carve(ws, rows, max_n, k);
+  return hip_status(lca::launch_topk(scores, ld_scores, rows, max_n, n_vis, k, idx, count, w,
+                                     (flags & LCA_TOPK_HIST_READY) != 0, (hipStream_t)stream),
+                    "csa_topk_select launch");
+}
+
+// ------------------------------------------------------------------ attention
+size_t lca_attn_workspace_bytes(int32_t rows, int32_t heads, int32_t max_q, int32_t splits) {
+  if (rows <= 0 || heads <= 0) return 0;
+  const int sp = splits > 0 ? splits : lca::attn_auto_splits(max_q);
+  return lca::attn_ws_bytes(rows, heads, sp);
+}
+
+static int32_t attn_common(const char* name, const lca_bf16* q, const lca_bf16* k_cmp,
+                           const lca_bf16* v_cmp, const int64_t* ent_off, const int64_t* q_off,
+                           int32_t batch, int32_t max_q, int32_t heads, int32_t head_dim,
+                           float scale, int32_t splits, lca_bf16* out, void* ws,
+                           size_t ws_bytes, lca::AttnArgs& a) {
+  if (head_dim != 128) return fail(LCA_ERR_UNSUPPORTED, "%s: head_dim=%d (only 128)", name, head_dim);
+  if (!heads_supported(heads)) return fail(LCA_ERR_UNSUPPORTED, "%s: heads=%d (16, 32 or a multiple of 64)", name, heads);
+  if (batch < 0 || max_q < 0 || splits < 0) return fail(LCA_ERR_SHAPE, "%s: negative size", name);
+  if (splits > 1024) return fail(LCA_ERR_SHAPE, "%s: splits=%d above 1024", name, splits);
+  if (!std::isfinite(scale)) return fail(LCA_ERR_SHAPE, "%s: scale not finite", name);
+  if ((int64_t)batch * max_q > 65535 * 1024LL) return fail(LCA_ERR_SHAPE, "%s: too many rows", name);
+  if (batch == 0 || max_q == 0) return LCA_OK + 1;   // nothing to do
+  if (!q || !k_cmp || !v_cmp || !ent_off || !q_off || !out) return fail(LCA_ERR_NULL, "%s: NULL pointer", name);
+  if (!al16(q) || !al16(k_cmp) || !al16(v_cmp) || !al16(out)) return fail(LCA_ERR_ALIGN, "%s: q / k_cmp / v_cmp / out not 16-byte aligned", name);
+  const int sp = splits > 0 ? splits : lca::attn_auto_splits(max_q);
+  const int rows = batch * max_q;
+  const size_t need = lca::attn_ws_bytes(rows, heads, sp);
+  if (need && (!ws || ws_bytes < need)) return fail(LCA_ERR_WORKSPACE, "%s: ws_bytes %zu < %zu", name, ws_bytes, need);
+  if (need && !al16(ws)) return fail(LCA_ERR_ALIGN, "%s: ws not 16-byte aligned", name);
+  a = lca::AttnArgs{};
+  a.q = q;
+  a.kc = k_cmp;
+  a.vc = v_cmp;
+  a.ent_off = ent_off;
+  a.q_off = q_off;
+  a.max_q = max_q;
+  a.heads = heads;
+  a.splits = sp;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  a.out = out;
+  lca::attn_ws_carve(ws, rows, heads, sp, a);
+  return LCA_OK;
+}
+
+int32_t lca_csa_sparse_attn(const lca_bf16* q, const lca_bf16* k_cmp, const lca_bf16* v_cmp,
+                            const int64_t* ent_off, const int64_t* q_off, int32_t batch,
+                            int32_t max_q, const int32_t* idx, const int32_t* count, int32_t k,
+                            int32_t heads, int32_t head_dim, float scale, int32_t splits,
+                            lca_bf16* out, float* lse, void* ws, size_t ws_bytes, void* stream) {
+  if (k <= 0) return fail(LCA_ERR_SHAPE, "csa_sparse_attn: k=%d must be positive", k);
+  lca::AttnArgs a;
+  int32_t st = attn_common("csa_sparse_attn", q, k_cmp, v_cmp, ent_off, q_off, batch, max_q, heads,
+                           head_dim, scale, splits, out, ws, ws_bytes, a);
+  if (st == LCA_OK + 1) return ok();
+  if (st != LCA_OK) return st;
+  if (!idx || !count) return fail(LCA_ERR_NULL, "csa_sparse_attn: idx / count NULL");
+  a.idx = idx;
+  a.count = count;
+  a.k = k;
+  a.ratio = 1;
+  a.lse = lse;
+  return hip_status(lca::launch_attention(a, batch, k, (hipStream_t)stream), "csa_sparse_attn launch");
+}
+
+int32_t lca_hca_dense_attn(const lca_bf16* q, const lca_bf16* k_cmp, const lca_bf16* v_cmp,
+                           const int64_t* ent_off, const int64_t* q_off, const int64_t* q_pos,
+                           int32_t batch, int32_t max_q, int32_t max_entries, int32_t m,
+                           int32_t heads, int32_t head_dim, float scale, int32_t splits,
+                           lca_bf16* out, float* lse, void* ws, size_t ws_bytes, void* stream) {
+  if (m < 1) return fail(LCA_ERR_SHAPE, "hca_dense_attn: ratio m=%d < 1", m);
+  if (max_entries < 0) return fail(LCA_ERR_SHAPE, "hca_dense_attn: negative max_entries");
+  lca::AttnArgs a;
+  int32_t st = attn_common("hca_dense_attn", q, k_cmp, v_cmp, ent_off, q_off, batch, max_q, heads,
+                           head_dim, scale, splits, out, ws, ws_bytes, a);
+  if (st == LCA_OK + 1) return ok();
+  if (st != LCA_OK) return st;
+  if (!q_pos) return fail(LCA_ERR_NULL, "hca_dense_attn: q_pos NULL");
+  a.q_pos = q_pos;
+  a.ratio = m;
+  a.lse = lse;
+  return hip_status(lca::launch_attention(a, batch, max_entries, (hipStream_t)stream),
+                    "hca_dense_attn launch");
+}
+
+// ------------------------------------------------------------------ hybrid step
+size_t lca_hybrid_workspace_bytes(const lca_layer* layers, int32_t n_layers, int32_t batch,
+                                  int32_t max_q, int32_t heads) {
+  if (!layers || n_layers <= 0 || batch <= 0 || max_q <= 0 || heads <= 0) return 0;
+  const int rows = batch * max_q;
+  const int sp = lca::attn_auto_splits(max_q);
+  size_t b = 0;
+  for (int l = 0; l < n_layers; ++l) {
+    if (layers[l].kind == LCA_LAYER_CSA)
+      b += csa_layer_bytes(rows, std::max(layers[l].max_entries, 0), std::max(layers[l].topk, 1),
+                           heads, sp);
+    else
+      b += lca::attn_ws_bytes(rows, heads, sp);
+  }
+  return b;
+}
+
+int32_t lca_hybrid_layer_step(const lca_layer* layers, int32_t n_layers, const int64_t* q_off,
+                              const int64_t* q_pos, int32_t batch, int32_t max_q, int32_t heads,
+                              int32_t head_dim, float scale, void* ws, size_t ws_bytes,
+                              void* stream) {
+  if (n_layers < 0 || batch < 0 || max_q < 0) return fail(LCA_ERR_SHAPE, "hybrid_layer_step: negative size");
+  if (n_layers == 0 || batch == 0 || max_q == 0) return ok();
+  if (!layers || !q_off || !q_pos) return fail(LCA_ERR_NULL, "hybrid_layer_step: NULL pointer");
+  const size_t need = lca_hybrid_workspace_bytes(layers, n_layers, batch, max_q, heads);
+  if (need && (!ws || ws_bytes < need)) return fail(LCA_ERR_WORKSPACE, "hybrid_layer_step: ws_bytes %zu < %zu", ws_bytes, need);
+  if (need && !al16(ws)) return fail(LCA_ERR_ALIGN, "hybrid_layer_step: ws not 16-byte aligned");
+  // validate every layer before enqueueing anything
+  for (int l = 0; l < n_layers; ++l) {
+    const lca_layer& L = layers[l];
+    if (L.kind != LCA_LAYER_CSA && L.kind != LCA_LAYER_HCA) return fail(LCA_ERR_SHAPE, "hybrid_layer_step: layer %d has unknown kind %d", l, L.kind);
+    if (L.ratio < 1 || L.max_entries < 0) return fail(LCA_ERR_SHAPE, "hybrid_layer_step: layer %d ratio/max_entries", l);
+    if (!L.q || !L.k_cmp || !L.v_cmp || !L.ent_off || !L.out) return fail(LCA_ERR_NULL, "hybrid_layer_step: layer %d NULL pointer", l);
+    if (L.kind == LCA_LAYER_CSA) {
+      if (L.topk <= 0) return fail(LCA_ERR_SHAPE, "hybrid_layer_step: layer %d topk=%d", l, L.topk);
+      if (!L.q_idx || !L.k_idx || !L.idx || !L.count) return fail(LCA_ERR_NULL, "hybrid_layer_step: CSA layer %d NULL pointer", l);
+      if (!al16(L.q_idx) || !al16(L.k_idx)) return fail(LCA_ERR_ALIGN, "hybrid_layer_step: layer %d indexer not aligned", l);
+      if ((int64_t)L.max_entries > (int64_t)lca::topk_max_chunks() * kTopkChunk) return fail(LCA_ERR_UNSUPPORTED, "hybrid_layer_step: layer %d max_entries too large", l);
+    }
+    if (head_dim != 128) return fail(LCA_ERR_UNSUPPORTED, "hybrid_layer_step: head_dim=%d (only 128)", head_dim);
+    if (!heads_supported(heads)) return fail(LCA_ERR_UNSUPPORTED, "hybrid_layer_step: heads=%d", heads);
+    if (!al16(L.q) || !al16(L.k_cmp) || !al16(L.v_cmp) || !al16(L.out)) return fail(LCA_ERR_ALIGN, "hybrid_layer_step: layer %d tensors not aligned", l);
+  }
+  if (!std::isfinite(scale)) return fail(LCA_ERR_SHAPE, "hybrid_layer_step: scale not finite");
+  const hipStream_t st = (hipStream_t)stream;
+  const int rows = batch * max_q;
+  const int sp = lca::attn_auto_splits(max_q);
+  char* p = reinterpret_cast<char*>(ws);
+  for (int l = 0; l < n_layers; ++l) {
+    const lca_layer& L = layers[l];
+    lca::AttnArgs a{};
+    a.q = L.q;
+    a.kc = L.k_cmp;
+    a.vc = L.v_cmp;
+    a.ent_off = L.ent_off;
+    a.q_off = q_off;
+    a.max_q = max_q;
+    a.heads = heads;
+    a.splits = sp;
+    a.scale_log2 = scale * 1.4426950408889634f;
+    a.out = L.out;
+    a.lse = L.lse;
+    hipError_t e;
+    if (L.kind == LCA_LAYER_CSA) {
+      const int ld = std::max((L.max_entries + 3) & ~3, 4);
+      int32_t* scores = reinterpret_cast<int32_t*>(p);
+      p += lca::align256((size_t)rows * ld * 4);
+      int32_t* n_vis = reinterpret_cast<int32_t*>(p);
+      p += lca::align256((size_t)rows * 4);
+      void* tws = p;
+      p += lca::topk_ws_bytes(rows, L.max_entries, L.topk);
+      lca::TopkWs w = lca::topk_ws_carve(tws, rows, L.max_entries, L.topk);
+      e = lca::launch_index_score(L.q_idx, q_off, q_pos, L.k_idx, L.ent_off, batch, max_q,
+                                  L.max_entries, L.ratio, scores, ld, n_vis, w.hist, st);
+      if (e == hipSuccess)
+        e = lca::launch_topk(scores, ld, rows, L.max_entries, n_vis, L.topk, L.idx, L.count, w,
+                             true, st);
+      a.idx = L.idx;
+      a.count = L.count;
+      a.k = L.topk;
+      a.ratio = 1;
+    } else {
+      a.q_pos = q_pos;
+      a.ratio = L.ratio;
+      e = hipSuccess;
+    }
+    lca::attn_ws_carve(p, rows, heads, sp, a);
+    p += lca::attn_ws_bytes(rows, heads, sp);
+    if (e == hipSuccess) e = lca::launch_attention(a, batch, L.max_entries, st);
+    if (e != hipSuccess) return fail(LCA_ERR_HIP, "hybrid_layer_step: layer %d: %s", l, hipGetErrorString(e));
+  }
+  return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,67 @@
+// Host-side interface between the C ABI (abi.cpp) and the kernel launchers.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace lca {
+
+// ------------------------------------------------------------ kv_compress
+hipError_t launch_kv_compress(const uint16_t* x, const int64_t* tok_off, int batch,
+                              int max_tokens, int head_dim, int c, uint16_t* y,
+                              const int64_t* ent_off, hipStream_t st);
+
+// ------------------------------------------------------------ index scores
+// hist != nullptr: also accumulate the first radix level for top-k into hist[rows][2048].
+hipError_t launch_index_score(const int8_t* q_idx, const int64_t* q_off, const int64_t* q_pos,
+                              const int8_t* k_idx, const int64_t* ent_off, int batch, int max_q,
+                              int max_entries, int c, int32_t* scores, int64_t ld,
+                              int32_t* n_vis, int32_t* hist, hipStream_t st);
+
+// ------------------------------------------------------------ top-k
+struct TopkWs {
+  int32_t* hist;   // [rows][2048], zero on entry and exit
+  int32_t* done;   // [rows], zero on entry and exit
+  int32_t* cnt;    // [rows][nchunks]
+  int2* cand;      // [rows][nchunks][TK_CHUNK]
+  int nchunks;
+};
+size_t topk_ws_bytes(int rows, int max_n, int k);
+TopkWs topk_ws_carve(void* ws, int rows, int max_n, int k);
+int topk_max_chunks();
+hipError_t launch_topk(const int32_t* scores, int64_t ld, int rows, int max_n,
+                       const int32_t* n_vis, int k, int32_t* idx, int32_t* count,
+                       const TopkWs& w, bool hist_ready, hipStream_t st);
+
+// ------------------------------------------------------------ attention
+struct AttnArgs {
+  const uint16_t* q;
+  const uint16_t* kc;
+  const uint16_t* vc;
+  const int64_t* ent_off;
+  const int64_t* q_off;
+  const int64_t* q_pos;    // dense only
+  const int32_t* idx;      // sparse: [rows][k]; nullptr selects the dense form
+  const int32_t* count;    // sparse
+  int32_t k;
+  int32_t ratio;           // dense visibility ratio
+  int32_t max_q;
+  int32_t heads;
+  int32_t splits;
+  float scale_log2;        // scale * log2(e)
+  uint16_t* out;
+  float* lse;
+  float* part_o;           // [rows][splits][heads][128]
+  float2* part_ml;         // [rows][splits][heads]  (running max in log2 units, sum)
+};
+int attn_auto_splits(int max_q);
+size_t attn_ws_bytes(int rows, int heads, int splits);
+void attn_ws_carve(void* ws, int rows, int heads, int splits, AttnArgs& a);
+hipError_t launch_attention(const AttnArgs& a, int batch, int max_entries_or_k, hipStream_t st);
+
+// ------------------------------------------------------------ misc
+hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t st);
+
+inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+}  // namespace lca

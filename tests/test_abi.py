@@ -1,0 +1,134 @@
+"""The C ABI library loads, exports every symbol include/lca.h declares, and
+rejects bad arguments on the host before any HIP call (no GPU needed)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import long_context_attention_19_amd as lca
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include",
+                      "lca.h")
+
+OK, E_NULL, E_SHAPE, E_ALIGN, E_UNSUP, E_WS = 0, -1, -2, -3, -4, -5
+FAKE = 0x10000          # an aligned address that validation failures never dereference
+MIS = 0x10001           # misaligned
+
+
+def declared():
+    txt = open(HEADER).read()
+    return sorted(set(re.findall(r"^(?:int32_t|size_t|const char\*)\s+(lca_\w+)\s*\(", txt, re.M)))
+
+
+def test_every_declared_symbol_is_exported():
+    names = declared()
+    assert len(names) >= 13
+    for n in names:
+        assert hasattr(lca._lib, n), n          # ctypes resolves the exported symbol
+    assert sorted(lca.EXPORTED) == names        # the binding covers exactly the header
+
+
+def test_version_and_struct_layout():
+    assert lca.abi_version() == 1
+    assert ctypes.sizeof(lca.LcaLayer) == 16 + 10 * 8
+
+
+def L():
+    return lca._lib
+
+
+def test_kv_compress_validation():
+    f = L().lca_kv_compress
+    assert f(None, None, 0, 100, 128, 4, None, None, None) == OK       # empty batch: nothing to do
+    assert f(FAKE, FAKE, 2, 100, 12, 4, FAKE, FAKE, None) == E_UNSUP   # head_dim % 8
+    assert f(FAKE, FAKE, 2, 100, 128, 0, FAKE, FAKE, None) == E_SHAPE  # ratio 0
+    assert f(None, FAKE, 2, 100, 128, 4, FAKE, FAKE, None) == E_NULL
+    assert f(MIS, FAKE, 2, 100, 128, 4, FAKE, FAKE, None) == E_ALIGN
+    assert "aligned" in lca.last_error()
+
+
+def test_index_score_validation():
+    f = L().lca_csa_index_score
+    args = [FAKE] * 5 + [2, 1, 1000, 64, 4, FAKE, 1000, FAKE, None, 0, None]
+    bad = list(args); bad[8] = 32
+    assert f(*bad) == E_UNSUP                          # d_idx != 64
+    bad = list(args); bad[11] = 999
+    assert f(*bad) == E_SHAPE                          # ld below max_entries
+    bad = list(args); bad[0] = None
+    assert f(*bad) == E_NULL
+    bad = list(args); bad[3] = MIS
+    assert f(*bad) == E_ALIGN
+    bad = list(args); bad[13] = FAKE; bad[14] = 100
+    assert f(*bad) == E_WS                             # fused histogram needs rows * 8 KiB
+
+
+def test_topk_validation_and_sizes():
+    f = L().lca_csa_topk_select
+    args = [FAKE, 4096, 4, 4096, FAKE, 256, FAKE, FAKE, FAKE, 1 << 30, 0, None]
+    bad = list(args); bad[5] = 0
+    assert f(*bad) == E_SHAPE                          # k = 0
+    bad = list(args); bad[9] = 16
+    assert f(*bad) == E_WS
+    bad = list(args); bad[10] = 7
+    assert f(*bad) == E_SHAPE                          # unknown flag
+    bad = list(args); bad[3] = 1 << 30; bad[1] = 1 << 30
+    assert f(*bad) == E_UNSUP                          # beyond the resolver's chunk table
+    bad = list(args); bad[6] = None
+    assert f(*bad) == E_NULL
+    n1 = lca.csa_topk_workspace_bytes(4, 262144, 2048)
+    n2 = lca.csa_topk_workspace_bytes(4, 2 * 262144, 2048)
+    assert 0 < n1 < n2
+
+
+def test_attention_validation():
+    f = L().lca_csa_sparse_attn
+    args = [FAKE] * 5 + [4, 1, FAKE, FAKE, 2048, 64, 128, 0.088, 0, FAKE, None, FAKE, 1 << 30, None]
+    bad = list(args); bad[11] = 64
+    assert f(*bad) == E_UNSUP                          # head_dim 64
+    for h in (8, 48, 80):
+        bad = list(args); bad[10] = h
+        assert f(*bad) == E_UNSUP                      # heads must be 16, 32 or 64k
+    bad = list(args); bad[9] = 0
+    assert f(*bad) == E_SHAPE
+    bad = list(args); bad[7] = None
+    assert f(*bad) == E_NULL
+    bad = list(args); bad[17] = 10
+    assert f(*bad) == E_WS                             # 32 splits need partial buffers
+    bad = list(args); bad[12] = float("nan")
+    assert f(*bad) == E_SHAPE
+    g = L().lca_hca_dense_attn
+    gargs = [FAKE] * 6 + [8, 1, 1024, 128, 64, 128, 0.088, 0, FAKE, None, FAKE, 1 << 30, None]
+    bad = list(gargs); bad[9] = 0
+    assert g(*bad) == E_SHAPE                          # ratio 0
+    bad = list(gargs); bad[5] = None
+    assert g(*bad) == E_NULL                           # q_pos
+    assert lca.attn_workspace_bytes(4, 64, 1, 0) == lca.attn_workspace_bytes(4, 64, 1, 32)
+    assert lca.attn_workspace_bytes(4096, 64, 4096, 0) == 0      # prefill rows are not split
+
+
+def test_hybrid_validation():
+    arr = (lca.LcaLayer * 2)()
+    arr[0] = lca.LcaLayer(lca.LCA_LAYER_CSA, 4, 2048, 1000, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                          None, FAKE, FAKE)
+    arr[1] = lca.LcaLayer(7, 128, 0, 100, FAKE, None, FAKE, FAKE, None, FAKE, FAKE, None, None,
+                          None)
+    need = lca.hybrid_workspace_bytes(arr, 16, 1, 64)
+    assert need > 0
+    f = L().lca_hybrid_layer_step
+    assert f(arr, 2, FAKE, FAKE, 16, 1, 64, 128, 0.088, FAKE, need, None) == E_SHAPE  # bad kind
+    assert f(arr, 2, FAKE, FAKE, 16, 1, 64, 128, 0.088, FAKE, need - 1, None) == E_WS
+    arr[1].kind = lca.LCA_LAYER_HCA
+    assert f(arr, 2, FAKE, FAKE, 16, 1, 64, 96, 0.088, FAKE, need, None) == E_UNSUP   # head_dim
+    arr[0].idx = None
+    assert f(arr, 2, FAKE, FAKE, 16, 1, 64, 128, 0.088, FAKE, need, None) == E_NULL
+
+
+def test_no_oracle_in_product_path():
+    # the product package never imports the oracle
+    root = os.path.dirname(os.path.abspath(lca.__file__))
+    for dp, _, fs in os.walk(root):
+        for fn in fs:
+            if fn.endswith((".py", ".hip", ".cpp", ".h")):
+                src = open(os.path.join(dp, fn)).read()
+                assert "oracle" not in src.replace("the oracle", ""), fn

@@ -5,13 +5,16 @@
 
 Prints ONE JSON line.  The default workload is the 8-layer hybrid decode stack
 (CSA on even layers, HCA on odd layers; 16 sequences with context lengths drawn
-uniformly from 65,536..1,048,576 tokens; 64 query heads on one KV head).  A
-"step" is one decode token for every sequence through all layers.  Inputs are
-seeded, synthetic and resident in HBM before timing starts.
+uniformly from 65,536..1,048,576 tokens; 64 query heads on one KV head); the
+other workloads (csa_decode_8k, hca_decode_128k, csa_decode_1m,
+csa_prefill_256k) can be named with --workload.  A step is one pass of the
+workload's whole path over one batch; inputs are seeded, synthetic and resident
+in HBM before timing starts.  Decode workloads smaller than the 256 MB
+last-level cache rotate input replicas so that each step reads from HBM.
 
 Reported: whole-step tokens/s and HBM GB/s (algorithmic bytes / step time), the
-dominant kernel's roofline (algorithmic bytes per launch / its average launch
-time, timed with HIP events on the stream it runs on) and the oracle's
+dominant kernel's roofline (algorithmic bytes or flops per launch / its average
+launch time, timed with HIP events on the stream it runs on) and the oracle's
 throughput on the host CPU for a bounded sample of the same workload.
 """
 from __future__ import annotations
@@ -26,203 +29,479 @@ import time
 
 import numpy as np
 
-HBM_PEAK_GBS = 8000.0
 ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
 METRIC = "decode tokens/s and achieved HBM GB/s (% peak), CSA+HCA at 1M ctx, 1 GPU"
+SCALE = 1.0 / math.sqrt(128)
+QO_BYTES_PER_HEAD = 128 * 2 * 2   # bf16 query row in, bf16 output row out
 
 
-def parse():
+def parse(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="hybrid_decode_1m")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample-seqs", type=int, default=16)
+    ap.add_argument("--cpu-sample", type=int, default=0, help="oracle sample size (0 = default)")
     ap.add_argument("--kernel-reps", type=int, default=50)
-    return ap.parse_args()
+    ap.add_argument("--no-graph", action="store_true",
+                    help="enqueue each step eagerly instead of replaying captured HIP graphs")
+    return ap.parse_args(argv)
 
 
-# ------------------------------------------------------------------ inputs
-def _lengths(wl):
-    from workloads import gen
-    if wl.ctx_len is not None:
-        return np.full(wl.batch, wl.ctx_len, dtype=np.int64)
-    return gen.ragged_lengths(gen.rng(wl.cfg_id, 0, gen.T_LEN), wl.batch, *wl.ctx_range)
+def _bits(t):
+    import torch
+    return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
 
 
-def _offsets(counts):
-    return np.concatenate([[0], np.cumsum(counts)]).astype(np.int64)
+def _src_hash(files):
+    h = hashlib.sha256()
+    for f in files:
+        h.update(open(os.path.join(ROOT, f), "rb").read())
+    return h.hexdigest()
 
 
-def build_hybrid(wl, torch, lca, dev):
-    """Per layer: compressed K/V drawn directly as bf16 N(0, 1/ratio), int8 indexer."""
-    from workloads import gen
-    L = _lengths(wl)
-    B, H = wl.batch, wl.heads
-    layers, host = [], []
-    for li in range(wl.n_layers):
-        csa = li % 2 == 0
-        ratio = wl.c if csa else wl.m
-        N = L // ratio
-        ent_off = _offsets(N)
-        tot = int(ent_off[-1])
-        std = 1.0 / math.sqrt(ratio)
-        d = dict(kind=lca.LCA_LAYER_CSA if csa else lca.LCA_LAYER_HCA, ratio=ratio,
-                 max_entries=int(N.max()),
-                 q=gen.device_bf16_normal((B, H, 128), gen.seed_of(wl.cfg_id, li, gen.T_Q), device=dev),
-                 k_cmp=gen.device_bf16_normal((tot, 128), gen.seed_of(wl.cfg_id, li, gen.T_CMP_K), std, dev),
-                 v_cmp=gen.device_bf16_normal((tot, 128), gen.seed_of(wl.cfg_id, li, gen.T_CMP_V), std, dev),
-                 ent_off=torch.tensor(ent_off, device=dev),
-                 out=torch.empty(B, H, 128, dtype=torch.bfloat16, device=dev),
-                 lse=torch.empty(B, H, dtype=torch.float32, device=dev))
-        if csa:
-            d.update(topk=wl.topk,
-                     k_idx=gen.device_int8_uniform((tot, 64), gen.seed_of(wl.cfg_id, li, gen.T_KIDX), dev),
-                     q_idx=gen.device_int8_uniform((B, 64), gen.seed_of(wl.cfg_id, li, gen.T_QIDX), dev))
-        layers.append(d)
-        host.append(dict(N=N, ent_off=ent_off, csa=csa, ratio=ratio))
-    return L, layers, host
-
-
-def hybrid_bytes(L, wl):
-    """Algorithmic HBM bytes of one hybrid step: indexer keys, gathered / streamed K+V,
-    queries and outputs (see the per-kernel figures in the design notes)."""
-    tot = 0
-    qo = wl.heads * 128 * 2 * 2
-    for li in range(wl.n_layers):
-        if li % 2 == 0:
-            N = L // wl.c
-            tot += int(np.sum(64 * N + np.minimum(N, wl.topk) * 512 + 64 + qo))
-        else:
-            N = L // wl.m
-            tot += int(np.sum(N * 512 + qo))
-    return tot
-
-
-# ------------------------------------------------------------------ cpu baseline
-def cpu_baseline_hybrid(wl, L, layers, host, torch, nseq):
-    """The oracle on the host for `nseq` sequences through all layers (one decode token each)."""
-    import oracle
-    try:
-        from threadpoolctl import threadpool_limits
-        limiter = threadpool_limits(limits=1)
-    except Exception:  # pragma: no cover
-        limiter = None
-    scale = 1.0 / math.sqrt(128)
-    elapsed = 0.0
-    for b in range(nseq):
-        for li, (d, h) in enumerate(zip(layers, host)):
-            s, e = int(h["ent_off"][b]), int(h["ent_off"][b + 1])
-            bits = lambda t: t.view(torch.int16).cpu().numpy().view(np.uint16)
-            Kc = oracle.bf16_bits_to_f64(bits(d["k_cmp"][s:e]))
-            Vc = oracle.bf16_bits_to_f64(bits(d["v_cmp"][s:e]))
-            q = oracle.bf16_bits_to_f64(bits(d["q"][b]))
-            if h["csa"]:
-                kidx = d["k_idx"][s:e].cpu().numpy()
-                qidx = d["q_idx"][b].cpu().numpy()
-                t0 = time.perf_counter()
-                oracle.csa_decode(q, qidx, int(L[b]), Kc, Vc, kidx, h["ratio"], wl.topk, scale)
-                elapsed += time.perf_counter() - t0
-            else:
-                t0 = time.perf_counter()
-                oracle.hca_decode(q, int(L[b]), Kc, Vc, h["ratio"], scale)
-                elapsed += time.perf_counter() - t0
-            del Kc, Vc
-    if limiter is not None:
-        limiter.unregister() if hasattr(limiter, "unregister") else None
-    return {"value": nseq / elapsed, "unit": "tokens/s", "cores": 1, "kind": "oracle",
-            "sample": f"{nseq} of {wl.batch} sequences x {wl.n_layers} layers, one decode token "
-                      f"each; oracle seconds {elapsed:.2f}, input transfer excluded, BLAS 1 thread"}
-
-
-# ------------------------------------------------------------------ profiles
-def traffic_from_profile(kernel_tag, src_files):
-    """HBM traffic per launch measured by rocprofv3 counters, if the committed
-    summary was taken on the current kernel source (matching hash); else None."""
+def traffic_from_profile(tag, src_files):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, only if
+    it was taken on the current kernel source (matching hash); else None."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(path):
         return None
     try:
-        rec = json.load(open(path)).get(kernel_tag)
+        rec = json.load(open(path)).get(tag)
     except Exception:
         return None
-    if not rec:
+    if not rec or rec.get("source_sha256") != _src_hash(src_files):
         return None
-    h = hashlib.sha256()
-    for f in src_files:
-        h.update(open(os.path.join(ROOT, f), "rb").read())
-    return rec.get("bytes_per_launch") if rec.get("source_sha256") == h.hexdigest() else None
+    return rec.get("bytes_per_launch")
 
 
-# ------------------------------------------------------------------ main
-def main():
-    args = parse()
+class _OneThread:
+    """Run the oracle with one BLAS thread so the reported core count is exact."""
+
+    def __enter__(self):
+        try:
+            from threadpoolctl import threadpool_limits
+            self._lim = threadpool_limits(limits=1)
+        except Exception:  # pragma: no cover
+            self._lim = None
+        return self
+
+    def __exit__(self, *a):
+        if self._lim is not None:
+            self._lim.restore_original_limits()
+
+
+# ====================================================================== runners
+class _Capture:
+    """One HIP graph per input replica: a step is then a single graph launch."""
+    R = 1
+
+    def capture(self):
+        torch = self.torch
+        self.step(0)                       # eager first: creates the library's streams
+        torch.cuda.synchronize()
+        graphs = []
+        for r in range(self.R):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                self.step(r)
+            graphs.append(g)
+        torch.cuda.synchronize()
+        return graphs
+
+
+class HybridRunner(_Capture):
+    """8 independent layers, CSA (even) / HCA (odd), one decode token per sequence."""
+    dominant_tag = "index_score_kernel"
+    dominant_src = ["long_context_attention_19_amd/csrc/index_score.hip"]
+
+    def __init__(self, wl, device="cuda"):
+        import torch
+        import long_context_attention_19_amd as lca
+        from long_context_attention_19_amd.pipeline import HybridStep
+        from workloads import device as wdev
+        self.wl, self.lca, self.torch = wl, lca, torch
+        self.L, self.layers = wdev.hybrid_inputs(wl, device)
+        B, H = wl.batch, wl.heads
+        specs = []
+        for d in self.layers:
+            s = dict(kind=lca.LCA_LAYER_CSA if d["csa"] else lca.LCA_LAYER_HCA, ratio=d["ratio"],
+                     max_entries=d["max_entries"], q=d["q"], k_cmp=d["k_cmp"], v_cmp=d["v_cmp"],
+                     ent_off=d["ent_off_dev"],
+                     out=torch.empty(B, H, 128, dtype=torch.bfloat16, device=device),
+                     lse=torch.empty(B, H, dtype=torch.float32, device=device))
+            if d["csa"]:
+                s.update(topk=wl.topk, k_idx=d["k_idx"], q_idx=d["q_idx"])
+            specs.append(s)
+        self.hs = HybridStep(specs, B, 1, H, device)
+        self.q_off = torch.arange(B + 1, dtype=torch.int64, device=device)
+        self.q_pos = torch.tensor(self.L, dtype=torch.int64, device=device)
+        self.tokens_per_step = B
+        # dominant kernel: CSA indexer scores (+ fused histogram), timed alone
+        csa = [d for d in self.layers if d["csa"]]
+        self._csa = csa
+        max_n = max(d["max_entries"] for d in csa)
+        self._scores = torch.empty(B, (max_n + 3) // 4 * 4, dtype=torch.int32, device=device)
+        self._nvis = torch.empty(B, dtype=torch.int32, device=device)
+        self._hws = lca.workspace(lca.csa_topk_workspace_bytes(B, max_n, wl.topk), device)
+        self._k = 0
+
+    @property
+    def outputs(self):
+        return self.hs.layers
+
+    def step(self, i=0):
+        self.hs.run(self.q_off, self.q_pos, SCALE)
+
+    def step_bytes(self):
+        wl, tot = self.wl, 0
+        for d in self.layers:
+            N = d["N"]
+            if d["csa"]:
+                tot += int(np.sum(64 * N + np.minimum(N, wl.topk) * 512 + 64))
+            else:
+                tot += int(np.sum(N * 512))
+            tot += wl.batch * wl.heads * QO_BYTES_PER_HEAD
+        return tot
+
+    def dominant_launch(self):
+        d = self._csa[self._k % len(self._csa)]
+        self._k += 1
+        self.lca.csa_index_score(d["q_idx"], self.q_off, self.q_pos, d["k_idx"], d["ent_off_dev"],
+                                 self.wl.batch, 1, d["max_entries"], self.wl.c, self._scores,
+                                 self._nvis, ws=self._hws)
+
+    def dominant_units(self):
+        n = float(np.mean([int(np.sum(d["N"])) for d in self._csa]))
+        return {"bound": "hbm", "per_launch": n * (64 + 4) + self.wl.batch * 64, "unit": "GB/s",
+                "kernel": "index_score_kernel<true>: int8 indexer scores + fused radix histogram",
+                "per_unit": "68 B per compressed entry (64 B key read, 4 B score written)"}
+
+    def cpu_baseline(self, n):
+        import oracle
+        wl, torch = self.wl, self.torch
+        n = n or wl.batch
+        t_or = 0.0
+        with _OneThread():
+            for b in range(n):
+                for d in self.layers:
+                    s, e = int(d["ent_off"][b]), int(d["ent_off"][b + 1])
+                    Kc = oracle.bf16_bits_to_f64(_bits(d["k_cmp"][s:e]))
+                    Vc = oracle.bf16_bits_to_f64(_bits(d["v_cmp"][s:e]))
+                    q = oracle.bf16_bits_to_f64(_bits(d["q"][b]))
+                    if d["csa"]:
+                        kidx, qidx = d["k_idx"][s:e].cpu().numpy(), d["q_idx"][b].cpu().numpy()
+                        t0 = time.perf_counter()
+                        oracle.csa_decode(q, qidx, int(self.L[b]), Kc, Vc, kidx, d["ratio"],
+                                          wl.topk, SCALE)
+                    else:
+                        t0 = time.perf_counter()
+                        oracle.hca_decode(q, int(self.L[b]), Kc, Vc, d["ratio"], SCALE)
+                    t_or += time.perf_counter() - t0
+        return {"value": n / t_or, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+                "sample": f"{n} of {wl.batch} sequences through all {wl.n_layers} layers, one "
+                          f"decode token each ({t_or:.1f} s of oracle time, transfers excluded)"}
+
+
+class CsaDecodeRunner(_Capture):
+    """CSA decode over caches compressed from raw tokens (compression is setup)."""
+    dominant_tag = "index_score_kernel"
+    dominant_src = ["long_context_attention_19_amd/csrc/index_score.hip"]
+
+    def __init__(self, wl, device="cuda", replicas=None):
+        import torch
+        import long_context_attention_19_amd as lca
+        from long_context_attention_19_amd.pipeline import CsaStep
+        from workloads import device as wdev
+        self.wl, self.lca, self.torch = wl, lca, torch
+        per_step = wl.batch * (wl.ctx_len // wl.c) * 64
+        R = replicas or max(1, min(16, math.ceil(1.0e9 / per_step)))
+        self.inp = wdev.decode_raw_inputs(wl, device, R)
+        inp = self.inp
+        n_tot = int(inp["ent_off"][-1])
+        self.k_cmp = torch.empty(n_tot, 128, dtype=torch.bfloat16, device=device)
+        self.v_cmp = torch.empty(n_tot, 128, dtype=torch.bfloat16, device=device)
+        T = int(inp["L"].max())
+        lca.kv_compress(inp["raw_k"], inp["tok_off_dev"], wl.batch, T, wl.c, self.k_cmp,
+                        inp["ent_off_dev"])
+        lca.kv_compress(inp["raw_v"], inp["tok_off_dev"], wl.batch, T, wl.c, self.v_cmp,
+                        inp["ent_off_dev"])
+        self.st = CsaStep(wl.batch, 1, int(inp["N"].max()), wl.heads, wl.topk, wl.c, device)
+        self.q_off = torch.arange(wl.batch + 1, dtype=torch.int64, device=device)
+        self.q_pos = torch.tensor(inp["L"], dtype=torch.int64, device=device)
+        self.out = torch.empty(wl.batch, wl.heads, 128, dtype=torch.bfloat16, device=device)
+        self.lse = torch.empty(wl.batch, wl.heads, dtype=torch.float32, device=device)
+        self.tokens_per_step = wl.batch
+        self.R = R
+
+    def step(self, i=0):
+        r = self.inp["replicas"][i % self.R]
+        self.st.run(r["q"], r["q_idx"], self.q_off, self.q_pos, r["k_idx"], self.k_cmp,
+                    self.v_cmp, self.inp["ent_off_dev"], SCALE, self.out, self.lse)
+
+    def step_bytes(self):
+        N, wl = self.inp["N"], self.wl
+        return int(np.sum(64 * N + np.minimum(N, wl.topk) * 512 + 64)) + \
+            wl.batch * wl.heads * QO_BYTES_PER_HEAD
+
+    def dominant_launch(self):
+        self._i = getattr(self, "_i", 0) + 1
+        r = self.inp["replicas"][self._i % self.R]
+        st = self.st
+        self.lca.csa_index_score(r["q_idx"], self.q_off, self.q_pos, r["k_idx"],
+                                 self.inp["ent_off_dev"], self.wl.batch, 1, st.max_entries,
+                                 self.wl.c, st.scores, st.n_vis, ws=self._dom_ws())
+
+    def _dom_ws(self):
+        if not hasattr(self, "_hws"):
+            self._hws = self.lca.workspace(self.lca.csa_topk_workspace_bytes(
+                self.wl.batch, self.st.max_entries, self.wl.topk))
+        return self._hws
+
+    def dominant_units(self):
+        n = int(np.sum(self.inp["N"]))
+        return {"bound": "hbm", "per_launch": n * (64 + 4) + self.wl.batch * 64, "unit": "GB/s",
+                "kernel": "index_score_kernel<true>: int8 indexer scores + fused radix histogram",
+                "per_unit": "68 B per compressed entry (64 B key read, 4 B score written)"}
+
+    def cpu_baseline(self, n):
+        import oracle
+        wl, inp = self.wl, self.inp
+        n = n or wl.batch
+        r = inp["replicas"][0]
+        t_or = 0.0
+        with _OneThread():
+            for b in range(n):
+                s, e = int(inp["ent_off"][b]), int(inp["ent_off"][b + 1])
+                Kc = oracle.bf16_bits_to_f64(_bits(self.k_cmp[s:e]))
+                Vc = oracle.bf16_bits_to_f64(_bits(self.v_cmp[s:e]))
+                kidx, qidx = r["k_idx"][s:e].cpu().numpy(), r["q_idx"][b].cpu().numpy()
+                q = oracle.bf16_bits_to_f64(_bits(r["q"][b]))
+                t0 = time.perf_counter()
+                oracle.csa_decode(q, qidx, int(inp["L"][b]), Kc, Vc, kidx, wl.c, wl.topk, SCALE)
+                t_or += time.perf_counter() - t0
+        return {"value": n / t_or, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+                "sample": f"{n} of {wl.batch} sequences, one decode token each over the "
+                          f"compressed cache ({t_or:.1f} s of oracle time)"}
+
+
+class HcaDecodeRunner(_Capture):
+    dominant_tag = "hca_dense_attn"
+    dominant_src = ["long_context_attention_19_amd/csrc/attention.hip"]
+
+    def __init__(self, wl, device="cuda", replicas=None):
+        import torch
+        import long_context_attention_19_amd as lca
+        from long_context_attention_19_amd.pipeline import HcaStep
+        from workloads import device as wdev
+        self.wl, self.lca, self.torch = wl, lca, torch
+        self.inp = wdev.decode_raw_inputs(wl, device, 1)
+        inp = self.inp
+        n_tot = int(inp["ent_off"][-1])
+        T = int(inp["L"].max())
+        k0 = torch.empty(n_tot, 128, dtype=torch.bfloat16, device=device)
+        v0 = torch.empty(n_tot, 128, dtype=torch.bfloat16, device=device)
+        lca.kv_compress(inp["raw_k"], inp["tok_off_dev"], wl.batch, T, wl.m, k0, inp["ent_off_dev"])
+        lca.kv_compress(inp["raw_v"], inp["tok_off_dev"], wl.batch, T, wl.m, v0, inp["ent_off_dev"])
+        per_step = n_tot * 512
+        self.R = replicas or max(1, min(256, math.ceil(1.0e9 / per_step)))
+        # replicas at distinct addresses so each step streams its caches from HBM
+        self.caches = [(k0, v0)] + [(k0.clone(), v0.clone()) for _ in range(self.R - 1)]
+        self.st = HcaStep(wl.batch, 1, int(inp["N"].max()), wl.heads, wl.m, device)
+        self.q_off = torch.arange(wl.batch + 1, dtype=torch.int64, device=device)
+        self.q_pos = torch.tensor(inp["L"], dtype=torch.int64, device=device)
+        self.out = torch.empty(wl.batch, wl.heads, 128, dtype=torch.bfloat16, device=device)
+        self.lse = torch.empty(wl.batch, wl.heads, dtype=torch.float32, device=device)
+        self.tokens_per_step = wl.batch
+
+    def step(self, i=0):
+        k, v = self.caches[i % self.R]
+        self.st.run(self.inp["replicas"][0]["q"], k, v, self.inp["ent_off_dev"], self.q_off,
+                    self.q_pos, SCALE, self.out, self.lse)
+
+    def step_bytes(self):
+        return int(np.sum(self.inp["N"])) * 512 + self.wl.batch * self.wl.heads * QO_BYTES_PER_HEAD
+
+    def dominant_launch(self):
+        self._i = getattr(self, "_i", 0) + 1
+        self.step(self._i)
+
+    def dominant_units(self):
+        return {"bound": "hbm", "per_launch": self.step_bytes(), "unit": "GB/s",
+                "kernel": "hca_dense_attn (attn_kernel + split combine)",
+                "per_unit": "512 B per visible entry (K+V bf16) + 512 B per head (q in, o out)"}
+
+    def cpu_baseline(self, n):
+        import oracle
+        wl, inp = self.wl, self.inp
+        n = n or wl.batch
+        k, v = self.caches[0]
+        t_or = 0.0
+        with _OneThread():
+            for b in range(n):
+                s, e = int(inp["ent_off"][b]), int(inp["ent_off"][b + 1])
+                Kc, Vc = oracle.bf16_bits_to_f64(_bits(k[s:e])), oracle.bf16_bits_to_f64(_bits(v[s:e]))
+                q = oracle.bf16_bits_to_f64(_bits(inp["replicas"][0]["q"][b]))
+                t0 = time.perf_counter()
+                oracle.hca_decode(q, int(inp["L"][b]), Kc, Vc, wl.m, SCALE)
+                t_or += time.perf_counter() - t0
+        return {"value": n / t_or, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+                "sample": f"{n} of {wl.batch} sequences ({t_or:.2f} s of oracle time)"}
+
+
+class PrefillRunner(_Capture):
+    """Chunked prefill: compress the new tokens into the cache, then score, select and
+    attend for every new query token under block-causal visibility."""
+    dominant_tag = "csa_sparse_attn"
+    dominant_src = ["long_context_attention_19_amd/csrc/attention.hip"]
+
+    def __init__(self, wl, device="cuda", replicas=None):
+        import torch
+        import long_context_attention_19_amd as lca
+        from long_context_attention_19_amd.pipeline import CsaStep
+        from workloads import device as wdev
+        self.wl, self.lca, self.torch = wl, lca, torch
+        self.inp = wdev.prefill_inputs(wl, device)
+        inp = self.inp
+        ctx, new, c = wl.ctx_len, wl.new_tokens, wl.c
+        self.n_ctx = ctx // c
+        self.k_cmp = torch.zeros(inp["n_ent"], 128, dtype=torch.bfloat16, device=device)
+        self.v_cmp = torch.zeros(inp["n_ent"], 128, dtype=torch.bfloat16, device=device)
+        i64 = lambda a: torch.tensor(a, dtype=torch.int64, device=device)
+        lca.kv_compress(inp["raw_k_ctx"], i64([0, ctx]), 1, ctx, c, self.k_cmp, i64([0, self.n_ctx]))
+        lca.kv_compress(inp["raw_v_ctx"], i64([0, ctx]), 1, ctx, c, self.v_cmp, i64([0, self.n_ctx]))
+        self.new_tok_off = i64([0, new])
+        self.new_ent_off = i64([0, new // c])
+        self.ent_off = i64([0, inp["n_ent"]])
+        self.q_off = i64([0, new])
+        self.q_pos = torch.arange(ctx, ctx + new, dtype=torch.int64, device=device)
+        self.st = CsaStep(1, new, inp["n_ent"], wl.heads, wl.topk, c, device)
+        self.out = torch.empty(new, wl.heads, 128, dtype=torch.bfloat16, device=device)
+        self.lse = torch.empty(new, wl.heads, dtype=torch.float32, device=device)
+        self.tokens_per_step = new
+
+    def step(self, i=0):
+        wl, inp, lca = self.wl, self.inp, self.lca
+        new, c = wl.new_tokens, wl.c
+        lca.kv_compress(inp["new_k"], self.new_tok_off, 1, new, c, self.k_cmp[self.n_ctx:],
+                        self.new_ent_off)
+        lca.kv_compress(inp["new_v"], self.new_tok_off, 1, new, c, self.v_cmp[self.n_ctx:],
+                        self.new_ent_off)
+        self.st.run(inp["q"], inp["q_idx"], self.q_off, self.q_pos, inp["k_idx"], self.k_cmp,
+                    self.v_cmp, self.ent_off, SCALE, self.out, self.lse)
+
+    def step_bytes(self):
+        wl = self.wl
+        new = wl.new_tokens
+        return (new * 128 * 2 * 2 + (new // wl.c) * 512 + self.inp["n_ent"] * 64 + new * 64 +
+                new * wl.heads * QO_BYTES_PER_HEAD + self.inp["n_ent"] * 512)
+
+    def dominant_launch(self):
+        self.st.attend(self.inp["q"], self.k_cmp, self.v_cmp, self.ent_off, self.q_off, SCALE,
+                       self.out, self.lse)
+
+    def dominant_units(self):
+        wl = self.wl
+        flops = wl.new_tokens * wl.heads * wl.topk * 128 * 4.0
+        return {"bound": "mfma", "per_launch": flops, "unit": "TFLOP/s",
+                "kernel": "csa_sparse_attn (attn_kernel, bf16 MFMA)",
+                "per_unit": "4*128 flops per (query, head, selected entry)"}
+
+    def cpu_baseline(self, n):
+        import oracle
+        wl, inp = self.wl, self.inp
+        n = n or 16
+        Kc = oracle.bf16_bits_to_f64(_bits(self.k_cmp))
+        Vc = oracle.bf16_bits_to_f64(_bits(self.v_cmp))
+        kidx = inp["k_idx"].cpu().numpy()
+        rows = np.linspace(0, wl.new_tokens - 1, n).astype(int)
+        t_or = 0.0
+        with _OneThread():
+            for i in rows:
+                q = oracle.bf16_bits_to_f64(_bits(inp["q"][i]))
+                qi = inp["q_idx"][i].cpu().numpy()
+                t0 = time.perf_counter()
+                oracle.csa_query(q, qi, wl.ctx_len + int(i), Kc, Vc, kidx, wl.c, wl.topk, SCALE)
+                t_or += time.perf_counter() - t0
+        return {"value": n / t_or, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+                "sample": f"{n} of {wl.new_tokens} query tokens after compression "
+                          f"({t_or:.1f} s of oracle time)"}
+
+
+RUNNERS = {"hybrid_decode": HybridRunner, "csa_decode": CsaDecodeRunner,
+           "hca_decode": HcaDecodeRunner, "csa_prefill": PrefillRunner}
+
+
+def make_runner(wl, device="cuda"):
+    return RUNNERS[wl.kind](wl, device)
+
+
+def _time(fn, n, stream, torch):
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for i in range(n):
+        fn(i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / n
+
+
+def main(argv=None):
+    args = parse(argv)
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; multi-GPU runs are not "
-                          "supported (--gpus must be 1)"}))
+        print(json.dumps({"error": "one GPU only: this build has no multi-GPU path; run with "
+                                   "--gpus 1"}), flush=True)
         sys.exit(2)
     import torch
-    sys.path.insert(0, ROOT)
-    import long_context_attention_19_amd as lca
-    from long_context_attention_19_amd.pipeline import HybridStep
     import workloads
 
     wl = workloads.get(args.workload)
-    if wl.kind != "hybrid_decode":
-        print(json.dumps({"error": f"bench times the hybrid decode stack; {wl.name} is covered by "
-                          "the parity tests"}))
-        sys.exit(2)
-    dev = "cuda"
     torch.cuda.init()
-    L, layers, host = build_hybrid(wl, torch, lca, dev)
-    hs = HybridStep(layers, wl.batch, 1, wl.heads, dev)
-    q_off = torch.arange(wl.batch + 1, dtype=torch.int64, device=dev)
-    q_pos = torch.tensor(L, dtype=torch.int64, device=dev)
-    scale = 1.0 / math.sqrt(128)
+    run = make_runner(wl)
     stream = torch.cuda.current_stream()
     torch.cuda.synchronize()
+    if args.no_graph:
+        step_fn = run.step
+    else:
+        graphs = run.capture()
+        step_fn = lambda i: graphs[i % len(graphs)].replay()
+    for i in range(args.warmup):
+        step_fn(i)
+    ms = _time(step_fn, args.steps, stream, torch)
+    sb = run.step_bytes()
 
-    for _ in range(args.warmup):
-        hs.run(q_off, q_pos, scale)
-    torch.cuda.synchronize()
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    ev0.record(stream)
-    for _ in range(args.steps):
-        hs.run(q_off, q_pos, scale)
-    ev1.record(stream)
-    torch.cuda.synchronize()
-    ms = ev0.elapsed_time(ev1) / args.steps
-    step_bytes = hybrid_bytes(L, wl)
-    tokens = wl.batch
-
-    # dominant kernel: the indexer score stream of the CSA layers, timed alone with the
-    # same launch shape (fused histogram on) on this stream
-    csa = [(d, h) for d, h in zip(layers, host) if h["csa"]]
-    rows = wl.batch
-    max_n = max(d["max_entries"] for d, _ in csa)
-    scores = torch.empty(rows, (max_n + 3) // 4 * 4, dtype=torch.int32, device=dev)
-    n_vis = torch.empty(rows, dtype=torch.int32, device=dev)
-    hws = lca.workspace(lca.csa_topk_workspace_bytes(rows, max_n, wl.topk))
-    for d, _ in csa:   # warm
-        lca.csa_index_score(d["q_idx"], q_off, q_pos, d["k_idx"], d["ent_off"], wl.batch, 1,
-                            d["max_entries"], wl.c, scores, n_vis, ws=hws)
-    torch.cuda.synchronize()
-    k0, k1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    k0.record(stream)
-    for r in range(args.kernel_reps):
-        d, _ = csa[r % len(csa)]
-        lca.csa_index_score(d["q_idx"], q_off, q_pos, d["k_idx"], d["ent_off"], wl.batch, 1,
-                            d["max_entries"], wl.c, scores, n_vis, ws=hws)
-    k1.record(stream)
-    torch.cuda.synchronize()
-    k_ms = k0.elapsed_time(k1) / args.kernel_reps
-    k_bytes = float(np.mean([int(np.sum(h["N"])) * (64 + 4) + rows * 64 for _, h in csa]))
-    k_gbs = k_bytes / (k_ms * 1e-3) / 1e9
-
+    # dominant kernel alone, same launch shape, same stream
+    for i in range(3):
+        run.dominant_launch()
+    k_ms = _time(lambda i: run.dominant_launch(), args.kernel_reps, stream, torch)
+    u = run.dominant_units()
+    scale_u = 1e9 if u["unit"] == "GB/s" else 1e12
+    peak = HBM_PEAK_GBS if u["bound"] == "hbm" else BF16_PEAK_TFLOPS
+    achieved = u["per_launch"] / (k_ms * 1e-3) / scale_u
+    cfg = {"workload": wl.name, "batch": wl.batch, "heads": wl.heads, "kv_heads": 1,
+           "head_dim": 128}
+    if wl.ctx_len is None:
+        cfg["ctx_len"] = f"uniform {wl.ctx_range[0]}..{wl.ctx_range[1]}"
+    else:
+        cfg["ctx_len"] = wl.ctx_len
+    if wl.kind == "hybrid_decode":
+        cfg["layers"] = f"{wl.n_layers} (CSA c={wl.c} top-k={wl.topk} d_idx=64 / HCA m={wl.m})"
+    elif wl.kind == "hca_decode":
+        cfg["m"] = wl.m
+    else:
+        cfg.update(c=wl.c, topk=wl.topk, d_idx=64)
+    if wl.new_tokens:
+        cfg["new_tokens"] = wl.new_tokens
     line = {
         "metric": METRIC,
-        "value": tokens / (ms * 1e-3),
+        "value": run.tokens_per_step / (ms * 1e-3),
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
@@ -233,24 +512,20 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16+int8",
         "data": "synthetic",
-        "config": {"workload": wl.name, "batch": wl.batch,
-                   "ctx_len": f"uniform {wl.ctx_range[0]}..{wl.ctx_range[1]} (mean {int(L.mean())})",
-                   "layers": f"{wl.n_layers} (CSA c={wl.c} top-k={wl.topk} d_idx=64 / HCA m={wl.m})",
-                   "heads": wl.heads, "kv_heads": 1, "head_dim": 128, "query_tokens": 1},
-        "hbm_gbs": step_bytes / (ms * 1e-3) / 1e9,
-        "hbm_frac": step_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
-        "step_bytes": step_bytes,
-        "roofline": {"kernel": "index_score_kernel<true> (CSA indexer scores + fused radix histogram)",
-                     "bound": "hbm", "achieved": k_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": k_gbs / HBM_PEAK_GBS, "avg_launch_us": k_ms * 1e3,
-                     "bytes_per_launch": k_bytes,
-                     "traffic": traffic_from_profile(
-                         "index_score_kernel", ["long_context_attention_19_amd/csrc/index_score.hip"])},
+        "config": cfg,
+        "launch": "eager" if args.no_graph else f"hip-graph replay ({getattr(run, 'R', 1)} replica graphs)",
+        "hbm_gbs": sb / (ms * 1e-3) / 1e9,
+        "hbm_frac": sb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+        "step_bytes": sb,
+        "roofline": {"kernel": u["kernel"], "bound": u["bound"], "achieved": achieved,
+                     "peak": peak, "unit": u["unit"], "frac": achieved / peak,
+                     "avg_launch_us": k_ms * 1e3, "per_launch": u["per_launch"],
+                     "per_unit": u["per_unit"],
+                     "traffic": traffic_from_profile(run.dominant_tag, run.dominant_src)},
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline_hybrid(wl, L, layers, host, torch,
-                                                   min(args.cpu_sample_seqs, wl.batch))
+        line["cpu_baseline"] = run.cpu_baseline(args.cpu_sample)
     print(json.dumps(line), flush=True)
 
 

@@ -17,8 +17,11 @@
  *
  * Conventions shared by every call
  *   Memory.   Every tensor pointer is DEVICE memory owned by the caller.  The
- *             library allocates nothing and keeps no state besides a per-thread
- *             error string.  Tensors are dense and row-major.  bf16 values are
+ *             library allocates no device memory.  Its only state is a
+ *             per-thread error string and, once lca_hybrid_layer_step has run on
+ *             a device, 4 internal streams + 5 events for that device (created on
+ *             first use, default priority, kept until exit).  Tensors are dense
+ *             and row-major.  bf16 values are
  *             passed as uint16_t bit patterns.  K/V/query rows and indexer rows
  *             must be 16-byte aligned (else LCA_ERR_ALIGN).
  *   Batches.  Sequences are packed.  ent_off[B+1] (device, int64) gives each
@@ -107,10 +110,11 @@ int32_t lca_kv_compress(const lca_bf16* x, const int64_t* tok_off, int32_t batch
  *            entries j < n_vis[r] hold the score, entries n_vis[r] <= j < N_b
  *            hold INT32_MIN; columns >= N_b are not written.
  *   n_vis    [rows] int32 out: min(floor(q_pos[r] / c), N_b).
- *   ws       optional top-k workspace (lca_csa_topk_workspace_bytes for the same
- *            rows, max_entries and k).  When given, the first radix pass of
- *            the following lca_csa_topk_select is fused here; that call must
- *            then pass LCA_TOPK_HIST_READY with the same workspace.
+ *   ws       optional top-k workspace, sized by lca_csa_topk_workspace_bytes(
+ *            batch * max_q, max_entries, k).  When given, the first radix pass
+ *            of the following lca_csa_topk_select (rows = batch * max_q) is fused
+ *            here; that call must then pass LCA_TOPK_HIST_READY with the same
+ *            workspace.
  *   rows     = q_off[B] must not exceed batch * max_q.
  *   d_idx == 64; ld_scores >= max_entries.
  * ------------------------------------------------------------------------- */
@@ -132,8 +136,9 @@ int32_t lca_csa_index_score(const int8_t* q_idx, const int64_t* q_off, const int
  *   idx      [rows, k] int32 out: selected entry indices in ascending order,
  *            then -1 padding.    count [rows] int32 out: min(k, n_vis[r]).
  *   flags    LCA_TOPK_HIST_READY if lca_csa_index_score already ran with ws.
- *   Radix select over a 21-bit key in two levels (2048 then 1024 bins), with a
- *   candidate list compacted in index order, so ties resolve deterministically.
+ *   Radix select over a 21-bit key in two levels (2048 then 1024 bins); each
+ *   chunk of 4096 scores places its selections from counts of the earlier
+ *   chunks, so ties resolve deterministically and no work-group waits on another.
  * ------------------------------------------------------------------------- */
 #define LCA_TOPK_HIST_READY 1u
 size_t lca_csa_topk_workspace_bytes(int32_t rows, int32_t max_n, int32_t k);
@@ -180,8 +185,11 @@ int32_t lca_hca_dense_attn(const lca_bf16* q, const lca_bf16* k_cmp, const lca_b
  * batch, CSA and HCA interleaved (page section 3-2 item 2).  Each layer has its
  * own cache and queries; a CSA layer runs index_score -> topk_select ->
  * sparse_attn, an HCA layer dense_attn, with the same kernels as the single
- * calls.  Layers are independent, so the step may run them concurrently on
- * internal streams forked from and joined back to `stream`.
+ * calls.  Layers are independent and each has its own workspace region, so with
+ * two or more layers the step forks onto the library's internal streams (layer
+ * l on stream l mod 4) after an event recorded on `stream`, and makes `stream`
+ * wait for all of them before returning: work enqueued on `stream` afterwards
+ * sees every output.  Graph capture of `stream` captures the fork and join.
  * ------------------------------------------------------------------------- */
 enum lca_layer_kind { LCA_LAYER_CSA = 0, LCA_LAYER_HCA = 1 };
 

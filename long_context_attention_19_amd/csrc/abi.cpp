@@ -6,6 +6,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <mutex>
 #include <string>
 
 #include "lca.h"
@@ -44,6 +45,35 @@ bool heads_supported(int32_t heads) {
 }
 
 constexpr int kTopkChunk = 4096;
+
+// Internal streams for running independent layers concurrently: created once per
+// device on first use, default priority, non-blocking; never destroyed.
+constexpr int kLayerStreams = 4;
+constexpr int kMaxDevices = 64;
+struct LayerStreams {
+  hipStream_t s[kLayerStreams];
+  hipEvent_t fork;
+  hipEvent_t join[kLayerStreams];
+  bool ready = false;
+};
+std::mutex g_streams_mu;
+LayerStreams g_streams[kMaxDevices];
+
+LayerStreams* layer_streams() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lk(g_streams_mu);
+  LayerStreams& ls = g_streams[dev];
+  if (!ls.ready) {
+    for (int i = 0; i < kLayerStreams; ++i) {
+      if (hipStreamCreateWithFlags(&ls.s[i], hipStreamNonBlocking) != hipSuccess) return nullptr;
+      if (hipEventCreateWithFlags(&ls.join[i], hipEventDisableTiming) != hipSuccess) return nullptr;
+    }
+    if (hipEventCreateWithFlags(&ls.fork, hipEventDisableTiming) != hipSuccess) return nullptr;
+    ls.ready = true;
+  }
+  return &ls;
+}
 
 size_t csa_layer_bytes(int rows, int max_entries, int topk, int heads, int splits) {
   const int ld = (max_entries + 3) & ~3;
@@ -106,14 +136,18 @@ int32_t lca_csa_index_score(const int8_t* q_idx, const int64_t* q_off, const int
   if (!q_idx || !q_off || !q_pos || !k_idx || !ent_off || !scores || !n_vis) return fail(LCA_ERR_NULL, "csa_index_score: NULL pointer");
   if (!al16(q_idx) || !al16(k_idx) || !al16(scores)) return fail(LCA_ERR_ALIGN, "csa_index_score: q_idx / k_idx / scores not 16-byte aligned");
   int32_t* hist = nullptr;
+  int32_t* fine = nullptr;
   if (ws) {
-    const size_t need = (size_t)batch * max_q * 2048 * 4;
+    const int rows = batch * max_q;
+    const size_t need = lca::topk_hist_region_bytes(rows);
     if (ws_bytes < need) return fail(LCA_ERR_WORKSPACE, "csa_index_score: ws_bytes %zu < %zu", ws_bytes, need);
     if (!al16(ws)) return fail(LCA_ERR_ALIGN, "csa_index_score: ws not 16-byte aligned");
-    hist = reinterpret_cast<int32_t*>(ws);   // the histogram leads the top-k workspace
+    lca::TopkWs w = lca::topk_ws_carve(ws, rows, 0, 1);   // the histograms lead the workspace
+    hist = w.hist;
+    fine = w.fine;
   }
   return hip_status(lca::launch_index_score(q_idx, q_off, q_pos, k_idx, ent_off, batch, max_q,
-                                            max_entries, c, scores, ld_scores, n_vis, hist,
+                                            max_entries, c, scores, ld_scores, n_vis, hist, fine,
                                             (hipStream_t)stream),
                     "csa_index_score launch");
 }
@@ -269,12 +303,21 @@ int32_t lca_hybrid_layer_step(const lca_layer* layers, int32_t n_layers, const i
     if (!al16(L.q) || !al16(L.k_cmp) || !al16(L.v_cmp) || !al16(L.out)) return fail(LCA_ERR_ALIGN, "hybrid_layer_step: layer %d tensors not aligned", l);
   }
   if (!std::isfinite(scale)) return fail(LCA_ERR_SHAPE, "hybrid_layer_step: scale not finite");
-  const hipStream_t st = (hipStream_t)stream;
+  const hipStream_t caller = (hipStream_t)stream;
   const int rows = batch * max_q;
   const int sp = lca::attn_auto_splits(max_q);
+  // fork: every layer has its own workspace region, so layers can run concurrently
+  LayerStreams* ls = n_layers > 1 ? layer_streams() : nullptr;
+  const int ns = ls ? std::min(kLayerStreams, (int)n_layers) : 0;
+  if (ls) {
+    if (hipEventRecord(ls->fork, caller) != hipSuccess) return fail(LCA_ERR_HIP, "hybrid_layer_step: fork record");
+    for (int i = 0; i < ns; ++i)
+      if (hipStreamWaitEvent(ls->s[i], ls->fork, 0) != hipSuccess) return fail(LCA_ERR_HIP, "hybrid_layer_step: fork wait");
+  }
   char* p = reinterpret_cast<char*>(ws);
   for (int l = 0; l < n_layers; ++l) {
     const lca_layer& L = layers[l];
+    const hipStream_t st = ls ? ls->s[l % ns] : caller;
     lca::AttnArgs a{};
     a.q = L.q;
     a.kc = L.k_cmp;
@@ -298,7 +341,7 @@ int32_t lca_hybrid_layer_step(const lca_layer* layers, int32_t n_layers, const i
       p += lca::topk_ws_bytes(rows, L.max_entries, L.topk);
       lca::TopkWs w = lca::topk_ws_carve(tws, rows, L.max_entries, L.topk);
       e = lca::launch_index_score(L.q_idx, q_off, q_pos, L.k_idx, L.ent_off, batch, max_q,
-                                  L.max_entries, L.ratio, scores, ld, n_vis, w.hist, st);
+                                  L.max_entries, L.ratio, scores, ld, n_vis, w.hist, w.fine, st);
       if (e == hipSuccess)
         e = lca::launch_topk(scores, ld, rows, L.max_entries, n_vis, L.topk, L.idx, L.count, w,
                              true, st);
@@ -314,7 +357,19 @@ int32_t lca_hybrid_layer_step(const lca_layer* layers, int32_t n_layers, const i
     lca::attn_ws_carve(p, rows, heads, sp, a);
     p += lca::attn_ws_bytes(rows, heads, sp);
     if (e == hipSuccess) e = lca::launch_attention(a, batch, L.max_entries, st);
-    if (e != hipSuccess) return fail(LCA_ERR_HIP, "hybrid_layer_step: layer %d: %s", l, hipGetErrorString(e));
+    if (e != hipSuccess) {
+      // join what was enqueued so far before reporting, so the caller's stream stays ordered
+      for (int i = 0; ls && i < ns; ++i) {
+        (void)hipEventRecord(ls->join[i], ls->s[i]);
+        (void)hipStreamWaitEvent(caller, ls->join[i], 0);
+      }
+      return fail(LCA_ERR_HIP, "hybrid_layer_step: layer %d: %s", l, hipGetErrorString(e));
+    }
+  }
+  for (int i = 0; ls && i < ns; ++i) {   // join
+    if (hipEventRecord(ls->join[i], ls->s[i]) != hipSuccess ||
+        hipStreamWaitEvent(caller, ls->join[i], 0) != hipSuccess)
+      return fail(LCA_ERR_HIP, "hybrid_layer_step: join");
   }
   return ok();
 }

@@ -20,9 +20,9 @@
 // operand is two 8-byte LDS reads per MFMA.
 //
 // Per work-group: 256 threads = 4 waves.  With HG = min(H, 64)/16 head groups,
-// wave w takes head group w % HG and entry sub-tile w / HG; a super-tile of
-// 32 * (4/HG) entries is gathered with 128-bit loads (one 256-byte row per 16
-// lanes), K row-major and V transposed into LDS, while the next super-tile's
+// wave w takes head group w % HG and entry sub-group w / HG; a super-tile of 64
+// entries (128 for H = 16) is gathered with 128-bit loads (one 256-byte row per
+// 16 lanes), K row-major and V transposed into LDS, while the next super-tile's
 // rows are already in flight in registers.  Softmax is fp32 in log2 units;
 // P is rounded to bf16 for the MFMA and the running sum uses the rounded values.
 //
@@ -94,9 +94,9 @@ __device__ __forceinline__ bool row_info(const AttnArgs& a, int supertile, RowIn
   return true;
 }
 
-template <int ES>
+template <int ES, int SUB>
 struct AttnSmem {
-  static constexpr int ST = 32 * ES;            // entries per super-tile
+  static constexpr int ST = 32 * ES * SUB;      // entries per super-tile
   static constexpr int VSTR = ST + 4;           // V^T row stride (bf16 elements)
   union {
     struct {
@@ -108,13 +108,15 @@ struct AttnSmem {
   float merge_ml[ES > 1 ? 4 : 1][16][2];
 };
 
-template <int ES>
+// ES entry sub-groups of waves; each wave takes SUB consecutive 32-entry sub-tiles
+// of every super-tile, so one super-tile (one gather round trip) covers 32*ES*SUB rows.
+template <int ES, int SUB>
 __global__ __launch_bounds__(AT_NT) void attn_kernel(AttnArgs a) {
-  constexpr int ST = AttnSmem<ES>::ST;
-  constexpr int VSTR = AttnSmem<ES>::VSTR;
+  constexpr int ST = AttnSmem<ES, SUB>::ST;
+  constexpr int VSTR = AttnSmem<ES, SUB>::VSTR;
   constexpr int NPT = ST * 16 / AT_NT;          // 16-byte row pieces per thread per matrix
   constexpr int HG = 4 / ES;                    // head groups of 16 per work-group
-  __shared__ AttnSmem<ES> sm;
+  __shared__ AttnSmem<ES, SUB> sm;
 
   RowInfo ri;
   if (!row_info(a, ST, ri)) return;
@@ -187,8 +189,10 @@ __global__ __launch_bounds__(AT_NT) void attn_kernel(AttnArgs a) {
     __syncthreads();
     if (tb + ST < e1) gather(tb + ST);   // next rows in flight during the math
 
-    const int el0 = es * 32;             // this wave's 32 entries of the super-tile
-    const int ev0 = tb + el0;            // their first entry number
+#pragma unroll
+    for (int sub = 0; sub < SUB; ++sub) {
+    const int el0 = (es * SUB + sub) * 32;   // this wave's 32 entries of the super-tile
+    const int ev0 = tb + el0;                // their first entry number
     if (ev0 < e1) {
       // S^T for two 16-entry blocks
       f32x4 sacc[2];
@@ -237,6 +241,7 @@ __global__ __launch_bounds__(AT_NT) void attn_kernel(AttnArgs a) {
         o[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf, o[db], 0, 0, 0);
       }
       m_run = m_new;
+    }
     }
   }
 
@@ -300,9 +305,12 @@ __global__ __launch_bounds__(AT_NT) void attn_kernel(AttnArgs a) {
   }
 }
 
-// Merge split partials: thread = (head, dim); partials read in piece order.
+// Merge split partials: thread = (head, dim).  Up to CB pieces are loaded at once
+// (all of them for the default split count), then merged in piece order with a
+// running maximum, so the result does not depend on load timing.
 template <int ST>
 __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
+  constexpr int CB = 32;
   RowInfo ri;
   if (!row_info(a, ST, ri)) return;
   if (ri.nsp <= 1) return;
@@ -310,15 +318,30 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
   if (head >= a.heads) return;
   const int d = threadIdx.x & 127;
   const int64_t base = ri.row * a.splits * a.heads + head;
-  float mm = -INFINITY;
-  for (int s = 0; s < ri.nsp; ++s) mm = fmaxf(mm, a.part_ml[base + (int64_t)s * a.heads].x);
-  float ll = 0.f, acc = 0.f;
-  for (int s = 0; s < ri.nsp; ++s) {
-    const int64_t slot = base + (int64_t)s * a.heads;
-    const float2 ml = a.part_ml[slot];
-    const float f = exp2f(ml.x - mm);
-    ll += ml.y * f;
-    acc += a.part_o[slot * HD + d] * f;
+  float mm = -INFINITY, ll = 0.f, acc = 0.f;
+  for (int s0 = 0; s0 < ri.nsp; s0 += CB) {
+    float2 ml[CB];
+    float ov[CB];
+#pragma unroll
+    for (int u = 0; u < CB; ++u) {
+      const bool in = s0 + u < ri.nsp;
+      const int64_t slot = base + (int64_t)(s0 + u) * a.heads;
+      ml[u] = in ? a.part_ml[slot] : make_float2(-INFINITY, 0.f);
+      ov[u] = in ? a.part_o[slot * HD + d] : 0.f;
+    }
+    float mb = mm;
+#pragma unroll
+    for (int u = 0; u < CB; ++u) mb = fmaxf(mb, ml[u].x);
+    const float r = exp2f(mm - mb);   // 0 on the first batch
+    ll *= r;
+    acc *= r;
+#pragma unroll
+    for (int u = 0; u < CB; ++u) {
+      const float f = exp2f(ml[u].x - mb);
+      ll += ml[u].y * f;
+      acc += ov[u] * f;
+    }
+    mm = mb;
   }
   a.out[(ri.row * a.heads + head) * HD + d] = (uint16_t)f32_to_bf16_bits(acc / ll);
   if (a.lse && d == 0) a.lse[ri.row * a.heads + head] = (mm + log2f(ll)) * 0.69314718055994530942f;
@@ -333,20 +356,19 @@ hipError_t launch_attention(const AttnArgs& a, int batch, int max_entries_or_k, 
   dim3 grid((unsigned)a.splits, rows_grid, (unsigned)hb);
   int st_size;
   if (hg == 4) {
-    hipLaunchKernelGGL(attn_kernel<1>, grid, dim3(AT_NT), 0, st, a);
-    st_size = 32;
+    hipLaunchKernelGGL((attn_kernel<1, 2>), grid, dim3(AT_NT), 0, st, a);
+    st_size = 64;
   } else if (hg == 2) {
-    hipLaunchKernelGGL(attn_kernel<2>, grid, dim3(AT_NT), 0, st, a);
+    hipLaunchKernelGGL((attn_kernel<2, 1>), grid, dim3(AT_NT), 0, st, a);
     st_size = 64;
   } else {
-    hipLaunchKernelGGL(attn_kernel<4>, grid, dim3(AT_NT), 0, st, a);
+    hipLaunchKernelGGL((attn_kernel<4, 1>), grid, dim3(AT_NT), 0, st, a);
     st_size = 128;
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.splits <= 1) return e;
   dim3 cgrid((unsigned)((a.heads + 1) / 2), rows_grid);
-  if (st_size == 32) hipLaunchKernelGGL(attn_combine_kernel<32>, cgrid, dim3(256), 0, st, a);
-  else if (st_size == 64) hipLaunchKernelGGL(attn_combine_kernel<64>, cgrid, dim3(256), 0, st, a);
+  if (st_size == 64) hipLaunchKernelGGL(attn_combine_kernel<64>, cgrid, dim3(256), 0, st, a);
   else hipLaunchKernelGGL(attn_combine_kernel<128>, cgrid, dim3(256), 0, st, a);
   return hipGetLastError();
 }

@@ -17,7 +17,8 @@
 //     segments and no lane picks a value by a dynamic index.
 // Optionally the first radix level of the top-k (a 2048-bin histogram of the
 // score's upper 11 bits) is built in LDS here and flushed with one global atomic
-// per non-empty bin, saving the top-k a pass over the scores.
+// per non-empty bin, saving the top-k a pass over the scores; the first group of
+// each row also zeroes the row's second-level histogram.
 #include "lca_device.h"
 #include "lca_internal.h"
 
@@ -35,7 +36,8 @@ __global__ __launch_bounds__(IS_NT) void index_score_kernel(
     const int64_t* __restrict__ q_pos, const int8_t* __restrict__ k_idx,
     const int64_t* __restrict__ ent_off, int max_q, int max_entries, int c,
     int32_t* __restrict__ scores,
-    int64_t ld, int32_t* __restrict__ n_vis_out, int32_t* __restrict__ hist) {
+    int64_t ld, int32_t* __restrict__ n_vis_out, int32_t* __restrict__ hist,
+    int32_t* __restrict__ fine) {
   __shared__ int32_t lh[HIST ? HIST_BINS : 1];
   const int b = blockIdx.y / max_q;
   const int i = blockIdx.y - b * max_q;
@@ -52,6 +54,8 @@ __global__ __launch_bounds__(IS_NT) void index_score_kernel(
   const int t = threadIdx.x;
   const int piece = t & 3;
   if (HIST) {
+    if (blockIdx.x == 0)
+      for (int k = t; k < FINE_BINS; k += IS_NT) fine[row * FINE_BINS + k] = 0;
     for (int k = t; k < HIST_BINS; k += IS_NT) lh[k] = 0;
     __syncthreads();
   }
@@ -106,16 +110,16 @@ __global__ __launch_bounds__(IS_NT) void index_score_kernel(
 hipError_t launch_index_score(const int8_t* q_idx, const int64_t* q_off, const int64_t* q_pos,
                               const int8_t* k_idx, const int64_t* ent_off, int batch, int max_q,
                               int max_entries, int c, int32_t* scores, int64_t ld,
-                              int32_t* n_vis, int32_t* hist, hipStream_t st) {
+                              int32_t* n_vis, int32_t* hist, int32_t* fine, hipStream_t st) {
   if (batch == 0 || max_q == 0) return hipSuccess;
   const int chunks = max(1, (max_entries + IS_CHUNK - 1) / IS_CHUNK);
   dim3 grid((unsigned)chunks, (unsigned)(batch * max_q));
   if (hist)
     hipLaunchKernelGGL(index_score_kernel<true>, grid, dim3(IS_NT), 0, st, q_idx, q_off, q_pos,
-                       k_idx, ent_off, max_q, max_entries, c, scores, ld, n_vis, hist);
+                       k_idx, ent_off, max_q, max_entries, c, scores, ld, n_vis, hist, fine);
   else
     hipLaunchKernelGGL(index_score_kernel<false>, grid, dim3(IS_NT), 0, st, q_idx, q_off, q_pos,
-                       k_idx, ent_off, max_q, max_entries, c, scores, ld, n_vis, hist);
+                       k_idx, ent_off, max_q, max_entries, c, scores, ld, n_vis, hist, fine);
   return hipGetLastError();
 }
 

@@ -12,21 +12,25 @@ hipError_t launch_kv_compress(const uint16_t* x, const int64_t* tok_off, int bat
                               const int64_t* ent_off, hipStream_t st);
 
 // ------------------------------------------------------------ index scores
-// hist != nullptr: also accumulate the first radix level for top-k into hist[rows][2048].
+// hist != nullptr: also build the top-k's coarse radix histogram (hist[rows][2048],
+// accumulated) and zero its fine histogram (fine[rows][1024]).
 hipError_t launch_index_score(const int8_t* q_idx, const int64_t* q_off, const int64_t* q_pos,
                               const int8_t* k_idx, const int64_t* ent_off, int batch, int max_q,
                               int max_entries, int c, int32_t* scores, int64_t ld,
-                              int32_t* n_vis, int32_t* hist, hipStream_t st);
+                              int32_t* n_vis, int32_t* hist, int32_t* fine, hipStream_t st);
 
 // ------------------------------------------------------------ top-k
 struct TopkWs {
-  int32_t* hist;   // [rows][2048], zero on entry and exit
-  int32_t* done;   // [rows], zero on entry and exit
-  int32_t* cnt;    // [rows][nchunks]
-  int2* cand;      // [rows][nchunks][TK_CHUNK]
+  int32_t* hist;       // [rows][2048] coarse histogram, zero on entry and on exit
+  int32_t* fine;       // [rows][1024] fine histogram, zeroed by the histogram pass
+  int2* rowstate;      // [rows] (threshold bin, keys above it)
+  int32_t* cnt_above;  // [rows][nchunks]
+  int32_t* cnt_bin;    // [rows][nchunks]
+  int32_t* bin_keys;   // [rows][nchunks][TK_CHUNK] threshold-bin keys of each chunk
   int nchunks;
 };
 size_t topk_ws_bytes(int rows, int max_n, int k);
+size_t topk_hist_region_bytes(int rows);   // the hist + fine prefix of the workspace
 TopkWs topk_ws_carve(void* ws, int rows, int max_n, int k);
 int topk_max_chunks();
 hipError_t launch_topk(const int32_t* scores, int64_t ld, int rows, int max_n,

@@ -6,22 +6,30 @@
 // the compressed entries.  The tie rule (lower index first) is this library's.
 //
 // Scores lie in [-2^20, 2^20), so key = score + 2^20 has 21 bits.  Two radix
-// levels pin the k-th key T exactly: 2048 bins of key >> 10, then 1024 bins of
-// key & 1023 within the threshold bin.  Every decision is a function of counts,
-// never of arrival order, so the selection is deterministic.
+// levels pin the k-th largest key T exactly: 2048 bins of key >> 10 (the coarse
+// histogram), then 1024 bins of key & 1023 among the keys of the threshold bin
+// (the fine histogram).  Every decision is a function of counts, never of the
+// order in which work-groups run, so the selection is deterministic.
 //
-// Kernels (grid = chunks of TK_CHUNK scores x rows):
-//   hist   — LDS histogram of key >> 10, one global atomic per non-empty bin
-//            (skipped when the index-score kernel already built it);
-//   select — every work-group finds the threshold bin from the histogram, then
-//            compacts its chunk's candidates (key bin >= threshold bin) in index
-//            order into a per-chunk slot.  The last work-group of a row to
-//            finish (an atomic ticket; nobody waits) resolves the row: it
-//            prefix-sums the per-chunk counts, so the candidates read back in
-//            index order, builds the second-level histogram, fixes T and the
-//            number of T-valued entries to keep, and writes the selected indices
-//            in ascending order.  It then clears the histogram and the ticket.
-// Rows with n_vis <= k select every visible entry without any of this.
+// Each row is cut into chunks of TK_CHUNK scores; every kernel's grid is
+// (chunks x rows) and work-groups never wait for one another — kernel
+// boundaries order the passes, so no work-group runs a device-scope fence:
+//   K1 hist  — coarse histogram (LDS, one global atomic per non-empty bin) and
+//              zeroing of the row's fine histogram.  The index-score kernel can
+//              do this pass while it computes the scores.
+//   K2 cand  — threshold bin bA from the coarse histogram; per chunk, the count
+//              of keys above bA, and the keys inside bA (few: ~k/8 per row for
+//              Gaussian-like scores) compacted in index order with their low 10
+//              bits, which also go to the fine histogram.
+//   K3 place — T and the number of T-valued keys to keep follow from the fine
+//              histogram; a chunk's output offset is the number of selected keys
+//              in earlier chunks: their above-bA counts plus the earlier chunks'
+//              threshold-bin keys that beat T or are T-valued within the quota.
+//              The chunk's own scores are then re-read and its selections written
+//              in index order.  The chunk-0 group clears the coarse histogram,
+//              which leaves the workspace zeroed for the next call.
+// Rows with n_vis <= k select every visible entry: K2 skips them, K3 writes
+// 0 .. n_vis-1 and -1 padding.
 #include "lca_device.h"
 #include "lca_internal.h"
 
@@ -31,8 +39,7 @@ constexpr int TK_NT = 256;
 constexpr int TK_PER_THREAD = 16;
 constexpr int TK_CHUNK = TK_NT * TK_PER_THREAD;   // 4096 scores per work-group
 constexpr int TK_MAX_CHUNKS = 1024;               // rows up to 4M entries
-constexpr int TK_LDS_CAND = 4096;                 // candidates the resolver caches in LDS
-constexpr int TK_CMP_PER_THREAD = 8;              // resolver compaction: entries per thread per block
+constexpr int TK_BATCH = 8;                       // threshold-bin keys in flight per thread
 
 int topk_max_chunks() { return TK_MAX_CHUNKS; }
 
@@ -41,10 +48,11 @@ static inline int topk_nchunks(int max_n) { return max(1, (max_n + TK_CHUNK - 1)
 size_t topk_ws_bytes(int rows, int max_n, int k) {
   (void)k;
   const size_t nc = (size_t)topk_nchunks(max_n);
-  size_t b = align256((size_t)rows * HIST_BINS * 4);
-  b += align256((size_t)rows * 4);
-  b += align256((size_t)rows * nc * 4);
-  b += align256((size_t)rows * nc * TK_CHUNK * 8);
+  size_t b = align256((size_t)rows * HIST_BINS * 4);        // coarse histogram
+  b += align256((size_t)rows * FINE_BINS * 4);               // fine histogram
+  b += align256((size_t)rows * 8);                           // (bA, above) per row
+  b += 2 * align256((size_t)rows * nc * 4);                  // per-chunk counts
+  b += align256((size_t)rows * nc * TK_CHUNK * 4);           // threshold-bin keys
   return b;
 }
 
@@ -55,15 +63,23 @@ TopkWs topk_ws_carve(void* ws, int rows, int max_n, int k) {
   char* p = reinterpret_cast<char*>(ws);
   w.hist = reinterpret_cast<int32_t*>(p);
   p += align256((size_t)rows * HIST_BINS * 4);
-  w.done = reinterpret_cast<int32_t*>(p);
-  p += align256((size_t)rows * 4);
-  w.cnt = reinterpret_cast<int32_t*>(p);
+  w.fine = reinterpret_cast<int32_t*>(p);
+  p += align256((size_t)rows * FINE_BINS * 4);
+  w.rowstate = reinterpret_cast<int2*>(p);
+  p += align256((size_t)rows * 8);
+  w.cnt_above = reinterpret_cast<int32_t*>(p);
   p += align256((size_t)rows * w.nchunks * 4);
-  w.cand = reinterpret_cast<int2*>(p);
+  w.cnt_bin = reinterpret_cast<int32_t*>(p);
+  p += align256((size_t)rows * w.nchunks * 4);
+  w.bin_keys = reinterpret_cast<int32_t*>(p);
   return w;
 }
 
-// Load this thread's 16 consecutive scores of the chunk; entries >= n read as "absent".
+size_t topk_hist_region_bytes(int rows) {
+  return align256((size_t)rows * HIST_BINS * 4) + align256((size_t)rows * FINE_BINS * 4);
+}
+
+// This thread's 16 consecutive scores of the chunk; entries >= n read as INT32_MIN.
 __device__ __forceinline__ void load16(const int32_t* srow, int64_t j0, int64_t n, int32_t v[16]) {
   if (j0 + 16 <= n) {
     const i32x4* p = reinterpret_cast<const i32x4*>(srow + j0);
@@ -81,9 +97,44 @@ __device__ __forceinline__ void load16(const int32_t* srow, int64_t j0, int64_t 
   }
 }
 
+// Threshold bin of the coarse histogram: the bin holding the k-th largest key, and
+// the number of keys in higher bins.  Thread t owns bins 2047-8t .. 2040-8t.
+__device__ __forceinline__ void coarse_threshold(const int32_t* hrow, int k, int32_t* s_scan,
+                                                 int32_t* s_b, int& bA, int& above) {
+  const int t = threadIdx.x;
+  int32_t hv[8];
+  const i32x4 lo = *reinterpret_cast<const i32x4*>(hrow + 2040 - 8 * t);
+  const i32x4 hi = *reinterpret_cast<const i32x4*>(hrow + 2044 - 8 * t);
+  hv[0] = hi[3]; hv[1] = hi[2]; hv[2] = hi[1]; hv[3] = hi[0];
+  hv[4] = lo[3]; hv[5] = lo[2]; hv[6] = lo[1]; hv[7] = lo[0];
+  int32_t hs = 0;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) hs += hv[e];
+  if (t < 2) s_b[t] = 0;   // defined even for an inconsistent histogram
+  int32_t htot;
+  const int32_t hpre = block_excl_scan<TK_NT>(hs, s_scan, &htot);
+  if (hpre < k && hpre + hs >= k) {
+    int32_t acc = hpre;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      if (acc < k && acc + hv[e] >= k) {
+        s_b[0] = 2047 - 8 * t - e;
+        s_b[1] = acc;
+      }
+      acc += hv[e];
+    }
+  }
+  __syncthreads();
+  bA = s_b[0];
+  above = s_b[1];
+  __syncthreads();
+}
+
+// ------------------------------------------------------------------ K1
 __global__ __launch_bounds__(TK_NT) void topk_hist_kernel(const int32_t* __restrict__ scores,
                                                           int64_t ld, const int32_t* __restrict__ n_vis,
-                                                          int max_n, int k, int32_t* __restrict__ hist) {
+                                                          int max_n, int k, int32_t* __restrict__ hist,
+                                                          int32_t* __restrict__ fine) {
   __shared__ int32_t lh[HIST_BINS];
   const int row = blockIdx.y;
   const int64_t n = min(n_vis[row], max_n);
@@ -91,6 +142,8 @@ __global__ __launch_bounds__(TK_NT) void topk_hist_kernel(const int32_t* __restr
   const int64_t base = (int64_t)blockIdx.x * TK_CHUNK;
   if (base >= n) return;
   const int t = threadIdx.x;
+  if (blockIdx.x == 0)
+    for (int b = t; b < FINE_BINS; b += TK_NT) fine[(int64_t)row * FINE_BINS + b] = 0;
   for (int b = t; b < HIST_BINS; b += TK_NT) lh[b] = 0;
   __syncthreads();
   int32_t v[16];
@@ -105,225 +158,216 @@ __global__ __launch_bounds__(TK_NT) void topk_hist_kernel(const int32_t* __restr
     if (lh[b]) atomicAdd(gh + b, lh[b]);
 }
 
-struct ResolveSmem {
-  int32_t prefix[TK_MAX_CHUNKS + 1];
-  int32_t fine[FINE_BINS];
-  int2 cache[TK_LDS_CAND];
-};
+// ------------------------------------------------------------------ K2
+__global__ __launch_bounds__(TK_NT) void topk_cand_kernel(
+    const int32_t* __restrict__ scores, int64_t ld, const int32_t* __restrict__ n_vis, int max_n,
+    int k, TopkWs w) {
+  __shared__ int32_t s_scan[TK_NT / WAVE + 1];
+  __shared__ int32_t s_b[2];
+  const int row = blockIdx.y;
+  const int ch = blockIdx.x;
+  const int t = threadIdx.x;
+  const int64_t n = min(n_vis[row], max_n);
+  if (n <= k) return;
+  const int nch = (int)((n + TK_CHUNK - 1) / TK_CHUNK);
+  if (ch >= nch) return;
 
-// Position p of the row's candidate sequence (index order) -> candidate.
-__device__ __forceinline__ int2 cand_at(const int2* crow, const int32_t* prefix, int nch, int p) {
-  int lo = 0, hi = nch;   // largest chunk c with prefix[c] <= p
-  while (hi - lo > 1) {
-    const int mid = (lo + hi) >> 1;
-    if (prefix[mid] <= p) lo = mid; else hi = mid;
+  const int64_t j0 = (int64_t)ch * TK_CHUNK + (int64_t)t * TK_PER_THREAD;
+  int32_t v[16];
+  load16(scores + (int64_t)row * ld, j0, n, v);   // in flight during the histogram scan
+  int bA, above;
+  coarse_threshold(w.hist + (int64_t)row * HIST_BINS, k, s_scan, s_b, bA, above);
+
+  int32_t na = 0, nb = 0;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) {
+    if (j0 + e < n) {
+      const int bin = (v[e] + KEY_BIAS) >> 10;
+      na += bin > bA ? 1 : 0;
+      nb += bin == bA ? 1 : 0;
+    }
   }
-  return crow[(int64_t)lo * TK_CHUNK + (p - prefix[lo])];
+  int32_t atot, btot;
+  (void)block_excl_scan<TK_NT>(na, s_scan, &atot);
+  int32_t off = block_excl_scan<TK_NT>(nb, s_scan, &btot);
+  const int64_t slot = (int64_t)row * w.nchunks + ch;
+  int32_t* keys = w.bin_keys + slot * TK_CHUNK;
+  int32_t* frow = w.fine + (int64_t)row * FINE_BINS;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) {
+    if (j0 + e < n) {
+      const int key = v[e] + KEY_BIAS;
+      if ((key >> 10) == bA) {
+        keys[off++] = ((t * TK_PER_THREAD + e) << 10) | (key & 1023);
+        atomicAdd(frow + (key & 1023), 1);
+      }
+    }
+  }
+  if (t == 0) {
+    w.cnt_above[slot] = atot;
+    w.cnt_bin[slot] = btot;
+    if (ch == 0) w.rowstate[row] = make_int2(bA, above);
+  }
 }
 
-__global__ __launch_bounds__(TK_NT) void topk_select_kernel(
+// ------------------------------------------------------------------ K3
+__global__ __launch_bounds__(TK_NT) void topk_place_kernel(
     const int32_t* __restrict__ scores, int64_t ld, const int32_t* __restrict__ n_vis, int max_n,
-    int k, int32_t* __restrict__ idx, int32_t* __restrict__ count, int32_t* hist, int32_t* done,
-    int32_t* cnt, int2* cand, int nchunks_alloc) {
+    int k, int32_t* __restrict__ idx, int32_t* __restrict__ count, TopkWs w) {
   __shared__ int32_t s_scan[TK_NT / WAVE + 1];
-  __shared__ int32_t s_b[4];
-  __shared__ ResolveSmem sm;
+  __shared__ int32_t s_b[2];
+  __shared__ int32_t s_pre[TK_MAX_CHUNKS + 1];   // prefix of earlier chunks' bin counts
 
   const int row = blockIdx.y;
   const int ch = blockIdx.x;
   const int t = threadIdx.x;
-  const int64_t n = min(n_vis[row], max_n);   // n_vis beyond the bound is not processed
+  const int64_t n = min(n_vis[row], max_n);
   int32_t* irow = idx + (int64_t)row * k;
-  int32_t* hrow = hist + (int64_t)row * HIST_BINS;
 
+  if (ch == 0) {   // nobody reads the coarse histogram in this kernel: clear it for the next call
+    int32_t* hrow = w.hist + (int64_t)row * HIST_BINS;
+    for (int b = t; b < HIST_BINS; b += TK_NT) hrow[b] = 0;
+    if (t == 0) count[row] = (int32_t)min(n, (int64_t)k);
+  }
   if (n <= k) {   // every visible entry is selected
     const int64_t p_end = min((int64_t)(ch + 1) * TK_CHUNK, (int64_t)k);
     for (int64_t p = (int64_t)ch * TK_CHUNK + t; p < p_end; p += TK_NT)
       irow[p] = p < n ? (int32_t)p : -1;
-    if (ch == 0) {
-      if (t == 0) count[row] = (int32_t)n;
-      for (int b = t; b < HIST_BINS; b += TK_NT) hrow[b] = 0;   // a fused histogram may exist
-    }
     return;
   }
   const int nch = (int)((n + TK_CHUNK - 1) / TK_CHUNK);
   if (ch >= nch) return;
-  if (t < 4) s_b[t] = 0;   // defined even if a caller-supplied histogram is inconsistent
-  __syncthreads();
 
-  // ---- 1. threshold bin: thread t owns bins 2047-8t .. 2040-8t (descending)
-  int32_t hv[8];
-  {
-    const i32x4 lo = *reinterpret_cast<const i32x4*>(hrow + 2040 - 8 * t);
-    const i32x4 hi = *reinterpret_cast<const i32x4*>(hrow + 2044 - 8 * t);
-    hv[0] = hi[3]; hv[1] = hi[2]; hv[2] = hi[1]; hv[3] = hi[0];
-    hv[4] = lo[3]; hv[5] = lo[2]; hv[6] = lo[1]; hv[7] = lo[0];
-  }
-  int32_t hs = 0;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) hs += hv[e];
-  int32_t htot;
-  const int32_t hpre = block_excl_scan<TK_NT>(hs, s_scan, &htot);
-  if (hpre < k && hpre + hs >= k) {
-    int32_t acc = hpre;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      if (acc + hv[e] >= k && acc < k) {
-        s_b[0] = 2047 - 8 * t - e;
-        s_b[1] = acc;
-      }
-      acc += hv[e];
-    }
-  }
-  __syncthreads();
-  const int bA = s_b[0];
-  const int above = s_b[1];
-
-  // ---- 2. this chunk's candidates, compacted in index order
+  // loads that do not depend on each other, issued together
   const int64_t j0 = (int64_t)ch * TK_CHUNK + (int64_t)t * TK_PER_THREAD;
   int32_t v[16];
   load16(scores + (int64_t)row * ld, j0, n, v);
-  int32_t nc = 0;
+  const int2 rs = w.rowstate[row];
+  const i32x4 fq = *reinterpret_cast<const i32x4*>(w.fine + (int64_t)row * FINE_BINS + 1020 - 4 * t);
+  const int64_t slot0 = (int64_t)row * w.nchunks;
+  int32_t ca[4], cb[4];
 #pragma unroll
-  for (int e = 0; e < 16; ++e) nc += (j0 + e < n && ((v[e] + KEY_BIAS) >> 10) >= bA) ? 1 : 0;
-  int32_t ctot;
-  int32_t off = block_excl_scan<TK_NT>(nc, s_scan, &ctot);
-  int2* crow = cand + (int64_t)row * nchunks_alloc * TK_CHUNK;
-  int2* cslot = crow + (int64_t)ch * TK_CHUNK;
+  for (int e = 0; e < 4; ++e) {
+    const int c = 4 * t + e;
+    ca[e] = c < ch ? w.cnt_above[slot0 + c] : 0;
+    cb[e] = c < ch ? w.cnt_bin[slot0 + c] : 0;
+  }
+  const int bA = rs.x;
+  const int need = k - rs.y;   // keys still to take from the threshold bin (>= 1)
+
+  // fine threshold: thread t owns fine bins 1023-4t .. 1020-4t (descending)
+  int32_t fv[4] = {fq[3], fq[2], fq[1], fq[0]};
+  if (t < 2) s_b[t] = 0;
+  int32_t fs = fv[0] + fv[1] + fv[2] + fv[3];
+  int32_t ftot;
+  const int32_t fpre = block_excl_scan<TK_NT>(fs, s_scan, &ftot);
+  if (fpre < need && fpre + fs >= need) {
+    int32_t acc = fpre;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      if (acc < need && acc + fv[e] >= need) {
+        s_b[0] = 1023 - 4 * t - e;
+        s_b[1] = acc;
+      }
+      acc += fv[e];
+    }
+  }
+  __syncthreads();
+  const int low_t = s_b[0];
+  const int T = (bA << 10) | low_t;       // the k-th largest key
+  const int need_eq = need - s_b[1];      // T-valued keys to keep, lowest indices first
+
+  // earlier chunks: above-bA totals, and a prefix of their threshold-bin counts
+  int32_t sa = ca[0] + ca[1] + ca[2] + ca[3];
+  int32_t sb = cb[0] + cb[1] + cb[2] + cb[3];
+  int32_t above_before;
+  (void)block_excl_scan<TK_NT>(sa, s_scan, &above_before);
+  int32_t bin_before;
+  int32_t bpre = block_excl_scan<TK_NT>(sb, s_scan, &bin_before);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int c = 4 * t + e;
+    if (c < ch) s_pre[c] = bpre;
+    bpre += cb[e];
+  }
+  if (t == 0) s_pre[ch] = bin_before;
+  __syncthreads();
+
+  // earlier chunks' threshold-bin keys: how many beat T, how many equal it
+  int32_t gt = 0, eq = 0;
+  for (int base = 0; base < bin_before; base += TK_NT * TK_BATCH) {
+    int32_t kv[TK_BATCH];
+#pragma unroll
+    for (int u = 0; u < TK_BATCH; ++u) {
+      const int p = base + t + TK_NT * u;
+      kv[u] = -1;
+      if (p < bin_before) {
+        int lo = 0, hi = ch;   // chunk c with s_pre[c] <= p < s_pre[c+1]
+        while (hi - lo > 1) {
+          const int mid = (lo + hi) >> 1;
+          if (s_pre[mid] <= p) lo = mid; else hi = mid;
+        }
+        kv[u] = w.bin_keys[(slot0 + lo) * TK_CHUNK + (p - s_pre[lo])];
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < TK_BATCH; ++u) {
+      if (kv[u] >= 0) {
+        const int low = kv[u] & 1023;
+        gt += low > low_t ? 1 : 0;
+        eq += low == low_t ? 1 : 0;
+      }
+    }
+  }
+  int32_t gt_before, eq_before;
+  (void)block_excl_scan<TK_NT>(gt, s_scan, &gt_before);
+  (void)block_excl_scan<TK_NT>(eq, s_scan, &eq_before);
+  const int32_t sel_before = above_before + gt_before + min(eq_before, need_eq);
+
+  // this chunk, in index order
+  int32_t ne = 0;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) ne += (j0 + e < n && v[e] + KEY_BIAS == T) ? 1 : 0;
+  int32_t etot;
+  int32_t rank = eq_before + block_excl_scan<TK_NT>(ne, s_scan, &etot);
+  uint32_t selmask = 0;
+  int32_t ns = 0;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) {
+    if (j0 + e < n) {
+      const int key = v[e] + KEY_BIAS;
+      bool sel = key > T;
+      if (key == T) sel = rank++ < need_eq;
+      if (sel) {
+        selmask |= 1u << e;
+        ++ns;
+      }
+    }
+  }
+  int32_t stot;
+  int32_t pos = sel_before + block_excl_scan<TK_NT>(ns, s_scan, &stot);
 #pragma unroll
   for (int e = 0; e < 16; ++e)
-    if (j0 + e < n && ((v[e] + KEY_BIAS) >> 10) >= bA) cslot[off++] = make_int2((int)(j0 + e), v[e]);
-  if (t == 0) cnt[(int64_t)row * nchunks_alloc + ch] = ctot;
-
-  // ---- 3. ticket: the last work-group of this row resolves it
-  __threadfence();
-  __syncthreads();
-  if (t == 0) s_b[2] = (atomicAdd(done + row, 1) == nch - 1) ? 1 : 0;
-  __syncthreads();
-  if (!s_b[2]) return;
-  __threadfence();
-
-  // prefix of per-chunk counts: thread t owns chunks 4t .. 4t+3
-  {
-    int32_t cv[4];
-    int32_t cs = 0;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int c = 4 * t + e;
-      cv[e] = c < nch ? __hip_atomic_load(cnt + (int64_t)row * nchunks_alloc + c, __ATOMIC_RELAXED,
-                                          __HIP_MEMORY_SCOPE_AGENT)
-                      : 0;
-      cs += cv[e];
+    if (selmask & (1u << e)) {
+      if (pos < k) irow[pos] = (int32_t)(j0 + e);   // exactly k in total; the bound guards bad input
+      ++pos;
     }
-    int32_t tot;
-    int32_t pre = block_excl_scan<TK_NT>(cs, s_scan, &tot);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int c = 4 * t + e;
-      if (c < nch) sm.prefix[c] = pre;
-      pre += cv[e];
-    }
-    if (t == 0) sm.prefix[nch] = tot;
-  }
-  for (int b = t; b < FINE_BINS; b += TK_NT) sm.fine[b] = 0;
-  __syncthreads();
-  const int ctotal = sm.prefix[nch];
-  const bool cached = ctotal <= TK_LDS_CAND;
-
-  // second level: histogram of key & 1023 over candidates in the threshold bin
-  for (int p = t; p < ctotal; p += TK_NT) {
-    const int2 c = cand_at(crow, sm.prefix, nch, p);
-    if (cached) sm.cache[p] = c;
-    const int key = c.y + KEY_BIAS;
-    if ((key >> 10) == bA) atomicAdd(&sm.fine[key & 1023], 1);
-  }
-  __syncthreads();
-  const int need = k - above;   // >= 1 entries still to take from the threshold bin
-  {
-    int32_t fv[4];
-    int32_t fs = 0;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      fv[e] = sm.fine[1023 - 4 * t - e];
-      fs += fv[e];
-    }
-    int32_t ftot;
-    const int32_t fpre = block_excl_scan<TK_NT>(fs, s_scan, &ftot);
-    if (fpre < need && fpre + fs >= need) {
-      int32_t acc = fpre;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        if (acc + fv[e] >= need && acc < need) {
-          s_b[0] = 1023 - 4 * t - e;
-          s_b[1] = acc;
-        }
-        acc += fv[e];
-      }
-    }
-  }
-  __syncthreads();
-  const int T = (bA << 10) | s_b[0];          // the k-th largest key
-  const int need_eq = need - s_b[1];          // entries with key == T to keep (lowest indices)
-
-  // ---- 4. compaction in index order
-  int32_t sel_before = 0, eq_before = 0;
-  for (int blk = 0; blk < ctotal; blk += TK_NT * TK_CMP_PER_THREAD) {
-    int2 c[TK_CMP_PER_THREAD];
-    int32_t ne = 0;
-#pragma unroll
-    for (int e = 0; e < TK_CMP_PER_THREAD; ++e) {
-      const int p = blk + t * TK_CMP_PER_THREAD + e;
-      if (p < ctotal) c[e] = cached ? sm.cache[p] : cand_at(crow, sm.prefix, nch, p);
-      else c[e] = make_int2(-1, INT32_MIN);
-      ne += (p < ctotal && c[e].y + KEY_BIAS == T) ? 1 : 0;
-    }
-    int32_t etot;
-    int32_t rank = eq_before + block_excl_scan<TK_NT>(ne, s_scan, &etot);
-    int32_t ns = 0;
-    uint32_t selmask = 0;
-#pragma unroll
-    for (int e = 0; e < TK_CMP_PER_THREAD; ++e) {
-      const int p = blk + t * TK_CMP_PER_THREAD + e;
-      const int key = c[e].y + KEY_BIAS;
-      bool sel = false;
-      if (p < ctotal) {
-        if (key > T) sel = true;
-        else if (key == T) sel = (rank++ < need_eq);
-      }
-      if (sel) { selmask |= 1u << e; ++ns; }
-    }
-    int32_t stot;
-    int32_t pos = sel_before + block_excl_scan<TK_NT>(ns, s_scan, &stot);
-#pragma unroll
-    for (int e = 0; e < TK_CMP_PER_THREAD; ++e)
-      if (selmask & (1u << e)) {
-        if (pos < k) irow[pos] = c[e].x;   // exactly k are selected; the bound guards bad input
-        ++pos;
-      }
-    sel_before += stot;
-    eq_before += etot;
-  }
-  if (t == 0) {
-    count[row] = k;
-    done[row] = 0;
-  }
-  for (int b = t; b < HIST_BINS; b += TK_NT) hrow[b] = 0;
 }
 
 hipError_t launch_topk(const int32_t* scores, int64_t ld, int rows, int max_n, const int32_t* n_vis,
                        int k, int32_t* idx, int32_t* count, const TopkWs& w, bool hist_ready,
                        hipStream_t st) {
   if (rows == 0) return hipSuccess;
-  if (!hist_ready) {
-    dim3 g((unsigned)topk_nchunks(max_n), (unsigned)rows);
-    hipLaunchKernelGGL(topk_hist_kernel, g, dim3(TK_NT), 0, st, scores, ld, n_vis, max_n, k,
-                       w.hist);
-  }
+  const unsigned nch = (unsigned)topk_nchunks(max_n);
+  if (!hist_ready)
+    hipLaunchKernelGGL(topk_hist_kernel, dim3(nch, rows), dim3(TK_NT), 0, st, scores, ld, n_vis,
+                       max_n, k, w.hist, w.fine);
+  hipLaunchKernelGGL(topk_cand_kernel, dim3(nch, rows), dim3(TK_NT), 0, st, scores, ld, n_vis,
+                     max_n, k, w);
   const int span = max(max_n, k);
-  dim3 g((unsigned)max(1, (span + TK_CHUNK - 1) / TK_CHUNK), (unsigned)rows);
-  hipLaunchKernelGGL(topk_select_kernel, g, dim3(TK_NT), 0, st, scores, ld, n_vis, max_n, k, idx,
-                     count,
-                     w.hist, w.done, w.cnt, w.cand, w.nchunks);
+  const unsigned pch = (unsigned)max(1, (span + TK_CHUNK - 1) / TK_CHUNK);
+  hipLaunchKernelGGL(topk_place_kernel, dim3(pch, rows), dim3(TK_NT), 0, st, scores, ld, n_vis,
+                     max_n, k, idx, count, w);
   return hipGetLastError();
 }
 

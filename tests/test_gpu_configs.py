@@ -1,0 +1,165 @@
+"""GPU parity at the workloads' full sizes, in the launch configuration bench.py
+times (its runners build and launch exactly what it measures).
+
+Every workload is checked against the fp64 oracle: index sets and counts
+bit-exact, compressed entries bit-exact, attention within rel-L2 <= 1e-2 and
+max-abs <= 2e-2.  Where the oracle would need minutes for every row, a seeded
+sample of rows (always including the first and last) is compared and
+properties that hold at any size are checked on every row."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import bench
+import oracle
+import workloads
+from gpu_util import assert_attn_close, assert_lse_close, bf16_bits, step
+
+pytestmark = pytest.mark.gpu
+SCALE = 1.0 / math.sqrt(128)
+
+
+def _f64(t):
+    return oracle.bf16_bits_to_f64(bf16_bits(t))
+
+
+def _check_compress_sample(raw, tok_off, ent_off, cache, c, nsample, seed):
+    """Compressed entries j of sequence b equal the oracle mean of their c raw tokens."""
+    g = np.random.default_rng(seed)
+    for b in range(len(tok_off) - 1):
+        n = int(ent_off[b + 1] - ent_off[b])
+        js = np.unique(np.concatenate([[0, n - 1], g.integers(0, n, nsample)]))
+        tok = (int(tok_off[b]) + js[:, None] * c + np.arange(c)[None, :]).reshape(-1)
+        rawb = _f64(raw[torch.from_numpy(tok).to(raw.device)]).reshape(len(js), c, 128)
+        ref = np.stack([oracle.csa_hca.compress_to_cache(rawb[i], c)[0] for i in range(len(js))])
+        got = bf16_bits(cache[torch.from_numpy(int(ent_off[b]) + js).to(cache.device)])
+        assert np.array_equal(got, ref), f"sequence {b}"
+
+
+def _check_csa_row(q, qidx, pos, k_cmp, v_cmp, kidx_host, c, topk, idx, cnt, out, lse, what):
+    """One CSA query row: scores -> top-k (bit-exact) -> attention, the selected K/V rows
+    fetched from the device cache by the oracle's own indices."""
+    n_vis = oracle.n_visible(pos, c, kidx_host.shape[0])
+    sel = oracle.topk_select(oracle.index_scores(qidx, kidx_host), n_vis, topk)
+    assert cnt == len(sel), what
+    assert np.array_equal(idx[:cnt], sel), what
+    assert np.all(idx[cnt:] == -1), what
+    rows = torch.from_numpy(sel).to(k_cmp.device)
+    o, l, _ = oracle.attention(q, _f64(k_cmp[rows]), _f64(v_cmp[rows]), SCALE)
+    assert_attn_close(out, o, what)
+    assert_lse_close(lse, l, what)
+
+
+@pytest.mark.parametrize("name", ["csa_decode_8k", "csa_decode_1m"])
+def test_csa_decode_full(name):
+    step(f"full-size {name}")
+    wl = workloads.get(name)
+    run = bench.CsaDecodeRunner(wl, replicas=2)
+    run.step(0)
+    torch.cuda.synchronize()
+    inp = run.inp
+    _check_compress_sample(inp["raw_k"], inp["tok_off"], inp["ent_off"], run.k_cmp, wl.c, 2048, 1)
+    _check_compress_sample(inp["raw_v"], inp["tok_off"], inp["ent_off"], run.v_cmp, wl.c, 2048, 2)
+    r = inp["replicas"][0]
+    idx, cnt = run.st.idx.cpu().numpy(), run.st.count.cpu().numpy()
+    out, lse = _f64(run.out), run.lse.cpu().numpy()
+    for b in range(wl.batch):
+        s, e = int(inp["ent_off"][b]), int(inp["ent_off"][b + 1])
+        _check_csa_row(_f64(r["q"][b]), r["q_idx"][b].cpu().numpy(), int(inp["L"][b]),
+                       run.k_cmp[s:e], run.v_cmp[s:e], r["k_idx"][s:e].cpu().numpy(), wl.c,
+                       wl.topk, idx[b], cnt[b], out[b], lse[b], f"{name} seq {b}")
+    # a second replica (different indexer inputs) in the same launch shape
+    run.step(1)
+    torch.cuda.synchronize()
+    r = inp["replicas"][1]
+    idx, cnt = run.st.idx.cpu().numpy(), run.st.count.cpu().numpy()
+    out, lse = _f64(run.out), run.lse.cpu().numpy()
+    b = wl.batch - 1
+    s, e = int(inp["ent_off"][b]), int(inp["ent_off"][b + 1])
+    _check_csa_row(_f64(r["q"][b]), r["q_idx"][b].cpu().numpy(), int(inp["L"][b]),
+                   run.k_cmp[s:e], run.v_cmp[s:e], r["k_idx"][s:e].cpu().numpy(), wl.c, wl.topk,
+                   idx[b], cnt[b], out[b], lse[b], f"{name} replica 1 seq {b}")
+
+
+def test_hca_decode_full():
+    step("full-size hca_decode_128k")
+    wl = workloads.get("hca_decode_128k")
+    run = bench.HcaDecodeRunner(wl, replicas=2)
+    inp = run.inp
+    k, v = run.caches[0]
+    # every compressed entry, bit-exact
+    for raw, cache in ((inp["raw_k"], k), (inp["raw_v"], v)):
+        got = bf16_bits(cache)
+        for b in range(wl.batch):
+            rb = _f64(raw[int(inp["tok_off"][b]):int(inp["tok_off"][b + 1])])
+            ref = oracle.csa_hca.compress_to_cache(rb, wl.m)
+            assert np.array_equal(got[inp["ent_off"][b]:inp["ent_off"][b + 1]], ref), f"seq {b}"
+    for rep in (0, 1):
+        run.step(rep)
+        torch.cuda.synchronize()
+        out, lse = _f64(run.out), run.lse.cpu().numpy()
+        kk, vv = run.caches[rep]
+        for b in range(wl.batch):
+            s, e = int(inp["ent_off"][b]), int(inp["ent_off"][b + 1])
+            ref = oracle.hca_decode(_f64(inp["replicas"][0]["q"][b]), int(inp["L"][b]),
+                                    _f64(kk[s:e]), _f64(vv[s:e]), wl.m, SCALE)
+            assert_attn_close(out[b], ref["o"], f"replica {rep} seq {b}")
+            assert_lse_close(lse[b], ref["lse"], f"replica {rep} seq {b}")
+
+
+def test_hybrid_full():
+    step("full-size hybrid_decode_1m")
+    wl = workloads.get("hybrid_decode_1m")
+    run = bench.HybridRunner(wl)
+    run.step(0)
+    torch.cuda.synchronize()
+    for li, (d, spec) in enumerate(zip(run.layers, run.outputs)):
+        out, lse = _f64(spec["out"]), spec["lse"].cpu().numpy()
+        if d["csa"]:
+            idx, cnt = spec["idx"].cpu().numpy(), spec["count"].cpu().numpy()
+        for b in range(wl.batch):
+            s, e = int(d["ent_off"][b]), int(d["ent_off"][b + 1])
+            q = _f64(d["q"][b])
+            what = f"layer {li} seq {b}"
+            if d["csa"]:
+                _check_csa_row(q, d["q_idx"][b].cpu().numpy(), int(run.L[b]), d["k_cmp"][s:e],
+                               d["v_cmp"][s:e], d["k_idx"][s:e].cpu().numpy(), d["ratio"],
+                               wl.topk, idx[b], cnt[b], out[b], lse[b], what)
+            else:
+                ref = oracle.hca_decode(q, int(run.L[b]), _f64(d["k_cmp"][s:e]),
+                                        _f64(d["v_cmp"][s:e]), d["ratio"], SCALE)
+                assert_attn_close(out[b], ref["o"], what)
+                assert_lse_close(lse[b], ref["lse"], what)
+
+
+def test_prefill_full():
+    step("full-size csa_prefill_256k")
+    wl = workloads.get("csa_prefill_256k")
+    run = bench.PrefillRunner(wl)
+    run.step(0)
+    torch.cuda.synchronize()
+    inp = run.inp
+    n_ctx, new, c = run.n_ctx, wl.new_tokens, wl.c
+    # the appended entries: every one bit-exact
+    for raw, cache in ((inp["new_k"], run.k_cmp), (inp["new_v"], run.v_cmp)):
+        ref = oracle.csa_hca.compress_to_cache(_f64(raw), c)
+        assert np.array_equal(bf16_bits(cache[n_ctx:]), ref)
+    idx, cnt = run.st.idx.cpu().numpy(), run.st.count.cpu().numpy()
+    # every row: k entries, ascending, unique, all visible under the block-causal rule
+    nvis = np.array([oracle.n_visible(wl.ctx_len + i, c, inp["n_ent"]) for i in range(new)])
+    assert np.all(cnt == wl.topk)
+    assert np.all(np.diff(idx, axis=1) > 0)
+    assert np.all(idx[:, -1] < nvis)
+    assert np.all(idx[:, 0] >= 0)
+    # sampled rows against the oracle
+    kidx = inp["k_idx"].cpu().numpy()
+    out, lse = _f64(run.out), run.lse.cpu().numpy()
+    g = np.random.default_rng(4)
+    rows = np.unique(np.concatenate([[0, 1, 2, 3, 4, new - 4, new - 3, new - 2, new - 1],
+                                     g.integers(0, new, 15)]))
+    for i in rows:
+        _check_csa_row(_f64(inp["q"][i]), inp["q_idx"][i].cpu().numpy(), wl.ctx_len + int(i),
+                       run.k_cmp, run.v_cmp, kidx, c, wl.topk, idx[i], cnt[i], out[i], lse[i],
+                       f"prefill row {i}")

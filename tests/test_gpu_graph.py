@@ -1,0 +1,101 @@
+"""HIP-graph capture of the composed steps: several replays, with the program's
+own eager work and synchronizations between them, each bitwise equal to the
+eager result (the kernels keep their workspace invariants across replays)."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import long_context_attention_19_amd as lca
+from long_context_attention_19_amd.pipeline import CsaStep, HybridStep
+from workloads import bf16_normal, int8_uniform, rng
+
+from gpu_util import DEV, bf16_dev, i64_dev, i8_dev, offsets, step
+
+pytestmark = pytest.mark.gpu
+SCALE = 1.0 / math.sqrt(128)
+
+
+def _same(a, b):
+    return torch.equal(a.view(torch.int16) if a.dtype == torch.bfloat16 else a,
+                       b.view(torch.int16) if b.dtype == torch.bfloat16 else b)
+
+
+def test_csa_step_graph_replays():
+    step("graph: CsaStep")
+    g = rng(300, 0, 0)
+    Ns, heads, c, k = [20000, 3000, 9001], 64, 4, 1024
+    B = len(Ns)
+    ent_off = offsets(Ns)
+    tot = int(ent_off[-1])
+    t = dict(q=bf16_dev(bf16_normal(g, (B, heads, 128))), q_idx=i8_dev(int8_uniform(g, (B, 64))),
+             k_idx=i8_dev(int8_uniform(g, (tot, 64))), Kc=bf16_dev(bf16_normal(g, (tot, 128))),
+             Vc=bf16_dev(bf16_normal(g, (tot, 128))), ent_off=i64_dev(ent_off),
+             q_off=i64_dev(np.arange(B + 1)), q_pos=i64_dev([n * c for n in Ns]))
+    st = CsaStep(B, 1, max(Ns), heads, k, c)
+    out = torch.empty(B, heads, 128, dtype=torch.bfloat16, device=DEV)
+    lse = torch.empty(B, heads, dtype=torch.float32, device=DEV)
+
+    def run():
+        st.run(t["q"], t["q_idx"], t["q_off"], t["q_pos"], t["k_idx"], t["Kc"], t["Vc"],
+               t["ent_off"], SCALE, out, lse)
+
+    run()
+    torch.cuda.synchronize()
+    ref = (out.clone(), lse.clone(), st.idx.clone(), st.count.clone())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        run()
+    for rep in range(4):
+        out.zero_(); lse.zero_(); st.idx.fill_(-9)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert _same(out, ref[0]) and _same(lse, ref[1]), rep
+        assert torch.equal(st.idx, ref[2]) and torch.equal(st.count, ref[3]), rep
+        run()   # eager work between replays, on the same workspaces
+        torch.cuda.synchronize()
+        assert _same(out, ref[0]) and torch.equal(st.idx, ref[2]), rep
+
+
+def test_hybrid_step_graph_replays():
+    step("graph: HybridStep (forks onto the library's streams)")
+    g = rng(301, 0, 0)
+    L = [70000, 300000, 5000]
+    B, heads = len(L), 64
+    layers = []
+    for li in range(4):
+        csa = li % 2 == 0
+        ratio = 4 if csa else 128
+        Ns = [x // ratio for x in L]
+        ent_off = offsets(Ns)
+        tot = int(ent_off[-1])
+        d = dict(kind=lca.LCA_LAYER_CSA if csa else lca.LCA_LAYER_HCA, ratio=ratio,
+                 max_entries=max(Ns), q=bf16_dev(bf16_normal(g, (B, heads, 128))),
+                 k_cmp=bf16_dev(bf16_normal(g, (tot, 128))),
+                 v_cmp=bf16_dev(bf16_normal(g, (tot, 128))), ent_off=i64_dev(ent_off),
+                 out=torch.empty(B, heads, 128, dtype=torch.bfloat16, device=DEV),
+                 lse=torch.empty(B, heads, dtype=torch.float32, device=DEV))
+        if csa:
+            d.update(topk=2048, k_idx=i8_dev(int8_uniform(g, (tot, 64))),
+                     q_idx=i8_dev(int8_uniform(g, (B, 64))))
+        layers.append(d)
+    hs = HybridStep(layers, B, 1, heads)
+    q_off, q_pos = i64_dev(np.arange(B + 1)), i64_dev(L)
+    hs.run(q_off, q_pos, SCALE)
+    torch.cuda.synchronize()
+    ref = [(L_["out"].clone(), L_["lse"].clone()) for L_ in hs.layers]
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        hs.run(q_off, q_pos, SCALE)
+    scratch = torch.randn(1 << 20, device=DEV)
+    for rep in range(4):
+        for L_ in hs.layers:
+            L_["out"].zero_(); L_["lse"].zero_()
+        scratch.mul_(1.0001)   # unrelated eager work on the default stream
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for li, L_ in enumerate(hs.layers):
+            assert _same(L_["out"], ref[li][0]) and _same(L_["lse"], ref[li][1]), (rep, li)

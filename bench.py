@@ -49,6 +49,8 @@ def parse(argv=None):
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample", type=int, default=0, help="oracle sample size (0 = default)")
     ap.add_argument("--kernel-reps", type=int, default=50)
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
+                    help="only run 10 plain device copies of BYTES bytes (counter calibration)")
     ap.add_argument("--no-graph", action="store_true",
                     help="enqueue each step eagerly instead of replaying captured HIP graphs")
     return ap.parse_args(argv)
@@ -462,6 +464,14 @@ def main(argv=None):
     import torch
     import workloads
 
+    if args.copy_probe:
+        a = torch.ones(args.copy_probe, dtype=torch.uint8, device="cuda")
+        b = torch.empty_like(a)
+        stream = torch.cuda.current_stream()
+        ms = _time(lambda i: b.copy_(a), 10, stream, torch)
+        print(json.dumps({"copy_probe_bytes": args.copy_probe, "ms": ms,
+                          "gbs_read_plus_write": 2 * args.copy_probe / (ms * 1e-3) / 1e9}), flush=True)
+        return
     wl = workloads.get(args.workload)
     torch.cuda.init()
     run = make_runner(wl)

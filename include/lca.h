@@ -187,9 +187,12 @@ int32_t lca_hca_dense_attn(const lca_bf16* q, const lca_bf16* k_cmp, const lca_b
  * sparse_attn, an HCA layer dense_attn, with the same kernels as the single
  * calls.  Layers are independent and each has its own workspace region, so with
  * two or more layers the step forks onto the library's internal streams (layer
- * l on stream l mod 4) after an event recorded on `stream`, and makes `stream`
+ * pair l/2 on stream (l/2) mod 4) after an event recorded on `stream`, and makes `stream`
  * wait for all of them before returning: work enqueued on `stream` afterwards
  * sees every output.  Graph capture of `stream` captures the fork and join.
+ * With L concurrent layers the attention uses 32 / min(L, 4) splits per row
+ * (decode), a function of the layer count only, so a row's bits still do not
+ * depend on the rest of the batch.
  * ------------------------------------------------------------------------- */
 enum lca_layer_kind { LCA_LAYER_CSA = 0, LCA_LAYER_HCA = 1 };
 

@@ -75,6 +75,15 @@ LayerStreams* layer_streams() {
   return &ls;
 }
 
+// Split count of the hybrid step's attention: with up to 4 layers in flight at once
+// each layer needs fewer work-groups per row, and fewer splits mean fewer partials.
+// It depends on the layer count and query count only, never on the batch.
+int hybrid_splits(int n_layers, int max_q) {
+  const int base = lca::attn_auto_splits(max_q);
+  const int conc = std::min(std::max(n_layers, 1), kLayerStreams);
+  return std::max(1, base / conc);
+}
+
 size_t csa_layer_bytes(int rows, int max_entries, int topk, int heads, int splits) {
   const int ld = (max_entries + 3) & ~3;
   size_t b = lca::align256((size_t)rows * (size_t)std::max(ld, 4) * 4);   // scores
@@ -264,7 +273,7 @@ size_t lca_hybrid_workspace_bytes(const lca_layer* layers, int32_t n_layers, int
                                   int32_t max_q, int32_t heads) {
   if (!layers || n_layers <= 0 || batch <= 0 || max_q <= 0 || heads <= 0) return 0;
   const int rows = batch * max_q;
-  const int sp = lca::attn_auto_splits(max_q);
+  const int sp = hybrid_splits(n_layers, max_q);
   size_t b = 0;
   for (int l = 0; l < n_layers; ++l) {
     if (layers[l].kind == LCA_LAYER_CSA)
@@ -305,7 +314,7 @@ int32_t lca_hybrid_layer_step(const lca_layer* layers, int32_t n_layers, const i
   if (!std::isfinite(scale)) return fail(LCA_ERR_SHAPE, "hybrid_layer_step: scale not finite");
   const hipStream_t caller = (hipStream_t)stream;
   const int rows = batch * max_q;
-  const int sp = lca::attn_auto_splits(max_q);
+  const int sp = hybrid_splits(n_layers, max_q);
   // fork: every layer has its own workspace region, so layers can run concurrently
   LayerStreams* ls = n_layers > 1 ? layer_streams() : nullptr;
   const int ns = ls ? std::min(kLayerStreams, (int)n_layers) : 0;
@@ -317,7 +326,8 @@ int32_t lca_hybrid_layer_step(const lca_layer* layers, int32_t n_layers, const i
   char* p = reinterpret_cast<char*>(ws);
   for (int l = 0; l < n_layers; ++l) {
     const lca_layer& L = layers[l];
-    const hipStream_t st = ls ? ls->s[l % ns] : caller;
+    // consecutive pairs share a stream, so each stream holds one CSA and one HCA layer
+    const hipStream_t st = ls ? ls->s[(l / 2) % ns] : caller;
     lca::AttnArgs a{};
     a.q = L.q;
     a.kc = L.k_cmp;

@@ -22,8 +22,8 @@
 // Per work-group: 256 threads = 4 waves.  With HG = min(H, 64)/16 head groups,
 // wave w takes head group w % HG and entry sub-group w / HG; a super-tile of 64
 // entries (128 for H = 16) is gathered with 128-bit loads (one 256-byte row per
-// 16 lanes), K row-major and V transposed into LDS, while the next super-tile's
-// rows are already in flight in registers.  Softmax is fp32 in log2 units;
+// 16 lanes), K row-major and V transposed into LDS, while the next two
+// super-tiles' rows are already in flight in registers.  Softmax is fp32 in log2 units;
 // P is rounded to bf16 for the MFMA and the running sum uses the rounded values.
 //
 // Splitting: a row's entries are cut into at most `splits` pieces of a multiple
@@ -148,100 +148,127 @@ __global__ __launch_bounds__(AT_NT) void attn_kernel(AttnArgs a) {
   float m_run = -INFINITY;
   float l_run = 0.f;
 
-  // staging: piece p = t + 256*u covers entry p/16, dims 8*(p%16) .. +7
-  i32x4 kreg[NPT], vreg[NPT];
-  auto gather = [&](int tb) {
+  // Staging: piece p = t + 256*u covers entry p/16, dims 8*(p%16) .. +7.  The loads
+  // form a fixed, branch-free sequence so the compiler can wait on exact load counts:
+  // the entry ids of a super-tile are fetched one stage before its K/V rows, and two
+  // super-tiles of K/V rows are in flight while the current one is in use.  Pieces
+  // past the split's end read the split's last row (already cached) and are zeroed
+  // when staged.
+  i32x4 kA[NPT], vA[NPT], kB[NPT], vB[NPT];
+  int idA[NPT], idB[NPT];
+  const int e_last = e1 - 1;
+  auto load_ids = [&](int* ids, int tb) {
 #pragma unroll
     for (int u = 0; u < NPT; ++u) {
-      const int p = t + AT_NT * u;
-      const int el = p >> 4;
-      const int col = p & 15;
-      const int e = tb + el;
-      if (e < e1) {
-        int64_t id = a.idx ? (int64_t)a.idx[ri.row * a.k + e] : (int64_t)e;
-        id = id < 0 ? 0 : (id >= ri.n_seq ? ri.n_seq - 1 : id);   // stay inside the sequence
-        const int64_t ent = ri.e_base + id;
-        kreg[u] = reinterpret_cast<const i32x4*>(a.kc + ent * HD)[col];
-        vreg[u] = reinterpret_cast<const i32x4*>(a.vc + ent * HD)[col];
-      } else {
-        kreg[u] = i32x4{0, 0, 0, 0};
-        vreg[u] = i32x4{0, 0, 0, 0};
-      }
+      const int e = min(tb + ((t + AT_NT * u) >> 4), e_last);
+      ids[u] = a.idx ? a.idx[ri.row * a.k + e] : e;
     }
   };
-
-  gather(e0);
-  for (int tb = e0; tb < e1; tb += ST) {
+  auto gather = [&](const int* ids, i32x4* kr, i32x4* vr) {
+#pragma unroll
+    for (int u = 0; u < NPT; ++u) {
+      const int col = (t + AT_NT * u) & 15;
+      int64_t id = ids[u];
+      id = id < 0 ? 0 : (id >= ri.n_seq ? ri.n_seq - 1 : id);   // stay inside the sequence
+      const int64_t ent = ri.e_base + id;
+      kr[u] = reinterpret_cast<const i32x4*>(a.kc + ent * HD)[col];
+      vr[u] = reinterpret_cast<const i32x4*>(a.vc + ent * HD)[col];
+    }
+  };
+  auto stage = [&](const i32x4* kr, const i32x4* vr, int tb) {
     __syncthreads();   // previous super-tile fully consumed
 #pragma unroll
     for (int u = 0; u < NPT; ++u) {
       const int p = t + AT_NT * u;
       const int el = p >> 4;
       const int col = p & 15;
-      *reinterpret_cast<i32x4*>(&sm.tile.k[el * KSTR + col * 8]) = kreg[u];
+      const bool valid = tb + el < e1;
+      const i32x4 kz = valid ? kr[u] : i32x4{0, 0, 0, 0};
+      const i32x4 vz = valid ? vr[u] : i32x4{0, 0, 0, 0};
+      *reinterpret_cast<i32x4*>(&sm.tile.k[el * KSTR + col * 8]) = kz;
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const uint32_t word = (uint32_t)vreg[u][q];
+        const uint32_t word = (uint32_t)vz[q];
         sm.tile.vt[(col * 8 + 2 * q) * VSTR + el] = (uint16_t)(word & 0xffffu);
         sm.tile.vt[(col * 8 + 2 * q + 1) * VSTR + el] = (uint16_t)(word >> 16);
       }
     }
     __syncthreads();
-    if (tb + ST < e1) gather(tb + ST);   // next rows in flight during the math
-
+  };
+  auto compute = [&](int tb) {
 #pragma unroll
     for (int sub = 0; sub < SUB; ++sub) {
-    const int el0 = (es * SUB + sub) * 32;   // this wave's 32 entries of the super-tile
-    const int ev0 = tb + el0;                // their first entry number
-    if (ev0 < e1) {
-      // S^T for two 16-entry blocks
-      f32x4 sacc[2];
+      const int el0 = (es * SUB + sub) * 32;   // this wave's 32 entries of the super-tile
+      const int ev0 = tb + el0;                // their first entry number
+      if (ev0 < e1) {
+        // S^T for two 16-entry blocks
+        f32x4 sacc[2];
 #pragma unroll
-      for (int rb = 0; rb < 2; ++rb) {
-        sacc[rb] = f32x4{0.f, 0.f, 0.f, 0.f};
-        const uint16_t* krow = &sm.tile.k[(el0 + rb * 16 + l16) * KSTR + 8 * g];
+        for (int rb = 0; rb < 2; ++rb) {
+          sacc[rb] = f32x4{0.f, 0.f, 0.f, 0.f};
+          const uint16_t* krow = &sm.tile.k[(el0 + rb * 16 + l16) * KSTR + 8 * g];
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-          const bf16x8 kf = __builtin_bit_cast(bf16x8, *reinterpret_cast<const i32x4*>(krow + 32 * ks));
-          sacc[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[ks], sacc[rb], 0, 0, 0);
+          for (int ks = 0; ks < 4; ++ks) {
+            const bf16x8 kf =
+                __builtin_bit_cast(bf16x8, *reinterpret_cast<const i32x4*>(krow + 32 * ks));
+            sacc[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[ks], sacc[rb], 0, 0, 0);
+          }
         }
-      }
-      // online softmax (log2 units); lane holds head l16, entries 16rb + 4g + i
-      float x[8];
-      float mx = -INFINITY;
+        // online softmax (log2 units); lane holds head l16, entries 16rb + 4g + i
+        float x[8];
+        float mx = -INFINITY;
 #pragma unroll
-      for (int rb = 0; rb < 2; ++rb)
+        for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int e = ev0 + rb * 16 + 4 * g + i;
-          const float v = (e < e1) ? sacc[rb][i] * a.scale_log2 : -INFINITY;
-          x[rb * 4 + i] = v;
-          mx = fmaxf(mx, v);
+          for (int i = 0; i < 4; ++i) {
+            const int e = ev0 + rb * 16 + 4 * g + i;
+            const float v = (e < e1) ? sacc[rb][i] * a.scale_log2 : -INFINITY;
+            x[rb * 4 + i] = v;
+            mx = fmaxf(mx, v);
+          }
+        mx = fmaxf(mx, __shfl_xor(mx, 16, WAVE));
+        mx = fmaxf(mx, __shfl_xor(mx, 32, WAVE));
+        const float m_new = fmaxf(m_run, mx);       // finite: the wave has a valid entry
+        const float alpha = exp2f(m_run - m_new);   // 0 on the first tile
+        bf16x8 pf;
+        float psum = 0.f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const __bf16 pb = (__bf16)exp2f(x[i] - m_new);
+          pf[i] = pb;
+          psum += (float)pb;
         }
-      mx = fmaxf(mx, __shfl_xor(mx, 16, WAVE));
-      mx = fmaxf(mx, __shfl_xor(mx, 32, WAVE));
-      const float m_new = fmaxf(m_run, mx);       // finite: the wave has a valid entry
-      const float alpha = exp2f(m_run - m_new);   // 0 on the first tile
-      bf16x8 pf;
-      float psum = 0.f;
+        l_run = l_run * alpha + psum;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const __bf16 pb = (__bf16)exp2f(x[i] - m_new);
-        pf[i] = pb;
-        psum += (float)pb;
+        for (int db = 0; db < 8; ++db) {
+          o[db] *= alpha;
+          const uint16_t* vrow = &sm.tile.vt[(db * 16 + l16) * VSTR + el0 + 4 * g];
+          const bf16x4 lo = *reinterpret_cast<const bf16x4*>(vrow);
+          const bf16x4 hi = *reinterpret_cast<const bf16x4*>(vrow + 16);
+          const bf16x8 vf = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+          o[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf, o[db], 0, 0, 0);
+        }
+        m_run = m_new;
       }
-      l_run = l_run * alpha + psum;
-#pragma unroll
-      for (int db = 0; db < 8; ++db) {
-        o[db] *= alpha;
-        const uint16_t* vrow = &sm.tile.vt[(db * 16 + l16) * VSTR + el0 + 4 * g];
-        const bf16x4 lo = *reinterpret_cast<const bf16x4*>(vrow);
-        const bf16x4 hi = *reinterpret_cast<const bf16x4*>(vrow + 16);
-        const bf16x8 vf = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-        o[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf, o[db], 0, 0, 0);
-      }
-      m_run = m_new;
     }
+  };
+
+  if (e1 > e0) {
+    load_ids(idA, e0);
+    load_ids(idB, e0 + ST);
+    gather(idA, kA, vA);
+    load_ids(idA, e0 + 2 * ST);
+    gather(idB, kB, vB);
+    load_ids(idB, e0 + 3 * ST);
+    for (int tb = e0; tb < e1; tb += 2 * ST) {
+      stage(kA, vA, tb);
+      gather(idA, kA, vA);               // rows of super-tile tb + 2*ST
+      load_ids(idA, tb + 4 * ST);
+      compute(tb);
+      stage(kB, vB, tb + ST);
+      gather(idB, kB, vB);               // rows of super-tile tb + 3*ST
+      load_ids(idB, tb + 5 * ST);
+      compute(tb + ST);                  // no-op past the end
     }
   }
 

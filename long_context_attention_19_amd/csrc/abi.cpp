@@ -8,6 +8,7 @@
 #include <cstdio>
 #include <mutex>
 #include <string>
+#include <vector>
 
 #include "lca.h"
 #include "lca_internal.h"
@@ -144,21 +145,23 @@ int32_t lca_csa_index_score(const int8_t* q_idx, const int64_t* q_off, const int
   if ((int64_t)batch * max_q > (1 << 30)) return fail(LCA_ERR_SHAPE, "csa_index_score: too many rows");
   if (!q_idx || !q_off || !q_pos || !k_idx || !ent_off || !scores || !n_vis) return fail(LCA_ERR_NULL, "csa_index_score: NULL pointer");
   if (!al16(q_idx) || !al16(k_idx) || !al16(scores)) return fail(LCA_ERR_ALIGN, "csa_index_score: q_idx / k_idx / scores not 16-byte aligned");
-  int32_t* hist = nullptr;
-  int32_t* fine = nullptr;
+  lca::IndexBatch ib{};
+  ib.q_off = q_off;
+  ib.q_pos = q_pos;
+  ib.max_q = max_q;
+  ib.n = 1;
+  ib.layer[0] = lca::IndexLayer{q_idx, k_idx, ent_off, scores, ld_scores, n_vis, nullptr, nullptr,
+                                c, max_entries};
   if (ws) {
     const int rows = batch * max_q;
     const size_t need = lca::topk_hist_region_bytes(rows);
     if (ws_bytes < need) return fail(LCA_ERR_WORKSPACE, "csa_index_score: ws_bytes %zu < %zu", ws_bytes, need);
     if (!al16(ws)) return fail(LCA_ERR_ALIGN, "csa_index_score: ws not 16-byte aligned");
     lca::TopkWs w = lca::topk_ws_carve(ws, rows, 0, 1);   // the histograms lead the workspace
-    hist = w.hist;
-    fine = w.fine;
+    ib.layer[0].hist = w.hist;
+    ib.layer[0].fine = w.fine;
   }
-  return hip_status(lca::launch_index_score(q_idx, q_off, q_pos, k_idx, ent_off, batch, max_q,
-                                            max_entries, c, scores, ld_scores, n_vis, hist, fine,
-                                            (hipStream_t)stream),
-                    "csa_index_score launch");
+  return hip_status(lca::launch_index_score(ib, batch, (hipStream_t)stream), "csa_index_score launch");
 }
 
 // ------------------------------------------------------------------ top-k
@@ -181,9 +184,11 @@ int32_t lca_csa_topk_select(const int32_t* scores, int64_t ld_scores, int32_t ro
   if (!al16(scores) || !al16(ws)) return fail(LCA_ERR_ALIGN, "csa_topk_select: scores / ws not 16-byte aligned");
   const size_t need = lca::topk_ws_bytes(rows, max_n, k);
   if (ws_bytes < need) return fail(LCA_ERR_WORKSPACE, "csa_topk_select: ws_bytes %zu < %zu", ws_bytes, need);
-  lca::TopkWs w = lca::topk_ws_carve(ws, rows, max_n, k);
-  return hip_status(lca::launch_topk(scores, ld_scores, rows, max_n, n_vis, k, idx, count, w,
-                                     (flags & LCA_TOPK_HIST_READY) != 0, (hipStream_t)stream),
+  lca::TopkBatch tb{};
+  tb.n = 1;
+  tb.layer[0] = lca::TopkLayer{scores, ld_scores, n_vis, idx, count, max_n, k,
+                               lca::topk_ws_carve(ws, rows, max_n, k)};
+  return hip_status(lca::launch_topk(tb, rows, (flags & LCA_TOPK_HIST_READY) != 0, (hipStream_t)stream),
                     "csa_topk_select launch");
 }
 
@@ -245,7 +250,8 @@ int32_t lca_csa_sparse_attn(const lca_bf16* q, const lca_bf16* k_cmp, const lca_
   a.k = k;
   a.ratio = 1;
   a.lse = lse;
-  return hip_status(lca::launch_attention(a, batch, k, (hipStream_t)stream), "csa_sparse_attn launch");
+  return hip_status(lca::launch_attention(lca::attn_batch1(a), batch, (hipStream_t)stream),
+                    "csa_sparse_attn launch");
 }
 
 int32_t lca_hca_dense_attn(const lca_bf16* q, const lca_bf16* k_cmp, const lca_bf16* v_cmp,
@@ -264,7 +270,7 @@ int32_t lca_hca_dense_attn(const lca_bf16* q, const lca_bf16* k_cmp, const lca_b
   a.q_pos = q_pos;
   a.ratio = m;
   a.lse = lse;
-  return hip_status(lca::launch_attention(a, batch, max_entries, (hipStream_t)stream),
+  return hip_status(lca::launch_attention(lca::attn_batch1(a), batch, (hipStream_t)stream),
                     "hca_dense_attn launch");
 }
 
@@ -315,19 +321,15 @@ int32_t lca_hybrid_layer_step(const lca_layer* layers, int32_t n_layers, const i
   const hipStream_t caller = (hipStream_t)stream;
   const int rows = batch * max_q;
   const int sp = hybrid_splits(n_layers, max_q);
-  // fork: every layer has its own workspace region, so layers can run concurrently
-  LayerStreams* ls = n_layers > 1 ? layer_streams() : nullptr;
-  const int ns = ls ? std::min(kLayerStreams, (int)n_layers) : 0;
-  if (ls) {
-    if (hipEventRecord(ls->fork, caller) != hipSuccess) return fail(LCA_ERR_HIP, "hybrid_layer_step: fork record");
-    for (int i = 0; i < ns; ++i)
-      if (hipStreamWaitEvent(ls->s[i], ls->fork, 0) != hipSuccess) return fail(LCA_ERR_HIP, "hybrid_layer_step: fork wait");
-  }
+  const float scale_log2 = scale * 1.4426950408889634f;
+
+  // carve each layer's workspace region (layer order, as lca_hybrid_workspace_bytes sizes it)
+  std::vector<lca::IndexLayer> il;
+  std::vector<lca::TopkLayer> tl;
+  std::vector<lca::AttnArgs> csa_a, hca_a;
   char* p = reinterpret_cast<char*>(ws);
   for (int l = 0; l < n_layers; ++l) {
     const lca_layer& L = layers[l];
-    // consecutive pairs share a stream, so each stream holds one CSA and one HCA layer
-    const hipStream_t st = ls ? ls->s[(l / 2) % ns] : caller;
     lca::AttnArgs a{};
     a.q = L.q;
     a.kc = L.k_cmp;
@@ -337,50 +339,86 @@ int32_t lca_hybrid_layer_step(const lca_layer* layers, int32_t n_layers, const i
     a.max_q = max_q;
     a.heads = heads;
     a.splits = sp;
-    a.scale_log2 = scale * 1.4426950408889634f;
+    a.scale_log2 = scale_log2;
     a.out = L.out;
     a.lse = L.lse;
-    hipError_t e;
     if (L.kind == LCA_LAYER_CSA) {
       const int ld = std::max((L.max_entries + 3) & ~3, 4);
       int32_t* scores = reinterpret_cast<int32_t*>(p);
       p += lca::align256((size_t)rows * ld * 4);
       int32_t* n_vis = reinterpret_cast<int32_t*>(p);
       p += lca::align256((size_t)rows * 4);
-      void* tws = p;
+      lca::TopkWs w = lca::topk_ws_carve(p, rows, L.max_entries, L.topk);
       p += lca::topk_ws_bytes(rows, L.max_entries, L.topk);
-      lca::TopkWs w = lca::topk_ws_carve(tws, rows, L.max_entries, L.topk);
-      e = lca::launch_index_score(L.q_idx, q_off, q_pos, L.k_idx, L.ent_off, batch, max_q,
-                                  L.max_entries, L.ratio, scores, ld, n_vis, w.hist, w.fine, st);
-      if (e == hipSuccess)
-        e = lca::launch_topk(scores, ld, rows, L.max_entries, n_vis, L.topk, L.idx, L.count, w,
-                             true, st);
+      il.push_back(lca::IndexLayer{L.q_idx, L.k_idx, L.ent_off, scores, ld, n_vis, w.hist, w.fine,
+                                   L.ratio, L.max_entries});
+      tl.push_back(lca::TopkLayer{scores, ld, n_vis, L.idx, L.count, L.max_entries, L.topk, w});
       a.idx = L.idx;
       a.count = L.count;
       a.k = L.topk;
       a.ratio = 1;
+      lca::attn_ws_carve(p, rows, heads, sp, a);
+      p += lca::attn_ws_bytes(rows, heads, sp);
+      csa_a.push_back(a);
     } else {
       a.q_pos = q_pos;
       a.ratio = L.ratio;
-      e = hipSuccess;
-    }
-    lca::attn_ws_carve(p, rows, heads, sp, a);
-    p += lca::attn_ws_bytes(rows, heads, sp);
-    if (e == hipSuccess) e = lca::launch_attention(a, batch, L.max_entries, st);
-    if (e != hipSuccess) {
-      // join what was enqueued so far before reporting, so the caller's stream stays ordered
-      for (int i = 0; ls && i < ns; ++i) {
-        (void)hipEventRecord(ls->join[i], ls->s[i]);
-        (void)hipStreamWaitEvent(caller, ls->join[i], 0);
-      }
-      return fail(LCA_ERR_HIP, "hybrid_layer_step: layer %d: %s", l, hipGetErrorString(e));
+      lca::attn_ws_carve(p, rows, heads, sp, a);
+      p += lca::attn_ws_bytes(rows, heads, sp);
+      hca_a.push_back(a);
     }
   }
-  for (int i = 0; ls && i < ns; ++i) {   // join
-    if (hipEventRecord(ls->join[i], ls->s[i]) != hipSuccess ||
-        hipStreamWaitEvent(caller, ls->join[i], 0) != hipSuccess)
-      return fail(LCA_ERR_HIP, "hybrid_layer_step: join");
+
+  // CSA layers run as batched phases on one stream (scores -> select -> attend), HCA layers
+  // as batched dense attention on another; both fork from and join back to the caller.
+  LayerStreams* ls = layer_streams();
+  const bool fork = ls && !csa_a.empty() && !hca_a.empty();
+  const hipStream_t s_csa = fork ? ls->s[0] : caller;
+  const hipStream_t s_hca = fork ? ls->s[1] : caller;
+  if (fork) {
+    if (hipEventRecord(ls->fork, caller) != hipSuccess ||
+        hipStreamWaitEvent(s_csa, ls->fork, 0) != hipSuccess ||
+        hipStreamWaitEvent(s_hca, ls->fork, 0) != hipSuccess)
+      return fail(LCA_ERR_HIP, "hybrid_layer_step: fork");
   }
+  hipError_t e = hipSuccess;
+  const int hb = (heads + 63) / 64;
+  for (size_t c0 = 0; c0 < csa_a.size() && e == hipSuccess; c0 += lca::MAX_BATCH_LAYERS) {
+    const int n = (int)std::min<size_t>(lca::MAX_BATCH_LAYERS, csa_a.size() - c0);
+    lca::IndexBatch ib{};
+    ib.q_off = q_off;
+    ib.q_pos = q_pos;
+    ib.max_q = max_q;
+    ib.n = n;
+    lca::TopkBatch tb{};
+    tb.n = n;
+    lca::AttnBatch ab{};
+    ab.n = n;
+    ab.head_blocks = hb;
+    for (int i = 0; i < n; ++i) {
+      ib.layer[i] = il[c0 + i];
+      tb.layer[i] = tl[c0 + i];
+      ab.a[i] = csa_a[c0 + i];
+    }
+    e = lca::launch_index_score(ib, batch, s_csa);
+    if (e == hipSuccess) e = lca::launch_topk(tb, rows, true, s_csa);
+    if (e == hipSuccess) e = lca::launch_attention(ab, batch, s_csa);
+  }
+  for (size_t c0 = 0; c0 < hca_a.size() && e == hipSuccess; c0 += lca::MAX_BATCH_LAYERS) {
+    const int n = (int)std::min<size_t>(lca::MAX_BATCH_LAYERS, hca_a.size() - c0);
+    lca::AttnBatch ab{};
+    ab.n = n;
+    ab.head_blocks = hb;
+    for (int i = 0; i < n; ++i) ab.a[i] = hca_a[c0 + i];
+    e = lca::launch_attention(ab, batch, s_hca);
+  }
+  if (fork) {   // join, also after a failed launch so the caller's stream stays ordered
+    (void)hipEventRecord(ls->join[0], s_csa);
+    (void)hipEventRecord(ls->join[1], s_hca);
+    (void)hipStreamWaitEvent(caller, ls->join[0], 0);
+    (void)hipStreamWaitEvent(caller, ls->join[1], 0);
+  }
+  if (e != hipSuccess) return fail(LCA_ERR_HIP, "hybrid_layer_step: %s", hipGetErrorString(e));
   return ok();
 }
 

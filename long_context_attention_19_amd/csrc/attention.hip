@@ -111,7 +111,8 @@ struct AttnSmem {
 // ES entry sub-groups of waves; each wave takes SUB consecutive 32-entry sub-tiles
 // of every super-tile, so one super-tile (one gather round trip) covers 32*ES*SUB rows.
 template <int ES, int SUB>
-__global__ __launch_bounds__(AT_NT) void attn_kernel(AttnArgs a) {
+__global__ __launch_bounds__(AT_NT) void attn_kernel(AttnBatch ab) {
+  const AttnArgs& a = ab.a[blockIdx.z / ab.head_blocks];   // grid z = layer x head block
   constexpr int ST = AttnSmem<ES, SUB>::ST;
   constexpr int VSTR = AttnSmem<ES, SUB>::VSTR;
   constexpr int NPT = ST * 16 / AT_NT;          // 16-byte row pieces per thread per matrix
@@ -122,7 +123,7 @@ __global__ __launch_bounds__(AT_NT) void attn_kernel(AttnArgs a) {
   if (!row_info(a, ST, ri)) return;
   const int s = blockIdx.x;
   if (s >= ri.nsp) return;
-  const int h0 = blockIdx.z * 64;
+  const int h0 = (blockIdx.z % ab.head_blocks) * 64;
   const int t = threadIdx.x;
   const int w = t >> 6;
   const int lane = t & 63;
@@ -336,7 +337,8 @@ __global__ __launch_bounds__(AT_NT) void attn_kernel(AttnArgs a) {
 // (all of them for the default split count), then merged in piece order with a
 // running maximum, so the result does not depend on load timing.
 template <int ST>
-__global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
+__global__ __launch_bounds__(256) void attn_combine_kernel(AttnBatch ab) {
+  const AttnArgs& a = ab.a[blockIdx.z];   // grid z = layer
   constexpr int CB = 32;
   RowInfo ri;
   if (!row_info(a, ST, ri)) return;
@@ -374,29 +376,29 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
   if (a.lse && d == 0) a.lse[ri.row * a.heads + head] = (mm + log2f(ll)) * 0.69314718055994530942f;
 }
 
-hipError_t launch_attention(const AttnArgs& a, int batch, int max_entries_or_k, hipStream_t st) {
-  (void)max_entries_or_k;
-  if (batch == 0 || a.max_q == 0) return hipSuccess;
-  const int hb = (a.heads + 63) / 64;
-  const int hg = min(a.heads, 64) / 16;          // 1, 2 or 4
-  const unsigned rows_grid = (unsigned)(batch * a.max_q);
-  dim3 grid((unsigned)a.splits, rows_grid, (unsigned)hb);
+hipError_t launch_attention(const AttnBatch& ab, int batch, hipStream_t st) {
+  if (batch == 0 || ab.n == 0) return hipSuccess;
+  const AttnArgs& a0 = ab.a[0];   // heads, splits and max_q are shared by the batch
+  if (a0.max_q == 0) return hipSuccess;
+  const int hg = min(a0.heads, 64) / 16;          // 1, 2 or 4
+  const unsigned rows_grid = (unsigned)(batch * a0.max_q);
+  dim3 grid((unsigned)a0.splits, rows_grid, (unsigned)(ab.n * ab.head_blocks));
   int st_size;
   if (hg == 4) {
-    hipLaunchKernelGGL((attn_kernel<1, 2>), grid, dim3(AT_NT), 0, st, a);
+    hipLaunchKernelGGL((attn_kernel<1, 2>), grid, dim3(AT_NT), 0, st, ab);
     st_size = 64;
   } else if (hg == 2) {
-    hipLaunchKernelGGL((attn_kernel<2, 1>), grid, dim3(AT_NT), 0, st, a);
+    hipLaunchKernelGGL((attn_kernel<2, 1>), grid, dim3(AT_NT), 0, st, ab);
     st_size = 64;
   } else {
-    hipLaunchKernelGGL((attn_kernel<4, 1>), grid, dim3(AT_NT), 0, st, a);
+    hipLaunchKernelGGL((attn_kernel<4, 1>), grid, dim3(AT_NT), 0, st, ab);
     st_size = 128;
   }
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess || a.splits <= 1) return e;
-  dim3 cgrid((unsigned)((a.heads + 1) / 2), rows_grid);
-  if (st_size == 64) hipLaunchKernelGGL(attn_combine_kernel<64>, cgrid, dim3(256), 0, st, a);
-  else hipLaunchKernelGGL(attn_combine_kernel<128>, cgrid, dim3(256), 0, st, a);
+  if (e != hipSuccess || a0.splits <= 1) return e;
+  dim3 cgrid((unsigned)((a0.heads + 1) / 2), rows_grid, (unsigned)ab.n);
+  if (st_size == 64) hipLaunchKernelGGL(attn_combine_kernel<64>, cgrid, dim3(256), 0, st, ab);
+  else hipLaunchKernelGGL(attn_combine_kernel<128>, cgrid, dim3(256), 0, st, ab);
   return hipGetLastError();
 }
 

@@ -7,7 +7,8 @@
 //
 // Decode streams 64 bytes of key per entry and does 16 int8 MACs per 16 bytes,
 // far below the ALU ridge: the kernel is bound by HBM.  Layout of the work:
-//   - a work-group owns IS_CHUNK consecutive entries of one sequence;
+//   - a work-group owns IS_CHUNK consecutive entries of one sequence of one layer
+//     (grid z = layer: the layers of a hybrid stack are scored in one launch);
 //   - in each round, lane t loads the 16-byte piece (t % 4) of key (t / 4), so a
 //     wave's 128-bit loads cover 1 KiB of contiguous key rows, and IS_ROUNDS
 //     such loads are in flight per thread (non-temporal: keys are read once);
@@ -31,24 +32,27 @@ constexpr int IS_PASSES = 4;
 constexpr int IS_CHUNK = IS_KEYS_PER_PASS * IS_PASSES;     // 2048 entries per work-group
 
 template <bool HIST>
-__global__ __launch_bounds__(IS_NT) void index_score_kernel(
-    const int8_t* __restrict__ q_idx, const int64_t* __restrict__ q_off,
-    const int64_t* __restrict__ q_pos, const int8_t* __restrict__ k_idx,
-    const int64_t* __restrict__ ent_off, int max_q, int max_entries, int c,
-    int32_t* __restrict__ scores,
-    int64_t ld, int32_t* __restrict__ n_vis_out, int32_t* __restrict__ hist,
-    int32_t* __restrict__ fine) {
+__global__ __launch_bounds__(IS_NT) void index_score_kernel(IndexBatch ib) {
   __shared__ int32_t lh[HIST ? HIST_BINS : 1];
+  const IndexLayer& L = ib.layer[blockIdx.z];
+  const int8_t* __restrict__ q_idx = L.q_idx;
+  const int8_t* __restrict__ k_idx = L.k_idx;
+  int32_t* __restrict__ scores = L.scores;
+  int32_t* __restrict__ hist = L.hist;
+  int32_t* __restrict__ fine = L.fine;
+  const int64_t ld = L.ld;
+  const int c = L.c;
+  const int max_q = ib.max_q;
   const int b = blockIdx.y / max_q;
   const int i = blockIdx.y - b * max_q;
-  const int64_t r0 = q_off[b];
-  if (i >= q_off[b + 1] - r0) return;
+  const int64_t r0 = ib.q_off[b];
+  if (i >= ib.q_off[b + 1] - r0) return;
   const int64_t row = r0 + i;
-  const int64_t e0 = ent_off[b];
-  const int64_t N = min(ent_off[b + 1] - e0, (int64_t)max_entries);
-  const int64_t nv = min(q_pos[row] / c, N);
+  const int64_t e0 = L.ent_off[b];
+  const int64_t N = min(L.ent_off[b + 1] - e0, (int64_t)L.max_entries);
+  const int64_t nv = min(ib.q_pos[row] / c, N);
   const int64_t base = (int64_t)blockIdx.x * IS_CHUNK;
-  if (blockIdx.x == 0 && threadIdx.x == 0) n_vis_out[row] = (int32_t)nv;
+  if (blockIdx.x == 0 && threadIdx.x == 0) L.n_vis[row] = (int32_t)nv;
   if (base >= N) return;
 
   const int t = threadIdx.x;
@@ -107,19 +111,19 @@ __global__ __launch_bounds__(IS_NT) void index_score_kernel(
   }
 }
 
-hipError_t launch_index_score(const int8_t* q_idx, const int64_t* q_off, const int64_t* q_pos,
-                              const int8_t* k_idx, const int64_t* ent_off, int batch, int max_q,
-                              int max_entries, int c, int32_t* scores, int64_t ld,
-                              int32_t* n_vis, int32_t* hist, int32_t* fine, hipStream_t st) {
-  if (batch == 0 || max_q == 0) return hipSuccess;
-  const int chunks = max(1, (max_entries + IS_CHUNK - 1) / IS_CHUNK);
-  dim3 grid((unsigned)chunks, (unsigned)(batch * max_q));
+hipError_t launch_index_score(const IndexBatch& ib, int batch, hipStream_t st) {
+  if (batch == 0 || ib.max_q == 0 || ib.n == 0) return hipSuccess;
+  int chunks = 1;
+  bool hist = false;
+  for (int l = 0; l < ib.n; ++l) {
+    chunks = max(chunks, (ib.layer[l].max_entries + IS_CHUNK - 1) / IS_CHUNK);
+    hist = hist || ib.layer[l].hist != nullptr;
+  }
+  dim3 grid((unsigned)chunks, (unsigned)(batch * ib.max_q), (unsigned)ib.n);
   if (hist)
-    hipLaunchKernelGGL(index_score_kernel<true>, grid, dim3(IS_NT), 0, st, q_idx, q_off, q_pos,
-                       k_idx, ent_off, max_q, max_entries, c, scores, ld, n_vis, hist, fine);
+    hipLaunchKernelGGL(index_score_kernel<true>, grid, dim3(IS_NT), 0, st, ib);
   else
-    hipLaunchKernelGGL(index_score_kernel<false>, grid, dim3(IS_NT), 0, st, q_idx, q_off, q_pos,
-                       k_idx, ent_off, max_q, max_entries, c, scores, ld, n_vis, hist, fine);
+    hipLaunchKernelGGL(index_score_kernel<false>, grid, dim3(IS_NT), 0, st, ib);
   return hipGetLastError();
 }
 

@@ -12,12 +12,31 @@ hipError_t launch_kv_compress(const uint16_t* x, const int64_t* tok_off, int bat
                               const int64_t* ent_off, hipStream_t st);
 
 // ------------------------------------------------------------ index scores
-// hist != nullptr: also build the top-k's coarse radix histogram (hist[rows][2048],
-// accumulated) and zero its fine histogram (fine[rows][1024]).
-hipError_t launch_index_score(const int8_t* q_idx, const int64_t* q_off, const int64_t* q_pos,
-                              const int8_t* k_idx, const int64_t* ent_off, int batch, int max_q,
-                              int max_entries, int c, int32_t* scores, int64_t ld,
-                              int32_t* n_vis, int32_t* hist, int32_t* fine, hipStream_t st);
+constexpr int MAX_BATCH_LAYERS = 8;   // layers per batched launch (grid z)
+
+// One layer of an indexer-score launch.  hist != nullptr: also build the top-k's
+// coarse radix histogram (hist[rows][2048], accumulated) and zero its fine
+// histogram (fine[rows][1024]); all layers of a launch either have it or not.
+struct IndexLayer {
+  const int8_t* q_idx;
+  const int8_t* k_idx;
+  const int64_t* ent_off;
+  int32_t* scores;
+  int64_t ld;
+  int32_t* n_vis;
+  int32_t* hist;
+  int32_t* fine;
+  int32_t c;
+  int32_t max_entries;
+};
+struct IndexBatch {
+  const int64_t* q_off;
+  const int64_t* q_pos;
+  int32_t max_q;
+  int32_t n;
+  IndexLayer layer[MAX_BATCH_LAYERS];
+};
+hipError_t launch_index_score(const IndexBatch& ib, int batch, hipStream_t st);
 
 // ------------------------------------------------------------ top-k
 struct TopkWs {
@@ -33,9 +52,22 @@ size_t topk_ws_bytes(int rows, int max_n, int k);
 size_t topk_hist_region_bytes(int rows);   // the hist + fine prefix of the workspace
 TopkWs topk_ws_carve(void* ws, int rows, int max_n, int k);
 int topk_max_chunks();
-hipError_t launch_topk(const int32_t* scores, int64_t ld, int rows, int max_n,
-                       const int32_t* n_vis, int k, int32_t* idx, int32_t* count,
-                       const TopkWs& w, bool hist_ready, hipStream_t st);
+// One layer of a top-k launch (all layers share the row count).
+struct TopkLayer {
+  const int32_t* scores;
+  int64_t ld;
+  const int32_t* n_vis;
+  int32_t* idx;
+  int32_t* count;
+  int32_t max_n;
+  int32_t k;
+  TopkWs w;
+};
+struct TopkBatch {
+  int32_t n;
+  TopkLayer layer[MAX_BATCH_LAYERS];
+};
+hipError_t launch_topk(const TopkBatch& tb, int rows, bool hist_ready, hipStream_t st);
 
 // ------------------------------------------------------------ attention
 struct AttnArgs {
@@ -58,10 +90,23 @@ struct AttnArgs {
   float* part_o;           // [rows][splits][heads][128]
   float2* part_ml;         // [rows][splits][heads]  (running max in log2 units, sum)
 };
+// Layers of one attention launch share heads, splits and max_q.
+struct AttnBatch {
+  int32_t n;
+  int32_t head_blocks;     // ceil(heads / 64)
+  AttnArgs a[MAX_BATCH_LAYERS];
+};
+inline AttnBatch attn_batch1(const AttnArgs& a) {
+  AttnBatch b{};
+  b.n = 1;
+  b.head_blocks = (a.heads + 63) / 64;
+  b.a[0] = a;
+  return b;
+}
 int attn_auto_splits(int max_q);
 size_t attn_ws_bytes(int rows, int heads, int splits);
 void attn_ws_carve(void* ws, int rows, int heads, int splits, AttnArgs& a);
-hipError_t launch_attention(const AttnArgs& a, int batch, int max_entries_or_k, hipStream_t st);
+hipError_t launch_attention(const AttnBatch& ab, int batch, hipStream_t st);
 
 // ------------------------------------------------------------ misc
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t st);

@@ -12,7 +12,7 @@
 // order in which work-groups run, so the selection is deterministic.
 //
 // Each row is cut into chunks of TK_CHUNK scores; every kernel's grid is
-// (chunks x rows) and work-groups never wait for one another — kernel
+// (chunks x rows x layers) and work-groups never wait for one another — kernel
 // boundaries order the passes, so no work-group runs a device-scope fence:
 //   K1 hist  — coarse histogram (LDS, one global atomic per non-empty bin) and
 //              zeroing of the row's fine histogram.  The index-score kernel can
@@ -131,13 +131,16 @@ __device__ __forceinline__ void coarse_threshold(const int32_t* hrow, int k, int
 }
 
 // ------------------------------------------------------------------ K1
-__global__ __launch_bounds__(TK_NT) void topk_hist_kernel(const int32_t* __restrict__ scores,
-                                                          int64_t ld, const int32_t* __restrict__ n_vis,
-                                                          int max_n, int k, int32_t* __restrict__ hist,
-                                                          int32_t* __restrict__ fine) {
+__global__ __launch_bounds__(TK_NT) void topk_hist_kernel(TopkBatch tb) {
+  const TopkLayer& TL = tb.layer[blockIdx.z];
+  const int32_t* __restrict__ scores = TL.scores;
+  const int64_t ld = TL.ld;
+  const int k = TL.k;
+  int32_t* __restrict__ hist = TL.w.hist;
+  int32_t* __restrict__ fine = TL.w.fine;
   __shared__ int32_t lh[HIST_BINS];
   const int row = blockIdx.y;
-  const int64_t n = min(n_vis[row], max_n);
+  const int64_t n = min(TL.n_vis[row], TL.max_n);
   if (n <= k) return;
   const int64_t base = (int64_t)blockIdx.x * TK_CHUNK;
   if (base >= n) return;
@@ -159,9 +162,14 @@ __global__ __launch_bounds__(TK_NT) void topk_hist_kernel(const int32_t* __restr
 }
 
 // ------------------------------------------------------------------ K2
-__global__ __launch_bounds__(TK_NT) void topk_cand_kernel(
-    const int32_t* __restrict__ scores, int64_t ld, const int32_t* __restrict__ n_vis, int max_n,
-    int k, TopkWs w) {
+__global__ __launch_bounds__(TK_NT) void topk_cand_kernel(TopkBatch tb) {
+  const TopkLayer& TL = tb.layer[blockIdx.z];
+  const int32_t* __restrict__ scores = TL.scores;
+  const int64_t ld = TL.ld;
+  const int k = TL.k;
+  const int max_n = TL.max_n;
+  const int32_t* __restrict__ n_vis = TL.n_vis;
+  const TopkWs& w = TL.w;
   __shared__ int32_t s_scan[TK_NT / WAVE + 1];
   __shared__ int32_t s_b[2];
   const int row = blockIdx.y;
@@ -211,9 +219,16 @@ __global__ __launch_bounds__(TK_NT) void topk_cand_kernel(
 }
 
 // ------------------------------------------------------------------ K3
-__global__ __launch_bounds__(TK_NT) void topk_place_kernel(
-    const int32_t* __restrict__ scores, int64_t ld, const int32_t* __restrict__ n_vis, int max_n,
-    int k, int32_t* __restrict__ idx, int32_t* __restrict__ count, TopkWs w) {
+__global__ __launch_bounds__(TK_NT) void topk_place_kernel(TopkBatch tb) {
+  const TopkLayer& TL = tb.layer[blockIdx.z];
+  const int32_t* __restrict__ scores = TL.scores;
+  const int64_t ld = TL.ld;
+  const int k = TL.k;
+  const int max_n = TL.max_n;
+  const int32_t* __restrict__ n_vis = TL.n_vis;
+  int32_t* __restrict__ idx = TL.idx;
+  int32_t* __restrict__ count = TL.count;
+  const TopkWs& w = TL.w;
   __shared__ int32_t s_scan[TK_NT / WAVE + 1];
   __shared__ int32_t s_b[2];
   __shared__ int32_t s_pre[TK_MAX_CHUNKS + 1];   // prefix of earlier chunks' bin counts
@@ -354,20 +369,17 @@ __global__ __launch_bounds__(TK_NT) void topk_place_kernel(
     }
 }
 
-hipError_t launch_topk(const int32_t* scores, int64_t ld, int rows, int max_n, const int32_t* n_vis,
-                       int k, int32_t* idx, int32_t* count, const TopkWs& w, bool hist_ready,
-                       hipStream_t st) {
-  if (rows == 0) return hipSuccess;
-  const unsigned nch = (unsigned)topk_nchunks(max_n);
+hipError_t launch_topk(const TopkBatch& tb, int rows, bool hist_ready, hipStream_t st) {
+  if (rows == 0 || tb.n == 0) return hipSuccess;
+  int nch = 1, pch = 1;
+  for (int l = 0; l < tb.n; ++l) {
+    nch = max(nch, topk_nchunks(tb.layer[l].max_n));
+    pch = max(pch, (max(tb.layer[l].max_n, tb.layer[l].k) + TK_CHUNK - 1) / TK_CHUNK);
+  }
   if (!hist_ready)
-    hipLaunchKernelGGL(topk_hist_kernel, dim3(nch, rows), dim3(TK_NT), 0, st, scores, ld, n_vis,
-                       max_n, k, w.hist, w.fine);
-  hipLaunchKernelGGL(topk_cand_kernel, dim3(nch, rows), dim3(TK_NT), 0, st, scores, ld, n_vis,
-                     max_n, k, w);
-  const int span = max(max_n, k);
-  const unsigned pch = (unsigned)max(1, (span + TK_CHUNK - 1) / TK_CHUNK);
-  hipLaunchKernelGGL(topk_place_kernel, dim3(pch, rows), dim3(TK_NT), 0, st, scores, ld, n_vis,
-                     max_n, k, idx, count, w);
+    hipLaunchKernelGGL(topk_hist_kernel, dim3(nch, rows, tb.n), dim3(TK_NT), 0, st, tb);
+  hipLaunchKernelGGL(topk_cand_kernel, dim3(nch, rows, tb.n), dim3(TK_NT), 0, st, tb);
+  hipLaunchKernelGGL(topk_place_kernel, dim3(pch, rows, tb.n), dim3(TK_NT), 0, st, tb);
   return hipGetLastError();
 }
 

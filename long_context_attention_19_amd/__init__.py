@@ -17,7 +17,7 @@ LIB_PATH = os.path.join(_HERE, "liblca.so")
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(
-        f"{LIB_PATH} is missing: build it with `python -m long_context_attention_19_amd.build_lib` "
+        f"{LIB_PATH} is missing: build it with `python long_context_attention_19_amd/build_lib.py` "
         "(or __graft_entry__.build()); there is no fallback implementation")
 
 _lib = ctypes.CDLL(LIB_PATH)

@@ -1,6 +1,8 @@
 """Build liblca.so (the gfx950 HIP kernels + C ABI) in-tree with hipcc.
 
-    python -m long_context_attention_19_amd.build_lib [--jobs N]
+    python long_context_attention_19_amd/build_lib.py [--jobs N]
+
+(run it as a file: importing the package requires the library it builds)
 
 Every translation unit under csrc/ is compiled for gfx950 only, then linked
 into long_context_attention_19_amd/liblca.so next to this file.  Packed fp32

@@ -157,7 +157,9 @@ int32_t lca_csa_topk_select(const int32_t* scores, int64_t ld_scores, int32_t ro
  *
  *   q        [rows, heads, 128] bf16;  out [rows, heads, 128] bf16
  *   lse      [rows, heads] fp32 (nullable)
- *   k_cmp, v_cmp  [ent_off[B], 128] bf16 compressed cache.
+ *   k_cmp, v_cmp  [ent_off[B], 128] bf16 compressed cache; a sequence may hold
+ *            at most 2^24 entries (max_entries above that is LCA_ERR_UNSUPPORTED;
+ *            sparse indices are clamped into the first 2^24 entries).
  *   heads % 16 == 0, head_dim == 128.
  *   splits   work-groups per (row, 64 heads) along the entries; 0 = automatic
  *            (32 when max_q == 1, fewer as max_q grows, 1 from max_q >= 32).

@@ -261,6 +261,7 @@ int32_t lca_hca_dense_attn(const lca_bf16* q, const lca_bf16* k_cmp, const lca_b
                            lca_bf16* out, float* lse, void* ws, size_t ws_bytes, void* stream) {
   if (m < 1) return fail(LCA_ERR_SHAPE, "hca_dense_attn: ratio m=%d < 1", m);
   if (max_entries < 0) return fail(LCA_ERR_SHAPE, "hca_dense_attn: negative max_entries");
+  if (max_entries > lca::ATTN_MAX_SEQ) return fail(LCA_ERR_UNSUPPORTED, "hca_dense_attn: max_entries=%d above %d", max_entries, lca::ATTN_MAX_SEQ);
   lca::AttnArgs a;
   int32_t st = attn_common("hca_dense_attn", q, k_cmp, v_cmp, ent_off, q_off, batch, max_q, heads,
                            head_dim, scale, splits, out, ws, ws_bytes, a);
@@ -306,6 +307,7 @@ int32_t lca_hybrid_layer_step(const lca_layer* layers, int32_t n_layers, const i
     const lca_layer& L = layers[l];
     if (L.kind != LCA_LAYER_CSA && L.kind != LCA_LAYER_HCA) return fail(LCA_ERR_SHAPE, "hybrid_layer_step: layer %d has unknown kind %d", l, L.kind);
     if (L.ratio < 1 || L.max_entries < 0) return fail(LCA_ERR_SHAPE, "hybrid_layer_step: layer %d ratio/max_entries", l);
+    if (L.max_entries > lca::ATTN_MAX_SEQ) return fail(LCA_ERR_UNSUPPORTED, "hybrid_layer_step: layer %d max_entries above %d", l, lca::ATTN_MAX_SEQ);
     if (!L.q || !L.k_cmp || !L.v_cmp || !L.ent_off || !L.out) return fail(LCA_ERR_NULL, "hybrid_layer_step: layer %d NULL pointer", l);
     if (L.kind == LCA_LAYER_CSA) {
       if (L.topk <= 0) return fail(LCA_ERR_SHAPE, "hybrid_layer_step: layer %d topk=%d", l, L.topk);

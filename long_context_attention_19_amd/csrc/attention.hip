@@ -16,21 +16,19 @@
 // only two cross-lane steps, the rescale factor is one scalar per lane, and the
 // S^T accumulator already sits in the lanes that feed P^T to the second product
 // (entries 4g..4g+3 of each 16-row block go to K-slots 8g..8g+7), so P never
-// leaves registers.  V is stored transposed in LDS when staged, so the V^T
-// operand is two 8-byte LDS reads per MFMA.
+// leaves registers.
 //
 // Per work-group: 256 threads = 4 waves.  With HG = min(H, 64)/16 head groups,
-// wave w takes head group w % HG and entry sub-group w / HG; a super-tile of 64
-// entries (128 for H = 16) is gathered with 128-bit loads (one 256-byte row per
-// 16 lanes), K row-major and V transposed into LDS, while the next two
-// super-tiles' rows are already in flight in registers.  Softmax is fp32 in log2 units;
-// P is rounded to bf16 for the MFMA and the running sum uses the rounded values.
+// wave w takes head group w % HG and entry sub-group w / HG.  A stage of 64
+// entries (128 for H = 16) is copied from HBM into LDS by the waves' DMA while
+// the previous stage is in use; softmax is fp32 in log2 units, P is rounded to
+// bf16 for the MFMA and the running sum uses the rounded values.
 //
 // Splitting: a row's entries are cut into at most `splits` pieces of a multiple
-// of the super-tile; each piece is a work-group.  A single piece writes the
-// final output; otherwise each writes (O, max, sum) partials and the combine
-// kernel merges them in piece order.  The cut depends only on the row's own
-// entry count, so a row's bits do not depend on the rest of the batch.
+// of the stage; each piece is a work-group.  A single piece writes the final
+// output; otherwise each writes (O, max, sum) partials and the combine kernel
+// merges them in piece order.  The cut depends only on the row's own entry
+// count, so a row's bits do not depend on the rest of the batch.
 #include "lca_device.h"
 #include "lca_internal.h"
 
@@ -38,7 +36,6 @@ namespace lca {
 
 constexpr int AT_NT = 256;
 constexpr int HD = 128;            // head_dim
-constexpr int KSTR = HD + 8;       // K row stride in LDS (bf16 elements): 272 B, spreads banks
 
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 
@@ -94,30 +91,77 @@ __device__ __forceinline__ bool row_info(const AttnArgs& a, int supertile, RowIn
   return true;
 }
 
-template <int ES, int SUB>
-struct AttnSmem {
-  static constexpr int ST = 32 * ES * SUB;      // entries per super-tile
-  static constexpr int VSTR = ST + 4;           // V^T row stride (bf16 elements)
-  union {
-    struct {
-      uint16_t k[ST * KSTR];
-      uint16_t vt[HD * VSTR];
-    } tile;
-    float merge_o[ES > 1 ? 4 : 1][ES > 1 ? 16 * HD : 1];   // per-wave O for the ES merge
-  };
-  float merge_ml[ES > 1 ? 4 : 1][16][2];
+// ---------------------------------------------------------------------------------
+// The K and V rows go from HBM straight into
+// LDS with global_load_lds_dwordx4 (no register staging, no LDS stores issued by the
+// waves), into two stage buffers: while one super-tile is in use the next one is in
+// flight.  V is kept row-major in LDS and the V^T operand is read with
+// ds_read_b64_tr_b16, which transposes 16-bit elements across each group of 16 lanes:
+// lane i of the group receives element i % 4 of the 8-byte reads of lanes
+// i / 4, 4 + i / 4, 8 + i / 4 and 12 + i / 4.  So lane 4e + q of group g points at
+// entry 4g + e, dims 16db + 4q .. +3, and lane i then holds dim 16db + i of entries
+// 4g .. 4g + 3: the V^T fragment of the same entry order as P^T.
+//
+// LDS layout: a 256-byte row is 16 slots of 16 bytes; one DMA instruction fills 4
+// rows (64 lanes x 16 bytes, contiguous), so rows are not padded and the slots are
+// permuted instead: K row r keeps dims 8c..8c+7 in slot c ^ (r & 15) (the 16 rows a
+// K-fragment read touches land in 16 distinct slots), V row r in slot c ^ 2(r & 7)
+// (the 8 rows x 32 bytes of a transposed read's half-wave are distinct slots).
+//
+// The DMA is issued from inline assembly so that the compiler does not order LDS
+// reads behind it: the transposed reads carry no alias information and the compiler
+// would otherwise wait for every DMA in flight, the next stage's included.  The
+// waits are explicit (vmcnt), and no compiler-visible global load is in flight while
+// the pipeline runs: the sparse form copies a chunk of entry ids to LDS first.
+constexpr int AT_IDS = 2048;       // entry ids staged in LDS per chunk (sparse form)
+
+template <int ST, bool SPARSE>
+struct AttnDmaSmem {
+  i32x4 k[2][ST * 16];
+  i32x4 v[2][ST * 16];
+  int ids[SPARSE ? AT_IDS : 1];
 };
 
-// ES entry sub-groups of waves; each wave takes SUB consecutive 32-entry sub-tiles
-// of every super-tile, so one super-tile (one gather round trip) covers 32*ES*SUB rows.
-template <int ES, int SUB>
-__global__ __launch_bounds__(AT_NT) void attn_kernel(AttnBatch ab) {
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(size_t)(const __attribute__((address_space(3))) char*)p;
+}
+
+// 64 lanes x 16 bytes from seq + voff (per lane) into LDS at lds .. lds + 1023
+__device__ __forceinline__ void dma16(const void* seq, uint32_t voff, uint32_t lds) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %3\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, %2\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(voff), "s"(seq), "s"(lds)
+      : "memory");
+}
+
+// wait until at most N vector-memory operations of this wave are outstanding
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt field is 6 bits");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// LDS reads done and work-group barrier, also a compiler barrier for memory
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// ES entry sub-groups of waves; each wave takes SUB consecutive 32-entry sub-tiles of
+// every stage, so a stage covers 32*ES*SUB entries.
+template <int ES, int SUB, bool SPARSE>
+__global__ __launch_bounds__(AT_NT) void attn_dma_kernel(AttnBatch ab) {
   const AttnArgs& a = ab.a[blockIdx.z / ab.head_blocks];   // grid z = layer x head block
-  constexpr int ST = AttnSmem<ES, SUB>::ST;
-  constexpr int VSTR = AttnSmem<ES, SUB>::VSTR;
-  constexpr int NPT = ST * 16 / AT_NT;          // 16-byte row pieces per thread per matrix
+  constexpr int ST = 32 * ES * SUB;             // entries per super-tile (stage)
   constexpr int HG = 4 / ES;                    // head groups of 16 per work-group
-  __shared__ AttnSmem<ES, SUB> sm;
+  constexpr int NU = ST / 16;                   // DMA instructions per wave per matrix
+  static_assert(NU >= 1 && NU <= 8 && AT_IDS % ST == 0, "stage size");
+  __shared__ AttnDmaSmem<ST, SPARSE> sm;
 
   RowInfo ri;
   if (!row_info(a, ST, ri)) return;
@@ -125,7 +169,7 @@ __global__ __launch_bounds__(AT_NT) void attn_kernel(AttnBatch ab) {
   if (s >= ri.nsp) return;
   const int h0 = (blockIdx.z % ab.head_blocks) * 64;
   const int t = threadIdx.x;
-  const int w = t >> 6;
+  const int w = __builtin_amdgcn_readfirstlane(t >> 6);
   const int lane = t & 63;
   const int hg = w % HG;
   const int es = w / HG;
@@ -134,88 +178,69 @@ __global__ __launch_bounds__(AT_NT) void attn_kernel(AttnBatch ab) {
   const int head = h0 + hg * 16 + l16;
   const int e0 = s * ri.per;
   const int e1 = min(e0 + ri.per, ri.n);
+  // kernel arguments used inside the pipeline are read once: the asm memory clobbers
+  // would otherwise make the compiler reload them
+  const float scale_log2 = a.scale_log2;
 
-  // Q^T fragments (B operand of S^T): head `head`, dims 32ks + 8g .. +7
   bf16x8 qf[4];
   {
     const i32x4* qp = reinterpret_cast<const i32x4*>(a.q + (ri.row * a.heads + head) * HD);
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) qf[ks] = __builtin_bit_cast(bf16x8, qp[ks * 4 + g]);
+    // take the compiler's wait for the query here, before any DMA is in flight
+    asm volatile("" : "+v"(qf[0]), "+v"(qf[1]), "+v"(qf[2]), "+v"(qf[3]));
   }
-
   f32x4 o[8];
 #pragma unroll
   for (int db = 0; db < 8; ++db) o[db] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m_run = -INFINITY;
   float l_run = 0.f;
 
-  // Staging: piece p = t + 256*u covers entry p/16, dims 8*(p%16) .. +7.  The loads
-  // form a fixed, branch-free sequence so the compiler can wait on exact load counts:
-  // the entry ids of a super-tile are fetched one stage before its K/V rows, and two
-  // super-tiles of K/V rows are in flight while the current one is in use.  Pieces
-  // past the split's end read the split's last row (already cached) and are zeroed
-  // when staged.
-  i32x4 kA[NPT], vA[NPT], kB[NPT], vB[NPT];
-  int idA[NPT], idB[NPT];
-  const int e_last = e1 - 1;
-  auto load_ids = [&](int* ids, int tb) {
+  // wave w fills rows w*ST/4 .. +ST/4 of a stage; DMA instruction u covers 4 of them
+  const int wrow0 = w * (ST / 4);
+  const int my_row = lane >> 4;
+  const int id_max = (int)min(ri.n_seq, (int64_t)ATTN_MAX_SEQ) - 1;
+  const char* kseq = reinterpret_cast<const char*>(a.kc + ri.e_base * HD);
+  const char* vseq = reinterpret_cast<const char*>(a.vc + ri.e_base * HD);
+  const uint32_t k_lds0 = lds_addr(&sm.k[0][wrow0 * 16]);
+  const uint32_t v_lds0 = lds_addr(&sm.v[0][wrow0 * 16]);
+  constexpr uint32_t BUF_BYTES = ST * 256;
+
+  // issue the DMA of the stage starting at entry tb into buffer buf; rows past
+  // e_last repeat row e_last (cached, and masked in the softmax)
+  auto issue = [&](int buf, int tb, int cbase, int e_last) {
 #pragma unroll
-    for (int u = 0; u < NPT; ++u) {
-      const int e = min(tb + ((t + AT_NT * u) >> 4), e_last);
-      ids[u] = a.idx ? a.idx[ri.row * a.k + e] : e;
+    for (int u = 0; u < NU; ++u) {
+      const int r = wrow0 + 4 * u + my_row;
+      const int e = min(tb + r, e_last);
+      int id = SPARSE ? sm.ids[e - cbase] : e;
+      id = min(max(id, 0), id_max);
+      const uint32_t row_off = (uint32_t)id * 256u;
+      const uint32_t ck = (uint32_t)(l16 ^ (r & 15)) << 4;
+      const uint32_t cv = (uint32_t)(l16 ^ ((r & 7) << 1)) << 4;
+      dma16(kseq, row_off + ck, k_lds0 + buf * BUF_BYTES + u * 1024);
+      dma16(vseq, row_off + cv, v_lds0 + buf * BUF_BYTES + u * 1024);
     }
   };
-  auto gather = [&](const int* ids, i32x4* kr, i32x4* vr) {
-#pragma unroll
-    for (int u = 0; u < NPT; ++u) {
-      const int col = (t + AT_NT * u) & 15;
-      int64_t id = ids[u];
-      id = id < 0 ? 0 : (id >= ri.n_seq ? ri.n_seq - 1 : id);   // stay inside the sequence
-      const int64_t ent = ri.e_base + id;
-      kr[u] = reinterpret_cast<const i32x4*>(a.kc + ent * HD)[col];
-      vr[u] = reinterpret_cast<const i32x4*>(a.vc + ent * HD)[col];
-    }
-  };
-  auto stage = [&](const i32x4* kr, const i32x4* vr, int tb) {
-    __syncthreads();   // previous super-tile fully consumed
-#pragma unroll
-    for (int u = 0; u < NPT; ++u) {
-      const int p = t + AT_NT * u;
-      const int el = p >> 4;
-      const int col = p & 15;
-      const bool valid = tb + el < e1;
-      const i32x4 kz = valid ? kr[u] : i32x4{0, 0, 0, 0};
-      const i32x4 vz = valid ? vr[u] : i32x4{0, 0, 0, 0};
-      *reinterpret_cast<i32x4*>(&sm.tile.k[el * KSTR + col * 8]) = kz;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const uint32_t word = (uint32_t)vz[q];
-        sm.tile.vt[(col * 8 + 2 * q) * VSTR + el] = (uint16_t)(word & 0xffffu);
-        sm.tile.vt[(col * 8 + 2 * q + 1) * VSTR + el] = (uint16_t)(word >> 16);
-      }
-    }
-    __syncthreads();
-  };
-  auto compute = [&](int tb) {
+  auto compute = [&](int buf, int tb) {
+    const i32x4* kb = sm.k[buf];
+    const char* vbase = reinterpret_cast<const char*>(sm.v[buf]);
 #pragma unroll
     for (int sub = 0; sub < SUB; ++sub) {
-      const int el0 = (es * SUB + sub) * 32;   // this wave's 32 entries of the super-tile
-      const int ev0 = tb + el0;                // their first entry number
+      const int el0 = (es * SUB + sub) * 32;   // this wave's 32 entries of the stage
+      const int ev0 = tb + el0;
       if (ev0 < e1) {
-        // S^T for two 16-entry blocks
         f32x4 sacc[2];
 #pragma unroll
         for (int rb = 0; rb < 2; ++rb) {
           sacc[rb] = f32x4{0.f, 0.f, 0.f, 0.f};
-          const uint16_t* krow = &sm.tile.k[(el0 + rb * 16 + l16) * KSTR + 8 * g];
+          const int r = el0 + rb * 16 + l16;
 #pragma unroll
           for (int ks = 0; ks < 4; ++ks) {
-            const bf16x8 kf =
-                __builtin_bit_cast(bf16x8, *reinterpret_cast<const i32x4*>(krow + 32 * ks));
+            const bf16x8 kf = __builtin_bit_cast(bf16x8, kb[r * 16 + ((4 * ks + g) ^ (r & 15))]);
             sacc[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[ks], sacc[rb], 0, 0, 0);
           }
         }
-        // online softmax (log2 units); lane holds head l16, entries 16rb + 4g + i
         float x[8];
         float mx = -INFINITY;
 #pragma unroll
@@ -223,14 +248,14 @@ __global__ __launch_bounds__(AT_NT) void attn_kernel(AttnBatch ab) {
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const int e = ev0 + rb * 16 + 4 * g + i;
-            const float v = (e < e1) ? sacc[rb][i] * a.scale_log2 : -INFINITY;
+            const float v = (e < e1) ? sacc[rb][i] * scale_log2 : -INFINITY;
             x[rb * 4 + i] = v;
             mx = fmaxf(mx, v);
           }
         mx = fmaxf(mx, __shfl_xor(mx, 16, WAVE));
         mx = fmaxf(mx, __shfl_xor(mx, 32, WAVE));
         const float m_new = fmaxf(m_run, mx);       // finite: the wave has a valid entry
-        const float alpha = exp2f(m_run - m_new);   // 0 on the first tile
+        const float alpha = exp2f(m_run - m_new);   // 0 on the first tile, 1 if unchanged
         bf16x8 pf;
         float psum = 0.f;
 #pragma unroll
@@ -240,72 +265,98 @@ __global__ __launch_bounds__(AT_NT) void attn_kernel(AttnBatch ab) {
           psum += (float)pb;
         }
         l_run = l_run * alpha + psum;
+        if (__any(m_new > m_run)) {                 // otherwise every factor is exactly 1
 #pragma unroll
-        for (int db = 0; db < 8; ++db) {
-          o[db] *= alpha;
-          const uint16_t* vrow = &sm.tile.vt[(db * 16 + l16) * VSTR + el0 + 4 * g];
-          const bf16x4 lo = *reinterpret_cast<const bf16x4*>(vrow);
-          const bf16x4 hi = *reinterpret_cast<const bf16x4*>(vrow + 16);
-          const bf16x8 vf = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-          o[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf, o[db], 0, 0, 0);
+          for (int db = 0; db < 8; ++db) o[db] *= alpha;
         }
         m_run = m_new;
+#pragma unroll
+        for (int db = 0; db < 8; ++db) {
+          bf16x4 half[2];
+#pragma unroll
+          for (int hh = 0; hh < 2; ++hh) {
+            const int r = el0 + 16 * hh + 4 * g + (l16 >> 2);
+            const int q = l16 & 3;
+            const int off = r * 256 + (((2 * db + (q >> 1)) ^ ((r & 7) << 1)) << 4) + (q & 1) * 8;
+            half[hh] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+                (__attribute__((address_space(3))) bf16x4*)(vbase + off));
+          }
+          const bf16x8 vf = {half[0][0], half[0][1], half[0][2], half[0][3],
+                             half[1][0], half[1][1], half[1][2], half[1][3]};
+          o[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf, o[db], 0, 0, 0);
+        }
       }
     }
   };
 
-  if (e1 > e0) {
-    load_ids(idA, e0);
-    load_ids(idB, e0 + ST);
-    gather(idA, kA, vA);
-    load_ids(idA, e0 + 2 * ST);
-    gather(idB, kB, vB);
-    load_ids(idB, e0 + 3 * ST);
-    for (int tb = e0; tb < e1; tb += 2 * ST) {
-      stage(kA, vA, tb);
-      gather(idA, kA, vA);               // rows of super-tile tb + 2*ST
-      load_ids(idA, tb + 4 * ST);
-      compute(tb);
-      stage(kB, vB, tb + ST);
-      gather(idB, kB, vB);               // rows of super-tile tb + 3*ST
-      load_ids(idB, tb + 5 * ST);
-      compute(tb + ST);                  // no-op past the end
+  // Per stage: issue the next stage's DMA into the other buffer, wait for this
+  // stage's own DMA (the next stage's 2*NU operations may stay outstanding), barrier,
+  // compute, barrier (the buffer is then free for the DMA two stages ahead).
+  for (int cbase = e0; cbase < e1; cbase += (SPARSE ? AT_IDS : (1 << 30))) {
+    const int cend = SPARSE ? min(cbase + AT_IDS, e1) : e1;
+    const int e_last = cend - 1;
+    if constexpr (SPARSE) {
+      __syncthreads();   // the previous chunk's ids are no longer read
+      const int* src = a.idx + ri.row * a.k + cbase;
+      const int cnt = cend - cbase;
+      int v[AT_IDS / AT_NT];
+#pragma unroll
+      for (int u = 0; u < AT_IDS / AT_NT; ++u) {   // all loads in flight, then the stores
+        const int j = t + AT_NT * u;
+        v[u] = j < cnt ? src[j] : 0;
+      }
+#pragma unroll
+      for (int u = 0; u < AT_IDS / AT_NT; ++u) sm.ids[t + AT_NT * u] = v[u];
+      __syncthreads();
+    }
+    int buf = 0;
+    issue(0, cbase, cbase, e_last);
+    for (int tb = cbase; tb < cend; tb += ST) {
+      if (tb + ST < cend) {
+        issue(buf ^ 1, tb + ST, cbase, e_last);
+        wait_vm<2 * NU>();
+      } else {
+        wait_vm<0>();
+      }
+      lds_barrier();
+      compute(buf, tb);
+      lds_barrier();
+      buf ^= 1;
     }
   }
 
-  // total of the per-lane-group partial sums for this lane's head
   l_run += __shfl_xor(l_run, 16, WAVE);
   l_run += __shfl_xor(l_run, 32, WAVE);
 
   if (ES > 1) {
-    // merge the ES entry sub-tiles of each head group through LDS
+    // merge the ES entry sub-groups of each head group; the stage buffers are free
+    float* merge_o = reinterpret_cast<float*>(sm.k[0]);        // [4][16][HD]
+    float* merge_ml = reinterpret_cast<float*>(sm.v[0]);       // [4][16][2]
     __syncthreads();
 #pragma unroll
     for (int db = 0; db < 8; ++db)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) sm.merge_o[w][l16 * HD + db * 16 + 4 * g + i] = o[db][i];
+      *reinterpret_cast<f32x4*>(&merge_o[(w * 16 + l16) * HD + db * 16 + 4 * g]) = o[db];
     if (g == 0) {
-      sm.merge_ml[w][l16][0] = m_run;
-      sm.merge_ml[w][l16][1] = l_run;
+      merge_ml[(w * 16 + l16) * 2] = m_run;
+      merge_ml[(w * 16 + l16) * 2 + 1] = l_run;
     }
     __syncthreads();
     if (es != 0) return;
     float mm = -INFINITY;
 #pragma unroll
-    for (int q = 0; q < ES; ++q) mm = fmaxf(mm, sm.merge_ml[hg + q * HG][l16][0]);
+    for (int q = 0; q < ES; ++q) mm = fmaxf(mm, merge_ml[((hg + q * HG) * 16 + l16) * 2]);
     float ll = 0.f;
 #pragma unroll
     for (int db = 0; db < 8; ++db) o[db] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int q = 0; q < ES; ++q) {
       const int wq = hg + q * HG;
-      const float mq = sm.merge_ml[wq][l16][0];
+      const float mq = merge_ml[(wq * 16 + l16) * 2];
       const float f = (mq == -INFINITY) ? 0.f : exp2f(mq - mm);
-      ll += sm.merge_ml[wq][l16][1] * f;
+      ll += merge_ml[(wq * 16 + l16) * 2 + 1] * f;
 #pragma unroll
       for (int db = 0; db < 8; ++db)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) o[db][i] += sm.merge_o[wq][l16 * HD + db * 16 + 4 * g + i] * f;
+        o[db] += *reinterpret_cast<const f32x4*>(&merge_o[(wq * 16 + l16) * HD + db * 16 + 4 * g]) * f;
     }
     m_run = mm;
     l_run = ll;
@@ -383,15 +434,19 @@ hipError_t launch_attention(const AttnBatch& ab, int batch, hipStream_t st) {
   const int hg = min(a0.heads, 64) / 16;          // 1, 2 or 4
   const unsigned rows_grid = (unsigned)(batch * a0.max_q);
   dim3 grid((unsigned)a0.splits, rows_grid, (unsigned)(ab.n * ab.head_blocks));
+  const bool sparse = a0.idx != nullptr;         // a batch holds one kind of layer
   int st_size;
   if (hg == 4) {
-    hipLaunchKernelGGL((attn_kernel<1, 2>), grid, dim3(AT_NT), 0, st, ab);
+    if (sparse) hipLaunchKernelGGL((attn_dma_kernel<1, 2, true>), grid, dim3(AT_NT), 0, st, ab);
+    else hipLaunchKernelGGL((attn_dma_kernel<1, 2, false>), grid, dim3(AT_NT), 0, st, ab);
     st_size = 64;
   } else if (hg == 2) {
-    hipLaunchKernelGGL((attn_kernel<2, 1>), grid, dim3(AT_NT), 0, st, ab);
+    if (sparse) hipLaunchKernelGGL((attn_dma_kernel<2, 1, true>), grid, dim3(AT_NT), 0, st, ab);
+    else hipLaunchKernelGGL((attn_dma_kernel<2, 1, false>), grid, dim3(AT_NT), 0, st, ab);
     st_size = 64;
   } else {
-    hipLaunchKernelGGL((attn_kernel<4, 1>), grid, dim3(AT_NT), 0, st, ab);
+    if (sparse) hipLaunchKernelGGL((attn_dma_kernel<4, 1, true>), grid, dim3(AT_NT), 0, st, ab);
+    else hipLaunchKernelGGL((attn_dma_kernel<4, 1, false>), grid, dim3(AT_NT), 0, st, ab);
     st_size = 128;
   }
   hipError_t e = hipGetLastError();

@@ -103,6 +103,8 @@ inline AttnBatch attn_batch1(const AttnArgs& a) {
   b.a[0] = a;
   return b;
 }
+// entries one sequence may hold for attention (32-bit byte offsets into its rows)
+constexpr int ATTN_MAX_SEQ = 1 << 24;
 int attn_auto_splits(int max_q);
 size_t attn_ws_bytes(int rows, int heads, int splits);
 void attn_ws_carve(void* ws, int rows, int heads, int splits, AttnArgs& a);

@@ -103,6 +103,8 @@ def test_attention_validation():
     assert g(*bad) == E_SHAPE                          # ratio 0
     bad = list(gargs); bad[5] = None
     assert g(*bad) == E_NULL                           # q_pos
+    bad = list(gargs); bad[8] = (1 << 24) + 1
+    assert g(*bad) == E_UNSUP                          # 32-bit row offsets per sequence
     assert lca.attn_workspace_bytes(4, 64, 1, 0) == lca.attn_workspace_bytes(4, 64, 1, 32)
     assert lca.attn_workspace_bytes(4096, 64, 4096, 0) == 0      # prefill rows are not split
 

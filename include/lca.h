@@ -161,10 +161,12 @@ int32_t lca_csa_topk_select(const int32_t* scores, int64_t ld_scores, int32_t ro
  *            at most 2^24 entries (max_entries above that is LCA_ERR_UNSUPPORTED;
  *            sparse indices are clamped into the first 2^24 entries).
  *   heads % 16 == 0, head_dim == 128.
- *   splits   work-groups per (row, 64 heads) along the entries; 0 = automatic
- *            (32 when max_q == 1, fewer as max_q grows, 1 from max_q >= 32).
- *            The split of a row depends only on its own entry count and
- *            `splits`, so a row's result does not depend on the rest of the batch.
+ *   splits   work-groups per (row, 64 heads) along the entries for a row at the
+ *            bound (k for CSA, max_entries for HCA); shorter rows take
+ *            proportionally fewer.  0 = automatic (32 when max_q == 1, fewer as
+ *            max_q grows, 1 from max_q >= 32).  The split of a row depends only on
+ *            its own entry count, the bound and `splits`, so a row's result does not
+ *            depend on the other rows of the batch.
  * ------------------------------------------------------------------------- */
 size_t lca_attn_workspace_bytes(int32_t rows, int32_t heads, int32_t max_q, int32_t splits);
 

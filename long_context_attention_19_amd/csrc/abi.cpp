@@ -248,6 +248,7 @@ int32_t lca_csa_sparse_attn(const lca_bf16* q, const lca_bf16* k_cmp, const lca_
   a.idx = idx;
   a.count = count;
   a.k = k;
+  a.max_n = k;
   a.ratio = 1;
   a.lse = lse;
   return hip_status(lca::launch_attention(lca::attn_batch1(a), batch, (hipStream_t)stream),
@@ -270,6 +271,7 @@ int32_t lca_hca_dense_attn(const lca_bf16* q, const lca_bf16* k_cmp, const lca_b
   if (!q_pos) return fail(LCA_ERR_NULL, "hca_dense_attn: q_pos NULL");
   a.q_pos = q_pos;
   a.ratio = m;
+  a.max_n = max_entries;
   a.lse = lse;
   return hip_status(lca::launch_attention(lca::attn_batch1(a), batch, (hipStream_t)stream),
                     "hca_dense_attn launch");
@@ -358,6 +360,7 @@ int32_t lca_hybrid_layer_step(const lca_layer* layers, int32_t n_layers, const i
       a.idx = L.idx;
       a.count = L.count;
       a.k = L.topk;
+      a.max_n = L.topk;
       a.ratio = 1;
       lca::attn_ws_carve(p, rows, heads, sp, a);
       p += lca::attn_ws_bytes(rows, heads, sp);
@@ -365,6 +368,7 @@ int32_t lca_hybrid_layer_step(const lca_layer* layers, int32_t n_layers, const i
     } else {
       a.q_pos = q_pos;
       a.ratio = L.ratio;
+      a.max_n = L.max_entries;
       lca::attn_ws_carve(p, rows, heads, sp, a);
       p += lca::attn_ws_bytes(rows, heads, sp);
       hca_a.push_back(a);

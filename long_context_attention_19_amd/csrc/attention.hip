@@ -24,11 +24,12 @@
 // the previous stage is in use; softmax is fp32 in log2 units, P is rounded to
 // bf16 for the MFMA and the running sum uses the rounded values.
 //
-// Splitting: a row's entries are cut into at most `splits` pieces of a multiple
-// of the stage; each piece is a work-group.  A single piece writes the final
-// output; otherwise each writes (O, max, sum) partials and the combine kernel
-// merges them in piece order.  The cut depends only on the row's own entry
-// count, so a row's bits do not depend on the rest of the batch.
+// Splitting: a row's entries are cut into pieces of one size per launch, a multiple
+// of the stage chosen so that a row at the host's bound (k for CSA, max_entries for
+// HCA) takes `splits` pieces; each piece is a work-group and shorter rows take fewer.
+// A single piece writes the final output; otherwise each writes (O, max, sum)
+// partials and the combine kernel merges them in piece order.  The cut depends on
+// the row's own entry count, the bound and `splits` only, never on other rows.
 #include "lca_device.h"
 #include "lca_internal.h"
 
@@ -72,6 +73,14 @@ struct RowInfo {
   int nsp;           // split pieces actually used
 };
 
+// One piece size for every row of the launch, from the host's bound on the entry
+// count: shorter rows get proportionally fewer pieces (a row beyond the bound widens
+// its own pieces so that it still fits in `splits`).
+__device__ __forceinline__ int piece_size(int n, int max_n, int splits, int stage) {
+  const int want = (max(n, max_n) + splits - 1) / splits;
+  return max(stage, (want + stage - 1) / stage * stage);
+}
+
 // Shared by the attention and combine kernels so both cut a row identically.
 __device__ __forceinline__ bool row_info(const AttnArgs& a, int supertile, RowInfo& ri) {
   const int b = blockIdx.y / a.max_q;
@@ -85,8 +94,7 @@ __device__ __forceinline__ bool row_info(const AttnArgs& a, int supertile, RowIn
   if (N <= 0) ri.n = 0;
   else if (a.idx) ri.n = max(0, min(a.count[ri.row], a.k));
   else ri.n = (int)min(a.q_pos[ri.row] / a.ratio, N);
-  const int want = (ri.n + a.splits - 1) / a.splits;
-  ri.per = max(supertile, (want + supertile - 1) / supertile * supertile);
+  ri.per = piece_size(ri.n, a.max_n, a.splits, supertile);
   ri.nsp = ri.n > 0 ? (ri.n + ri.per - 1) / ri.per : 1;
   return true;
 }
@@ -113,12 +121,18 @@ __device__ __forceinline__ bool row_info(const AttnArgs& a, int supertile, RowIn
 // would otherwise wait for every DMA in flight, the next stage's included.  The
 // waits are explicit (vmcnt), and no compiler-visible global load is in flight while
 // the pipeline runs: the sparse form copies a chunk of entry ids to LDS first.
+#ifndef AT_SUB64
+#define AT_SUB64 2          // 64 heads: 32-entry sub-tiles per wave per stage
+#endif
+#ifndef AT_NB64
+#define AT_NB64 2           // 64 heads: stage buffers
+#endif
 constexpr int AT_IDS = 2048;       // entry ids staged in LDS per chunk (sparse form)
 
-template <int ST, bool SPARSE>
+template <int ST, int NB, bool SPARSE>
 struct AttnDmaSmem {
-  i32x4 k[2][ST * 16];
-  i32x4 v[2][ST * 16];
+  i32x4 k[NB][ST * 16];
+  i32x4 v[NB][ST * 16];
   int ids[SPARSE ? AT_IDS : 1];
 };
 
@@ -126,8 +140,18 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(size_t)(const __attribute__((address_space(3))) char*)p;
 }
 
-// 64 lanes x 16 bytes from seq + voff (per lane) into LDS at lds .. lds + 1023
-__device__ __forceinline__ void dma16(const void* seq, uint32_t voff, uint32_t lds) {
+// 64 lanes x 16 bytes from seq + voff (per lane) into LDS at lds .. lds + 1023.
+// seq and lds are the same in every lane; they are read from the first lane so that
+// the compiler keeps them in scalar registers.
+__device__ __forceinline__ void dma16(const void* seq_any, uint32_t voff, uint32_t lds_any) {
+  const uint64_t sp = reinterpret_cast<uint64_t>(seq_any);
+  // readfirstlane returns int: convert through uint32_t so the low half is not
+  // sign-extended into the high half
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(sp >> 32));
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)sp);
+  const uint64_t su = ((uint64_t)hi << 32) | (uint64_t)lo;
+  const void* seq = reinterpret_cast<const void*>(su);
+  const uint32_t lds = (uint32_t)__builtin_amdgcn_readfirstlane((int)lds_any);
   uint32_t saved;
   asm volatile(
       "s_mov_b32 %0, m0\n\t"
@@ -154,19 +178,35 @@ __device__ __forceinline__ void lds_barrier() {
 
 // ES entry sub-groups of waves; each wave takes SUB consecutive 32-entry sub-tiles of
 // every stage, so a stage covers 32*ES*SUB entries.
-template <int ES, int SUB, bool SPARSE>
+template <int ES, int SUB, int NB, bool SPARSE>
 __global__ __launch_bounds__(AT_NT) void attn_dma_kernel(AttnBatch ab) {
   const AttnArgs& a = ab.a[blockIdx.z / ab.head_blocks];   // grid z = layer x head block
   constexpr int ST = 32 * ES * SUB;             // entries per super-tile (stage)
   constexpr int HG = 4 / ES;                    // head groups of 16 per work-group
   constexpr int NU = ST / 16;                   // DMA instructions per wave per matrix
   static_assert(NU >= 1 && NU <= 8 && AT_IDS % ST == 0, "stage size");
-  __shared__ AttnDmaSmem<ST, SPARSE> sm;
+  constexpr int D = NB - 1;                     // stages in flight ahead of the one in use
+  static_assert(NB >= 2 && D * 2 * NU < 64, "pipeline depth");
+  __shared__ AttnDmaSmem<ST, NB, SPARSE> sm;
 
-  RowInfo ri;
-  if (!row_info(a, ST, ri)) return;
+  // The loads that set up a work-group form a short dependency chain; the query,
+  // the first entry ids and the first stages' rows are issued as soon as their
+  // addresses are known, before the row's entry count (and so the exact end of the
+  // piece) is back.  Rows past the end are read but masked in the softmax.
+  const int b = blockIdx.y / a.max_q;
+  const int qi = blockIdx.y - b * a.max_q;
+  const int64_t r0 = a.q_off[b];
+  const int64_t nq = a.q_off[b + 1] - r0;
+  const int64_t e_base = a.ent_off[b];
+  const int64_t n_seq = a.ent_off[b + 1] - e_base;
+  if (qi >= nq) return;
+  const int64_t row = r0 + qi;
   const int s = blockIdx.x;
-  if (s >= ri.nsp) return;
+  // the row's entry count: only needed after the first DMAs are issued
+  const int n_raw = SPARSE ? a.count[row] : (int)min(a.q_pos[row] / a.ratio, (int64_t)INT32_MAX);
+  const int max_n = a.max_n;
+  const int splits = a.splits;
+  const int kk = a.k;
   const int h0 = (blockIdx.z % ab.head_blocks) * 64;
   const int t = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(t >> 6);
@@ -176,19 +216,15 @@ __global__ __launch_bounds__(AT_NT) void attn_dma_kernel(AttnBatch ab) {
   const int l16 = lane & 15;
   const int g = lane >> 4;
   const int head = h0 + hg * 16 + l16;
-  const int e0 = s * ri.per;
-  const int e1 = min(e0 + ri.per, ri.n);
   // kernel arguments used inside the pipeline are read once: the asm memory clobbers
   // would otherwise make the compiler reload them
   const float scale_log2 = a.scale_log2;
 
   bf16x8 qf[4];
   {
-    const i32x4* qp = reinterpret_cast<const i32x4*>(a.q + (ri.row * a.heads + head) * HD);
+    const i32x4* qp = reinterpret_cast<const i32x4*>(a.q + (row * a.heads + head) * HD);
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) qf[ks] = __builtin_bit_cast(bf16x8, qp[ks * 4 + g]);
-    // take the compiler's wait for the query here, before any DMA is in flight
-    asm volatile("" : "+v"(qf[0]), "+v"(qf[1]), "+v"(qf[2]), "+v"(qf[3]));
   }
   f32x4 o[8];
 #pragma unroll
@@ -199,16 +235,24 @@ __global__ __launch_bounds__(AT_NT) void attn_dma_kernel(AttnBatch ab) {
   // wave w fills rows w*ST/4 .. +ST/4 of a stage; DMA instruction u covers 4 of them
   const int wrow0 = w * (ST / 4);
   const int my_row = lane >> 4;
-  const int id_max = (int)min(ri.n_seq, (int64_t)ATTN_MAX_SEQ) - 1;
-  const char* kseq = reinterpret_cast<const char*>(a.kc + ri.e_base * HD);
-  const char* vseq = reinterpret_cast<const char*>(a.vc + ri.e_base * HD);
+  const int id_max = (int)min(n_seq, (int64_t)ATTN_MAX_SEQ) - 1;
+  const char* kseq = reinterpret_cast<const char*>(a.kc + e_base * HD);
+  const char* vseq = reinterpret_cast<const char*>(a.vc + e_base * HD);
   const uint32_t k_lds0 = lds_addr(&sm.k[0][wrow0 * 16]);
   const uint32_t v_lds0 = lds_addr(&sm.v[0][wrow0 * 16]);
   constexpr uint32_t BUF_BYTES = ST * 256;
 
+  // the piece as far as it is known before the entry count: exact when the count is
+  // within the bound (always for the sparse form); its end is where reads stay valid
+  const int per_g = piece_size(0, max_n, splits, ST);
+  const int e0_g = s * per_g;
+  const int end_g = n_seq <= 0 ? e0_g   // an empty sequence: nothing to fetch
+                    : SPARSE ? min(e0_g + per_g, kk)
+                             : (int)min((int64_t)e0_g + per_g, (int64_t)id_max + 1);
+
   // issue the DMA of the stage starting at entry tb into buffer buf; rows past
   // e_last repeat row e_last (cached, and masked in the softmax)
-  auto issue = [&](int buf, int tb, int cbase, int e_last) {
+  auto issue = [&](int buf, int tb, int cbase, int e_last) __attribute__((always_inline)) {
 #pragma unroll
     for (int u = 0; u < NU; ++u) {
       const int r = wrow0 + 4 * u + my_row;
@@ -222,7 +266,56 @@ __global__ __launch_bounds__(AT_NT) void attn_dma_kernel(AttnBatch ab) {
       dma16(vseq, row_off + cv, v_lds0 + buf * BUF_BYTES + u * 1024);
     }
   };
-  auto compute = [&](int buf, int tb) {
+  // copy the entry ids [cbase, cend) to LDS (sparse form; nothing else in flight)
+  auto load_ids = [&](int cbase, int cend) __attribute__((always_inline)) {
+    const int* src = a.idx + row * kk + cbase;
+    const int cnt = cend - cbase;
+    int v[AT_IDS / AT_NT];
+#pragma unroll
+    for (int u = 0; u < AT_IDS / AT_NT; ++u) {   // all loads in flight, then the stores
+      const int j = t + AT_NT * u;
+      v[u] = j < cnt ? src[j] : 0;
+    }
+    __syncthreads();   // the previous chunk's ids are no longer read
+#pragma unroll
+    for (int u = 0; u < AT_IDS / AT_NT; ++u) sm.ids[t + AT_NT * u] = v[u];
+    __syncthreads();
+  };
+  // first stages of a chunk, one per buffer; returns the number issued
+  auto prologue = [&](int cbase, int cend) __attribute__((always_inline)) {
+    const int nst = (cend - cbase + ST - 1) / ST;
+    const int p = min(NB, nst);
+#pragma unroll
+    for (int j = 0; j < NB; ++j)
+      if (j < p) issue(j, cbase + j * ST, cbase, cend - 1);
+    return p;
+  };
+
+  int issued = 0;
+  int cb0 = e0_g;
+  const int cend0 = SPARSE ? min(end_g, e0_g + AT_IDS) : end_g;
+  if (cend0 > e0_g) {
+    if constexpr (SPARSE) load_ids(e0_g, cend0);
+    issued = prologue(e0_g, cend0);
+  }
+  // the query is needed now: the compiler's wait for it lands here, behind the DMAs
+  asm volatile("" : "+v"(qf[0]), "+v"(qf[1]), "+v"(qf[2]), "+v"(qf[3]));
+
+  // as row_info computes it for the combine kernel
+  const int n = n_seq <= 0 ? 0 : SPARSE ? max(0, min(n_raw, kk)) : (int)min((int64_t)n_raw, n_seq);
+  const int per = piece_size(n, max_n, splits, ST);
+  const int nsp = n > 0 ? (n + per - 1) / per : 1;
+  if (s >= nsp || per != per_g) {
+    // outside the row, or a row beyond the bound: drop what was fetched speculatively
+    wait_vm<0>();
+    lds_barrier();
+    issued = 0;
+    if (s >= nsp) return;
+  }
+  const int e0 = s * per;
+  const int e1 = min(e0 + per, n);
+
+  auto compute = [&](int buf, int tb) __attribute__((always_inline)) {
     const i32x4* kb = sm.k[buf];
     const char* vbase = reinterpret_cast<const char*>(sm.v[buf]);
 #pragma unroll
@@ -289,47 +382,44 @@ __global__ __launch_bounds__(AT_NT) void attn_dma_kernel(AttnBatch ab) {
     }
   };
 
-  // Per stage: issue the next stage's DMA into the other buffer, wait for this
-  // stage's own DMA (the next stage's 2*NU operations may stay outstanding), barrier,
-  // compute, barrier (the buffer is then free for the DMA two stages ahead).
+
+  // Per stage: wait for this stage's DMA (the later stages' may stay outstanding),
+  // barrier, compute, barrier, then reuse the buffer for the stage NB ahead.
   for (int cbase = e0; cbase < e1; cbase += (SPARSE ? AT_IDS : (1 << 30))) {
     const int cend = SPARSE ? min(cbase + AT_IDS, e1) : e1;
-    const int e_last = cend - 1;
-    if constexpr (SPARSE) {
-      __syncthreads();   // the previous chunk's ids are no longer read
-      const int* src = a.idx + ri.row * a.k + cbase;
-      const int cnt = cend - cbase;
-      int v[AT_IDS / AT_NT];
-#pragma unroll
-      for (int u = 0; u < AT_IDS / AT_NT; ++u) {   // all loads in flight, then the stores
-        const int j = t + AT_NT * u;
-        v[u] = j < cnt ? src[j] : 0;
-      }
-#pragma unroll
-      for (int u = 0; u < AT_IDS / AT_NT; ++u) sm.ids[t + AT_NT * u] = v[u];
-      __syncthreads();
+    const int nst = (cend - cbase + ST - 1) / ST;
+    if (cbase != cb0 || issued == 0) {
+      wait_vm<0>();
+      if constexpr (SPARSE) load_ids(cbase, cend);
+      else lds_barrier();
+      issued = prologue(cbase, cend);
+      cb0 = cbase;
     }
     int buf = 0;
-    issue(0, cbase, cbase, e_last);
-    for (int tb = cbase; tb < cend; tb += ST) {
-      if (tb + ST < cend) {
-        issue(buf ^ 1, tb + ST, cbase, e_last);
-        wait_vm<2 * NU>();
-      } else {
-        wait_vm<0>();
+    for (int j = 0; j < nst; ++j) {
+      const int ahead = issued - 1 - j;   // stages issued after stage j
+      if (NB > 3 && ahead >= 3) wait_vm<(NB > 3 ? 3 : 0) * 2 * NU>();
+      else if (NB > 2 && ahead == 2) wait_vm<(NB > 2 ? 2 : 0) * 2 * NU>();
+      else if (ahead == 1) wait_vm<2 * NU>();
+      else wait_vm<0>();
+      lds_barrier();
+      compute(buf, cbase + j * ST);
+      lds_barrier();
+      if (j + NB < nst) {
+        issue(buf, cbase + (j + NB) * ST, cbase, cend - 1);
+        issued = j + NB + 1;
       }
-      lds_barrier();
-      compute(buf, tb);
-      lds_barrier();
-      buf ^= 1;
+      buf = buf + 1 == NB ? 0 : buf + 1;
     }
   }
+  wait_vm<0>();   // stages fetched past the end
 
   l_run += __shfl_xor(l_run, 16, WAVE);
   l_run += __shfl_xor(l_run, 32, WAVE);
 
   if (ES > 1) {
     // merge the ES entry sub-groups of each head group; the stage buffers are free
+    static_assert(sizeof(sm.k) >= 4 * 16 * HD * 4, "merge buffer");
     float* merge_o = reinterpret_cast<float*>(sm.k[0]);        // [4][16][HD]
     float* merge_ml = reinterpret_cast<float*>(sm.v[0]);       // [4][16][2]
     __syncthreads();
@@ -362,9 +452,9 @@ __global__ __launch_bounds__(AT_NT) void attn_dma_kernel(AttnBatch ab) {
     l_run = ll;
   }
 
-  if (ri.nsp == 1) {
+  if (nsp == 1) {
     const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
-    uint16_t* op = a.out + (ri.row * a.heads + head) * HD;
+    uint16_t* op = a.out + (row * a.heads + head) * HD;
 #pragma unroll
     for (int db = 0; db < 8; ++db) {
       uint2 pk;
@@ -373,10 +463,10 @@ __global__ __launch_bounds__(AT_NT) void attn_dma_kernel(AttnBatch ab) {
       *reinterpret_cast<uint2*>(op + db * 16 + 4 * g) = pk;
     }
     if (a.lse && g == 0)
-      a.lse[ri.row * a.heads + head] =
+      a.lse[row * a.heads + head] =
           l_run > 0.f ? (m_run + log2f(l_run)) * 0.69314718055994530942f : -INFINITY;
   } else {
-    const int64_t slot = (ri.row * a.splits + s) * a.heads + head;
+    const int64_t slot = (row * a.splits + s) * a.heads + head;
     float* pp = a.part_o + slot * HD;
 #pragma unroll
     for (int db = 0; db < 8; ++db) *reinterpret_cast<f32x4*>(pp + db * 16 + 4 * g) = o[db];
@@ -384,47 +474,80 @@ __global__ __launch_bounds__(AT_NT) void attn_dma_kernel(AttnBatch ab) {
   }
 }
 
-// Merge split partials: thread = (head, dim).  Up to CB pieces are loaded at once
-// (all of them for the default split count), then merged in piece order with a
-// running maximum, so the result does not depend on load timing.
-template <int ST>
-__global__ __launch_bounds__(256) void attn_combine_kernel(AttnBatch ab) {
+// Merge split partials: a work-group takes 2 heads of one row; per head, 32 dim
+// groups (4 dims, one 16-byte load per piece) x 4 piece groups (pieces g, g+4, ...).
+// Each thread merges its pieces in order with a running maximum, up to CB pieces per
+// round of loads, then piece group 0 merges the 4 groups' results in group order.
+// The result therefore does not depend on load timing.
+constexpr int CMB_HEADS = 2;
+constexpr int CMB_PG = 4;
+__global__ __launch_bounds__(256) void attn_combine_kernel(AttnBatch ab, int stage) {
   const AttnArgs& a = ab.a[blockIdx.z];   // grid z = layer
-  constexpr int CB = 32;
+  constexpr int CB = 8;
+  __shared__ float red[CMB_HEADS][CMB_PG][32][6];
   RowInfo ri;
-  if (!row_info(a, ST, ri)) return;
+  if (!row_info(a, stage, ri)) return;
   if (ri.nsp <= 1) return;
-  const int head = blockIdx.x * 2 + (threadIdx.x >> 7);
-  if (head >= a.heads) return;
-  const int d = threadIdx.x & 127;
+  const int hl = threadIdx.x >> 7;
+  const int head = blockIdx.x * CMB_HEADS + hl;   // heads is a multiple of CMB_HEADS
+  const int pg = (threadIdx.x >> 5) & (CMB_PG - 1);
+  const int dg = threadIdx.x & 31;
   const int64_t base = ri.row * a.splits * a.heads + head;
-  float mm = -INFINITY, ll = 0.f, acc = 0.f;
-  for (int s0 = 0; s0 < ri.nsp; s0 += CB) {
+  float mm = -INFINITY, ll = 0.f;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  for (int s0 = pg; s0 < ri.nsp; s0 += CB * CMB_PG) {
     float2 ml[CB];
-    float ov[CB];
+    f32x4 ov[CB];
 #pragma unroll
     for (int u = 0; u < CB; ++u) {
-      const bool in = s0 + u < ri.nsp;
-      const int64_t slot = base + (int64_t)(s0 + u) * a.heads;
-      ml[u] = in ? a.part_ml[slot] : make_float2(-INFINITY, 0.f);
-      ov[u] = in ? a.part_o[slot * HD + d] : 0.f;
+      const int sp = s0 + u * CMB_PG;
+      const bool in = sp < ri.nsp;
+      const int64_t slot = base + (int64_t)(in ? sp : s0) * a.heads;
+      ml[u] = a.part_ml[slot];
+      ov[u] = *reinterpret_cast<const f32x4*>(a.part_o + slot * HD + dg * 4);
+      if (!in) ml[u] = make_float2(-INFINITY, 0.f);
     }
     float mb = mm;
 #pragma unroll
     for (int u = 0; u < CB; ++u) mb = fmaxf(mb, ml[u].x);
-    const float r = exp2f(mm - mb);   // 0 on the first batch
+    const float r = exp2f(mm - mb);   // 0 on the first round
     ll *= r;
     acc *= r;
 #pragma unroll
     for (int u = 0; u < CB; ++u) {
-      const float f = exp2f(ml[u].x - mb);
+      const float f = exp2f(ml[u].x - mb);   // 0 for pieces past the end
       ll += ml[u].y * f;
       acc += ov[u] * f;
     }
     mm = mb;
   }
-  a.out[(ri.row * a.heads + head) * HD + d] = (uint16_t)f32_to_bf16_bits(acc / ll);
-  if (a.lse && d == 0) a.lse[ri.row * a.heads + head] = (mm + log2f(ll)) * 0.69314718055994530942f;
+  float* my = red[hl][pg][dg];
+  my[0] = mm;
+  my[1] = ll;
+  my[2] = acc[0];
+  my[3] = acc[1];
+  my[4] = acc[2];
+  my[5] = acc[3];
+  __syncthreads();
+  if (pg != 0) return;
+  float mt = -INFINITY;
+#pragma unroll
+  for (int q = 0; q < CMB_PG; ++q) mt = fmaxf(mt, red[hl][q][dg][0]);   // pg 0 holds piece 0
+  float lt = 0.f;
+  f32x4 at = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int q = 0; q < CMB_PG; ++q) {
+    const float* o = red[hl][q][dg];
+    const float f = o[0] == -INFINITY ? 0.f : exp2f(o[0] - mt);
+    lt += o[1] * f;
+    at += f32x4{o[2], o[3], o[4], o[5]} * f;
+  }
+  const float inv = 1.f / lt;
+  uint2 pk;
+  pk.x = f32_to_bf16_bits(at[0] * inv) | (f32_to_bf16_bits(at[1] * inv) << 16);
+  pk.y = f32_to_bf16_bits(at[2] * inv) | (f32_to_bf16_bits(at[3] * inv) << 16);
+  *reinterpret_cast<uint2*>(a.out + (ri.row * a.heads + head) * HD + dg * 4) = pk;
+  if (a.lse && dg == 0) a.lse[ri.row * a.heads + head] = (mt + log2f(lt)) * 0.69314718055994530942f;
 }
 
 hipError_t launch_attention(const AttnBatch& ab, int batch, hipStream_t st) {
@@ -437,23 +560,22 @@ hipError_t launch_attention(const AttnBatch& ab, int batch, hipStream_t st) {
   const bool sparse = a0.idx != nullptr;         // a batch holds one kind of layer
   int st_size;
   if (hg == 4) {
-    if (sparse) hipLaunchKernelGGL((attn_dma_kernel<1, 2, true>), grid, dim3(AT_NT), 0, st, ab);
-    else hipLaunchKernelGGL((attn_dma_kernel<1, 2, false>), grid, dim3(AT_NT), 0, st, ab);
-    st_size = 64;
+    if (sparse) hipLaunchKernelGGL((attn_dma_kernel<1, AT_SUB64, AT_NB64, true>), grid, dim3(AT_NT), 0, st, ab);
+    else hipLaunchKernelGGL((attn_dma_kernel<1, AT_SUB64, AT_NB64, false>), grid, dim3(AT_NT), 0, st, ab);
+    st_size = 32 * AT_SUB64;
   } else if (hg == 2) {
-    if (sparse) hipLaunchKernelGGL((attn_dma_kernel<2, 1, true>), grid, dim3(AT_NT), 0, st, ab);
-    else hipLaunchKernelGGL((attn_dma_kernel<2, 1, false>), grid, dim3(AT_NT), 0, st, ab);
+    if (sparse) hipLaunchKernelGGL((attn_dma_kernel<2, 1, 2, true>), grid, dim3(AT_NT), 0, st, ab);
+    else hipLaunchKernelGGL((attn_dma_kernel<2, 1, 2, false>), grid, dim3(AT_NT), 0, st, ab);
     st_size = 64;
   } else {
-    if (sparse) hipLaunchKernelGGL((attn_dma_kernel<4, 1, true>), grid, dim3(AT_NT), 0, st, ab);
-    else hipLaunchKernelGGL((attn_dma_kernel<4, 1, false>), grid, dim3(AT_NT), 0, st, ab);
+    if (sparse) hipLaunchKernelGGL((attn_dma_kernel<4, 1, 2, true>), grid, dim3(AT_NT), 0, st, ab);
+    else hipLaunchKernelGGL((attn_dma_kernel<4, 1, 2, false>), grid, dim3(AT_NT), 0, st, ab);
     st_size = 128;
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a0.splits <= 1) return e;
-  dim3 cgrid((unsigned)((a0.heads + 1) / 2), rows_grid, (unsigned)ab.n);
-  if (st_size == 64) hipLaunchKernelGGL(attn_combine_kernel<64>, cgrid, dim3(256), 0, st, ab);
-  else hipLaunchKernelGGL(attn_combine_kernel<128>, cgrid, dim3(256), 0, st, ab);
+  dim3 cgrid((unsigned)((a0.heads + CMB_HEADS - 1) / CMB_HEADS), rows_grid, (unsigned)ab.n);
+  hipLaunchKernelGGL(attn_combine_kernel, cgrid, dim3(256), 0, st, ab, st_size);
   return hipGetLastError();
 }
 

@@ -84,6 +84,7 @@ struct AttnArgs {
   int32_t max_q;
   int32_t heads;
   int32_t splits;
+  int32_t max_n;           // bound on a row's entries (k / max_entries): sets the piece size
   float scale_log2;        // scale * log2(e)
   uint16_t* out;
   float* lse;

@@ -28,6 +28,7 @@ _i32, _i64, _u32, _f32, _sz, _vp = (ctypes.c_int32, ctypes.c_int64, ctypes.c_uin
 LCA_LAYER_CSA = 0
 LCA_LAYER_HCA = 1
 LCA_TOPK_HIST_READY = 1
+LCA_HYBRID_PHASES = 4
 
 
 class LcaLayer(ctypes.Structure):
@@ -55,6 +56,8 @@ _SIGS = {
     "lca_hybrid_workspace_bytes": (_sz, [ctypes.POINTER(LcaLayer), _i32, _i32, _i32, _i32]),
     "lca_hybrid_layer_step": (_i32, [ctypes.POINTER(LcaLayer), _i32, _vp, _vp, _i32, _i32, _i32,
                                      _i32, _f32, _vp, _sz, _vp]),
+    "lca_hybrid_timing_enable": (_i32, [_i32]),
+    "lca_hybrid_timing_read": (_i32, [ctypes.POINTER(_f32), _i32]),
 }
 for _name, (_res, _args) in _SIGS.items():
     _fn = getattr(_lib, _name)
@@ -174,3 +177,15 @@ def hybrid_layer_step(layer_arr, q_off, q_pos, batch, max_q, heads, head_dim, sc
     _check("lca_hybrid_layer_step", _lib.lca_hybrid_layer_step(
         layer_arr, len(layer_arr), _p(q_off), _p(q_pos), batch, max_q, heads, head_dim, scale,
         _p(ws), _nb(ws), _s(stream)))
+
+
+def hybrid_timing_enable(enable: bool = True):
+    """Record HIP events around the phases of later hybrid steps (not under graph capture)."""
+    _check("lca_hybrid_timing_enable", _lib.lca_hybrid_timing_enable(1 if enable else 0))
+
+
+def hybrid_timing_read():
+    """[scores, top-k, CSA attention, HCA attention] of the last timed hybrid step, in ms."""
+    buf = (_f32 * LCA_HYBRID_PHASES)()
+    _check("lca_hybrid_timing_read", _lib.lca_hybrid_timing_read(buf, LCA_HYBRID_PHASES))
+    return [float(x) for x in buf]

@@ -55,6 +55,11 @@ struct LayerStreams {
   hipStream_t s[kLayerStreams];
   hipEvent_t fork;
   hipEvent_t join[kLayerStreams];
+  // phase timing: [0..1] scores, [1..2] top-k, [2..3] CSA attention, [4..5] HCA attention
+  hipEvent_t tev[6];
+  bool timing = false;
+  bool timed = false;     // a step recorded tev since timing was enabled
+  bool has_csa = false, has_hca = false;
   bool ready = false;
 };
 std::mutex g_streams_mu;
@@ -71,6 +76,8 @@ LayerStreams* layer_streams() {
       if (hipEventCreateWithFlags(&ls.join[i], hipEventDisableTiming) != hipSuccess) return nullptr;
     }
     if (hipEventCreateWithFlags(&ls.fork, hipEventDisableTiming) != hipSuccess) return nullptr;
+    for (int i = 0; i < 6; ++i)
+      if (hipEventCreate(&ls.tev[i]) != hipSuccess) return nullptr;
     ls.ready = true;
   }
   return &ls;
@@ -389,6 +396,15 @@ int32_t lca_hybrid_layer_step(const lca_layer* layers, int32_t n_layers, const i
   }
   hipError_t e = hipSuccess;
   const int hb = (heads + 63) / 64;
+  const bool timing = ls && ls->timing;
+  if (timing) {
+    ls->has_csa = !csa_a.empty();
+    ls->has_hca = !hca_a.empty();
+    ls->timed = true;
+  }
+  auto mark = [&](int i, hipStream_t s) {
+    if (timing && e == hipSuccess) e = hipEventRecord(ls->tev[i], s);
+  };
   for (size_t c0 = 0; c0 < csa_a.size() && e == hipSuccess; c0 += lca::MAX_BATCH_LAYERS) {
     const int n = (int)std::min<size_t>(lca::MAX_BATCH_LAYERS, csa_a.size() - c0);
     lca::IndexBatch ib{};
@@ -406,9 +422,14 @@ int32_t lca_hybrid_layer_step(const lca_layer* layers, int32_t n_layers, const i
       tb.layer[i] = tl[c0 + i];
       ab.a[i] = csa_a[c0 + i];
     }
+    const bool first = c0 == 0;
+    if (first) mark(0, s_csa);
     e = lca::launch_index_score(ib, batch, s_csa);
+    if (first) mark(1, s_csa);
     if (e == hipSuccess) e = lca::launch_topk(tb, rows, true, s_csa);
+    if (first) mark(2, s_csa);
     if (e == hipSuccess) e = lca::launch_attention(ab, batch, s_csa);
+    if (first) mark(3, s_csa);
   }
   for (size_t c0 = 0; c0 < hca_a.size() && e == hipSuccess; c0 += lca::MAX_BATCH_LAYERS) {
     const int n = (int)std::min<size_t>(lca::MAX_BATCH_LAYERS, hca_a.size() - c0);
@@ -416,7 +437,9 @@ int32_t lca_hybrid_layer_step(const lca_layer* layers, int32_t n_layers, const i
     ab.n = n;
     ab.head_blocks = hb;
     for (int i = 0; i < n; ++i) ab.a[i] = hca_a[c0 + i];
+    if (c0 == 0) mark(4, s_hca);
     e = lca::launch_attention(ab, batch, s_hca);
+    if (c0 == 0) mark(5, s_hca);
   }
   if (fork) {   // join, also after a failed launch so the caller's stream stays ordered
     (void)hipEventRecord(ls->join[0], s_csa);
@@ -425,6 +448,32 @@ int32_t lca_hybrid_layer_step(const lca_layer* layers, int32_t n_layers, const i
     (void)hipStreamWaitEvent(caller, ls->join[1], 0);
   }
   if (e != hipSuccess) return fail(LCA_ERR_HIP, "hybrid_layer_step: %s", hipGetErrorString(e));
+  return ok();
+}
+
+int32_t lca_hybrid_timing_enable(int32_t enable) {
+  LayerStreams* ls = layer_streams();
+  if (!ls) return fail(LCA_ERR_HIP, "hybrid_timing_enable: no device streams");
+  ls->timing = enable != 0;
+  ls->timed = false;
+  return ok();
+}
+
+int32_t lca_hybrid_timing_read(float* ms, int32_t n) {
+  if (!ms || n < 0) return fail(LCA_ERR_NULL, "hybrid_timing_read: ms NULL");
+  LayerStreams* ls = layer_streams();
+  if (!ls) return fail(LCA_ERR_HIP, "hybrid_timing_read: no device streams");
+  if (!ls->timing || !ls->timed) return fail(LCA_ERR_SHAPE, "hybrid_timing_read: no timed step");
+  float t[LCA_HYBRID_PHASES] = {0.f, 0.f, 0.f, 0.f};
+  const int pairs[LCA_HYBRID_PHASES][2] = {{0, 1}, {1, 2}, {2, 3}, {4, 5}};
+  for (int p = 0; p < LCA_HYBRID_PHASES; ++p) {
+    const bool present = p < 3 ? ls->has_csa : ls->has_hca;
+    if (!present) continue;
+    if (hipEventSynchronize(ls->tev[pairs[p][1]]) != hipSuccess ||
+        hipEventElapsedTime(&t[p], ls->tev[pairs[p][0]], ls->tev[pairs[p][1]]) != hipSuccess)
+      return fail(LCA_ERR_HIP, "hybrid_timing_read: event query");
+  }
+  for (int p = 0; p < n && p < LCA_HYBRID_PHASES; ++p) ms[p] = t[p];
   return ok();
 }
 

@@ -126,6 +126,10 @@ def test_hybrid_validation():
     assert f(arr, 2, FAKE, FAKE, 16, 1, 64, 128, 0.088, FAKE, need, None) == E_NULL
 
 
+def test_hybrid_timing_validation():
+    assert L().lca_hybrid_timing_read(None, 4) == E_NULL
+
+
 def test_no_oracle_in_product_path():
     # the product package never imports the oracle
     root = os.path.dirname(os.path.abspath(lca.__file__))

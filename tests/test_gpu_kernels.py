@@ -340,3 +340,16 @@ def test_hybrid_step_small():
                 r = oracle.hca_decode(qf[b], L[b], Kf[sl], Vf[sl], 128, SCALE)
             assert_attn_close(O[b], r["o"], f"layer {li} row {b}")
             assert_lse_close(LSE[b], r["lse"], f"layer {li} row {b}")
+    # phase timing: a timed eager step gives positive durations for all four phases and
+    # the same outputs as the untimed step
+    before = [Ld["out"].clone() for Ld in hs.layers]
+    lca.hybrid_timing_enable(True)
+    try:
+        hs.run(i64_dev(np.arange(B + 1)), i64_dev(q_pos), SCALE)
+        t = lca.hybrid_timing_read()
+    finally:
+        torch.cuda.synchronize()
+        lca.hybrid_timing_enable(False)
+    assert len(t) == 4 and all(x > 0 for x in t), t
+    for Ld, o in zip(hs.layers, before):
+        assert torch.equal(Ld["out"].view(torch.int16), o.view(torch.int16))

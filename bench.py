@@ -180,7 +180,7 @@ class HybridRunner(_Capture):
         finally:
             torch.cuda.synchronize()
             lca.hybrid_timing_enable(False)
-        self.phase_ms = [float(np.mean([x[p] for x in t])) for p in range(4)]
+        self.phase_ms = [float(np.mean([x[p] for x in t])) for p in range(len(t[0]))]
         return self.phase_ms[0]
 
     def dominant_units(self):
@@ -546,8 +546,7 @@ def main(argv=None):
         "cpu_baseline": None,
     }
     if hasattr(run, "phase_ms"):
-        line["phases_ms"] = dict(zip(["csa_scores", "csa_topk", "csa_attention", "hca_attention"],
-                                     run.phase_ms))
+        line["phases_ms"] = dict(zip(["csa_scores", "csa_topk", "attention"], run.phase_ms))
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = run.cpu_baseline(args.cpu_sample)
     print(json.dumps(line), flush=True)

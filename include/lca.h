@@ -189,15 +189,12 @@ int32_t lca_hca_dense_attn(const lca_bf16* q, const lca_bf16* k_cmp, const lca_b
  * batch, CSA and HCA interleaved (page section 3-2 item 2).  Each layer has its
  * own cache and queries; a CSA layer runs index_score -> topk_select ->
  * sparse_attn, an HCA layer dense_attn, with the same kernels as the single
- * calls.  Layers are independent and each has its own workspace region.  The
- * CSA layers run as batched phases (up to 8 layers per launch: scores, then
- * selection, then attention), the HCA layers as one batched attention launch;
- * with both kinds present the two run on the library's internal streams after
- * an event recorded on `stream`, and `stream` waits for both before the call
- * returns: work enqueued on `stream` afterwards sees every output.  Graph capture
- * of `stream` captures the fork and join.  With L layers the attention uses
- * 32 / min(L, 4) splits per row (decode), a function of the layer count only, so
- * a row's bits still do not depend on the rest of the batch.
+ * calls.  Layers are independent and each has its own workspace region.  All
+ * work is enqueued on `stream` in three phases: the CSA layers' scores and their
+ * top-k selection (up to 8 layers per launch), then the attention of every
+ * layer, CSA and HCA in the same launches (up to 8 layers each).  With L layers
+ * the attention uses 32 / min(L, 4) splits per row (decode), a function of the
+ * layer count only, so a row's bits still do not depend on the rest of the batch.
  * ------------------------------------------------------------------------- */
 enum lca_layer_kind { LCA_LAYER_CSA = 0, LCA_LAYER_HCA = 1 };
 
@@ -232,11 +229,11 @@ int32_t lca_hybrid_layer_step(const lca_layer* layers, int32_t n_layers, const i
  *   lca_hybrid_timing_enable(1 / 0) switches it on / off for the current device.
  *   lca_hybrid_timing_read(ms, n) waits for the last timed step and writes up to
  *   n durations in milliseconds: [0] indexer scores of the first batch of CSA
- *   layers (one launch), [1] their top-k selection, [2] their attention with the
- *   split combine, [3] the HCA attention with the split combine (0 for a phase
- *   the step did not have).  LCA_ERR_SHAPE if no timed step ran since enabling.
+ *   layers (one launch), [1] their top-k selection, [2] the attention of all
+ *   layers with the split combine (0 for a phase the step did not have).
+ *   LCA_ERR_SHAPE if no timed step ran since enabling.
  * ------------------------------------------------------------------------- */
-#define LCA_HYBRID_PHASES 4
+#define LCA_HYBRID_PHASES 3
 int32_t lca_hybrid_timing_enable(int32_t enable);
 int32_t lca_hybrid_timing_read(float* ms, int32_t n);
 

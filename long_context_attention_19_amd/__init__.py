@@ -28,7 +28,7 @@ _i32, _i64, _u32, _f32, _sz, _vp = (ctypes.c_int32, ctypes.c_int64, ctypes.c_uin
 LCA_LAYER_CSA = 0
 LCA_LAYER_HCA = 1
 LCA_TOPK_HIST_READY = 1
-LCA_HYBRID_PHASES = 4
+LCA_HYBRID_PHASES = 3
 
 
 class LcaLayer(ctypes.Structure):
@@ -185,7 +185,7 @@ def hybrid_timing_enable(enable: bool = True):
 
 
 def hybrid_timing_read():
-    """[scores, top-k, CSA attention, HCA attention] of the last timed hybrid step, in ms."""
+    """[scores, top-k, attention] of the last timed hybrid step, in ms."""
     buf = (_f32 * LCA_HYBRID_PHASES)()
     _check("lca_hybrid_timing_read", _lib.lca_hybrid_timing_read(buf, LCA_HYBRID_PHASES))
     return [float(x) for x in buf]

@@ -40,6 +40,14 @@ def hipcc() -> str:
     return p
 
 
+# per-file code generation options
+EXTRA = {
+    # MFMA accumulators in VGPRs: the online-softmax rescale and the masked tail
+    # otherwise move every accumulator between AGPRs and VGPRs on each stage
+    "attention.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+}
+
+
 def sources():
     return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC)
                   if f.endswith(".hip") or f.endswith(".cpp"))
@@ -48,7 +56,7 @@ def sources():
 def _compile(src: str) -> str:
     obj = os.path.join(OBJ_DIR, os.path.basename(src) + ".o")
     lang = ["-x", "hip"] if src.endswith(".hip") else []
-    cmd = [hipcc()] + COMMON + lang + ["-c", src, "-o", obj]
+    cmd = [hipcc()] + COMMON + EXTRA.get(os.path.basename(src), []) + lang + ["-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     # the host pass does not know the packed-fp32 feature and says so; that line is noise
     noise = "is not a recognized feature for this target"

@@ -55,11 +55,11 @@ struct LayerStreams {
   hipStream_t s[kLayerStreams];
   hipEvent_t fork;
   hipEvent_t join[kLayerStreams];
-  // phase timing: [0..1] scores, [1..2] top-k, [2..3] CSA attention, [4..5] HCA attention
-  hipEvent_t tev[6];
+  // phase timing: [0..1] scores, [1..2] top-k, [3..4] attention
+  hipEvent_t tev[5];
   bool timing = false;
   bool timed = false;     // a step recorded tev since timing was enabled
-  bool has_csa = false, has_hca = false;
+  bool has_csa = false;
   bool ready = false;
 };
 std::mutex g_streams_mu;
@@ -76,7 +76,7 @@ LayerStreams* layer_streams() {
       if (hipEventCreateWithFlags(&ls.join[i], hipEventDisableTiming) != hipSuccess) return nullptr;
     }
     if (hipEventCreateWithFlags(&ls.fork, hipEventDisableTiming) != hipSuccess) return nullptr;
-    for (int i = 0; i < 6; ++i)
+    for (int i = 0; i < 5; ++i)
       if (hipEventCreate(&ls.tev[i]) != hipSuccess) return nullptr;
     ls.ready = true;
   }
@@ -90,6 +90,41 @@ int hybrid_splits(int n_layers, int max_q) {
   const int base = lca::attn_auto_splits(max_q);
   const int conc = std::min(std::max(n_layers, 1), kLayerStreams);
   return std::max(1, base / conc);
+}
+
+// The hybrid step's attention takes the balanced persistent form when every launch
+// of up to 8 layers fits it (64-head blocks, at most ATTN_PS_MAX_ITEMS items, and
+// entry bounds that keep the runs short); one partial region serves all launches.
+struct HybridAttnPlan {
+  bool persist = false;
+  int G = 0;        // persistent work-groups: two per compute unit
+  int items = 0;    // largest launch
+};
+HybridAttnPlan hybrid_attn_plan(const lca_layer* layers, int n_layers, int rows, int heads) {
+  HybridAttnPlan p;
+  if (heads % 64 != 0 || rows <= 0) return p;
+  const int cu = lca_device_cu_count();
+  if (cu <= 0) return p;
+  const int G = 2 * cu;
+  const int hb = heads / 64;
+  int items_max = 0;
+  for (int c0 = 0; c0 < n_layers; c0 += lca::MAX_BATCH_LAYERS) {
+    const int n = std::min(lca::MAX_BATCH_LAYERS, n_layers - c0);
+    const int64_t items = (int64_t)n * rows * hb;
+    if (items > lca::ATTN_PS_MAX_ITEMS) return p;
+    int64_t stages = 0;
+    for (int l = c0; l < c0 + n; ++l) {
+      const int max_n = layers[l].kind == LCA_LAYER_CSA ? layers[l].topk : layers[l].max_entries;
+      stages += (int64_t)rows * hb *
+                std::max(1, (std::max(max_n, 0) + lca::ATTN_PS_STAGE - 1) / lca::ATTN_PS_STAGE);
+    }
+    if (stages > (int64_t)lca::ATTN_PS_MAX_RUN * G) return p;
+    items_max = std::max(items_max, (int)items);
+  }
+  p.persist = true;
+  p.G = G;
+  p.items = items_max;
+  return p;
 }
 
 size_t csa_layer_bytes(int rows, int max_entries, int topk, int heads, int splits) {
@@ -289,7 +324,8 @@ size_t lca_hybrid_workspace_bytes(const lca_layer* layers, int32_t n_layers, int
                                   int32_t max_q, int32_t heads) {
   if (!layers || n_layers <= 0 || batch <= 0 || max_q <= 0 || heads <= 0) return 0;
   const int rows = batch * max_q;
-  const int sp = hybrid_splits(n_layers, max_q);
+  const HybridAttnPlan plan = hybrid_attn_plan(layers, n_layers, rows, heads);
+  const int sp = plan.persist ? 1 : hybrid_splits(n_layers, max_q);
   size_t b = 0;
   for (int l = 0; l < n_layers; ++l) {
     if (layers[l].kind == LCA_LAYER_CSA)
@@ -298,6 +334,7 @@ size_t lca_hybrid_workspace_bytes(const lca_layer* layers, int32_t n_layers, int
     else
       b += lca::attn_ws_bytes(rows, heads, sp);
   }
+  if (plan.persist) b += lca::attn_persist_ws_bytes(plan.G, plan.items);
   return b;
 }
 
@@ -331,7 +368,8 @@ int32_t lca_hybrid_layer_step(const lca_layer* layers, int32_t n_layers, const i
   if (!std::isfinite(scale)) return fail(LCA_ERR_SHAPE, "hybrid_layer_step: scale not finite");
   const hipStream_t caller = (hipStream_t)stream;
   const int rows = batch * max_q;
-  const int sp = hybrid_splits(n_layers, max_q);
+  const HybridAttnPlan plan = hybrid_attn_plan(layers, n_layers, rows, heads);
+  const int sp = plan.persist ? 1 : hybrid_splits(n_layers, max_q);
   const float scale_log2 = scale * 1.4426950408889634f;
 
   // carve each layer's workspace region (layer order, as lca_hybrid_workspace_bytes sizes it)
@@ -382,31 +420,24 @@ int32_t lca_hybrid_layer_step(const lca_layer* layers, int32_t n_layers, const i
     }
   }
 
-  // CSA layers run as batched phases on one stream (scores -> select -> attend), HCA layers
-  // as batched dense attention on another; both fork from and join back to the caller.
+  // One stream, three phases: the CSA layers' scores and selections (batched, up to 8
+  // layers per launch), then the attention of every layer, CSA and HCA together in
+  // launches of up to 8 layers.  Everything is bound by HBM bandwidth except the
+  // selection, and one attention launch for all layers pays the pipeline start and
+  // drain once instead of per kind.
   LayerStreams* ls = layer_streams();
-  const bool fork = ls && !csa_a.empty() && !hca_a.empty();
-  const hipStream_t s_csa = fork ? ls->s[0] : caller;
-  const hipStream_t s_hca = fork ? ls->s[1] : caller;
-  if (fork) {
-    if (hipEventRecord(ls->fork, caller) != hipSuccess ||
-        hipStreamWaitEvent(s_csa, ls->fork, 0) != hipSuccess ||
-        hipStreamWaitEvent(s_hca, ls->fork, 0) != hipSuccess)
-      return fail(LCA_ERR_HIP, "hybrid_layer_step: fork");
-  }
   hipError_t e = hipSuccess;
   const int hb = (heads + 63) / 64;
   const bool timing = ls && ls->timing;
   if (timing) {
     ls->has_csa = !csa_a.empty();
-    ls->has_hca = !hca_a.empty();
     ls->timed = true;
   }
-  auto mark = [&](int i, hipStream_t s) {
-    if (timing && e == hipSuccess) e = hipEventRecord(ls->tev[i], s);
+  auto mark = [&](int i) {
+    if (timing && e == hipSuccess) e = hipEventRecord(ls->tev[i], caller);
   };
-  for (size_t c0 = 0; c0 < csa_a.size() && e == hipSuccess; c0 += lca::MAX_BATCH_LAYERS) {
-    const int n = (int)std::min<size_t>(lca::MAX_BATCH_LAYERS, csa_a.size() - c0);
+  for (size_t c0 = 0; c0 < il.size() && e == hipSuccess; c0 += lca::MAX_BATCH_LAYERS) {
+    const int n = (int)std::min<size_t>(lca::MAX_BATCH_LAYERS, il.size() - c0);
     lca::IndexBatch ib{};
     ib.q_off = q_off;
     ib.q_pos = q_pos;
@@ -414,39 +445,35 @@ int32_t lca_hybrid_layer_step(const lca_layer* layers, int32_t n_layers, const i
     ib.n = n;
     lca::TopkBatch tb{};
     tb.n = n;
-    lca::AttnBatch ab{};
-    ab.n = n;
-    ab.head_blocks = hb;
     for (int i = 0; i < n; ++i) {
       ib.layer[i] = il[c0 + i];
       tb.layer[i] = tl[c0 + i];
-      ab.a[i] = csa_a[c0 + i];
     }
     const bool first = c0 == 0;
-    if (first) mark(0, s_csa);
-    e = lca::launch_index_score(ib, batch, s_csa);
-    if (first) mark(1, s_csa);
-    if (e == hipSuccess) e = lca::launch_topk(tb, rows, true, s_csa);
-    if (first) mark(2, s_csa);
-    if (e == hipSuccess) e = lca::launch_attention(ab, batch, s_csa);
-    if (first) mark(3, s_csa);
+    if (first) mark(0);
+    e = lca::launch_index_score(ib, batch, caller);
+    if (first) mark(1);
+    if (e == hipSuccess) e = lca::launch_topk(tb, rows, true, caller);
+    if (first) mark(2);
   }
-  for (size_t c0 = 0; c0 < hca_a.size() && e == hipSuccess; c0 += lca::MAX_BATCH_LAYERS) {
-    const int n = (int)std::min<size_t>(lca::MAX_BATCH_LAYERS, hca_a.size() - c0);
+  mark(3);
+  std::vector<lca::AttnArgs> all = hca_a;   // longest rows first for the per-row form
+  all.insert(all.end(), csa_a.begin(), csa_a.end());
+  lca::AttnPersist pp{};
+  if (plan.persist) {
+    lca::attn_persist_carve(p, plan.G, plan.items, pp);
+    pp.rows = rows;
+  }
+  for (size_t c0 = 0; c0 < all.size() && e == hipSuccess; c0 += lca::MAX_BATCH_LAYERS) {
+    const int n = (int)std::min<size_t>(lca::MAX_BATCH_LAYERS, all.size() - c0);
     lca::AttnBatch ab{};
     ab.n = n;
     ab.head_blocks = hb;
-    for (int i = 0; i < n; ++i) ab.a[i] = hca_a[c0 + i];
-    if (c0 == 0) mark(4, s_hca);
-    e = lca::launch_attention(ab, batch, s_hca);
-    if (c0 == 0) mark(5, s_hca);
+    for (int i = 0; i < n; ++i) ab.a[i] = all[c0 + i];
+    e = plan.persist ? lca::launch_attention_persist(ab, pp, caller)
+                     : lca::launch_attention(ab, batch, caller);
   }
-  if (fork) {   // join, also after a failed launch so the caller's stream stays ordered
-    (void)hipEventRecord(ls->join[0], s_csa);
-    (void)hipEventRecord(ls->join[1], s_hca);
-    (void)hipStreamWaitEvent(caller, ls->join[0], 0);
-    (void)hipStreamWaitEvent(caller, ls->join[1], 0);
-  }
+  mark(4);
   if (e != hipSuccess) return fail(LCA_ERR_HIP, "hybrid_layer_step: %s", hipGetErrorString(e));
   return ok();
 }
@@ -464,10 +491,10 @@ int32_t lca_hybrid_timing_read(float* ms, int32_t n) {
   LayerStreams* ls = layer_streams();
   if (!ls) return fail(LCA_ERR_HIP, "hybrid_timing_read: no device streams");
   if (!ls->timing || !ls->timed) return fail(LCA_ERR_SHAPE, "hybrid_timing_read: no timed step");
-  float t[LCA_HYBRID_PHASES] = {0.f, 0.f, 0.f, 0.f};
-  const int pairs[LCA_HYBRID_PHASES][2] = {{0, 1}, {1, 2}, {2, 3}, {4, 5}};
+  float t[LCA_HYBRID_PHASES] = {0.f, 0.f, 0.f};
+  const int pairs[LCA_HYBRID_PHASES][2] = {{0, 1}, {1, 2}, {3, 4}};
   for (int p = 0; p < LCA_HYBRID_PHASES; ++p) {
-    const bool present = p < 3 ? ls->has_csa : ls->has_hca;
+    const bool present = p < 2 ? ls->has_csa : true;
     if (!present) continue;
     if (hipEventSynchronize(ls->tev[pairs[p][1]]) != hipSuccess ||
         hipEventElapsedTime(&t[p], ls->tev[pairs[p][0]], ls->tev[pairs[p][1]]) != hipSuccess)

@@ -129,11 +129,12 @@ __device__ __forceinline__ bool row_info(const AttnArgs& a, int supertile, RowIn
 #endif
 constexpr int AT_IDS = 2048;       // entry ids staged in LDS per chunk (sparse form)
 
-template <int ST, int NB, bool SPARSE>
+// MODE: 0 dense (HCA), 1 sparse (CSA), 2 either, per layer of the launch
+template <int ST, int NB, int MODE>
 struct AttnDmaSmem {
   i32x4 k[NB][ST * 16];
   i32x4 v[NB][ST * 16];
-  int ids[SPARSE ? AT_IDS : 1];
+  int ids[MODE != 0 ? AT_IDS : 1];
 };
 
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
@@ -176,18 +177,130 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
+// One stage of the online softmax attention for the 16 heads of this wave (head
+// l16 of the lane) over its SUB 32-entry sub-tiles starting at stage row el_base:
+// S^T = K Q^T from the stage's K tile, online softmax in log2 units, O^T += V^T P^T
+// with the V^T operand read transposed from the stage's V tile.  Entries at or past
+// e1 are masked (their rows were fetched but hold repeats).
+// max / sum over the 4 lanes that share l16 (lanes l16, l16+16, l16+32, l16+48):
+// v_permlane32_swap exchanges the two 32-lane halves, v_permlane16_swap the odd and
+// even 16-lane rows, both without LDS
+__device__ __forceinline__ float lanes4_max(float x) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float lanes4_sum(float x) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
+// One stage of the online softmax attention for the 16 heads of this wave (head
+// l16 of the lane) over its SUB 32-entry sub-tiles starting at stage row el_base:
+// S^T = K Q^T from the stage's K tile, online softmax in log2 units, O^T += V^T P^T
+// with the V^T operand read transposed from the stage's V tile.  Entries at or past
+// e1 are masked (their rows were fetched but hold repeats).  The running max is kept
+// in scaled log2 units; the exponent is one fma, v_exp_f32 without range fix-up (a
+// weight below 2^-126 flushes to 0, as it would in bf16).
+template <int SUB>
+__device__ __forceinline__ void attn_stage(const i32x4* kb, const char* vbase, int el_base, int tb,
+                                           int e1, const bf16x8 (&qf)[4], f32x4 (&o)[8],
+                                           float& m_run, float& l_run, float scale_log2, int l16,
+                                           int g) {
+#pragma unroll
+  for (int sub = 0; sub < SUB; ++sub) {
+    const int el0 = el_base + sub * 32;   // this wave's 32 entries of the stage
+    const int ev0 = tb + el0;
+    if (ev0 < e1) {
+      f32x4 sacc[2];
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb) {
+        sacc[rb] = f32x4{0.f, 0.f, 0.f, 0.f};
+        const int r = el0 + rb * 16 + l16;
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+          const bf16x8 kf = __builtin_bit_cast(bf16x8, kb[r * 16 + ((4 * ks + g) ^ (r & 15))]);
+          sacc[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[ks], sacc[rb], 0, 0, 0);
+        }
+      }
+      float x[8];
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) x[rb * 4 + i] = sacc[rb][i];
+      if (ev0 + 32 > e1) {   // the last sub-tile of the piece: mask entries >= e1
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (ev0 + rb * 16 + 4 * g + i >= e1) x[rb * 4 + i] = -INFINITY;
+      }
+      float mx = x[0];
+#pragma unroll
+      for (int i = 1; i < 8; ++i) mx = fmaxf(mx, x[i]);
+      mx = lanes4_max(mx) * scale_log2;            // scale > 0: max commutes with it
+      const float m_new = fmaxf(m_run, mx);         // finite: the wave has a valid entry
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);   // 0 first, 1 if unchanged
+      bf16x8 pf;
+      float psum = 0.f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const __bf16 pb = (__bf16)__builtin_amdgcn_exp2f(fmaf(x[i], scale_log2, -m_new));
+        pf[i] = pb;
+        psum += (float)pb;
+      }
+      l_run = l_run * alpha + psum;
+      if (__any(m_new > m_run)) {                 // otherwise every factor is exactly 1
+#pragma unroll
+        for (int db = 0; db < 8; ++db) o[db] *= alpha;
+      }
+      m_run = m_new;
+#pragma unroll
+      for (int db = 0; db < 8; ++db) {
+        bf16x4 half[2];
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          const int r = el0 + 16 * hh + 4 * g + (l16 >> 2);
+          const int q = l16 & 3;
+          const int off = r * 256 + (((2 * db + (q >> 1)) ^ ((r & 7) << 1)) << 4) + (q & 1) * 8;
+          half[hh] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+              (__attribute__((address_space(3))) bf16x4*)(vbase + off));
+        }
+        const bf16x8 vf = {half[0][0], half[0][1], half[0][2], half[0][3],
+                           half[1][0], half[1][1], half[1][2], half[1][3]};
+        o[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf, o[db], 0, 0, 0);
+      }
+    }
+  }
+}
+
+// The K and V row pieces of one DMA instruction: lane (r, slot l16) of instruction
+// u fetches row r's 16-byte chunk l16 ^ (r & 15) for K and l16 ^ 2(r & 7) for V.
+__device__ __forceinline__ void attn_issue_rows(const char* kseq, const char* vseq,
+                                                uint32_t row_off, int r, int l16, uint32_t k_lds,
+                                                uint32_t v_lds) {
+  const uint32_t ck = (uint32_t)(l16 ^ (r & 15)) << 4;
+  const uint32_t cv = (uint32_t)(l16 ^ ((r & 7) << 1)) << 4;
+  dma16(kseq, row_off + ck, k_lds);
+  dma16(vseq, row_off + cv, v_lds);
+}
+
 // ES entry sub-groups of waves; each wave takes SUB consecutive 32-entry sub-tiles of
 // every stage, so a stage covers 32*ES*SUB entries.
-template <int ES, int SUB, int NB, bool SPARSE>
+template <int ES, int SUB, int NB, int MODE>
 __global__ __launch_bounds__(AT_NT) void attn_dma_kernel(AttnBatch ab) {
   const AttnArgs& a = ab.a[blockIdx.z / ab.head_blocks];   // grid z = layer x head block
+  const bool sparse = MODE == 2 ? a.idx != nullptr : MODE == 1;   // uniform
   constexpr int ST = 32 * ES * SUB;             // entries per super-tile (stage)
   constexpr int HG = 4 / ES;                    // head groups of 16 per work-group
   constexpr int NU = ST / 16;                   // DMA instructions per wave per matrix
   static_assert(NU >= 1 && NU <= 8 && AT_IDS % ST == 0, "stage size");
   constexpr int D = NB - 1;                     // stages in flight ahead of the one in use
   static_assert(NB >= 2 && D * 2 * NU < 64, "pipeline depth");
-  __shared__ AttnDmaSmem<ST, NB, SPARSE> sm;
+  __shared__ AttnDmaSmem<ST, NB, MODE> sm;
 
   // The loads that set up a work-group form a short dependency chain; the query,
   // the first entry ids and the first stages' rows are issued as soon as their
@@ -203,7 +316,7 @@ __global__ __launch_bounds__(AT_NT) void attn_dma_kernel(AttnBatch ab) {
   const int64_t row = r0 + qi;
   const int s = blockIdx.x;
   // the row's entry count: only needed after the first DMAs are issued
-  const int n_raw = SPARSE ? a.count[row] : (int)min(a.q_pos[row] / a.ratio, (int64_t)INT32_MAX);
+  const int n_raw = sparse ? a.count[row] : (int)min(a.q_pos[row] / a.ratio, (int64_t)INT32_MAX);
   const int max_n = a.max_n;
   const int splits = a.splits;
   const int kk = a.k;
@@ -247,7 +360,7 @@ __global__ __launch_bounds__(AT_NT) void attn_dma_kernel(AttnBatch ab) {
   const int per_g = piece_size(0, max_n, splits, ST);
   const int e0_g = s * per_g;
   const int end_g = n_seq <= 0 ? e0_g   // an empty sequence: nothing to fetch
-                    : SPARSE ? min(e0_g + per_g, kk)
+                    : sparse ? min(e0_g + per_g, kk)
                              : (int)min((int64_t)e0_g + per_g, (int64_t)id_max + 1);
 
   // issue the DMA of the stage starting at entry tb into buffer buf; rows past
@@ -257,13 +370,10 @@ __global__ __launch_bounds__(AT_NT) void attn_dma_kernel(AttnBatch ab) {
     for (int u = 0; u < NU; ++u) {
       const int r = wrow0 + 4 * u + my_row;
       const int e = min(tb + r, e_last);
-      int id = SPARSE ? sm.ids[e - cbase] : e;
+      int id = (MODE != 0 && sparse) ? sm.ids[e - cbase] : e;
       id = min(max(id, 0), id_max);
-      const uint32_t row_off = (uint32_t)id * 256u;
-      const uint32_t ck = (uint32_t)(l16 ^ (r & 15)) << 4;
-      const uint32_t cv = (uint32_t)(l16 ^ ((r & 7) << 1)) << 4;
-      dma16(kseq, row_off + ck, k_lds0 + buf * BUF_BYTES + u * 1024);
-      dma16(vseq, row_off + cv, v_lds0 + buf * BUF_BYTES + u * 1024);
+      attn_issue_rows(kseq, vseq, (uint32_t)id * 256u, r, l16, k_lds0 + buf * BUF_BYTES + u * 1024,
+                      v_lds0 + buf * BUF_BYTES + u * 1024);
     }
   };
   // copy the entry ids [cbase, cend) to LDS (sparse form; nothing else in flight)
@@ -293,16 +403,16 @@ __global__ __launch_bounds__(AT_NT) void attn_dma_kernel(AttnBatch ab) {
 
   int issued = 0;
   int cb0 = e0_g;
-  const int cend0 = SPARSE ? min(end_g, e0_g + AT_IDS) : end_g;
+  const int cend0 = sparse ? min(end_g, e0_g + AT_IDS) : end_g;
   if (cend0 > e0_g) {
-    if constexpr (SPARSE) load_ids(e0_g, cend0);
+    if (MODE != 0 && sparse) load_ids(e0_g, cend0);
     issued = prologue(e0_g, cend0);
   }
   // the query is needed now: the compiler's wait for it lands here, behind the DMAs
   asm volatile("" : "+v"(qf[0]), "+v"(qf[1]), "+v"(qf[2]), "+v"(qf[3]));
 
   // as row_info computes it for the combine kernel
-  const int n = n_seq <= 0 ? 0 : SPARSE ? max(0, min(n_raw, kk)) : (int)min((int64_t)n_raw, n_seq);
+  const int n = n_seq <= 0 ? 0 : sparse ? max(0, min(n_raw, kk)) : (int)min((int64_t)n_raw, n_seq);
   const int per = piece_size(n, max_n, splits, ST);
   const int nsp = n > 0 ? (n + per - 1) / per : 1;
   if (s >= nsp || per != per_g) {
@@ -316,81 +426,18 @@ __global__ __launch_bounds__(AT_NT) void attn_dma_kernel(AttnBatch ab) {
   const int e1 = min(e0 + per, n);
 
   auto compute = [&](int buf, int tb) __attribute__((always_inline)) {
-    const i32x4* kb = sm.k[buf];
-    const char* vbase = reinterpret_cast<const char*>(sm.v[buf]);
-#pragma unroll
-    for (int sub = 0; sub < SUB; ++sub) {
-      const int el0 = (es * SUB + sub) * 32;   // this wave's 32 entries of the stage
-      const int ev0 = tb + el0;
-      if (ev0 < e1) {
-        f32x4 sacc[2];
-#pragma unroll
-        for (int rb = 0; rb < 2; ++rb) {
-          sacc[rb] = f32x4{0.f, 0.f, 0.f, 0.f};
-          const int r = el0 + rb * 16 + l16;
-#pragma unroll
-          for (int ks = 0; ks < 4; ++ks) {
-            const bf16x8 kf = __builtin_bit_cast(bf16x8, kb[r * 16 + ((4 * ks + g) ^ (r & 15))]);
-            sacc[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[ks], sacc[rb], 0, 0, 0);
-          }
-        }
-        float x[8];
-        float mx = -INFINITY;
-#pragma unroll
-        for (int rb = 0; rb < 2; ++rb)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int e = ev0 + rb * 16 + 4 * g + i;
-            const float v = (e < e1) ? sacc[rb][i] * scale_log2 : -INFINITY;
-            x[rb * 4 + i] = v;
-            mx = fmaxf(mx, v);
-          }
-        mx = fmaxf(mx, __shfl_xor(mx, 16, WAVE));
-        mx = fmaxf(mx, __shfl_xor(mx, 32, WAVE));
-        const float m_new = fmaxf(m_run, mx);       // finite: the wave has a valid entry
-        const float alpha = exp2f(m_run - m_new);   // 0 on the first tile, 1 if unchanged
-        bf16x8 pf;
-        float psum = 0.f;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const __bf16 pb = (__bf16)exp2f(x[i] - m_new);
-          pf[i] = pb;
-          psum += (float)pb;
-        }
-        l_run = l_run * alpha + psum;
-        if (__any(m_new > m_run)) {                 // otherwise every factor is exactly 1
-#pragma unroll
-          for (int db = 0; db < 8; ++db) o[db] *= alpha;
-        }
-        m_run = m_new;
-#pragma unroll
-        for (int db = 0; db < 8; ++db) {
-          bf16x4 half[2];
-#pragma unroll
-          for (int hh = 0; hh < 2; ++hh) {
-            const int r = el0 + 16 * hh + 4 * g + (l16 >> 2);
-            const int q = l16 & 3;
-            const int off = r * 256 + (((2 * db + (q >> 1)) ^ ((r & 7) << 1)) << 4) + (q & 1) * 8;
-            half[hh] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-                (__attribute__((address_space(3))) bf16x4*)(vbase + off));
-          }
-          const bf16x8 vf = {half[0][0], half[0][1], half[0][2], half[0][3],
-                             half[1][0], half[1][1], half[1][2], half[1][3]};
-          o[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf, o[db], 0, 0, 0);
-        }
-      }
-    }
+    attn_stage<SUB>(sm.k[buf], reinterpret_cast<const char*>(sm.v[buf]), es * SUB * 32, tb, e1, qf,
+                    o, m_run, l_run, scale_log2, l16, g);
   };
-
 
   // Per stage: wait for this stage's DMA (the later stages' may stay outstanding),
   // barrier, compute, barrier, then reuse the buffer for the stage NB ahead.
-  for (int cbase = e0; cbase < e1; cbase += (SPARSE ? AT_IDS : (1 << 30))) {
-    const int cend = SPARSE ? min(cbase + AT_IDS, e1) : e1;
+  for (int cbase = e0; cbase < e1; cbase += (sparse ? AT_IDS : (1 << 30))) {
+    const int cend = sparse ? min(cbase + AT_IDS, e1) : e1;
     const int nst = (cend - cbase + ST - 1) / ST;
     if (cbase != cb0 || issued == 0) {
       wait_vm<0>();
-      if constexpr (SPARSE) load_ids(cbase, cend);
+      if (MODE != 0 && sparse) load_ids(cbase, cend);
       else lds_barrier();
       issued = prologue(cbase, cend);
       cb0 = cbase;
@@ -414,8 +461,7 @@ __global__ __launch_bounds__(AT_NT) void attn_dma_kernel(AttnBatch ab) {
   }
   wait_vm<0>();   // stages fetched past the end
 
-  l_run += __shfl_xor(l_run, 16, WAVE);
-  l_run += __shfl_xor(l_run, 32, WAVE);
+  l_run = lanes4_sum(l_run);
 
   if (ES > 1) {
     // merge the ES entry sub-groups of each head group; the stage buffers are free
@@ -550,30 +596,408 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnBatch ab, int sta
   if (a.lse && dg == 0) a.lse[ri.row * a.heads + head] = (mt + log2f(lt)) * 0.69314718055994530942f;
 }
 
+// ---------------------------------------------------------------------------------
+// Balanced persistent form, for decode over a batch of layers (64-head blocks).
+// An item is (layer, row, 64-head block) with n entries; it takes max(1, ceil(n / 64))
+// stages (an empty item still takes one, to write its zero output).  The stages of
+// all items are laid end to end, S in total, and work-group g of G streams the run
+// [g*S/G, (g+1)*S/G) as one pipeline that crosses item boundaries.  An item that
+// lies wholly inside a run gets its output there; any other item leaves a partial
+// (O, max, sum) in slot 2g (the run's first item) or 2g + 1 (its last item), and the
+// persistent combine merges an item's partials in work-group order.  The split of an
+// item therefore depends on every item's length, unlike the per-row pieces above.
+__device__ __forceinline__ int ps_run_start(int g, int S, int G) {
+  return (int)((int64_t)g * S / G);
+}
+__device__ __forceinline__ int ps_group_of(int p, int S, int G) {   // run holding stage p
+  int g = (int)((int64_t)p * G / S);
+  while (g + 1 < G && ps_run_start(g + 1, S, G) <= p) ++g;
+  while (g > 0 && ps_run_start(g, S, G) > p) --g;
+  return g;
+}
+// last item whose first stage is <= j (items without stages share their successor's
+// offset, so the search lands on the item that owns stage j)
+__device__ __forceinline__ int ps_item_of(const int* pre, int W, int j) {
+  int lo = 0, hi = W;   // pre[lo] <= j < pre[hi]
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (pre[mid] <= j) lo = mid; else hi = mid;
+  }
+  return lo;
+}
+
+__global__ __launch_bounds__(AT_NT) void attn_persist_kernel(AttnBatch ab, AttnPersist pp) {
+  constexpr int ST = ATTN_PS_STAGE, SUB = 2, NU = ST / 16, NB = 2;
+  constexpr int MAXW = ATTN_PS_MAX_ITEMS;
+  static_assert(MAXW <= AT_NT && ATTN_PS_MAX_RUN * ST <= AT_IDS, "persistent sizes");
+  __shared__ i32x4 s_k[NB][ST * 16];
+  __shared__ i32x4 s_v[NB][ST * 16];
+  __shared__ int s_ids[AT_IDS];
+  __shared__ int s_pre[MAXW + 1];
+  __shared__ int4 s_item[MAXW];   // entries, first entry of the sequence, sequence size, query row
+  __shared__ int s_scan[AT_NT / WAVE + 1];
+
+  const int t = threadIdx.x;
+  const int R0 = pp.rows;
+  const int HB = ab.head_blocks;
+  const int W = ab.n * R0 * HB;   // the host keeps W <= MAXW
+  const int G = pp.G;
+  const int gid = blockIdx.x;
+
+  // ---- the plan: every work-group derives the same item table and stage offsets
+  int my_st = 0;
+  if (t < W) {
+    const int lr = t / HB;
+    const AttnArgs& a = ab.a[lr / R0];
+    const int r = lr % R0;
+    const int b = r / a.max_q;
+    const int qi = r - b * a.max_q;
+    const int64_t r0 = a.q_off[b];
+    int4 it = make_int4(0, 0, 0, -1);   // row -1: no such query
+    if (qi < a.q_off[b + 1] - r0) {
+      const int64_t eb = a.ent_off[b];
+      const int64_t ns = a.ent_off[b + 1] - eb;
+      const int64_t row = r0 + qi;
+      int n = 0;
+      if (ns > 0) n = a.idx ? min(a.count[row], a.k) : (int)min(a.q_pos[row] / a.ratio, ns);
+      n = max(n, 0);
+      it = make_int4(n, (int)eb, (int)min(ns, (int64_t)ATTN_MAX_SEQ), (int)row);
+      my_st = max(1, (n + ST - 1) / ST);
+    }
+    s_item[t] = it;
+  }
+  int S;
+  const int pre = block_excl_scan<AT_NT>(my_st, s_scan, &S);
+  if (t < W) s_pre[t] = pre;
+  if (t == 0) s_pre[W] = S;
+  if (gid == 0) {   // for the combine
+    if (t < W) {
+      pp.plan[t] = pre;
+      pp.plan[W + 1 + t] = s_item[t].w;
+    }
+    if (t == 0) pp.plan[W] = S;
+  }
+  __syncthreads();
+  const int s0 = ps_run_start(gid, S, G);
+  const int s1 = ps_run_start(gid + 1, S, G);
+  if (s0 >= s1) return;
+
+  const int w = __builtin_amdgcn_readfirstlane(t >> 6);   // wave = head group of 16
+  const int lane = t & 63;
+  const int l16 = lane & 15;
+  const int g = lane >> 4;
+  const int my_row = lane >> 4;
+  const int wrow0 = w * (ST / 4);
+  const uint32_t k_lds0 = lds_addr(&s_k[0][wrow0 * 16]);
+  const uint32_t v_lds0 = lds_addr(&s_v[0][wrow0 * 16]);
+  constexpr uint32_t BUF_BYTES = ST * 256;
+
+  bf16x8 qf[4], qn0[4], qn1[4];
+  f32x4 o[8];
+#pragma unroll
+  for (int db = 0; db < 8; ++db) o[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY, l_run = 0.f;
+  int cur = -1;     // item being accumulated
+  int nseg = 0;     // items started in this run
+  int nq = 0;       // queries prefetched
+  float scale_log2 = 0.f;
+
+  auto load_q = [&](int item) __attribute__((always_inline)) {
+    const AttnArgs& a = ab.a[(item / HB) / R0];
+    const int head = (item % HB) * 64 + w * 16 + l16;
+    const i32x4* qp = reinterpret_cast<const i32x4*>(a.q + ((int64_t)s_item[item].w * a.heads + head) * HD);
+    if (nq & 1) {
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) qn1[ks] = __builtin_bit_cast(bf16x8, qp[ks * 4 + g]);
+    } else {
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) qn0[ks] = __builtin_bit_cast(bf16x8, qp[ks * 4 + g]);
+    }
+    ++nq;
+  };
+  // DMA of global stage js into buffer buf (nothing for an empty item); returns
+  // whether anything was issued.  The first stage of an item in this run also
+  // prefetches the item's query.  Stages are issued in order, so the item is
+  // tracked, and its sequence pointers are kept, instead of looked up per stage.
+  int iss_item = ps_item_of(s_pre, W, s0);
+  int iss_pre = s_pre[iss_item], iss_next = s_pre[iss_item + 1];
+  int4 iss_it = s_item[iss_item];
+  const AttnArgs* iss_a = &ab.a[(iss_item / HB) / R0];
+  const char* iss_k = reinterpret_cast<const char*>(iss_a->kc + (int64_t)iss_it.y * HD);
+  const char* iss_v = reinterpret_cast<const char*>(iss_a->vc + (int64_t)iss_it.y * HD);
+  bool iss_sparse = iss_a->idx != nullptr;
+  auto issue = [&](int js, int buf, int c0) __attribute__((always_inline)) -> bool {
+    while (js >= iss_next) {   // next item (items without stages are passed over)
+      ++iss_item;
+      iss_pre = iss_next;
+      iss_next = s_pre[iss_item + 1];
+      iss_it = s_item[iss_item];
+      iss_a = &ab.a[(iss_item / HB) / R0];
+      iss_k = reinterpret_cast<const char*>(iss_a->kc + (int64_t)iss_it.y * HD);
+      iss_v = reinterpret_cast<const char*>(iss_a->vc + (int64_t)iss_it.y * HD);
+      iss_sparse = iss_a->idx != nullptr;
+    }
+    if (js == iss_pre || js == s0) load_q(iss_item);
+    if (iss_it.x <= 0) return false;
+    const int tb = (js - iss_pre) * ST;
+    const int e_last = iss_it.x - 1;
+#pragma unroll
+    for (int u = 0; u < NU; ++u) {
+      const int r = wrow0 + 4 * u + my_row;
+      const int e = min(tb + r, e_last);
+      int id = iss_sparse ? s_ids[(js - c0) * ST + (e - tb)] : e;
+      id = min(max(id, 0), iss_it.z - 1);
+      attn_issue_rows(iss_k, iss_v, (uint32_t)id * 256u, r, l16,
+                      k_lds0 + buf * BUF_BYTES + u * 1024, v_lds0 + buf * BUF_BYTES + u * 1024);
+    }
+    return true;
+  };
+  // output of item `item` from this run: final when the item lies inside the run,
+  // else a partial in slot 2g (first item of the run) or 2g + 1
+  auto finish = [&](int item) __attribute__((always_inline)) {
+    const float l = lanes4_sum(l_run);
+    const AttnArgs& a = ab.a[(item / HB) / R0];
+    const int hl = w * 16 + l16;
+    const int head = (item % HB) * 64 + hl;
+    const int64_t row = s_item[item].w;
+    if (s_pre[item] >= s0 && s_pre[item + 1] <= s1) {
+      const float inv = l > 0.f ? 1.f / l : 0.f;
+      uint16_t* op = a.out + (row * a.heads + head) * HD;
+#pragma unroll
+      for (int db = 0; db < 8; ++db) {
+        uint2 pk;
+        pk.x = f32_to_bf16_bits(o[db][0] * inv) | (f32_to_bf16_bits(o[db][1] * inv) << 16);
+        pk.y = f32_to_bf16_bits(o[db][2] * inv) | (f32_to_bf16_bits(o[db][3] * inv) << 16);
+        *reinterpret_cast<uint2*>(op + db * 16 + 4 * g) = pk;
+      }
+      if (a.lse && g == 0)
+        a.lse[row * a.heads + head] = l > 0.f ? (m_run + log2f(l)) * 0.69314718055994530942f : -INFINITY;
+    } else {
+      const int64_t slot = 2 * (int64_t)gid + (nseg > 1 ? 1 : 0);
+      float* pp_o = pp.part_o + (slot * 64 + hl) * HD;
+#pragma unroll
+      for (int db = 0; db < 8; ++db) *reinterpret_cast<f32x4*>(pp_o + db * 16 + 4 * g) = o[db];
+      if (g == 0) pp.part_ml[slot * 64 + hl] = make_float2(m_run, l);
+    }
+  };
+
+  int cmp_item = iss_item, cmp_pre = iss_pre, cmp_next = iss_next, cmp_n = 0;
+  for (int c0 = s0; c0 < s1; c0 += ATTN_PS_MAX_RUN) {
+    const int c1 = min(c0 + ATTN_PS_MAX_RUN, s1);
+    const int nst = c1 - c0;
+    // entry ids of the sparse stages of this part of the run (nothing is in flight)
+    {
+      int v[AT_IDS / AT_NT];
+#pragma unroll
+      for (int u = 0; u < AT_IDS / AT_NT; ++u) {
+        const int f = t + AT_NT * u;
+        const int js = c0 + f / ST;
+        v[u] = 0;
+        if (js < c1) {
+          const int item = ps_item_of(s_pre, W, js);
+          const AttnArgs& a = ab.a[(item / HB) / R0];
+          const int e = (js - s_pre[item]) * ST + f % ST;
+          if (a.idx && e < s_item[item].x) v[u] = a.idx[(int64_t)s_item[item].w * a.k + e];
+        }
+      }
+      __syncthreads();   // the previous part's ids are no longer read
+#pragma unroll
+      for (int u = 0; u < AT_IDS / AT_NT; ++u) s_ids[t + AT_NT * u] = v[u];
+      __syncthreads();
+    }
+    bool dma1 = false;                     // whether the stage after the current one fetched rows
+    const bool dma0 = issue(c0, 0, c0);
+    if (nst > 1) dma1 = issue(c0 + 1, 1, c0);
+    bool cur_dma = dma0;
+    (void)cur_dma;
+    for (int j = 0; j < nst; ++j) {
+      const int js = c0 + j;
+      const int buf = j & 1;
+      if (j + 1 < nst && dma1) wait_vm<2 * NU>();
+      else wait_vm<0>();
+      lds_barrier();
+      while (js >= cmp_next) {   // the item of stage js
+        ++cmp_item;
+        cmp_pre = cmp_next;
+        cmp_next = s_pre[cmp_item + 1];
+      }
+      const int item = cmp_item;
+      if (item != cur) {
+        if (cur >= 0) finish(cur);
+        // the query prefetched when this item's first stage was issued
+        const bool odd = (nseg & 1) != 0;
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) qf[ks] = odd ? qn1[ks] : qn0[ks];
+#pragma unroll
+        for (int db = 0; db < 8; ++db) o[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+        m_run = -INFINITY;
+        l_run = 0.f;
+        scale_log2 = ab.a[(item / HB) / R0].scale_log2;
+        cmp_n = s_item[item].x;
+        cur = item;
+        ++nseg;
+      }
+      attn_stage<SUB>(s_k[buf], reinterpret_cast<const char*>(s_v[buf]), 0, (js - cmp_pre) * ST,
+                      cmp_n, qf, o, m_run, l_run, scale_log2, l16, g);
+      lds_barrier();
+      dma1 = false;
+      if (j + 2 < nst) dma1 = issue(js + 2, buf, c0);
+    }
+    wait_vm<0>();
+  }
+  if (cur >= 0) finish(cur);
+}
+
+// Merge an item's partials from consecutive work-groups, as attn_combine_kernel does
+// for per-row pieces.  grid (32, items): 2 heads per work-group.
+__global__ __launch_bounds__(256) void attn_persist_combine_kernel(AttnBatch ab, AttnPersist pp) {
+  constexpr int CB = 8;
+  __shared__ float red[CMB_HEADS][CMB_PG][32][6];
+  const int R0 = pp.rows;
+  const int HB = ab.head_blocks;
+  const int W = ab.n * R0 * HB;
+  const int item = blockIdx.y;
+  if (item >= W) return;
+  const int* plan = pp.plan;
+  const int S = plan[W];
+  const int p0 = plan[item], p1 = plan[item + 1];
+  if (p1 <= p0) return;   // no such query row
+  const int G = pp.G;
+  const int g_first = ps_group_of(p0, S, G);
+  const int g_last = ps_group_of(p1 - 1, S, G);
+  if (g_first == g_last) return;   // written whole by its run
+  const int npc = g_last - g_first + 1;
+  const bool first_is_last_slot = p0 > ps_run_start(g_first, S, G);
+  const AttnArgs& a = ab.a[(item / HB) / R0];
+  const int hl = blockIdx.x * CMB_HEADS + (threadIdx.x >> 7);
+  const int head = (item % HB) * 64 + hl;
+  const int pg = (threadIdx.x >> 5) & (CMB_PG - 1);
+  const int dg = threadIdx.x & 31;
+  float mm = -INFINITY, ll = 0.f;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  for (int s0 = pg; s0 < npc; s0 += CB * CMB_PG) {
+    float2 ml[CB];
+    f32x4 ov[CB];
+#pragma unroll
+    for (int u = 0; u < CB; ++u) {
+      const int pc = s0 + u * CMB_PG;
+      const bool in = pc < npc;
+      const int pcc = in ? pc : s0;
+      const int64_t slot = 2 * (int64_t)(g_first + pcc) + ((pcc == 0 && first_is_last_slot) ? 1 : 0);
+      ml[u] = pp.part_ml[slot * 64 + hl];
+      ov[u] = *reinterpret_cast<const f32x4*>(pp.part_o + (slot * 64 + hl) * HD + dg * 4);
+      if (!in) ml[u] = make_float2(-INFINITY, 0.f);
+    }
+    float mb = mm;
+#pragma unroll
+    for (int u = 0; u < CB; ++u) mb = fmaxf(mb, ml[u].x);
+    const float r = exp2f(mm - mb);
+    ll *= r;
+    acc *= r;
+#pragma unroll
+    for (int u = 0; u < CB; ++u) {
+      const float f = exp2f(ml[u].x - mb);
+      ll += ml[u].y * f;
+      acc += ov[u] * f;
+    }
+    mm = mb;
+  }
+  float* my = red[threadIdx.x >> 7][pg][dg];
+  my[0] = mm;
+  my[1] = ll;
+  my[2] = acc[0];
+  my[3] = acc[1];
+  my[4] = acc[2];
+  my[5] = acc[3];
+  __syncthreads();
+  if (pg != 0) return;
+  const int hw = threadIdx.x >> 7;
+  float mt = -INFINITY;
+#pragma unroll
+  for (int q = 0; q < CMB_PG; ++q) mt = fmaxf(mt, red[hw][q][dg][0]);
+  float lt = 0.f;
+  f32x4 at = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int q = 0; q < CMB_PG; ++q) {
+    const float* o = red[hw][q][dg];
+    const float f = o[0] == -INFINITY ? 0.f : exp2f(o[0] - mt);
+    lt += o[1] * f;
+    at += f32x4{o[2], o[3], o[4], o[5]} * f;
+  }
+  const int64_t row = plan[W + 1 + item];
+  const float inv = lt > 0.f ? 1.f / lt : 0.f;
+  uint2 pk;
+  pk.x = f32_to_bf16_bits(at[0] * inv) | (f32_to_bf16_bits(at[1] * inv) << 16);
+  pk.y = f32_to_bf16_bits(at[2] * inv) | (f32_to_bf16_bits(at[3] * inv) << 16);
+  *reinterpret_cast<uint2*>(a.out + (row * a.heads + head) * HD + dg * 4) = pk;
+  if (a.lse && dg == 0)
+    a.lse[row * a.heads + head] = lt > 0.f ? (mt + log2f(lt)) * 0.69314718055994530942f : -INFINITY;
+}
+
+size_t attn_persist_ws_bytes(int G, int items) {
+  return align256((size_t)2 * G * 64 * HD * 4) + align256((size_t)2 * G * 64 * 8) +
+         align256((size_t)(2 * items + 1) * 4);
+}
+
+void attn_persist_carve(void* ws, int G, int items, AttnPersist& pp) {
+  char* p = reinterpret_cast<char*>(ws);
+  pp.part_o = reinterpret_cast<float*>(p);
+  p += align256((size_t)2 * G * 64 * HD * 4);
+  pp.part_ml = reinterpret_cast<float2*>(p);
+  p += align256((size_t)2 * G * 64 * 8);
+  pp.plan = reinterpret_cast<int32_t*>(p);
+  pp.G = G;
+}
+
+bool attn_persist_fits(const AttnBatch& ab, int rows, int G) {
+  if (ab.n == 0 || G <= 0) return false;
+  if (ab.a[0].heads % 64 != 0) return false;
+  const int64_t items = (int64_t)ab.n * rows * ab.head_blocks;
+  if (items > ATTN_PS_MAX_ITEMS) return false;
+  int64_t stages = 0;   // bound on S from the host bounds on the entry counts
+  for (int l = 0; l < ab.n; ++l)
+    stages += (int64_t)rows * ab.head_blocks *
+              max(1, (ab.a[l].max_n + ATTN_PS_STAGE - 1) / ATTN_PS_STAGE);
+  return stages <= (int64_t)ATTN_PS_MAX_RUN * G;
+}
+
+hipError_t launch_attention_persist(const AttnBatch& ab, const AttnPersist& pp, hipStream_t st) {
+  if (ab.n == 0 || pp.rows == 0) return hipSuccess;
+  const int items = ab.n * pp.rows * ab.head_blocks;
+  hipLaunchKernelGGL(attn_persist_kernel, dim3((unsigned)pp.G), dim3(AT_NT), 0, st, ab, pp);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(attn_persist_combine_kernel, dim3(64 / CMB_HEADS, (unsigned)items), dim3(256),
+                     0, st, ab, pp);
+  return hipGetLastError();
+}
+
 hipError_t launch_attention(const AttnBatch& ab, int batch, hipStream_t st) {
   if (batch == 0 || ab.n == 0) return hipSuccess;
-  const AttnArgs& a0 = ab.a[0];   // heads, splits and max_q are shared by the batch
+  const AttnArgs& a0 = ab.a[0];   // heads and max_q are shared by the batch
   if (a0.max_q == 0) return hipSuccess;
+  int max_splits = 1;               // each layer has its own split count
+  for (int l = 0; l < ab.n; ++l) max_splits = max(max_splits, ab.a[l].splits);
   const int hg = min(a0.heads, 64) / 16;          // 1, 2 or 4
   const unsigned rows_grid = (unsigned)(batch * a0.max_q);
-  dim3 grid((unsigned)a0.splits, rows_grid, (unsigned)(ab.n * ab.head_blocks));
-  const bool sparse = a0.idx != nullptr;         // a batch holds one kind of layer
+  dim3 grid((unsigned)max_splits, rows_grid, (unsigned)(ab.n * ab.head_blocks));
+  int n_sparse = 0;
+  for (int l = 0; l < ab.n; ++l) n_sparse += ab.a[l].idx != nullptr;
+  const int mode = n_sparse == 0 ? 0 : n_sparse == ab.n ? 1 : 2;
   int st_size;
-  if (hg == 4) {
-    if (sparse) hipLaunchKernelGGL((attn_dma_kernel<1, AT_SUB64, AT_NB64, true>), grid, dim3(AT_NT), 0, st, ab);
-    else hipLaunchKernelGGL((attn_dma_kernel<1, AT_SUB64, AT_NB64, false>), grid, dim3(AT_NT), 0, st, ab);
-    st_size = 32 * AT_SUB64;
-  } else if (hg == 2) {
-    if (sparse) hipLaunchKernelGGL((attn_dma_kernel<2, 1, 2, true>), grid, dim3(AT_NT), 0, st, ab);
-    else hipLaunchKernelGGL((attn_dma_kernel<2, 1, 2, false>), grid, dim3(AT_NT), 0, st, ab);
-    st_size = 64;
-  } else {
-    if (sparse) hipLaunchKernelGGL((attn_dma_kernel<4, 1, 2, true>), grid, dim3(AT_NT), 0, st, ab);
-    else hipLaunchKernelGGL((attn_dma_kernel<4, 1, 2, false>), grid, dim3(AT_NT), 0, st, ab);
-    st_size = 128;
-  }
+#define LCA_ATTN_LAUNCH(ES, SUB, NB)                                                          \
+  do {                                                                                        \
+    if (mode == 0) hipLaunchKernelGGL((attn_dma_kernel<ES, SUB, NB, 0>), grid, dim3(AT_NT), 0, st, ab); \
+    else if (mode == 1) hipLaunchKernelGGL((attn_dma_kernel<ES, SUB, NB, 1>), grid, dim3(AT_NT), 0, st, ab); \
+    else hipLaunchKernelGGL((attn_dma_kernel<ES, SUB, NB, 2>), grid, dim3(AT_NT), 0, st, ab); \
+    st_size = 32 * ES * SUB;                                                                  \
+  } while (0)
+  if (hg == 4) LCA_ATTN_LAUNCH(1, AT_SUB64, AT_NB64);
+  else if (hg == 2) LCA_ATTN_LAUNCH(2, 1, 2);
+  else LCA_ATTN_LAUNCH(4, 1, 2);
+#undef LCA_ATTN_LAUNCH
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess || a0.splits <= 1) return e;
+  if (e != hipSuccess || max_splits <= 1) return e;
   dim3 cgrid((unsigned)((a0.heads + CMB_HEADS - 1) / CMB_HEADS), rows_grid, (unsigned)ab.n);
   hipLaunchKernelGGL(attn_combine_kernel, cgrid, dim3(256), 0, st, ab, st_size);
   return hipGetLastError();

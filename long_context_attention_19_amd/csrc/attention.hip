@@ -848,11 +848,13 @@ __global__ __launch_bounds__(AT_NT) void attn_persist_kernel(AttnBatch ab, AttnP
   if (cur >= 0) finish(cur);
 }
 
-// Merge an item's partials from consecutive work-groups, as attn_combine_kernel does
-// for per-row pieces.  grid (32, items): 2 heads per work-group.
+// Merge an item's partials from consecutive work-groups, in work-group order.
+// grid (64 / 8, items): a work-group takes 8 heads of one item, 32 threads per head
+// (4 dims each), and loads up to CB pieces per round, all of them in one round for
+// the usual item sizes.
+constexpr int PSC_HEADS = 8;
 __global__ __launch_bounds__(256) void attn_persist_combine_kernel(AttnBatch ab, AttnPersist pp) {
   constexpr int CB = 8;
-  __shared__ float red[CMB_HEADS][CMB_PG][32][6];
   const int R0 = pp.rows;
   const int HB = ab.head_blocks;
   const int W = ab.n * R0 * HB;
@@ -869,20 +871,19 @@ __global__ __launch_bounds__(256) void attn_persist_combine_kernel(AttnBatch ab,
   const int npc = g_last - g_first + 1;
   const bool first_is_last_slot = p0 > ps_run_start(g_first, S, G);
   const AttnArgs& a = ab.a[(item / HB) / R0];
-  const int hl = blockIdx.x * CMB_HEADS + (threadIdx.x >> 7);
+  const int hl = blockIdx.x * PSC_HEADS + (threadIdx.x >> 5);
   const int head = (item % HB) * 64 + hl;
-  const int pg = (threadIdx.x >> 5) & (CMB_PG - 1);
   const int dg = threadIdx.x & 31;
   float mm = -INFINITY, ll = 0.f;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  for (int s0 = pg; s0 < npc; s0 += CB * CMB_PG) {
+  for (int c0 = 0; c0 < npc; c0 += CB) {
     float2 ml[CB];
     f32x4 ov[CB];
 #pragma unroll
     for (int u = 0; u < CB; ++u) {
-      const int pc = s0 + u * CMB_PG;
+      const int pc = c0 + u;
       const bool in = pc < npc;
-      const int pcc = in ? pc : s0;
+      const int pcc = in ? pc : c0;
       const int64_t slot = 2 * (int64_t)(g_first + pcc) + ((pcc == 0 && first_is_last_slot) ? 1 : 0);
       ml[u] = pp.part_ml[slot * 64 + hl];
       ov[u] = *reinterpret_cast<const f32x4*>(pp.part_o + (slot * 64 + hl) * HD + dg * 4);
@@ -891,47 +892,25 @@ __global__ __launch_bounds__(256) void attn_persist_combine_kernel(AttnBatch ab,
     float mb = mm;
 #pragma unroll
     for (int u = 0; u < CB; ++u) mb = fmaxf(mb, ml[u].x);
-    const float r = exp2f(mm - mb);
+    const float r = exp2f(mm - mb);   // 0 on the first round
     ll *= r;
     acc *= r;
 #pragma unroll
     for (int u = 0; u < CB; ++u) {
-      const float f = exp2f(ml[u].x - mb);
+      const float f = exp2f(ml[u].x - mb);   // 0 for pieces past the end
       ll += ml[u].y * f;
       acc += ov[u] * f;
     }
     mm = mb;
   }
-  float* my = red[threadIdx.x >> 7][pg][dg];
-  my[0] = mm;
-  my[1] = ll;
-  my[2] = acc[0];
-  my[3] = acc[1];
-  my[4] = acc[2];
-  my[5] = acc[3];
-  __syncthreads();
-  if (pg != 0) return;
-  const int hw = threadIdx.x >> 7;
-  float mt = -INFINITY;
-#pragma unroll
-  for (int q = 0; q < CMB_PG; ++q) mt = fmaxf(mt, red[hw][q][dg][0]);
-  float lt = 0.f;
-  f32x4 at = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int q = 0; q < CMB_PG; ++q) {
-    const float* o = red[hw][q][dg];
-    const float f = o[0] == -INFINITY ? 0.f : exp2f(o[0] - mt);
-    lt += o[1] * f;
-    at += f32x4{o[2], o[3], o[4], o[5]} * f;
-  }
   const int64_t row = plan[W + 1 + item];
-  const float inv = lt > 0.f ? 1.f / lt : 0.f;
+  const float inv = ll > 0.f ? 1.f / ll : 0.f;
   uint2 pk;
-  pk.x = f32_to_bf16_bits(at[0] * inv) | (f32_to_bf16_bits(at[1] * inv) << 16);
-  pk.y = f32_to_bf16_bits(at[2] * inv) | (f32_to_bf16_bits(at[3] * inv) << 16);
+  pk.x = f32_to_bf16_bits(acc[0] * inv) | (f32_to_bf16_bits(acc[1] * inv) << 16);
+  pk.y = f32_to_bf16_bits(acc[2] * inv) | (f32_to_bf16_bits(acc[3] * inv) << 16);
   *reinterpret_cast<uint2*>(a.out + (row * a.heads + head) * HD + dg * 4) = pk;
   if (a.lse && dg == 0)
-    a.lse[row * a.heads + head] = lt > 0.f ? (mt + log2f(lt)) * 0.69314718055994530942f : -INFINITY;
+    a.lse[row * a.heads + head] = ll > 0.f ? (mm + log2f(ll)) * 0.69314718055994530942f : -INFINITY;
 }
 
 size_t attn_persist_ws_bytes(int G, int items) {
@@ -967,7 +946,7 @@ hipError_t launch_attention_persist(const AttnBatch& ab, const AttnPersist& pp, 
   hipLaunchKernelGGL(attn_persist_kernel, dim3((unsigned)pp.G), dim3(AT_NT), 0, st, ab, pp);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(attn_persist_combine_kernel, dim3(64 / CMB_HEADS, (unsigned)items), dim3(256),
+  hipLaunchKernelGGL(attn_persist_combine_kernel, dim3(64 / PSC_HEADS, (unsigned)items), dim3(256),
                      0, st, ab, pp);
   return hipGetLastError();
 }

@@ -17,11 +17,15 @@
 //   K1 hist  — coarse histogram (LDS, one global atomic per non-empty bin) and
 //              zeroing of the row's fine histogram.  The index-score kernel can
 //              do this pass while it computes the scores.
-//   K2 cand  — threshold bin bA from the coarse histogram; per chunk, the count
-//              of keys above bA, and the keys inside bA (few: ~k/8 per row for
-//              Gaussian-like scores) compacted in index order with their low 10
-//              bits, which also go to the fine histogram.
-//   K3 place — T and the number of T-valued keys to keep follow from the fine
+//   K2 cand  — threshold bin bA from the coarse histogram; per chunk, the keys
+//              above bA (their local indices) and the keys inside bA (few: ~k/8
+//              per row for Gaussian-like scores, with their low 10 bits, which
+//              also go to the fine histogram), each compacted in index order.
+//   K3 merge — (k <= 4096, 32 rows or more) one work-group per row: T and the quota of T-valued
+//              keys from the fine histogram, then the row's candidate lists merged
+//              in index order; no score is read again.  The coarse histogram is
+//              cleared here.
+//   K3 place — (otherwise) T and the number of T-valued keys to keep follow from the fine
 //              histogram; a chunk's output offset is the number of selected keys
 //              in earlier chunks: their above-bA counts plus the earlier chunks'
 //              threshold-bin keys that beat T or are T-valued within the quota.
@@ -196,17 +200,22 @@ __global__ __launch_bounds__(TK_NT) void topk_cand_kernel(TopkBatch tb) {
     }
   }
   int32_t atot, btot;
-  (void)block_excl_scan<TK_NT>(na, s_scan, &atot);
+  int32_t aoff = block_excl_scan<TK_NT>(na, s_scan, &atot);
   int32_t off = block_excl_scan<TK_NT>(nb, s_scan, &btot);
   const int64_t slot = (int64_t)row * w.nchunks + ch;
+  // the chunk's region: local indices of its above-bA keys, then its bA keys
   int32_t* keys = w.bin_keys + slot * TK_CHUNK;
   int32_t* frow = w.fine + (int64_t)row * FINE_BINS;
+  off += atot;
 #pragma unroll
   for (int e = 0; e < 16; ++e) {
     if (j0 + e < n) {
       const int key = v[e] + KEY_BIAS;
-      if ((key >> 10) == bA) {
-        keys[off++] = ((t * TK_PER_THREAD + e) << 10) | (key & 1023);
+      const int li = t * TK_PER_THREAD + e;
+      if ((key >> 10) > bA) {
+        keys[aoff++] = li;
+      } else if ((key >> 10) == bA) {
+        keys[off++] = (li << 10) | (key & 1023);
         atomicAdd(frow + (key & 1023), 1);
       }
     }
@@ -232,6 +241,7 @@ __global__ __launch_bounds__(TK_NT) void topk_place_kernel(TopkBatch tb) {
   __shared__ int32_t s_scan[TK_NT / WAVE + 1];
   __shared__ int32_t s_b[2];
   __shared__ int32_t s_pre[TK_MAX_CHUNKS + 1];   // prefix of earlier chunks' bin counts
+  __shared__ int32_t s_ca[TK_MAX_CHUNKS];        // earlier chunks' above-bA counts
 
   const int row = blockIdx.y;
   const int ch = blockIdx.x;
@@ -302,7 +312,10 @@ __global__ __launch_bounds__(TK_NT) void topk_place_kernel(TopkBatch tb) {
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
     const int c = 4 * t + e;
-    if (c < ch) s_pre[c] = bpre;
+    if (c < ch) {
+      s_pre[c] = bpre;
+      s_ca[c] = ca[e];
+    }
     bpre += cb[e];
   }
   if (t == 0) s_pre[ch] = bin_before;
@@ -322,7 +335,7 @@ __global__ __launch_bounds__(TK_NT) void topk_place_kernel(TopkBatch tb) {
           const int mid = (lo + hi) >> 1;
           if (s_pre[mid] <= p) lo = mid; else hi = mid;
         }
-        kv[u] = w.bin_keys[(slot0 + lo) * TK_CHUNK + (p - s_pre[lo])];
+        kv[u] = w.bin_keys[(slot0 + lo) * TK_CHUNK + s_ca[lo] + (p - s_pre[lo])];
       }
     }
 #pragma unroll
@@ -369,6 +382,155 @@ __global__ __launch_bounds__(TK_NT) void topk_place_kernel(TopkBatch tb) {
     }
 }
 
+// ------------------------------------------------------------------ K3' (k <= TK_MERGE_K)
+// One work-group per row merges the chunks' candidate lists instead of re-reading the
+// scores: the above-bA entries (all selected, fewer than k) and the bA entries that
+// beat T or are T-valued within the quota, both already in index order chunk by
+// chunk; an entry's output slot is its rank in its own list plus the number of
+// entries of the other list with a lower index.
+constexpr int TK_MERGE_K = 4096;
+constexpr int TK_MNT = 1024;   // threads of the merge work-group
+constexpr int TK_MERGE_MIN_ROWS = 32;
+__device__ __forceinline__ int upper_le(const int32_t* a, int n, int32_t x) {   // #a[i] <= x
+  int lo = 0, hi = n;
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    if (a[mid] <= x) lo = mid + 1; else hi = mid;
+  }
+  return lo;
+}
+__device__ __forceinline__ int lower_lt(const int32_t* a, int n, int32_t x) {   // #a[i] < x
+  int lo = 0, hi = n;
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    if (a[mid] < x) lo = mid + 1; else hi = mid;
+  }
+  return lo;
+}
+
+__global__ __launch_bounds__(TK_MNT) void topk_merge_kernel(TopkBatch tb) {
+  const TopkLayer& TL = tb.layer[blockIdx.z];
+  const int k = TL.k;
+  const int max_n = TL.max_n;
+  const TopkWs& w = TL.w;
+  __shared__ int32_t s_scan[TK_MNT / WAVE + 1];
+  __shared__ int32_t s_b[2];
+  __shared__ int32_t s_apre[TK_MAX_CHUNKS + 1];   // above-bA entries before chunk c
+  __shared__ int32_t s_bpre[TK_MAX_CHUNKS + 1];   // bA entries before chunk c
+  __shared__ int32_t s_above[TK_MERGE_K];          // global indices, ascending
+  __shared__ int32_t s_sel[TK_MERGE_K];            // selected bA entries, ascending
+  const int row = blockIdx.y;
+  const int t = threadIdx.x;
+  const int64_t n = min(TL.n_vis[row], max_n);
+  int32_t* irow = TL.idx + (int64_t)row * k;
+  {   // nobody reads the coarse histogram any more: clear it for the next call
+    int32_t* hrow = w.hist + (int64_t)row * HIST_BINS;
+    for (int b = t; b < HIST_BINS; b += TK_MNT) hrow[b] = 0;
+  }
+  if (t == 0) TL.count[row] = (int32_t)min(n, (int64_t)k);
+  if (n <= k) {   // every visible entry is selected
+    for (int p = t; p < k; p += TK_MNT) irow[p] = p < n ? p : -1;
+    return;
+  }
+  const int nch = (int)((n + TK_CHUNK - 1) / TK_CHUNK);
+  const int64_t slot0 = (int64_t)row * w.nchunks;
+
+  // loads that do not depend on each other, issued together: thread t owns chunk t
+  // and fine bin 1023 - t
+  static_assert(TK_MNT == TK_MAX_CHUNKS && TK_MNT == FINE_BINS, "one chunk and one bin per thread");
+  const int2 rs = w.rowstate[row];
+  const int32_t fv = w.fine[(int64_t)row * FINE_BINS + 1023 - t];
+  const int32_t ca = t < nch ? w.cnt_above[slot0 + t] : 0;
+  const int32_t cb = t < nch ? w.cnt_bin[slot0 + t] : 0;
+  const int need = k - rs.y;   // keys to take from the threshold bin (>= 1)
+
+  // fine threshold: the bin where the descending count reaches `need`
+  if (t < 2) s_b[t] = 0;
+  int32_t ftot;
+  const int32_t fpre = block_excl_scan<TK_MNT>(fv, s_scan, &ftot);
+  if (fpre < need && fpre + fv >= need) {
+    s_b[0] = 1023 - t;
+    s_b[1] = fpre;
+  }
+  __syncthreads();
+  const int low_t = s_b[0];
+  const int need_eq = need - s_b[1];   // T-valued keys to keep, lowest indices first
+
+  // chunk offsets of both lists
+  int32_t a_tot, b_tot;
+  const int32_t apre = block_excl_scan<TK_MNT>(ca, s_scan, &a_tot);
+  const int32_t bpre = block_excl_scan<TK_MNT>(cb, s_scan, &b_tot);
+  if (t < nch) {
+    s_apre[t] = apre;
+    s_bpre[t] = bpre;
+  }
+  if (t == 0) {
+    s_apre[nch] = a_tot;
+    s_bpre[nch] = b_tot;
+  }
+  __syncthreads();
+  a_tot = min(a_tot, TK_MERGE_K);   // fewer than k for consistent counts; the bound guards bad input
+
+  // gather the above-bA entries (each chunk's list is in index order), all loads in flight
+  {
+    constexpr int GU = TK_MERGE_K / TK_MNT;
+    int32_t gc[GU], gv[GU];
+#pragma unroll
+    for (int u = 0; u < GU; ++u) {
+      const int p = t + TK_MNT * u;
+      gc[u] = 0;
+      gv[u] = 0;
+      if (p < a_tot) {
+        gc[u] = upper_le(s_apre, nch, p) - 1;   // s_apre[c] <= p < s_apre[c+1]
+        gv[u] = w.bin_keys[(slot0 + gc[u]) * TK_CHUNK + (p - s_apre[gc[u]])];
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < GU; ++u) {
+      const int p = t + TK_MNT * u;
+      if (p < a_tot) s_above[p] = gc[u] * TK_CHUNK + gv[u];
+    }
+  }
+  // threshold-bin entries in index order: those above T, and T-valued ones in order
+  // until the quota is met
+  int32_t eq_run = 0, sel_run = 0;
+  for (int base = 0; base < b_tot; base += TK_MNT) {
+    const int p = base + t;
+    int gi = 0;
+    bool gt = false, eq = false;
+    if (p < b_tot) {
+      const int c = upper_le(s_bpre, nch, p) - 1;
+      const int32_t a_c = s_apre[c + 1] - s_apre[c];
+      const int32_t kv = w.bin_keys[(slot0 + c) * TK_CHUNK + a_c + (p - s_bpre[c])];
+      const int low = kv & 1023;
+      gi = c * TK_CHUNK + (kv >> 10);
+      gt = low > low_t;
+      eq = low == low_t;
+    }
+    int32_t eq_n;
+    const int32_t eq_rank = eq_run + block_excl_scan<TK_MNT>(eq ? 1 : 0, s_scan, &eq_n);
+    const bool sel = gt || (eq && eq_rank < need_eq);
+    int32_t sel_n;
+    const int32_t q = sel_run + block_excl_scan<TK_MNT>(sel ? 1 : 0, s_scan, &sel_n);
+    if (sel && q < TK_MERGE_K) s_sel[q] = gi;
+    eq_run += eq_n;
+    sel_run += sel_n;
+  }
+  __syncthreads();
+  const int nsel = min(sel_run, TK_MERGE_K);
+  // merge: rank in own list + entries of the other list with a lower index
+  for (int p = t; p < a_tot; p += TK_MNT) {
+    const int32_t x = s_above[p];
+    const int pos = p + lower_lt(s_sel, nsel, x);
+    if (pos < k) irow[pos] = x;
+  }
+  for (int q = t; q < nsel; q += TK_MNT) {
+    const int32_t y = s_sel[q];
+    const int pos = q + lower_lt(s_above, a_tot, y);
+    if (pos < k) irow[pos] = y;
+  }
+}
+
 hipError_t launch_topk(const TopkBatch& tb, int rows, bool hist_ready, hipStream_t st) {
   if (rows == 0 || tb.n == 0) return hipSuccess;
   int nch = 1, pch = 1;
@@ -379,7 +541,14 @@ hipError_t launch_topk(const TopkBatch& tb, int rows, bool hist_ready, hipStream
   if (!hist_ready)
     hipLaunchKernelGGL(topk_hist_kernel, dim3(nch, rows, tb.n), dim3(TK_NT), 0, st, tb);
   hipLaunchKernelGGL(topk_cand_kernel, dim3(nch, rows, tb.n), dim3(TK_NT), 0, st, tb);
-  hipLaunchKernelGGL(topk_place_kernel, dim3(pch, rows, tb.n), dim3(TK_NT), 0, st, tb);
+  int max_k = 0;
+  for (int l = 0; l < tb.n; ++l) max_k = max(max_k, tb.layer[l].k);
+  // one work-group per row pays off once there are enough rows to fill the chip's
+  // latency; a few rows go faster with every chunk placing its own selections
+  if (max_k <= TK_MERGE_K && rows * tb.n >= TK_MERGE_MIN_ROWS)
+    hipLaunchKernelGGL(topk_merge_kernel, dim3(1, rows, tb.n), dim3(TK_MNT), 0, st, tb);
+  else
+    hipLaunchKernelGGL(topk_place_kernel, dim3(pch, rows, tb.n), dim3(TK_NT), 0, st, tb);
   return hipGetLastError();
 }
 

@@ -120,19 +120,22 @@ def _topk_cases():
         "extreme": (ext, 5000, 77),
         "k_one": (rand, 10001, 1),
         "one_candidate_bin": (np.concatenate([np.full(5000, 7), np.arange(10)]), 5010, 3),
+        # k above the per-row merge's limit: the chunk-parallel placement
+        "k_large": (big, 70001, 5000),
+        "k_large_ties": (g.integers(-3, 4, 20000), 20000, 6000),
     }
 
 
+@pytest.mark.parametrize("rows", [2, 40])   # 2: chunk-parallel placement, 40: per-row merge
 @pytest.mark.parametrize("name", list(_topk_cases()))
-def test_topk_bit_exact(name):
-    step(f"csa_topk_select {name}")
+def test_topk_bit_exact(name, rows):
+    step(f"csa_topk_select {name} rows={rows}")
     sc, n, k = _topk_cases()[name]
-    rows = 2   # the same scores twice, the second row seeing fewer entries
+    # the same scores in every row, alternate rows seeing 1000 fewer entries
     ld = (max(len(sc), 4) + 3) // 4 * 4
     S = np.full((rows, ld), I32MIN, dtype=np.int32)
-    S[0, :len(sc)] = sc
-    S[1, :len(sc)] = sc
-    nvs = [n, max(0, n - 1000)]
+    S[:, :len(sc)] = sc
+    nvs = [n if r % 2 == 0 else max(0, n - 1000) for r in range(rows)]
     scores = torch.from_numpy(S).to(DEV)
     n_vis = torch.tensor(nvs, dtype=torch.int32, device=DEV)
     idx = torch.full((rows, k), -5, dtype=torch.int32, device=DEV)
@@ -143,12 +146,44 @@ def test_topk_bit_exact(name):
         torch.cuda.synchronize()
         I = idx.cpu().numpy()
         C = count.cpu().numpy()
+        refs = {v: oracle.topk_select(sc, v, k) for v in set(nvs)}
         for r in range(rows):
-            ref = oracle.topk_select(sc, nvs[r], k)
+            ref = refs[nvs[r]]
             assert C[r] == len(ref), (rep, r)
             assert np.array_equal(I[r, :len(ref)], ref), (rep, r)
             assert np.all(I[r, len(ref):] == -1), (rep, r)
     assert int(ws[: rows * 2048 * 4].count_nonzero()) == 0   # coarse histogram left zeroed
+
+
+def test_topk_many_rows_multi_chunk():
+    # many rows of many chunks in one launch: ragged visibility, a tie-heavy row every
+    # 7th row, rows at and below k, an empty row; two calls on the same workspace
+    step("csa_topk_select 64 rows x 70001")
+    g = rng(221, 0, 0)
+    rows, m, k = 64, 70001, 2048
+    q = int8_uniform(g, (64,))
+    base = oracle.index_scores(q, int8_uniform(g, (m, 64)))
+    S = np.full((rows, (m + 3) // 4 * 4), I32MIN, dtype=np.int32)
+    nvs = []
+    for r in range(rows):
+        sc = g.integers(-5, 6, m) if r % 7 == 0 else np.roll(base, 977 * r)
+        S[r, :m] = sc
+        nvs.append([m, m - 12345 * (r % 5), k, k - 1, 0][r % 5] if r % 11 == 3 else m - 97 * r)
+    scores = torch.from_numpy(S).to(DEV)
+    n_vis = torch.tensor(nvs, dtype=torch.int32, device=DEV)
+    idx = torch.full((rows, k), -5, dtype=torch.int32, device=DEV)
+    count = torch.full((rows,), -5, dtype=torch.int32, device=DEV)
+    ws = lca.workspace(lca.csa_topk_workspace_bytes(rows, m, k))
+    for rep in range(2):
+        lca.csa_topk_select(scores, rows, m, n_vis, k, idx, count, ws)
+        torch.cuda.synchronize()
+        I, C = idx.cpu().numpy(), count.cpu().numpy()
+        for r in range(rows):
+            ref = oracle.topk_select(S[r, :m], nvs[r], k)
+            assert C[r] == len(ref), (rep, r)
+            assert np.array_equal(I[r, :len(ref)], ref), (rep, r)
+            assert np.all(I[r, len(ref):] == -1), (rep, r)
+    assert int(ws[: rows * 2048 * 4].count_nonzero()) == 0
 
 
 # ------------------------------------------------------------------ attention

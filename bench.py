@@ -343,7 +343,7 @@ class HcaDecodeRunner(_Capture):
 
     def dominant_units(self):
         return {"bound": "hbm", "per_launch": self.step_bytes(), "unit": "GB/s",
-                "kernel": "hca_dense_attn (attn_kernel + split combine)",
+                "kernel": "hca_dense_attn (attn_dma_kernel + split combine)",
                 "per_unit": "512 B per visible entry (K+V bf16) + 512 B per head (q in, o out)"}
 
     def cpu_baseline(self, n):
@@ -419,7 +419,7 @@ class PrefillRunner(_Capture):
         wl = self.wl
         flops = wl.new_tokens * wl.heads * wl.topk * 128 * 4.0
         return {"bound": "mfma", "per_launch": flops, "unit": "TFLOP/s",
-                "kernel": "csa_sparse_attn (attn_kernel, bf16 MFMA)",
+                "kernel": "csa_sparse_attn (attn_dma_kernel, bf16 MFMA)",
                 "per_unit": "4*128 flops per (query, head, selected entry)"}
 
     def cpu_baseline(self, n):

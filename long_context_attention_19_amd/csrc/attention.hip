@@ -177,11 +177,6 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
-// One stage of the online softmax attention for the 16 heads of this wave (head
-// l16 of the lane) over its SUB 32-entry sub-tiles starting at stage row el_base:
-// S^T = K Q^T from the stage's K tile, online softmax in log2 units, O^T += V^T P^T
-// with the V^T operand read transposed from the stage's V tile.  Entries at or past
-// e1 are masked (their rows were fetched but hold repeats).
 // max / sum over the 4 lanes that share l16 (lanes l16, l16+16, l16+32, l16+48):
 // v_permlane32_swap exchanges the two 32-lane halves, v_permlane16_swap the odd and
 // even 16-lane rows, both without LDS
@@ -199,82 +194,90 @@ __device__ __forceinline__ float lanes4_sum(float x) {
 }
 
 // One stage of the online softmax attention for the 16 heads of this wave (head
-// l16 of the lane) over its SUB 32-entry sub-tiles starting at stage row el_base:
-// S^T = K Q^T from the stage's K tile, online softmax in log2 units, O^T += V^T P^T
-// with the V^T operand read transposed from the stage's V tile.  Entries at or past
-// e1 are masked (their rows were fetched but hold repeats).  The running max is kept
-// in scaled log2 units; the exponent is one fma, v_exp_f32 without range fix-up (a
-// weight below 2^-126 flushes to 0, as it would in bf16).
+// l16 of the lane) over its SUB 32-entry sub-tiles starting at stage row el_base,
+// treated as one block of 32*SUB entries: S^T = K Q^T for every sub-tile first
+// (independent MFMA chains), one running-max update and one rescale for the block,
+// then O^T += V^T P^T with the V^T operand read transposed from the stage's V tile.
+// Entries at or past e1 are masked (their rows were fetched but hold repeats; their
+// weights are exactly 0).  The caller guarantees the block's first entry is valid.
+// The running max is kept in scaled log2 units; the exponent is one fma, v_exp_f32
+// without range fix-up (a weight below 2^-126 flushes to 0, as it would in bf16).
 template <int SUB>
 __device__ __forceinline__ void attn_stage(const i32x4* kb, const char* vbase, int el_base, int tb,
                                            int e1, const bf16x8 (&qf)[4], f32x4 (&o)[8],
                                            float& m_run, float& l_run, float scale_log2, int l16,
                                            int g) {
+  f32x4 sacc[SUB][2];
 #pragma unroll
-  for (int sub = 0; sub < SUB; ++sub) {
-    const int el0 = el_base + sub * 32;   // this wave's 32 entries of the stage
-    const int ev0 = tb + el0;
-    if (ev0 < e1) {
-      f32x4 sacc[2];
+  for (int sub = 0; sub < SUB; ++sub)
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) sacc[sub][rb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+    for (int sub = 0; sub < SUB; ++sub)
 #pragma unroll
       for (int rb = 0; rb < 2; ++rb) {
-        sacc[rb] = f32x4{0.f, 0.f, 0.f, 0.f};
-        const int r = el0 + rb * 16 + l16;
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-          const bf16x8 kf = __builtin_bit_cast(bf16x8, kb[r * 16 + ((4 * ks + g) ^ (r & 15))]);
-          sacc[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[ks], sacc[rb], 0, 0, 0);
-        }
+        const int r = el_base + sub * 32 + rb * 16 + l16;
+        const bf16x8 kf = __builtin_bit_cast(bf16x8, kb[r * 16 + ((4 * ks + g) ^ (r & 15))]);
+        sacc[sub][rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[ks], sacc[sub][rb], 0, 0, 0);
       }
-      float x[8];
+  float x[SUB * 8];
+#pragma unroll
+  for (int sub = 0; sub < SUB; ++sub)
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) x[sub * 8 + rb * 4 + i] = sacc[sub][rb][i];
+  const int ev0 = tb + el_base;
+  if (ev0 + 32 * SUB > e1) {   // the block crosses the end: mask entries >= e1
+#pragma unroll
+    for (int sub = 0; sub < SUB; ++sub)
 #pragma unroll
       for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) x[rb * 4 + i] = sacc[rb][i];
-      if (ev0 + 32 > e1) {   // the last sub-tile of the piece: mask entries >= e1
-#pragma unroll
-        for (int rb = 0; rb < 2; ++rb)
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-            if (ev0 + rb * 16 + 4 * g + i >= e1) x[rb * 4 + i] = -INFINITY;
-      }
-      float mx = x[0];
-#pragma unroll
-      for (int i = 1; i < 8; ++i) mx = fmaxf(mx, x[i]);
-      mx = lanes4_max(mx) * scale_log2;            // scale > 0: max commutes with it
-      const float m_new = fmaxf(m_run, mx);         // finite: the wave has a valid entry
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);   // 0 first, 1 if unchanged
-      bf16x8 pf;
-      float psum = 0.f;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const __bf16 pb = (__bf16)__builtin_amdgcn_exp2f(fmaf(x[i], scale_log2, -m_new));
-        pf[i] = pb;
-        psum += (float)pb;
-      }
-      l_run = l_run * alpha + psum;
-      if (__any(m_new > m_run)) {                 // otherwise every factor is exactly 1
-#pragma unroll
-        for (int db = 0; db < 8; ++db) o[db] *= alpha;
-      }
-      m_run = m_new;
-#pragma unroll
-      for (int db = 0; db < 8; ++db) {
-        bf16x4 half[2];
-#pragma unroll
-        for (int hh = 0; hh < 2; ++hh) {
-          const int r = el0 + 16 * hh + 4 * g + (l16 >> 2);
-          const int q = l16 & 3;
-          const int off = r * 256 + (((2 * db + (q >> 1)) ^ ((r & 7) << 1)) << 4) + (q & 1) * 8;
-          half[hh] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-              (__attribute__((address_space(3))) bf16x4*)(vbase + off));
-        }
-        const bf16x8 vf = {half[0][0], half[0][1], half[0][2], half[0][3],
-                           half[1][0], half[1][1], half[1][2], half[1][3]};
-        o[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf, o[db], 0, 0, 0);
-      }
-    }
+        for (int i = 0; i < 4; ++i)
+          if (ev0 + sub * 32 + rb * 16 + 4 * g + i >= e1) x[sub * 8 + rb * 4 + i] = -INFINITY;
   }
+  float mx = x[0];
+#pragma unroll
+  for (int i = 1; i < SUB * 8; ++i) mx = fmaxf(mx, x[i]);
+  mx = lanes4_max(mx) * scale_log2;            // scale > 0: max commutes with it
+  const float m_new = fmaxf(m_run, mx);         // finite: the block has a valid entry
+  const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);   // 0 first, 1 if unchanged
+  bf16x8 pf[SUB];
+  float psum = 0.f;
+#pragma unroll
+  for (int sub = 0; sub < SUB; ++sub)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const __bf16 pb = (__bf16)__builtin_amdgcn_exp2f(fmaf(x[sub * 8 + i], scale_log2, -m_new));
+      pf[sub][i] = pb;
+      psum += (float)pb;
+    }
+  l_run = l_run * alpha + psum;
+  if (__any(m_new > m_run)) {                 // otherwise every factor is exactly 1
+#pragma unroll
+    for (int db = 0; db < 8; ++db) o[db] *= alpha;
+  }
+  m_run = m_new;
+#pragma unroll
+  for (int sub = 0; sub < SUB; ++sub)
+#pragma unroll
+    for (int db = 0; db < 8; ++db) {
+      bf16x4 half[2];
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        const int r = el_base + sub * 32 + 16 * hh + 4 * g + (l16 >> 2);
+        const int q = l16 & 3;
+        const int off = r * 256 + (((2 * db + (q >> 1)) ^ ((r & 7) << 1)) << 4) + (q & 1) * 8;
+        half[hh] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+            (__attribute__((address_space(3))) bf16x4*)(vbase + off));
+      }
+      const bf16x8 vf = {half[0][0], half[0][1], half[0][2], half[0][3],
+                         half[1][0], half[1][1], half[1][2], half[1][3]};
+      o[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf[sub], o[db], 0, 0, 0);
+    }
 }
 
 // The K and V row pieces of one DMA instruction: lane (r, slot l16) of instruction
@@ -426,8 +429,9 @@ __global__ __launch_bounds__(AT_NT) void attn_dma_kernel(AttnBatch ab) {
   const int e1 = min(e0 + per, n);
 
   auto compute = [&](int buf, int tb) __attribute__((always_inline)) {
-    attn_stage<SUB>(sm.k[buf], reinterpret_cast<const char*>(sm.v[buf]), es * SUB * 32, tb, e1, qf,
-                    o, m_run, l_run, scale_log2, l16, g);
+    if (tb + es * SUB * 32 < e1)   // this wave's block has a valid entry
+      attn_stage<SUB>(sm.k[buf], reinterpret_cast<const char*>(sm.v[buf]), es * SUB * 32, tb, e1,
+                      qf, o, m_run, l_run, scale_log2, l16, g);
   };
 
   // Per stage: wait for this stage's DMA (the later stages' may stay outstanding),
@@ -837,8 +841,9 @@ __global__ __launch_bounds__(AT_NT) void attn_persist_kernel(AttnBatch ab, AttnP
         cur = item;
         ++nseg;
       }
-      attn_stage<SUB>(s_k[buf], reinterpret_cast<const char*>(s_v[buf]), 0, (js - cmp_pre) * ST,
-                      cmp_n, qf, o, m_run, l_run, scale_log2, l16, g);
+      if ((js - cmp_pre) * ST < cmp_n)   // an empty item's stage has nothing to attend
+        attn_stage<SUB>(s_k[buf], reinterpret_cast<const char*>(s_v[buf]), 0, (js - cmp_pre) * ST,
+                        cmp_n, qf, o, m_run, l_run, scale_log2, l16, g);
       lds_barrier();
       dma1 = false;
       if (j + 2 < nst) dma1 = issue(js + 2, buf, c0);

@@ -34,6 +34,7 @@ constexpr int IS_CHUNK = IS_KEYS_PER_PASS * IS_PASSES;     // 2048 entries per w
 template <bool HIST>
 __global__ __launch_bounds__(IS_NT) void index_score_kernel(IndexBatch ib) {
   __shared__ int32_t lh[HIST ? HIST_BINS : 1];
+  __shared__ __attribute__((aligned(16))) int32_t s_sc[IS_CHUNK];   // the group's scores
   const IndexLayer& L = ib.layer[blockIdx.z];
   const int8_t* __restrict__ q_idx = L.q_idx;
   const int8_t* __restrict__ k_idx = L.k_idx;
@@ -93,11 +94,26 @@ __global__ __launch_bounds__(IS_NT) void index_score_kernel(IndexBatch ib) {
       const int q0 = (b0 ? p1 : p0) + __shfl_xor(b0 ? p0 : p1, 1, WAVE);
       const int q1 = (b0 ? p3 : p2) + __shfl_xor(b0 ? p2 : p3, 1, WAVE);
       const int32_t v = (b1 ? q1 : q0) + __shfl_xor(b1 ? q0 : q1, 2, WAVE);
-      const int64_t j = pb + (4 * w + piece) * (IS_NT / 4) + (t >> 2);
-      if (j < N) {
-        const bool vis = j < nv;
-        srow[j] = vis ? v : INT32_MIN;
-        if (HIST && vis) atomicAdd(&lh[(v + KEY_BIAS) >> 10], 1);
+      const int jl = pass * IS_KEYS_PER_PASS + (4 * w + piece) * (IS_NT / 4) + (t >> 2);
+      const int64_t j = base + jl;
+      const bool vis = j < nv;
+      s_sc[jl] = vis ? v : INT32_MIN;
+      if (HIST && vis && j < N) atomicAdd(&lh[(v + KEY_BIAS) >> 10], 1);
+    }
+  }
+  // the group's scores leave at the end, 16 bytes per thread per store, 8 KiB
+  // contiguous; nothing past the sequence's last entry is written
+  __syncthreads();
+  {
+    const int64_t cnt = min((int64_t)IS_CHUNK, N - base);
+#pragma unroll
+    for (int u = 0; u < IS_CHUNK / (4 * IS_NT); ++u) {
+      const int q = 4 * (t + IS_NT * u);
+      if (q + 4 <= cnt) {
+        *reinterpret_cast<i32x4*>(srow + base + q) = *reinterpret_cast<const i32x4*>(&s_sc[q]);
+      } else {
+        for (int e = 0; e < 4; ++e)
+          if (q + e < cnt) srow[base + q + e] = s_sc[q + e];
       }
     }
   }

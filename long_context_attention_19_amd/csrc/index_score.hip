@@ -22,6 +22,7 @@
 // each row also zeroes the row's second-level histogram.
 #include "lca_device.h"
 #include "lca_internal.h"
+#include "lca.h"
 
 namespace lca {
 
@@ -127,14 +128,229 @@ __global__ __launch_bounds__(IS_NT) void index_score_kernel(IndexBatch ib) {
   }
 }
 
+// ---------------------------------------------------------------- many query rows
+// With 16 or more query tokens per sequence (prefill) the scores are the int8 GEMM
+// Q_idx [rows x 64] . K_idx^T [64 x N].  One v_mfma_i32_16x16x64_i8 yields the 16 x 16
+// scores of 16 entries (operand A) against 16 query tokens (operand B) over the whole
+// d_idx = 64, exactly, in int32.  In both operands lane l supplies row l % 16 of its
+// matrix and bytes 16 (l / 16) .. 16 (l / 16) + 15 of that row, so the two operands
+// agree on which byte pairs are multiplied; in the result lane l holds entries
+// 4 (l / 16) + r, r < 4, of query token l % 16 — the same token whose query it loaded.
+//
+// A work-group owns 16 query tokens and a range of the entries (all of them when
+// the grid has enough row tiles to fill the GPU).  It reads 64 B of keys per entry,
+// shared by every row tile and so mostly from L2, and writes 64 B of scores per
+// entry: it is bound by the HBM writes.  Those only run at full rate as long runs of
+// whole lines, so each round of 8 blocks (512 entries) is staged in LDS and leaves
+// as 2 KiB per token, 1 KiB per store instruction.  LDS holds, in 160 KiB:
+//   - the 16 tokens' histograms, 2048 bins each, bin b of token j at b ^ j so that
+//     tokens hitting the same bin use different banks;
+//   - the staging tile, 16 x 512 scores, 16-byte chunk c of token j at c ^ j.
+constexpr int IG_NT = 512;                   // 8 waves
+constexpr int IG_NW = IG_NT / WAVE;
+constexpr int IG_ROWS = 16;                  // query tokens per work-group (MFMA N)
+constexpr int IG_BLOCK = 64;                 // entries per wave and round: 4 MFMA tiles
+constexpr int IG_ROUND = IG_BLOCK * IG_NW;   // 512 entries per round
+constexpr int IG_CHUNKS = IG_ROUND / 4;      // 16-byte chunks per staged token row
+
+// word 3 of a raw buffer resource on gfx950: 32-bit data format, no swizzle
+constexpr int IG_RSRC_WORD3 = 0x00020000;
+constexpr int IG_STORE_NT = 2;   // cache-policy operand of a buffer store: non-temporal
+
+__device__ __forceinline__ void ig_lds_barrier() {   // LDS traffic only: no memory fence
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// Keys of one 64-entry block: tile u, lane l -> entry blk*64 + 16u + l%16, bytes
+// 16 (l/16) ..; entries past N re-read entry N-1 (their scores are dropped).  The
+// keys are read by every row tile, so these loads are ordinary (kept in L2) and
+// the score stores are the non-temporal ones.
+__device__ __forceinline__ void ig_load(i32x4 (&kv)[4], const i32x4* __restrict__ kp, int32_t blk,
+                                        int32_t N, int lane) {
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int32_t j = min(blk * IG_BLOCK + 16 * u + (lane & 15), N - 1);
+    kv[u] = kp[j * 4 + (lane >> 4)];
+  }
+}
+
+// One round: this wave scores its block into the staging tile and the histograms,
+// then the work-group writes the round's whole 16-byte chunks out, token row by
+// token row.  Nothing here branches around a global memory access: on this
+// architecture loads and stores share one in-order completion counter, and a store
+// under a branch would make the compiler's wait for a later-issued load also wait
+// for this round's stores.  So the stores are buffer stores whose range check drops
+// what lies past the work-group's last whole chunk (or a whole row past the last
+// token, or a round wholly past the range: `live` false); the partial last chunk of
+// each row is written after the loop, from the last live round still in LDS.
+template <bool HIST>
+__device__ __forceinline__ void ig_round(const i32x4 (&kv)[4], const i32x4& qv, int32_t blk,
+                                         int32_t rbase, int32_t cap4, int32_t nv, bool live,
+                                         int64_t nr, int t, int w, int n, int grp,
+                                         int32_t* __restrict__ srow0, int64_t ld,
+                                         int32_t* lh, int32_t* st) {
+  const i32x4 zero4 = {0, 0, 0, 0};
+  i32x4 o[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const i32x4 acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(kv[u], qv, zero4, 0, 0, 0);
+    const int32_t j0 = blk * IG_BLOCK + 16 * u + 4 * grp;   // first of this lane's 4 entries
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const bool vis = j0 + r < nv;
+      o[u][r] = vis ? acc[r] : INT32_MIN;
+      if (HIST && vis) atomicAdd(&lh[n * HIST_BINS + (((acc[r] + KEY_BIAS) >> 10) ^ n)], 1);
+    }
+  }
+  if (live) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int c = (w * IG_BLOCK + 16 * u + 4 * grp) >> 2;   // chunk within the round
+      *reinterpret_cast<i32x4*>(st + n * IG_ROUND + 4 * (c ^ n)) = o[u];
+    }
+  }
+  ig_lds_barrier();
+  // wave w writes chunks 64 (w % 2) + lane of token rows w / 2 + 4 v, 1 KiB per store
+  constexpr int NV = IG_ROWS * IG_CHUNKS / IG_NT;
+  const int lane = t & (WAVE - 1);
+  const int c = WAVE * (w & 1) + lane;
+  i32x4 ov[NV];
+#pragma unroll
+  for (int v = 0; v < NV; ++v) {
+    const int row = (w >> 1) + 4 * v;
+    ov[v] = *reinterpret_cast<const i32x4*>(st + row * IG_ROUND + 4 * (c ^ row));
+  }
+#pragma unroll
+  for (int v = 0; v < NV; ++v) {
+    const int row = (w >> 1) + 4 * v;   // uniform
+    const int32_t nrec = (live && row < nr) ? cap4 * 4 : 0;
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc(srow0 + row * ld, 0, nrec, IG_RSRC_WORD3);
+    __builtin_amdgcn_raw_buffer_store_b128(ov[v], rs, (rbase + 4 * c) * 4, 0, IG_STORE_NT);
+  }
+  ig_lds_barrier();
+}
+
+template <bool HIST>
+__global__ __launch_bounds__(IG_NT) void index_gemm_kernel(IndexBatch ib, int tiles_per_seq,
+                                                           int ranges) {
+  __shared__ __attribute__((aligned(16))) int32_t lh[HIST ? IG_ROWS * HIST_BINS : 1];
+  __shared__ __attribute__((aligned(16))) int32_t st[IG_ROWS * IG_ROUND];
+  const IndexLayer& L = ib.layer[blockIdx.z];
+  const int b = blockIdx.y / tiles_per_seq;
+  const int q0 = (blockIdx.y - b * tiles_per_seq) * IG_ROWS;
+  const int64_t r0 = ib.q_off[b];
+  const int64_t nrows = ib.q_off[b + 1] - r0;
+  if (q0 >= nrows) return;
+  const int64_t nr = min((int64_t)IG_ROWS, nrows - q0);
+  const int64_t e0 = L.ent_off[b];
+  const int32_t N = (int32_t)min(L.ent_off[b + 1] - e0, (int64_t)L.max_entries);
+  const int t = threadIdx.x;
+  const int lane = t & (WAVE - 1);
+  const int w = __builtin_amdgcn_readfirstlane(t / WAVE);
+  const int n = lane & 15;                 // query token of this lane (tile column)
+  const int grp = lane >> 4;               // lane group: entries 4 grp .. 4 grp + 3 of a tile
+  const bool qok = n < nr;
+  const int64_t row = r0 + q0 + (qok ? n : 0);
+  const int32_t nv = qok ? (int32_t)min(ib.q_pos[row] / L.c, (int64_t)N) : 0;
+  const int er = blockIdx.x;
+  if (er == 0) {
+    if (t < nr) {
+      const int64_t rr = r0 + q0 + t;
+      L.n_vis[rr] = (int32_t)min(ib.q_pos[rr] / L.c, (int64_t)N);
+    }
+    if (HIST)
+      for (int i = t; i < nr * FINE_BINS; i += IG_NT) L.fine[(r0 + q0) * FINE_BINS + i] = 0;
+  }
+  if (N <= 0) return;
+  const int32_t nblk = (N + IG_BLOCK - 1) / IG_BLOCK;
+  const int32_t blk0 = (int32_t)((int64_t)nblk * er / ranges);
+  const int32_t blk1 = (int32_t)((int64_t)nblk * (er + 1) / ranges);
+  if (blk0 >= blk1) return;
+  const int32_t cap = min(N, blk1 * IG_BLOCK);   // this work-group writes entries < cap
+  const int32_t cap4 = cap & ~3;                 // ... the whole chunks of them in the loop
+  const int32_t nround = (blk1 - blk0 + IG_NW - 1) / IG_NW;
+
+  const i32x4* kp = reinterpret_cast<const i32x4*>(L.k_idx + e0 * 64);
+  const i32x4 zero4 = {0, 0, 0, 0};
+  const i32x4 qv = qok ? *reinterpret_cast<const i32x4*>(L.q_idx + row * 64 + 16 * grp) : zero4;
+  int32_t* srow0 = L.scores + (r0 + q0) * L.ld;
+  // Three key buffers: each round's block is loaded two rounds ahead, before the
+  // stores of the round in between.
+  i32x4 ka[4], kb[4], kc[4];
+  ig_load(ka, kp, blk0 + w, N, lane);
+  ig_load(kb, kp, blk0 + IG_NW + w, N, lane);
+  if (HIST) {
+    for (int i = t; i < IG_ROWS * HIST_BINS; i += IG_NT) lh[i] = 0;
+    __syncthreads();
+  }
+  auto round = [&](const i32x4 (&kv)[4], int32_t rd) __attribute__((always_inline)) {
+    const int32_t bb = blk0 + rd * IG_NW;
+    ig_round<HIST>(kv, qv, bb + w, bb * IG_BLOCK, cap4, blk1 > bb + w ? nv : 0, rd < nround,
+                   nr, t, w, n, grp, srow0, L.ld, lh, st);
+  };
+  for (int32_t rd = 0; rd < nround; rd += 3) {
+    ig_load(kc, kp, blk0 + (rd + 2) * IG_NW + w, N, lane);
+    round(ka, rd);
+    ig_load(ka, kp, blk0 + (rd + 3) * IG_NW + w, N, lane);
+    round(kb, rd + 1);
+    ig_load(kb, kp, blk0 + (rd + 4) * IG_NW + w, N, lane);
+    round(kc, rd + 2);
+  }
+  // the partial last chunk of each row (cap not a multiple of 4), from the staging
+  // tile, which still holds the last live round
+  if (cap4 < cap && t < 4 * nr) {
+    const int j = t >> 2, e = t & 3;
+    if (cap4 + e < cap) {
+      const int32_t rl = (blk0 + (nround - 1) * IG_NW) * IG_BLOCK;   // the last round's base
+      const int cc = (cap4 - rl) >> 2;
+      srow0[j * L.ld + cap4 + e] = st[j * IG_ROUND + 4 * (cc ^ j) + e];
+    }
+  }
+  if (HIST) {
+    __syncthreads();
+    int32_t* gh = L.hist + (r0 + q0) * HIST_BINS;
+    if (ranges == 1) {   // the work-group saw every entry of its rows: plain stores
+      for (int i = t; i < nr * HIST_BINS; i += IG_NT) {
+        const int j = i / HIST_BINS, bin = i % HIST_BINS;
+        gh[i] = lh[j * HIST_BINS + (bin ^ j)];
+      }
+    } else {
+      for (int i = t; i < nr * HIST_BINS; i += IG_NT) {
+        const int j = i / HIST_BINS, bin = i % HIST_BINS;
+        const int32_t v = lh[j * HIST_BINS + (bin ^ j)];
+        if (v) atomicAdd(gh + i, v);
+      }
+    }
+  }
+}
+
 hipError_t launch_index_score(const IndexBatch& ib, int batch, hipStream_t st) {
   if (batch == 0 || ib.max_q == 0 || ib.n == 0) return hipSuccess;
-  int chunks = 1;
+  int max_n = 1;
   bool hist = false;
   for (int l = 0; l < ib.n; ++l) {
-    chunks = max(chunks, (ib.layer[l].max_entries + IS_CHUNK - 1) / IS_CHUNK);
+    max_n = max(max_n, ib.layer[l].max_entries);
     hist = hist || ib.layer[l].hist != nullptr;
   }
+  if (ib.max_q >= IG_ROWS) {
+    // enough query tokens per sequence for 16-wide MFMA tiles; split the entries
+    // only as far as needed to give every CU a work-group
+    const int tiles = (ib.max_q + IG_ROWS - 1) / IG_ROWS;
+    const int64_t row_tiles = (int64_t)batch * tiles * ib.n;
+    const int64_t nblk = (max_n + IG_BLOCK - 1) / IG_BLOCK;
+    const int ranges = (int)std::max<int64_t>(1, std::min<int64_t>(
+        nblk / (4 * IG_NW), (lca_device_cu_count() + row_tiles - 1) / row_tiles));
+    dim3 grid((unsigned)ranges, (unsigned)(batch * tiles), (unsigned)ib.n);
+    if (hist)
+      hipLaunchKernelGGL(index_gemm_kernel<true>, grid, dim3(IG_NT), 0, st, ib, tiles, ranges);
+    else
+      hipLaunchKernelGGL(index_gemm_kernel<false>, grid, dim3(IG_NT), 0, st, ib, tiles, ranges);
+    return hipGetLastError();
+  }
+  int chunks = 1;
+  for (int l = 0; l < ib.n; ++l)
+    chunks = max(chunks, (ib.layer[l].max_entries + IS_CHUNK - 1) / IS_CHUNK);
   dim3 grid((unsigned)chunks, (unsigned)(batch * ib.max_q), (unsigned)ib.n);
   if (hist)
     hipLaunchKernelGGL(index_score_kernel<true>, grid, dim3(IS_NT), 0, st, ib);

@@ -100,6 +100,69 @@ def test_index_score_bit_exact(fused):
                 assert np.array_equal(H[r], hist)
 
 
+def _check_index(S, NV, H, q_idx, k_idx, q_pos, Ns, nq, ent_off, q_off, c):
+    for b in range(len(Ns)):
+        keys = k_idx[ent_off[b]:ent_off[b + 1]]
+        rows = slice(int(q_off[b]), int(q_off[b + 1]))
+        if nq[b] == 0:
+            continue
+        # all of the sequence's query tokens at once: the plain definition per row
+        ref_all = q_idx[rows].astype(np.int64) @ keys.astype(np.int64).T if Ns[b] else \
+            np.zeros((nq[b], 0), np.int64)
+        for i in range(nq[b]):
+            r = int(q_off[b]) + i
+            nv = oracle.n_visible(q_pos[r], c, Ns[b])
+            ref = ref_all[i]
+            if i % 7 == 0:   # the oracle routine itself on a sample of rows
+                assert np.array_equal(oracle.index_scores(q_idx[r], keys), ref)
+            assert NV[r] == nv, (b, i)
+            assert np.array_equal(S[r, :nv], ref[:nv]), (b, i)
+            assert np.all(S[r, nv:Ns[b]] == I32MIN), (b, i)
+            assert np.all(S[r, Ns[b]:] == 12345), (b, i)
+            if H is not None:
+                hist = np.bincount((ref[:nv] + (1 << 20)) >> 10, minlength=2048)
+                assert np.array_equal(H[r], hist), (b, i)
+
+
+@pytest.mark.parametrize("fused", [False, True])
+@pytest.mark.parametrize("case", ["ragged", "many_rows"])
+def test_index_score_gemm_bit_exact(fused, case):
+    """16 or more query tokens per sequence: the int8 MFMA path.  "ragged" splits the
+    entries over several work-groups (histograms merged by atomics) and has row
+    tiles that are partly empty; "many_rows" has one work-group per row tile over
+    all entries (histograms stored whole)."""
+    step(f"csa_index_score gemm case={case} fused={fused}")
+    g = rng(211, int(fused), 0 if case == "ragged" else 1)
+    c = 4
+    if case == "ragged":
+        Ns, nq = [3000, 10001, 0, 700, 64], [16, 37, 5, 50, 17]
+    else:
+        Ns, nq = [701], [4096]
+    B, max_q = len(Ns), max(nq)
+    ent_off, q_off = offsets(Ns), offsets(nq)
+    rows = int(q_off[-1])
+    k_idx = int8_uniform(g, (max(1, int(ent_off[-1])), 64))
+    q_idx = int8_uniform(g, (rows, 64))
+    q_pos = []
+    for b in range(B):
+        for i in range(nq[b]):
+            # causal positions: the last token sees every block, earlier ones fewer;
+            # a few see none
+            q_pos.append(0 if i % 13 == 5 else ((i + 1) * (Ns[b] * c + 2)) // nq[b])
+    ld = max(Ns) + 4 - max(Ns) % 4
+    scores = torch.full((rows, ld), 12345, dtype=torch.int32, device=DEV)
+    n_vis = torch.full((rows,), -7, dtype=torch.int32, device=DEV)
+    ws = lca.workspace(lca.csa_topk_workspace_bytes(B * max_q, max(Ns), 64)) if fused else None
+    # rows are packed: row r of the output belongs to query token r (q_off)
+    lca.csa_index_score(i8_dev(q_idx), i64_dev(q_off), i64_dev(q_pos), i8_dev(k_idx),
+                        i64_dev(ent_off), B, max_q, max(Ns), c, scores, n_vis, ws=ws)
+    torch.cuda.synchronize()
+    H = ws[: B * max_q * 2048 * 4].view(torch.int32).view(B * max_q, 2048).cpu().numpy() \
+        if fused else None
+    _check_index(scores.cpu().numpy(), n_vis.cpu().numpy(), H, q_idx, k_idx, q_pos, Ns, nq,
+                 ent_off, q_off, c)
+
+
 # ------------------------------------------------------------------ top-k
 def _topk_cases():
     g = rng(220, 0, 0)

@@ -125,6 +125,30 @@ int32_t lca_csa_index_score(const int8_t* q_idx, const int64_t* q_off, const int
                             size_t ws_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * csa_index_select — csa_index_score and csa_topk_select in one call, without
+ * the scores: idx, count and n_vis are exactly what those two calls give.  Page
+ * section 3-2 items 2 and 4 (indexer scores, then a sparse top-k).
+ *
+ * For query batches of max_q >= 16 tokens per sequence (prefill): a work-group
+ * owns 16 query tokens of a sequence and all its entries and recomputes the
+ * int8 scores (MFMA) in three sweeps over the keys: coarse histogram, fine
+ * histogram of the threshold bin, selection in index order.  No score matrix is
+ * written and no workspace is needed.
+ *   q_idx, q_off, q_pos, k_idx, ent_off, batch, max_q, max_entries, d_idx, c
+ *            as for lca_csa_index_score.
+ *   k        entries kept per query row (>= 1).
+ *   idx      [rows, k] int32 out: selected entry indices in ascending order,
+ *            then -1 padding.    count [rows] int32 out: min(k, n_vis[r]).
+ *   n_vis    [rows] int32 out, or NULL: min(floor(q_pos[r] / c), N_b).
+ *   LCA_ERR_UNSUPPORTED for max_q < 16 (use the two calls there).
+ * ------------------------------------------------------------------------- */
+int32_t lca_csa_index_select(const int8_t* q_idx, const int64_t* q_off, const int64_t* q_pos,
+                             const int8_t* k_idx, const int64_t* ent_off, int32_t batch,
+                             int32_t max_q, int32_t max_entries, int32_t d_idx, int32_t c,
+                             int32_t k, int32_t* idx, int32_t* count, int32_t* n_vis,
+                             void* stream);
+
+/* ---------------------------------------------------------------------------
  * csa_topk_select — per row, the top min(k, n_vis[r]) entries of
  * scores[r, 0 .. n_vis[r]) ranked by (score desc, index asc).
  * Page section 3-2 item 2 (component table): CSA keeps a sparse top-k of the

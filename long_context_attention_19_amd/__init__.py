@@ -45,6 +45,8 @@ _SIGS = {
     "lca_kv_compress": (_i32, [_vp, _vp, _i32, _i32, _i32, _i32, _vp, _vp, _vp]),
     "lca_csa_index_score": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _vp,
                                    _i64, _vp, _vp, _sz, _vp]),
+    "lca_csa_index_select": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32,
+                                    _vp, _vp, _vp, _vp]),
     "lca_csa_topk_workspace_bytes": (_sz, [_i32, _i32, _i32]),
     "lca_csa_topk_select": (_i32, [_vp, _i64, _i32, _i32, _vp, _i32, _vp, _vp, _vp, _sz, _u32,
                                    _vp]),
@@ -133,6 +135,13 @@ def csa_index_score(q_idx, q_off, q_pos, k_idx, ent_off, batch, max_q, max_entri
         _p(q_idx), _p(q_off), _p(q_pos), _p(k_idx), _p(ent_off), batch, max_q, max_entries,
         q_idx.shape[-1], c, _p(scores), scores.stride(0), _p(n_vis), _p(ws), _nb(ws),
         _s(stream)))
+
+
+def csa_index_select(q_idx, q_off, q_pos, k_idx, ent_off, batch, max_q, max_entries, c, k, idx,
+                     count, n_vis=None, stream=None):
+    _check("lca_csa_index_select", _lib.lca_csa_index_select(
+        _p(q_idx), _p(q_off), _p(q_pos), _p(k_idx), _p(ent_off), batch, max_q, max_entries,
+        q_idx.shape[-1], c, k, _p(idx), _p(count), _p(n_vis), _s(stream)))
 
 
 def csa_topk_select(scores, rows, max_n, n_vis, k, idx, count, ws, hist_ready=False,

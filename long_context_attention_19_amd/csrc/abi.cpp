@@ -206,6 +206,26 @@ int32_t lca_csa_index_score(const int8_t* q_idx, const int64_t* q_off, const int
   return hip_status(lca::launch_index_score(ib, batch, (hipStream_t)stream), "csa_index_score launch");
 }
 
+// ------------------------------------------------------------------ fused scores + top-k
+int32_t lca_csa_index_select(const int8_t* q_idx, const int64_t* q_off, const int64_t* q_pos,
+                             const int8_t* k_idx, const int64_t* ent_off, int32_t batch,
+                             int32_t max_q, int32_t max_entries, int32_t d_idx, int32_t c,
+                             int32_t k, int32_t* idx, int32_t* count, int32_t* n_vis,
+                             void* stream) {
+  if (d_idx != 64) return fail(LCA_ERR_UNSUPPORTED, "csa_index_select: d_idx=%d (only 64)", d_idx);
+  if (batch < 0 || max_q < 0 || max_entries < 0) return fail(LCA_ERR_SHAPE, "csa_index_select: negative size");
+  if (c < 1) return fail(LCA_ERR_SHAPE, "csa_index_select: ratio c=%d < 1", c);
+  if (k <= 0) return fail(LCA_ERR_SHAPE, "csa_index_select: k=%d must be positive", k);
+  if (batch == 0 || max_q == 0) return ok();
+  if (max_q < lca::SELECT_MIN_Q) return fail(LCA_ERR_UNSUPPORTED, "csa_index_select: max_q=%d below %d (use csa_index_score + csa_topk_select)", max_q, lca::SELECT_MIN_Q);
+  if ((int64_t)batch * max_q > (1 << 30)) return fail(LCA_ERR_SHAPE, "csa_index_select: too many rows");
+  if ((int64_t)batch * max_q * k > ((int64_t)1 << 40)) return fail(LCA_ERR_SHAPE, "csa_index_select: output too large");
+  if (!q_idx || !q_off || !q_pos || !k_idx || !ent_off || !idx || !count) return fail(LCA_ERR_NULL, "csa_index_select: NULL pointer");
+  if (!al16(q_idx) || !al16(k_idx)) return fail(LCA_ERR_ALIGN, "csa_index_select: q_idx / k_idx not 16-byte aligned");
+  lca::SelectArgs a{q_idx, k_idx, ent_off, q_off, q_pos, idx, count, n_vis, c, max_entries, max_q, k};
+  return hip_status(lca::launch_index_select(a, batch, (hipStream_t)stream), "csa_index_select launch");
+}
+
 // ------------------------------------------------------------------ top-k
 size_t lca_csa_topk_workspace_bytes(int32_t rows, int32_t max_n, int32_t k) {
   if (rows <= 0 || max_n < 0 || k <= 0) return 0;

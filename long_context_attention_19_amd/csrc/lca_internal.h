@@ -38,6 +38,25 @@ struct IndexBatch {
 };
 hipError_t launch_index_score(const IndexBatch& ib, int batch, hipStream_t st);
 
+// Scores and top-k in one pass over the keys, without the scores (16+ query rows
+// per sequence).
+struct SelectArgs {
+  const int8_t* q_idx;
+  const int8_t* k_idx;
+  const int64_t* ent_off;
+  const int64_t* q_off;
+  const int64_t* q_pos;
+  int32_t* idx;
+  int32_t* count;
+  int32_t* n_vis;   // may be null
+  int32_t c;
+  int32_t max_entries;
+  int32_t max_q;
+  int32_t k;
+};
+constexpr int SELECT_MIN_Q = 16;
+hipError_t launch_index_select(const SelectArgs& a, int batch, hipStream_t st);
+
 // ------------------------------------------------------------ top-k
 struct TopkWs {
   int32_t* hist;       // [rows][2048] coarse histogram, zero on entry and on exit

@@ -1,8 +1,9 @@
 """Composed steps over the C ABI: buffer allocation and call order only.
 
-CsaStep   csa_index_score (with the fused first radix pass) -> csa_topk_select
-          -> csa_sparse_attn, for decode (one query per sequence) or chunked
-          prefill (many queries per sequence).
+CsaStep   selection, then csa_sparse_attn.  Selection is csa_index_score (with the
+          fused first radix pass) -> csa_topk_select for decode (fewer than 16
+          queries per sequence), and csa_index_select (scores never written) for
+          chunked prefill (16 or more queries per sequence).
 HcaStep   hca_dense_attn.
 HybridStep  hybrid_layer_step over a list of CSA / HCA layers.
 
@@ -14,8 +15,11 @@ from __future__ import annotations
 import torch
 
 from . import (LCA_LAYER_CSA, LCA_LAYER_HCA, attn_workspace_bytes, csa_index_score,
-               csa_sparse_attn, csa_topk_select, csa_topk_workspace_bytes, hca_dense_attn,
+               csa_index_select, csa_sparse_attn, csa_topk_select, csa_topk_workspace_bytes, hca_dense_attn,
                hybrid_layer_step, hybrid_workspace_bytes, make_layers, workspace)
+
+
+SELECT_MIN_Q = 16   # query tokens per sequence from which csa_index_select applies
 
 
 def _round4(n: int) -> int:
@@ -23,19 +27,31 @@ def _round4(n: int) -> int:
 
 
 class CsaStep:
-    def __init__(self, batch, max_q, max_entries, heads, topk, c, device="cuda", splits=0):
+    """fused: None picks csa_index_select when max_q >= 16; True / False force it
+    on / off (the two-call path materialises the scores in self.scores)."""
+
+    def __init__(self, batch, max_q, max_entries, heads, topk, c, device="cuda", splits=0,
+                 fused=None):
         self.batch, self.max_q, self.max_entries = batch, max_q, max_entries
         self.heads, self.topk, self.c, self.splits = heads, topk, c, splits
         rows = batch * max_q
         self.rows = rows
-        self.scores = torch.empty(rows, _round4(max_entries), dtype=torch.int32, device=device)
+        self.fused = (max_q >= SELECT_MIN_Q) if fused is None else fused
         self.n_vis = torch.empty(rows, dtype=torch.int32, device=device)
         self.idx = torch.empty(rows, topk, dtype=torch.int32, device=device)
         self.count = torch.empty(rows, dtype=torch.int32, device=device)
-        self.tws = workspace(csa_topk_workspace_bytes(rows, max_entries, topk), device)
+        if not self.fused:
+            self.scores = torch.empty(rows, _round4(max_entries), dtype=torch.int32,
+                                      device=device)
+            self.tws = workspace(csa_topk_workspace_bytes(rows, max_entries, topk), device)
         self.aws = workspace(attn_workspace_bytes(rows, heads, max_q, splits), device)
 
     def select(self, q_idx, q_off, q_pos, k_idx, ent_off, stream=None):
+        if self.fused:
+            csa_index_select(q_idx, q_off, q_pos, k_idx, ent_off, self.batch, self.max_q,
+                             self.max_entries, self.c, self.topk, self.idx, self.count,
+                             self.n_vis, stream=stream)
+            return
         csa_index_score(q_idx, q_off, q_pos, k_idx, ent_off, self.batch, self.max_q,
                         self.max_entries, self.c, self.scores, self.n_vis, ws=self.tws,
                         stream=stream)

@@ -163,6 +163,79 @@ def test_index_score_gemm_bit_exact(fused, case):
                  ent_off, q_off, c)
 
 
+def _select_case(name):
+    """(Ns, nq, k, k_idx, q_idx) for csa_index_select: 16+ query tokens per sequence."""
+    g = rng(212, 0, ["ragged", "ties", "all_equal", "extreme", "k_large", "k_one",
+                     "tiles"].index(name))
+    if name == "ragged":
+        Ns, nq, k = [3000, 10001, 0, 700, 64], [16, 37, 5, 50, 17], 256
+        kk = int8_uniform(g, (sum(Ns), 64))
+        qq = int8_uniform(g, (sum(nq), 64))
+    elif name == "ties":   # scores in [-64, 64]: the threshold value has many copies
+        Ns, nq, k = [20000], [40], 2048
+        kk = g.integers(-1, 2, (sum(Ns), 64)).astype(np.int8)
+        qq = g.integers(-1, 2, (sum(nq), 64)).astype(np.int8)
+    elif name == "all_equal":
+        Ns, nq, k = [9000], [16], 100
+        kk = np.tile(int8_uniform(g, (1, 64)), (9000, 1))
+        qq = int8_uniform(g, (16, 64))
+    elif name == "extreme":   # scores up to +-64 * 127^2
+        Ns, nq, k = [5000], [16], 77
+        kk = (127 * np.where(g.random((5000, 64)) < 0.5, -1, 1)).astype(np.int8)
+        kk[:3] = 127
+        kk[3:6] = -127
+        qq = np.full((16, 64), 127, np.int8)
+        qq[1::2] = -127
+    elif name == "k_large":   # k above the LDS-staged rows: rows written in place
+        Ns, nq, k = [10001], [20], 3000
+        kk = int8_uniform(g, (sum(Ns), 64))
+        qq = int8_uniform(g, (sum(nq), 64))
+    elif name == "k_one":
+        Ns, nq, k = [5000, 300], [16, 33], 1
+        kk = int8_uniform(g, (sum(Ns), 64))
+        qq = int8_uniform(g, (sum(nq), 64))
+    else:   # "tiles": several row tiles of one sequence, k = 2048
+        Ns, nq, k = [20000], [64], 2048
+        kk = int8_uniform(g, (sum(Ns), 64))
+        qq = int8_uniform(g, (sum(nq), 64))
+    return Ns, nq, k, kk, qq
+
+
+@pytest.mark.parametrize("name", ["ragged", "ties", "all_equal", "extreme", "k_large", "k_one",
+                                  "tiles"])
+def test_index_select_bit_exact(name):
+    """csa_index_select (scores never written) against the oracle's scores + top-k."""
+    step(f"csa_index_select {name}")
+    Ns, nq, k, k_idx, q_idx = _select_case(name)
+    c = 4
+    B, max_q = len(Ns), max(nq)
+    ent_off, q_off = offsets(Ns), offsets(nq)
+    rows = int(q_off[-1])
+    q_pos = []
+    for b in range(B):
+        for i in range(nq[b]):
+            q_pos.append(0 if i % 13 == 5 else ((i + 1) * (Ns[b] * c + 2)) // nq[b])
+    idx = torch.full((rows, k), -5, dtype=torch.int32, device=DEV)
+    count = torch.full((rows,), -5, dtype=torch.int32, device=DEV)
+    n_vis = torch.full((rows,), -5, dtype=torch.int32, device=DEV)
+    lca.csa_index_select(i8_dev(q_idx), i64_dev(q_off), i64_dev(q_pos),
+                         i8_dev(k_idx if len(k_idx) else np.zeros((1, 64), np.int8)),
+                         i64_dev(ent_off), B, max_q, max(Ns), c, k, idx, count, n_vis)
+    torch.cuda.synchronize()
+    I, C, NV = idx.cpu().numpy(), count.cpu().numpy(), n_vis.cpu().numpy()
+    for b in range(B):
+        keys = k_idx[ent_off[b]:ent_off[b + 1]]
+        for i in range(nq[b]):
+            r = int(q_off[b]) + i
+            nv = oracle.n_visible(q_pos[r], c, Ns[b])
+            ref = oracle.topk_select(oracle.index_scores(q_idx[r], keys) if Ns[b] else
+                                     np.zeros(0, np.int64), nv, k)
+            assert NV[r] == nv, (b, i)
+            assert C[r] == len(ref), (b, i)
+            assert np.array_equal(I[r, :len(ref)], ref), (b, i)
+            assert np.all(I[r, len(ref):] == -1), (b, i)
+
+
 # ------------------------------------------------------------------ top-k
 def _topk_cases():
     g = rng(220, 0, 0)

@@ -208,7 +208,6 @@ __global__ __launch_bounds__(SL_NT) void index_select_kernel(SelectArgs a, int t
     __syncthreads();
     // ---- sweep 2: fine histograms of the threshold bins
     const int32_t bA = s_bin[n];
-    const int32_t need = k - s_above[n];
     for (int i = t; i < SL_ROWS * FINE_BINS; i += SL_NT) sm[i] = 0;
     __syncthreads();
     int32_t* hf = sm + n * FINE_BINS;

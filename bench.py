@@ -83,6 +83,21 @@ def traffic_from_profile(tag, src_files):
     return rec.get("bytes_per_launch")
 
 
+CPU_BUDGET_S = 12.0   # oracle time the cpu_baseline leg aims for
+
+
+def _timed_reps(fn, budget):
+    """Mean time of fn() over repeated calls until `budget` seconds are spent (at least
+    one call; the inputs are converted once, outside the timing)."""
+    spent, reps = 0.0, 0
+    while reps == 0 or spent < budget:
+        t0 = time.perf_counter()
+        fn()
+        spent += time.perf_counter() - t0
+        reps += 1
+    return spent / reps, spent, reps
+
+
 class _OneThread:
     """Run the oracle with one BLAS thread so the reported core count is exact."""
 
@@ -196,7 +211,8 @@ class HybridRunner(_Capture):
         import oracle
         wl, torch = self.wl, self.torch
         n = n or wl.batch
-        t_or = 0.0
+        per_call = CPU_BUDGET_S / (n * len(self.layers))
+        t_tok, spent, calls = 0.0, 0.0, 0
         with _OneThread():
             for b in range(n):
                 for d in self.layers:
@@ -204,18 +220,21 @@ class HybridRunner(_Capture):
                     Kc = oracle.bf16_bits_to_f64(_bits(d["k_cmp"][s:e]))
                     Vc = oracle.bf16_bits_to_f64(_bits(d["v_cmp"][s:e]))
                     q = oracle.bf16_bits_to_f64(_bits(d["q"][b]))
+                    L = int(self.L[b])
                     if d["csa"]:
                         kidx, qidx = d["k_idx"][s:e].cpu().numpy(), d["q_idx"][b].cpu().numpy()
-                        t0 = time.perf_counter()
-                        oracle.csa_decode(q, qidx, int(self.L[b]), Kc, Vc, kidx, d["ratio"],
-                                          wl.topk, SCALE)
+                        fn = lambda: oracle.csa_decode(q, qidx, L, Kc, Vc, kidx, d["ratio"],
+                                                       wl.topk, SCALE)
                     else:
-                        t0 = time.perf_counter()
-                        oracle.hca_decode(q, int(self.L[b]), Kc, Vc, d["ratio"], SCALE)
-                    t_or += time.perf_counter() - t0
-        return {"value": n / t_or, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+                        fn = lambda: oracle.hca_decode(q, L, Kc, Vc, d["ratio"], SCALE)
+                    mean, sp, r = _timed_reps(fn, per_call)
+                    t_tok += mean
+                    spent += sp
+                    calls += r
+        return {"value": n / t_tok, "unit": "tokens/s", "cores": 1, "kind": "oracle",
                 "sample": f"{n} of {wl.batch} sequences through all {wl.n_layers} layers, one "
-                          f"decode token each ({t_or:.1f} s of oracle time, transfers excluded)"}
+                          f"decode token each; {calls} oracle layer calls, {spent:.1f} s of "
+                          f"oracle time (transfers and conversions excluded)"}
 
 
 class CsaDecodeRunner(_Capture):
@@ -284,7 +303,7 @@ class CsaDecodeRunner(_Capture):
         wl, inp = self.wl, self.inp
         n = n or wl.batch
         r = inp["replicas"][0]
-        t_or = 0.0
+        t_tok, spent, calls = 0.0, 0.0, 0
         with _OneThread():
             for b in range(n):
                 s, e = int(inp["ent_off"][b]), int(inp["ent_off"][b + 1])
@@ -292,12 +311,16 @@ class CsaDecodeRunner(_Capture):
                 Vc = oracle.bf16_bits_to_f64(_bits(self.v_cmp[s:e]))
                 kidx, qidx = r["k_idx"][s:e].cpu().numpy(), r["q_idx"][b].cpu().numpy()
                 q = oracle.bf16_bits_to_f64(_bits(r["q"][b]))
-                t0 = time.perf_counter()
-                oracle.csa_decode(q, qidx, int(inp["L"][b]), Kc, Vc, kidx, wl.c, wl.topk, SCALE)
-                t_or += time.perf_counter() - t0
-        return {"value": n / t_or, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+                L = int(inp["L"][b])
+                mean, sp, rp = _timed_reps(
+                    lambda: oracle.csa_decode(q, qidx, L, Kc, Vc, kidx, wl.c, wl.topk, SCALE),
+                    CPU_BUDGET_S / n)
+                t_tok += mean
+                spent += sp
+                calls += rp
+        return {"value": n / t_tok, "unit": "tokens/s", "cores": 1, "kind": "oracle",
                 "sample": f"{n} of {wl.batch} sequences, one decode token each over the "
-                          f"compressed cache ({t_or:.1f} s of oracle time)"}
+                          f"compressed cache; {calls} oracle calls, {spent:.1f} s of oracle time"}
 
 
 class HcaDecodeRunner(_Capture):
@@ -351,17 +374,21 @@ class HcaDecodeRunner(_Capture):
         wl, inp = self.wl, self.inp
         n = n or wl.batch
         k, v = self.caches[0]
-        t_or = 0.0
+        t_tok, spent, calls = 0.0, 0.0, 0
         with _OneThread():
             for b in range(n):
                 s, e = int(inp["ent_off"][b]), int(inp["ent_off"][b + 1])
                 Kc, Vc = oracle.bf16_bits_to_f64(_bits(k[s:e])), oracle.bf16_bits_to_f64(_bits(v[s:e]))
                 q = oracle.bf16_bits_to_f64(_bits(inp["replicas"][0]["q"][b]))
-                t0 = time.perf_counter()
-                oracle.hca_decode(q, int(inp["L"][b]), Kc, Vc, wl.m, SCALE)
-                t_or += time.perf_counter() - t0
-        return {"value": n / t_or, "unit": "tokens/s", "cores": 1, "kind": "oracle",
-                "sample": f"{n} of {wl.batch} sequences ({t_or:.2f} s of oracle time)"}
+                L = int(inp["L"][b])
+                mean, sp, rp = _timed_reps(lambda: oracle.hca_decode(q, L, Kc, Vc, wl.m, SCALE),
+                                           CPU_BUDGET_S / n)
+                t_tok += mean
+                spent += sp
+                calls += rp
+        return {"value": n / t_tok, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+                "sample": f"{n} of {wl.batch} sequences; {calls} oracle calls, {spent:.1f} s "
+                          f"of oracle time"}
 
 
 class PrefillRunner(_Capture):
@@ -425,22 +452,25 @@ class PrefillRunner(_Capture):
     def cpu_baseline(self, n):
         import oracle
         wl, inp = self.wl, self.inp
-        n = n or 16
         Kc = oracle.bf16_bits_to_f64(_bits(self.k_cmp))
         Vc = oracle.bf16_bits_to_f64(_bits(self.v_cmp))
         kidx = inp["k_idx"].cpu().numpy()
-        rows = np.linspace(0, wl.new_tokens - 1, n).astype(int)
-        t_or = 0.0
+        # query tokens spread over the chunk, until the budget is spent (or n given)
+        order = np.random.default_rng(0).permutation(wl.new_tokens)
+        t_or, done = 0.0, 0
         with _OneThread():
-            for i in rows:
+            for i in order:
+                if (n and done >= n) or (not n and t_or >= CPU_BUDGET_S):
+                    break
                 q = oracle.bf16_bits_to_f64(_bits(inp["q"][i]))
                 qi = inp["q_idx"][i].cpu().numpy()
                 t0 = time.perf_counter()
                 oracle.csa_query(q, qi, wl.ctx_len + int(i), Kc, Vc, kidx, wl.c, wl.topk, SCALE)
                 t_or += time.perf_counter() - t0
-        return {"value": n / t_or, "unit": "tokens/s", "cores": 1, "kind": "oracle",
-                "sample": f"{n} of {wl.new_tokens} query tokens after compression "
-                          f"({t_or:.1f} s of oracle time)"}
+                done += 1
+        return {"value": done / t_or, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+                "sample": f"{done} of {wl.new_tokens} query tokens (random order) after "
+                          f"compression ({t_or:.1f} s of oracle time)"}
 
 
 RUNNERS = {"hybrid_decode": HybridRunner, "csa_decode": CsaDecodeRunner,

@@ -14,8 +14,11 @@
 // query tokens of one sequence and all of that sequence's entries, so it sees
 // every score of its rows and never needs another work-group's counts.  It
 // recomputes the scores with v_mfma_i32_16x16x64_i8 (16 entries x 16 tokens over
-// the whole d_idx = 64, exact int32) in three sweeps over the keys, which stream
-// from L2 (every row tile reads the same keys):
+// the whole d_idx = 64, exact int32) in sweeps over the keys, which stream from L2
+// (every row tile reads the same keys).  Usually two sweeps: the coarse
+// histograms, then (when every token's threshold bin holds at most SL_BIN_CAP
+// entries) the entries above the bin and inside it, collected in index order and
+// resolved in LDS.  Otherwise three:
 //   1. the coarse histogram, 2048 bins of key >> 10 per token, in LDS (key =
 //      score + 2^20, 21 bits); from it the threshold bin bA holding the k-th
 //      largest key and the count above it;
@@ -41,10 +44,12 @@ constexpr int SL_NW = SL_NT / WAVE;
 constexpr int SL_ROWS = 16;                   // query tokens per work-group (MFMA N)
 constexpr int SL_BLOCK = 64;                  // entries per wave and round: 4 MFMA tiles
 constexpr int SL_STAGE_K = 2048;              // k up to this: rows are staged in LDS
-constexpr int SL_FRONT = 2048;               // words ahead of the staged rows
+constexpr int SL_BIN_CAP = 256;              // threshold-bin entries per token, two-sweep path
+constexpr int SL_WT = 2 * SL_ROWS * (SL_NT / WAVE);   // wave totals, two round parities
+constexpr int SL_FRONT = SL_WT + SL_ROWS * SL_BIN_CAP;   // words ahead of the staged rows
 constexpr int SL_LDS = SL_FRONT + SL_ROWS * SL_STAGE_K;   // words; >= 16 x 2048 coarse bins
 static_assert(SL_LDS >= SL_ROWS * HIST_BINS, "LDS region must hold the coarse histograms");
-static_assert(SL_FRONT >= 2 * SL_ROWS * SL_NW, "the wave totals sit ahead of the staged rows");
+static_assert(SL_LDS >= SL_ROWS * FINE_BINS + SL_ROWS, "fine histograms and their counts");
 static_assert(SL_NW <= SL_ROWS, "s_tot holds one value per wave");
 
 // The value of lane l ^ 16 (l ^ 32): v_permlane16_swap (v_permlane32_swap) of a
@@ -135,10 +140,158 @@ __device__ __forceinline__ void sl_threshold(const int32_t* h, int j, int need, 
   }
 }
 
+// Two-sweep path, second sweep: each token's entries above its threshold bin bA
+// (all of them selected; fewer than k) and inside bA, each list in index order
+// (bA = -1 for a token that keeps every visible entry: they all count as above).
+// Then one wave per token resolves the threshold inside bA by ranking the bin's
+// entries (score desc, index asc), and writes the row: each entry's slot is its
+// rank in its own list plus the number of selected entries of the other list
+// with a lower index.
+__device__ __forceinline__ void sl_collect_finalize(
+    const i32x4* __restrict__ kp, const i32x4& qv, int32_t N, int32_t nround, int w, int lane,
+    int n, int grp, int32_t nv, int32_t bA, int k, int nr, int32_t* sm, int32_t* s_tot,
+    int32_t* s_na, int32_t* s_nb, int32_t* __restrict__ idx0) {
+  int32_t* wt = sm;                                // [2][16][waves] wave totals
+  int32_t* blist = sm + SL_WT;                     // [16][SL_BIN_CAP] (index << 10 | key & 1023)
+  int32_t* alist = sm + SL_FRONT;                  // [16][SL_STAGE_K] indices above bA
+  int32_t a_base = 0, b_base = 0;
+  __syncthreads();
+  sl_sweep(kp, qv, N, nround, w, lane, [&](const int32_t (&key)[4][4], int32_t rd, int32_t blk) __attribute__((always_inline)) {
+    uint32_t ba[4], bb[4];
+    int32_t ex[4];
+    int32_t wtot = 0;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      ba[u] = 0;
+      bb[u] = 0;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const bool vis = blk * SL_BLOCK + 16 * u + 4 * grp + r < nv;
+        const int32_t bin = key[u][r] >> 10;
+        ba[u] |= (uint32_t)(vis && bin > bA) << r;
+        bb[u] |= (uint32_t)(vis && bin == bA) << r;
+      }
+      const int32_t cnt = (int32_t)((__builtin_popcount(bb[u]) << 16) | __builtin_popcount(ba[u]));
+      const int32_t c1 = sl_partner16(cnt);
+      const int32_t pair = cnt + c1;
+      const int32_t x = (grp & 1) ? pair : cnt;
+      const int32_t lowpair = sl_partner32(pair);
+      ex[u] = wtot + ((grp & 2) ? x + lowpair : x) - cnt;
+      wtot += pair + lowpair;
+    }
+    int32_t* wr = wt + (rd & 1) * (SL_ROWS * SL_NW) + n * SL_NW;
+    if (grp == 0) wr[w] = wtot;
+    sl_lds_barrier();
+    int32_t pre = 0, tot = 0;
+#pragma unroll
+    for (int i = 0; i < SL_NW; ++i) {
+      const int32_t v = wr[i];
+      pre += i < w ? v : 0;
+      tot += v;
+    }
+    // entries above bA: walk the set bits
+    uint32_t m = 0;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) m |= ba[u] << (4 * u);
+    while (m) {
+      const int bit = __builtin_ctz(m);
+      m &= m - 1;
+      const int u = bit >> 2, r = bit & 3;
+      const uint32_t bau = u == 0 ? ba[0] : u == 1 ? ba[1] : u == 2 ? ba[2] : ba[3];
+      const int32_t exu = u == 0 ? ex[0] : u == 1 ? ex[1] : u == 2 ? ex[2] : ex[3];
+      const int32_t pos = a_base + ((pre + exu) & 0xffff) + __builtin_popcount(bau & ((1u << r) - 1));
+      if (pos < SL_STAGE_K) alist[n * SL_STAGE_K + pos] = blk * SL_BLOCK + 16 * u + 4 * grp + r;
+    }
+    // entries inside bA (rare)
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      if (bb[u] == 0) continue;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        if (bb[u] >> r & 1) {
+          const int32_t pos = b_base + ((pre + ex[u]) >> 16) + __builtin_popcount(bb[u] & ((1u << r) - 1));
+          if (pos < SL_BIN_CAP)
+            blist[n * SL_BIN_CAP + pos] = ((blk * SL_BLOCK + 16 * u + 4 * grp + r) << 10) | (key[u][r] & 1023);
+        }
+      }
+    }
+    a_base += tot & 0xffff;
+    b_base += tot >> 16;
+  });
+  if (w == 0 && grp == 0) {
+    s_na[n] = a_base;
+    s_nb[n] = b_base;
+  }
+  __syncthreads();
+  // one wave per token
+  for (int j = w; j < nr; j += SL_NW) {
+    const int32_t na = min(s_na[j], SL_STAGE_K), nb = min(s_nb[j], SL_BIN_CAP);
+    const int32_t need = max(0, k - na);                // keys to take from the bin
+    int32_t* bl = blist + j * SL_BIN_CAP;
+    const int32_t* al = alist + j * SL_STAGE_K;
+    constexpr int PB = SL_BIN_CAP / WAVE;
+    int32_t e[PB], rank[PB];
+#pragma unroll
+    for (int u = 0; u < PB; ++u) {
+      e[u] = lane + WAVE * u < nb ? bl[lane + WAVE * u] : 0;
+      rank[u] = 0;
+    }
+    for (int q = 0; q < nb; ++q) {   // rank by (key desc, index asc)
+      const int32_t lq = bl[q] & 1023;
+#pragma unroll
+      for (int u = 0; u < PB; ++u) {
+        const int32_t li = e[u] & 1023;
+        rank[u] += (lq > li || (lq == li && q < lane + WAVE * u)) ? 1 : 0;
+      }
+    }
+    // selected bin entries, and how many of them precede each list position
+    int32_t run = 0;
+    int32_t sel_ex[PB];
+    bool sel[PB];
+#pragma unroll
+    for (int u = 0; u < PB; ++u) {
+      sel[u] = lane + WAVE * u < nb && rank[u] < need;
+      const uint64_t bal = __ballot(sel[u]);
+      sel_ex[u] = run + __builtin_popcountll(bal & ((1ull << lane) - 1));
+      run += __builtin_popcountll(bal);
+    }
+    const int32_t nsel = run;
+#pragma unroll
+    for (int u = 0; u < PB; ++u)   // keep the index, replace the key bits by the count
+      if (lane + WAVE * u < nb) bl[lane + WAVE * u] = (e[u] & ~1023) | sel_ex[u];
+    int32_t* orow = idx0 + (int64_t)j * k;
+    for (int p = lane; p < na; p += WAVE) {   // above-bA entries
+      const int32_t x = al[p];
+      int lo = 0, hi = nb;                     // bin entries with a lower index
+      while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if ((bl[mid] >> 10) < x) lo = mid + 1; else hi = mid;
+      }
+      const int32_t before = lo < nb ? (bl[lo] & 1023) : nsel;
+      const int32_t pos = p + before;
+      if (pos < k) orow[pos] = x;
+    }
+#pragma unroll
+    for (int u = 0; u < PB; ++u) {            // selected bin entries
+      if (!sel[u]) continue;
+      const int32_t y = e[u] >> 10;
+      int lo = 0, hi = na;
+      while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (al[mid] < y) lo = mid + 1; else hi = mid;
+      }
+      const int32_t pos = sel_ex[u] + lo;
+      if (pos < k) orow[pos] = y;
+    }
+    for (int p = na + nsel + lane; p < k; p += WAVE) orow[p] = -1;
+  }
+}
+
 template <bool STAGE>
 __global__ __launch_bounds__(SL_NT) void index_select_kernel(SelectArgs a, int tiles_per_seq) {
   __shared__ __attribute__((aligned(16))) int32_t sm[SL_LDS];
   __shared__ int32_t s_bin[SL_ROWS], s_above[SL_ROWS], s_tot[SL_ROWS], s_flag;
+  __shared__ int32_t s_na[SL_ROWS], s_nb[SL_ROWS];
   const int b = blockIdx.y / tiles_per_seq;
   const int q0 = (blockIdx.y - b * tiles_per_seq) * SL_ROWS;
   const int64_t r0 = a.q_off[b];
@@ -205,7 +358,19 @@ __global__ __launch_bounds__(SL_NT) void index_select_kernel(SelectArgs a, int t
       const int32_t vj = (int32_t)min(a.q_pos[r0 + q0 + j] / a.c, (int64_t)N);
       if (vj > k) sl_threshold<HIST_BINS>(sm + j * HIST_BINS, j, k, lane, &s_bin[j], &s_above[j]);
     }
+    // Two-sweep path: when every token's threshold bin holds at most SL_BIN_CAP
+    // entries (the usual case: about k/20 for Gaussian-like scores), one more sweep
+    // collects each token's entries above the bin and inside it, in index order,
+    // and the threshold and the merge are resolved in LDS.
+    if (t == 0) s_flag = (STAGE && N < (1 << 21)) ? 1 : 0;
     __syncthreads();
+    if (t < nr && s_bin[t] >= 0 && sm[t * HIST_BINS + (s_bin[t] ^ t)] > SL_BIN_CAP) s_flag = 0;
+    __syncthreads();
+    if (s_flag) {
+      sl_collect_finalize(kp, qv, N, nround, w, lane, n, grp, nv, thr ? s_bin[n] : -1, k, nr,
+                          sm, s_tot, s_na, s_nb, idx0);
+      return;
+    }
     // ---- sweep 2: fine histograms of the threshold bins
     const int32_t bA = s_bin[n];
     for (int i = t; i < SL_ROWS * FINE_BINS; i += SL_NT) sm[i] = 0;

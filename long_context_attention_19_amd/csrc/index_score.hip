@@ -7,7 +7,7 @@
 //
 // Decode streams 64 bytes of key per entry and does 16 int8 MACs per 16 bytes,
 // far below the ALU ridge: the kernel is bound by HBM.  Layout of the work:
-//   - a work-group owns IS_CHUNK consecutive entries of one sequence of one layer
+//   - a work-group owns 1024 or 2048 consecutive entries of one sequence of one layer
 //     (grid z = layer: the layers of a hybrid stack are scored in one launch);
 //   - in each round, lane t loads the 16-byte piece (t % 4) of key (t / 4), so a
 //     wave's 128-bit loads cover 1 KiB of contiguous key rows, and IS_ROUNDS
@@ -29,11 +29,15 @@ namespace lca {
 constexpr int IS_NT = 256;
 constexpr int IS_ROUNDS = 8;
 constexpr int IS_KEYS_PER_PASS = IS_NT / 4 * IS_ROUNDS;   // 512
-constexpr int IS_PASSES = 4;
-constexpr int IS_CHUNK = IS_KEYS_PER_PASS * IS_PASSES;     // 2048 entries per work-group
+// Entries per work-group: IS_KEYS_PER_PASS x PASSES.  2048 (4 passes) for a few rows,
+// where larger groups keep the per-group setup small against the stream; 1024 (2
+// passes) from IS_SMALL_CHUNK_ROWS rows on, where the finer grain evens out the
+// ragged ends of the rows across the chip.
+constexpr int IS_SMALL_CHUNK_ROWS = 32;
 
-template <bool HIST>
+template <bool HIST, int IS_PASSES>
 __global__ __launch_bounds__(IS_NT) void index_score_kernel(IndexBatch ib) {
+  constexpr int IS_CHUNK = IS_KEYS_PER_PASS * IS_PASSES;
   __shared__ int32_t lh[HIST ? HIST_BINS : 1];
   __shared__ __attribute__((aligned(16))) int32_t s_sc[IS_CHUNK];   // the group's scores
   const IndexLayer& L = ib.layer[blockIdx.z];
@@ -348,14 +352,20 @@ hipError_t launch_index_score(const IndexBatch& ib, int batch, hipStream_t st) {
       hipLaunchKernelGGL(index_gemm_kernel<false>, grid, dim3(IG_NT), 0, st, ib, tiles, ranges);
     return hipGetLastError();
   }
+  const bool fine_grain = (int64_t)batch * ib.max_q * ib.n >= IS_SMALL_CHUNK_ROWS;
+  const int chunk = IS_KEYS_PER_PASS * (fine_grain ? 2 : 4);
   int chunks = 1;
   for (int l = 0; l < ib.n; ++l)
-    chunks = max(chunks, (ib.layer[l].max_entries + IS_CHUNK - 1) / IS_CHUNK);
+    chunks = max(chunks, (ib.layer[l].max_entries + chunk - 1) / chunk);
   dim3 grid((unsigned)chunks, (unsigned)(batch * ib.max_q), (unsigned)ib.n);
-  if (hist)
-    hipLaunchKernelGGL(index_score_kernel<true>, grid, dim3(IS_NT), 0, st, ib);
+  if (hist && fine_grain)
+    hipLaunchKernelGGL((index_score_kernel<true, 2>), grid, dim3(IS_NT), 0, st, ib);
+  else if (hist)
+    hipLaunchKernelGGL((index_score_kernel<true, 4>), grid, dim3(IS_NT), 0, st, ib);
+  else if (fine_grain)
+    hipLaunchKernelGGL((index_score_kernel<false, 2>), grid, dim3(IS_NT), 0, st, ib);
   else
-    hipLaunchKernelGGL(index_score_kernel<false>, grid, dim3(IS_NT), 0, st, ib);
+    hipLaunchKernelGGL((index_score_kernel<false, 4>), grid, dim3(IS_NT), 0, st, ib);
   return hipGetLastError();
 }
 

@@ -59,11 +59,12 @@ def test_kv_compress_append_and_capacity():
 
 # ------------------------------------------------------------------ index scores
 @pytest.mark.parametrize("fused", [False, True])
-def test_index_score_bit_exact(fused):
-    step(f"csa_index_score fused={fused}")
-    g = rng(210, int(fused), 0)
-    Ns = [100, 5000, 10001, 0, 2048]
-    nq = [1, 3, 1, 2, 1]
+@pytest.mark.parametrize("many", [False, True])   # 40 rows: the 1024-entry work-groups
+def test_index_score_bit_exact(fused, many):
+    step(f"csa_index_score fused={fused} many_rows={many}")
+    g = rng(210, int(fused), int(many))
+    Ns = [100, 5000, 10001, 0, 2048] * (8 if many else 1)
+    nq = [1, 3, 1, 2, 1] * (8 if many else 1)
     c = 4
     B, max_q = len(Ns), max(nq)
     ent_off, q_off = offsets(Ns), offsets(nq)

@@ -7,7 +7,7 @@
 //
 // Decode streams 64 bytes of key per entry and does 16 int8 MACs per 16 bytes,
 // far below the ALU ridge: the kernel is bound by HBM.  Layout of the work:
-//   - a work-group owns 1024 or 2048 consecutive entries of one sequence of one layer
+//   - a work-group owns 512 to 2048 consecutive entries of one sequence of one layer
 //     (grid z = layer: the layers of a hybrid stack are scored in one launch);
 //   - in each round, lane t loads the 16-byte piece (t % 4) of key (t / 4), so a
 //     wave's 128-bit loads cover 1 KiB of contiguous key rows, and IS_ROUNDS
@@ -29,11 +29,14 @@ namespace lca {
 constexpr int IS_NT = 256;
 constexpr int IS_ROUNDS = 8;
 constexpr int IS_KEYS_PER_PASS = IS_NT / 4 * IS_ROUNDS;   // 512
-// Entries per work-group: IS_KEYS_PER_PASS x PASSES.  2048 (4 passes) for a few rows,
-// where larger groups keep the per-group setup small against the stream; 1024 (2
-// passes) from IS_SMALL_CHUNK_ROWS rows on, where the finer grain evens out the
-// ragged ends of the rows across the chip.
+// Entries per work-group: IS_KEYS_PER_PASS x PASSES (512, 1024 or 2048).  Many rows
+// (IS_SMALL_CHUNK_ROWS and up) take 1024: a finer grain than 2048 evens out the
+// ragged ends of the rows across the chip (512 measured slower again).  With few rows
+// nearly every resident group works on the same few rows, and each flushes its
+// histogram into that row's bins with global atomics: groups then take up to 2048
+// entries, so that a row has at most about IS_GROUPS_PER_ROW of them.
 constexpr int IS_SMALL_CHUNK_ROWS = 32;
+constexpr int IS_GROUPS_PER_ROW = 128;
 
 template <bool HIST, int IS_PASSES>
 __global__ __launch_bounds__(IS_NT) void index_score_kernel(IndexBatch ib) {
@@ -111,9 +114,11 @@ __global__ __launch_bounds__(IS_NT) void index_score_kernel(IndexBatch ib) {
   __syncthreads();
   {
     const int64_t cnt = min((int64_t)IS_CHUNK, N - base);
+    // 4 scores per thread and store: a 512-entry chunk needs only half the threads
 #pragma unroll
-    for (int u = 0; u < IS_CHUNK / (4 * IS_NT); ++u) {
+    for (int u = 0; u < (IS_CHUNK + 4 * IS_NT - 1) / (4 * IS_NT); ++u) {
       const int q = 4 * (t + IS_NT * u);
+      if (q >= IS_CHUNK) break;
       if (q + 4 <= cnt) {
         *reinterpret_cast<i32x4*>(srow + base + q) = *reinterpret_cast<const i32x4*>(&s_sc[q]);
       } else {
@@ -352,20 +357,25 @@ hipError_t launch_index_score(const IndexBatch& ib, int batch, hipStream_t st) {
       hipLaunchKernelGGL(index_gemm_kernel<false>, grid, dim3(IG_NT), 0, st, ib, tiles, ranges);
     return hipGetLastError();
   }
-  const bool fine_grain = (int64_t)batch * ib.max_q * ib.n >= IS_SMALL_CHUNK_ROWS;
-  const int chunk = IS_KEYS_PER_PASS * (fine_grain ? 2 : 4);
+  int passes = 2;
+  if ((int64_t)batch * ib.max_q * ib.n < IS_SMALL_CHUNK_ROWS) {
+    passes = 1;
+    while (passes < 4 && (int64_t)passes * IS_KEYS_PER_PASS * IS_GROUPS_PER_ROW < max_n) passes *= 2;
+  }
+  const int chunk = IS_KEYS_PER_PASS * passes;
   int chunks = 1;
   for (int l = 0; l < ib.n; ++l)
     chunks = max(chunks, (ib.layer[l].max_entries + chunk - 1) / chunk);
   dim3 grid((unsigned)chunks, (unsigned)(batch * ib.max_q), (unsigned)ib.n);
-  if (hist && fine_grain)
-    hipLaunchKernelGGL((index_score_kernel<true, 2>), grid, dim3(IS_NT), 0, st, ib);
-  else if (hist)
-    hipLaunchKernelGGL((index_score_kernel<true, 4>), grid, dim3(IS_NT), 0, st, ib);
-  else if (fine_grain)
-    hipLaunchKernelGGL((index_score_kernel<false, 2>), grid, dim3(IS_NT), 0, st, ib);
-  else
-    hipLaunchKernelGGL((index_score_kernel<false, 4>), grid, dim3(IS_NT), 0, st, ib);
+#define LCA_IS_LAUNCH(P)                                                                  \
+  do {                                                                                    \
+    if (hist) hipLaunchKernelGGL((index_score_kernel<true, P>), grid, dim3(IS_NT), 0, st, ib); \
+    else hipLaunchKernelGGL((index_score_kernel<false, P>), grid, dim3(IS_NT), 0, st, ib); \
+  } while (0)
+  if (passes == 1) LCA_IS_LAUNCH(1);
+  else if (passes == 2) LCA_IS_LAUNCH(2);
+  else LCA_IS_LAUNCH(4);
+#undef LCA_IS_LAUNCH
   return hipGetLastError();
 }
 

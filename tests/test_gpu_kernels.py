@@ -59,12 +59,17 @@ def test_kv_compress_append_and_capacity():
 
 # ------------------------------------------------------------------ index scores
 @pytest.mark.parametrize("fused", [False, True])
-@pytest.mark.parametrize("many", [False, True])   # 40 rows: the 1024-entry work-groups
-def test_index_score_bit_exact(fused, many):
-    step(f"csa_index_score fused={fused} many_rows={many}")
-    g = rng(210, int(fused), int(many))
-    Ns = [100, 5000, 10001, 0, 2048] * (8 if many else 1)
-    nq = [1, 3, 1, 2, 1] * (8 if many else 1)
+@pytest.mark.parametrize("shape", ["few", "many", "long"])
+def test_index_score_bit_exact(fused, shape):
+    """Work-group sizes: few short rows (512 entries), 40 rows (512), a few rows of
+    up to 100,000 entries (1024)."""
+    step(f"csa_index_score fused={fused} shape={shape}")
+    g = rng(210, int(fused), ["few", "many", "long"].index(shape))
+    if shape == "long":
+        Ns, nq = [100000, 70001], [2, 1]
+    else:
+        Ns = [100, 5000, 10001, 0, 2048] * (8 if shape == "many" else 1)
+        nq = [1, 3, 1, 2, 1] * (8 if shape == "many" else 1)
     c = 4
     B, max_q = len(Ns), max(nq)
     ent_off, q_off = offsets(Ns), offsets(nq)
@@ -76,7 +81,7 @@ def test_index_score_bit_exact(fused, many):
     for b in range(B):
         for i in range(nq[b]):
             q_pos.append(Ns[b] * c + 3 if i == 0 else max(0, Ns[b] * c - 17 * i * c - i))
-    ld = 10004
+    ld = max(Ns) + 4 - max(Ns) % 4
     scores = torch.full((B * max_q, ld), 12345, dtype=torch.int32, device=DEV)
     n_vis = torch.full((B * max_q,), -7, dtype=torch.int32, device=DEV)
     ws = lca.workspace(lca.csa_topk_workspace_bytes(B * max_q, max(Ns), 64)) if fused else None

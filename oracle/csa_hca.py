@@ -166,6 +166,64 @@ def hca_query(q, pos: int, Kc, Vc, m: int, scale: float):
 
 
 # --------------------------------------------------------------------------------------
+# sliding-window branch over the state cache
+
+
+def window_tokens(pos: int, w: int, pos0: int, n_buf: int):
+    """Raw tokens the sliding-window branch of a query at position `pos` attends.
+
+    PAGE section 3-2 item 2: CSA and HCA both add a branch that sees the most
+    recent tokens uncompressed (window 128 in the config table); section 3-2
+    item 4: those tokens, and the tail not yet ready for compression, live in a
+    state cache apart from the compressed cache.  Reading: the window is the w
+    raw tokens strictly before the query, absolute positions [pos - w, pos) (the
+    compressed blocks a query sees also end before it).  The state buffer holds
+    the tokens at positions pos0 .. pos0 + n_buf - 1; the window is what of it
+    falls in that range.  Returns buffer indices [lo, hi), lo <= hi."""
+    lo = max(pos - w, pos0) - pos0
+    hi = min(pos, pos0 + n_buf) - pos0
+    lo = min(max(lo, 0), n_buf)
+    return lo, max(hi, lo)
+
+
+def attention_union(q, K, V, Kw, Vw, scale: float):
+    """Attention over the compressed branch's entries and the window's raw tokens.
+
+    Reading: the window branch adds its keys to the same softmax (one
+    distribution over both key sets); the page gives no weights that a separate
+    combination of two branches would need.  Plain definition: concatenate the
+    two key / value sets and attend."""
+    D = np.asarray(q).shape[-1]
+    K = np.asarray(K, np.float64).reshape(-1, D)
+    V = np.asarray(V, np.float64).reshape(-1, D)
+    Kw = np.asarray(Kw, np.float64).reshape(-1, D)
+    Vw = np.asarray(Vw, np.float64).reshape(-1, D)
+    return attention(q, np.concatenate([K, Kw]), np.concatenate([V, Vw]), scale)
+
+
+def csa_query_swa(q, q_idx, pos: int, Kc, Vc, k_idx, c: int, topk: int, scale: float,
+                  Kw, Vw, pos0: int, w: int):
+    """CSA query with the sliding-window branch: the selected compressed entries and
+    the window's raw tokens (Kw, Vw: the state buffer starting at position pos0)."""
+    n_vis = n_visible(pos, c, Kc.shape[0])
+    idx = topk_select(index_scores(q_idx, k_idx), n_vis, topk)
+    lo, hi = window_tokens(pos, w, pos0, np.asarray(Kw).shape[0])
+    o, lse, p = attention_union(q, np.asarray(Kc)[idx], np.asarray(Vc)[idx],
+                                np.asarray(Kw)[lo:hi], np.asarray(Vw)[lo:hi], scale)
+    return {"o": o, "lse": lse, "p": p, "idx": idx, "n_vis": n_vis, "window": (lo, hi)}
+
+
+def hca_query_swa(q, pos: int, Kc, Vc, m: int, scale: float, Kw, Vw, pos0: int, w: int):
+    """HCA query with the sliding-window branch: every visible compressed entry and
+    the window's raw tokens."""
+    n_vis = n_visible(pos, m, Kc.shape[0])
+    lo, hi = window_tokens(pos, w, pos0, np.asarray(Kw).shape[0])
+    o, lse, p = attention_union(q, np.asarray(Kc)[:n_vis], np.asarray(Vc)[:n_vis],
+                                np.asarray(Kw)[lo:hi], np.asarray(Vw)[lo:hi], scale)
+    return {"o": o, "lse": lse, "p": p, "n_vis": n_vis, "window": (lo, hi)}
+
+
+# --------------------------------------------------------------------------------------
 # composed steps
 
 

@@ -58,7 +58,7 @@
 extern "C" {
 #endif
 
-#define LCA_ABI_VERSION 1
+#define LCA_ABI_VERSION 2
 
 enum lca_status {
   LCA_OK = 0,
@@ -209,6 +209,30 @@ int32_t lca_hca_dense_attn(const lca_bf16* q, const lca_bf16* k_cmp, const lca_b
                            lca_bf16* out, float* lse, void* ws, size_t ws_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * window_attn — the sliding-window branch, merged into a compressed branch's result.
+ * Page section 3-2 item 2: CSA and HCA both add a branch over the most recent tokens
+ * uncompressed (window 128 in the config table); section 3-2 item 4: those tokens
+ * live in a state cache beside the compressed cache.  Reading: the window is the
+ * `window` raw tokens strictly before the query (positions [p - window, p)), and
+ * the branch adds its keys to the same softmax as the compressed entries.
+ *
+ *   win_k, win_v  [win_off[B], head_dim] bf16 raw tokens of each sequence's state
+ *            buffer; buffer b's first row is the token at absolute position
+ *            win_pos0[b] (device int64 [B]).  Tokens of the window missing from the
+ *            buffer are not attended.
+ *   q, q_off, q_pos, batch, max_q, heads, head_dim, scale  as for the attention calls.
+ *   out, lse in: the compressed branch's result for every row (lse natural log,
+ *            -inf with out = 0 for a row that attended nothing); out: the result
+ *            of one softmax over both key sets (log-sum-exp merge).  lse required.
+ *   window >= 0 (0: nothing to do).  No workspace.
+ * ------------------------------------------------------------------------- */
+int32_t lca_window_attn(const lca_bf16* q, const lca_bf16* win_k, const lca_bf16* win_v,
+                        const int64_t* win_off, const int64_t* win_pos0, const int64_t* q_off,
+                        const int64_t* q_pos, int32_t batch, int32_t max_q, int32_t window,
+                        int32_t heads, int32_t head_dim, float scale, lca_bf16* out, float* lse,
+                        void* stream);
+
+/* ---------------------------------------------------------------------------
  * hybrid_layer_step — a stack of independent attention layers over the same
  * batch, CSA and HCA interleaved (page section 3-2 item 2).  Each layer has its
  * own cache and queries; a CSA layer runs index_score -> topk_select ->
@@ -237,6 +261,12 @@ typedef struct lca_layer {
   float* lse;            /* [rows, heads] or NULL */
   int32_t* idx;          /* CSA out: [rows, topk] */
   int32_t* count;        /* CSA out: [rows] */
+  /* optional sliding-window branch (window = 0: none), as lca_window_attn; needs lse */
+  const lca_bf16* win_k; /* [win_off[B], 128] raw tokens of the state cache */
+  const lca_bf16* win_v;
+  const int64_t* win_off;  /* [B+1] device */
+  const int64_t* win_pos0; /* [B] device: absolute position of each buffer's first row */
+  int32_t window;
 } lca_layer;
 
 size_t lca_hybrid_workspace_bytes(const lca_layer* layers, int32_t n_layers, int32_t batch,

@@ -34,7 +34,9 @@ LCA_HYBRID_PHASES = 3
 class LcaLayer(ctypes.Structure):
     _fields_ = [("kind", _i32), ("ratio", _i32), ("topk", _i32), ("max_entries", _i32),
                 ("q", _vp), ("q_idx", _vp), ("k_cmp", _vp), ("v_cmp", _vp), ("k_idx", _vp),
-                ("ent_off", _vp), ("out", _vp), ("lse", _vp), ("idx", _vp), ("count", _vp)]
+                ("ent_off", _vp), ("out", _vp), ("lse", _vp), ("idx", _vp), ("count", _vp),
+                ("win_k", _vp), ("win_v", _vp), ("win_off", _vp), ("win_pos0", _vp),
+                ("window", _i32)]
 
 
 _SIGS = {
@@ -47,6 +49,8 @@ _SIGS = {
                                    _i64, _vp, _vp, _sz, _vp]),
     "lca_csa_index_select": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32,
                                     _vp, _vp, _vp, _vp]),
+    "lca_window_attn": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
+                               _f32, _vp, _vp, _vp]),
     "lca_csa_topk_workspace_bytes": (_sz, [_i32, _i32, _i32]),
     "lca_csa_topk_select": (_i32, [_vp, _i64, _i32, _i32, _vp, _i32, _vp, _vp, _vp, _sz, _u32,
                                    _vp]),
@@ -144,6 +148,13 @@ def csa_index_select(q_idx, q_off, q_pos, k_idx, ent_off, batch, max_q, max_entr
         q_idx.shape[-1], c, k, _p(idx), _p(count), _p(n_vis), _s(stream)))
 
 
+def window_attn(q, win_k, win_v, win_off, win_pos0, q_off, q_pos, batch, max_q, window, scale,
+                out, lse, stream=None):
+    _check("lca_window_attn", _lib.lca_window_attn(
+        _p(q), _p(win_k), _p(win_v), _p(win_off), _p(win_pos0), _p(q_off), _p(q_pos), batch,
+        max_q, window, q.shape[-2], q.shape[-1], scale, _p(out), _p(lse), _s(stream)))
+
+
 def csa_topk_select(scores, rows, max_n, n_vis, k, idx, count, ws, hist_ready=False,
                     stream=None):
     _check("lca_csa_topk_select", _lib.lca_csa_topk_select(
@@ -173,7 +184,9 @@ def make_layers(layers):
         arr[i] = LcaLayer(L["kind"], L["ratio"], L.get("topk", 0), L["max_entries"],
                           _p(L["q"]), _p(L.get("q_idx")), _p(L["k_cmp"]), _p(L["v_cmp"]),
                           _p(L.get("k_idx")), _p(L["ent_off"]), _p(L["out"]), _p(L.get("lse")),
-                          _p(L.get("idx")), _p(L.get("count")))
+                          _p(L.get("idx")), _p(L.get("count")), _p(L.get("win_k")),
+                          _p(L.get("win_v")), _p(L.get("win_off")), _p(L.get("win_pos0")),
+                          int(L.get("window", 0)))
     return arr
 
 

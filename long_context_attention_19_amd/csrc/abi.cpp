@@ -339,6 +339,53 @@ int32_t lca_hca_dense_attn(const lca_bf16* q, const lca_bf16* k_cmp, const lca_b
                     "hca_dense_attn launch");
 }
 
+// ------------------------------------------------------------------ sliding window
+static lca::AttnArgs window_args(const lca_bf16* q, const lca_bf16* win_k, const lca_bf16* win_v,
+                                 const int64_t* win_off, const int64_t* win_pos0,
+                                 const int64_t* q_off, const int64_t* q_pos, int32_t max_q,
+                                 int32_t window, int32_t heads, float scale_log2, lca_bf16* out,
+                                 float* lse) {
+  lca::AttnArgs a{};
+  a.q = q;
+  a.kc = win_k;
+  a.vc = win_v;
+  a.ent_off = win_off;
+  a.q_off = q_off;
+  a.q_pos = q_pos;
+  a.max_q = max_q;
+  a.heads = heads;
+  a.splits = 1;
+  a.ratio = 1;
+  a.max_n = window;
+  a.scale_log2 = scale_log2;
+  a.out = out;
+  a.lse = lse;
+  a.win_pos0 = win_pos0;
+  a.window = window;
+  a.merge = 1;
+  return a;
+}
+
+int32_t lca_window_attn(const lca_bf16* q, const lca_bf16* win_k, const lca_bf16* win_v,
+                        const int64_t* win_off, const int64_t* win_pos0, const int64_t* q_off,
+                        const int64_t* q_pos, int32_t batch, int32_t max_q, int32_t window,
+                        int32_t heads, int32_t head_dim, float scale, lca_bf16* out, float* lse,
+                        void* stream) {
+  if (head_dim != 128) return fail(LCA_ERR_UNSUPPORTED, "window_attn: head_dim=%d (only 128)", head_dim);
+  if (!heads_supported(heads)) return fail(LCA_ERR_UNSUPPORTED, "window_attn: heads=%d (16, 32 or a multiple of 64)", heads);
+  if (batch < 0 || max_q < 0 || window < 0) return fail(LCA_ERR_SHAPE, "window_attn: negative size");
+  if (window > lca::ATTN_MAX_SEQ) return fail(LCA_ERR_UNSUPPORTED, "window_attn: window=%d above %d", window, lca::ATTN_MAX_SEQ);
+  if (!std::isfinite(scale)) return fail(LCA_ERR_SHAPE, "window_attn: scale not finite");
+  if ((int64_t)batch * max_q > 65535 * 1024LL) return fail(LCA_ERR_SHAPE, "window_attn: too many rows");
+  if (batch == 0 || max_q == 0 || window == 0) return ok();
+  if (!q || !win_k || !win_v || !win_off || !win_pos0 || !q_off || !q_pos || !out || !lse) return fail(LCA_ERR_NULL, "window_attn: NULL pointer");
+  if (!al16(q) || !al16(win_k) || !al16(win_v) || !al16(out)) return fail(LCA_ERR_ALIGN, "window_attn: q / win_k / win_v / out not 16-byte aligned");
+  const lca::AttnArgs a = window_args(q, win_k, win_v, win_off, win_pos0, q_off, q_pos, max_q,
+                                      window, heads, scale * 1.4426950408889634f, out, lse);
+  return hip_status(lca::launch_attention(lca::attn_batch1(a), batch, (hipStream_t)stream),
+                    "window_attn launch");
+}
+
 // ------------------------------------------------------------------ hybrid step
 size_t lca_hybrid_workspace_bytes(const lca_layer* layers, int32_t n_layers, int32_t batch,
                                   int32_t max_q, int32_t heads) {
@@ -384,6 +431,11 @@ int32_t lca_hybrid_layer_step(const lca_layer* layers, int32_t n_layers, const i
     if (head_dim != 128) return fail(LCA_ERR_UNSUPPORTED, "hybrid_layer_step: head_dim=%d (only 128)", head_dim);
     if (!heads_supported(heads)) return fail(LCA_ERR_UNSUPPORTED, "hybrid_layer_step: heads=%d", heads);
     if (!al16(L.q) || !al16(L.k_cmp) || !al16(L.v_cmp) || !al16(L.out)) return fail(LCA_ERR_ALIGN, "hybrid_layer_step: layer %d tensors not aligned", l);
+    if (L.window < 0 || L.window > lca::ATTN_MAX_SEQ) return fail(LCA_ERR_SHAPE, "hybrid_layer_step: layer %d window=%d", l, L.window);
+    if (L.window > 0) {
+      if (!L.win_k || !L.win_v || !L.win_off || !L.win_pos0 || !L.lse) return fail(LCA_ERR_NULL, "hybrid_layer_step: layer %d window buffers / lse NULL", l);
+      if (!al16(L.win_k) || !al16(L.win_v)) return fail(LCA_ERR_ALIGN, "hybrid_layer_step: layer %d window buffers not aligned", l);
+    }
   }
   if (!std::isfinite(scale)) return fail(LCA_ERR_SHAPE, "hybrid_layer_step: scale not finite");
   const hipStream_t caller = (hipStream_t)stream;
@@ -492,6 +544,22 @@ int32_t lca_hybrid_layer_step(const lca_layer* layers, int32_t n_layers, const i
     for (int i = 0; i < n; ++i) ab.a[i] = all[c0 + i];
     e = plan.persist ? lca::launch_attention_persist(ab, pp, caller)
                      : lca::launch_attention(ab, batch, caller);
+  }
+  // sliding-window branches, merged into each layer's result (one launch per 8 layers)
+  std::vector<lca::AttnArgs> win_a;
+  for (int l = 0; l < n_layers; ++l) {
+    const lca_layer& L = layers[l];
+    if (L.window > 0)
+      win_a.push_back(window_args(L.q, L.win_k, L.win_v, L.win_off, L.win_pos0, q_off, q_pos,
+                                  max_q, L.window, heads, scale_log2, L.out, L.lse));
+  }
+  for (size_t c0 = 0; c0 < win_a.size() && e == hipSuccess; c0 += lca::MAX_BATCH_LAYERS) {
+    const int n = (int)std::min<size_t>(lca::MAX_BATCH_LAYERS, win_a.size() - c0);
+    lca::AttnBatch ab{};
+    ab.n = n;
+    ab.head_blocks = hb;
+    for (int i = 0; i < n; ++i) ab.a[i] = win_a[c0 + i];
+    e = lca::launch_attention(ab, batch, caller);
   }
   mark(4);
   if (e != hipSuccess) return fail(LCA_ERR_HIP, "hybrid_layer_step: %s", hipGetErrorString(e));

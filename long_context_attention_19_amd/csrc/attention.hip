@@ -313,13 +313,23 @@ __global__ __launch_bounds__(AT_NT) void attn_dma_kernel(AttnBatch ab) {
   const int qi = blockIdx.y - b * a.max_q;
   const int64_t r0 = a.q_off[b];
   const int64_t nq = a.q_off[b + 1] - r0;
-  const int64_t e_base = a.ent_off[b];
-  const int64_t n_seq = a.ent_off[b + 1] - e_base;
+  int64_t e_base = a.ent_off[b];
+  int64_t n_seq = a.ent_off[b + 1] - e_base;
   if (qi >= nq) return;
   const int64_t row = r0 + qi;
   const int s = blockIdx.x;
   // the row's entry count: only needed after the first DMAs are issued
-  const int n_raw = sparse ? a.count[row] : (int)min(a.q_pos[row] / a.ratio, (int64_t)INT32_MAX);
+  int n_raw = sparse ? a.count[row] : (int)min(a.q_pos[row] / a.ratio, (int64_t)INT32_MAX);
+  if (MODE == 0 && a.win_pos0 != nullptr) {
+    // sliding window: the buffer's tokens at positions [p - window, p), as buffer
+    // rows [lo, hi); the rows before lo are skipped by moving the sequence base
+    const int64_t p = a.q_pos[row], pos0 = a.win_pos0[b];
+    const int64_t lo = min(max(p - a.window, pos0) - pos0, max(n_seq, (int64_t)0));
+    const int64_t hi = max(min(p, pos0 + n_seq) - pos0, lo);
+    e_base += lo;
+    n_seq -= lo;
+    n_raw = (int)(hi - lo);
+  }
   const int max_n = a.max_n;
   const int splits = a.splits;
   const int kk = a.k;
@@ -502,7 +512,33 @@ __global__ __launch_bounds__(AT_NT) void attn_dma_kernel(AttnBatch ab) {
     l_run = ll;
   }
 
-  if (nsp == 1) {
+  if (nsp == 1 && MODE == 0 && a.merge) {
+    // one softmax over this result and the one already in out / lse: weights
+    // exp(lse - max) of the two normalised outputs
+    const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
+    const float lse_w = l_run > 0.f ? (m_run + log2f(l_run)) * 0.69314718055994530942f : -INFINITY;
+    uint16_t* op = a.out + (row * a.heads + head) * HD;
+    float* lp = a.lse + row * a.heads + head;
+    const float lse_c = *lp;
+    const float mx = fmaxf(lse_c, lse_w);
+    const float wc = mx == -INFINITY ? 0.f : __expf(lse_c - mx);
+    const float ww = mx == -INFINITY ? 0.f : __expf(lse_w - mx);
+    const float den = wc + ww;
+    const float rden = den > 0.f ? 1.f / den : 0.f;
+#pragma unroll
+    for (int db = 0; db < 8; ++db) {
+      const uint2 ck = *reinterpret_cast<const uint2*>(op + db * 16 + 4 * g);
+      const float c0 = bf16_bits_to_f32(ck.x & 0xffffu), c1 = bf16_bits_to_f32(ck.x >> 16);
+      const float c2 = bf16_bits_to_f32(ck.y & 0xffffu), c3 = bf16_bits_to_f32(ck.y >> 16);
+      uint2 pk;
+      pk.x = f32_to_bf16_bits((wc * c0 + ww * o[db][0] * inv) * rden) |
+             (f32_to_bf16_bits((wc * c1 + ww * o[db][1] * inv) * rden) << 16);
+      pk.y = f32_to_bf16_bits((wc * c2 + ww * o[db][2] * inv) * rden) |
+             (f32_to_bf16_bits((wc * c3 + ww * o[db][3] * inv) * rden) << 16);
+      *reinterpret_cast<uint2*>(op + db * 16 + 4 * g) = pk;
+    }
+    if (g == 0) *lp = den > 0.f ? mx + __logf(den) : -INFINITY;
+  } else if (nsp == 1) {
     const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
     uint16_t* op = a.out + (row * a.heads + head) * HD;
 #pragma unroll

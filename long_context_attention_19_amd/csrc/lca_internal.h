@@ -109,6 +109,14 @@ struct AttnArgs {
   float* lse;
   float* part_o;           // [rows][splits][heads][128]
   float2* part_ml;         // [rows][splits][heads]  (running max in log2 units, sum)
+  // Sliding-window form (dense, win_pos0 != nullptr): kc / vc / ent_off describe the
+  // state buffers, whose first rows sit at absolute positions win_pos0[b]; a row at
+  // position p attends the buffer's tokens at positions [p - window, p).  With
+  // merge set, the result is merged by log-sum-exp into the out / lse already there
+  // (the compressed branch's), one softmax over both key sets.  One piece per row.
+  const int64_t* win_pos0;
+  int32_t window;
+  int32_t merge;
 };
 // Layers of one attention launch share heads, splits and max_q.
 struct AttnBatch {

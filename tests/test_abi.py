@@ -30,8 +30,10 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_version_and_struct_layout():
-    assert lca.abi_version() == 1
-    assert ctypes.sizeof(lca.LcaLayer) == 16 + 10 * 8
+    assert lca.abi_version() == 2
+    # 4 int32, 10 pointers, 4 window pointers, int32 window (+4 padding)
+    assert ctypes.sizeof(lca.LcaLayer) == 16 + 10 * 8 + 4 * 8 + 8
+    assert lca.LcaLayer.window.offset == 16 + 14 * 8
 
 
 def L():
@@ -138,3 +140,20 @@ def test_no_oracle_in_product_path():
             if fn.endswith((".py", ".hip", ".cpp", ".h")):
                 src = open(os.path.join(dp, fn)).read()
                 assert "oracle" not in src.replace("the oracle", ""), fn
+
+
+def test_window_attn_validation():
+    f = L().lca_window_attn
+    args = lambda **kw: [kw.get("q", FAKE), kw.get("wk", FAKE), kw.get("wv", FAKE), FAKE, FAKE,
+                         FAKE, FAKE, kw.get("B", 2), kw.get("mq", 1), kw.get("win", 128),
+                         kw.get("H", 64), kw.get("D", 128), ctypes.c_float(0.088),
+                         kw.get("out", FAKE), kw.get("lse", FAKE), None]
+    assert f(*args(win=0, q=None, lse=None)) == OK        # no window: nothing to do
+    assert f(*args(B=0, q=None)) == OK                     # empty batch
+    assert f(*args(D=64)) == E_UNSUP
+    assert f(*args(H=48)) == E_UNSUP
+    assert f(*args(win=-1)) == E_SHAPE
+    assert f(*args(lse=None)) == E_NULL                    # the merge needs the branch's lse
+    assert f(*args(wk=None)) == E_NULL
+    assert f(*args(wv=MIS)) == E_ALIGN
+    assert "aligned" in lca.last_error()

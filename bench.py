@@ -7,7 +7,8 @@ Prints ONE JSON line.  The default workload is the 8-layer hybrid decode stack
 (CSA on even layers, HCA on odd layers; 16 sequences with context lengths drawn
 uniformly from 65,536..1,048,576 tokens; 64 query heads on one KV head); the
 other workloads (csa_decode_8k, hca_decode_128k, csa_decode_1m,
-csa_prefill_256k) can be named with --workload.  A step is one pass of the
+csa_prefill_256k, hybrid_decode_1m_swa: the stack with a 128-token sliding window on
+every layer) can be named with --workload.  A step is one pass of the
 workload's whole path over one batch; inputs are seeded, synthetic and resident
 in HBM before timing starts.  Decode workloads smaller than the 256 MB
 last-level cache rotate input replicas so that each step reads from HBM.
@@ -155,6 +156,9 @@ class HybridRunner(_Capture):
                      lse=torch.empty(B, H, dtype=torch.float32, device=device))
             if d["csa"]:
                 s.update(topk=wl.topk, k_idx=d["k_idx"], q_idx=d["q_idx"])
+            if wl.window:
+                s.update(win_k=d["win_k"], win_v=d["win_v"], win_off=d["win_off_dev"],
+                         win_pos0=d["win_pos0_dev"], window=wl.window)
             specs.append(s)
         self.hs = HybridStep(specs, B, 1, H, device)
         self.q_off = torch.arange(B + 1, dtype=torch.int64, device=device)
@@ -179,6 +183,8 @@ class HybridRunner(_Capture):
             else:
                 tot += int(np.sum(N * 512))
             tot += wl.batch * wl.heads * QO_BYTES_PER_HEAD
+            if wl.window:   # window K/V rows, and the merge's re-read of out and lse
+                tot += int(np.sum(d["win_n"]) * 512) + wl.batch * wl.heads * QO_BYTES_PER_HEAD
         return tot
 
     def dominant_ms(self, reps):
@@ -221,10 +227,22 @@ class HybridRunner(_Capture):
                     Vc = oracle.bf16_bits_to_f64(_bits(d["v_cmp"][s:e]))
                     q = oracle.bf16_bits_to_f64(_bits(d["q"][b]))
                     L = int(self.L[b])
+                    if wl.window:
+                        ws, we = int(d["win_off"][b]), int(d["win_off"][b + 1])
+                        Kw = oracle.bf16_bits_to_f64(_bits(d["win_k"][ws:we]))
+                        Vw = oracle.bf16_bits_to_f64(_bits(d["win_v"][ws:we]))
+                        p0 = int(d["win_pos0"][b])
                     if d["csa"]:
                         kidx, qidx = d["k_idx"][s:e].cpu().numpy(), d["q_idx"][b].cpu().numpy()
-                        fn = lambda: oracle.csa_decode(q, qidx, L, Kc, Vc, kidx, d["ratio"],
-                                                       wl.topk, SCALE)
+                        if wl.window:
+                            fn = lambda: oracle.csa_query_swa(q, qidx, L, Kc, Vc, kidx, d["ratio"],
+                                                              wl.topk, SCALE, Kw, Vw, p0, wl.window)
+                        else:
+                            fn = lambda: oracle.csa_decode(q, qidx, L, Kc, Vc, kidx, d["ratio"],
+                                                           wl.topk, SCALE)
+                    elif wl.window:
+                        fn = lambda: oracle.hca_query_swa(q, L, Kc, Vc, d["ratio"], SCALE, Kw, Vw,
+                                                          p0, wl.window)
                     else:
                         fn = lambda: oracle.hca_decode(q, L, Kc, Vc, d["ratio"], SCALE)
                     mean, sp, r = _timed_reps(fn, per_call)
@@ -550,6 +568,8 @@ def main(argv=None):
         cfg.update(c=wl.c, topk=wl.topk, d_idx=64)
     if wl.new_tokens:
         cfg["new_tokens"] = wl.new_tokens
+    if wl.window:
+        cfg["window"] = wl.window
     line = {
         "metric": METRIC,
         "value": run.tokens_per_step / (ms * 1e-3),

@@ -30,6 +30,7 @@ class Workload:
     n_layers: int = 1
     new_tokens: int = 0    # prefill: query tokens appended after ctx_len
     direct_entries: bool = False   # draw compressed entries directly (no raw tokens)
+    window: int = 0        # sliding-window branch: raw tokens before the query (0: none)
     notes: str = field(default="", compare=False)
 
     @property
@@ -55,6 +56,13 @@ WORKLOADS = {
         name="hybrid_decode_1m", cfg_id=3, kind="hybrid_decode", batch=16, ctx_len=None,
         ctx_range=(65536, 1048576), heads=64, topk=2048, n_layers=8, direct_entries=True,
         notes="compressed entries drawn directly as bf16 N(0, 1/ratio)"),
+    # the same stack with the sliding-window branch (128 raw tokens) on every layer
+    "hybrid_decode_1m_swa": Workload(
+        name="hybrid_decode_1m_swa", cfg_id=3, kind="hybrid_decode", batch=16, ctx_len=None,
+        ctx_range=(65536, 1048576), heads=64, topk=2048, n_layers=8, direct_entries=True,
+        window=128,
+        notes="compressed entries drawn directly as bf16 N(0, 1/ratio); state buffers of the "
+              "last 128 raw tokens drawn as bf16 N(0, 1)"),
     # CSA chunked prefill: 4096 new tokens after a 256K context
     "csa_prefill_256k": Workload(
         name="csa_prefill_256k", cfg_id=4, kind="csa_prefill", batch=1, ctx_len=262144,

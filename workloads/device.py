@@ -54,6 +54,19 @@ def hybrid_inputs(wl: Workload, device="cuda"):
                                                  device)
             d["q_idx"] = gen.device_int8_uniform((B, 64), gen.seed_of(wl.cfg_id, li, gen.T_QIDX),
                                                  device)
+        if wl.window:
+            # state buffer: the last `window` raw tokens of each sequence, N(0,1)
+            nbuf = np.minimum(L, wl.window)
+            boff = offsets(nbuf)
+            d["win_n"] = nbuf
+            d["win_off"] = boff
+            d["win_pos0"] = (L - nbuf).astype(np.int64)
+            d["win_k"] = gen.device_bf16_normal((int(boff[-1]), 128),
+                                                gen.seed_of(wl.cfg_id, li, gen.T_WIN_K), device=device)
+            d["win_v"] = gen.device_bf16_normal((int(boff[-1]), 128),
+                                                gen.seed_of(wl.cfg_id, li, gen.T_WIN_V), device=device)
+            d["win_off_dev"] = torch.tensor(boff, device=device)
+            d["win_pos0_dev"] = torch.tensor(d["win_pos0"], device=device)
         layers.append(d)
     return L, layers
 

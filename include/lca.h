@@ -18,9 +18,10 @@
  * Conventions shared by every call
  *   Memory.   Every tensor pointer is DEVICE memory owned by the caller.  The
  *             library allocates no device memory.  Its only state is a
- *             per-thread error string and, once lca_hybrid_layer_step has run on
- *             a device, 4 internal streams + 5 events for that device (created on
- *             first use, default priority, kept until exit).  Tensors are dense
+ *             per-thread error string and, once lca_hybrid_layer_step or its
+ *             timing calls have run on a device, 5 timing events for that device
+ *             (created on first use, kept until exit).  Every call runs on the
+ *             caller's stream only.  Tensors are dense
  *             and row-major.  bf16 values are
  *             passed as uint16_t bit patterns.  K/V/query rows and indexer rows
  *             must be 16-byte aligned (else LCA_ERR_ALIGN).
@@ -240,9 +241,11 @@ int32_t lca_window_attn(const lca_bf16* q, const lca_bf16* win_k, const lca_bf16
  * calls.  Layers are independent and each has its own workspace region.  All
  * work is enqueued on `stream` in three phases: the CSA layers' scores and their
  * top-k selection (up to 8 layers per launch), then the attention of every
- * layer, CSA and HCA in the same launches (up to 8 layers each).  With L layers
- * the attention uses 32 / min(L, 4) splits per row (decode), a function of the
- * layer count only, so a row's bits still do not depend on the rest of the batch.
+ * layer, CSA and HCA in the same launches (up to 8 layers each), followed by the
+ * sliding-window branch of every layer that has one (window > 0).  The attention
+ * takes a balanced persistent form when the step fits it (64-head blocks, at most
+ * 256 (layer, row) items); otherwise with L layers it uses 32 / min(L, 4) splits
+ * per row, a function of the layer count only.
  * ------------------------------------------------------------------------- */
 enum lca_layer_kind { LCA_LAYER_CSA = 0, LCA_LAYER_HCA = 1 };
 
@@ -279,12 +282,13 @@ int32_t lca_hybrid_layer_step(const lca_layer* layers, int32_t n_layers, const i
 /* ---------------------------------------------------------------------------
  * Phase timing of lca_hybrid_layer_step, for measurement.  While enabled, each
  * hybrid step on the current device records HIP events around its phases on the
- * streams those phases run on (not for use under graph capture).
+ * caller's stream (not for use under graph capture).
  *   lca_hybrid_timing_enable(1 / 0) switches it on / off for the current device.
  *   lca_hybrid_timing_read(ms, n) waits for the last timed step and writes up to
  *   n durations in milliseconds: [0] indexer scores of the first batch of CSA
  *   layers (one launch), [1] their top-k selection, [2] the attention of all
- *   layers with the split combine (0 for a phase the step did not have).
+ *   layers with the split combine and the sliding-window branches (0 for a phase
+ *   the step did not have).
  *   LCA_ERR_SHAPE if no timed step ran since enabling.
  * ------------------------------------------------------------------------- */
 #define LCA_HYBRID_PHASES 3

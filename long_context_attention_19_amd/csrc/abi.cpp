@@ -47,48 +47,39 @@ bool heads_supported(int32_t heads) {
 
 constexpr int kTopkChunk = 4096;
 
-// Internal streams for running independent layers concurrently: created once per
-// device on first use, default priority, non-blocking; never destroyed.
-constexpr int kLayerStreams = 4;
+// Phase-timing events of the hybrid step, created once per device on first use and
+// never destroyed: [0..1] scores, [1..2] top-k, [3..4] attention.
 constexpr int kMaxDevices = 64;
-struct LayerStreams {
-  hipStream_t s[kLayerStreams];
-  hipEvent_t fork;
-  hipEvent_t join[kLayerStreams];
-  // phase timing: [0..1] scores, [1..2] top-k, [3..4] attention
+struct HybridTiming {
   hipEvent_t tev[5];
   bool timing = false;
   bool timed = false;     // a step recorded tev since timing was enabled
   bool has_csa = false;
   bool ready = false;
 };
-std::mutex g_streams_mu;
-LayerStreams g_streams[kMaxDevices];
+std::mutex g_timing_mu;
+HybridTiming g_timing[kMaxDevices];
 
-LayerStreams* layer_streams() {
+HybridTiming* hybrid_timing() {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
-  std::lock_guard<std::mutex> lk(g_streams_mu);
-  LayerStreams& ls = g_streams[dev];
-  if (!ls.ready) {
-    for (int i = 0; i < kLayerStreams; ++i) {
-      if (hipStreamCreateWithFlags(&ls.s[i], hipStreamNonBlocking) != hipSuccess) return nullptr;
-      if (hipEventCreateWithFlags(&ls.join[i], hipEventDisableTiming) != hipSuccess) return nullptr;
-    }
-    if (hipEventCreateWithFlags(&ls.fork, hipEventDisableTiming) != hipSuccess) return nullptr;
+  std::lock_guard<std::mutex> lk(g_timing_mu);
+  HybridTiming& ht = g_timing[dev];
+  if (!ht.ready) {
     for (int i = 0; i < 5; ++i)
-      if (hipEventCreate(&ls.tev[i]) != hipSuccess) return nullptr;
-    ls.ready = true;
+      if (hipEventCreate(&ht.tev[i]) != hipSuccess) return nullptr;
+    ht.ready = true;
   }
-  return &ls;
+  return &ht;
 }
 
-// Split count of the hybrid step's attention: with up to 4 layers in flight at once
-// each layer needs fewer work-groups per row, and fewer splits mean fewer partials.
-// It depends on the layer count and query count only, never on the batch.
+// Split count of the hybrid step's attention (the per-row form): the layers of one
+// launch share the chip, so each row needs fewer work-groups, and fewer splits mean
+// fewer partials.  It depends on the layer and query counts only, never on the batch.
+constexpr int kHybridLayerShare = 4;
 int hybrid_splits(int n_layers, int max_q) {
   const int base = lca::attn_auto_splits(max_q);
-  const int conc = std::min(std::max(n_layers, 1), kLayerStreams);
+  const int conc = std::min(std::max(n_layers, 1), kHybridLayerShare);
   return std::max(1, base / conc);
 }
 
@@ -497,7 +488,7 @@ int32_t lca_hybrid_layer_step(const lca_layer* layers, int32_t n_layers, const i
   // launches of up to 8 layers.  Everything is bound by HBM bandwidth except the
   // selection, and one attention launch for all layers pays the pipeline start and
   // drain once instead of per kind.
-  LayerStreams* ls = layer_streams();
+  HybridTiming* ls = hybrid_timing();
   hipError_t e = hipSuccess;
   const int hb = (heads + 63) / 64;
   const bool timing = ls && ls->timing;
@@ -567,8 +558,8 @@ int32_t lca_hybrid_layer_step(const lca_layer* layers, int32_t n_layers, const i
 }
 
 int32_t lca_hybrid_timing_enable(int32_t enable) {
-  LayerStreams* ls = layer_streams();
-  if (!ls) return fail(LCA_ERR_HIP, "hybrid_timing_enable: no device streams");
+  HybridTiming* ls = hybrid_timing();
+  if (!ls) return fail(LCA_ERR_HIP, "hybrid_timing_enable: no timing events");
   ls->timing = enable != 0;
   ls->timed = false;
   return ok();
@@ -576,8 +567,8 @@ int32_t lca_hybrid_timing_enable(int32_t enable) {
 
 int32_t lca_hybrid_timing_read(float* ms, int32_t n) {
   if (!ms || n < 0) return fail(LCA_ERR_NULL, "hybrid_timing_read: ms NULL");
-  LayerStreams* ls = layer_streams();
-  if (!ls) return fail(LCA_ERR_HIP, "hybrid_timing_read: no device streams");
+  HybridTiming* ls = hybrid_timing();
+  if (!ls) return fail(LCA_ERR_HIP, "hybrid_timing_read: no timing events");
   if (!ls->timing || !ls->timed) return fail(LCA_ERR_SHAPE, "hybrid_timing_read: no timed step");
   float t[LCA_HYBRID_PHASES] = {0.f, 0.f, 0.f};
   const int pairs[LCA_HYBRID_PHASES][2] = {{0, 1}, {1, 2}, {3, 4}};

@@ -7,7 +7,7 @@
 //
 // Decode streams 64 bytes of key per entry and does 16 int8 MACs per 16 bytes,
 // far below the ALU ridge: the kernel is bound by HBM.  Layout of the work:
-//   - a work-group owns 512 to 2048 consecutive entries of one sequence of one layer
+//   - a work-group owns 1024 to 4096 consecutive entries of one sequence of one layer
 //     (grid z = layer: the layers of a hybrid stack are scored in one launch);
 //   - in each round, lane t loads the 16-byte piece (t % 4) of key (t / 4), so a
 //     wave's 128-bit loads cover 1 KiB of contiguous key rows, and IS_ROUNDS
@@ -27,14 +27,15 @@
 namespace lca {
 
 constexpr int IS_NT = 256;
-constexpr int IS_ROUNDS = 8;
-constexpr int IS_KEYS_PER_PASS = IS_NT / 4 * IS_ROUNDS;   // 512
-// Entries per work-group: IS_KEYS_PER_PASS x PASSES (512, 1024 or 2048).  Many rows
-// (IS_SMALL_CHUNK_ROWS and up) take 1024: a finer grain than 2048 evens out the
-// ragged ends of the rows across the chip (512 measured slower again).  With few rows
-// nearly every resident group works on the same few rows, and each flushes its
-// histogram into that row's bins with global atomics: groups then take up to 2048
-// entries, so that a row has at most about IS_GROUPS_PER_ROW of them.
+constexpr int IS_ROUNDS = 16;
+constexpr int IS_KEYS_PER_PASS = IS_NT / 4 * IS_ROUNDS;   // 1024
+// Entries per work-group: IS_KEYS_PER_PASS x PASSES (1024, 2048 or 4096).  Many rows
+// (IS_SMALL_CHUNK_ROWS and up) take one pass of 1024, all 16 loads issued before the
+// first is used: a finer grain than 2048 evens out the ragged ends of the rows across
+// the chip, and 16 loads in flight beat two passes of 8 (512 per group measured slower).
+// With few rows nearly every resident group works on the same few rows, and each
+// flushes its histogram into that row's bins with global atomics: groups then take
+// more entries, so that a row has at most about IS_GROUPS_PER_ROW of them.
 constexpr int IS_SMALL_CHUNK_ROWS = 32;
 constexpr int IS_GROUPS_PER_ROW = 128;
 
@@ -109,12 +110,11 @@ __global__ __launch_bounds__(IS_NT) void index_score_kernel(IndexBatch ib) {
       if (HIST && vis && j < N) atomicAdd(&lh[(v + KEY_BIAS) >> 10], 1);
     }
   }
-  // the group's scores leave at the end, 16 bytes per thread per store, 8 KiB
-  // contiguous; nothing past the sequence's last entry is written
+  // the group's scores leave at the end, 16 bytes per thread per store, 4 KiB
+  // contiguous per store instruction; nothing past the sequence's last entry is written
   __syncthreads();
   {
     const int64_t cnt = min((int64_t)IS_CHUNK, N - base);
-    // 4 scores per thread and store: a 512-entry chunk needs only half the threads
 #pragma unroll
     for (int u = 0; u < (IS_CHUNK + 4 * IS_NT - 1) / (4 * IS_NT); ++u) {
       const int q = 4 * (t + IS_NT * u);
@@ -357,7 +357,7 @@ hipError_t launch_index_score(const IndexBatch& ib, int batch, hipStream_t st) {
       hipLaunchKernelGGL(index_gemm_kernel<false>, grid, dim3(IG_NT), 0, st, ib, tiles, ranges);
     return hipGetLastError();
   }
-  int passes = 2;
+  int passes = 1;
   if ((int64_t)batch * ib.max_q * ib.n < IS_SMALL_CHUNK_ROWS) {
     passes = 1;
     while (passes < 4 && (int64_t)passes * IS_KEYS_PER_PASS * IS_GROUPS_PER_ROW < max_n) passes *= 2;

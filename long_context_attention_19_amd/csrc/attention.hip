@@ -132,8 +132,8 @@ constexpr int AT_IDS = 2048;       // entry ids staged in LDS per chunk (sparse 
 // MODE: 0 dense (HCA), 1 sparse (CSA), 2 either, per layer of the launch
 template <int ST, int NB, int MODE>
 struct AttnDmaSmem {
-  i32x4 k[NB][ST * 16];
-  i32x4 v[NB][ST * 16];
+  alignas(256) i32x4 k[NB][ST * 16];   // 256-byte aligned: attn_stage XORs slot bits
+  alignas(256) i32x4 v[NB][ST * 16];
   int ids[MODE != 0 ? AT_IDS : 1];
 };
 
@@ -182,9 +182,9 @@ __device__ __forceinline__ void lds_barrier() {
 // even 16-lane rows, both without LDS
 __device__ __forceinline__ float lanes4_max(float x) {
   const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  x = __builtin_elementwise_maximum(__uint_as_float(a[0]), __uint_as_float(a[1]));
   const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+  return __builtin_elementwise_maximum(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 __device__ __forceinline__ float lanes4_sum(float x) {
   const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
@@ -193,35 +193,56 @@ __device__ __forceinline__ float lanes4_sum(float x) {
   return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
+// The running max of the online softmax moves only when a block's max exceeds it
+// by more than this (log2 units): until then the weights are taken against the
+// stale max, so they stay below 2^8, and the rescale of O and the sum (32 + 1
+// multiplies per lane) is skipped.  O, the sum and the max stay consistent, so the
+// result and the log-sum-exp are those of the exact max.
+constexpr float AT_MAX_SLACK = 8.f;
+
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
 // One stage of the online softmax attention for the 16 heads of this wave (head
-// l16 of the lane) over its SUB 32-entry sub-tiles starting at stage row el_base,
-// treated as one block of 32*SUB entries: S^T = K Q^T for every sub-tile first
-// (independent MFMA chains), one running-max update and one rescale for the block,
+// l16 of the lane) over its SUB 32-entry sub-tiles starting at stage row el_base
+// (a multiple of 32), treated as one block of 32*SUB entries: S^T = K Q^T for every
+// sub-tile first (independent MFMA chains), one running-max update for the block,
 // then O^T += V^T P^T with the V^T operand read transposed from the stage's V tile.
 // Entries at or past e1 are masked (their rows were fetched but hold repeats; their
 // weights are exactly 0).  The caller guarantees the block's first entry is valid.
 // The running max is kept in scaled log2 units; the exponent is one fma, v_exp_f32
 // without range fix-up (a weight below 2^-126 flushes to 0, as it would in bf16).
+// The lane's share of the sum adds the bf16-rounded weights in pairs (v_dot2 with
+// ones).
+//
+// LDS addresses: both stage buffers start on 256-byte boundaries, so the slot
+// permutation of a row (bits 4..7 of the address) is an XOR on a per-lane base:
+// K fragment ks of row r sits at base_k ^ (ks << 6), V^T fragment db at
+// base_v ^ (db << 5), and the sub-tile / half offsets are instruction immediates.
 template <int SUB>
 __device__ __forceinline__ void attn_stage(const i32x4* kb, const char* vbase, int el_base, int tb,
                                            int e1, const bf16x8 (&qf)[4], f32x4 (&o)[8],
                                            float& m_run, float& l_run, float scale_log2, int l16,
                                            int g) {
+  typedef __attribute__((address_space(3))) const i32x4 lds_i32x4;
+  typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+  // K: row el_base + 32 sub + 16 rb + l16 keeps dims 8(4ks + g) .. in slot (4ks + g) ^ l16
+  const uint32_t base_k = lds_addr(kb) + (uint32_t)(el_base + l16) * 256u + ((uint32_t)(g ^ l16) << 4);
   f32x4 sacc[SUB][2];
 #pragma unroll
   for (int sub = 0; sub < SUB; ++sub)
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb) sacc[sub][rb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int ks = 0; ks < 4; ++ks)
+  for (int ks = 0; ks < 4; ++ks) {
+    const uint32_t ak = base_k ^ ((uint32_t)ks << 6);
 #pragma unroll
     for (int sub = 0; sub < SUB; ++sub)
 #pragma unroll
       for (int rb = 0; rb < 2; ++rb) {
-        const int r = el_base + sub * 32 + rb * 16 + l16;
-        const bf16x8 kf = __builtin_bit_cast(bf16x8, kb[r * 16 + ((4 * ks + g) ^ (r & 15))]);
+        const bf16x8 kf = __builtin_bit_cast(bf16x8, *(lds_i32x4*)(size_t)(ak + (sub * 32 + rb * 16) * 256));
         sacc[sub][rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[ks], sacc[sub][rb], 0, 0, 0);
       }
+  }
   float x[SUB * 8];
 #pragma unroll
   for (int sub = 0; sub < SUB; ++sub)
@@ -241,41 +262,48 @@ __device__ __forceinline__ void attn_stage(const i32x4* kb, const char* vbase, i
   }
   float mx = x[0];
 #pragma unroll
-  for (int i = 1; i < SUB * 8; ++i) mx = fmaxf(mx, x[i]);
+  for (int i = 1; i < SUB * 8; ++i) mx = __builtin_elementwise_maximum(mx, x[i]);
   mx = lanes4_max(mx) * scale_log2;            // scale > 0: max commutes with it
-  const float m_new = fmaxf(m_run, mx);         // finite: the block has a valid entry
-  const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);   // 0 first, 1 if unchanged
+  // finite: the block has a valid entry; true on the first block (m_run = -inf)
+  const bool raise = mx > m_run + AT_MAX_SLACK;
+  if (__any(raise)) {
+    const float m_new = raise ? mx : m_run;
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);   // 0 first, 1 if kept
+#pragma unroll
+    for (int db = 0; db < 8; ++db) o[db] *= alpha;
+    l_run *= alpha;
+    m_run = m_new;
+  }
+  const float m_use = m_run;
   bf16x8 pf[SUB];
-  float psum = 0.f;
 #pragma unroll
   for (int sub = 0; sub < SUB; ++sub)
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const __bf16 pb = (__bf16)__builtin_amdgcn_exp2f(fmaf(x[sub * 8 + i], scale_log2, -m_new));
-      pf[sub][i] = pb;
-      psum += (float)pb;
-    }
-  l_run = l_run * alpha + psum;
-  if (__any(m_new > m_run)) {                 // otherwise every factor is exactly 1
+    for (int i = 0; i < 8; ++i)
+      pf[sub][i] = (__bf16)__builtin_amdgcn_exp2f(fmaf(x[sub * 8 + i], scale_log2, -m_use));
+  const bf16x2 one2 = {(__bf16)1.f, (__bf16)1.f};
+  float psum = l_run;
 #pragma unroll
-    for (int db = 0; db < 8; ++db) o[db] *= alpha;
-  }
-  m_run = m_new;
+  for (int sub = 0; sub < SUB; ++sub)
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      psum = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pf[sub][2 * i], pf[sub][2 * i + 1]}, one2, psum,
+                                             false);
+  l_run = psum;
+  // V: row r = el_base + 32 sub + 16 hh + 4g + (l16 >> 2), r & 7 = (4g + (l16 >> 2)) & 7,
+  // keeps dims 8c .. in slot c ^ 2(r & 7); lane q = l16 & 3 reads dims 16db + 4q .. +3
+  const int r7 = (4 * g + (l16 >> 2)) & 7;
+  const int q = l16 & 3;
+  const uint32_t base_v = lds_addr(vbase) + (uint32_t)(el_base + 4 * g + (l16 >> 2)) * 256u +
+                          ((uint32_t)r7 << 5) + ((uint32_t)(q >> 1) << 4) + (uint32_t)(q & 1) * 8u;
 #pragma unroll
   for (int sub = 0; sub < SUB; ++sub)
 #pragma unroll
     for (int db = 0; db < 8; ++db) {
-      bf16x4 half[2];
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {
-        const int r = el_base + sub * 32 + 16 * hh + 4 * g + (l16 >> 2);
-        const int q = l16 & 3;
-        const int off = r * 256 + (((2 * db + (q >> 1)) ^ ((r & 7) << 1)) << 4) + (q & 1) * 8;
-        half[hh] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-            (__attribute__((address_space(3))) bf16x4*)(vbase + off));
-      }
-      const bf16x8 vf = {half[0][0], half[0][1], half[0][2], half[0][3],
-                         half[1][0], half[1][1], half[1][2], half[1][3]};
+      const uint32_t av = (base_v ^ ((uint32_t)db << 5)) + (uint32_t)sub * 32u * 256u;
+      const bf16x4 h0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(size_t)av);
+      const bf16x4 h1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(size_t)(av + 16 * 256));
+      const bf16x8 vf = {h0[0], h0[1], h0[2], h0[3], h1[0], h1[1], h1[2], h1[3]};
       o[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf[sub], o[db], 0, 0, 0);
     }
 }
@@ -670,8 +698,8 @@ __global__ __launch_bounds__(AT_NT) void attn_persist_kernel(AttnBatch ab, AttnP
   constexpr int ST = ATTN_PS_STAGE, SUB = 2, NU = ST / 16, NB = 2;
   constexpr int MAXW = ATTN_PS_MAX_ITEMS;
   static_assert(MAXW <= AT_NT && ATTN_PS_MAX_RUN * ST <= AT_IDS, "persistent sizes");
-  __shared__ i32x4 s_k[NB][ST * 16];
-  __shared__ i32x4 s_v[NB][ST * 16];
+  __shared__ __attribute__((aligned(256))) i32x4 s_k[NB][ST * 16];   // attn_stage needs 256 B
+  __shared__ __attribute__((aligned(256))) i32x4 s_v[NB][ST * 16];
   __shared__ int s_ids[AT_IDS];
   __shared__ int s_pre[MAXW + 1];
   __shared__ int4 s_item[MAXW];   // entries, first entry of the sequence, sequence size, query row

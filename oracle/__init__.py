@@ -35,11 +35,14 @@ from .csa_hca import (
     attention_union,
     csa_query_swa,
     hca_query_swa,
+    attention_sink,
+    csa_query_sink,
+    hca_query_sink,
 )
 
 __all__ = [
     "bf16_bits_to_f64", "f64_to_bf16_bits", "kv_compress", "n_visible", "index_scores",
     "topk_select", "attention", "csa_query", "hca_query", "csa_decode", "hca_decode",
     "hybrid_decode", "csa_prefill", "window_tokens", "attention_union", "csa_query_swa",
-    "hca_query_swa",
+    "hca_query_swa", "attention_sink", "csa_query_sink", "hca_query_sink",
 ]

@@ -224,6 +224,66 @@ def hca_query_swa(q, pos: int, Kc, Vc, m: int, scale: float, Kw, Vw, pos0: int, 
 
 
 # --------------------------------------------------------------------------------------
+# attention sink
+
+
+def attention_sink(q, K, V, scale: float, sink):
+    """Softmax attention with a sink: one more logit per head that takes part in the
+    normalisation and carries no value.
+
+    PAGE section 3-2 item 2 lists an attention sink among the parts of the CSA /
+    HCA attention without defining it.  Reading: head h has a scalar logit
+    sink[h] (natural-log units, like the scaled q.K logits) that joins the
+    softmax as an extra key with a zero value row:
+        p_j = exp(l_j) / (exp(sink_h) + sum_i exp(l_i)),   o_h = sum_j p_j V_j,
+        lse_h = log(exp(sink_h) + sum_i exp(l_i)).
+    sink[h] = -inf is plain attention.  Returns (o [H, D], lse [H], p [H, n])."""
+    q = np.asarray(q, dtype=np.float64)
+    K = np.asarray(K, dtype=np.float64).reshape(-1, q.shape[-1])
+    V = np.asarray(V, dtype=np.float64).reshape(-1, q.shape[-1])
+    z = np.asarray(sink, dtype=np.float64).reshape(-1)
+    h, n = q.shape[0], K.shape[0]
+    logits = np.concatenate([scale * (q @ K.T), z[:, None]], axis=1)   # the sink is column n
+    m = logits.max(axis=1, keepdims=True)
+    with np.errstate(invalid="ignore"):   # a head whose every logit is -inf
+        w = np.where(np.isneginf(logits), 0.0, np.exp(logits - m))
+    l = w.sum(axis=1, keepdims=True)
+    p = np.divide(w, l, out=np.zeros_like(w), where=l > 0)
+    o = p[:, :n] @ V
+    lse = np.where(l[:, 0] > 0, m[:, 0] + np.log(np.where(l[:, 0] > 0, l[:, 0], 1.0)), -np.inf)
+    return o, lse, p[:, :n]
+
+
+def csa_query_sink(q, q_idx, pos: int, Kc, Vc, k_idx, c: int, topk: int, scale: float, sink,
+                   Kw=None, Vw=None, pos0: int = 0, w: int = 0):
+    """CSA query with a sink, and optionally the sliding-window branch: one softmax
+    over the selected entries, the window's raw tokens and the sink."""
+    n_vis = n_visible(pos, c, Kc.shape[0])
+    idx = topk_select(index_scores(q_idx, k_idx), n_vis, topk)
+    D = np.asarray(q).shape[-1]
+    lo, hi = (0, 0) if Kw is None else window_tokens(pos, w, pos0, np.asarray(Kw).shape[0])
+    Kw_ = np.zeros((0, D)) if Kw is None else np.asarray(Kw, np.float64)[lo:hi]
+    Vw_ = np.zeros((0, D)) if Vw is None else np.asarray(Vw, np.float64)[lo:hi]
+    o, lse, p = attention_sink(q, np.concatenate([np.asarray(Kc, np.float64)[idx], Kw_]),
+                               np.concatenate([np.asarray(Vc, np.float64)[idx], Vw_]), scale, sink)
+    return {"o": o, "lse": lse, "p": p, "idx": idx, "n_vis": n_vis, "window": (lo, hi)}
+
+
+def hca_query_sink(q, pos: int, Kc, Vc, m: int, scale: float, sink, Kw=None, Vw=None,
+                   pos0: int = 0, w: int = 0):
+    """HCA query with a sink, and optionally the sliding-window branch."""
+    n_vis = n_visible(pos, m, Kc.shape[0])
+    D = np.asarray(q).shape[-1]
+    lo, hi = (0, 0) if Kw is None else window_tokens(pos, w, pos0, np.asarray(Kw).shape[0])
+    Kw_ = np.zeros((0, D)) if Kw is None else np.asarray(Kw, np.float64)[lo:hi]
+    Vw_ = np.zeros((0, D)) if Vw is None else np.asarray(Vw, np.float64)[lo:hi]
+    o, lse, p = attention_sink(q, np.concatenate([np.asarray(Kc, np.float64)[:n_vis], Kw_]),
+                               np.concatenate([np.asarray(Vc, np.float64)[:n_vis], Vw_]), scale,
+                               sink)
+    return {"o": o, "lse": lse, "p": p, "n_vis": n_vis, "window": (lo, hi)}
+
+
+# --------------------------------------------------------------------------------------
 # composed steps
 
 

@@ -403,6 +403,39 @@ def test_dense_attn(qmul, splits):
         assert_lse_close(LSE[b], r["lse"], f"row {b}")
 
 
+@pytest.mark.parametrize("profile", ["ramp", "step", "wave"])
+@pytest.mark.parametrize("splits", [0, 5])
+def test_dense_attn_running_max_paths(profile, splits):
+    """Scores that climb through the sequence (the running max is raised many times,
+    and between raises the weights are taken against a max up to 2^8 below the
+    true one), jump once late by far more than that, or oscillate around the raise
+    threshold; heads see different slopes, some falling."""
+    step(f"hca_dense_attn running max {profile} splits={splits}")
+    g = rng(241, len(profile), splits)
+    n, m, heads = 5000, 128, 64
+    e = np.arange(n, dtype=np.float64)
+    s_e = {"ramp": 0.05 * e,
+           "step": np.where(e < 3000, 0.0, 30.0),
+           "wave": 5.0 * np.sin(e / 50.0) + e / 1000.0}[profile]
+    w = g.standard_normal(128)
+    kf = s_e[:, None] * w[None, :] + 0.1 * g.standard_normal((n, 128))
+    Kc = bf16_bits_from_f32(kf.astype(np.float32))
+    Vc = bf16_normal(g, (n, 128))
+    q = bf16_normal(g, (1, heads, 128))
+    q_pos = [n * m + 5]
+    out = torch.empty(1, heads, 128, dtype=torch.bfloat16, device=DEV)
+    lse = torch.empty(1, heads, dtype=torch.float32, device=DEV)
+    ws = lca.workspace(lca.attn_workspace_bytes(1, heads, 1, splits))
+    lca.hca_dense_attn(bf16_dev(q), bf16_dev(Kc), bf16_dev(Vc), i64_dev([0, n]),
+                       i64_dev([0, 1]), i64_dev(q_pos), 1, 1, n, m, SCALE, out, lse, ws=ws,
+                       splits=splits)
+    torch.cuda.synchronize()
+    Kf, Vf, qf = (oracle.bf16_bits_to_f64(x) for x in (Kc, Vc, q))
+    r = oracle.hca_query(qf[0], q_pos[0], Kf, Vf, m, SCALE)
+    assert_attn_close(bf16_vals(out)[0], r["o"], profile)
+    assert_lse_close(lse.cpu().numpy()[0], r["lse"], profile)
+
+
 # ------------------------------------------------------------------ composed steps
 def _csa_batch(cfg, Ns, nq, heads, c, g):
     ent_off, q_off = offsets(Ns), offsets(nq)

@@ -8,7 +8,8 @@ Prints ONE JSON line.  The default workload is the 8-layer hybrid decode stack
 uniformly from 65,536..1,048,576 tokens; 64 query heads on one KV head); the
 other workloads (csa_decode_8k, hca_decode_128k, csa_decode_1m,
 csa_prefill_256k, hybrid_decode_1m_swa: the stack with a 128-token sliding window on
-every layer) can be named with --workload.  A step is one pass of the
+every layer, hybrid_decode_1m_swa_sink: that and a per-head attention sink on every
+layer) can be named with --workload.  A step is one pass of the
 workload's whole path over one batch; inputs are seeded, synthetic and resident
 in HBM before timing starts.  Decode workloads smaller than the 256 MB
 last-level cache rotate input replicas so that each step reads from HBM.
@@ -159,6 +160,8 @@ class HybridRunner(_Capture):
             if wl.window:
                 s.update(win_k=d["win_k"], win_v=d["win_v"], win_off=d["win_off_dev"],
                          win_pos0=d["win_pos0_dev"], window=wl.window)
+            if wl.sink:
+                s.update(sink=d["sink_dev"])
             specs.append(s)
         self.hs = HybridStep(specs, B, 1, H, device)
         self.q_off = torch.arange(B + 1, dtype=torch.int64, device=device)
@@ -185,6 +188,8 @@ class HybridRunner(_Capture):
             tot += wl.batch * wl.heads * QO_BYTES_PER_HEAD
             if wl.window:   # window K/V rows, and the merge's re-read of out and lse
                 tot += int(np.sum(d["win_n"]) * 512) + wl.batch * wl.heads * QO_BYTES_PER_HEAD
+            if wl.sink:     # the sink logits
+                tot += wl.heads * 4
         return tot
 
     def dominant_ms(self, reps):
@@ -232,7 +237,17 @@ class HybridRunner(_Capture):
                         Kw = oracle.bf16_bits_to_f64(_bits(d["win_k"][ws:we]))
                         Vw = oracle.bf16_bits_to_f64(_bits(d["win_v"][ws:we]))
                         p0 = int(d["win_pos0"][b])
-                    if d["csa"]:
+                    if wl.sink:
+                        z = d["sink"].astype(np.float64)
+                        Kw_, Vw_, p0_, w_ = (Kw, Vw, p0, wl.window) if wl.window else (None, None, 0, 0)
+                        if d["csa"]:
+                            kidx, qidx = d["k_idx"][s:e].cpu().numpy(), d["q_idx"][b].cpu().numpy()
+                            fn = lambda: oracle.csa_query_sink(q, qidx, L, Kc, Vc, kidx, d["ratio"],
+                                                               wl.topk, SCALE, z, Kw_, Vw_, p0_, w_)
+                        else:
+                            fn = lambda: oracle.hca_query_sink(q, L, Kc, Vc, d["ratio"], SCALE, z,
+                                                               Kw_, Vw_, p0_, w_)
+                    elif d["csa"]:
                         kidx, qidx = d["k_idx"][s:e].cpu().numpy(), d["q_idx"][b].cpu().numpy()
                         if wl.window:
                             fn = lambda: oracle.csa_query_swa(q, qidx, L, Kc, Vc, kidx, d["ratio"],
@@ -570,6 +585,8 @@ def main(argv=None):
         cfg["new_tokens"] = wl.new_tokens
     if wl.window:
         cfg["window"] = wl.window
+    if wl.sink:
+        cfg["sink"] = "per-head logits on every layer"
     line = {
         "metric": METRIC,
         "value": run.tokens_per_step / (ms * 1e-3),

@@ -59,7 +59,7 @@
 extern "C" {
 #endif
 
-#define LCA_ABI_VERSION 2
+#define LCA_ABI_VERSION 3
 
 enum lca_status {
   LCA_OK = 0,
@@ -234,6 +234,26 @@ int32_t lca_window_attn(const lca_bf16* q, const lca_bf16* win_k, const lca_bf16
                         void* stream);
 
 /* ---------------------------------------------------------------------------
+ * attn_sink — fold an attention sink into a finished attention result, in place.
+ * Page section 3-2 item 2 lists an attention sink among the parts of the CSA / HCA
+ * attention without defining it.  Reading: head h has a scalar logit sink[h]
+ * (natural-log units, like the scaled q.K logits) that joins the softmax
+ * normalisation as one more key with a zero value row:
+ *     p_j = e^(l_j) / (e^(sink_h) + sum_i e^(l_i)),   o_h = sum_j p_j V_j.
+ * Applied to a result (o, lse) of the attention calls (after lca_window_attn when
+ * the window branch is used, so that the sink joins that one softmax once):
+ *     o <- o / (1 + e^(sink_h - lse)),   lse <- log(e^lse + e^(sink_h)).
+ * A row that attended nothing (o = 0, lse = -inf) gets lse = sink_h; sink_h = -inf
+ * leaves the row unchanged.
+ *   out   [rows, heads, head_dim] bf16, in / out.
+ *   lse   [rows, heads] fp32 natural log, in / out (required).
+ *   sink  [heads] fp32 device.
+ *   rows >= 0 query rows (0: nothing to do); head_dim 128.  No workspace.
+ * ------------------------------------------------------------------------- */
+int32_t lca_attn_sink(lca_bf16* out, float* lse, const float* sink, int64_t rows, int32_t heads,
+                      int32_t head_dim, void* stream);
+
+/* ---------------------------------------------------------------------------
  * hybrid_layer_step — a stack of independent attention layers over the same
  * batch, CSA and HCA interleaved (page section 3-2 item 2).  Each layer has its
  * own cache and queries; a CSA layer runs index_score -> topk_select ->
@@ -242,7 +262,9 @@ int32_t lca_window_attn(const lca_bf16* q, const lca_bf16* win_k, const lca_bf16
  * work is enqueued on `stream` in three phases: the CSA layers' scores and their
  * top-k selection (up to 8 layers per launch), then the attention of every
  * layer, CSA and HCA in the same launches (up to 8 layers each), followed by the
- * sliding-window branch of every layer that has one (window > 0).  The attention
+ * sliding-window branch of every layer that has one (window > 0).  A layer's sink
+ * (sink != NULL, as lca_attn_sink) is folded in by the kernel that writes the
+ * layer's final result, after the window branch.  The attention
  * takes a balanced persistent form when the step fits it (64-head blocks, at most
  * 256 (layer, row) items); otherwise with L layers it uses 32 / min(L, 4) splits
  * per row, a function of the layer count only.
@@ -270,6 +292,7 @@ typedef struct lca_layer {
   const int64_t* win_off;  /* [B+1] device */
   const int64_t* win_pos0; /* [B] device: absolute position of each buffer's first row */
   int32_t window;
+  const float* sink;     /* optional [heads] per-head sink logits (NULL: none), as lca_attn_sink */
 } lca_layer;
 
 size_t lca_hybrid_workspace_bytes(const lca_layer* layers, int32_t n_layers, int32_t batch,

@@ -36,7 +36,7 @@ class LcaLayer(ctypes.Structure):
                 ("q", _vp), ("q_idx", _vp), ("k_cmp", _vp), ("v_cmp", _vp), ("k_idx", _vp),
                 ("ent_off", _vp), ("out", _vp), ("lse", _vp), ("idx", _vp), ("count", _vp),
                 ("win_k", _vp), ("win_v", _vp), ("win_off", _vp), ("win_pos0", _vp),
-                ("window", _i32)]
+                ("window", _i32), ("sink", _vp)]
 
 
 _SIGS = {
@@ -51,6 +51,7 @@ _SIGS = {
                                     _vp, _vp, _vp, _vp]),
     "lca_window_attn": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
                                _f32, _vp, _vp, _vp]),
+    "lca_attn_sink": (_i32, [_vp, _vp, _vp, _i64, _i32, _i32, _vp]),
     "lca_csa_topk_workspace_bytes": (_sz, [_i32, _i32, _i32]),
     "lca_csa_topk_select": (_i32, [_vp, _i64, _i32, _i32, _vp, _i32, _vp, _vp, _vp, _sz, _u32,
                                    _vp]),
@@ -155,6 +156,13 @@ def window_attn(q, win_k, win_v, win_off, win_pos0, q_off, q_pos, batch, max_q, 
         max_q, window, q.shape[-2], q.shape[-1], scale, _p(out), _p(lse), _s(stream)))
 
 
+def attn_sink(out, lse, sink, stream=None):
+    """Fold per-head sink logits into a finished result (out [rows, heads, 128], lse
+    [rows, heads]) in place."""
+    _check("lca_attn_sink", _lib.lca_attn_sink(
+        _p(out), _p(lse), _p(sink), out.shape[0], out.shape[-2], out.shape[-1], _s(stream)))
+
+
 def csa_topk_select(scores, rows, max_n, n_vis, k, idx, count, ws, hist_ready=False,
                     stream=None):
     _check("lca_csa_topk_select", _lib.lca_csa_topk_select(
@@ -186,7 +194,7 @@ def make_layers(layers):
                           _p(L.get("k_idx")), _p(L["ent_off"]), _p(L["out"]), _p(L.get("lse")),
                           _p(L.get("idx")), _p(L.get("count")), _p(L.get("win_k")),
                           _p(L.get("win_v")), _p(L.get("win_off")), _p(L.get("win_pos0")),
-                          int(L.get("window", 0)))
+                          int(L.get("window", 0)), _p(L.get("sink")))
     return arr
 
 

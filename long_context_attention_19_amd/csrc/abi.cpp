@@ -377,6 +377,18 @@ int32_t lca_window_attn(const lca_bf16* q, const lca_bf16* win_k, const lca_bf16
                     "window_attn launch");
 }
 
+int32_t lca_attn_sink(lca_bf16* out, float* lse, const float* sink, int64_t rows, int32_t heads,
+                      int32_t head_dim, void* stream) {
+  if (head_dim != 128) return fail(LCA_ERR_UNSUPPORTED, "attn_sink: head_dim=%d (only 128)", head_dim);
+  if (rows < 0 || heads <= 0) return fail(LCA_ERR_SHAPE, "attn_sink: rows=%lld heads=%d", (long long)rows, heads);
+  if (rows * heads > ((int64_t)1 << 27)) return fail(LCA_ERR_SHAPE, "attn_sink: rows x heads above 2^27");
+  if (rows == 0) return ok();
+  if (!out || !lse || !sink) return fail(LCA_ERR_NULL, "attn_sink: NULL pointer");
+  if (!al16(out)) return fail(LCA_ERR_ALIGN, "attn_sink: out not 16-byte aligned");
+  return hip_status(lca::launch_attn_sink(out, lse, sink, rows, heads, (hipStream_t)stream),
+                    "attn_sink launch");
+}
+
 // ------------------------------------------------------------------ hybrid step
 size_t lca_hybrid_workspace_bytes(const lca_layer* layers, int32_t n_layers, int32_t batch,
                                   int32_t max_q, int32_t heads) {
@@ -454,6 +466,7 @@ int32_t lca_hybrid_layer_step(const lca_layer* layers, int32_t n_layers, const i
     a.scale_log2 = scale_log2;
     a.out = L.out;
     a.lse = L.lse;
+    a.sink = L.window > 0 ? nullptr : L.sink;   // else the window branch writes last
     if (L.kind == LCA_LAYER_CSA) {
       const int ld = std::max((L.max_entries + 3) & ~3, 4);
       int32_t* scores = reinterpret_cast<int32_t*>(p);
@@ -540,9 +553,11 @@ int32_t lca_hybrid_layer_step(const lca_layer* layers, int32_t n_layers, const i
   std::vector<lca::AttnArgs> win_a;
   for (int l = 0; l < n_layers; ++l) {
     const lca_layer& L = layers[l];
-    if (L.window > 0)
+    if (L.window > 0) {
       win_a.push_back(window_args(L.q, L.win_k, L.win_v, L.win_off, L.win_pos0, q_off, q_pos,
                                   max_q, L.window, heads, scale_log2, L.out, L.lse));
+      win_a.back().sink = L.sink;
+    }
   }
   for (size_t c0 = 0; c0 < win_a.size() && e == hipSuccess; c0 += lca::MAX_BATCH_LAYERS) {
     const int n = (int)std::min<size_t>(lca::MAX_BATCH_LAYERS, win_a.size() - c0);

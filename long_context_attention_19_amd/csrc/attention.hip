@@ -193,6 +193,21 @@ __device__ __forceinline__ float lanes4_sum(float x) {
   return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
+// Attention sink ("DeepSeek-V4: Towards Highly Efficient Million-Token Context
+// Intelligence Review", section 3-2 item 2 names one; reading: a per-head logit z
+// in the softmax normalisation with a zero value).  Folded into a finished result
+// whose log-sum-exp is lse (natural log): the output is multiplied by the returned
+// 1 / (1 + e^(z - lse)) and lse becomes log(e^lse + e^z).
+__device__ __forceinline__ float sink_fold(float lse, float z, float* lse_out) {
+  const float mx = fmaxf(lse, z);
+  if (mx == -INFINITY) {   // nothing attended and no sink
+    *lse_out = -INFINITY;
+    return 0.f;
+  }
+  *lse_out = mx + log1pf(__expf(-fabsf(lse - z)));
+  return 1.f / (1.f + __expf(z - lse));   // z - lse = +inf gives 0, -inf gives 1
+}
+
 // The running max of the online softmax moves only when a block's max exceeds it
 // by more than this (log2 units): until then the weights are taken against the
 // stale max, so they stay below 2^8, and the rescale of O and the sum (32 + 1
@@ -552,7 +567,9 @@ __global__ __launch_bounds__(AT_NT) void attn_dma_kernel(AttnBatch ab) {
     const float wc = mx == -INFINITY ? 0.f : __expf(lse_c - mx);
     const float ww = mx == -INFINITY ? 0.f : __expf(lse_w - mx);
     const float den = wc + ww;
-    const float rden = den > 0.f ? 1.f / den : 0.f;
+    float rden = den > 0.f ? 1.f / den : 0.f;
+    float lse_new = den > 0.f ? mx + __logf(den) : -INFINITY;
+    if (a.sink) rden *= sink_fold(lse_new, a.sink[head], &lse_new);
 #pragma unroll
     for (int db = 0; db < 8; ++db) {
       const uint2 ck = *reinterpret_cast<const uint2*>(op + db * 16 + 4 * g);
@@ -565,9 +582,11 @@ __global__ __launch_bounds__(AT_NT) void attn_dma_kernel(AttnBatch ab) {
              (f32_to_bf16_bits((wc * c3 + ww * o[db][3] * inv) * rden) << 16);
       *reinterpret_cast<uint2*>(op + db * 16 + 4 * g) = pk;
     }
-    if (g == 0) *lp = den > 0.f ? mx + __logf(den) : -INFINITY;
+    if (g == 0) *lp = lse_new;
   } else if (nsp == 1) {
-    const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
+    float inv = l_run > 0.f ? 1.f / l_run : 0.f;
+    float lse_v = l_run > 0.f ? (m_run + log2f(l_run)) * 0.69314718055994530942f : -INFINITY;
+    if (a.sink) inv *= sink_fold(lse_v, a.sink[head], &lse_v);
     uint16_t* op = a.out + (row * a.heads + head) * HD;
 #pragma unroll
     for (int db = 0; db < 8; ++db) {
@@ -576,9 +595,7 @@ __global__ __launch_bounds__(AT_NT) void attn_dma_kernel(AttnBatch ab) {
       pk.y = f32_to_bf16_bits(o[db][2] * inv) | (f32_to_bf16_bits(o[db][3] * inv) << 16);
       *reinterpret_cast<uint2*>(op + db * 16 + 4 * g) = pk;
     }
-    if (a.lse && g == 0)
-      a.lse[row * a.heads + head] =
-          l_run > 0.f ? (m_run + log2f(l_run)) * 0.69314718055994530942f : -INFINITY;
+    if (a.lse && g == 0) a.lse[row * a.heads + head] = lse_v;
   } else {
     const int64_t slot = (row * a.splits + s) * a.heads + head;
     float* pp = a.part_o + slot * HD;
@@ -656,12 +673,14 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnBatch ab, int sta
     lt += o[1] * f;
     at += f32x4{o[2], o[3], o[4], o[5]} * f;
   }
-  const float inv = 1.f / lt;
+  float inv = 1.f / lt;
+  float lse_v = (mt + log2f(lt)) * 0.69314718055994530942f;
+  if (a.sink) inv *= sink_fold(lse_v, a.sink[head], &lse_v);
   uint2 pk;
   pk.x = f32_to_bf16_bits(at[0] * inv) | (f32_to_bf16_bits(at[1] * inv) << 16);
   pk.y = f32_to_bf16_bits(at[2] * inv) | (f32_to_bf16_bits(at[3] * inv) << 16);
   *reinterpret_cast<uint2*>(a.out + (ri.row * a.heads + head) * HD + dg * 4) = pk;
-  if (a.lse && dg == 0) a.lse[ri.row * a.heads + head] = (mt + log2f(lt)) * 0.69314718055994530942f;
+  if (a.lse && dg == 0) a.lse[ri.row * a.heads + head] = lse_v;
 }
 
 // ---------------------------------------------------------------------------------
@@ -829,7 +848,9 @@ __global__ __launch_bounds__(AT_NT) void attn_persist_kernel(AttnBatch ab, AttnP
     const int head = (item % HB) * 64 + hl;
     const int64_t row = s_item[item].w;
     if (s_pre[item] >= s0 && s_pre[item + 1] <= s1) {
-      const float inv = l > 0.f ? 1.f / l : 0.f;
+      float inv = l > 0.f ? 1.f / l : 0.f;
+      float lse_v = l > 0.f ? (m_run + log2f(l)) * 0.69314718055994530942f : -INFINITY;
+      if (a.sink) inv *= sink_fold(lse_v, a.sink[head], &lse_v);
       uint16_t* op = a.out + (row * a.heads + head) * HD;
 #pragma unroll
       for (int db = 0; db < 8; ++db) {
@@ -838,8 +859,7 @@ __global__ __launch_bounds__(AT_NT) void attn_persist_kernel(AttnBatch ab, AttnP
         pk.y = f32_to_bf16_bits(o[db][2] * inv) | (f32_to_bf16_bits(o[db][3] * inv) << 16);
         *reinterpret_cast<uint2*>(op + db * 16 + 4 * g) = pk;
       }
-      if (a.lse && g == 0)
-        a.lse[row * a.heads + head] = l > 0.f ? (m_run + log2f(l)) * 0.69314718055994530942f : -INFINITY;
+      if (a.lse && g == 0) a.lse[row * a.heads + head] = lse_v;
     } else {
       const int64_t slot = 2 * (int64_t)gid + (nseg > 1 ? 1 : 0);
       float* pp_o = pp.part_o + (slot * 64 + hl) * HD;
@@ -973,13 +993,48 @@ __global__ __launch_bounds__(256) void attn_persist_combine_kernel(AttnBatch ab,
     mm = mb;
   }
   const int64_t row = plan[W + 1 + item];
-  const float inv = ll > 0.f ? 1.f / ll : 0.f;
+  float inv = ll > 0.f ? 1.f / ll : 0.f;
+  float lse_v = ll > 0.f ? (mm + log2f(ll)) * 0.69314718055994530942f : -INFINITY;
+  if (a.sink) inv *= sink_fold(lse_v, a.sink[head], &lse_v);
   uint2 pk;
   pk.x = f32_to_bf16_bits(acc[0] * inv) | (f32_to_bf16_bits(acc[1] * inv) << 16);
   pk.y = f32_to_bf16_bits(acc[2] * inv) | (f32_to_bf16_bits(acc[3] * inv) << 16);
   *reinterpret_cast<uint2*>(a.out + (row * a.heads + head) * HD + dg * 4) = pk;
-  if (a.lse && dg == 0)
-    a.lse[row * a.heads + head] = ll > 0.f ? (mm + log2f(ll)) * 0.69314718055994530942f : -INFINITY;
+  if (a.lse && dg == 0) a.lse[row * a.heads + head] = lse_v;
+}
+
+// lca_attn_sink: the sink folded into a finished result, in place.  A thread takes
+// 8 dims of one (row, head); 16 threads per (row, head).
+__global__ __launch_bounds__(256) void attn_sink_kernel(uint16_t* __restrict__ out,
+                                                        float* __restrict__ lse,
+                                                        const float* __restrict__ sink,
+                                                        int64_t rows, int heads) {
+  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t rh = t >> 4;   // (row, head)
+  if (rh >= rows * heads) return;
+  const int head = (int)(rh % heads);
+  float lse_v;
+  const float f = sink_fold(lse[rh], sink[head], &lse_v);
+  uint4* op = reinterpret_cast<uint4*>(out + rh * HD) + (t & 15);
+  const uint4 v = *op;
+  uint4 r;
+  r.x = f32_to_bf16_bits(bf16_bits_to_f32(v.x & 0xffffu) * f) | (f32_to_bf16_bits(bf16_bits_to_f32(v.x >> 16) * f) << 16);
+  r.y = f32_to_bf16_bits(bf16_bits_to_f32(v.y & 0xffffu) * f) | (f32_to_bf16_bits(bf16_bits_to_f32(v.y >> 16) * f) << 16);
+  r.z = f32_to_bf16_bits(bf16_bits_to_f32(v.z & 0xffffu) * f) | (f32_to_bf16_bits(bf16_bits_to_f32(v.z >> 16) * f) << 16);
+  r.w = f32_to_bf16_bits(bf16_bits_to_f32(v.w & 0xffffu) * f) | (f32_to_bf16_bits(bf16_bits_to_f32(v.w >> 16) * f) << 16);
+  *op = r;
+  // every thread of the (row, head) read lse before any writes it: the 16 threads sit
+  // in one wave (t & 15 spans an aligned group of 16 lanes)
+  if ((t & 15) == 0) lse[rh] = lse_v;
+}
+
+hipError_t launch_attn_sink(uint16_t* out, float* lse, const float* sink, int64_t rows, int heads,
+                            hipStream_t st) {
+  const int64_t threads = rows * heads * 16;
+  if (threads == 0) return hipSuccess;
+  hipLaunchKernelGGL(attn_sink_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, st,
+                     out, lse, sink, rows, heads);
+  return hipGetLastError();
 }
 
 size_t attn_persist_ws_bytes(int G, int items) {

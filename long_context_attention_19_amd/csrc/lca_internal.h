@@ -117,8 +117,13 @@ struct AttnArgs {
   const int64_t* win_pos0;
   int32_t window;
   int32_t merge;
+  // Attention sink: per-head logits (natural log) folded into the final result by
+  // whichever kernel writes it; nullptr: none.
+  const float* sink;
 };
 // Layers of one attention launch share heads, splits and max_q.
+hipError_t launch_attn_sink(uint16_t* out, float* lse, const float* sink, int64_t rows, int heads,
+                            hipStream_t st);
 struct AttnBatch {
   int32_t n;
   int32_t head_blocks;     // ceil(heads / 64)

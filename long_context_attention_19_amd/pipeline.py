@@ -84,8 +84,8 @@ class HcaStep:
 class HybridStep:
     """layers: dicts with kind, ratio, topk, max_entries and the layer's tensors
     (q, q_idx, k_cmp, v_cmp, k_idx, ent_off, out, lse), optionally a sliding window
-    (win_k, win_v, win_off, win_pos0, window); idx/count for CSA layers are allocated
-    here when absent."""
+    (win_k, win_v, win_off, win_pos0, window) and per-head sink logits (sink); idx / count
+    of CSA layers are allocated here when absent."""
 
     def __init__(self, layers, batch, max_q, heads, device="cuda"):
         rows = batch * max_q

@@ -30,10 +30,11 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_version_and_struct_layout():
-    assert lca.abi_version() == 2
-    # 4 int32, 10 pointers, 4 window pointers, int32 window (+4 padding)
-    assert ctypes.sizeof(lca.LcaLayer) == 16 + 10 * 8 + 4 * 8 + 8
+    assert lca.abi_version() == 3
+    # 4 int32, 10 pointers, 4 window pointers, int32 window (+4 padding), sink pointer
+    assert ctypes.sizeof(lca.LcaLayer) == 16 + 10 * 8 + 4 * 8 + 8 + 8
     assert lca.LcaLayer.window.offset == 16 + 14 * 8
+    assert lca.LcaLayer.sink.offset == 16 + 14 * 8 + 8
 
 
 def L():
@@ -156,4 +157,19 @@ def test_window_attn_validation():
     assert f(*args(lse=None)) == E_NULL                    # the merge needs the branch's lse
     assert f(*args(wk=None)) == E_NULL
     assert f(*args(wv=MIS)) == E_ALIGN
+    assert "aligned" in lca.last_error()
+
+
+def test_attn_sink_validation():
+    f = L().lca_attn_sink
+    args = lambda **kw: [kw.get("out", FAKE), kw.get("lse", FAKE), kw.get("sink", FAKE),
+                         ctypes.c_int64(kw.get("rows", 4)), kw.get("H", 64), kw.get("D", 128), None]
+    assert f(*args(rows=0, out=None)) == OK               # nothing to do
+    assert f(*args(D=64)) == E_UNSUP
+    assert f(*args(rows=-1)) == E_SHAPE
+    assert f(*args(H=0)) == E_SHAPE
+    assert f(*args(rows=1 << 22, H=64)) == E_SHAPE        # rows x heads above 2^27
+    assert f(*args(lse=None)) == E_NULL
+    assert f(*args(sink=None)) == E_NULL
+    assert f(*args(out=MIS)) == E_ALIGN
     assert "aligned" in lca.last_error()

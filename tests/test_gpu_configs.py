@@ -163,6 +163,35 @@ def test_hybrid_swa_full():
             assert_lse_close(lse[b], ref["lse"], f"layer {li} seq {b}")
 
 
+def test_hybrid_swa_sink_full():
+    """The full-size stack with the window branch and a per-head sink on every layer,
+    on a sample of sequences against the oracle's one softmax over the selected (or
+    all) compressed entries, the window's tokens and the sink."""
+    step("full-size hybrid_decode_1m_swa_sink")
+    wl = workloads.get("hybrid_decode_1m_swa_sink")
+    run = bench.HybridRunner(wl)
+    run.step(0)
+    torch.cuda.synchronize()
+    for li, (d, spec) in enumerate(zip(run.layers, run.outputs)):
+        out, lse = _f64(spec["out"]), spec["lse"].cpu().numpy()
+        z = d["sink"].astype(np.float64)
+        for b in (0, 9, wl.batch - 1):
+            s, e = int(d["ent_off"][b]), int(d["ent_off"][b + 1])
+            ws, we = int(d["win_off"][b]), int(d["win_off"][b + 1])
+            Kw, Vw = _f64(d["win_k"][ws:we]), _f64(d["win_v"][ws:we])
+            q, L, p0 = _f64(d["q"][b]), int(run.L[b]), int(d["win_pos0"][b])
+            if d["csa"]:
+                ref = oracle.csa_query_sink(q, d["q_idx"][b].cpu().numpy(), L,
+                                            _f64(d["k_cmp"][s:e]), _f64(d["v_cmp"][s:e]),
+                                            d["k_idx"][s:e].cpu().numpy(), d["ratio"], wl.topk,
+                                            SCALE, z, Kw, Vw, p0, wl.window)
+            else:
+                ref = oracle.hca_query_sink(q, L, _f64(d["k_cmp"][s:e]), _f64(d["v_cmp"][s:e]),
+                                            d["ratio"], SCALE, z, Kw, Vw, p0, wl.window)
+            assert_attn_close(out[b], ref["o"], f"layer {li} seq {b}")
+            assert_lse_close(lse[b], ref["lse"], f"layer {li} seq {b}")
+
+
 def test_prefill_full():
     step("full-size csa_prefill_256k")
     wl = workloads.get("csa_prefill_256k")

@@ -1,0 +1,170 @@
+"""GPU parity of the attention sink: lca_attn_sink on a finished result, and the sink
+folded in by the hybrid step's final writers (persistent attention and its combine,
+the per-row attention and its combine, the window branch's merge), against the
+oracle's softmax with one extra per-head logit and a zero value."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import long_context_attention_19_amd as lca
+import oracle
+from long_context_attention_19_amd.pipeline import CsaStep, HybridStep
+from workloads import bf16_normal, int8_uniform, rng
+
+from gpu_util import (DEV, assert_attn_close, assert_lse_close, bf16_dev, bf16_vals, i64_dev,
+                      i8_dev, offsets, step)
+
+pytestmark = pytest.mark.gpu
+SCALE = 1.0 / math.sqrt(128)
+W = 128
+
+
+def _sinks(g, heads):
+    """Ordinary logits, one of -inf (no sink), one far above every score, one far below."""
+    z = g.standard_normal(heads) * 2.0
+    z[0], z[1], z[2] = -np.inf, 40.0, -40.0
+    return z.astype(np.float32)
+
+
+@pytest.mark.parametrize("heads", [16, 64])
+def test_attn_sink_after_dense_attn(heads):
+    step(f"attn_sink after hca_dense_attn heads={heads}")
+    g = rng(310, heads, 0)
+    Ns, m = [0, 1, 700, 5000], 128
+    B = len(Ns)
+    ent_off = offsets(Ns)
+    tot = max(1, int(ent_off[-1]))
+    Kc, Vc = bf16_normal(g, (tot, 128)), bf16_normal(g, (tot, 128))
+    q = bf16_normal(g, (B, heads, 128), std=2.0)
+    z = _sinks(g, heads)
+    q_pos = [n * m + 3 for n in Ns]
+    out = torch.empty(B, heads, 128, dtype=torch.bfloat16, device=DEV)
+    lse = torch.empty(B, heads, dtype=torch.float32, device=DEV)
+    ws = lca.workspace(lca.attn_workspace_bytes(B, heads, 1, 0))
+    lca.hca_dense_attn(bf16_dev(q), bf16_dev(Kc), bf16_dev(Vc), i64_dev(ent_off),
+                       i64_dev(np.arange(B + 1)), i64_dev(q_pos), B, 1, max(Ns), m, SCALE, out,
+                       lse, ws=ws)
+    lca.attn_sink(out, lse, torch.from_numpy(z).to(DEV))
+    torch.cuda.synchronize()
+    O, LSE = bf16_vals(out), lse.cpu().numpy()
+    Kf, Vf, qf = (oracle.bf16_bits_to_f64(x) for x in (Kc, Vc, q))
+    for b in range(B):
+        sl = slice(ent_off[b], ent_off[b + 1])
+        r = oracle.hca_query_sink(qf[b], q_pos[b], Kf[sl], Vf[sl], m, SCALE, z.astype(np.float64))
+        assert_attn_close(O[b], r["o"], f"seq {b}")
+        assert_lse_close(LSE[b], r["lse"], f"seq {b}")
+    assert np.array_equal(O[0], np.zeros((heads, 128)))          # nothing attended
+    assert np.array_equal(LSE[0, 3:], z[3:]) and LSE[0, 0] == -np.inf
+
+
+def test_attn_sink_after_csa_prefill_and_window():
+    """Prefill-shaped CSA rows with the window branch, then the sink: one softmax over
+    the selected entries, the window's tokens and the sink."""
+    step("attn_sink after CsaStep + window_attn (prefill rows)")
+    g = rng(311, 0, 0)
+    ctx, nq, c, k, heads = 4000, 40, 4, 256, 64
+    N = (ctx + nq) // c
+    Kc, Vc = bf16_normal(g, (N, 128), std=0.5), bf16_normal(g, (N, 128), std=0.5)
+    kidx, qidx = int8_uniform(g, (N, 64)), int8_uniform(g, (nq, 64))
+    q = bf16_normal(g, (nq, heads, 128))
+    pos0, nbuf = ctx - W, W + nq
+    wk, wv = bf16_normal(g, (nbuf, 128)), bf16_normal(g, (nbuf, 128))
+    z = _sinks(g, heads)
+    out = torch.empty(nq, heads, 128, dtype=torch.bfloat16, device=DEV)
+    lse = torch.empty(nq, heads, dtype=torch.float32, device=DEV)
+    q_off, q_pos = i64_dev([0, nq]), i64_dev(np.arange(ctx, ctx + nq))
+    st = CsaStep(1, nq, N, heads, k, c, DEV)
+    st.run(bf16_dev(q), i8_dev(qidx), q_off, q_pos, i8_dev(kidx), bf16_dev(Kc), bf16_dev(Vc),
+           i64_dev([0, N]), SCALE, out, lse)
+    lca.window_attn(bf16_dev(q), bf16_dev(wk), bf16_dev(wv), i64_dev([0, nbuf]), i64_dev([pos0]),
+                    q_off, q_pos, 1, nq, W, SCALE, out, lse)
+    lca.attn_sink(out, lse, torch.from_numpy(z).to(DEV))
+    torch.cuda.synchronize()
+    O, LSE = bf16_vals(out), lse.cpu().numpy()
+    Kf, Vf, qf = (oracle.bf16_bits_to_f64(x) for x in (Kc, Vc, q))
+    wkf, wvf = oracle.bf16_bits_to_f64(wk), oracle.bf16_bits_to_f64(wv)
+    for i in range(nq):
+        r = oracle.csa_query_sink(qf[i], qidx[i], ctx + i, Kf, Vf, kidx, c, k, SCALE,
+                                  z.astype(np.float64), wkf, wvf, pos0, W)
+        assert_attn_close(O[i], r["o"], f"row {i}")
+        assert_lse_close(LSE[i], r["lse"], f"row {i}")
+
+
+def _hybrid_case(g, L, heads, n_layers, windows, sinks_on):
+    B = len(L)
+    nbuf = [min(x, W + 16) for x in L]
+    pos0 = [x - n for x, n in zip(L, nbuf)]
+    boff = offsets(nbuf)
+    layers, refs = [], []
+    for li in range(n_layers):
+        csa = li % 2 == 0
+        ratio = 4 if csa else 128
+        Ns = [x // ratio for x in L]
+        ent_off = offsets(Ns)
+        tot = max(1, int(ent_off[-1]))
+        Kc = bf16_normal(g, (tot, 128), std=1 / math.sqrt(ratio))
+        Vc = bf16_normal(g, (tot, 128), std=1 / math.sqrt(ratio))
+        q = bf16_normal(g, (B, heads, 128))
+        wk = bf16_normal(g, (max(1, int(boff[-1])), 128))
+        wv = bf16_normal(g, (max(1, int(boff[-1])), 128))
+        window = windows[li % len(windows)]
+        z = _sinks(g, heads) if sinks_on[li % len(sinks_on)] else None
+        Ld = dict(kind=lca.LCA_LAYER_CSA if csa else lca.LCA_LAYER_HCA, ratio=ratio,
+                  max_entries=max(Ns), q=bf16_dev(q), k_cmp=bf16_dev(Kc), v_cmp=bf16_dev(Vc),
+                  ent_off=i64_dev(ent_off),
+                  out=torch.empty(B, heads, 128, dtype=torch.bfloat16, device=DEV),
+                  lse=torch.empty(B, heads, dtype=torch.float32, device=DEV),
+                  win_k=bf16_dev(wk), win_v=bf16_dev(wv), win_off=i64_dev(boff),
+                  win_pos0=i64_dev(pos0), window=window,
+                  sink=None if z is None else torch.from_numpy(z).to(DEV))
+        host = dict(q=q, Kc=Kc, Vc=Vc, ent_off=ent_off, wk=wk, wv=wv, window=window, z=z)
+        if csa:
+            host["k_idx"] = int8_uniform(g, (tot, 64))
+            host["q_idx"] = int8_uniform(g, (B, 64))
+            Ld.update(topk=2048, k_idx=i8_dev(host["k_idx"]), q_idx=i8_dev(host["q_idx"]))
+        layers.append(Ld)
+        refs.append(host)
+    hs = HybridStep(layers, B, 1, heads)
+    hs.run(i64_dev(np.arange(B + 1)), i64_dev(L), SCALE)
+    torch.cuda.synchronize()
+    for li, (Ld, host) in enumerate(zip(hs.layers, refs)):
+        O, LSE = bf16_vals(Ld["out"]), Ld["lse"].cpu().numpy()
+        Kf, Vf, qf = (oracle.bf16_bits_to_f64(host[x]) for x in ("Kc", "Vc", "q"))
+        wkf, wvf = oracle.bf16_bits_to_f64(host["wk"]), oracle.bf16_bits_to_f64(host["wv"])
+        z = np.full(heads, -np.inf) if host["z"] is None else host["z"].astype(np.float64)
+        for b in range(B):
+            sl, ws = slice(host["ent_off"][b], host["ent_off"][b + 1]), slice(boff[b], boff[b + 1])
+            if li % 2 == 0:
+                r = oracle.csa_query_sink(qf[b], host["q_idx"][b], L[b], Kf[sl], Vf[sl],
+                                          host["k_idx"][sl], 4, 2048, SCALE, z, wkf[ws], wvf[ws],
+                                          pos0[b], host["window"])
+            else:
+                r = oracle.hca_query_sink(qf[b], L[b], Kf[sl], Vf[sl], 128, SCALE, z, wkf[ws],
+                                          wvf[ws], pos0[b], host["window"])
+            assert_attn_close(O[b], r["o"], f"layer {li} seq {b}")
+            assert_lse_close(LSE[b], r["lse"], f"layer {li} seq {b}")
+
+
+def test_hybrid_sinks_persistent_split_items():
+    """64 heads, few long rows: every item is split between work-groups, so the
+    persistent combine writes the results (window on some layers, one layer without sink)."""
+    step("HybridStep sinks, persistent form, split items")
+    _hybrid_case(rng(312, 0, 0), [4000, 65537, 1000 * 128 + 77], 64, 4, [0, 0, W, 0],
+                 [True, True, True, False])
+
+
+def test_hybrid_sinks_persistent_whole_items():
+    """Many short rows: most items lie inside one work-group's run and are written
+    there; some rows see nothing but their window or nothing at all."""
+    step("HybridStep sinks, persistent form, whole items")
+    g = rng(313, 0, 0)
+    L = list(g.integers(0, 700, size=30)) + [2, 0]
+    _hybrid_case(g, [int(x) for x in L], 64, 8, [0, W], [True])
+
+
+def test_hybrid_sinks_per_row_form():
+    """16 heads: the per-row attention and its split combine write the results."""
+    step("HybridStep sinks, per-row form")
+    _hybrid_case(rng(314, 0, 0), [4000, 65537, 300], 16, 4, [0, W], [True, True, False, True])

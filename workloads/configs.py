@@ -31,6 +31,7 @@ class Workload:
     new_tokens: int = 0    # prefill: query tokens appended after ctx_len
     direct_entries: bool = False   # draw compressed entries directly (no raw tokens)
     window: int = 0        # sliding-window branch: raw tokens before the query (0: none)
+    sink: bool = False     # per-head attention-sink logits on every layer
     notes: str = field(default="", compare=False)
 
     @property
@@ -63,6 +64,14 @@ WORKLOADS = {
         window=128,
         notes="compressed entries drawn directly as bf16 N(0, 1/ratio); state buffers of the "
               "last 128 raw tokens drawn as bf16 N(0, 1)"),
+    # the same stack with the window branch and an attention sink on every layer: the
+    # attention as the method lists it (compressed entries, window, sink)
+    "hybrid_decode_1m_swa_sink": Workload(
+        name="hybrid_decode_1m_swa_sink", cfg_id=3, kind="hybrid_decode", batch=16, ctx_len=None,
+        ctx_range=(65536, 1048576), heads=64, topk=2048, n_layers=8, direct_entries=True,
+        window=128, sink=True,
+        notes="compressed entries drawn directly as bf16 N(0, 1/ratio); state buffers of the "
+              "last 128 raw tokens drawn as bf16 N(0, 1); sink logits fp32 N(0, 1) per head"),
     # CSA chunked prefill: 4096 new tokens after a 256K context
     "csa_prefill_256k": Workload(
         name="csa_prefill_256k", cfg_id=4, kind="csa_prefill", batch=1, ctx_len=262144,

@@ -67,6 +67,9 @@ def hybrid_inputs(wl: Workload, device="cuda"):
                                                 gen.seed_of(wl.cfg_id, li, gen.T_WIN_V), device=device)
             d["win_off_dev"] = torch.tensor(boff, device=device)
             d["win_pos0_dev"] = torch.tensor(d["win_pos0"], device=device)
+        if wl.sink:   # per-head sink logits, fp32 N(0, 1)
+            d["sink"] = gen.rng(wl.cfg_id, li, gen.T_SINK).standard_normal(H).astype(np.float32)
+            d["sink_dev"] = torch.from_numpy(d["sink"]).to(device)
         layers.append(d)
     return L, layers
 

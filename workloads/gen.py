@@ -19,6 +19,7 @@ import numpy as np
 
 T_RAW_K, T_RAW_V, T_KIDX, T_Q, T_QIDX, T_LEN, T_CMP_K, T_CMP_V, T_NEW_K, T_NEW_V = range(10)
 T_WIN_K, T_WIN_V = 10, 11   # sliding-window state buffers (raw tokens)
+T_SINK = 12                  # per-head attention-sink logits
 
 
 def seed_of(cfg_id: int, layer: int, tensor_id: int, replica: int = 0) -> int:

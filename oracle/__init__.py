@@ -38,6 +38,10 @@ from .csa_hca import (
     attention_sink,
     csa_query_sink,
     hca_query_sink,
+    fp4_values,
+    fp4_unpack,
+    index_scores_fp4,
+    csa_query_fp4,
 )
 
 __all__ = [
@@ -45,4 +49,5 @@ __all__ = [
     "topk_select", "attention", "csa_query", "hca_query", "csa_decode", "hca_decode",
     "hybrid_decode", "csa_prefill", "window_tokens", "attention_union", "csa_query_swa",
     "hca_query_swa", "attention_sink", "csa_query_sink", "hca_query_sink",
+    "fp4_values", "fp4_unpack", "index_scores_fp4", "csa_query_fp4",
 ]

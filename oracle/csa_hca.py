@@ -101,6 +101,46 @@ def index_scores(q_idx, k_idx) -> np.ndarray:
     return k @ q
 
 
+def fp4_values(codes) -> np.ndarray:
+    """Values of FP4 E2M1 codes (OCP Microscaling formats, E2M1 element type): bit 3
+    is the sign, bits 2..1 the exponent with bias 1, bit 0 the mantissa; exponent
+    field 0 is subnormal (m * 2^-1), otherwise (1 + m/2) * 2^(e - 1)."""
+    c = np.asarray(codes).astype(np.int64) & 15
+    sign, e, m = c >> 3, (c >> 1) & 3, c & 1
+    mag = np.where(e == 0, 0.5 * m, (1.0 + 0.5 * m) * np.exp2(e - 1.0))
+    return np.where(sign == 1, -mag, mag)
+
+
+def fp4_unpack(packed) -> np.ndarray:
+    """Packed FP4 [..., n/2] bytes -> codes [..., n]: element 2i sits in the low
+    nibble of byte i, element 2i + 1 in the high nibble."""
+    b = np.asarray(packed, dtype=np.uint8).astype(np.int64)
+    return np.stack([b & 15, b >> 4], axis=-1).reshape(*b.shape[:-1], 2 * b.shape[-1])
+
+
+def index_scores_fp4(q_fp4, k_fp4) -> np.ndarray:
+    """FP4 indexer scores: J_j = 4 * sum_d q[d] * k[j, d] over E2M1 values, exactly.
+
+    PAGE section 3-2 item 4: the CSA indexer's Q.K path is trained with FP4
+    quantisation-aware training.  Reading: query and keys are E2M1 codes (d_idx = 64,
+    32 packed bytes per vector) with one power-of-two scale per tensor; a positive
+    common factor cannot change the ranking, so the score is the dot product of the
+    code values, reported x4 (every product is a multiple of 1/4, so J is an exact
+    integer, |J| <= 64 * 6 * 6 * 4 = 9216)."""
+    q = fp4_values(fp4_unpack(q_fp4))
+    k = fp4_values(fp4_unpack(k_fp4))
+    return np.rint(4.0 * (k @ q)).astype(np.int64)   # exact: quarter-multiples far below 2^53
+
+
+def csa_query_fp4(q, q_fp4, pos: int, Kc, Vc, k_fp4, c: int, topk: int, scale: float):
+    """One CSA query token with the FP4 indexer: FP4 scores -> top-k -> sparse attention."""
+    n_vis = n_visible(pos, c, Kc.shape[0])
+    scores = index_scores_fp4(q_fp4, k_fp4)
+    idx = topk_select(scores, n_vis, topk)
+    o, lse, p = attention(q, np.asarray(Kc)[idx], np.asarray(Vc)[idx], scale)
+    return {"o": o, "lse": lse, "p": p, "idx": idx, "scores": scores, "n_vis": n_vis}
+
+
 def topk_select(scores, n_vis: int, k: int) -> np.ndarray:
     """Indices of the top-k visible entries, returned in ascending index order.
 

@@ -6,6 +6,7 @@ SeedSequence, so any tensor can be regenerated on its own.  Tensor ids:
     0 raw K tokens     1 raw V tokens     2 indexer keys      3 queries
     4 indexer queries  5 context lengths  6 compressed K (direct)
     7 compressed V (direct)  8 new raw K (prefill)  9 new raw V (prefill)
+    10, 11 window state K / V   12 sink logits   13 FP4 indexer keys   14 FP4 indexer queries
 
 Host generation (numpy PCG64) is exact and reproducible on any CPU; it is what
 the parity tests use.  The device generators (torch Philox on the GPU) exist
@@ -20,6 +21,7 @@ import numpy as np
 T_RAW_K, T_RAW_V, T_KIDX, T_Q, T_QIDX, T_LEN, T_CMP_K, T_CMP_V, T_NEW_K, T_NEW_V = range(10)
 T_WIN_K, T_WIN_V = 10, 11   # sliding-window state buffers (raw tokens)
 T_SINK = 12                  # per-head attention-sink logits
+T_KFP4, T_QFP4 = 13, 14       # FP4 indexer keys / queries (packed E2M1 codes)
 
 
 def seed_of(cfg_id: int, layer: int, tensor_id: int, replica: int = 0) -> int:
@@ -52,6 +54,12 @@ def bf16_normal(gen: np.random.Generator, shape, std: float = 1.0) -> np.ndarray
 def int8_uniform(gen: np.random.Generator, shape) -> np.ndarray:
     """int8 uniform over the 255 integers -127..127 inclusive."""
     return gen.integers(-127, 128, size=shape, dtype=np.int8)
+
+
+def fp4_uniform(gen: np.random.Generator, shape) -> np.ndarray:
+    """Packed FP4 codes: uint8 bytes uniform over 0..255, i.e. two codes per byte, each
+    uniform over the 16 E2M1 codes."""
+    return gen.integers(0, 256, size=shape, dtype=np.uint8)
 
 
 def ragged_lengths(gen: np.random.Generator, n: int, lo: int, hi: int) -> np.ndarray:
@@ -96,3 +104,11 @@ def device_int8_uniform(shape, seed: int, device="cuda"):
 
     g = _torch_gen(seed, device)
     return torch.randint(-127, 128, shape, generator=g, device=device, dtype=torch.int8)
+
+
+def device_fp4_uniform(shape, seed: int, device="cuda"):
+    """Packed FP4 codes (uint8, two per byte, each uniform over the 16 codes), on the device."""
+    import torch
+
+    g = _torch_gen(seed, device)
+    return torch.randint(0, 256, shape, generator=g, device=device, dtype=torch.uint8)

@@ -59,7 +59,7 @@
 extern "C" {
 #endif
 
-#define LCA_ABI_VERSION 3
+#define LCA_ABI_VERSION 4
 
 enum lca_status {
   LCA_OK = 0,
@@ -124,6 +124,27 @@ int32_t lca_csa_index_score(const int8_t* q_idx, const int64_t* q_off, const int
                             int32_t max_q, int32_t max_entries, int32_t d_idx, int32_t c,
                             int32_t* scores, int64_t ld_scores, int32_t* n_vis, void* ws,
                             size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * csa_index_score_fp4 — the indexer scores with FP4 query and keys.  Page section
+ * 3-2 item 4: the indexer's Q.K path is trained with FP4 quantisation-aware
+ * training.  Reading: E2M1 codes (the OCP Microscaling FP4 element: sign, 2
+ * exponent bits with bias 1, 1 mantissa bit; values 0, 0.5, 1, 1.5, 2, 3, 4, 6 and
+ * their negatives), d_idx = 64 codes packed two per byte (element 2i in the low
+ * nibble of byte i), 32 bytes per vector, with one power-of-two scale per tensor,
+ * which cannot change the ranking and is left out.  score = 4 * sum_d q_d k_d, an
+ * exact integer in [-9216, 9216]: the same key range as the int8 scores, so
+ * lca_csa_topk_select and its fused histogram apply unchanged.
+ *
+ *   q_fp4    [rows, 32] uint8, k_fp4 [ent_off[B], 32] uint8; 16-byte aligned.
+ *   Every other argument as lca_csa_index_score (d_idx == 64).  Query batches of
+ *   any size run the same per-row kernel.
+ * ------------------------------------------------------------------------- */
+int32_t lca_csa_index_score_fp4(const uint8_t* q_fp4, const int64_t* q_off, const int64_t* q_pos,
+                                const uint8_t* k_fp4, const int64_t* ent_off, int32_t batch,
+                                int32_t max_q, int32_t max_entries, int32_t d_idx, int32_t c,
+                                int32_t* scores, int64_t ld_scores, int32_t* n_vis, void* ws,
+                                size_t ws_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------
  * csa_index_select — csa_index_score and csa_topk_select in one call, without
@@ -270,6 +291,7 @@ int32_t lca_attn_sink(lca_bf16* out, float* lse, const float* sink, int64_t rows
  * per row, a function of the layer count only.
  * ------------------------------------------------------------------------- */
 enum lca_layer_kind { LCA_LAYER_CSA = 0, LCA_LAYER_HCA = 1 };
+enum lca_idx_format { LCA_IDX_INT8 = 0, LCA_IDX_FP4 = 1 };
 
 typedef struct lca_layer {
   int32_t kind;          /* LCA_LAYER_CSA or LCA_LAYER_HCA */
@@ -293,6 +315,8 @@ typedef struct lca_layer {
   const int64_t* win_pos0; /* [B] device: absolute position of each buffer's first row */
   int32_t window;
   const float* sink;     /* optional [heads] per-head sink logits (NULL: none), as lca_attn_sink */
+  int32_t idx_format;    /* CSA: LCA_IDX_INT8, or LCA_IDX_FP4 (q_idx [rows, 32] / k_idx
+                            [ent_off[B], 32] hold packed FP4 codes, as lca_csa_index_score_fp4) */
 } lca_layer;
 
 size_t lca_hybrid_workspace_bytes(const lca_layer* layers, int32_t n_layers, int32_t batch,

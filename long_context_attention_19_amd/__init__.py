@@ -27,6 +27,8 @@ _i32, _i64, _u32, _f32, _sz, _vp = (ctypes.c_int32, ctypes.c_int64, ctypes.c_uin
 
 LCA_LAYER_CSA = 0
 LCA_LAYER_HCA = 1
+LCA_IDX_INT8 = 0
+LCA_IDX_FP4 = 1
 LCA_TOPK_HIST_READY = 1
 LCA_HYBRID_PHASES = 3
 
@@ -36,7 +38,7 @@ class LcaLayer(ctypes.Structure):
                 ("q", _vp), ("q_idx", _vp), ("k_cmp", _vp), ("v_cmp", _vp), ("k_idx", _vp),
                 ("ent_off", _vp), ("out", _vp), ("lse", _vp), ("idx", _vp), ("count", _vp),
                 ("win_k", _vp), ("win_v", _vp), ("win_off", _vp), ("win_pos0", _vp),
-                ("window", _i32), ("sink", _vp)]
+                ("window", _i32), ("sink", _vp), ("idx_format", _i32)]
 
 
 _SIGS = {
@@ -47,6 +49,8 @@ _SIGS = {
     "lca_kv_compress": (_i32, [_vp, _vp, _i32, _i32, _i32, _i32, _vp, _vp, _vp]),
     "lca_csa_index_score": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _vp,
                                    _i64, _vp, _vp, _sz, _vp]),
+    "lca_csa_index_score_fp4": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
+                                       _vp, _i64, _vp, _vp, _sz, _vp]),
     "lca_csa_index_select": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32,
                                     _vp, _vp, _vp, _vp]),
     "lca_window_attn": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
@@ -142,6 +146,15 @@ def csa_index_score(q_idx, q_off, q_pos, k_idx, ent_off, batch, max_q, max_entri
         _s(stream)))
 
 
+def csa_index_score_fp4(q_fp4, q_off, q_pos, k_fp4, ent_off, batch, max_q, max_entries, c, scores,
+                        n_vis, ws=None, stream=None):
+    """q_fp4 [rows, 32] / k_fp4 [entries, 32] uint8 packed E2M1 codes (d_idx = 64)."""
+    _check("lca_csa_index_score_fp4", _lib.lca_csa_index_score_fp4(
+        _p(q_fp4), _p(q_off), _p(q_pos), _p(k_fp4), _p(ent_off), batch, max_q, max_entries,
+        2 * q_fp4.shape[-1], c, _p(scores), scores.stride(0), _p(n_vis), _p(ws), _nb(ws),
+        _s(stream)))
+
+
 def csa_index_select(q_idx, q_off, q_pos, k_idx, ent_off, batch, max_q, max_entries, c, k, idx,
                      count, n_vis=None, stream=None):
     _check("lca_csa_index_select", _lib.lca_csa_index_select(
@@ -194,7 +207,8 @@ def make_layers(layers):
                           _p(L.get("k_idx")), _p(L["ent_off"]), _p(L["out"]), _p(L.get("lse")),
                           _p(L.get("idx")), _p(L.get("count")), _p(L.get("win_k")),
                           _p(L.get("win_v")), _p(L.get("win_off")), _p(L.get("win_pos0")),
-                          int(L.get("window", 0)), _p(L.get("sink")))
+                          int(L.get("window", 0)), _p(L.get("sink")),
+                          int(L.get("idx_format", LCA_IDX_INT8)))
     return arr
 
 

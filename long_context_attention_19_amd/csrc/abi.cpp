@@ -165,11 +165,11 @@ int32_t lca_kv_compress(const lca_bf16* x, const int64_t* tok_off, int32_t batch
 }
 
 // ------------------------------------------------------------------ index scores
-int32_t lca_csa_index_score(const int8_t* q_idx, const int64_t* q_off, const int64_t* q_pos,
+static int32_t index_score_impl(const int8_t* q_idx, const int64_t* q_off, const int64_t* q_pos,
                             const int8_t* k_idx, const int64_t* ent_off, int32_t batch,
                             int32_t max_q, int32_t max_entries, int32_t d_idx, int32_t c,
                             int32_t* scores, int64_t ld_scores, int32_t* n_vis, void* ws,
-                            size_t ws_bytes, void* stream) {
+                            size_t ws_bytes, void* stream, bool fp4) {
   if (d_idx != 64) return fail(LCA_ERR_UNSUPPORTED, "csa_index_score: d_idx=%d (only 64)", d_idx);
   if (batch < 0 || max_q < 0 || max_entries < 0) return fail(LCA_ERR_SHAPE, "csa_index_score: negative size");
   if (c < 1) return fail(LCA_ERR_SHAPE, "csa_index_score: ratio c=%d < 1", c);
@@ -183,6 +183,7 @@ int32_t lca_csa_index_score(const int8_t* q_idx, const int64_t* q_off, const int
   ib.q_pos = q_pos;
   ib.max_q = max_q;
   ib.n = 1;
+  ib.fp4 = fp4 ? 1 : 0;
   ib.layer[0] = lca::IndexLayer{q_idx, k_idx, ent_off, scores, ld_scores, n_vis, nullptr, nullptr,
                                 c, max_entries};
   if (ws) {
@@ -195,6 +196,26 @@ int32_t lca_csa_index_score(const int8_t* q_idx, const int64_t* q_off, const int
     ib.layer[0].fine = w.fine;
   }
   return hip_status(lca::launch_index_score(ib, batch, (hipStream_t)stream), "csa_index_score launch");
+}
+
+int32_t lca_csa_index_score(const int8_t* q_idx, const int64_t* q_off, const int64_t* q_pos,
+                            const int8_t* k_idx, const int64_t* ent_off, int32_t batch,
+                            int32_t max_q, int32_t max_entries, int32_t d_idx, int32_t c,
+                            int32_t* scores, int64_t ld_scores, int32_t* n_vis, void* ws,
+                            size_t ws_bytes, void* stream) {
+  return index_score_impl(q_idx, q_off, q_pos, k_idx, ent_off, batch, max_q, max_entries, d_idx, c,
+                          scores, ld_scores, n_vis, ws, ws_bytes, stream, false);
+}
+
+int32_t lca_csa_index_score_fp4(const uint8_t* q_fp4, const int64_t* q_off, const int64_t* q_pos,
+                                const uint8_t* k_fp4, const int64_t* ent_off, int32_t batch,
+                                int32_t max_q, int32_t max_entries, int32_t d_idx, int32_t c,
+                                int32_t* scores, int64_t ld_scores, int32_t* n_vis, void* ws,
+                                size_t ws_bytes, void* stream) {
+  return index_score_impl(reinterpret_cast<const int8_t*>(q_fp4), q_off, q_pos,
+                          reinterpret_cast<const int8_t*>(k_fp4), ent_off, batch, max_q,
+                          max_entries, d_idx, c, scores, ld_scores, n_vis, ws, ws_bytes, stream,
+                          true);
 }
 
 // ------------------------------------------------------------------ fused scores + top-k
@@ -429,6 +450,7 @@ int32_t lca_hybrid_layer_step(const lca_layer* layers, int32_t n_layers, const i
       if (L.topk <= 0) return fail(LCA_ERR_SHAPE, "hybrid_layer_step: layer %d topk=%d", l, L.topk);
       if (!L.q_idx || !L.k_idx || !L.idx || !L.count) return fail(LCA_ERR_NULL, "hybrid_layer_step: CSA layer %d NULL pointer", l);
       if (!al16(L.q_idx) || !al16(L.k_idx)) return fail(LCA_ERR_ALIGN, "hybrid_layer_step: layer %d indexer not aligned", l);
+      if (L.idx_format != LCA_IDX_INT8 && L.idx_format != LCA_IDX_FP4) return fail(LCA_ERR_SHAPE, "hybrid_layer_step: layer %d idx_format=%d", l, L.idx_format);
       if ((int64_t)L.max_entries > (int64_t)lca::topk_max_chunks() * kTopkChunk) return fail(LCA_ERR_UNSUPPORTED, "hybrid_layer_step: layer %d max_entries too large", l);
     }
     if (head_dim != 128) return fail(LCA_ERR_UNSUPPORTED, "hybrid_layer_step: head_dim=%d (only 128)", head_dim);
@@ -450,6 +472,7 @@ int32_t lca_hybrid_layer_step(const lca_layer* layers, int32_t n_layers, const i
   // carve each layer's workspace region (layer order, as lca_hybrid_workspace_bytes sizes it)
   std::vector<lca::IndexLayer> il;
   std::vector<lca::TopkLayer> tl;
+  std::vector<int> il_fp4;   // per CSA layer: FP4 indexer codes
   std::vector<lca::AttnArgs> csa_a, hca_a;
   char* p = reinterpret_cast<char*>(ws);
   for (int l = 0; l < n_layers; ++l) {
@@ -478,6 +501,7 @@ int32_t lca_hybrid_layer_step(const lca_layer* layers, int32_t n_layers, const i
       il.push_back(lca::IndexLayer{L.q_idx, L.k_idx, L.ent_off, scores, ld, n_vis, w.hist, w.fine,
                                    L.ratio, L.max_entries});
       tl.push_back(lca::TopkLayer{scores, ld, n_vis, L.idx, L.count, L.max_entries, L.topk, w});
+      il_fp4.push_back(L.idx_format == LCA_IDX_FP4 ? 1 : 0);
       a.idx = L.idx;
       a.count = L.count;
       a.k = L.topk;
@@ -512,20 +536,36 @@ int32_t lca_hybrid_layer_step(const lca_layer* layers, int32_t n_layers, const i
   auto mark = [&](int i) {
     if (timing && e == hipSuccess) e = hipEventRecord(ls->tev[i], caller);
   };
-  for (size_t c0 = 0; c0 < il.size() && e == hipSuccess; c0 += lca::MAX_BATCH_LAYERS) {
-    const int n = (int)std::min<size_t>(lca::MAX_BATCH_LAYERS, il.size() - c0);
+  // index launches group the CSA layers by indexer format, up to 8 layers each
+  std::vector<std::vector<int>> groups;
+  for (int f = 0; f < 2; ++f) {
+    std::vector<int> cur;
+    for (size_t l = 0; l < il.size(); ++l) {
+      if (il_fp4[l] != f) continue;
+      cur.push_back((int)l);
+      if ((int)cur.size() == lca::MAX_BATCH_LAYERS) {
+        groups.push_back(cur);
+        cur.clear();
+      }
+    }
+    if (!cur.empty()) groups.push_back(cur);
+  }
+  for (size_t gi = 0; gi < groups.size() && e == hipSuccess; ++gi) {
+    const std::vector<int>& grp = groups[gi];
+    const int n = (int)grp.size();
     lca::IndexBatch ib{};
     ib.q_off = q_off;
     ib.q_pos = q_pos;
     ib.max_q = max_q;
     ib.n = n;
+    ib.fp4 = il_fp4[grp[0]];
     lca::TopkBatch tb{};
     tb.n = n;
     for (int i = 0; i < n; ++i) {
-      ib.layer[i] = il[c0 + i];
-      tb.layer[i] = tl[c0 + i];
+      ib.layer[i] = il[grp[i]];
+      tb.layer[i] = tl[grp[i]];
     }
-    const bool first = c0 == 0;
+    const bool first = gi == 0;
     if (first) mark(0);
     e = lca::launch_index_score(ib, batch, caller);
     if (first) mark(1);

@@ -137,6 +137,145 @@ __global__ __launch_bounds__(IS_NT) void index_score_kernel(IndexBatch ib) {
   }
 }
 
+// ---------------------------------------------------------------- FP4 indexer
+// The same scores for the FP4 indexer ("DeepSeek-V4 ... Review", section 3-2 item 4:
+// the indexer's Q.K path is trained for FP4): query and keys are E2M1 codes, 32
+// packed bytes per vector (element 2i in the low nibble of byte i), with one
+// power-of-two scale per tensor, which cannot change the ranking and is left out.
+// The score is J = 4 * sum q_d k_d: every product of two E2M1 values is a multiple of
+// 1/4, so J is an exact integer with |J| <= 9216 and shares the int8 path's key range.
+//
+// The key stream halves (32 B per entry), and the products run on the MFMA in its
+// native FP4 form: v_mfma_scale_f32_32x32x64_f8f6f4 with both operands E2M1 and unit
+// scales.  Operand A is the query in every row (lane l brings bytes 16 (l / 32) ..
+// + 15, i.e. elements 32 (l / 32) .. + 31), operand B holds 32 keys as columns (lane
+// l brings the same elements of key l % 32), so a wave's 128-bit loads cover 32
+// consecutive keys = 1 KiB.  Row 0 of the 32 x 32 result sits in register 0 of lanes
+// 0..31: lane l gets key l's score.  The sums are exact in fp32 (quarter multiples
+// far below 2^24), so the order in which the hardware adds them does not matter.
+constexpr int IF_NT = 256;
+constexpr int IF_NW = IF_NT / WAVE;
+constexpr int IF_ROUNDS = 16;                                   // loads in flight per lane
+constexpr int IF_KEYS_PER_PASS = IF_NW * 32 * IF_ROUNDS;         // 2048
+
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+template <bool HIST, int PASSES>
+__global__ __launch_bounds__(IF_NT) void index_score_fp4_kernel(IndexBatch ib) {
+  constexpr int CHUNK = IF_KEYS_PER_PASS * PASSES;
+  constexpr int FP4_E2M1 = 4;   // MFMA operand format code
+  constexpr int UNIT_SCALE = 127;   // E8M0 2^0
+  __shared__ int32_t lh[HIST ? HIST_BINS : 1];
+  __shared__ __attribute__((aligned(16))) int32_t s_sc[CHUNK];
+  const IndexLayer& L = ib.layer[blockIdx.z];
+  const uint8_t* __restrict__ q_fp4 = reinterpret_cast<const uint8_t*>(L.q_idx);
+  const uint8_t* __restrict__ k_fp4 = reinterpret_cast<const uint8_t*>(L.k_idx);
+  int32_t* __restrict__ scores = L.scores;
+  int32_t* __restrict__ hist = L.hist;
+  int32_t* __restrict__ fine = L.fine;
+  const int64_t ld = L.ld;
+  const int c = L.c;
+  const int max_q = ib.max_q;
+  const int b = blockIdx.y / max_q;
+  const int i = blockIdx.y - b * max_q;
+  const int64_t r0 = ib.q_off[b];
+  if (i >= ib.q_off[b + 1] - r0) return;
+  const int64_t row = r0 + i;
+  const int64_t e0 = L.ent_off[b];
+  const int64_t N = min(L.ent_off[b + 1] - e0, (int64_t)L.max_entries);
+  const int64_t nv = min(ib.q_pos[row] / c, N);
+  const int64_t base = (int64_t)blockIdx.x * CHUNK;
+  if (blockIdx.x == 0 && threadIdx.x == 0) L.n_vis[row] = (int32_t)nv;
+  if (base >= N) return;
+
+  const int t = threadIdx.x;
+  const int w = __builtin_amdgcn_readfirstlane(t / WAVE);
+  const int lane = t & (WAVE - 1);
+  const int half = lane >> 5;   // which 32 elements of the vector this lane brings
+  const int kl = lane & 31;     // which of the wave's 32 keys
+  if (HIST) {
+    if (blockIdx.x == 0)
+      for (int k = t; k < FINE_BINS; k += IF_NT) fine[row * FINE_BINS + k] = 0;
+    for (int k = t; k < HIST_BINS; k += IF_NT) lh[k] = 0;
+    __syncthreads();
+  }
+  const i32x4 qv = *reinterpret_cast<const i32x4*>(q_fp4 + row * 32 + half * 16);
+  const i32x8 qa = {qv[0], qv[1], qv[2], qv[3], 0, 0, 0, 0};
+  const i32x4* kp = reinterpret_cast<const i32x4*>(k_fp4 + e0 * 32);   // 2 pieces per key
+  int32_t* srow = scores + row * ld;
+  const f32x16 zero16 = {};
+
+  for (int pass = 0; pass < PASSES; ++pass) {
+    const int64_t pb = base + pass * IF_KEYS_PER_PASS;
+    if (pb >= N) break;
+    i32x4 kv[IF_ROUNDS];
+#pragma unroll
+    for (int u = 0; u < IF_ROUNDS; ++u) {
+      const int64_t j = pb + u * (IF_NW * 32) + w * 32 + kl;
+      kv[u] = (j < N) ? __builtin_nontemporal_load(kp + j * 2 + half) : i32x4{0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int u = 0; u < IF_ROUNDS; ++u) {
+      const i32x8 kb = {kv[u][0], kv[u][1], kv[u][2], kv[u][3], 0, 0, 0, 0};
+      const f32x16 acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+          qa, kb, zero16, FP4_E2M1, FP4_E2M1, 0, UNIT_SCALE, 0, UNIT_SCALE);
+      if (half == 0) {   // row 0 of the product: lane kl holds key kl's score
+        const int jl = pass * IF_KEYS_PER_PASS + u * (IF_NW * 32) + w * 32 + kl;
+        const int64_t j = base + jl;
+        const int32_t v = (int32_t)(acc[0] * 4.0f);   // exact
+        const bool vis = j < nv;
+        s_sc[jl] = vis ? v : INT32_MIN;
+        if (HIST && vis && j < N) atomicAdd(&lh[(v + KEY_BIAS) >> 10], 1);
+      }
+    }
+  }
+  __syncthreads();
+  {
+    const int64_t cnt = min((int64_t)CHUNK, N - base);
+#pragma unroll
+    for (int u = 0; u < CHUNK / (4 * IF_NT); ++u) {
+      const int q = 4 * (t + IF_NT * u);
+      if (q + 4 <= cnt) {
+        *reinterpret_cast<i32x4*>(srow + base + q) = *reinterpret_cast<const i32x4*>(&s_sc[q]);
+      } else {
+        for (int e = 0; e < 4; ++e)
+          if (q + e < cnt) srow[base + q + e] = s_sc[q + e];
+      }
+    }
+  }
+  if (HIST) {
+    __syncthreads();
+    int32_t* gh = hist + row * HIST_BINS;
+    for (int k = t; k < HIST_BINS; k += IF_NT) {
+      const int32_t v = lh[k];
+      if (v) atomicAdd(gh + k, v);
+    }
+  }
+}
+
+static hipError_t launch_index_score_fp4(const IndexBatch& ib, int batch, int max_n, bool hist,
+                                         hipStream_t st) {
+  int passes = 1;
+  if ((int64_t)batch * ib.max_q * ib.n < IS_SMALL_CHUNK_ROWS)
+    while (passes < 4 && (int64_t)passes * IF_KEYS_PER_PASS * IS_GROUPS_PER_ROW < max_n) passes *= 2;
+  const int chunk = IF_KEYS_PER_PASS * passes;
+  int chunks = 1;
+  for (int l = 0; l < ib.n; ++l)
+    chunks = max(chunks, (ib.layer[l].max_entries + chunk - 1) / chunk);
+  dim3 grid((unsigned)chunks, (unsigned)(batch * ib.max_q), (unsigned)ib.n);
+#define LCA_IF_LAUNCH(P)                                                                      \
+  do {                                                                                        \
+    if (hist) hipLaunchKernelGGL((index_score_fp4_kernel<true, P>), grid, dim3(IF_NT), 0, st, ib); \
+    else hipLaunchKernelGGL((index_score_fp4_kernel<false, P>), grid, dim3(IF_NT), 0, st, ib); \
+  } while (0)
+  if (passes == 1) LCA_IF_LAUNCH(1);
+  else if (passes == 2) LCA_IF_LAUNCH(2);
+  else LCA_IF_LAUNCH(4);
+#undef LCA_IF_LAUNCH
+  return hipGetLastError();
+}
+
 // ---------------------------------------------------------------- many query rows
 // With 16 or more query tokens per sequence (prefill) the scores are the int8 GEMM
 // Q_idx [rows x 64] . K_idx^T [64 x N].  One v_mfma_i32_16x16x64_i8 yields the 16 x 16
@@ -342,6 +481,7 @@ hipError_t launch_index_score(const IndexBatch& ib, int batch, hipStream_t st) {
     max_n = max(max_n, ib.layer[l].max_entries);
     hist = hist || ib.layer[l].hist != nullptr;
   }
+  if (ib.fp4) return launch_index_score_fp4(ib, batch, max_n, hist, st);
   if (ib.max_q >= IG_ROWS) {
     // enough query tokens per sequence for 16-wide MFMA tiles; split the entries
     // only as far as needed to give every CU a work-group

@@ -34,6 +34,7 @@ struct IndexBatch {
   const int64_t* q_pos;
   int32_t max_q;
   int32_t n;
+  int32_t fp4;             // q_idx / k_idx hold packed FP4 (E2M1) codes, 32 bytes per vector
   IndexLayer layer[MAX_BATCH_LAYERS];
 };
 hipError_t launch_index_score(const IndexBatch& ib, int batch, hipStream_t st);

@@ -3,7 +3,8 @@
 CsaStep   selection, then csa_sparse_attn.  Selection is csa_index_score (with the
           fused first radix pass) -> csa_topk_select for decode (fewer than 16
           queries per sequence), and csa_index_select (scores never written) for
-          chunked prefill (16 or more queries per sequence).
+          chunked prefill (16 or more queries per sequence); with the FP4 indexer,
+          csa_index_score_fp4 -> csa_topk_select for any query batch.
 HcaStep   hca_dense_attn.
 HybridStep  hybrid_layer_step over a list of CSA / HCA layers.
 
@@ -14,9 +15,10 @@ from __future__ import annotations
 
 import torch
 
-from . import (LCA_LAYER_CSA, LCA_LAYER_HCA, attn_workspace_bytes, csa_index_score,
-               csa_index_select, csa_sparse_attn, csa_topk_select, csa_topk_workspace_bytes, hca_dense_attn,
-               hybrid_layer_step, hybrid_workspace_bytes, make_layers, workspace)
+from . import (LCA_IDX_FP4, LCA_IDX_INT8, LCA_LAYER_CSA, LCA_LAYER_HCA, attn_workspace_bytes,
+               csa_index_score, csa_index_score_fp4, csa_index_select, csa_sparse_attn,
+               csa_topk_select, csa_topk_workspace_bytes, hca_dense_attn, hybrid_layer_step,
+               hybrid_workspace_bytes, make_layers, workspace)
 
 
 SELECT_MIN_Q = 16   # query tokens per sequence from which csa_index_select applies
@@ -28,15 +30,17 @@ def _round4(n: int) -> int:
 
 class CsaStep:
     """fused: None picks csa_index_select when max_q >= 16; True / False force it
-    on / off (the two-call path materialises the scores in self.scores)."""
+    on / off (the two-call path materialises the scores in self.scores).  fp4: the
+    indexer query / keys are packed FP4 codes (csa_index_score_fp4, never fused)."""
 
     def __init__(self, batch, max_q, max_entries, heads, topk, c, device="cuda", splits=0,
-                 fused=None):
+                 fused=None, fp4=False):
         self.batch, self.max_q, self.max_entries = batch, max_q, max_entries
         self.heads, self.topk, self.c, self.splits = heads, topk, c, splits
         rows = batch * max_q
         self.rows = rows
-        self.fused = (max_q >= SELECT_MIN_Q) if fused is None else fused
+        self.fp4 = fp4
+        self.fused = False if fp4 else (max_q >= SELECT_MIN_Q) if fused is None else fused
         self.n_vis = torch.empty(rows, dtype=torch.int32, device=device)
         self.idx = torch.empty(rows, topk, dtype=torch.int32, device=device)
         self.count = torch.empty(rows, dtype=torch.int32, device=device)
@@ -52,9 +56,9 @@ class CsaStep:
                              self.max_entries, self.c, self.topk, self.idx, self.count,
                              self.n_vis, stream=stream)
             return
-        csa_index_score(q_idx, q_off, q_pos, k_idx, ent_off, self.batch, self.max_q,
-                        self.max_entries, self.c, self.scores, self.n_vis, ws=self.tws,
-                        stream=stream)
+        score = csa_index_score_fp4 if self.fp4 else csa_index_score
+        score(q_idx, q_off, q_pos, k_idx, ent_off, self.batch, self.max_q, self.max_entries,
+              self.c, self.scores, self.n_vis, ws=self.tws, stream=stream)
         csa_topk_select(self.scores, self.rows, self.max_entries, self.n_vis, self.topk, self.idx,
                         self.count, self.tws, hist_ready=True, stream=stream)
 
@@ -84,8 +88,9 @@ class HcaStep:
 class HybridStep:
     """layers: dicts with kind, ratio, topk, max_entries and the layer's tensors
     (q, q_idx, k_cmp, v_cmp, k_idx, ent_off, out, lse), optionally a sliding window
-    (win_k, win_v, win_off, win_pos0, window) and per-head sink logits (sink); idx / count
-    of CSA layers are allocated here when absent."""
+    (win_k, win_v, win_off, win_pos0, window), per-head sink logits (sink) and, for CSA
+    layers, idx_format (LCA_IDX_FP4: packed FP4 indexer codes); idx / count of CSA layers
+    are allocated here when absent."""
 
     def __init__(self, layers, batch, max_q, heads, device="cuda"):
         rows = batch * max_q
@@ -105,4 +110,5 @@ class HybridStep:
                           scale, self.ws, stream=stream)
 
 
-__all__ = ["CsaStep", "HcaStep", "HybridStep", "LCA_LAYER_CSA", "LCA_LAYER_HCA"]
+__all__ = ["CsaStep", "HcaStep", "HybridStep", "LCA_LAYER_CSA", "LCA_LAYER_HCA", "LCA_IDX_INT8",
+           "LCA_IDX_FP4"]

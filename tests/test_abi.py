@@ -30,11 +30,13 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_version_and_struct_layout():
-    assert lca.abi_version() == 3
-    # 4 int32, 10 pointers, 4 window pointers, int32 window (+4 padding), sink pointer
-    assert ctypes.sizeof(lca.LcaLayer) == 16 + 10 * 8 + 4 * 8 + 8 + 8
+    assert lca.abi_version() == 4
+    # 4 int32, 10 pointers, 4 window pointers, int32 window (+4 padding), sink pointer,
+    # int32 idx_format (+4 padding)
+    assert ctypes.sizeof(lca.LcaLayer) == 16 + 10 * 8 + 4 * 8 + 8 + 8 + 8
     assert lca.LcaLayer.window.offset == 16 + 14 * 8
     assert lca.LcaLayer.sink.offset == 16 + 14 * 8 + 8
+    assert lca.LcaLayer.idx_format.offset == 16 + 14 * 8 + 16
 
 
 def L():
@@ -173,3 +175,15 @@ def test_attn_sink_validation():
     assert f(*args(sink=None)) == E_NULL
     assert f(*args(out=MIS)) == E_ALIGN
     assert "aligned" in lca.last_error()
+
+
+def test_index_score_fp4_validation():
+    f = L().lca_csa_index_score_fp4
+    args = lambda **kw: [kw.get("q", FAKE), FAKE, FAKE, kw.get("k", FAKE), FAKE, kw.get("B", 2),
+                         1, 100, kw.get("d", 64), 4, kw.get("s", FAKE), ctypes.c_int64(kw.get("ld", 100)),
+                         FAKE, None, 0, None]
+    assert f(*args(B=0, q=None)) == OK
+    assert f(*args(d=128)) == E_UNSUP
+    assert f(*args(ld=98)) == E_SHAPE
+    assert f(*args(k=None)) == E_NULL
+    assert f(*args(q=MIS)) == E_ALIGN

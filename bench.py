@@ -9,7 +9,7 @@ uniformly from 65,536..1,048,576 tokens; 64 query heads on one KV head); the
 other workloads (csa_decode_8k, hca_decode_128k, csa_decode_1m,
 csa_prefill_256k, hybrid_decode_1m_swa: the stack with a 128-token sliding window on
 every layer, hybrid_decode_1m_swa_sink: that and a per-head attention sink on every
-layer) can be named with --workload.  A step is one pass of the
+layer, hybrid_decode_1m_fp4: the stack with the FP4 indexer) can be named with --workload.  A step is one pass of the
 workload's whole path over one batch; inputs are seeded, synthetic and resident
 in HBM before timing starts.  Decode workloads smaller than the 256 MB
 last-level cache rotate input replicas so that each step reads from HBM.
@@ -146,6 +146,8 @@ class HybridRunner(_Capture):
         from long_context_attention_19_amd.pipeline import HybridStep
         from workloads import device as wdev
         self.wl, self.lca, self.torch = wl, lca, torch
+        if wl.idx_fp4:
+            self.dominant_tag = "index_score_fp4_kernel"
         self.L, self.layers = wdev.hybrid_inputs(wl, device)
         B, H = wl.batch, wl.heads
         specs = []
@@ -157,6 +159,8 @@ class HybridRunner(_Capture):
                      lse=torch.empty(B, H, dtype=torch.float32, device=device))
             if d["csa"]:
                 s.update(topk=wl.topk, k_idx=d["k_idx"], q_idx=d["q_idx"])
+                if wl.idx_fp4:
+                    s.update(idx_format=lca.LCA_IDX_FP4)
             if wl.window:
                 s.update(win_k=d["win_k"], win_v=d["win_v"], win_off=d["win_off_dev"],
                          win_pos0=d["win_pos0_dev"], window=wl.window)
@@ -182,7 +186,8 @@ class HybridRunner(_Capture):
         for d in self.layers:
             N = d["N"]
             if d["csa"]:
-                tot += int(np.sum(64 * N + np.minimum(N, wl.topk) * 512 + 64))
+                kb = 32 if wl.idx_fp4 else 64   # indexer key / query bytes
+                tot += int(np.sum(kb * N + np.minimum(N, wl.topk) * 512 + kb))
             else:
                 tot += int(np.sum(N * 512))
             tot += wl.batch * wl.heads * QO_BYTES_PER_HEAD
@@ -211,6 +216,13 @@ class HybridRunner(_Capture):
 
     def dominant_units(self):
         n = float(sum(int(np.sum(d["N"])) for d in self._csa))
+        if self.wl.idx_fp4:
+            return {"bound": "hbm", "per_launch": n * (32 + 4) + len(self._csa) * self.wl.batch * 32,
+                    "unit": "GB/s",
+                    "kernel": f"index_score_fp4_kernel<true> ({len(self._csa)} CSA layers in one "
+                              "launch): FP4 indexer scores (FP4 MFMA) + fused radix histogram",
+                    "per_unit": "36 B per compressed entry (32 B FP4 key read, 4 B score "
+                                "written) + 32 B per query"}
         return {"bound": "hbm", "per_launch": n * (64 + 4) + len(self._csa) * self.wl.batch * 64,
                 "unit": "GB/s",
                 "kernel": f"index_score_kernel<true> ({len(self._csa)} CSA layers in one launch): "
@@ -247,6 +259,10 @@ class HybridRunner(_Capture):
                         else:
                             fn = lambda: oracle.hca_query_sink(q, L, Kc, Vc, d["ratio"], SCALE, z,
                                                                Kw_, Vw_, p0_, w_)
+                    elif d["csa"] and wl.idx_fp4:
+                        kidx, qidx = d["k_idx"][s:e].cpu().numpy(), d["q_idx"][b].cpu().numpy()
+                        fn = lambda: oracle.csa_query_fp4(q, qidx, L, Kc, Vc, kidx, d["ratio"],
+                                                          wl.topk, SCALE)
                     elif d["csa"]:
                         kidx, qidx = d["k_idx"][s:e].cpu().numpy(), d["q_idx"][b].cpu().numpy()
                         if wl.window:
@@ -587,6 +603,8 @@ def main(argv=None):
         cfg["window"] = wl.window
     if wl.sink:
         cfg["sink"] = "per-head logits on every layer"
+    if wl.idx_fp4:
+        cfg["indexer"] = "FP4 E2M1 (32 B per key)"
     line = {
         "metric": METRIC,
         "value": run.tokens_per_step / (ms * 1e-3),

@@ -132,9 +132,10 @@ int32_t lca_csa_index_score(const int8_t* q_idx, const int64_t* q_off, const int
  * exponent bits with bias 1, 1 mantissa bit; values 0, 0.5, 1, 1.5, 2, 3, 4, 6 and
  * their negatives), d_idx = 64 codes packed two per byte (element 2i in the low
  * nibble of byte i), 32 bytes per vector, with one power-of-two scale per tensor,
- * which cannot change the ranking and is left out.  score = 4 * sum_d q_d k_d, an
- * exact integer in [-9216, 9216]: the same key range as the int8 scores, so
- * lca_csa_topk_select and its fused histogram apply unchanged.
+ * which cannot change the ranking and is left out.  score = 256 * sum_d q_d k_d, an
+ * exact integer (a multiple of 64) in [-589824, 589824]: inside the int8 scores'
+ * range (|score| < 2^20) and spread over it, so lca_csa_topk_select and its fused
+ * histogram apply unchanged and their 2048 coarse bins resolve it.
  *
  *   q_fp4    [rows, 32] uint8, k_fp4 [ent_off[B], 32] uint8; 16-byte aligned.
  *   Every other argument as lca_csa_index_score (d_idx == 64).  Query batches of

@@ -142,8 +142,10 @@ __global__ __launch_bounds__(IS_NT) void index_score_kernel(IndexBatch ib) {
 // the indexer's Q.K path is trained for FP4): query and keys are E2M1 codes, 32
 // packed bytes per vector (element 2i in the low nibble of byte i), with one
 // power-of-two scale per tensor, which cannot change the ranking and is left out.
-// The score is J = 4 * sum q_d k_d: every product of two E2M1 values is a multiple of
-// 1/4, so J is an exact integer with |J| <= 9216 and shares the int8 path's key range.
+// The score is J = 256 * sum q_d k_d: every product of two E2M1 values is a multiple
+// of 1/4, so J is an exact integer with |J| <= 589,824 < 2^20.  The unit (a power of two,
+// free since the tensor scales are) spreads the scores over the int8 path's key range:
+// in units of 1/4 they would fill only a few of the top-k's 1024-wide coarse bins.
 //
 // The key stream halves (32 B per entry), and the products run on the MFMA in its
 // native FP4 form: v_mfma_scale_f32_32x32x64_f8f6f4 with both operands E2M1 and unit
@@ -223,7 +225,7 @@ __global__ __launch_bounds__(IF_NT) void index_score_fp4_kernel(IndexBatch ib) {
       if (half == 0) {   // row 0 of the product: lane kl holds key kl's score
         const int jl = pass * IF_KEYS_PER_PASS + u * (IF_NW * 32) + w * 32 + kl;
         const int64_t j = base + jl;
-        const int32_t v = (int32_t)(acc[0] * 4.0f);   // exact
+        const int32_t v = (int32_t)(acc[0] * 256.0f);   // exact
         const bool vis = j < nv;
         s_sc[jl] = vis ? v : INT32_MIN;
         if (HIST && vis && j < N) atomicAdd(&lh[(v + KEY_BIAS) >> 10], 1);

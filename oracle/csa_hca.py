@@ -119,17 +119,18 @@ def fp4_unpack(packed) -> np.ndarray:
 
 
 def index_scores_fp4(q_fp4, k_fp4) -> np.ndarray:
-    """FP4 indexer scores: J_j = 4 * sum_d q[d] * k[j, d] over E2M1 values, exactly.
+    """FP4 indexer scores: J_j = 256 * sum_d q[d] * k[j, d] over E2M1 values, exactly.
 
     PAGE section 3-2 item 4: the CSA indexer's Q.K path is trained with FP4
     quantisation-aware training.  Reading: query and keys are E2M1 codes (d_idx = 64,
     32 packed bytes per vector) with one power-of-two scale per tensor; a positive
     common factor cannot change the ranking, so the score is the dot product of the
-    code values, reported x4 (every product is a multiple of 1/4, so J is an exact
-    integer, |J| <= 64 * 6 * 6 * 4 = 9216)."""
+    code values in a fixed power-of-two unit: x256 (every product is a multiple of
+    1/4, so J is an exact integer, a multiple of 64, |J| <= 64 * 6 * 6 * 256 =
+    589,824 < 2^20: the same range as the int8 scores)."""
     q = fp4_values(fp4_unpack(q_fp4))
     k = fp4_values(fp4_unpack(k_fp4))
-    return np.rint(4.0 * (k @ q)).astype(np.int64)   # exact: quarter-multiples far below 2^53
+    return np.rint(256.0 * (k @ q)).astype(np.int64)   # exact: quarter-multiples far below 2^53
 
 
 def csa_query_fp4(q, q_fp4, pos: int, Kc, Vc, k_fp4, c: int, topk: int, scale: float):

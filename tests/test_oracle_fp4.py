@@ -1,5 +1,5 @@
 """Pins for the oracle's FP4 indexer (E2M1 codes, packed two per byte, scores as
-exact integers J = 4 * sum q k).
+exact integers J = 256 * sum q k).
 
 Witnesses: the E2M1 value table of the OCP Microscaling specification, a hand-packed
 byte, a packer written here, Python-integer brute force, the exactly pinned int8
@@ -49,7 +49,7 @@ def test_scores_brute_force():
     q, k = fp4_uniform(g, (32,)), fp4_uniform(g, (200, 32))
     s = oracle.index_scores_fp4(q, k)
     assert s.dtype == np.int64
-    assert [int(x) for x in s] == [_py_score(q, k[j]) for j in range(200)]
+    assert [int(x) for x in s] == [64 * _py_score(q, k[j]) for j in range(200)]
 
 
 def test_scores_equal_int8_scorer_on_doubled_values():
@@ -57,18 +57,18 @@ def test_scores_equal_int8_scorer_on_doubled_values():
     q, k = fp4_uniform(g, (32,)), fp4_uniform(g, (1000, 32))
     q2 = (2 * oracle.fp4_values(oracle.fp4_unpack(q))).astype(np.int8)
     k2 = (2 * oracle.fp4_values(oracle.fp4_unpack(k))).astype(np.int8)
-    assert np.array_equal(oracle.index_scores_fp4(q, k), oracle.index_scores(q2, k2))
+    assert np.array_equal(oracle.index_scores_fp4(q, k), 64 * oracle.index_scores(q2, k2))
 
 
 def test_score_bound_and_zero():
     six, msix = 0x77, 0xFF                       # both nibbles +6, both -6
     q = np.full(32, six, np.uint8)
-    assert oracle.index_scores_fp4(q, np.full((1, 32), six, np.uint8))[0] == 9216
-    assert oracle.index_scores_fp4(q, np.full((1, 32), msix, np.uint8))[0] == -9216
+    assert oracle.index_scores_fp4(q, np.full((1, 32), six, np.uint8))[0] == 589824
+    assert oracle.index_scores_fp4(q, np.full((1, 32), msix, np.uint8))[0] == -589824
     assert oracle.index_scores_fp4(q, np.full((1, 32), 0x88, np.uint8))[0] == 0   # -0 codes
     g = rng(953, 0, 0)
     s = oracle.index_scores_fp4(fp4_uniform(g, (32,)), fp4_uniform(g, (5000, 32)))
-    assert np.abs(s).max() <= 9216
+    assert np.abs(s).max() <= 589824 < (1 << 20) and np.all(s % 64 == 0)
 
 
 @pytest.mark.parametrize("pos", [7, 3000])

@@ -32,6 +32,7 @@ class Workload:
     direct_entries: bool = False   # draw compressed entries directly (no raw tokens)
     window: int = 0        # sliding-window branch: raw tokens before the query (0: none)
     sink: bool = False     # per-head attention-sink logits on every layer
+    idx_fp4: bool = False  # FP4 (E2M1) indexer query / keys instead of int8
     notes: str = field(default="", compare=False)
 
     @property
@@ -72,6 +73,13 @@ WORKLOADS = {
         window=128, sink=True,
         notes="compressed entries drawn directly as bf16 N(0, 1/ratio); state buffers of the "
               "last 128 raw tokens drawn as bf16 N(0, 1); sink logits fp32 N(0, 1) per head"),
+    # the stack with the FP4 indexer on its CSA layers (packed E2M1 codes, 32 B per key)
+    "hybrid_decode_1m_fp4": Workload(
+        name="hybrid_decode_1m_fp4", cfg_id=3, kind="hybrid_decode", batch=16, ctx_len=None,
+        ctx_range=(65536, 1048576), heads=64, topk=2048, n_layers=8, direct_entries=True,
+        idx_fp4=True,
+        notes="compressed entries drawn directly as bf16 N(0, 1/ratio); FP4 indexer codes "
+              "uniform over the 16 E2M1 codes"),
     # CSA chunked prefill: 4096 new tokens after a 256K context
     "csa_prefill_256k": Workload(
         name="csa_prefill_256k", cfg_id=4, kind="csa_prefill", batch=1, ctx_len=262144,

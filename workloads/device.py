@@ -49,7 +49,12 @@ def hybrid_inputs(wl: Workload, device="cuda"):
                  v_cmp=gen.device_bf16_normal((tot, 128), gen.seed_of(wl.cfg_id, li, gen.T_CMP_V),
                                               std, device),
                  ent_off_dev=torch.tensor(ent_off, device=device))
-        if csa:
+        if csa and wl.idx_fp4:   # packed FP4 codes, 32 bytes per vector
+            d["k_idx"] = gen.device_fp4_uniform((tot, 32), gen.seed_of(wl.cfg_id, li, gen.T_KFP4),
+                                                device)
+            d["q_idx"] = gen.device_fp4_uniform((B, 32), gen.seed_of(wl.cfg_id, li, gen.T_QFP4),
+                                                device)
+        elif csa:
             d["k_idx"] = gen.device_int8_uniform((tot, 64), gen.seed_of(wl.cfg_id, li, gen.T_KIDX),
                                                  device)
             d["q_idx"] = gen.device_int8_uniform((B, 64), gen.seed_of(wl.cfg_id, li, gen.T_QIDX),

@@ -42,6 +42,9 @@ from .csa_hca import (
     fp4_unpack,
     index_scores_fp4,
     csa_query_fp4,
+    fp8_e4m3_values,
+    kv8_values,
+    KV8_ROW_BYTES,
 )
 
 __all__ = [
@@ -50,4 +53,5 @@ __all__ = [
     "hybrid_decode", "csa_prefill", "window_tokens", "attention_union", "csa_query_swa",
     "hca_query_swa", "attention_sink", "csa_query_sink", "hca_query_sink",
     "fp4_values", "fp4_unpack", "index_scores_fp4", "csa_query_fp4",
+    "fp8_e4m3_values", "kv8_values", "KV8_ROW_BYTES",
 ]

@@ -51,6 +51,35 @@ def to_bf16_values(x) -> np.ndarray:
 # compression
 
 
+def fp8_e4m3_values(codes) -> np.ndarray:
+    """Values of FP8 E4M3 codes (the OCP 8-bit floating point E4M3 format): bit 7 the
+    sign, bits 6..3 the exponent with bias 7, bits 2..0 the mantissa; exponent field
+    0 is subnormal (m * 2^-9), otherwise (1 + m/8) * 2^(e - 7); S.1111.111 is NaN and
+    there are no infinities (largest finite value 448)."""
+    c = np.asarray(codes).astype(np.int64) & 255
+    sign, e, m = c >> 7, (c >> 3) & 15, c & 7
+    mag = np.where(e == 0, m * 2.0 ** -9, (1.0 + m / 8.0) * np.exp2(e - 7.0))
+    mag = np.where((e == 15) & (m == 7), np.nan, mag)
+    return np.where(sign == 1, -mag, mag)
+
+
+KV8_ROW_BYTES = 192   # 64 FP8 bytes (dims 0..63), then 64 bf16 values (dims 64..127)
+
+
+def kv8_values(rows) -> np.ndarray:
+    """Values of mixed-storage KV rows [N, 192] (uint8) as fp64 [N, 128].
+
+    PAGE section 3-2 item 2 (component table): the KV cache keeps the RoPE dims in
+    BF16 and the rest in FP8.  Reading: of the 128 dims of a compressed entry the last
+    64 are the RoPE dims; a row stores dims 0..63 as FP8 E4M3 codes (one scale per
+    tensor, 1) in bytes 0..63 and dims 64..127 as bf16 (little-endian) in bytes
+    64..191.  The same row format serves the K and the V cache."""
+    r = np.asarray(rows, dtype=np.uint8).reshape(-1, KV8_ROW_BYTES)
+    lo = fp8_e4m3_values(r[:, :64])
+    hi = bf16_bits_to_f64(np.ascontiguousarray(r[:, 64:]).view("<u2"))
+    return np.concatenate([lo, hi], axis=1)
+
+
 def kv_compress(x, c: int) -> np.ndarray:
     """Sequence-direction compression: one entry per complete block of c tokens.
 

@@ -56,6 +56,44 @@ def int8_uniform(gen: np.random.Generator, shape) -> np.ndarray:
     return gen.integers(-127, 128, size=shape, dtype=np.int8)
 
 
+def _e4m3_table():
+    """Non-negative finite FP8 E4M3 values by code 0..126 (exponent bias 7, 3 mantissa
+    bits, subnormals below 2^-6); ascending in the code."""
+    codes = np.arange(127)
+    e, m = codes >> 3, codes & 7
+    return np.where(e == 0, m * 2.0 ** -9, (1.0 + m / 8.0) * 2.0 ** (e - 7.0))
+
+
+def fp8_e4m3_bits(x) -> np.ndarray:
+    """Round to FP8 E4M3 codes: nearest value, ties to the even code, saturating at
+    +-448 (the storage rounding of the mixed KV rows)."""
+    x = np.asarray(x, dtype=np.float64)
+    vals = _e4m3_table()
+    a = np.minimum(np.abs(x), vals[-1])
+    hi = np.clip(np.searchsorted(vals, a), 1, len(vals) - 1)
+    lo = hi - 1
+    dl, dh = a - vals[lo], vals[hi] - a
+    pick = np.where(dl < dh, lo, np.where(dh < dl, hi, np.where(lo % 2 == 0, lo, hi)))
+    return (pick | np.where(np.signbit(x), 128, 0)).astype(np.uint8)
+
+
+def kv8_rows(x) -> np.ndarray:
+    """Mixed KV rows [N, 192] uint8 from values [N, 128]: dims 0..63 as FP8 E4M3 codes,
+    dims 64..127 as bf16 (little-endian)."""
+    x = np.asarray(x, dtype=np.float32).reshape(-1, 128)
+    lo = fp8_e4m3_bits(x[:, :64])
+    hi = bf16_bits_from_f32(np.ascontiguousarray(x[:, 64:])).astype("<u2").view(np.uint8)
+    return np.concatenate([lo, hi.reshape(-1, 128)], axis=1)
+
+
+def kv8_normal(gen: np.random.Generator, n: int, std: float = 1.0) -> np.ndarray:
+    """Mixed KV rows of N(0, std^2) float32 draws."""
+    x = gen.standard_normal(size=(n, 128), dtype=np.float32)
+    if std != 1.0:
+        x = (x.astype(np.float64) * std).astype(np.float32)
+    return kv8_rows(x)
+
+
 def fp4_uniform(gen: np.random.Generator, shape) -> np.ndarray:
     """Packed FP4 codes: uint8 bytes uniform over 0..255, i.e. two codes per byte, each
     uniform over the 16 E2M1 codes."""
@@ -112,3 +150,21 @@ def device_fp4_uniform(shape, seed: int, device="cuda"):
 
     g = _torch_gen(seed, device)
     return torch.randint(0, 256, shape, generator=g, device=device, dtype=torch.uint8)
+
+
+def device_kv8_normal(n: int, seed: int, std: float = 1.0, device="cuda"):
+    """Mixed KV rows [n, 192] uint8 of N(0, std^2) draws made on the device: dims 0..63
+    rounded to FP8 E4M3 (nearest even, saturating), dims 64..127 to bf16."""
+    import torch
+
+    g = _torch_gen(seed, device)
+    out = torch.empty((n, 192), dtype=torch.uint8, device=device)
+    slab = 1 << 19
+    for s0 in range(0, n, slab):
+        e = min(n, s0 + slab)
+        x = torch.randn((e - s0, 128), generator=g, device=device, dtype=torch.float32)
+        if std != 1.0:
+            x.mul_(std)
+        out[s0:e, :64] = x[:, :64].clamp(-448.0, 448.0).to(torch.float8_e4m3fn).view(torch.uint8)
+        out[s0:e, 64:] = x[:, 64:].to(torch.bfloat16).contiguous().view(torch.uint8)
+    return out

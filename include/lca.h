@@ -59,7 +59,7 @@
 extern "C" {
 #endif
 
-#define LCA_ABI_VERSION 4
+#define LCA_ABI_VERSION 5
 
 enum lca_status {
   LCA_OK = 0,
@@ -231,6 +231,27 @@ int32_t lca_hca_dense_attn(const lca_bf16* q, const lca_bf16* k_cmp, const lca_b
                            int32_t heads, int32_t head_dim, float scale, int32_t splits,
                            lca_bf16* out, float* lse, void* ws, size_t ws_bytes, void* stream);
 
+/* Mixed KV storage.  Page section 3-2 item 2 (component table): the KV cache keeps the
+ * RoPE dims in BF16 and the rest in FP8.  Reading: of the 128 dims of a compressed
+ * entry the last 64 are the RoPE dims; a row of KV8 (192 bytes, 16-byte aligned)
+ * holds dims 0..63 as FP8 E4M3 codes (OCP E4M3: bias 7, no infinities, largest 448;
+ * one scale per tensor, 1) in bytes 0..63 and dims 64..127 as bf16 in bytes 64..191.
+ * The K and the V cache use the same row format.  The _kv8 calls take k_cmp / v_cmp
+ * [ent_off[B], 192] uint8 in that format and are otherwise the calls above; heads must
+ * be a multiple of 64 (LCA_ERR_UNSUPPORTED otherwise).  The FP8 dims are widened to
+ * bf16 exactly (every E4M3 value is a bf16 value) and the arithmetic is the same. */
+int32_t lca_csa_sparse_attn_kv8(const lca_bf16* q, const uint8_t* k_cmp, const uint8_t* v_cmp,
+                                const int64_t* ent_off, const int64_t* q_off, int32_t batch,
+                                int32_t max_q, const int32_t* idx, const int32_t* count, int32_t k,
+                                int32_t heads, int32_t head_dim, float scale, int32_t splits,
+                                lca_bf16* out, float* lse, void* ws, size_t ws_bytes,
+                                void* stream);
+int32_t lca_hca_dense_attn_kv8(const lca_bf16* q, const uint8_t* k_cmp, const uint8_t* v_cmp,
+                               const int64_t* ent_off, const int64_t* q_off, const int64_t* q_pos,
+                               int32_t batch, int32_t max_q, int32_t max_entries, int32_t m,
+                               int32_t heads, int32_t head_dim, float scale, int32_t splits,
+                               lca_bf16* out, float* lse, void* ws, size_t ws_bytes, void* stream);
+
 /* ---------------------------------------------------------------------------
  * window_attn — the sliding-window branch, merged into a compressed branch's result.
  * Page section 3-2 item 2: CSA and HCA both add a branch over the most recent tokens
@@ -293,6 +314,7 @@ int32_t lca_attn_sink(lca_bf16* out, float* lse, const float* sink, int64_t rows
  * ------------------------------------------------------------------------- */
 enum lca_layer_kind { LCA_LAYER_CSA = 0, LCA_LAYER_HCA = 1 };
 enum lca_idx_format { LCA_IDX_INT8 = 0, LCA_IDX_FP4 = 1 };
+enum lca_kv_format { LCA_KV_BF16 = 0, LCA_KV_MIXED = 1 };
 
 typedef struct lca_layer {
   int32_t kind;          /* LCA_LAYER_CSA or LCA_LAYER_HCA */
@@ -318,6 +340,8 @@ typedef struct lca_layer {
   const float* sink;     /* optional [heads] per-head sink logits (NULL: none), as lca_attn_sink */
   int32_t idx_format;    /* CSA: LCA_IDX_INT8, or LCA_IDX_FP4 (q_idx [rows, 32] / k_idx
                             [ent_off[B], 32] hold packed FP4 codes, as lca_csa_index_score_fp4) */
+  int32_t kv_format;     /* LCA_KV_BF16, or LCA_KV_MIXED (k_cmp / v_cmp hold 192-byte mixed
+                            rows, as lca_csa_sparse_attn_kv8; heads a multiple of 64) */
 } lca_layer;
 
 size_t lca_hybrid_workspace_bytes(const lca_layer* layers, int32_t n_layers, int32_t batch,

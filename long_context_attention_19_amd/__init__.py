@@ -29,6 +29,8 @@ LCA_LAYER_CSA = 0
 LCA_LAYER_HCA = 1
 LCA_IDX_INT8 = 0
 LCA_IDX_FP4 = 1
+LCA_KV_BF16 = 0
+LCA_KV_MIXED = 1
 LCA_TOPK_HIST_READY = 1
 LCA_HYBRID_PHASES = 3
 
@@ -38,7 +40,7 @@ class LcaLayer(ctypes.Structure):
                 ("q", _vp), ("q_idx", _vp), ("k_cmp", _vp), ("v_cmp", _vp), ("k_idx", _vp),
                 ("ent_off", _vp), ("out", _vp), ("lse", _vp), ("idx", _vp), ("count", _vp),
                 ("win_k", _vp), ("win_v", _vp), ("win_off", _vp), ("win_pos0", _vp),
-                ("window", _i32), ("sink", _vp), ("idx_format", _i32)]
+                ("window", _i32), ("sink", _vp), ("idx_format", _i32), ("kv_format", _i32)]
 
 
 _SIGS = {
@@ -60,6 +62,10 @@ _SIGS = {
     "lca_csa_topk_select": (_i32, [_vp, _i64, _i32, _i32, _vp, _i32, _vp, _vp, _vp, _sz, _u32,
                                    _vp]),
     "lca_attn_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32]),
+    "lca_csa_sparse_attn_kv8": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _vp, _vp, _i32, _i32,
+                                       _i32, _f32, _i32, _vp, _vp, _vp, _sz, _vp]),
+    "lca_hca_dense_attn_kv8": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
+                                      _i32, _f32, _i32, _vp, _vp, _vp, _sz, _vp]),
     "lca_csa_sparse_attn": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _vp, _vp, _i32, _i32,
                                    _i32, _f32, _i32, _vp, _vp, _vp, _sz, _vp]),
     "lca_hca_dense_attn": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
@@ -190,6 +196,23 @@ def csa_sparse_attn(q, k_cmp, v_cmp, ent_off, q_off, batch, max_q, idx, count, k
         q.shape[-2], q.shape[-1], scale, splits, _p(out), _p(lse), _p(ws), _nb(ws), _s(stream)))
 
 
+def csa_sparse_attn_kv8(q, k_cmp, v_cmp, ent_off, q_off, batch, max_q, idx, count, k, scale, out,
+                        lse=None, ws=None, splits=0, stream=None):
+    """k_cmp / v_cmp: [entries, 192] uint8 mixed rows (dims 0..63 FP8 E4M3, 64..127 bf16)."""
+    _check("lca_csa_sparse_attn_kv8", _lib.lca_csa_sparse_attn_kv8(
+        _p(q), _p(k_cmp), _p(v_cmp), _p(ent_off), _p(q_off), batch, max_q, _p(idx), _p(count), k,
+        q.shape[-2], q.shape[-1], scale, splits, _p(out), _p(lse), _p(ws), _nb(ws), _s(stream)))
+
+
+def hca_dense_attn_kv8(q, k_cmp, v_cmp, ent_off, q_off, q_pos, batch, max_q, max_entries, m,
+                       scale, out, lse=None, ws=None, splits=0, stream=None):
+    """k_cmp / v_cmp: [entries, 192] uint8 mixed rows (dims 0..63 FP8 E4M3, 64..127 bf16)."""
+    _check("lca_hca_dense_attn_kv8", _lib.lca_hca_dense_attn_kv8(
+        _p(q), _p(k_cmp), _p(v_cmp), _p(ent_off), _p(q_off), _p(q_pos), batch, max_q,
+        max_entries, m, q.shape[-2], q.shape[-1], scale, splits, _p(out), _p(lse), _p(ws),
+        _nb(ws), _s(stream)))
+
+
 def hca_dense_attn(q, k_cmp, v_cmp, ent_off, q_off, q_pos, batch, max_q, max_entries, m, scale,
                    out, lse=None, ws=None, splits=0, stream=None):
     _check("lca_hca_dense_attn", _lib.lca_hca_dense_attn(
@@ -208,7 +231,8 @@ def make_layers(layers):
                           _p(L.get("idx")), _p(L.get("count")), _p(L.get("win_k")),
                           _p(L.get("win_v")), _p(L.get("win_off")), _p(L.get("win_pos0")),
                           int(L.get("window", 0)), _p(L.get("sink")),
-                          int(L.get("idx_format", LCA_IDX_INT8)))
+                          int(L.get("idx_format", LCA_IDX_INT8)),
+                          int(L.get("kv_format", LCA_KV_BF16)))
     return arr
 
 

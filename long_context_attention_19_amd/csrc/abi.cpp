@@ -94,6 +94,8 @@ struct HybridAttnPlan {
 HybridAttnPlan hybrid_attn_plan(const lca_layer* layers, int n_layers, int rows, int heads) {
   HybridAttnPlan p;
   if (heads % 64 != 0 || rows <= 0) return p;
+  for (int l = 0; l < n_layers; ++l)   // the persistent form reads bf16 rows only
+    if (layers[l].kv_format != LCA_KV_BF16) return p;
   const int cu = lca_device_cu_count();
   if (cu <= 0) return p;
   const int G = 2 * cu;
@@ -307,26 +309,76 @@ static int32_t attn_common(const char* name, const lca_bf16* q, const lca_bf16* 
   return LCA_OK;
 }
 
-int32_t lca_csa_sparse_attn(const lca_bf16* q, const lca_bf16* k_cmp, const lca_bf16* v_cmp,
-                            const int64_t* ent_off, const int64_t* q_off, int32_t batch,
-                            int32_t max_q, const int32_t* idx, const int32_t* count, int32_t k,
-                            int32_t heads, int32_t head_dim, float scale, int32_t splits,
-                            lca_bf16* out, float* lse, void* ws, size_t ws_bytes, void* stream) {
-  if (k <= 0) return fail(LCA_ERR_SHAPE, "csa_sparse_attn: k=%d must be positive", k);
+static int32_t sparse_attn_impl(const char* name, const lca_bf16* q, const lca_bf16* k_cmp,
+                                const lca_bf16* v_cmp, const int64_t* ent_off, const int64_t* q_off,
+                                int32_t batch, int32_t max_q, const int32_t* idx,
+                                const int32_t* count, int32_t k, int32_t heads, int32_t head_dim,
+                                float scale, int32_t splits, lca_bf16* out, float* lse, void* ws,
+                                size_t ws_bytes, void* stream, bool kv8) {
+  if (k <= 0) return fail(LCA_ERR_SHAPE, "%s: k=%d must be positive", name, k);
+  if (kv8 && heads % 64 != 0) return fail(LCA_ERR_UNSUPPORTED, "%s: heads=%d (mixed KV rows need a multiple of 64)", name, heads);
   lca::AttnArgs a;
-  int32_t st = attn_common("csa_sparse_attn", q, k_cmp, v_cmp, ent_off, q_off, batch, max_q, heads,
+  int32_t st = attn_common(name, q, k_cmp, v_cmp, ent_off, q_off, batch, max_q, heads,
                            head_dim, scale, splits, out, ws, ws_bytes, a);
   if (st == LCA_OK + 1) return ok();
   if (st != LCA_OK) return st;
-  if (!idx || !count) return fail(LCA_ERR_NULL, "csa_sparse_attn: idx / count NULL");
+  if (!idx || !count) return fail(LCA_ERR_NULL, "%s: idx / count NULL", name);
   a.idx = idx;
   a.count = count;
   a.k = k;
   a.max_n = k;
   a.ratio = 1;
   a.lse = lse;
+  a.kv8 = kv8 ? 1 : 0;
   return hip_status(lca::launch_attention(lca::attn_batch1(a), batch, (hipStream_t)stream),
-                    "csa_sparse_attn launch");
+                    "sparse attention launch");
+}
+
+int32_t lca_csa_sparse_attn(const lca_bf16* q, const lca_bf16* k_cmp, const lca_bf16* v_cmp,
+                            const int64_t* ent_off, const int64_t* q_off, int32_t batch,
+                            int32_t max_q, const int32_t* idx, const int32_t* count, int32_t k,
+                            int32_t heads, int32_t head_dim, float scale, int32_t splits,
+                            lca_bf16* out, float* lse, void* ws, size_t ws_bytes, void* stream) {
+  return sparse_attn_impl("csa_sparse_attn", q, k_cmp, v_cmp, ent_off, q_off, batch, max_q, idx,
+                          count, k, heads, head_dim, scale, splits, out, lse, ws, ws_bytes, stream,
+                          false);
+}
+
+int32_t lca_csa_sparse_attn_kv8(const lca_bf16* q, const uint8_t* k_cmp, const uint8_t* v_cmp,
+                                const int64_t* ent_off, const int64_t* q_off, int32_t batch,
+                                int32_t max_q, const int32_t* idx, const int32_t* count, int32_t k,
+                                int32_t heads, int32_t head_dim, float scale, int32_t splits,
+                                lca_bf16* out, float* lse, void* ws, size_t ws_bytes,
+                                void* stream) {
+  return sparse_attn_impl("csa_sparse_attn_kv8", q, reinterpret_cast<const lca_bf16*>(k_cmp),
+                          reinterpret_cast<const lca_bf16*>(v_cmp), ent_off, q_off, batch, max_q,
+                          idx, count, k, heads, head_dim, scale, splits, out, lse, ws, ws_bytes,
+                          stream, true);
+}
+
+static int32_t dense_attn_impl(const char* name, const lca_bf16* q, const lca_bf16* k_cmp,
+                               const lca_bf16* v_cmp, const int64_t* ent_off, const int64_t* q_off,
+                               const int64_t* q_pos, int32_t batch, int32_t max_q,
+                               int32_t max_entries, int32_t m, int32_t heads, int32_t head_dim,
+                               float scale, int32_t splits, lca_bf16* out, float* lse, void* ws,
+                               size_t ws_bytes, void* stream, bool kv8) {
+  if (kv8 && heads % 64 != 0) return fail(LCA_ERR_UNSUPPORTED, "%s: heads=%d (mixed KV rows need a multiple of 64)", name, heads);
+  if (m < 1) return fail(LCA_ERR_SHAPE, "%s: ratio m=%d < 1", name, m);
+  if (max_entries < 0) return fail(LCA_ERR_SHAPE, "%s: negative max_entries", name);
+  if (max_entries > lca::ATTN_MAX_SEQ) return fail(LCA_ERR_UNSUPPORTED, "%s: max_entries=%d above %d", name, max_entries, lca::ATTN_MAX_SEQ);
+  lca::AttnArgs a;
+  int32_t st = attn_common(name, q, k_cmp, v_cmp, ent_off, q_off, batch, max_q, heads,
+                           head_dim, scale, splits, out, ws, ws_bytes, a);
+  if (st == LCA_OK + 1) return ok();
+  if (st != LCA_OK) return st;
+  if (!q_pos) return fail(LCA_ERR_NULL, "%s: q_pos NULL", name);
+  a.q_pos = q_pos;
+  a.ratio = m;
+  a.max_n = max_entries;
+  a.lse = lse;
+  a.kv8 = kv8 ? 1 : 0;
+  return hip_status(lca::launch_attention(lca::attn_batch1(a), batch, (hipStream_t)stream),
+                    "hca_dense_attn launch");
 }
 
 int32_t lca_hca_dense_attn(const lca_bf16* q, const lca_bf16* k_cmp, const lca_bf16* v_cmp,
@@ -334,21 +386,20 @@ int32_t lca_hca_dense_attn(const lca_bf16* q, const lca_bf16* k_cmp, const lca_b
                            int32_t batch, int32_t max_q, int32_t max_entries, int32_t m,
                            int32_t heads, int32_t head_dim, float scale, int32_t splits,
                            lca_bf16* out, float* lse, void* ws, size_t ws_bytes, void* stream) {
-  if (m < 1) return fail(LCA_ERR_SHAPE, "hca_dense_attn: ratio m=%d < 1", m);
-  if (max_entries < 0) return fail(LCA_ERR_SHAPE, "hca_dense_attn: negative max_entries");
-  if (max_entries > lca::ATTN_MAX_SEQ) return fail(LCA_ERR_UNSUPPORTED, "hca_dense_attn: max_entries=%d above %d", max_entries, lca::ATTN_MAX_SEQ);
-  lca::AttnArgs a;
-  int32_t st = attn_common("hca_dense_attn", q, k_cmp, v_cmp, ent_off, q_off, batch, max_q, heads,
-                           head_dim, scale, splits, out, ws, ws_bytes, a);
-  if (st == LCA_OK + 1) return ok();
-  if (st != LCA_OK) return st;
-  if (!q_pos) return fail(LCA_ERR_NULL, "hca_dense_attn: q_pos NULL");
-  a.q_pos = q_pos;
-  a.ratio = m;
-  a.max_n = max_entries;
-  a.lse = lse;
-  return hip_status(lca::launch_attention(lca::attn_batch1(a), batch, (hipStream_t)stream),
-                    "hca_dense_attn launch");
+  return dense_attn_impl("hca_dense_attn", q, k_cmp, v_cmp, ent_off, q_off, q_pos, batch, max_q,
+                         max_entries, m, heads, head_dim, scale, splits, out, lse, ws, ws_bytes,
+                         stream, false);
+}
+
+int32_t lca_hca_dense_attn_kv8(const lca_bf16* q, const uint8_t* k_cmp, const uint8_t* v_cmp,
+                               const int64_t* ent_off, const int64_t* q_off, const int64_t* q_pos,
+                               int32_t batch, int32_t max_q, int32_t max_entries, int32_t m,
+                               int32_t heads, int32_t head_dim, float scale, int32_t splits,
+                               lca_bf16* out, float* lse, void* ws, size_t ws_bytes, void* stream) {
+  return dense_attn_impl("hca_dense_attn_kv8", q, reinterpret_cast<const lca_bf16*>(k_cmp),
+                         reinterpret_cast<const lca_bf16*>(v_cmp), ent_off, q_off, q_pos, batch,
+                         max_q, max_entries, m, heads, head_dim, scale, splits, out, lse, ws,
+                         ws_bytes, stream, true);
 }
 
 // ------------------------------------------------------------------ sliding window
@@ -457,6 +508,8 @@ int32_t lca_hybrid_layer_step(const lca_layer* layers, int32_t n_layers, const i
     if (!heads_supported(heads)) return fail(LCA_ERR_UNSUPPORTED, "hybrid_layer_step: heads=%d", heads);
     if (!al16(L.q) || !al16(L.k_cmp) || !al16(L.v_cmp) || !al16(L.out)) return fail(LCA_ERR_ALIGN, "hybrid_layer_step: layer %d tensors not aligned", l);
     if (L.window < 0 || L.window > lca::ATTN_MAX_SEQ) return fail(LCA_ERR_SHAPE, "hybrid_layer_step: layer %d window=%d", l, L.window);
+    if (L.kv_format != LCA_KV_BF16 && L.kv_format != LCA_KV_MIXED) return fail(LCA_ERR_SHAPE, "hybrid_layer_step: layer %d kv_format=%d", l, L.kv_format);
+    if (L.kv_format == LCA_KV_MIXED && heads % 64 != 0) return fail(LCA_ERR_UNSUPPORTED, "hybrid_layer_step: layer %d mixed KV rows need heads a multiple of 64", l);
     if (L.window > 0) {
       if (!L.win_k || !L.win_v || !L.win_off || !L.win_pos0 || !L.lse) return fail(LCA_ERR_NULL, "hybrid_layer_step: layer %d window buffers / lse NULL", l);
       if (!al16(L.win_k) || !al16(L.win_v)) return fail(LCA_ERR_ALIGN, "hybrid_layer_step: layer %d window buffers not aligned", l);
@@ -490,6 +543,7 @@ int32_t lca_hybrid_layer_step(const lca_layer* layers, int32_t n_layers, const i
     a.out = L.out;
     a.lse = L.lse;
     a.sink = L.window > 0 ? nullptr : L.sink;   // else the window branch writes last
+    a.kv8 = L.kv_format == LCA_KV_MIXED ? 1 : 0;
     if (L.kind == LCA_LAYER_CSA) {
       const int ld = std::max((L.max_entries + 3) & ~3, 4);
       int32_t* scores = reinterpret_cast<int32_t*>(p);
@@ -580,14 +634,20 @@ int32_t lca_hybrid_layer_step(const lca_layer* layers, int32_t n_layers, const i
     lca::attn_persist_carve(p, plan.G, plan.items, pp);
     pp.rows = rows;
   }
-  for (size_t c0 = 0; c0 < all.size() && e == hipSuccess; c0 += lca::MAX_BATCH_LAYERS) {
-    const int n = (int)std::min<size_t>(lca::MAX_BATCH_LAYERS, all.size() - c0);
-    lca::AttnBatch ab{};
-    ab.n = n;
-    ab.head_blocks = hb;
-    for (int i = 0; i < n; ++i) ab.a[i] = all[c0 + i];
-    e = plan.persist ? lca::launch_attention_persist(ab, pp, caller)
-                     : lca::launch_attention(ab, batch, caller);
+  // launches of up to 8 layers, layers with bf16 rows and with mixed rows apart
+  for (int f = 0; f < 2 && e == hipSuccess; ++f) {
+    std::vector<lca::AttnArgs> fa;
+    for (const lca::AttnArgs& x : all)
+      if (x.kv8 == f) fa.push_back(x);
+    for (size_t c0 = 0; c0 < fa.size() && e == hipSuccess; c0 += lca::MAX_BATCH_LAYERS) {
+      const int n = (int)std::min<size_t>(lca::MAX_BATCH_LAYERS, fa.size() - c0);
+      lca::AttnBatch ab{};
+      ab.n = n;
+      ab.head_blocks = hb;
+      for (int i = 0; i < n; ++i) ab.a[i] = fa[c0 + i];
+      e = plan.persist ? lca::launch_attention_persist(ab, pp, caller)
+                       : lca::launch_attention(ab, batch, caller);
+    }
   }
   // sliding-window branches, merged into each layer's result (one launch per 8 layers)
   std::vector<lca::AttnArgs> win_a;

@@ -130,10 +130,23 @@ __device__ __forceinline__ bool row_info(const AttnArgs& a, int supertile, RowIn
 constexpr int AT_IDS = 2048;       // entry ids staged in LDS per chunk (sparse form)
 
 // MODE: 0 dense (HCA), 1 sparse (CSA), 2 either, per layer of the launch
-template <int ST, int NB, int MODE>
+template <int ST, int NB, int MODE, int KV>
 struct AttnDmaSmem {
   alignas(256) i32x4 k[NB][ST * 16];   // 256-byte aligned: attn_stage XORs slot bits
   alignas(256) i32x4 v[NB][ST * 16];
+  int ids[MODE != 0 ? AT_IDS : 1];
+};
+// Mixed KV rows (dims 0..63 FP8, 64..127 bf16): per stage buffer the FP8 halves as
+// fetched (64 B rows) and the bf16 halves (128 B rows, slots permuted as the bf16
+// tiles); the FP8 halves are converted once per stage into one bf16 tile (128 B rows).
+template <int ST, int NB, int MODE>
+struct AttnDmaSmem<ST, NB, MODE, 1> {
+  alignas(256) i32x4 k8[NB][ST * 4];
+  alignas(256) i32x4 v8[NB][ST * 4];
+  alignas(256) i32x4 khi[NB][ST * 8];
+  alignas(256) i32x4 vhi[NB][ST * 8];
+  alignas(256) i32x4 klo[ST * 8];
+  alignas(256) i32x4 vlo[ST * 8];
   int ids[MODE != 0 ? AT_IDS : 1];
 };
 
@@ -323,6 +336,108 @@ __device__ __forceinline__ void attn_stage(const i32x4* kb, const char* vbase, i
     }
 }
 
+// Mixed KV rows: 128-byte half rows (dims 0..63 converted from FP8 in `lo`, dims
+// 64..127 as fetched in `hi`, both bf16).  Slot permutations of a half row (8 slots of
+// 16 bytes): K row r keeps dims 8c .. 8c+7 of its half in slot c ^ ((r >> 1) & 7), so
+// the 16 rows of a K-fragment read cover both row parities x 8 slots (every bank once);
+// V row r in slot c ^ 2((r >> 1) & 3), so the 8 rows x 32 bytes of a transposed read's
+// half-wave land on distinct banks.
+__device__ __forceinline__ uint32_t kv8_kslot(int r, int c) { return (uint32_t)(c ^ ((r >> 1) & 7)); }
+__device__ __forceinline__ uint32_t kv8_vslot(int r, int c) { return (uint32_t)(c ^ (((r >> 1) & 3) << 1)); }
+
+// attn_stage over mixed KV rows: the same arithmetic, with K fragments ks = 0, 1 and
+// V^T fragments db = 0..3 read from the `lo` tiles and the others from the `hi` tiles.
+template <int SUB>
+__device__ __forceinline__ void attn_stage_kv8(const i32x4* klo, const i32x4* khi,
+                                               const i32x4* vlo, const i32x4* vhi, int el_base,
+                                               int tb, int e1, const bf16x8 (&qf)[4],
+                                               f32x4 (&o)[8], float& m_run, float& l_run,
+                                               float scale_log2, int l16, int g) {
+  typedef __attribute__((address_space(3))) const i32x4 lds_i32x4;
+  typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+  // K row el_base + 32 sub + 16 rb + l16: (row >> 1) & 7 = (l16 >> 1) & 7
+  const uint32_t koff = (uint32_t)(el_base + l16) * 128u + ((uint32_t)(g ^ ((l16 >> 1) & 7)) << 4);
+  const uint32_t bk[2] = {lds_addr(klo) + koff, lds_addr(khi) + koff};
+  f32x4 sacc[SUB][2];
+#pragma unroll
+  for (int sub = 0; sub < SUB; ++sub)
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) sacc[sub][rb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) {
+    const uint32_t ak = bk[ks >> 1] ^ ((uint32_t)(ks & 1) << 6);
+#pragma unroll
+    for (int sub = 0; sub < SUB; ++sub)
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb) {
+        const bf16x8 kf = __builtin_bit_cast(bf16x8, *(lds_i32x4*)(size_t)(ak + (sub * 32 + rb * 16) * 128));
+        sacc[sub][rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[ks], sacc[sub][rb], 0, 0, 0);
+      }
+  }
+  float x[SUB * 8];
+#pragma unroll
+  for (int sub = 0; sub < SUB; ++sub)
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) x[sub * 8 + rb * 4 + i] = sacc[sub][rb][i];
+  const int ev0 = tb + el_base;
+  if (ev0 + 32 * SUB > e1) {
+#pragma unroll
+    for (int sub = 0; sub < SUB; ++sub)
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (ev0 + sub * 32 + rb * 16 + 4 * g + i >= e1) x[sub * 8 + rb * 4 + i] = -INFINITY;
+  }
+  float mx = x[0];
+#pragma unroll
+  for (int i = 1; i < SUB * 8; ++i) mx = __builtin_elementwise_maximum(mx, x[i]);
+  mx = lanes4_max(mx) * scale_log2;
+  const bool raise = mx > m_run + AT_MAX_SLACK;
+  if (__any(raise)) {
+    const float m_new = raise ? mx : m_run;
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+#pragma unroll
+    for (int db = 0; db < 8; ++db) o[db] *= alpha;
+    l_run *= alpha;
+    m_run = m_new;
+  }
+  const float m_use = m_run;
+  bf16x8 pf[SUB];
+#pragma unroll
+  for (int sub = 0; sub < SUB; ++sub)
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      pf[sub][i] = (__bf16)__builtin_amdgcn_exp2f(fmaf(x[sub * 8 + i], scale_log2, -m_use));
+  const bf16x2 one2 = {(__bf16)1.f, (__bf16)1.f};
+  float psum = l_run;
+#pragma unroll
+  for (int sub = 0; sub < SUB; ++sub)
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      psum = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pf[sub][2 * i], pf[sub][2 * i + 1]}, one2, psum,
+                                             false);
+  l_run = psum;
+  // V row R = el_base + 32 sub + 16 hh + 4g + (l16 >> 2): (R >> 1) & 3 = (2g + (l16 >> 3)) & 3
+  const int m2 = (2 * g + (l16 >> 3)) & 3;
+  const int q = l16 & 3;
+  const uint32_t voff = (uint32_t)(el_base + 4 * g + (l16 >> 2)) * 128u + ((uint32_t)m2 << 5) +
+                        ((uint32_t)(q >> 1) << 4) + (uint32_t)(q & 1) * 8u;
+  const uint32_t bv[2] = {lds_addr(vlo) + voff, lds_addr(vhi) + voff};
+#pragma unroll
+  for (int sub = 0; sub < SUB; ++sub)
+#pragma unroll
+    for (int db = 0; db < 8; ++db) {
+      const uint32_t av = (bv[db >> 2] ^ ((uint32_t)(db & 3) << 5)) + (uint32_t)sub * 32u * 128u;
+      const bf16x4 h0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(size_t)av);
+      const bf16x4 h1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(size_t)(av + 16 * 128));
+      const bf16x8 vf = {h0[0], h0[1], h0[2], h0[3], h1[0], h1[1], h1[2], h1[3]};
+      o[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf[sub], o[db], 0, 0, 0);
+    }
+}
+
 // The K and V row pieces of one DMA instruction: lane (r, slot l16) of instruction
 // u fetches row r's 16-byte chunk l16 ^ (r & 15) for K and l16 ^ 2(r & 7) for V.
 __device__ __forceinline__ void attn_issue_rows(const char* kseq, const char* vseq,
@@ -335,8 +450,10 @@ __device__ __forceinline__ void attn_issue_rows(const char* kseq, const char* vs
 }
 
 // ES entry sub-groups of waves; each wave takes SUB consecutive 32-entry sub-tiles of
-// every stage, so a stage covers 32*ES*SUB entries.
-template <int ES, int SUB, int NB, int MODE>
+// every stage, so a stage covers 32*ES*SUB entries.  KV = 1: mixed KV rows (dims
+// 0..63 FP8 E4M3, 64..127 bf16, 192 bytes); each stage's FP8 halves are converted to
+// bf16 in LDS by the whole work-group before the waves use the stage.
+template <int ES, int SUB, int NB, int MODE, int KV>
 __global__ __launch_bounds__(AT_NT) void attn_dma_kernel(AttnBatch ab) {
   const AttnArgs& a = ab.a[blockIdx.z / ab.head_blocks];   // grid z = layer x head block
   const bool sparse = MODE == 2 ? a.idx != nullptr : MODE == 1;   // uniform
@@ -344,9 +461,13 @@ __global__ __launch_bounds__(AT_NT) void attn_dma_kernel(AttnBatch ab) {
   constexpr int HG = 4 / ES;                    // head groups of 16 per work-group
   constexpr int NU = ST / 16;                   // DMA instructions per wave per matrix
   static_assert(NU >= 1 && NU <= 8 && AT_IDS % ST == 0, "stage size");
+  static_assert(KV == 0 || (ES == 1 && ST == 64), "mixed KV rows: 64-entry stages, 64 heads");
+  // DMA instructions per wave per stage: bf16 rows 2 x NU; mixed rows, per matrix, one
+  // for the 16 FP8 half rows of the wave and two for its 16 bf16 half rows
+  constexpr int DPS = KV ? 6 : 2 * NU;
   constexpr int D = NB - 1;                     // stages in flight ahead of the one in use
-  static_assert(NB >= 2 && D * 2 * NU < 64, "pipeline depth");
-  __shared__ AttnDmaSmem<ST, NB, MODE> sm;
+  static_assert(NB >= 2 && D * DPS < 64, "pipeline depth");
+  __shared__ AttnDmaSmem<ST, NB, MODE, KV> sm;
 
   // The loads that set up a work-group form a short dependency chain; the query,
   // the first entry ids and the first stages' rows are issued as soon as their
@@ -405,10 +526,17 @@ __global__ __launch_bounds__(AT_NT) void attn_dma_kernel(AttnBatch ab) {
   const int wrow0 = w * (ST / 4);
   const int my_row = lane >> 4;
   const int id_max = (int)min(n_seq, (int64_t)ATTN_MAX_SEQ) - 1;
-  const char* kseq = reinterpret_cast<const char*>(a.kc + e_base * HD);
-  const char* vseq = reinterpret_cast<const char*>(a.vc + e_base * HD);
-  const uint32_t k_lds0 = lds_addr(&sm.k[0][wrow0 * 16]);
-  const uint32_t v_lds0 = lds_addr(&sm.v[0][wrow0 * 16]);
+  const int64_t row_bytes = KV ? KV8_ROW_BYTES : HD * 2;
+  const char* kseq = reinterpret_cast<const char*>(a.kc) + e_base * row_bytes;
+  const char* vseq = reinterpret_cast<const char*>(a.vc) + e_base * row_bytes;
+  uint32_t k_lds0, v_lds0;
+  if constexpr (KV) {   // FP8 half rows of this wave; the bf16 half rows are offset below
+    k_lds0 = lds_addr(&sm.k8[0][wrow0 * 4]);
+    v_lds0 = lds_addr(&sm.v8[0][wrow0 * 4]);
+  } else {
+    k_lds0 = lds_addr(&sm.k[0][wrow0 * 16]);
+    v_lds0 = lds_addr(&sm.v[0][wrow0 * 16]);
+  }
   constexpr uint32_t BUF_BYTES = ST * 256;
 
   // the piece as far as it is known before the entry count: exact when the count is
@@ -421,15 +549,37 @@ __global__ __launch_bounds__(AT_NT) void attn_dma_kernel(AttnBatch ab) {
 
   // issue the DMA of the stage starting at entry tb into buffer buf; rows past
   // e_last repeat row e_last (cached, and masked in the softmax)
+  auto row_id = [&](int r, int tb, int cbase, int e_last) __attribute__((always_inline)) {
+    const int e = min(tb + r, e_last);
+    const int id = (MODE != 0 && sparse) ? sm.ids[e - cbase] : e;
+    return (uint32_t)min(max(id, 0), id_max);
+  };
   auto issue = [&](int buf, int tb, int cbase, int e_last) __attribute__((always_inline)) {
+    if constexpr (KV) {
+      // FP8 halves: 16 rows of 64 bytes, lane -> (row lane / 4, chunk lane % 4)
+      {
+        const int r = wrow0 + (lane >> 2);
+        const uint32_t off = row_id(r, tb, cbase, e_last) * KV8_ROW_BYTES + (uint32_t)(lane & 3) * 16u;
+        dma16(kseq, off, k_lds0 + buf * (ST * 64));
+        dma16(vseq, off, v_lds0 + buf * (ST * 64));
+      }
+      // bf16 halves: 2 x 8 rows of 128 bytes, lane -> (row lane / 8, slot lane % 8)
+      const uint32_t khi0 = lds_addr(&sm.khi[buf][0]), vhi0 = lds_addr(&sm.vhi[buf][0]);
 #pragma unroll
-    for (int u = 0; u < NU; ++u) {
-      const int r = wrow0 + 4 * u + my_row;
-      const int e = min(tb + r, e_last);
-      int id = (MODE != 0 && sparse) ? sm.ids[e - cbase] : e;
-      id = min(max(id, 0), id_max);
-      attn_issue_rows(kseq, vseq, (uint32_t)id * 256u, r, l16, k_lds0 + buf * BUF_BYTES + u * 1024,
-                      v_lds0 + buf * BUF_BYTES + u * 1024);
+      for (int u = 0; u < 2; ++u) {
+        const int r = wrow0 + 8 * u + (lane >> 3);
+        const uint32_t base = row_id(r, tb, cbase, e_last) * KV8_ROW_BYTES + 64u;
+        const int sl = lane & 7;
+        dma16(kseq, base + kv8_kslot(r, sl) * 16u, khi0 + (uint32_t)(wrow0 + 8 * u) * 128u);
+        dma16(vseq, base + kv8_vslot(r, sl) * 16u, vhi0 + (uint32_t)(wrow0 + 8 * u) * 128u);
+      }
+    } else {
+#pragma unroll
+      for (int u = 0; u < NU; ++u) {
+        const int r = wrow0 + 4 * u + my_row;
+        attn_issue_rows(kseq, vseq, row_id(r, tb, cbase, e_last) * 256u, r, l16,
+                        k_lds0 + buf * BUF_BYTES + u * 1024, v_lds0 + buf * BUF_BYTES + u * 1024);
+      }
     }
   };
   // copy the entry ids [cbase, cend) to LDS (sparse form; nothing else in flight)
@@ -482,9 +632,37 @@ __global__ __launch_bounds__(AT_NT) void attn_dma_kernel(AttnBatch ab) {
   const int e1 = min(e0 + per, n);
 
   auto compute = [&](int buf, int tb) __attribute__((always_inline)) {
-    if (tb + es * SUB * 32 < e1)   // this wave's block has a valid entry
-      attn_stage<SUB>(sm.k[buf], reinterpret_cast<const char*>(sm.v[buf]), es * SUB * 32, tb, e1,
-                      qf, o, m_run, l_run, scale_log2, l16, g);
+    if constexpr (KV) {
+      // the stage's FP8 halves to bf16, once for all waves: thread t converts the 16
+      // dims 16 (t % 4) .. of K and V row t / 4 into two slots of the lo tiles
+      const int r = t >> 2, ch = t & 3;
+      const i32x4 k8 = sm.k8[buf][r * 4 + ch];
+      const i32x4 v8 = sm.v8[buf][r * 4 + ch];
+      i32x4 klo[2], vlo[2];
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int d = 0; d < 2; ++d) {
+          const int word = 2 * h + d;
+          klo[h][2 * d] = __builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(k8[word], 1.f, false));
+          klo[h][2 * d + 1] = __builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(k8[word], 1.f, true));
+          vlo[h][2 * d] = __builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v8[word], 1.f, false));
+          vlo[h][2 * d + 1] = __builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v8[word], 1.f, true));
+        }
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        sm.klo[r * 8 + kv8_kslot(r, 2 * ch + h)] = klo[h];
+        sm.vlo[r * 8 + kv8_vslot(r, 2 * ch + h)] = vlo[h];
+      }
+      lds_barrier();
+      if (tb < e1)
+        attn_stage_kv8<SUB>(sm.klo, sm.khi[buf], sm.vlo, sm.vhi[buf], 0, tb, e1, qf, o, m_run,
+                            l_run, scale_log2, l16, g);
+    } else {
+      if (tb + es * SUB * 32 < e1)   // this wave's block has a valid entry
+        attn_stage<SUB>(sm.k[buf], reinterpret_cast<const char*>(sm.v[buf]), es * SUB * 32, tb,
+                        e1, qf, o, m_run, l_run, scale_log2, l16, g);
+    }
   };
 
   // Per stage: wait for this stage's DMA (the later stages' may stay outstanding),
@@ -502,9 +680,9 @@ __global__ __launch_bounds__(AT_NT) void attn_dma_kernel(AttnBatch ab) {
     int buf = 0;
     for (int j = 0; j < nst; ++j) {
       const int ahead = issued - 1 - j;   // stages issued after stage j
-      if (NB > 3 && ahead >= 3) wait_vm<(NB > 3 ? 3 : 0) * 2 * NU>();
-      else if (NB > 2 && ahead == 2) wait_vm<(NB > 2 ? 2 : 0) * 2 * NU>();
-      else if (ahead == 1) wait_vm<2 * NU>();
+      if (NB > 3 && ahead >= 3) wait_vm<(NB > 3 ? 3 : 0) * DPS>();
+      else if (NB > 2 && ahead == 2) wait_vm<(NB > 2 ? 2 : 0) * DPS>();
+      else if (ahead == 1) wait_vm<DPS>();
       else wait_vm<0>();
       lds_barrier();
       compute(buf, cbase + j * ST);
@@ -1088,21 +1266,27 @@ hipError_t launch_attention(const AttnBatch& ab, int batch, hipStream_t st) {
   for (int l = 0; l < ab.n; ++l) n_sparse += ab.a[l].idx != nullptr;
   const int mode = n_sparse == 0 ? 0 : n_sparse == ab.n ? 1 : 2;
   int st_size;
-#define LCA_ATTN_LAUNCH(ES, SUB, NB)                                                          \
+#define LCA_ATTN_LAUNCH_KV(ES, SUB, NB, KV)                                                   \
   do {                                                                                        \
-    if (mode == 0) hipLaunchKernelGGL((attn_dma_kernel<ES, SUB, NB, 0>), grid, dim3(AT_NT), 0, st, ab); \
-    else if (mode == 1) hipLaunchKernelGGL((attn_dma_kernel<ES, SUB, NB, 1>), grid, dim3(AT_NT), 0, st, ab); \
-    else hipLaunchKernelGGL((attn_dma_kernel<ES, SUB, NB, 2>), grid, dim3(AT_NT), 0, st, ab); \
+    if (mode == 0) hipLaunchKernelGGL((attn_dma_kernel<ES, SUB, NB, 0, KV>), grid, dim3(AT_NT), 0, st, ab); \
+    else if (mode == 1) hipLaunchKernelGGL((attn_dma_kernel<ES, SUB, NB, 1, KV>), grid, dim3(AT_NT), 0, st, ab); \
+    else hipLaunchKernelGGL((attn_dma_kernel<ES, SUB, NB, 2, KV>), grid, dim3(AT_NT), 0, st, ab); \
     st_size = 32 * ES * SUB;                                                                  \
   } while (0)
+#define LCA_ATTN_LAUNCH(ES, SUB, NB) LCA_ATTN_LAUNCH_KV(ES, SUB, NB, 0)
+  // mixed KV rows (every layer of the batch; 64-head blocks): 64-entry stages
   // 64 heads: 64-entry stages, except for sparse prefill-sized query batches, which
   // run 32-entry stages (more groups resident per CU; measured 4 % faster there,
   // slower for dense rows)
-  if (hg == 4 && mode == 1 && a0.max_q >= 16) LCA_ATTN_LAUNCH(1, 1, 2);
+  if (a0.kv8) {
+    if (hg != 4) return hipErrorInvalidValue;
+    LCA_ATTN_LAUNCH_KV(1, 2, 2, 1);
+  } else if (hg == 4 && mode == 1 && a0.max_q >= 16) LCA_ATTN_LAUNCH(1, 1, 2);
   else if (hg == 4) LCA_ATTN_LAUNCH(1, AT_SUB64, AT_NB64);
   else if (hg == 2) LCA_ATTN_LAUNCH(2, 1, 2);
   else LCA_ATTN_LAUNCH(4, 1, 2);
 #undef LCA_ATTN_LAUNCH
+#undef LCA_ATTN_LAUNCH_KV
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || max_splits <= 1) return e;
   dim3 cgrid((unsigned)((a0.heads + CMB_HEADS - 1) / CMB_HEADS), rows_grid, (unsigned)ab.n);

@@ -121,7 +121,10 @@ struct AttnArgs {
   // Attention sink: per-head logits (natural log) folded into the final result by
   // whichever kernel writes it; nullptr: none.
   const float* sink;
+  // kc / vc hold mixed rows of KV8_ROW_BYTES: dims 0..63 FP8 E4M3, dims 64..127 bf16
+  int32_t kv8;
 };
+constexpr int KV8_ROW_BYTES = 192;
 // Layers of one attention launch share heads, splits and max_q.
 hipError_t launch_attn_sink(uint16_t* out, float* lse, const float* sink, int64_t rows, int heads,
                             hipStream_t st);

@@ -15,10 +15,11 @@ from __future__ import annotations
 
 import torch
 
-from . import (LCA_IDX_FP4, LCA_IDX_INT8, LCA_LAYER_CSA, LCA_LAYER_HCA, attn_workspace_bytes,
-               csa_index_score, csa_index_score_fp4, csa_index_select, csa_sparse_attn,
-               csa_topk_select, csa_topk_workspace_bytes, hca_dense_attn, hybrid_layer_step,
-               hybrid_workspace_bytes, make_layers, workspace)
+from . import (LCA_IDX_FP4, LCA_IDX_INT8, LCA_KV_BF16, LCA_KV_MIXED, LCA_LAYER_CSA, LCA_LAYER_HCA,
+               attn_workspace_bytes, csa_index_score, csa_index_score_fp4, csa_index_select,
+               csa_sparse_attn, csa_sparse_attn_kv8, csa_topk_select, csa_topk_workspace_bytes,
+               hca_dense_attn, hca_dense_attn_kv8, hybrid_layer_step, hybrid_workspace_bytes,
+               make_layers, workspace)
 
 
 SELECT_MIN_Q = 16   # query tokens per sequence from which csa_index_select applies
@@ -31,15 +32,16 @@ def _round4(n: int) -> int:
 class CsaStep:
     """fused: None picks csa_index_select when max_q >= 16; True / False force it
     on / off (the two-call path materialises the scores in self.scores).  fp4: the
-    indexer query / keys are packed FP4 codes (csa_index_score_fp4, never fused)."""
+    indexer query / keys are packed FP4 codes (csa_index_score_fp4, never fused); kv8: the
+    cache holds mixed FP8 / bf16 rows (csa_sparse_attn_kv8)."""
 
     def __init__(self, batch, max_q, max_entries, heads, topk, c, device="cuda", splits=0,
-                 fused=None, fp4=False):
+                 fused=None, fp4=False, kv8=False):
         self.batch, self.max_q, self.max_entries = batch, max_q, max_entries
         self.heads, self.topk, self.c, self.splits = heads, topk, c, splits
         rows = batch * max_q
         self.rows = rows
-        self.fp4 = fp4
+        self.fp4, self.kv8 = fp4, kv8
         self.fused = False if fp4 else (max_q >= SELECT_MIN_Q) if fused is None else fused
         self.n_vis = torch.empty(rows, dtype=torch.int32, device=device)
         self.idx = torch.empty(rows, topk, dtype=torch.int32, device=device)
@@ -63,9 +65,9 @@ class CsaStep:
                         self.count, self.tws, hist_ready=True, stream=stream)
 
     def attend(self, q, k_cmp, v_cmp, ent_off, q_off, scale, out, lse=None, stream=None):
-        csa_sparse_attn(q, k_cmp, v_cmp, ent_off, q_off, self.batch, self.max_q, self.idx,
-                        self.count, self.topk, scale, out, lse, ws=self.aws, splits=self.splits,
-                        stream=stream)
+        attn = csa_sparse_attn_kv8 if self.kv8 else csa_sparse_attn
+        attn(q, k_cmp, v_cmp, ent_off, q_off, self.batch, self.max_q, self.idx, self.count,
+             self.topk, scale, out, lse, ws=self.aws, splits=self.splits, stream=stream)
 
     def run(self, q, q_idx, q_off, q_pos, k_idx, k_cmp, v_cmp, ent_off, scale, out, lse=None,
             stream=None):
@@ -74,23 +76,25 @@ class CsaStep:
 
 
 class HcaStep:
-    def __init__(self, batch, max_q, max_entries, heads, m, device="cuda", splits=0):
+    """kv8: the cache holds mixed rows (hca_dense_attn_kv8)."""
+
+    def __init__(self, batch, max_q, max_entries, heads, m, device="cuda", splits=0, kv8=False):
         self.batch, self.max_q, self.max_entries, self.heads, self.m = batch, max_q, max_entries, heads, m
-        self.splits = splits
+        self.splits, self.kv8 = splits, kv8
         self.aws = workspace(attn_workspace_bytes(batch * max_q, heads, max_q, splits), device)
 
     def run(self, q, k_cmp, v_cmp, ent_off, q_off, q_pos, scale, out, lse=None, stream=None):
-        hca_dense_attn(q, k_cmp, v_cmp, ent_off, q_off, q_pos, self.batch, self.max_q,
-                       self.max_entries, self.m, scale, out, lse, ws=self.aws,
-                       splits=self.splits, stream=stream)
+        attn = hca_dense_attn_kv8 if self.kv8 else hca_dense_attn
+        attn(q, k_cmp, v_cmp, ent_off, q_off, q_pos, self.batch, self.max_q, self.max_entries,
+             self.m, scale, out, lse, ws=self.aws, splits=self.splits, stream=stream)
 
 
 class HybridStep:
     """layers: dicts with kind, ratio, topk, max_entries and the layer's tensors
     (q, q_idx, k_cmp, v_cmp, k_idx, ent_off, out, lse), optionally a sliding window
     (win_k, win_v, win_off, win_pos0, window), per-head sink logits (sink) and, for CSA
-    layers, idx_format (LCA_IDX_FP4: packed FP4 indexer codes); idx / count of CSA layers
-    are allocated here when absent."""
+    layers, idx_format (LCA_IDX_FP4: packed FP4 indexer codes), and kv_format (LCA_KV_MIXED:
+    mixed FP8 / bf16 cache rows); idx / count of CSA layers are allocated here when absent."""
 
     def __init__(self, layers, batch, max_q, heads, device="cuda"):
         rows = batch * max_q
@@ -111,4 +115,4 @@ class HybridStep:
 
 
 __all__ = ["CsaStep", "HcaStep", "HybridStep", "LCA_LAYER_CSA", "LCA_LAYER_HCA", "LCA_IDX_INT8",
-           "LCA_IDX_FP4"]
+           "LCA_IDX_FP4", "LCA_KV_BF16", "LCA_KV_MIXED"]

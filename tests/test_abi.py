@@ -30,13 +30,14 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_version_and_struct_layout():
-    assert lca.abi_version() == 4
+    assert lca.abi_version() == 5
     # 4 int32, 10 pointers, 4 window pointers, int32 window (+4 padding), sink pointer,
-    # int32 idx_format (+4 padding)
+    # int32 idx_format, int32 kv_format
     assert ctypes.sizeof(lca.LcaLayer) == 16 + 10 * 8 + 4 * 8 + 8 + 8 + 8
     assert lca.LcaLayer.window.offset == 16 + 14 * 8
     assert lca.LcaLayer.sink.offset == 16 + 14 * 8 + 8
     assert lca.LcaLayer.idx_format.offset == 16 + 14 * 8 + 16
+    assert lca.LcaLayer.kv_format.offset == 16 + 14 * 8 + 20
 
 
 def L():
@@ -187,3 +188,17 @@ def test_index_score_fp4_validation():
     assert f(*args(ld=98)) == E_SHAPE
     assert f(*args(k=None)) == E_NULL
     assert f(*args(q=MIS)) == E_ALIGN
+
+
+def test_kv8_attention_validation():
+    f = L().lca_hca_dense_attn_kv8
+    args = lambda **kw: [FAKE, kw.get("k", FAKE), FAKE, FAKE, FAKE, FAKE, 2, 1, 100, 128,
+                         kw.get("H", 64), 128, ctypes.c_float(0.088), 0, FAKE, FAKE, FAKE,
+                         1 << 20, None]
+    assert f(*args(H=16)) == E_UNSUP                       # 64-head blocks only
+    assert "multiple of 64" in lca.last_error()
+    assert f(*args(k=None)) == E_NULL
+    assert f(*args(k=MIS)) == E_ALIGN
+    g = L().lca_csa_sparse_attn_kv8
+    assert g(FAKE, FAKE, FAKE, FAKE, FAKE, 2, 1, FAKE, FAKE, 256, 32, 128, ctypes.c_float(0.088),
+             0, FAKE, FAKE, FAKE, 1 << 20, None) == E_UNSUP

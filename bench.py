@@ -9,7 +9,8 @@ uniformly from 65,536..1,048,576 tokens; 64 query heads on one KV head); the
 other workloads (csa_decode_8k, hca_decode_128k, csa_decode_1m,
 csa_prefill_256k, hybrid_decode_1m_swa: the stack with a 128-token sliding window on
 every layer, hybrid_decode_1m_swa_sink: that and a per-head attention sink on every
-layer, hybrid_decode_1m_fp4: the stack with the FP4 indexer) can be named with --workload.  A step is one pass of the
+layer, hybrid_decode_1m_fp4: the stack with the FP4 indexer, hybrid_decode_1m_kv8: the
+stack over mixed FP8 / bf16 KV rows) can be named with --workload.  A step is one pass of the
 workload's whole path over one batch; inputs are seeded, synthetic and resident
 in HBM before timing starts.  Decode workloads smaller than the 256 MB
 last-level cache rotate input replicas so that each step reads from HBM.
@@ -161,6 +162,8 @@ class HybridRunner(_Capture):
                 s.update(topk=wl.topk, k_idx=d["k_idx"], q_idx=d["q_idx"])
                 if wl.idx_fp4:
                     s.update(idx_format=lca.LCA_IDX_FP4)
+            if wl.kv8:
+                s.update(kv_format=lca.LCA_KV_MIXED)
             if wl.window:
                 s.update(win_k=d["win_k"], win_v=d["win_v"], win_off=d["win_off_dev"],
                          win_pos0=d["win_pos0_dev"], window=wl.window)
@@ -185,11 +188,12 @@ class HybridRunner(_Capture):
         wl, tot = self.wl, 0
         for d in self.layers:
             N = d["N"]
+            kv = 2 * 192 if wl.kv8 else 512   # K + V bytes per attended entry
             if d["csa"]:
                 kb = 32 if wl.idx_fp4 else 64   # indexer key / query bytes
-                tot += int(np.sum(kb * N + np.minimum(N, wl.topk) * 512 + kb))
+                tot += int(np.sum(kb * N + np.minimum(N, wl.topk) * kv + kb))
             else:
-                tot += int(np.sum(N * 512))
+                tot += int(np.sum(N * kv))
             tot += wl.batch * wl.heads * QO_BYTES_PER_HEAD
             if wl.window:   # window K/V rows, and the merge's re-read of out and lse
                 tot += int(np.sum(d["win_n"]) * 512) + wl.batch * wl.heads * QO_BYTES_PER_HEAD
@@ -240,8 +244,12 @@ class HybridRunner(_Capture):
             for b in range(n):
                 for d in self.layers:
                     s, e = int(d["ent_off"][b]), int(d["ent_off"][b + 1])
-                    Kc = oracle.bf16_bits_to_f64(_bits(d["k_cmp"][s:e]))
-                    Vc = oracle.bf16_bits_to_f64(_bits(d["v_cmp"][s:e]))
+                    if wl.kv8:
+                        Kc = oracle.kv8_values(d["k_cmp"][s:e].cpu().numpy())
+                        Vc = oracle.kv8_values(d["v_cmp"][s:e].cpu().numpy())
+                    else:
+                        Kc = oracle.bf16_bits_to_f64(_bits(d["k_cmp"][s:e]))
+                        Vc = oracle.bf16_bits_to_f64(_bits(d["v_cmp"][s:e]))
                     q = oracle.bf16_bits_to_f64(_bits(d["q"][b]))
                     L = int(self.L[b])
                     if wl.window:
@@ -605,6 +613,8 @@ def main(argv=None):
         cfg["sink"] = "per-head logits on every layer"
     if wl.idx_fp4:
         cfg["indexer"] = "FP4 E2M1 (32 B per key)"
+    if wl.kv8:
+        cfg["kv_storage"] = "mixed rows: FP8 E4M3 dims 0..63, bf16 dims 64..127 (192 B)"
     line = {
         "metric": METRIC,
         "value": run.tokens_per_step / (ms * 1e-3),

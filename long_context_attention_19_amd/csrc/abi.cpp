@@ -94,8 +94,6 @@ struct HybridAttnPlan {
 HybridAttnPlan hybrid_attn_plan(const lca_layer* layers, int n_layers, int rows, int heads) {
   HybridAttnPlan p;
   if (heads % 64 != 0 || rows <= 0) return p;
-  for (int l = 0; l < n_layers; ++l)   // the persistent form reads bf16 rows only
-    if (layers[l].kv_format != LCA_KV_BF16) return p;
   const int cu = lca_device_cu_count();
   if (cu <= 0) return p;
   const int G = 2 * cu;

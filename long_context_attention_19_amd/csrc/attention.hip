@@ -891,12 +891,14 @@ __device__ __forceinline__ int ps_item_of(const int* pre, int W, int j) {
   return lo;
 }
 
+template <int KV>
 __global__ __launch_bounds__(AT_NT) void attn_persist_kernel(AttnBatch ab, AttnPersist pp) {
   constexpr int ST = ATTN_PS_STAGE, SUB = 2, NU = ST / 16, NB = 2;
   constexpr int MAXW = ATTN_PS_MAX_ITEMS;
   static_assert(MAXW <= AT_NT && ATTN_PS_MAX_RUN * ST <= AT_IDS, "persistent sizes");
-  __shared__ __attribute__((aligned(256))) i32x4 s_k[NB][ST * 16];   // attn_stage needs 256 B
-  __shared__ __attribute__((aligned(256))) i32x4 s_v[NB][ST * 16];
+  static_assert(KV == 0 || ST == 64, "mixed KV rows: 64-entry stages");
+  constexpr int DPS = KV ? 6 : 2 * NU;   // DMA instructions per wave per stage
+  __shared__ AttnDmaSmem<ST, NB, 0, KV> sm;   // stage buffers (bf16 or mixed rows)
   __shared__ int s_ids[AT_IDS];
   __shared__ int s_pre[MAXW + 1];
   __shared__ int4 s_item[MAXW];   // entries, first entry of the sequence, sequence size, query row
@@ -953,9 +955,16 @@ __global__ __launch_bounds__(AT_NT) void attn_persist_kernel(AttnBatch ab, AttnP
   const int g = lane >> 4;
   const int my_row = lane >> 4;
   const int wrow0 = w * (ST / 4);
-  const uint32_t k_lds0 = lds_addr(&s_k[0][wrow0 * 16]);
-  const uint32_t v_lds0 = lds_addr(&s_v[0][wrow0 * 16]);
+  uint32_t k_lds0, v_lds0;
+  if constexpr (KV) {
+    k_lds0 = lds_addr(&sm.k8[0][wrow0 * 4]);
+    v_lds0 = lds_addr(&sm.v8[0][wrow0 * 4]);
+  } else {
+    k_lds0 = lds_addr(&sm.k[0][wrow0 * 16]);
+    v_lds0 = lds_addr(&sm.v[0][wrow0 * 16]);
+  }
   constexpr uint32_t BUF_BYTES = ST * 256;
+  constexpr int64_t ROW_BYTES = KV ? KV8_ROW_BYTES : HD * 2;
 
   bf16x8 qf[4], qn0[4], qn1[4];
   f32x4 o[8];
@@ -988,8 +997,8 @@ __global__ __launch_bounds__(AT_NT) void attn_persist_kernel(AttnBatch ab, AttnP
   int iss_pre = s_pre[iss_item], iss_next = s_pre[iss_item + 1];
   int4 iss_it = s_item[iss_item];
   const AttnArgs* iss_a = &ab.a[(iss_item / HB) / R0];
-  const char* iss_k = reinterpret_cast<const char*>(iss_a->kc + (int64_t)iss_it.y * HD);
-  const char* iss_v = reinterpret_cast<const char*>(iss_a->vc + (int64_t)iss_it.y * HD);
+  const char* iss_k = reinterpret_cast<const char*>(iss_a->kc) + (int64_t)iss_it.y * ROW_BYTES;
+  const char* iss_v = reinterpret_cast<const char*>(iss_a->vc) + (int64_t)iss_it.y * ROW_BYTES;
   bool iss_sparse = iss_a->idx != nullptr;
   auto issue = [&](int js, int buf, int c0) __attribute__((always_inline)) -> bool {
     while (js >= iss_next) {   // next item (items without stages are passed over)
@@ -998,22 +1007,39 @@ __global__ __launch_bounds__(AT_NT) void attn_persist_kernel(AttnBatch ab, AttnP
       iss_next = s_pre[iss_item + 1];
       iss_it = s_item[iss_item];
       iss_a = &ab.a[(iss_item / HB) / R0];
-      iss_k = reinterpret_cast<const char*>(iss_a->kc + (int64_t)iss_it.y * HD);
-      iss_v = reinterpret_cast<const char*>(iss_a->vc + (int64_t)iss_it.y * HD);
+      iss_k = reinterpret_cast<const char*>(iss_a->kc) + (int64_t)iss_it.y * ROW_BYTES;
+      iss_v = reinterpret_cast<const char*>(iss_a->vc) + (int64_t)iss_it.y * ROW_BYTES;
       iss_sparse = iss_a->idx != nullptr;
     }
     if (js == iss_pre || js == s0) load_q(iss_item);
     if (iss_it.x <= 0) return false;
     const int tb = (js - iss_pre) * ST;
     const int e_last = iss_it.x - 1;
-#pragma unroll
-    for (int u = 0; u < NU; ++u) {
-      const int r = wrow0 + 4 * u + my_row;
+    auto row_id = [&](int r) __attribute__((always_inline)) {
       const int e = min(tb + r, e_last);
-      int id = iss_sparse ? s_ids[(js - c0) * ST + (e - tb)] : e;
-      id = min(max(id, 0), iss_it.z - 1);
-      attn_issue_rows(iss_k, iss_v, (uint32_t)id * 256u, r, l16,
-                      k_lds0 + buf * BUF_BYTES + u * 1024, v_lds0 + buf * BUF_BYTES + u * 1024);
+      const int id = iss_sparse ? s_ids[(js - c0) * ST + (e - tb)] : e;
+      return (uint32_t)min(max(id, 0), iss_it.z - 1);
+    };
+    if constexpr (KV) {   // as in attn_dma_kernel: FP8 halves, then two runs of bf16 halves
+      const uint32_t off = row_id(wrow0 + (lane >> 2)) * KV8_ROW_BYTES + (uint32_t)(lane & 3) * 16u;
+      dma16(iss_k, off, k_lds0 + buf * (ST * 64));
+      dma16(iss_v, off, v_lds0 + buf * (ST * 64));
+      const uint32_t khi0 = lds_addr(&sm.khi[buf][0]), vhi0 = lds_addr(&sm.vhi[buf][0]);
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int r = wrow0 + 8 * u + (lane >> 3);
+        const uint32_t base = row_id(r) * KV8_ROW_BYTES + 64u;
+        const int sl = lane & 7;
+        dma16(iss_k, base + kv8_kslot(r, sl) * 16u, khi0 + (uint32_t)(wrow0 + 8 * u) * 128u);
+        dma16(iss_v, base + kv8_vslot(r, sl) * 16u, vhi0 + (uint32_t)(wrow0 + 8 * u) * 128u);
+      }
+    } else {
+#pragma unroll
+      for (int u = 0; u < NU; ++u) {
+        const int r = wrow0 + 4 * u + my_row;
+        attn_issue_rows(iss_k, iss_v, row_id(r) * 256u, r, l16,
+                        k_lds0 + buf * BUF_BYTES + u * 1024, v_lds0 + buf * BUF_BYTES + u * 1024);
+      }
     }
     return true;
   };
@@ -1079,7 +1105,7 @@ __global__ __launch_bounds__(AT_NT) void attn_persist_kernel(AttnBatch ab, AttnP
     for (int j = 0; j < nst; ++j) {
       const int js = c0 + j;
       const int buf = j & 1;
-      if (j + 1 < nst && dma1) wait_vm<2 * NU>();
+      if (j + 1 < nst && dma1) wait_vm<DPS>();
       else wait_vm<0>();
       lds_barrier();
       while (js >= cmp_next) {   // the item of stage js
@@ -1103,9 +1129,36 @@ __global__ __launch_bounds__(AT_NT) void attn_persist_kernel(AttnBatch ab, AttnP
         cur = item;
         ++nseg;
       }
-      if ((js - cmp_pre) * ST < cmp_n)   // an empty item's stage has nothing to attend
-        attn_stage<SUB>(s_k[buf], reinterpret_cast<const char*>(s_v[buf]), 0, (js - cmp_pre) * ST,
-                        cmp_n, qf, o, m_run, l_run, scale_log2, l16, g);
+      if constexpr (KV) {
+        // the stage's FP8 halves to bf16 (stale rows of an empty item's stage are harmless)
+        const int r = t >> 2, ch = t & 3;
+        const i32x4 k8 = sm.k8[buf][r * 4 + ch];
+        const i32x4 v8 = sm.v8[buf][r * 4 + ch];
+        i32x4 klo[2], vlo[2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+          for (int d = 0; d < 2; ++d) {
+            const int word = 2 * h + d;
+            klo[h][2 * d] = __builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(k8[word], 1.f, false));
+            klo[h][2 * d + 1] = __builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(k8[word], 1.f, true));
+            vlo[h][2 * d] = __builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v8[word], 1.f, false));
+            vlo[h][2 * d + 1] = __builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v8[word], 1.f, true));
+          }
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          sm.klo[r * 8 + kv8_kslot(r, 2 * ch + h)] = klo[h];
+          sm.vlo[r * 8 + kv8_vslot(r, 2 * ch + h)] = vlo[h];
+        }
+        lds_barrier();
+        if ((js - cmp_pre) * ST < cmp_n)
+          attn_stage_kv8<SUB>(sm.klo, sm.khi[buf], sm.vlo, sm.vhi[buf], 0, (js - cmp_pre) * ST,
+                              cmp_n, qf, o, m_run, l_run, scale_log2, l16, g);
+      } else {
+        if ((js - cmp_pre) * ST < cmp_n)   // an empty item's stage has nothing to attend
+          attn_stage<SUB>(sm.k[buf], reinterpret_cast<const char*>(sm.v[buf]), 0,
+                          (js - cmp_pre) * ST, cmp_n, qf, o, m_run, l_run, scale_log2, l16, g);
+      }
       lds_barrier();
       dma1 = false;
       if (j + 2 < nst) dma1 = issue(js + 2, buf, c0);
@@ -1149,12 +1202,18 @@ __global__ __launch_bounds__(256) void attn_persist_combine_kernel(AttnBatch ab,
 #pragma unroll
     for (int u = 0; u < CB; ++u) {
       const int pc = c0 + u;
-      const bool in = pc < npc;
-      const int pcc = in ? pc : c0;
-      const int64_t slot = 2 * (int64_t)(g_first + pcc) + ((pcc == 0 && first_is_last_slot) ? 1 : 0);
+      const int gq = g_first + (pc < npc ? pc : c0);
+      // with fewer stages than work-groups some runs are empty: they wrote no partial,
+      // and their slots hold whatever an earlier launch left there
+      const bool in = pc < npc && ps_run_start(gq, S, G) < ps_run_start(gq + 1, S, G);
+      const int pcc = gq - g_first;
+      const int64_t slot = 2 * (int64_t)gq + ((pcc == 0 && first_is_last_slot) ? 1 : 0);
       ml[u] = pp.part_ml[slot * 64 + hl];
       ov[u] = *reinterpret_cast<const f32x4*>(pp.part_o + (slot * 64 + hl) * HD + dg * 4);
-      if (!in) ml[u] = make_float2(-INFINITY, 0.f);
+      if (!in) {
+        ml[u] = make_float2(-INFINITY, 0.f);
+        ov[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
     }
     float mb = mm;
 #pragma unroll
@@ -1245,7 +1304,10 @@ bool attn_persist_fits(const AttnBatch& ab, int rows, int G) {
 hipError_t launch_attention_persist(const AttnBatch& ab, const AttnPersist& pp, hipStream_t st) {
   if (ab.n == 0 || pp.rows == 0) return hipSuccess;
   const int items = ab.n * pp.rows * ab.head_blocks;
-  hipLaunchKernelGGL(attn_persist_kernel, dim3((unsigned)pp.G), dim3(AT_NT), 0, st, ab, pp);
+  if (ab.a[0].kv8)   // one row format per launch
+    hipLaunchKernelGGL(attn_persist_kernel<1>, dim3((unsigned)pp.G), dim3(AT_NT), 0, st, ab, pp);
+  else
+    hipLaunchKernelGGL(attn_persist_kernel<0>, dim3((unsigned)pp.G), dim3(AT_NT), 0, st, ab, pp);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(attn_persist_combine_kernel, dim3(64 / PSC_HEADS, (unsigned)items), dim3(256),

@@ -218,6 +218,31 @@ def test_hybrid_fp4_full():
             assert_lse_close(lse[b], ref["lse"], f"layer {li} seq {b}")
 
 
+def test_hybrid_kv8_full():
+    """The full-size stack over mixed FP8 / bf16 KV rows, on a sample of sequences."""
+    step("full-size hybrid_decode_1m_kv8")
+    wl = workloads.get("hybrid_decode_1m_kv8")
+    run = bench.HybridRunner(wl)
+    run.step(0)
+    torch.cuda.synchronize()
+    for li, (d, spec) in enumerate(zip(run.layers, run.outputs)):
+        out, lse = _f64(spec["out"]), spec["lse"].cpu().numpy()
+        for b in (0, 11, wl.batch - 1):
+            s, e = int(d["ent_off"][b]), int(d["ent_off"][b + 1])
+            Kc = oracle.kv8_values(d["k_cmp"][s:e].cpu().numpy())
+            Vc = oracle.kv8_values(d["v_cmp"][s:e].cpu().numpy())
+            q, L = _f64(d["q"][b]), int(run.L[b])
+            if d["csa"]:
+                ref = oracle.csa_decode(q, d["q_idx"][b].cpu().numpy(), L, Kc, Vc,
+                                        d["k_idx"][s:e].cpu().numpy(), d["ratio"], wl.topk, SCALE)
+                assert np.array_equal(spec["idx"][b, :int(spec["count"][b])].cpu().numpy(),
+                                      ref["idx"])
+            else:
+                ref = oracle.hca_decode(q, L, Kc, Vc, d["ratio"], SCALE)
+            assert_attn_close(out[b], ref["o"], f"layer {li} seq {b}")
+            assert_lse_close(lse[b], ref["lse"], f"layer {li} seq {b}")
+
+
 def test_prefill_full():
     step("full-size csa_prefill_256k")
     wl = workloads.get("csa_prefill_256k")

@@ -563,3 +563,50 @@ def test_hybrid_step_small():
     assert len(t) == 3 and all(x > 0 for x in t), t
     for Ld, o in zip(hs.layers, before):
         assert torch.equal(Ld["out"].view(torch.int16), o.view(torch.int16))
+
+
+def test_hybrid_two_persistent_launches_few_stages():
+    """More than 8 layers (two attention launches sharing the partial slots) with fewer
+    stages than work-groups: a launch's merge must not pick up the other launch's
+    partials from the slots of work-groups whose runs hold no stage."""
+    step("HybridStep 12 layers, short rows")
+    g = rng(275, 0, 0)
+    L = [3000, 9000, 20000]
+    B, heads = len(L), 64
+    layers, refs = [], []
+    for li in range(12):
+        csa = li % 2 == 0
+        ratio = 4 if csa else 128
+        Ns = [x // ratio for x in L]
+        ent_off = offsets(Ns)
+        tot = int(ent_off[-1])
+        Kc = bf16_normal(g, (tot, 128), std=1 / math.sqrt(ratio))
+        Vc = bf16_normal(g, (tot, 128), std=1 / math.sqrt(ratio))
+        q = bf16_normal(g, (B, heads, 128))
+        Ld = dict(kind=lca.LCA_LAYER_CSA if csa else lca.LCA_LAYER_HCA, ratio=ratio,
+                  max_entries=max(Ns), q=bf16_dev(q), k_cmp=bf16_dev(Kc), v_cmp=bf16_dev(Vc),
+                  ent_off=i64_dev(ent_off),
+                  out=torch.empty(B, heads, 128, dtype=torch.bfloat16, device=DEV),
+                  lse=torch.empty(B, heads, dtype=torch.float32, device=DEV))
+        host = dict(q=q, Kc=Kc, Vc=Vc, ent_off=ent_off)
+        if csa:
+            host["k_idx"], host["q_idx"] = int8_uniform(g, (tot, 64)), int8_uniform(g, (B, 64))
+            Ld.update(topk=512, k_idx=i8_dev(host["k_idx"]), q_idx=i8_dev(host["q_idx"]))
+        layers.append(Ld)
+        refs.append(host)
+    hs = HybridStep(layers, B, 1, heads)
+    for _ in range(2):   # the second step runs over the partials the first one left
+        hs.run(i64_dev(np.arange(B + 1)), i64_dev(L), SCALE)
+    torch.cuda.synchronize()
+    for li, (Ld, host) in enumerate(zip(hs.layers, refs)):
+        O, LSE = bf16_vals(Ld["out"]), Ld["lse"].cpu().numpy()
+        Kf, Vf, qf = (oracle.bf16_bits_to_f64(host[x]) for x in ("Kc", "Vc", "q"))
+        for b in range(B):
+            sl = slice(host["ent_off"][b], host["ent_off"][b + 1])
+            if li % 2 == 0:
+                r = oracle.csa_decode(qf[b], host["q_idx"][b], L[b], Kf[sl], Vf[sl],
+                                      host["k_idx"][sl], 4, 512, SCALE)
+            else:
+                r = oracle.hca_decode(qf[b], L[b], Kf[sl], Vf[sl], 128, SCALE)
+            assert_attn_close(O[b], r["o"], f"layer {li} seq {b}")
+            assert_lse_close(LSE[b], r["lse"], f"layer {li} seq {b}")

@@ -33,6 +33,7 @@ class Workload:
     window: int = 0        # sliding-window branch: raw tokens before the query (0: none)
     sink: bool = False     # per-head attention-sink logits on every layer
     idx_fp4: bool = False  # FP4 (E2M1) indexer query / keys instead of int8
+    kv8: bool = False      # mixed KV rows: dims 0..63 FP8 E4M3, dims 64..127 bf16
     notes: str = field(default="", compare=False)
 
     @property
@@ -80,6 +81,13 @@ WORKLOADS = {
         idx_fp4=True,
         notes="compressed entries drawn directly as bf16 N(0, 1/ratio); FP4 indexer codes "
               "uniform over the 16 E2M1 codes"),
+    # the stack over mixed KV storage rows (FP8 for dims 0..63, bf16 for the RoPE dims)
+    "hybrid_decode_1m_kv8": Workload(
+        name="hybrid_decode_1m_kv8", cfg_id=3, kind="hybrid_decode", batch=16, ctx_len=None,
+        ctx_range=(65536, 1048576), heads=64, topk=2048, n_layers=8, direct_entries=True,
+        kv8=True,
+        notes="compressed entries drawn directly as N(0, 1/ratio), stored as 192-byte mixed "
+              "rows (FP8 E4M3 dims 0..63, bf16 dims 64..127)"),
     # CSA chunked prefill: 4096 new tokens after a 256K context
     "csa_prefill_256k": Workload(
         name="csa_prefill_256k", cfg_id=4, kind="csa_prefill", batch=1, ctx_len=262144,

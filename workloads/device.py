@@ -44,10 +44,14 @@ def hybrid_inputs(wl: Workload, device="cuda"):
         d = dict(csa=csa, ratio=ratio, N=N, ent_off=ent_off, max_entries=int(N.max()),
                  q=gen.device_bf16_normal((B, H, 128), gen.seed_of(wl.cfg_id, li, gen.T_Q),
                                           device=device),
-                 k_cmp=gen.device_bf16_normal((tot, 128), gen.seed_of(wl.cfg_id, li, gen.T_CMP_K),
-                                              std, device),
-                 v_cmp=gen.device_bf16_normal((tot, 128), gen.seed_of(wl.cfg_id, li, gen.T_CMP_V),
-                                              std, device),
+                 k_cmp=(gen.device_kv8_normal(tot, gen.seed_of(wl.cfg_id, li, gen.T_CMP_K), std, device)
+                        if wl.kv8 else
+                        gen.device_bf16_normal((tot, 128), gen.seed_of(wl.cfg_id, li, gen.T_CMP_K),
+                                               std, device)),
+                 v_cmp=(gen.device_kv8_normal(tot, gen.seed_of(wl.cfg_id, li, gen.T_CMP_V), std, device)
+                        if wl.kv8 else
+                        gen.device_bf16_normal((tot, 128), gen.seed_of(wl.cfg_id, li, gen.T_CMP_V),
+                                               std, device)),
                  ent_off_dev=torch.tensor(ent_off, device=device))
         if csa and wl.idx_fp4:   # packed FP4 codes, 32 bytes per vector
             d["k_idx"] = gen.device_fp4_uniform((tot, 32), gen.seed_of(wl.cfg_id, li, gen.T_KFP4),

@@ -115,28 +115,27 @@ __device__ __forceinline__ void sl_sweep(const i32x4* __restrict__ kp, const i32
 }
 
 // Threshold of one token's histogram (nbins bins, bin b at h[b ^ j]), by one wave:
-// the bin holding the need-th largest key and the count in higher bins.
+// the bin holding the need-th largest key and the count in higher bins.  Blocks of 64
+// bins from the top, lane l reading bin top - l (consecutive banks), each scanned
+// across the wave until the running count reaches `need` (the caller guarantees the
+// histogram holds at least that many keys).
 template <int NBINS>
 __device__ __forceinline__ void sl_threshold(const int32_t* h, int j, int need, int lane,
                                              int32_t* out_bin, int32_t* out_above) {
-  constexpr int P = NBINS / WAVE;   // bins per lane, from the top
-  int32_t s = 0;
-#pragma unroll 8
-  for (int e = 0; e < P; ++e) s += h[(NBINS - 1 - P * lane - e) ^ j];
-  const int32_t incl = wave_incl_scan(s);
-  const int32_t excl = incl - s;
-  if (excl < need && incl >= need) {
-    int32_t acc = excl;
-    for (int e = 0; e < P; ++e) {
-      const int b = NBINS - 1 - P * lane - e;
-      const int32_t cnt = h[b ^ j];
-      if (acc + cnt >= need) {
+  int32_t acc = 0;   // keys in the blocks above the current one
+  for (int blk = 0; blk < NBINS / WAVE; ++blk) {
+    const int b = NBINS - 1 - blk * WAVE - lane;
+    const int32_t c = h[b ^ j];
+    const int32_t incl = wave_incl_scan(c);   // keys in this block's bins >= b
+    const int32_t tot = __shfl(incl, WAVE - 1, WAVE);
+    if (acc + tot >= need) {   // wave-uniform: the bin is in this block
+      if (acc + incl >= need && acc + incl - c < need) {   // exactly one lane
         *out_bin = b;
-        *out_above = acc;
-        break;
+        *out_above = acc + incl - c;
       }
-      acc += cnt;
+      return;
     }
+    acc += tot;
   }
 }
 

@@ -10,7 +10,8 @@ other workloads (csa_decode_8k, hca_decode_128k, csa_decode_1m,
 csa_prefill_256k, hybrid_decode_1m_swa: the stack with a 128-token sliding window on
 every layer, hybrid_decode_1m_swa_sink: that and a per-head attention sink on every
 layer, hybrid_decode_1m_fp4: the stack with the FP4 indexer, hybrid_decode_1m_kv8: the
-stack over mixed FP8 / bf16 KV rows) can be named with --workload.  A step is one pass of the
+stack over mixed FP8 / bf16 KV rows, csa_decode_1m_fp4: the 1M CSA decode with the FP4
+indexer) can be named with --workload.  A step is one pass of the
 workload's whole path over one batch; inputs are seeded, synthetic and resident
 in HBM before timing starts.  Decode workloads smaller than the 256 MB
 last-level cache rotate input replicas so that each step reads from HBM.
@@ -317,7 +318,10 @@ class CsaDecodeRunner(_Capture):
                         inp["ent_off_dev"])
         lca.kv_compress(inp["raw_v"], inp["tok_off_dev"], wl.batch, T, wl.c, self.v_cmp,
                         inp["ent_off_dev"])
-        self.st = CsaStep(wl.batch, 1, int(inp["N"].max()), wl.heads, wl.topk, wl.c, device)
+        self.st = CsaStep(wl.batch, 1, int(inp["N"].max()), wl.heads, wl.topk, wl.c, device,
+                          fp4=wl.idx_fp4)
+        if wl.idx_fp4:
+            self.dominant_tag = "index_score_fp4_kernel"
         self.q_off = torch.arange(wl.batch + 1, dtype=torch.int64, device=device)
         self.q_pos = torch.tensor(inp["L"], dtype=torch.int64, device=device)
         self.out = torch.empty(wl.batch, wl.heads, 128, dtype=torch.bfloat16, device=device)
@@ -332,16 +336,17 @@ class CsaDecodeRunner(_Capture):
 
     def step_bytes(self):
         N, wl = self.inp["N"], self.wl
-        return int(np.sum(64 * N + np.minimum(N, wl.topk) * 512 + 64)) + \
+        kb = 32 if wl.idx_fp4 else 64   # indexer key / query bytes
+        return int(np.sum(kb * N + np.minimum(N, wl.topk) * 512 + kb)) + \
             wl.batch * wl.heads * QO_BYTES_PER_HEAD
 
     def dominant_launch(self):
         self._i = getattr(self, "_i", 0) + 1
         r = self.inp["replicas"][self._i % self.R]
         st = self.st
-        self.lca.csa_index_score(r["q_idx"], self.q_off, self.q_pos, r["k_idx"],
-                                 self.inp["ent_off_dev"], self.wl.batch, 1, st.max_entries,
-                                 self.wl.c, st.scores, st.n_vis, ws=self._dom_ws())
+        score = self.lca.csa_index_score_fp4 if self.wl.idx_fp4 else self.lca.csa_index_score
+        score(r["q_idx"], self.q_off, self.q_pos, r["k_idx"], self.inp["ent_off_dev"],
+              self.wl.batch, 1, st.max_entries, self.wl.c, st.scores, st.n_vis, ws=self._dom_ws())
 
     def _dom_ws(self):
         if not hasattr(self, "_hws"):
@@ -351,6 +356,11 @@ class CsaDecodeRunner(_Capture):
 
     def dominant_units(self):
         n = int(np.sum(self.inp["N"]))
+        if self.wl.idx_fp4:
+            return {"bound": "hbm", "per_launch": n * (32 + 4) + self.wl.batch * 32, "unit": "GB/s",
+                    "kernel": "index_score_fp4_kernel<true>: FP4 indexer scores (FP4 MFMA) + "
+                              "fused radix histogram",
+                    "per_unit": "36 B per compressed entry (32 B FP4 key read, 4 B score written)"}
         return {"bound": "hbm", "per_launch": n * (64 + 4) + self.wl.batch * 64, "unit": "GB/s",
                 "kernel": "index_score_kernel<true>: int8 indexer scores + fused radix histogram",
                 "per_unit": "68 B per compressed entry (64 B key read, 4 B score written)"}
@@ -369,8 +379,9 @@ class CsaDecodeRunner(_Capture):
                 kidx, qidx = r["k_idx"][s:e].cpu().numpy(), r["q_idx"][b].cpu().numpy()
                 q = oracle.bf16_bits_to_f64(_bits(r["q"][b]))
                 L = int(inp["L"][b])
+                query = oracle.csa_query_fp4 if wl.idx_fp4 else oracle.csa_decode
                 mean, sp, rp = _timed_reps(
-                    lambda: oracle.csa_decode(q, qidx, L, Kc, Vc, kidx, wl.c, wl.topk, SCALE),
+                    lambda: query(q, qidx, L, Kc, Vc, kidx, wl.c, wl.topk, SCALE),
                     CPU_BUDGET_S / n)
                 t_tok += mean
                 spent += sp

@@ -121,12 +121,8 @@ __device__ __forceinline__ bool row_info(const AttnArgs& a, int supertile, RowIn
 // would otherwise wait for every DMA in flight, the next stage's included.  The
 // waits are explicit (vmcnt), and no compiler-visible global load is in flight while
 // the pipeline runs: the sparse form copies a chunk of entry ids to LDS first.
-#ifndef AT_SUB64
-#define AT_SUB64 2          // 64 heads: 32-entry sub-tiles per wave per stage
-#endif
-#ifndef AT_NB64
-#define AT_NB64 2           // 64 heads: stage buffers
-#endif
+constexpr int AT_SUB64 = 2;        // 64 heads: 32-entry sub-tiles per wave per stage
+constexpr int AT_NB64 = 2;         // 64 heads: stage buffers
 constexpr int AT_IDS = 2048;       // entry ids staged in LDS per chunk (sparse form)
 
 // MODE: 0 dense (HCA), 1 sparse (CSA), 2 either, per layer of the launch
@@ -1098,10 +1094,8 @@ __global__ __launch_bounds__(AT_NT) void attn_persist_kernel(AttnBatch ab, AttnP
       __syncthreads();
     }
     bool dma1 = false;                     // whether the stage after the current one fetched rows
-    const bool dma0 = issue(c0, 0, c0);
+    issue(c0, 0, c0);
     if (nst > 1) dma1 = issue(c0 + 1, 1, c0);
-    bool cur_dma = dma0;
-    (void)cur_dma;
     for (int j = 0; j < nst; ++j) {
       const int js = c0 + j;
       const int buf = j & 1;

@@ -38,11 +38,13 @@ def _check_compress_sample(raw, tok_off, ent_off, cache, c, nsample, seed):
         assert np.array_equal(got, ref), f"sequence {b}"
 
 
-def _check_csa_row(q, qidx, pos, k_cmp, v_cmp, kidx_host, c, topk, idx, cnt, out, lse, what):
+def _check_csa_row(q, qidx, pos, k_cmp, v_cmp, kidx_host, c, topk, idx, cnt, out, lse, what,
+                   fp4=False):
     """One CSA query row: scores -> top-k (bit-exact) -> attention, the selected K/V rows
     fetched from the device cache by the oracle's own indices."""
     n_vis = oracle.n_visible(pos, c, kidx_host.shape[0])
-    sel = oracle.topk_select(oracle.index_scores(qidx, kidx_host), n_vis, topk)
+    scorer = oracle.index_scores_fp4 if fp4 else oracle.index_scores
+    sel = oracle.topk_select(scorer(qidx, kidx_host), n_vis, topk)
     assert cnt == len(sel), what
     assert np.array_equal(idx[:cnt], sel), what
     assert np.all(idx[cnt:] == -1), what
@@ -52,7 +54,7 @@ def _check_csa_row(q, qidx, pos, k_cmp, v_cmp, kidx_host, c, topk, idx, cnt, out
     assert_lse_close(lse, l, what)
 
 
-@pytest.mark.parametrize("name", ["csa_decode_8k", "csa_decode_1m"])
+@pytest.mark.parametrize("name", ["csa_decode_8k", "csa_decode_1m", "csa_decode_1m_fp4"])
 def test_csa_decode_full(name):
     step(f"full-size {name}")
     wl = workloads.get(name)
@@ -69,7 +71,7 @@ def test_csa_decode_full(name):
         s, e = int(inp["ent_off"][b]), int(inp["ent_off"][b + 1])
         _check_csa_row(_f64(r["q"][b]), r["q_idx"][b].cpu().numpy(), int(inp["L"][b]),
                        run.k_cmp[s:e], run.v_cmp[s:e], r["k_idx"][s:e].cpu().numpy(), wl.c,
-                       wl.topk, idx[b], cnt[b], out[b], lse[b], f"{name} seq {b}")
+                       wl.topk, idx[b], cnt[b], out[b], lse[b], f"{name} seq {b}", wl.idx_fp4)
     # a second replica (different indexer inputs) in the same launch shape
     run.step(1)
     torch.cuda.synchronize()
@@ -80,7 +82,7 @@ def test_csa_decode_full(name):
     s, e = int(inp["ent_off"][b]), int(inp["ent_off"][b + 1])
     _check_csa_row(_f64(r["q"][b]), r["q_idx"][b].cpu().numpy(), int(inp["L"][b]),
                    run.k_cmp[s:e], run.v_cmp[s:e], r["k_idx"][s:e].cpu().numpy(), wl.c, wl.topk,
-                   idx[b], cnt[b], out[b], lse[b], f"{name} replica 1 seq {b}")
+                   idx[b], cnt[b], out[b], lse[b], f"{name} replica 1 seq {b}", wl.idx_fp4)
 
 
 def test_hca_decode_full():

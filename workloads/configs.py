@@ -54,6 +54,10 @@ WORKLOADS = {
     "csa_decode_1m": Workload(
         name="csa_decode_1m", cfg_id=2, kind="csa_decode", batch=4, ctx_len=1048576,
         heads=64, topk=2048),
+    # the same with the FP4 indexer (32 B per key instead of 64)
+    "csa_decode_1m_fp4": Workload(
+        name="csa_decode_1m_fp4", cfg_id=2, kind="csa_decode", batch=4, ctx_len=1048576,
+        heads=64, topk=2048, idx_fp4=True),
     # 8-layer hybrid stack (CSA on even layers, HCA on odd), 16 ragged sequences
     "hybrid_decode_1m": Workload(
         name="hybrid_decode_1m", cfg_id=3, kind="hybrid_decode", batch=16, ctx_len=None,

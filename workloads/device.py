@@ -102,10 +102,16 @@ def decode_raw_inputs(wl: Workload, device="cuda", replicas: int = 1):
         d = dict(q=gen.device_bf16_normal((wl.batch, wl.heads, 128),
                                           gen.seed_of(wl.cfg_id, 0, gen.T_Q, r), device=device))
         if wl.kind == "csa_decode":
-            d["k_idx"] = gen.device_int8_uniform((int(ent_off[-1]), 64),
-                                                 gen.seed_of(wl.cfg_id, 0, gen.T_KIDX, r), device)
-            d["q_idx"] = gen.device_int8_uniform((wl.batch, 64),
-                                                 gen.seed_of(wl.cfg_id, 0, gen.T_QIDX, r), device)
+            if wl.idx_fp4:   # packed FP4 codes, 32 bytes per vector
+                d["k_idx"] = gen.device_fp4_uniform((int(ent_off[-1]), 32),
+                                                    gen.seed_of(wl.cfg_id, 0, gen.T_KFP4, r), device)
+                d["q_idx"] = gen.device_fp4_uniform((wl.batch, 32),
+                                                    gen.seed_of(wl.cfg_id, 0, gen.T_QFP4, r), device)
+            else:
+                d["k_idx"] = gen.device_int8_uniform((int(ent_off[-1]), 64),
+                                                     gen.seed_of(wl.cfg_id, 0, gen.T_KIDX, r), device)
+                d["q_idx"] = gen.device_int8_uniform((wl.batch, 64),
+                                                     gen.seed_of(wl.cfg_id, 0, gen.T_QIDX, r), device)
         reps.append(d)
     return dict(L=L, tok_off=tok_off, raw_k=raw_k, raw_v=raw_v, ratio=ratio, N=N, ent_off=ent_off,
                 tok_off_dev=torch.tensor(tok_off, device=device),

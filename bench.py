@@ -72,9 +72,10 @@ def _src_hash(files):
     return h.hexdigest()
 
 
-def traffic_from_profile(tag, src_files):
+def traffic_from_profile(tag, src_files, workload):
     """HBM bytes per launch from the committed rocprofv3 counter summary, only if
-    it was taken on the current kernel source (matching hash); else None."""
+    it was taken on this workload and on the current kernel source (matching hash);
+    else None."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(path):
         return None
@@ -82,9 +83,22 @@ def traffic_from_profile(tag, src_files):
         rec = json.load(open(path)).get(tag)
     except Exception:
         return None
-    if not rec or rec.get("source_sha256") != _src_hash(src_files):
+    if not rec or rec.get("workload", "").split(" ")[0] != workload:
+        return None
+    if rec.get("source_sha256") != _src_hash(src_files):
         return None
     return rec.get("bytes_per_launch")
+
+
+def _dtype(wl):
+    """Arithmetic types of the step: bf16 attention, the indexer's codes (CSA layers),
+    FP8 halves of mixed cache rows."""
+    parts = ["bf16"]
+    if wl.kv8:
+        parts.append("fp8")
+    if wl.kind != "hca_decode":
+        parts.append("fp4" if wl.idx_fp4 else "int8")
+    return "+".join(parts)
 
 
 CPU_BUDGET_S = 12.0   # oracle time the cpu_baseline leg aims for
@@ -563,8 +577,9 @@ def _time(fn, n, stream, torch):
 def main(argv=None):
     args = parse(argv)
     if args.gpus != 1:
-        print(json.dumps({"error": "one GPU only: this build has no multi-GPU path; run with "
-                                   "--gpus 1"}), flush=True)
+        print(json.dumps({"error": "one GPU only: the step runs on a single GPU's share of the "
+                                   "work and has no multi-GPU path; run with --gpus 1"}),
+              flush=True)
         sys.exit(2)
     import torch
     import workloads
@@ -637,7 +652,7 @@ def main(argv=None):
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16+int8",
+        "dtype": _dtype(wl),
         "data": "synthetic",
         "config": cfg,
         "launch": "eager" if args.no_graph else f"hip-graph replay ({getattr(run, 'R', 1)} replica graphs)",
@@ -648,7 +663,8 @@ def main(argv=None):
                      "peak": peak, "unit": u["unit"], "frac": achieved / peak,
                      "avg_launch_us": k_ms * 1e3, "per_launch": u["per_launch"],
                      "per_unit": u["per_unit"],
-                     "traffic": traffic_from_profile(run.dominant_tag, run.dominant_src)},
+                     "traffic": traffic_from_profile(run.dominant_tag, run.dominant_src,
+                                                     wl.name)},
         "cpu_baseline": None,
     }
     if hasattr(run, "phase_ms"):

@@ -83,9 +83,34 @@ int hybrid_splits(int n_layers, int max_q) {
   return std::max(1, base / conc);
 }
 
-// The hybrid step's attention takes the balanced persistent form when every launch
-// of up to 8 layers fits it (64-head blocks, at most ATTN_PS_MAX_ITEMS items, and
-// entry bounds that keep the runs short); one partial region serves all launches.
+// Attention launches of the hybrid step: up to 8 layers each, one row format per
+// launch, HCA layers first (their rows are the longest, for the per-row form).  The
+// plan below and the step both take the launches from here.
+std::vector<std::vector<int>> attn_groups(const lca_layer* layers, int n_layers) {
+  std::vector<int> order;
+  for (int kind : {LCA_LAYER_HCA, LCA_LAYER_CSA})
+    for (int l = 0; l < n_layers; ++l)
+      if (layers[l].kind == kind) order.push_back(l);
+  std::vector<std::vector<int>> groups;
+  for (int f = 0; f < 2; ++f) {
+    std::vector<int> cur;
+    for (int l : order) {
+      if ((layers[l].kv_format == LCA_KV_MIXED ? 1 : 0) != f) continue;
+      cur.push_back(l);
+      if ((int)cur.size() == lca::MAX_BATCH_LAYERS) {
+        groups.push_back(cur);
+        cur.clear();
+      }
+    }
+    if (!cur.empty()) groups.push_back(cur);
+  }
+  return groups;
+}
+
+// The hybrid step's attention takes the balanced persistent form when every one of
+// its launches fits it (64-head blocks, at most ATTN_PS_MAX_ITEMS items, and entry
+// bounds that keep the runs short); one partial region serves all launches, which
+// run one after another on the caller's stream.
 struct HybridAttnPlan {
   bool persist = false;
   int G = 0;        // persistent work-groups: two per compute unit
@@ -99,12 +124,11 @@ HybridAttnPlan hybrid_attn_plan(const lca_layer* layers, int n_layers, int rows,
   const int G = 2 * cu;
   const int hb = heads / 64;
   int items_max = 0;
-  for (int c0 = 0; c0 < n_layers; c0 += lca::MAX_BATCH_LAYERS) {
-    const int n = std::min(lca::MAX_BATCH_LAYERS, n_layers - c0);
-    const int64_t items = (int64_t)n * rows * hb;
+  for (const std::vector<int>& grp : attn_groups(layers, n_layers)) {
+    const int64_t items = (int64_t)grp.size() * rows * hb;
     if (items > lca::ATTN_PS_MAX_ITEMS) return p;
     int64_t stages = 0;
-    for (int l = c0; l < c0 + n; ++l) {
+    for (int l : grp) {
       const int max_n = layers[l].kind == LCA_LAYER_CSA ? layers[l].topk : layers[l].max_entries;
       stages += (int64_t)rows * hb *
                 std::max(1, (std::max(max_n, 0) + lca::ATTN_PS_STAGE - 1) / lca::ATTN_PS_STAGE);
@@ -524,7 +548,8 @@ int32_t lca_hybrid_layer_step(const lca_layer* layers, int32_t n_layers, const i
   std::vector<lca::IndexLayer> il;
   std::vector<lca::TopkLayer> tl;
   std::vector<int> il_fp4;   // per CSA layer: FP4 indexer codes
-  std::vector<lca::AttnArgs> csa_a, hca_a;
+  std::vector<lca::AttnArgs> args((size_t)n_layers);
+  bool has_csa = false;
   char* p = reinterpret_cast<char*>(ws);
   for (int l = 0; l < n_layers; ++l) {
     const lca_layer& L = layers[l];
@@ -561,15 +586,15 @@ int32_t lca_hybrid_layer_step(const lca_layer* layers, int32_t n_layers, const i
       a.ratio = 1;
       lca::attn_ws_carve(p, rows, heads, sp, a);
       p += lca::attn_ws_bytes(rows, heads, sp);
-      csa_a.push_back(a);
+      has_csa = true;
     } else {
       a.q_pos = q_pos;
       a.ratio = L.ratio;
       a.max_n = L.max_entries;
       lca::attn_ws_carve(p, rows, heads, sp, a);
       p += lca::attn_ws_bytes(rows, heads, sp);
-      hca_a.push_back(a);
     }
+    args[l] = a;
   }
 
   // One stream, three phases: the CSA layers' scores and selections (batched, up to 8
@@ -582,7 +607,7 @@ int32_t lca_hybrid_layer_step(const lca_layer* layers, int32_t n_layers, const i
   const int hb = (heads + 63) / 64;
   const bool timing = ls && ls->timing;
   if (timing) {
-    ls->has_csa = !csa_a.empty();
+    ls->has_csa = has_csa;
     ls->timed = true;
   }
   auto mark = [&](int i) {
@@ -625,27 +650,19 @@ int32_t lca_hybrid_layer_step(const lca_layer* layers, int32_t n_layers, const i
     if (first) mark(2);
   }
   mark(3);
-  std::vector<lca::AttnArgs> all = hca_a;   // longest rows first for the per-row form
-  all.insert(all.end(), csa_a.begin(), csa_a.end());
   lca::AttnPersist pp{};
   if (plan.persist) {
     lca::attn_persist_carve(p, plan.G, plan.items, pp);
     pp.rows = rows;
   }
-  // launches of up to 8 layers, layers with bf16 rows and with mixed rows apart
-  for (int f = 0; f < 2 && e == hipSuccess; ++f) {
-    std::vector<lca::AttnArgs> fa;
-    for (const lca::AttnArgs& x : all)
-      if (x.kv8 == f) fa.push_back(x);
-    for (size_t c0 = 0; c0 < fa.size() && e == hipSuccess; c0 += lca::MAX_BATCH_LAYERS) {
-      const int n = (int)std::min<size_t>(lca::MAX_BATCH_LAYERS, fa.size() - c0);
-      lca::AttnBatch ab{};
-      ab.n = n;
-      ab.head_blocks = hb;
-      for (int i = 0; i < n; ++i) ab.a[i] = fa[c0 + i];
-      e = plan.persist ? lca::launch_attention_persist(ab, pp, caller)
-                       : lca::launch_attention(ab, batch, caller);
-    }
+  for (const std::vector<int>& grp : attn_groups(layers, n_layers)) {
+    if (e != hipSuccess) break;
+    lca::AttnBatch ab{};
+    ab.n = (int)grp.size();
+    ab.head_blocks = hb;
+    for (int i = 0; i < ab.n; ++i) ab.a[i] = args[grp[i]];
+    e = plan.persist ? lca::launch_attention_persist(ab, pp, caller)
+                     : lca::launch_attention(ab, batch, caller);
   }
   // sliding-window branches, merged into each layer's result (one launch per 8 layers)
   std::vector<lca::AttnArgs> win_a;

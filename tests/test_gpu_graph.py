@@ -60,7 +60,7 @@ def test_csa_step_graph_replays():
 
 
 def test_hybrid_step_graph_replays():
-    step("graph: HybridStep (forks onto the library's streams)")
+    step("graph: HybridStep")
     g = rng(301, 0, 0)
     L = [70000, 300000, 5000]
     B, heads = len(L), 64

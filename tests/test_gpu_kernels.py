@@ -565,17 +565,27 @@ def test_hybrid_step_small():
         assert torch.equal(Ld["out"].view(torch.int16), o.view(torch.int16))
 
 
-def test_hybrid_two_persistent_launches_few_stages():
+# 12-layer stacks, each attended in two launches of up to 8 layers (HCA layers first):
+# CSA / HCA alternating, HCA-heavy (a launch of HCA layers only) and CSA-heavy (a launch
+# of CSA layers only)
+_KIND_PATTERNS = {"alternate": [i % 2 == 0 for i in range(12)],
+                  "hca_heavy": [i in (3, 8) for i in range(12)],
+                  "csa_heavy": [i not in (1, 10) for i in range(12)]}
+
+
+@pytest.mark.parametrize("pattern", list(_KIND_PATTERNS))
+def test_hybrid_two_persistent_launches_few_stages(pattern):
     """More than 8 layers (two attention launches sharing the partial slots) with fewer
     stages than work-groups: a launch's merge must not pick up the other launch's
     partials from the slots of work-groups whose runs hold no stage."""
-    step("HybridStep 12 layers, short rows")
-    g = rng(275, 0, 0)
+    step(f"HybridStep 12 layers, short rows, {pattern}")
+    g = rng(275, list(_KIND_PATTERNS).index(pattern), 0)
     L = [3000, 9000, 20000]
     B, heads = len(L), 64
     layers, refs = [], []
+    kinds = _KIND_PATTERNS[pattern]
     for li in range(12):
-        csa = li % 2 == 0
+        csa = kinds[li]
         ratio = 4 if csa else 128
         Ns = [x // ratio for x in L]
         ent_off = offsets(Ns)
@@ -603,7 +613,7 @@ def test_hybrid_two_persistent_launches_few_stages():
         Kf, Vf, qf = (oracle.bf16_bits_to_f64(host[x]) for x in ("Kc", "Vc", "q"))
         for b in range(B):
             sl = slice(host["ent_off"][b], host["ent_off"][b + 1])
-            if li % 2 == 0:
+            if kinds[li]:
                 r = oracle.csa_decode(qf[b], host["q_idx"][b], L[b], Kf[sl], Vf[sl],
                                       host["k_idx"][sl], 4, 512, SCALE)
             else:

@@ -45,6 +45,9 @@ from .csa_hca import (
     fp8_e4m3_values,
     kv8_values,
     KV8_ROW_BYTES,
+    compress_to_cache,
+    fp8_e4m3_round,
+    compress_to_cache_kv8,
 )
 
 __all__ = [
@@ -53,5 +56,6 @@ __all__ = [
     "hybrid_decode", "csa_prefill", "window_tokens", "attention_union", "csa_query_swa",
     "hca_query_swa", "attention_sink", "csa_query_sink", "hca_query_sink",
     "fp4_values", "fp4_unpack", "index_scores_fp4", "csa_query_fp4",
-    "fp8_e4m3_values", "kv8_values", "KV8_ROW_BYTES",
+    "fp8_e4m3_values", "kv8_values", "KV8_ROW_BYTES", "compress_to_cache", "fp8_e4m3_round",
+    "compress_to_cache_kv8",
 ]

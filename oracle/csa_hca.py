@@ -102,6 +102,38 @@ def compress_to_cache(x, c: int) -> np.ndarray:
     return f64_to_bf16_bits(kv_compress(x, c))
 
 
+def fp8_e4m3_round(x) -> np.ndarray:
+    """FP8 E4M3 codes of fp64 values: the nearest finite E4M3 value (ties to the code
+    with an even mantissa), magnitudes beyond the largest finite value 448 clamped to
+    it, the sign kept (a negative value that rounds to zero gives -0).
+
+    Written as the definition: every non-negative finite magnitude is listed with its
+    code, and each input picks the closest one by brute force."""
+    x = np.asarray(x, dtype=np.float64)
+    codes = np.arange(128)
+    mags = fp8_e4m3_values(codes)
+    finite = ~np.isnan(mags)
+    codes, mags = codes[finite], mags[finite]          # 0x00 .. 0x7E, increasing
+    a = np.minimum(np.abs(x), mags[-1]).reshape(-1, 1)
+    dist = np.abs(a - mags[None, :])
+    best = dist.min(axis=1, keepdims=True)
+    tied = dist == best                                  # one or two candidates
+    even = tied & (codes[None, :] % 2 == 0)
+    pick = np.where(even.any(axis=1), np.argmax(even, axis=1), np.argmax(tied, axis=1))
+    out = codes[pick].reshape(x.shape) | np.where(np.signbit(x), 128, 0)
+    return out.astype(np.uint8)
+
+
+def compress_to_cache_kv8(x, c: int) -> np.ndarray:
+    """Compressed entries as stored in a mixed KV cache: rows [T // c, 192] (uint8)
+    holding the fp64 block means, dims 0..63 rounded once to FP8 E4M3 and dims
+    64..127 once to bf16 (the row format of kv8_values)."""
+    m = kv_compress(x, c)
+    lo = fp8_e4m3_round(m[:, :64])
+    hi = f64_to_bf16_bits(m[:, 64:]).astype("<u2").view(np.uint8).reshape(len(m), 128)
+    return np.concatenate([lo, hi], axis=1)
+
+
 # --------------------------------------------------------------------------------------
 # CSA selection
 

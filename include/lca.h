@@ -59,7 +59,7 @@
 extern "C" {
 #endif
 
-#define LCA_ABI_VERSION 5
+#define LCA_ABI_VERSION 6
 
 enum lca_status {
   LCA_OK = 0,
@@ -98,6 +98,21 @@ int32_t lca_workspace_reset(void* ws, size_t ws_bytes, void* stream);
 int32_t lca_kv_compress(const lca_bf16* x, const int64_t* tok_off, int32_t batch,
                         int32_t max_tokens, int32_t head_dim, int32_t c, lca_bf16* y,
                         const int64_t* ent_off, void* stream);
+
+/* kv_compress_kv8 — the same pooling into mixed KV rows (head_dim 128), the row
+ * format the _kv8 attention calls read (page section 3-2 item 2, component table:
+ * the cache keeps the RoPE dims in BF16, the rest in FP8; the last 64 dims are taken
+ * as the RoPE dims).
+ *   y        [*, 192] bytes, 16-byte aligned; entry rows at ent_off[b] .. as in
+ *            lca_kv_compress.  Bytes 0..63 of a row: dims 0..63 of the fp64 mean,
+ *            each rounded once to an FP8 E4M3 code (nearest, ties to the even code,
+ *            magnitudes above 448 clamped to 448, the sign kept); bytes 64..191:
+ *            dims 64..127 rounded once to bf16 (little-endian).
+ *   Other arguments and errors as lca_kv_compress (head_dim is 128).
+ */
+int32_t lca_kv_compress_kv8(const lca_bf16* x, const int64_t* tok_off, int32_t batch,
+                            int32_t max_tokens, int32_t c, uint8_t* y, const int64_t* ent_off,
+                            void* stream);
 
 /* ---------------------------------------------------------------------------
  * csa_index_score — indexer scores of every query row against its sequence's

@@ -49,6 +49,7 @@ _SIGS = {
     "lca_device_cu_count": (_i32, []),
     "lca_workspace_reset": (_i32, [_vp, _sz, _vp]),
     "lca_kv_compress": (_i32, [_vp, _vp, _i32, _i32, _i32, _i32, _vp, _vp, _vp]),
+    "lca_kv_compress_kv8": (_i32, [_vp, _vp, _i32, _i32, _i32, _vp, _vp, _vp]),
     "lca_csa_index_score": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _vp,
                                    _i64, _vp, _vp, _sz, _vp]),
     "lca_csa_index_score_fp4": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
@@ -142,6 +143,12 @@ def attn_workspace_bytes(rows, heads, max_q, splits=0) -> int:
 def kv_compress(x, tok_off, batch, max_tokens, c, y, ent_off, stream=None):
     _check("lca_kv_compress", _lib.lca_kv_compress(
         _p(x), _p(tok_off), batch, max_tokens, x.shape[-1], c, _p(y), _p(ent_off), _s(stream)))
+
+
+def kv_compress_kv8(x, tok_off, batch, max_tokens, c, y, ent_off, stream=None):
+    """y: uint8 [*, 192] mixed rows (dims 0..63 FP8 E4M3, dims 64..127 bf16)."""
+    _check("lca_kv_compress_kv8", _lib.lca_kv_compress_kv8(
+        _p(x), _p(tok_off), batch, max_tokens, c, _p(y), _p(ent_off), _s(stream)))
 
 
 def csa_index_score(q_idx, q_off, q_pos, k_idx, ent_off, batch, max_q, max_entries, c, scores,

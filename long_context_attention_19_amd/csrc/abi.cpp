@@ -188,6 +188,19 @@ int32_t lca_kv_compress(const lca_bf16* x, const int64_t* tok_off, int32_t batch
                     "kv_compress launch");
 }
 
+int32_t lca_kv_compress_kv8(const lca_bf16* x, const int64_t* tok_off, int32_t batch,
+                            int32_t max_tokens, int32_t c, uint8_t* y, const int64_t* ent_off,
+                            void* stream) {
+  if (batch < 0 || max_tokens < 0) return fail(LCA_ERR_SHAPE, "kv_compress_kv8: negative batch or max_tokens");
+  if (c < 1 || c > 4096) return fail(LCA_ERR_SHAPE, "kv_compress_kv8: ratio c=%d outside 1..4096", c);
+  if (batch == 0 || max_tokens / c == 0) return ok();
+  if (!x || !tok_off || !y || !ent_off) return fail(LCA_ERR_NULL, "kv_compress_kv8: NULL pointer");
+  if (!al16(x) || !al16(y)) return fail(LCA_ERR_ALIGN, "kv_compress_kv8: x / y not 16-byte aligned");
+  return hip_status(lca::launch_kv_compress_kv8(x, tok_off, batch, max_tokens, c, y, ent_off,
+                                                (hipStream_t)stream),
+                    "kv_compress_kv8 launch");
+}
+
 // ------------------------------------------------------------------ index scores
 static int32_t index_score_impl(const int8_t* q_idx, const int64_t* q_off, const int64_t* q_pos,
                             const int8_t* k_idx, const int64_t* ent_off, int32_t batch,

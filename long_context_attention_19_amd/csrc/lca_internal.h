@@ -10,6 +10,10 @@ namespace lca {
 hipError_t launch_kv_compress(const uint16_t* x, const int64_t* tok_off, int batch,
                               int max_tokens, int head_dim, int c, uint16_t* y,
                               const int64_t* ent_off, hipStream_t st);
+// mixed rows (head_dim 128): y holds KV8_ROW_BYTES per entry
+hipError_t launch_kv_compress_kv8(const uint16_t* x, const int64_t* tok_off, int batch,
+                                  int max_tokens, int c, uint8_t* y, const int64_t* ent_off,
+                                  hipStream_t st);
 
 // ------------------------------------------------------------ index scores
 constexpr int MAX_BATCH_LAYERS = 8;   // layers per batched launch (grid z)

@@ -30,7 +30,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_version_and_struct_layout():
-    assert lca.abi_version() == 5
+    assert lca.abi_version() == 6
     # 4 int32, 10 pointers, 4 window pointers, int32 window (+4 padding), sink pointer,
     # int32 idx_format, int32 kv_format
     assert ctypes.sizeof(lca.LcaLayer) == 16 + 10 * 8 + 4 * 8 + 8 + 8 + 8
@@ -51,6 +51,18 @@ def test_kv_compress_validation():
     assert f(FAKE, FAKE, 2, 100, 128, 0, FAKE, FAKE, None) == E_SHAPE  # ratio 0
     assert f(None, FAKE, 2, 100, 128, 4, FAKE, FAKE, None) == E_NULL
     assert f(MIS, FAKE, 2, 100, 128, 4, FAKE, FAKE, None) == E_ALIGN
+    assert "aligned" in lca.last_error()
+
+
+def test_kv_compress_kv8_validation():
+    f = L().lca_kv_compress_kv8
+    assert f(None, None, 0, 100, 4, None, None, None) == OK            # empty batch: nothing to do
+    assert f(FAKE, FAKE, 2, 3, 4, None, None, None) == OK              # no complete block
+    assert f(FAKE, FAKE, 2, 100, 0, FAKE, FAKE, None) == E_SHAPE       # ratio 0
+    assert f(FAKE, FAKE, 2, 100, 5000, FAKE, FAKE, None) == E_SHAPE    # ratio above 4096
+    assert f(FAKE, FAKE, -1, 100, 4, FAKE, FAKE, None) == E_SHAPE
+    assert f(FAKE, FAKE, 2, 100, 4, None, FAKE, None) == E_NULL
+    assert f(FAKE, FAKE, 2, 100, 4, MIS, FAKE, None) == E_ALIGN
     assert "aligned" in lca.last_error()
 
 

@@ -192,3 +192,73 @@ def test_hybrid_mixed_kv_formats():
                                           wkf[ws], wvf[ws], pos0[b], host["window"])
             assert_attn_close(O[b], r["o"], f"layer {li} seq {b}")
             assert_lse_close(LSE[b], r["lse"], f"layer {li} seq {b}")
+
+
+# ------------------------------------------------------------------ compression into mixed rows
+@pytest.mark.parametrize("c,lens,std", [(4, [37, 4099, 1000, 8195], 1.0),
+                                        (128, [127, 40000, 8300], 1.0),
+                                        (4, [4096, 333], 300.0),       # means beyond 448: clamped
+                                        (4, [4096], 2.0 ** -7),        # means in the subnormal codes
+                                        (1, [5, 300], 1.0), (3, [100, 7], 1.0)])
+def test_kv_compress_kv8_bit_exact(c, lens, std):
+    step(f"kv_compress_kv8 c={c} lens={lens} std={std}")
+    g = rng(340, c, len(lens))
+    raw = bf16_normal(g, (sum(lens), 128), std)
+    tok_off = offsets(lens)
+    ent_off = offsets([L // c for L in lens])
+    n = max(1, int(ent_off[-1]))
+    y = torch.full((n + 1, 192), 0xAB, dtype=torch.uint8, device=DEV)
+    yb = torch.zeros(n, 128, dtype=torch.bfloat16, device=DEV)
+    x = bf16_dev(raw)
+    lca.kv_compress_kv8(x, i64_dev(tok_off), len(lens), max(lens), c, y, i64_dev(ent_off))
+    lca.kv_compress(x, i64_dev(tok_off), len(lens), max(lens), c, yb, i64_dev(ent_off))
+    torch.cuda.synchronize()
+    got = y.cpu().numpy()
+    ref = np.concatenate([oracle.compress_to_cache_kv8(
+        oracle.bf16_bits_to_f64(raw[tok_off[b]:tok_off[b + 1]]), c) for b in range(len(lens))])
+    assert np.array_equal(got[: ent_off[-1]], ref)
+    assert np.all(got[ent_off[-1]:] == 0xAB)            # nothing past the last entry
+    # the bf16 half holds the same bits as the bf16 cache's dims 64..127
+    hi = np.ascontiguousarray(got[: ent_off[-1], 64:]).view("<u2")
+    assert np.array_equal(hi, yb.view(torch.int16).cpu().numpy().view(np.uint16)[: ent_off[-1], 64:])
+    if std > 100:
+        assert np.any(ref[:, :64] == 0x7E) and np.any(ref[:, :64] == 0xFE)
+    if std < 0.01:
+        assert np.any((ref[:, :64] & 0x78) == 0)          # subnormal codes occur
+
+
+def test_prefill_appends_mixed_rows_then_attends():
+    """Chunked prefill over a mixed cache: the new tokens are compressed into mixed rows
+    appended after the context's, then the chunk's queries attend over the whole cache."""
+    step("kv_compress_kv8 append + CsaStep kv8 prefill")
+    g = rng(341, 0, 0)
+    c, k, heads, n_ctx, t_new, nq = 4, 256, 64, 2000, 400, 40
+    ctx_len = n_ctx * c
+    n_new = t_new // c
+    Kctx, Vctx = kv8_normal(g, n_ctx), kv8_normal(g, n_ctx)
+    new_k, new_v = bf16_normal(g, (t_new, 128)), bf16_normal(g, (t_new, 128))
+    kidx = int8_uniform(g, (n_ctx + n_new, 64))
+    qidx, q = int8_uniform(g, (nq, 64)), bf16_normal(g, (nq, heads, 128))
+    q_pos = ctx_len + np.arange(0, t_new, t_new // nq)
+    Kc = torch.zeros(n_ctx + n_new, 192, dtype=torch.uint8, device=DEV)
+    Vc = torch.zeros(n_ctx + n_new, 192, dtype=torch.uint8, device=DEV)
+    Kc[:n_ctx], Vc[:n_ctx] = u8_dev(Kctx), u8_dev(Vctx)
+    for src, dst in ((new_k, Kc), (new_v, Vc)):
+        lca.kv_compress_kv8(bf16_dev(src), i64_dev([0, t_new]), 1, t_new, c, dst[n_ctx:],
+                            i64_dev([0, n_new]))
+    st = CsaStep(1, nq, n_ctx + n_new, heads, k, c, kv8=True)
+    out = torch.empty(nq, heads, 128, dtype=torch.bfloat16, device=DEV)
+    lse = torch.empty(nq, heads, dtype=torch.float32, device=DEV)
+    st.run(bf16_dev(q), i8_dev(qidx), i64_dev([0, nq]), i64_dev(q_pos), i8_dev(kidx), Kc, Vc,
+           i64_dev([0, n_ctx + n_new]), SCALE, out, lse)
+    torch.cuda.synchronize()
+    Kall = np.concatenate([Kctx, oracle.compress_to_cache_kv8(oracle.bf16_bits_to_f64(new_k), c)])
+    Vall = np.concatenate([Vctx, oracle.compress_to_cache_kv8(oracle.bf16_bits_to_f64(new_v), c)])
+    assert np.array_equal(Kc.cpu().numpy(), Kall) and np.array_equal(Vc.cpu().numpy(), Vall)
+    O, LSE = bf16_vals(out), lse.cpu().numpy()
+    Kf, Vf, qf = oracle.kv8_values(Kall), oracle.kv8_values(Vall), oracle.bf16_bits_to_f64(q)
+    for i in range(nq):
+        ref = oracle.csa_query(qf[i], qidx[i], int(q_pos[i]), Kf, Vf, kidx, c, k, SCALE)
+        assert np.array_equal(st.idx[i, :st.count[i]].cpu().numpy(), ref["idx"]), i
+        assert_attn_close(O[i], ref["o"], f"row {i}")
+        assert_lse_close(LSE[i], ref["lse"], f"row {i}")

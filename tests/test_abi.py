@@ -92,6 +92,10 @@ def test_topk_validation_and_sizes():
     assert f(*bad) == E_SHAPE                          # unknown flag
     bad = list(args); bad[3] = 1 << 30; bad[1] = 1 << 30
     assert f(*bad) == E_UNSUP                          # beyond the resolver's chunk table
+    edge = list(args); edge[3] = 1024 * 4096; edge[1] = 1024 * 4096
+    assert f(*edge[:9], 0, 0, None) == E_WS            # the longest row passes the size checks
+    edge[3] += 1
+    assert f(*edge) == E_UNSUP                         # one entry more does not
     bad = list(args); bad[6] = None
     assert f(*bad) == E_NULL
     n1 = lca.csa_topk_workspace_bytes(4, 262144, 2048)

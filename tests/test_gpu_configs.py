@@ -274,3 +274,36 @@ def test_prefill_full():
         _check_csa_row(_f64(inp["q"][i]), inp["q_idx"][i].cpu().numpy(), wl.ctx_len + int(i),
                        run.k_cmp, run.v_cmp, kidx, c, wl.topk, idx[i], cnt[i], out[i], lse[i],
                        f"prefill row {i}")
+
+
+def test_csa_decode_at_the_largest_row():
+    """The longest row the top-k takes (1024 chunks of 4096: 4,194,304 compressed
+    entries, a 16.8M-token context at c = 4) and a ragged one 77 entries shorter, one
+    decode token each: selections bit-exact, attention within the bars."""
+    from long_context_attention_19_amd.pipeline import CsaStep
+
+    step("CSA decode at the largest row: 4,194,304 entries")
+    nmax = 1024 * 4096
+    Ns, heads, c, k = [nmax, nmax - 77], 64, 4, 2048
+    B = len(Ns)
+    ent_off = np.concatenate([[0], np.cumsum(Ns)]).astype(np.int64)
+    tot = int(ent_off[-1])
+    seed = lambda t: workloads.seed_of(970, 0, t)
+    kidx = workloads.device_int8_uniform((tot, 64), seed(2))
+    Kc = workloads.device_bf16_normal((tot, 128), seed(0), std=0.5)
+    Vc = workloads.device_bf16_normal((tot, 128), seed(1), std=0.5)
+    q = workloads.device_bf16_normal((B, heads, 128), seed(3))
+    qidx = workloads.device_int8_uniform((B, 64), seed(4))
+    L = [n * c + 3 for n in Ns]   # 3 tail tokens: every complete block is visible
+    dev = lambda a: torch.from_numpy(np.asarray(a, dtype=np.int64)).to(q.device)
+    st = CsaStep(B, 1, nmax, heads, k, c)
+    out = torch.empty(B, heads, 128, dtype=torch.bfloat16, device=q.device)
+    lse = torch.empty(B, heads, dtype=torch.float32, device=q.device)
+    st.run(q, qidx, dev(np.arange(B + 1)), dev(L), kidx, Kc, Vc, dev(ent_off), SCALE, out, lse)
+    torch.cuda.synchronize()
+    idx, cnt = st.idx.cpu().numpy(), st.count.cpu().numpy()
+    O, LSE, qi = _f64(out), lse.cpu().numpy(), qidx.cpu().numpy()
+    for b in range(B):
+        s, e = int(ent_off[b]), int(ent_off[b + 1])
+        _check_csa_row(_f64(q[b]), qi[b], L[b], Kc[s:e], Vc[s:e], kidx[s:e].cpu().numpy(), c, k,
+                       idx[b], cnt[b], O[b], LSE[b], f"largest row, seq {b}")

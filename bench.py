@@ -11,7 +11,8 @@ csa_prefill_256k, hybrid_decode_1m_swa: the stack with a 128-token sliding windo
 every layer, hybrid_decode_1m_swa_sink: that and a per-head attention sink on every
 layer, hybrid_decode_1m_fp4: the stack with the FP4 indexer, hybrid_decode_1m_kv8: the
 stack over mixed FP8 / bf16 KV rows, csa_decode_1m_fp4: the 1M CSA decode with the FP4
-indexer) can be named with --workload.  A step is one pass of the
+indexer, csa_prefill_256k_fp4: the prefill chunk with the FP4 indexer) can be named with
+--workload.  A step is one pass of the
 workload's whole path over one batch; inputs are seeded, synthetic and resident
 in HBM before timing starts.  Decode workloads smaller than the 256 MB
 last-level cache rotate input replicas so that each step reads from HBM.
@@ -499,7 +500,7 @@ class PrefillRunner(_Capture):
         self.ent_off = i64([0, inp["n_ent"]])
         self.q_off = i64([0, new])
         self.q_pos = torch.arange(ctx, ctx + new, dtype=torch.int64, device=device)
-        self.st = CsaStep(1, new, inp["n_ent"], wl.heads, wl.topk, c, device)
+        self.st = CsaStep(1, new, inp["n_ent"], wl.heads, wl.topk, c, device, fp4=wl.idx_fp4)
         self.out = torch.empty(new, wl.heads, 128, dtype=torch.bfloat16, device=device)
         self.lse = torch.empty(new, wl.heads, dtype=torch.float32, device=device)
         self.tokens_per_step = new
@@ -517,7 +518,8 @@ class PrefillRunner(_Capture):
     def step_bytes(self):
         wl = self.wl
         new = wl.new_tokens
-        return (new * 128 * 2 * 2 + (new // wl.c) * 512 + self.inp["n_ent"] * 64 + new * 64 +
+        kb = 32 if wl.idx_fp4 else 64   # indexer key / query bytes
+        return (new * 128 * 2 * 2 + (new // wl.c) * 512 + self.inp["n_ent"] * kb + new * kb +
                 new * wl.heads * QO_BYTES_PER_HEAD + self.inp["n_ent"] * 512)
 
     def dominant_launch(self):
@@ -547,7 +549,8 @@ class PrefillRunner(_Capture):
                 q = oracle.bf16_bits_to_f64(_bits(inp["q"][i]))
                 qi = inp["q_idx"][i].cpu().numpy()
                 t0 = time.perf_counter()
-                oracle.csa_query(q, qi, wl.ctx_len + int(i), Kc, Vc, kidx, wl.c, wl.topk, SCALE)
+                query = oracle.csa_query_fp4 if wl.idx_fp4 else oracle.csa_query
+                query(q, qi, wl.ctx_len + int(i), Kc, Vc, kidx, wl.c, wl.topk, SCALE)
                 t_or += time.perf_counter() - t0
                 done += 1
         return {"value": done / t_or, "unit": "tokens/s", "cores": 1, "kind": "oracle",

@@ -154,7 +154,8 @@ int32_t lca_csa_index_score(const int8_t* q_idx, const int64_t* q_off, const int
  *
  *   q_fp4    [rows, 32] uint8, k_fp4 [ent_off[B], 32] uint8; 16-byte aligned.
  *   Every other argument as lca_csa_index_score (d_idx == 64).  Query batches of
- *   any size run the same per-row kernel.
+ *   any size run the same per-row kernel; for prefill-sized batches
+ *   lca_csa_index_select_fp4 selects without writing the scores.
  * ------------------------------------------------------------------------- */
 int32_t lca_csa_index_score_fp4(const uint8_t* q_fp4, const int64_t* q_off, const int64_t* q_pos,
                                 const uint8_t* k_fp4, const int64_t* ent_off, int32_t batch,
@@ -187,6 +188,18 @@ int32_t lca_csa_index_select(const int8_t* q_idx, const int64_t* q_off, const in
                              int32_t max_q, int32_t max_entries, int32_t d_idx, int32_t c,
                              int32_t k, int32_t* idx, int32_t* count, int32_t* n_vis,
                              void* stream);
+
+/* csa_index_select_fp4 — the same selection over FP4 indexer codes: exactly what
+ * lca_csa_index_score_fp4 followed by lca_csa_topk_select gives.  The sweeps score
+ * with the FP4 MFMA (v_mfma_scale_f32_16x16x128_f8f6f4, E2M1 operands, unit scales).
+ *   q_fp4 [rows, 32], k_fp4 [ent_off[B], 32] packed E2M1 codes as for
+ *   lca_csa_index_score_fp4; every other argument and error as lca_csa_index_select.
+ */
+int32_t lca_csa_index_select_fp4(const uint8_t* q_fp4, const int64_t* q_off, const int64_t* q_pos,
+                                 const uint8_t* k_fp4, const int64_t* ent_off, int32_t batch,
+                                 int32_t max_q, int32_t max_entries, int32_t d_idx, int32_t c,
+                                 int32_t k, int32_t* idx, int32_t* count, int32_t* n_vis,
+                                 void* stream);
 
 /* ---------------------------------------------------------------------------
  * csa_topk_select — per row, the top min(k, n_vis[r]) entries of

@@ -56,6 +56,8 @@ _SIGS = {
                                        _vp, _i64, _vp, _vp, _sz, _vp]),
     "lca_csa_index_select": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32,
                                     _vp, _vp, _vp, _vp]),
+    "lca_csa_index_select_fp4": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
+                                        _i32, _vp, _vp, _vp, _vp]),
     "lca_window_attn": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
                                _f32, _vp, _vp, _vp]),
     "lca_attn_sink": (_i32, [_vp, _vp, _vp, _i64, _i32, _i32, _vp]),
@@ -173,6 +175,14 @@ def csa_index_select(q_idx, q_off, q_pos, k_idx, ent_off, batch, max_q, max_entr
     _check("lca_csa_index_select", _lib.lca_csa_index_select(
         _p(q_idx), _p(q_off), _p(q_pos), _p(k_idx), _p(ent_off), batch, max_q, max_entries,
         q_idx.shape[-1], c, k, _p(idx), _p(count), _p(n_vis), _s(stream)))
+
+
+def csa_index_select_fp4(q_fp4, q_off, q_pos, k_fp4, ent_off, batch, max_q, max_entries, c, k,
+                         idx, count, n_vis=None, stream=None):
+    """q_fp4 [rows, 32] / k_fp4 [entries, 32] uint8 packed E2M1 codes (d_idx = 64)."""
+    _check("lca_csa_index_select_fp4", _lib.lca_csa_index_select_fp4(
+        _p(q_fp4), _p(q_off), _p(q_pos), _p(k_fp4), _p(ent_off), batch, max_q, max_entries,
+        2 * q_fp4.shape[-1], c, k, _p(idx), _p(count), _p(n_vis), _s(stream)))
 
 
 def window_attn(q, win_k, win_v, win_off, win_pos0, q_off, q_pos, batch, max_q, window, scale,

@@ -256,23 +256,44 @@ int32_t lca_csa_index_score_fp4(const uint8_t* q_fp4, const int64_t* q_off, cons
 }
 
 // ------------------------------------------------------------------ fused scores + top-k
+static int32_t index_select_impl(const int8_t* q_idx, const int64_t* q_off, const int64_t* q_pos,
+                                 const int8_t* k_idx, const int64_t* ent_off, int32_t batch,
+                                 int32_t max_q, int32_t max_entries, int32_t d_idx, int32_t c,
+                                 int32_t k, int32_t* idx, int32_t* count, int32_t* n_vis,
+                                 void* stream, bool fp4) {
+  const char* name = fp4 ? "csa_index_select_fp4" : "csa_index_select";
+  if (d_idx != 64) return fail(LCA_ERR_UNSUPPORTED, "%s: d_idx=%d (only 64)", name, d_idx);
+  if (batch < 0 || max_q < 0 || max_entries < 0) return fail(LCA_ERR_SHAPE, "%s: negative size", name);
+  if (c < 1) return fail(LCA_ERR_SHAPE, "%s: ratio c=%d < 1", name, c);
+  if (k <= 0) return fail(LCA_ERR_SHAPE, "%s: k=%d must be positive", name, k);
+  if (batch == 0 || max_q == 0) return ok();
+  if (max_q < lca::SELECT_MIN_Q) return fail(LCA_ERR_UNSUPPORTED, "%s: max_q=%d below %d (use the score + csa_topk_select pair)", name, max_q, lca::SELECT_MIN_Q);
+  if ((int64_t)batch * max_q > (1 << 30)) return fail(LCA_ERR_SHAPE, "%s: too many rows", name);
+  if ((int64_t)batch * max_q * k > ((int64_t)1 << 40)) return fail(LCA_ERR_SHAPE, "%s: output too large", name);
+  if (!q_idx || !q_off || !q_pos || !k_idx || !ent_off || !idx || !count) return fail(LCA_ERR_NULL, "%s: NULL pointer", name);
+  if (!al16(q_idx) || !al16(k_idx)) return fail(LCA_ERR_ALIGN, "%s: q_idx / k_idx not 16-byte aligned", name);
+  lca::SelectArgs a{q_idx, k_idx, ent_off, q_off, q_pos, idx, count, n_vis, c, max_entries, max_q, k,
+                    fp4 ? 1 : 0};
+  return hip_status(lca::launch_index_select(a, batch, (hipStream_t)stream), name);
+}
+
 int32_t lca_csa_index_select(const int8_t* q_idx, const int64_t* q_off, const int64_t* q_pos,
                              const int8_t* k_idx, const int64_t* ent_off, int32_t batch,
                              int32_t max_q, int32_t max_entries, int32_t d_idx, int32_t c,
                              int32_t k, int32_t* idx, int32_t* count, int32_t* n_vis,
                              void* stream) {
-  if (d_idx != 64) return fail(LCA_ERR_UNSUPPORTED, "csa_index_select: d_idx=%d (only 64)", d_idx);
-  if (batch < 0 || max_q < 0 || max_entries < 0) return fail(LCA_ERR_SHAPE, "csa_index_select: negative size");
-  if (c < 1) return fail(LCA_ERR_SHAPE, "csa_index_select: ratio c=%d < 1", c);
-  if (k <= 0) return fail(LCA_ERR_SHAPE, "csa_index_select: k=%d must be positive", k);
-  if (batch == 0 || max_q == 0) return ok();
-  if (max_q < lca::SELECT_MIN_Q) return fail(LCA_ERR_UNSUPPORTED, "csa_index_select: max_q=%d below %d (use csa_index_score + csa_topk_select)", max_q, lca::SELECT_MIN_Q);
-  if ((int64_t)batch * max_q > (1 << 30)) return fail(LCA_ERR_SHAPE, "csa_index_select: too many rows");
-  if ((int64_t)batch * max_q * k > ((int64_t)1 << 40)) return fail(LCA_ERR_SHAPE, "csa_index_select: output too large");
-  if (!q_idx || !q_off || !q_pos || !k_idx || !ent_off || !idx || !count) return fail(LCA_ERR_NULL, "csa_index_select: NULL pointer");
-  if (!al16(q_idx) || !al16(k_idx)) return fail(LCA_ERR_ALIGN, "csa_index_select: q_idx / k_idx not 16-byte aligned");
-  lca::SelectArgs a{q_idx, k_idx, ent_off, q_off, q_pos, idx, count, n_vis, c, max_entries, max_q, k};
-  return hip_status(lca::launch_index_select(a, batch, (hipStream_t)stream), "csa_index_select launch");
+  return index_select_impl(q_idx, q_off, q_pos, k_idx, ent_off, batch, max_q, max_entries, d_idx,
+                           c, k, idx, count, n_vis, stream, false);
+}
+
+int32_t lca_csa_index_select_fp4(const uint8_t* q_fp4, const int64_t* q_off, const int64_t* q_pos,
+                                 const uint8_t* k_fp4, const int64_t* ent_off, int32_t batch,
+                                 int32_t max_q, int32_t max_entries, int32_t d_idx, int32_t c,
+                                 int32_t k, int32_t* idx, int32_t* count, int32_t* n_vis,
+                                 void* stream) {
+  return index_select_impl(reinterpret_cast<const int8_t*>(q_fp4), q_off, q_pos,
+                           reinterpret_cast<const int8_t*>(k_fp4), ent_off, batch, max_q,
+                           max_entries, d_idx, c, k, idx, count, n_vis, stream, true);
 }
 
 // ------------------------------------------------------------------ top-k

@@ -34,6 +34,13 @@
 // Operand layout of the MFMA (both operands: lane l supplies row l % 16 of its
 // matrix and bytes 16 (l / 16) .. + 15 of it; result: lane l holds entries
 // 4 (l / 16) + r, r < 4, of query token l % 16) as in the prefill scoring GEMM.
+//
+// FP4 indexer (query and keys packed E2M1, 32 bytes per vector): the scores come
+// from v_mfma_scale_f32_16x16x128_f8f6f4 with both operands E2M1 and unit scales.
+// Lane l supplies row l % 16 and elements 32 (l / 16) .. + 31 (16 bytes) of its
+// operand; d_idx = 64 fills elements 0..63, so lanes 32..63 supply zeros.  The
+// result has the int8 form's layout; the fp32 sums are exact (quarter multiples far
+// below 2^24) and the score is 256 x the sum, the unit of csa_index_score_fp4.
 #include "lca_device.h"
 #include "lca_internal.h"
 
@@ -71,45 +78,64 @@ __device__ __forceinline__ void sl_lds_barrier() {   // LDS traffic only: no mem
 // Keys of one 64-entry block: tile u, lane l -> entry blk*64 + 16u + l%16, bytes
 // 16 (l/16) ..; entries past N re-read entry N-1 (their scores are never used).
 // Ordinary loads: the keys are shared by every row tile and should stay in L2.
+// FP4 keys are 2 x 16 bytes: lanes 32..63 load nothing and hold zeros.
+template <bool FP4>
 __device__ __forceinline__ void sl_load(i32x4 (&kv)[4], const i32x4* __restrict__ kp, int32_t blk,
                                         int32_t N, int lane) {
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
     const int32_t j = min(blk * SL_BLOCK + 16 * u + (lane & 15), N - 1);
-    kv[u] = kp[j * 4 + (lane >> 4)];
+    if (FP4)
+      kv[u] = lane < 32 ? kp[j * 2 + (lane >> 4)] : i32x4{0, 0, 0, 0};
+    else
+      kv[u] = kp[j * 4 + (lane >> 4)];
   }
 }
 
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
 // The block's 16 keys (score + 2^20) of this lane's token: [tile u][r].
+template <bool FP4>
 __device__ __forceinline__ void sl_keys(const i32x4 (&kv)[4], const i32x4& qv, int32_t (&key)[4][4]) {
   const i32x4 zero4 = {0, 0, 0, 0};
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
-    const i32x4 acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(kv[u], qv, zero4, 0, 0, 0);
+    if (FP4) {
+      constexpr int FP4_E2M1 = 4, UNIT_SCALE = 127;   // operand format code, E8M0 2^0
+      const i32x8 ka = {kv[u][0], kv[u][1], kv[u][2], kv[u][3], 0, 0, 0, 0};
+      const i32x8 qb = {qv[0], qv[1], qv[2], qv[3], 0, 0, 0, 0};
+      const f32x4_t acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+          ka, qb, f32x4_t{0.f, 0.f, 0.f, 0.f}, FP4_E2M1, FP4_E2M1, 0, UNIT_SCALE, 0, UNIT_SCALE);
 #pragma unroll
-    for (int r = 0; r < 4; ++r) key[u][r] = acc[r] + KEY_BIAS;
+      for (int r = 0; r < 4; ++r) key[u][r] = (int32_t)(acc[r] * 256.f) + KEY_BIAS;
+    } else {
+      const i32x4 acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(kv[u], qv, zero4, 0, 0, 0);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) key[u][r] = acc[r] + KEY_BIAS;
+    }
   }
 }
 
 // One sweep over the work-group's blocks, keys loaded two rounds ahead; `body`
 // gets (keys, round, block).  Every wave runs every round (a block past the end
 // has no visible entry), so bodies may hold work-group barriers.
-template <class Body>
+template <bool FP4, class Body>
 __device__ __forceinline__ void sl_sweep(const i32x4* __restrict__ kp, const i32x4& qv, int32_t N,
                                          int32_t nround, int w, int lane, Body&& body) {
   i32x4 ka[4], kb[4], kc[4];
   int32_t key[4][4];
-  sl_load(ka, kp, w, N, lane);
-  sl_load(kb, kp, SL_NW + w, N, lane);
+  sl_load<FP4>(ka, kp, w, N, lane);
+  sl_load<FP4>(kb, kp, SL_NW + w, N, lane);
   for (int32_t rd = 0; rd < nround; rd += 3) {
-    sl_load(kc, kp, (rd + 2) * SL_NW + w, N, lane);
-    sl_keys(ka, qv, key);
+    sl_load<FP4>(kc, kp, (rd + 2) * SL_NW + w, N, lane);
+    sl_keys<FP4>(ka, qv, key);
     body(key, rd, rd * SL_NW + w);
-    sl_load(ka, kp, (rd + 3) * SL_NW + w, N, lane);
-    sl_keys(kb, qv, key);
+    sl_load<FP4>(ka, kp, (rd + 3) * SL_NW + w, N, lane);
+    sl_keys<FP4>(kb, qv, key);
     body(key, rd + 1, (rd + 1) * SL_NW + w);
-    sl_load(kb, kp, (rd + 4) * SL_NW + w, N, lane);
-    sl_keys(kc, qv, key);
+    sl_load<FP4>(kb, kp, (rd + 4) * SL_NW + w, N, lane);
+    sl_keys<FP4>(kc, qv, key);
     body(key, rd + 2, (rd + 2) * SL_NW + w);
   }
 }
@@ -146,6 +172,7 @@ __device__ __forceinline__ void sl_threshold(const int32_t* h, int j, int need, 
 // entries (score desc, index asc), and writes the row: each entry's slot is its
 // rank in its own list plus the number of selected entries of the other list
 // with a lower index.
+template <bool FP4>
 __device__ __forceinline__ void sl_collect_finalize(
     const i32x4* __restrict__ kp, const i32x4& qv, int32_t N, int32_t nround, int w, int lane,
     int n, int grp, int32_t nv, int32_t bA, int k, int nr, int32_t* sm, int32_t* s_tot,
@@ -155,7 +182,7 @@ __device__ __forceinline__ void sl_collect_finalize(
   int32_t* alist = sm + SL_FRONT;                  // [16][SL_STAGE_K] indices above bA
   int32_t a_base = 0, b_base = 0;
   __syncthreads();
-  sl_sweep(kp, qv, N, nround, w, lane, [&](const int32_t (&key)[4][4], int32_t rd, int32_t blk) __attribute__((always_inline)) {
+  sl_sweep<FP4>(kp, qv, N, nround, w, lane, [&](const int32_t (&key)[4][4], int32_t rd, int32_t blk) __attribute__((always_inline)) {
     uint32_t ba[4], bb[4];
     int32_t ex[4];
     int32_t wtot = 0;
@@ -286,7 +313,7 @@ __device__ __forceinline__ void sl_collect_finalize(
   }
 }
 
-template <bool STAGE>
+template <bool STAGE, bool FP4>
 __global__ __launch_bounds__(SL_NT) void index_select_kernel(SelectArgs a, int tiles_per_seq) {
   __shared__ __attribute__((aligned(16))) int32_t sm[SL_LDS];
   __shared__ int32_t s_bin[SL_ROWS], s_above[SL_ROWS], s_tot[SL_ROWS], s_flag;
@@ -335,16 +362,18 @@ __global__ __launch_bounds__(SL_NT) void index_select_kernel(SelectArgs a, int t
   const int32_t nblk = (nvmax + SL_BLOCK - 1) / SL_BLOCK;
   const int32_t nround = (nblk + SL_NW - 1) / SL_NW;
 
-  const i32x4* kp = reinterpret_cast<const i32x4*>(a.k_idx + e0 * 64);
+  constexpr int VB = FP4 ? 32 : 64;        // bytes per indexer vector
+  const i32x4* kp = reinterpret_cast<const i32x4*>(a.k_idx + e0 * VB);
   const i32x4 zero4 = {0, 0, 0, 0};
-  const i32x4 qv = qok ? *reinterpret_cast<const i32x4*>(a.q_idx + row * 64 + 16 * grp) : zero4;
+  const i32x4 qv = qok && 16 * grp < VB ? *reinterpret_cast<const i32x4*>(a.q_idx + row * VB + 16 * grp)
+                                        : zero4;
 
   if (nvmax > 0 && any_thr) {
     // ---- sweep 1: coarse histograms
     for (int i = t; i < SL_ROWS * HIST_BINS; i += SL_NT) sm[i] = 0;
     __syncthreads();
     int32_t* hc = sm + n * HIST_BINS;
-    sl_sweep(kp, qv, N, nround, w, lane, [&](const int32_t (&key)[4][4], int32_t, int32_t blk) __attribute__((always_inline)) {
+    sl_sweep<FP4>(kp, qv, N, nround, w, lane, [&](const int32_t (&key)[4][4], int32_t, int32_t blk) __attribute__((always_inline)) {
 #pragma unroll
       for (int u = 0; u < 4; ++u)
 #pragma unroll
@@ -366,7 +395,7 @@ __global__ __launch_bounds__(SL_NT) void index_select_kernel(SelectArgs a, int t
     if (t < nr && s_bin[t] >= 0 && sm[t * HIST_BINS + (s_bin[t] ^ t)] > SL_BIN_CAP) s_flag = 0;
     __syncthreads();
     if (s_flag) {
-      sl_collect_finalize(kp, qv, N, nround, w, lane, n, grp, nv, thr ? s_bin[n] : -1, k, nr,
+      sl_collect_finalize<FP4>(kp, qv, N, nround, w, lane, n, grp, nv, thr ? s_bin[n] : -1, k, nr,
                           sm, s_tot, s_na, s_nb, idx0);
       return;
     }
@@ -375,7 +404,7 @@ __global__ __launch_bounds__(SL_NT) void index_select_kernel(SelectArgs a, int t
     for (int i = t; i < SL_ROWS * FINE_BINS; i += SL_NT) sm[i] = 0;
     __syncthreads();
     int32_t* hf = sm + n * FINE_BINS;
-    sl_sweep(kp, qv, N, nround, w, lane, [&](const int32_t (&key)[4][4], int32_t, int32_t blk) __attribute__((always_inline)) {
+    sl_sweep<FP4>(kp, qv, N, nround, w, lane, [&](const int32_t (&key)[4][4], int32_t, int32_t blk) __attribute__((always_inline)) {
 #pragma unroll
       for (int u = 0; u < 4; ++u)
 #pragma unroll
@@ -413,7 +442,7 @@ __global__ __launch_bounds__(SL_NT) void index_select_kernel(SelectArgs a, int t
   int32_t a_base = 0, e_base = 0;                 // selected-above / T-valued so far (row n)
   __syncthreads();
   if (nvmax > 0) {
-    sl_sweep(kp, qv, N, nround, w, lane, [&](const int32_t (&key)[4][4], int32_t rd, int32_t blk) __attribute__((always_inline)) {
+    sl_sweep<FP4>(kp, qv, N, nround, w, lane, [&](const int32_t (&key)[4][4], int32_t rd, int32_t blk) __attribute__((always_inline)) {
       // Counts are packed (T-valued << 16 | above); a round adds at most 1024 to
       // either half.  Within the wave, segment (tile u, lane group g) precedes
       // (u, g') for g < g' and every segment of tiles after u: a scan over the
@@ -501,10 +530,14 @@ hipError_t launch_index_select(const SelectArgs& a, int batch, hipStream_t st) {
   if (batch == 0 || a.max_q == 0) return hipSuccess;
   const int tiles = (a.max_q + SL_ROWS - 1) / SL_ROWS;
   dim3 grid(1, (unsigned)(batch * tiles));
-  if (a.k <= SL_STAGE_K)
-    hipLaunchKernelGGL(index_select_kernel<true>, grid, dim3(SL_NT), 0, st, a, tiles);
-  else
-    hipLaunchKernelGGL(index_select_kernel<false>, grid, dim3(SL_NT), 0, st, a, tiles);
+  const bool stage = a.k <= SL_STAGE_K;
+  if (a.fp4) {
+    if (stage) hipLaunchKernelGGL((index_select_kernel<true, true>), grid, dim3(SL_NT), 0, st, a, tiles);
+    else hipLaunchKernelGGL((index_select_kernel<false, true>), grid, dim3(SL_NT), 0, st, a, tiles);
+  } else {
+    if (stage) hipLaunchKernelGGL((index_select_kernel<true, false>), grid, dim3(SL_NT), 0, st, a, tiles);
+    else hipLaunchKernelGGL((index_select_kernel<false, false>), grid, dim3(SL_NT), 0, st, a, tiles);
+  }
   return hipGetLastError();
 }
 

@@ -58,6 +58,7 @@ struct SelectArgs {
   int32_t max_entries;
   int32_t max_q;
   int32_t k;
+  int32_t fp4;      // q_idx / k_idx hold packed FP4 codes (32 bytes per vector)
 };
 constexpr int SELECT_MIN_Q = 16;
 hipError_t launch_index_select(const SelectArgs& a, int batch, hipStream_t st);

@@ -3,8 +3,8 @@
 CsaStep   selection, then csa_sparse_attn.  Selection is csa_index_score (with the
           fused first radix pass) -> csa_topk_select for decode (fewer than 16
           queries per sequence), and csa_index_select (scores never written) for
-          chunked prefill (16 or more queries per sequence); with the FP4 indexer,
-          csa_index_score_fp4 -> csa_topk_select for any query batch.
+          chunked prefill (16 or more queries per sequence); the FP4 indexer takes
+          csa_index_score_fp4 and csa_index_select_fp4 in the same places.
 HcaStep   hca_dense_attn.
 HybridStep  hybrid_layer_step over a list of CSA / HCA layers.
 
@@ -17,6 +17,7 @@ import torch
 
 from . import (LCA_IDX_FP4, LCA_IDX_INT8, LCA_KV_BF16, LCA_KV_MIXED, LCA_LAYER_CSA, LCA_LAYER_HCA,
                attn_workspace_bytes, csa_index_score, csa_index_score_fp4, csa_index_select,
+               csa_index_select_fp4,
                csa_sparse_attn, csa_sparse_attn_kv8, csa_topk_select, csa_topk_workspace_bytes,
                hca_dense_attn, hca_dense_attn_kv8, hybrid_layer_step, hybrid_workspace_bytes,
                make_layers, workspace)
@@ -32,8 +33,8 @@ def _round4(n: int) -> int:
 class CsaStep:
     """fused: None picks csa_index_select when max_q >= 16; True / False force it
     on / off (the two-call path materialises the scores in self.scores).  fp4: the
-    indexer query / keys are packed FP4 codes (csa_index_score_fp4, never fused); kv8: the
-    cache holds mixed FP8 / bf16 rows (csa_sparse_attn_kv8)."""
+    indexer query / keys are packed FP4 codes (the _fp4 scoring and selection calls);
+    kv8: the cache holds mixed FP8 / bf16 rows (csa_sparse_attn_kv8)."""
 
     def __init__(self, batch, max_q, max_entries, heads, topk, c, device="cuda", splits=0,
                  fused=None, fp4=False, kv8=False):
@@ -42,7 +43,7 @@ class CsaStep:
         rows = batch * max_q
         self.rows = rows
         self.fp4, self.kv8 = fp4, kv8
-        self.fused = False if fp4 else (max_q >= SELECT_MIN_Q) if fused is None else fused
+        self.fused = (max_q >= SELECT_MIN_Q) if fused is None else fused
         self.n_vis = torch.empty(rows, dtype=torch.int32, device=device)
         self.idx = torch.empty(rows, topk, dtype=torch.int32, device=device)
         self.count = torch.empty(rows, dtype=torch.int32, device=device)
@@ -54,9 +55,9 @@ class CsaStep:
 
     def select(self, q_idx, q_off, q_pos, k_idx, ent_off, stream=None):
         if self.fused:
-            csa_index_select(q_idx, q_off, q_pos, k_idx, ent_off, self.batch, self.max_q,
-                             self.max_entries, self.c, self.topk, self.idx, self.count,
-                             self.n_vis, stream=stream)
+            sel = csa_index_select_fp4 if self.fp4 else csa_index_select
+            sel(q_idx, q_off, q_pos, k_idx, ent_off, self.batch, self.max_q, self.max_entries,
+                self.c, self.topk, self.idx, self.count, self.n_vis, stream=stream)
             return
         score = csa_index_score_fp4 if self.fp4 else csa_index_score
         score(q_idx, q_off, q_pos, k_idx, ent_off, self.batch, self.max_q, self.max_entries,

@@ -54,6 +54,28 @@ def test_kv_compress_validation():
     assert "aligned" in lca.last_error()
 
 
+@pytest.mark.parametrize("fn", ["lca_csa_index_select", "lca_csa_index_select_fp4"])
+def test_index_select_validation(fn):
+    f = getattr(L(), fn)
+    # q, q_off, q_pos, k, ent_off, batch, max_q, max_entries, d_idx, c, k, idx, count, n_vis
+    args = [FAKE] * 5 + [2, 32, 1000, 64, 4, 256, FAKE, FAKE, None, None]
+    bad = list(args); bad[8] = 32
+    assert f(*bad) == E_UNSUP                          # d_idx other than 64
+    bad = list(args); bad[6] = 8
+    assert f(*bad) == E_UNSUP                          # fewer than 16 query tokens per sequence
+    assert "16" in lca.last_error()
+    bad = list(args); bad[10] = 0
+    assert f(*bad) == E_SHAPE                          # k = 0
+    bad = list(args); bad[9] = 0
+    assert f(*bad) == E_SHAPE                          # ratio 0
+    bad = list(args); bad[3] = None
+    assert f(*bad) == E_NULL
+    bad = list(args); bad[0] = MIS
+    assert f(*bad) == E_ALIGN
+    bad = list(args); bad[5] = 0
+    assert f(*bad) == OK                               # empty batch: nothing to do
+
+
 def test_kv_compress_kv8_validation():
     f = L().lca_kv_compress_kv8
     assert f(None, None, 0, 100, 4, None, None, None) == OK            # empty batch: nothing to do

@@ -245,9 +245,10 @@ def test_hybrid_kv8_full():
             assert_lse_close(lse[b], ref["lse"], f"layer {li} seq {b}")
 
 
-def test_prefill_full():
-    step("full-size csa_prefill_256k")
-    wl = workloads.get("csa_prefill_256k")
+@pytest.mark.parametrize("name", ["csa_prefill_256k", "csa_prefill_256k_fp4"])
+def test_prefill_full(name):
+    step(f"full-size {name}")
+    wl = workloads.get(name)
     run = bench.PrefillRunner(wl)
     run.step(0)
     torch.cuda.synchronize()
@@ -273,7 +274,7 @@ def test_prefill_full():
     for i in rows:
         _check_csa_row(_f64(inp["q"][i]), inp["q_idx"][i].cpu().numpy(), wl.ctx_len + int(i),
                        run.k_cmp, run.v_cmp, kidx, c, wl.topk, idx[i], cnt[i], out[i], lse[i],
-                       f"prefill row {i}")
+                       f"{name} row {i}", wl.idx_fp4)
 
 
 def test_csa_decode_at_the_largest_row():

@@ -93,6 +93,60 @@ def test_index_score_fp4_extremes():
     assert S[0, :N].max() == 589824 and S[0, :N].min() == -589824 and S[0, N] == 12345
 
 
+def _select_fp4_case(name):
+    g = rng(325, ["ragged", "prefill_tile", "k_large", "ties", "extremes"].index(name), 0)
+    if name == "ragged":          # an empty sequence, one shorter than k, rows at position 0
+        Ns, nq, k = [3000, 0, 70, 20000], [16, 20, 17, 40], 256
+    elif name == "prefill_tile":  # the prefill shape: 66,560 entries, several row tiles
+        Ns, nq, k = [66560], [64], 2048
+    elif name == "k_large":       # k above the LDS-staged rows: rows written in place
+        Ns, nq, k = [10001], [20], 3000
+    else:
+        Ns, nq, k = [9000, 4097], [16, 33], 512
+    kk, qq = fp4_uniform(g, (max(1, sum(Ns)), 32)), fp4_uniform(g, (sum(nq), 32))
+    if name == "ties":            # codes from {0, +-0.5}: few distinct scores, big threshold bins
+        kk = np.take(np.array([0, 1, 9]), g.integers(0, 3, (max(1, sum(Ns)), 64)))
+        kk = (kk[:, 0::2] | (kk[:, 1::2] << 4)).astype(np.uint8)
+    elif name == "extremes":      # +-6 everywhere in some keys and queries, zeros in others
+        kk[::7], kk[1::7], kk[2::7] = 0x77, 0xFF, 0x00
+        qq[::3] = 0x77
+    return Ns, nq, k, kk, qq
+
+
+@pytest.mark.parametrize("name", ["ragged", "prefill_tile", "k_large", "ties", "extremes"])
+def test_index_select_fp4_bit_exact(name):
+    """csa_index_select_fp4 (scores never written) against the oracle's FP4 scores and
+    top-k."""
+    step(f"csa_index_select_fp4 {name}")
+    Ns, nq, k, k_fp4, q_fp4 = _select_fp4_case(name)
+    c = 4
+    B, max_q = len(Ns), max(nq)
+    ent_off, q_off = offsets(Ns), offsets(nq)
+    rows = int(q_off[-1])
+    q_pos = []
+    for b in range(B):
+        for i in range(nq[b]):
+            q_pos.append(0 if i % 13 == 5 else ((i + 1) * (Ns[b] * c + 2)) // nq[b])
+    idx = torch.full((rows, k), -5, dtype=torch.int32, device=DEV)
+    count = torch.full((rows,), -5, dtype=torch.int32, device=DEV)
+    n_vis = torch.full((rows,), -5, dtype=torch.int32, device=DEV)
+    lca.csa_index_select_fp4(u8_dev(q_fp4), i64_dev(q_off), i64_dev(q_pos), u8_dev(k_fp4),
+                             i64_dev(ent_off), B, max_q, max(Ns), c, k, idx, count, n_vis)
+    torch.cuda.synchronize()
+    I, C, NV = idx.cpu().numpy(), count.cpu().numpy(), n_vis.cpu().numpy()
+    for b in range(B):
+        keys = k_fp4[ent_off[b]:ent_off[b + 1]]
+        for i in range(nq[b]):
+            r = int(q_off[b]) + i
+            nv = oracle.n_visible(q_pos[r], c, Ns[b])
+            sc = oracle.index_scores_fp4(q_fp4[r], keys) if Ns[b] else np.zeros(0, np.int64)
+            ref = oracle.topk_select(sc, nv, k)
+            assert NV[r] == nv, (b, i)
+            assert C[r] == len(ref), (b, i)
+            assert np.array_equal(I[r, :len(ref)], ref), (b, i)
+            assert np.all(I[r, len(ref):] == -1), (b, i)
+
+
 @pytest.mark.parametrize("heads,nq", [(64, [1, 1, 1, 1]), (16, [1, 1, 1, 1]), (64, [20, 1, 17, 2])])
 def test_csa_step_fp4(heads, nq):
     step(f"CsaStep fp4 heads={heads} nq={nq}")

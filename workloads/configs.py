@@ -96,6 +96,11 @@ WORKLOADS = {
     "csa_prefill_256k": Workload(
         name="csa_prefill_256k", cfg_id=4, kind="csa_prefill", batch=1, ctx_len=262144,
         heads=64, topk=2048, new_tokens=4096),
+    # the same chunk with the FP4 indexer (packed E2M1 query and key codes)
+    "csa_prefill_256k_fp4": Workload(
+        name="csa_prefill_256k_fp4", cfg_id=4, kind="csa_prefill", batch=1, ctx_len=262144,
+        heads=64, topk=2048, new_tokens=4096, idx_fp4=True,
+        notes="FP4 indexer codes uniform over the 16 E2M1 codes"),
 }
 
 

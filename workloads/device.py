@@ -120,7 +120,8 @@ def decode_raw_inputs(wl: Workload, device="cuda", replicas: int = 1):
 
 def prefill_inputs(wl: Workload, device="cuda"):
     """Context raw tokens (ctx_len), the new raw tokens (new_tokens), indexer keys for
-    all ctx/c + new/c entries, and per-new-token queries and indexer queries."""
+    all ctx/c + new/c entries, and per-new-token queries and indexer queries (packed FP4
+    codes, 32 bytes per vector, for a workload with the FP4 indexer)."""
     ctx, new, c = wl.ctx_len, wl.new_tokens, wl.c
     n_ent = ctx // c + new // c
     return dict(
@@ -132,9 +133,13 @@ def prefill_inputs(wl: Workload, device="cuda"):
                                      device=device),
         new_v=gen.device_bf16_normal((new, 128), gen.seed_of(wl.cfg_id, 0, gen.T_NEW_V),
                                      device=device),
-        k_idx=gen.device_int8_uniform((n_ent, 64), gen.seed_of(wl.cfg_id, 0, gen.T_KIDX), device),
+        k_idx=(gen.device_fp4_uniform((n_ent, 32), gen.seed_of(wl.cfg_id, 0, gen.T_KFP4), device)
+               if wl.idx_fp4 else
+               gen.device_int8_uniform((n_ent, 64), gen.seed_of(wl.cfg_id, 0, gen.T_KIDX), device)),
         q=gen.device_bf16_normal((new, wl.heads, 128), gen.seed_of(wl.cfg_id, 0, gen.T_Q),
                                  device=device),
-        q_idx=gen.device_int8_uniform((new, 64), gen.seed_of(wl.cfg_id, 0, gen.T_QIDX), device),
+        q_idx=(gen.device_fp4_uniform((new, 32), gen.seed_of(wl.cfg_id, 0, gen.T_QFP4), device)
+               if wl.idx_fp4 else
+               gen.device_int8_uniform((new, 64), gen.seed_of(wl.cfg_id, 0, gen.T_QIDX), device)),
         n_ent=n_ent,
     )

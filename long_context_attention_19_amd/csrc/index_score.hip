@@ -111,7 +111,8 @@ __global__ __launch_bounds__(IS_NT) void index_score_kernel(IndexBatch ib) {
     }
   }
   // the group's scores leave at the end, 16 bytes per thread per store, 4 KiB
-  // contiguous per store instruction; nothing past the sequence's last entry is written
+  // contiguous per store instruction, non-temporal (measured faster for this launch
+  // than ordinary stores); nothing past the sequence's last entry is written
   __syncthreads();
   {
     const int64_t cnt = min((int64_t)IS_CHUNK, N - base);
@@ -120,7 +121,8 @@ __global__ __launch_bounds__(IS_NT) void index_score_kernel(IndexBatch ib) {
       const int q = 4 * (t + IS_NT * u);
       if (q >= IS_CHUNK) break;
       if (q + 4 <= cnt) {
-        *reinterpret_cast<i32x4*>(srow + base + q) = *reinterpret_cast<const i32x4*>(&s_sc[q]);
+        __builtin_nontemporal_store(*reinterpret_cast<const i32x4*>(&s_sc[q]),
+                                    reinterpret_cast<i32x4*>(srow + base + q));
       } else {
         for (int e = 0; e < 4; ++e)
           if (q + e < cnt) srow[base + q + e] = s_sc[q + e];
@@ -239,7 +241,8 @@ __global__ __launch_bounds__(IF_NT) void index_score_fp4_kernel(IndexBatch ib) {
     for (int u = 0; u < CHUNK / (4 * IF_NT); ++u) {
       const int q = 4 * (t + IF_NT * u);
       if (q + 4 <= cnt) {
-        *reinterpret_cast<i32x4*>(srow + base + q) = *reinterpret_cast<const i32x4*>(&s_sc[q]);
+        __builtin_nontemporal_store(*reinterpret_cast<const i32x4*>(&s_sc[q]),
+                                    reinterpret_cast<i32x4*>(srow + base + q));
       } else {
         for (int e = 0; e < 4; ++e)
           if (q + e < cnt) srow[base + q + e] = s_sc[q + e];

@@ -10,7 +10,7 @@ import torch
 import long_context_attention_19_amd as lca
 import oracle
 from long_context_attention_19_amd.pipeline import CsaStep, HcaStep, HybridStep
-from workloads import bf16_normal, int8_uniform, kv8_normal, kv8_rows, rng
+from workloads import bf16_normal, fp4_uniform, int8_uniform, kv8_normal, kv8_rows, rng
 
 from gpu_util import (DEV, assert_attn_close, assert_lse_close, bf16_dev, bf16_vals, i64_dev,
                       i8_dev, offsets, step)
@@ -128,11 +128,14 @@ def test_csa_step_kv8_prefill_rows():
             assert_lse_close(LSE[r], ref["lse"], f"seq {b} row {i}")
 
 
-def test_hybrid_mixed_kv_formats():
+@pytest.mark.parametrize("fp4", [False, True])
+def test_hybrid_mixed_kv_formats(fp4):
     """Layers with bf16 rows and with mixed rows in one step (separate launches), with a
-    window and a sink on some of them."""
-    step("HybridStep bf16 + kv8 layers")
-    g = rng(333, 0, 0)
+    window and a sink on some of them; with `fp4`, CSA layers 0 and 4 score FP4 codes
+    and layer 2 int8 codes, so every optional part meets every other in one step.  A
+    second step reproduces every output bit for bit."""
+    step(f"HybridStep bf16 + kv8 layers fp4={fp4}")
+    g = rng(333, int(fp4), 0)
     L = [4000, 65537, 1000 * 128 + 77]
     B, heads, W = len(L), 64, 128
     nbuf = [min(x, W + 16) for x in L]
@@ -168,7 +171,11 @@ def test_hybrid_mixed_kv_formats():
                   sink=None if z is None else torch.from_numpy(z).to(DEV),
                   kv_format=lca.LCA_KV_MIXED if kv8 else lca.LCA_KV_BF16)
         host = dict(q=q, Kf=Kf, Vf=Vf, ent_off=ent_off, wk=wk, wv=wv, window=window, z=z)
-        if csa:
+        if csa and fp4 and li in (0, 4):
+            host["k_fp4"], host["q_fp4"] = fp4_uniform(g, (tot, 32)), fp4_uniform(g, (B, 32))
+            Ld.update(topk=2048, k_idx=u8_dev(host["k_fp4"]), q_idx=u8_dev(host["q_fp4"]),
+                      idx_format=lca.LCA_IDX_FP4)
+        elif csa:
             host["k_idx"], host["q_idx"] = int8_uniform(g, (tot, 64)), int8_uniform(g, (B, 64))
             Ld.update(topk=2048, k_idx=i8_dev(host["k_idx"]), q_idx=i8_dev(host["q_idx"]))
         layers.append(Ld)
@@ -176,6 +183,12 @@ def test_hybrid_mixed_kv_formats():
     hs = HybridStep(layers, B, 1, heads)
     hs.run(i64_dev(np.arange(B + 1)), i64_dev(L), SCALE)
     torch.cuda.synchronize()
+    first = [(Ld["out"].clone(), Ld["lse"].clone()) for Ld in hs.layers]
+    hs.run(i64_dev(np.arange(B + 1)), i64_dev(L), SCALE)
+    torch.cuda.synchronize()
+    for li, (Ld, (o1, l1)) in enumerate(zip(hs.layers, first)):
+        assert torch.equal(Ld["out"].view(torch.int16), o1.view(torch.int16)), li
+        assert torch.equal(Ld["lse"], l1), li
     for li, (Ld, host) in enumerate(zip(hs.layers, refs)):
         O, LSE = bf16_vals(Ld["out"]), Ld["lse"].cpu().numpy()
         qf = oracle.bf16_bits_to_f64(host["q"])
@@ -183,7 +196,17 @@ def test_hybrid_mixed_kv_formats():
         z = np.full(heads, -np.inf) if host["z"] is None else host["z"].astype(np.float64)
         for b in range(B):
             sl, ws = slice(host["ent_off"][b], host["ent_off"][b + 1]), slice(boff[b], boff[b + 1])
-            if li % 2 == 0:
+            if "k_fp4" in host:   # FP4 selection, then the union with the window and the sink
+                sel = oracle.topk_select(oracle.index_scores_fp4(host["q_fp4"][b], host["k_fp4"][sl]),
+                                         oracle.n_visible(L[b], 4, len(host["k_fp4"][sl])), 2048)
+                I, C = Ld["idx"].cpu().numpy(), Ld["count"].cpu().numpy()
+                assert C[b] == len(sel) and np.array_equal(I[b, :C[b]], sel), (li, b)
+                lo, hi = oracle.window_tokens(L[b], host["window"], pos0[b], nbuf[b])
+                wkb, wvb = wkf[ws][lo:hi], wvf[ws][lo:hi]
+                o, lse, _ = oracle.attention_sink(qf[b], np.concatenate([host["Kf"][sl][sel], wkb]),
+                                                  np.concatenate([host["Vf"][sl][sel], wvb]), SCALE, z)
+                r = {"o": o, "lse": lse}
+            elif li % 2 == 0:
                 r = oracle.csa_query_sink(qf[b], host["q_idx"][b], L[b], host["Kf"][sl], host["Vf"][sl],
                                           host["k_idx"][sl], 4, 2048, SCALE, z, wkf[ws], wvf[ws],
                                           pos0[b], host["window"])

@@ -133,7 +133,8 @@ def test_hybrid_mixed_kv_formats(fp4):
     """Layers with bf16 rows and with mixed rows in one step (separate launches), with a
     window and a sink on some of them; with `fp4`, CSA layers 0 and 4 score FP4 codes
     and layer 2 int8 codes, so every optional part meets every other in one step.  A
-    second step reproduces every output bit for bit."""
+    second step, and every replay of the step captured into a HIP graph, reproduces every
+    output bit for bit."""
     step(f"HybridStep bf16 + kv8 layers fp4={fp4}")
     g = rng(333, int(fp4), 0)
     L = [4000, 65537, 1000 * 128 + 77]
@@ -189,6 +190,21 @@ def test_hybrid_mixed_kv_formats(fp4):
     for li, (Ld, (o1, l1)) in enumerate(zip(hs.layers, first)):
         assert torch.equal(Ld["out"].view(torch.int16), o1.view(torch.int16)), li
         assert torch.equal(Ld["lse"], l1), li
+    # captured into a HIP graph: every replay, with eager work between, equals the eager step
+    q_off_d, q_pos_d = i64_dev(np.arange(B + 1)), i64_dev(L)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        hs.run(q_off_d, q_pos_d, SCALE)
+    for rep in range(3):
+        for Ld in hs.layers:
+            Ld["out"].zero_()
+            Ld["lse"].zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for li, (Ld, (o1, l1)) in enumerate(zip(hs.layers, first)):
+            assert torch.equal(Ld["out"].view(torch.int16), o1.view(torch.int16)), (rep, li)
+            assert torch.equal(Ld["lse"], l1), (rep, li)
     for li, (Ld, host) in enumerate(zip(hs.layers, refs)):
         O, LSE = bf16_vals(Ld["out"]), Ld["lse"].cpu().numpy()
         qf = oracle.bf16_bits_to_f64(host["q"])

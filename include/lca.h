@@ -189,7 +189,9 @@ int32_t lca_csa_index_select(const int8_t* q_idx, const int64_t* q_off, const in
                              int32_t k, int32_t* idx, int32_t* count, int32_t* n_vis,
                              void* stream);
 
-/* csa_index_select_fp4 — the same selection over FP4 indexer codes: exactly what
+/* csa_index_select_fp4 — the same selection over FP4 indexer codes (page section 3-2
+ * item 4: the indexer's Q.K path trained with FP4 quantisation-aware training; the code
+ * format and score unit as lca_csa_index_score_fp4): exactly what
  * lca_csa_index_score_fp4 followed by lca_csa_topk_select gives.  The sweeps score
  * with the FP4 MFMA (v_mfma_scale_f32_16x16x128_f8f6f4, E2M1 operands, unit scales).
  *   q_fp4 [rows, 32], k_fp4 [ent_off[B], 32] packed E2M1 codes as for

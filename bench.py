@@ -58,6 +58,8 @@ def parse(argv=None):
                     help="only run 10 plain device copies of BYTES bytes (counter calibration)")
     ap.add_argument("--no-graph", action="store_true",
                     help="enqueue each step eagerly instead of replaying captured HIP graphs")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="the hybrid workload alone: skip the 1M CSA decode measured beside it")
     return ap.parse_args(argv)
 
 
@@ -117,13 +119,25 @@ def _timed_reps(fn, budget):
     return spent / reps, spent, reps
 
 
-class _OneThread:
-    """Run the oracle with one BLAS thread so the reported core count is exact."""
+def host_cores() -> int:
+    """Host cores this process may run on (its CPU affinity), capped by OMP_NUM_THREADS
+    where the environment sets it (a shared host's per-job share)."""
+    n = len(os.sched_getaffinity(0))
+    try:
+        cap = int(os.environ.get("OMP_NUM_THREADS", "0"))
+    except ValueError:
+        cap = 0
+    return max(1, min(n, cap) if cap > 0 else n)
+
+
+class _HostThreads:
+    """Run the oracle with its BLAS pool at the host's core count (host_cores())."""
 
     def __enter__(self):
+        self.cores = host_cores()
         try:
             from threadpoolctl import threadpool_limits
-            self._lim = threadpool_limits(limits=1)
+            self._lim = threadpool_limits(limits=self.cores)
         except Exception:  # pragma: no cover
             self._lim = None
         return self
@@ -154,8 +168,8 @@ class _Capture:
 
 class HybridRunner(_Capture):
     """8 independent layers, CSA (even) / HCA (odd), one decode token per sequence."""
-    dominant_tag = "index_score_kernel"
-    dominant_src = ["long_context_attention_19_amd/csrc/index_score.hip"]
+    dominant_tag = "ds_index_kernel"
+    dominant_src = ["long_context_attention_19_amd/csrc/decode_select.hip"]
 
     def __init__(self, wl, device="cuda"):
         import torch
@@ -163,8 +177,6 @@ class HybridRunner(_Capture):
         from long_context_attention_19_amd.pipeline import HybridStep
         from workloads import device as wdev
         self.wl, self.lca, self.torch = wl, lca, torch
-        if wl.idx_fp4:
-            self.dominant_tag = "index_score_fp4_kernel"
         self.L, self.layers = wdev.hybrid_inputs(wl, device)
         B, H = wl.batch, wl.heads
         specs = []
@@ -236,19 +248,13 @@ class HybridRunner(_Capture):
 
     def dominant_units(self):
         n = float(sum(int(np.sum(d["N"])) for d in self._csa))
-        if self.wl.idx_fp4:
-            return {"bound": "hbm", "per_launch": n * (32 + 4) + len(self._csa) * self.wl.batch * 32,
-                    "unit": "GB/s",
-                    "kernel": f"index_score_fp4_kernel<true> ({len(self._csa)} CSA layers in one "
-                              "launch): FP4 indexer scores (FP4 MFMA) + fused radix histogram",
-                    "per_unit": "36 B per compressed entry (32 B FP4 key read, 4 B score "
-                                "written) + 32 B per query"}
-        return {"bound": "hbm", "per_launch": n * (64 + 4) + len(self._csa) * self.wl.batch * 64,
+        kb = 32 if self.wl.idx_fp4 else 64
+        fmt = "FP4 (FP4 MFMA)" if self.wl.idx_fp4 else "int8 (v_dot4)"
+        return {"bound": "hbm", "per_launch": n * kb + len(self._csa) * self.wl.batch * kb,
                 "unit": "GB/s",
-                "kernel": f"index_score_kernel<true> ({len(self._csa)} CSA layers in one launch): "
-                          "int8 indexer scores + fused radix histogram",
-                "per_unit": "68 B per compressed entry (64 B key read, 4 B score written) "
-                            "+ 64 B per query"}
+                "kernel": f"ds_index_kernel ({len(self._csa)} CSA layers in one launch): {fmt} "
+                          "indexer scores in LDS, per-chunk top-k candidates (no score matrix)",
+                "per_unit": f"{kb} B per compressed entry (indexer key read) + {kb} B per query"}
 
     def cpu_baseline(self, n):
         import oracle
@@ -256,7 +262,7 @@ class HybridRunner(_Capture):
         n = n or wl.batch
         per_call = CPU_BUDGET_S / (n * len(self.layers))
         t_tok, spent, calls = 0.0, 0.0, 0
-        with _OneThread():
+        with _HostThreads() as ht:
             for b in range(n):
                 for d in self.layers:
                     s, e = int(d["ent_off"][b]), int(d["ent_off"][b + 1])
@@ -304,24 +310,27 @@ class HybridRunner(_Capture):
                     t_tok += mean
                     spent += sp
                     calls += r
-        return {"value": n / t_tok, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+        return {"value": n / t_tok, "unit": "tokens/s", "cores": ht.cores, "kind": "oracle",
                 "sample": f"{n} of {wl.batch} sequences through all {wl.n_layers} layers, one "
                           f"decode token each; {calls} oracle layer calls, {spent:.1f} s of "
                           f"oracle time (transfers and conversions excluded)"}
 
 
 class CsaDecodeRunner(_Capture):
-    """CSA decode over caches compressed from raw tokens (compression is setup)."""
-    dominant_tag = "index_score_kernel"
-    dominant_src = ["long_context_attention_19_amd/csrc/index_score.hip"]
+    """CSA decode over caches compressed from raw tokens (compression is setup).  The
+    step is the library's layer-stack step with one CSA layer: the candidate index
+    pass, the top-k selection and the sparse attention; one step object per input
+    replica (distinct indexer keys, queries and outputs)."""
+    dominant_tag = "ds_index_kernel"
+    dominant_src = ["long_context_attention_19_amd/csrc/decode_select.hip"]
 
     def __init__(self, wl, device="cuda", replicas=None):
         import torch
         import long_context_attention_19_amd as lca
-        from long_context_attention_19_amd.pipeline import CsaStep
+        from long_context_attention_19_amd.pipeline import HybridStep
         from workloads import device as wdev
         self.wl, self.lca, self.torch = wl, lca, torch
-        per_step = wl.batch * (wl.ctx_len // wl.c) * 64
+        per_step = wl.batch * (wl.ctx_len // wl.c) * (32 if wl.idx_fp4 else 64)
         R = replicas or max(1, min(16, math.ceil(1.0e9 / per_step)))
         self.inp = wdev.decode_raw_inputs(wl, device, R)
         inp = self.inp
@@ -333,21 +342,30 @@ class CsaDecodeRunner(_Capture):
                         inp["ent_off_dev"])
         lca.kv_compress(inp["raw_v"], inp["tok_off_dev"], wl.batch, T, wl.c, self.v_cmp,
                         inp["ent_off_dev"])
-        self.st = CsaStep(wl.batch, 1, int(inp["N"].max()), wl.heads, wl.topk, wl.c, device,
-                          fp4=wl.idx_fp4)
-        if wl.idx_fp4:
-            self.dominant_tag = "index_score_fp4_kernel"
+        self.max_entries = int(inp["N"].max())
+        self.steps = []
+        for r in inp["replicas"]:
+            spec = dict(kind=lca.LCA_LAYER_CSA, ratio=wl.c, topk=wl.topk,
+                        max_entries=self.max_entries, q=r["q"], q_idx=r["q_idx"],
+                        k_idx=r["k_idx"], k_cmp=self.k_cmp, v_cmp=self.v_cmp,
+                        ent_off=inp["ent_off_dev"],
+                        out=torch.empty(wl.batch, wl.heads, 128, dtype=torch.bfloat16,
+                                        device=device),
+                        lse=torch.empty(wl.batch, wl.heads, dtype=torch.float32, device=device))
+            if wl.idx_fp4:
+                spec["idx_format"] = lca.LCA_IDX_FP4
+            self.steps.append(HybridStep([spec], wl.batch, 1, wl.heads, device))
         self.q_off = torch.arange(wl.batch + 1, dtype=torch.int64, device=device)
         self.q_pos = torch.tensor(inp["L"], dtype=torch.int64, device=device)
-        self.out = torch.empty(wl.batch, wl.heads, 128, dtype=torch.bfloat16, device=device)
-        self.lse = torch.empty(wl.batch, wl.heads, dtype=torch.float32, device=device)
         self.tokens_per_step = wl.batch
         self.R = R
 
+    def layer(self, i=0):
+        """The layer dict of replica i: its inputs and its idx / count / out / lse."""
+        return self.steps[i % self.R].layers[0]
+
     def step(self, i=0):
-        r = self.inp["replicas"][i % self.R]
-        self.st.run(r["q"], r["q_idx"], self.q_off, self.q_pos, r["k_idx"], self.k_cmp,
-                    self.v_cmp, self.inp["ent_off_dev"], SCALE, self.out, self.lse)
+        self.steps[i % self.R].run(self.q_off, self.q_pos, SCALE)
 
     def step_bytes(self):
         N, wl = self.inp["N"], self.wl
@@ -355,30 +373,30 @@ class CsaDecodeRunner(_Capture):
         return int(np.sum(kb * N + np.minimum(N, wl.topk) * 512 + kb)) + \
             wl.batch * wl.heads * QO_BYTES_PER_HEAD
 
-    def dominant_launch(self):
-        self._i = getattr(self, "_i", 0) + 1
-        r = self.inp["replicas"][self._i % self.R]
-        st = self.st
-        score = self.lca.csa_index_score_fp4 if self.wl.idx_fp4 else self.lca.csa_index_score
-        score(r["q_idx"], self.q_off, self.q_pos, r["k_idx"], self.inp["ent_off_dev"],
-              self.wl.batch, 1, st.max_entries, self.wl.c, st.scores, st.n_vis, ws=self._dom_ws())
-
-    def _dom_ws(self):
-        if not hasattr(self, "_hws"):
-            self._hws = self.lca.workspace(self.lca.csa_topk_workspace_bytes(
-                self.wl.batch, self.st.max_entries, self.wl.topk))
-        return self._hws
+    def dominant_ms(self, reps):
+        """Average duration of the step's index pass (scores and candidates), from HIP
+        events the library records around it on its stream, over `reps` eager steps."""
+        lca, torch = self.lca, self.torch
+        lca.hybrid_timing_enable(True)
+        try:
+            t = []
+            for i in range(max(1, reps)):
+                self.step(i)
+                t.append(lca.hybrid_timing_read())
+        finally:
+            torch.cuda.synchronize()
+            lca.hybrid_timing_enable(False)
+        self.phase_ms = [float(np.mean([x[p] for x in t])) for p in range(len(t[0]))]
+        return self.phase_ms[0]
 
     def dominant_units(self):
         n = int(np.sum(self.inp["N"]))
-        if self.wl.idx_fp4:
-            return {"bound": "hbm", "per_launch": n * (32 + 4) + self.wl.batch * 32, "unit": "GB/s",
-                    "kernel": "index_score_fp4_kernel<true>: FP4 indexer scores (FP4 MFMA) + "
-                              "fused radix histogram",
-                    "per_unit": "36 B per compressed entry (32 B FP4 key read, 4 B score written)"}
-        return {"bound": "hbm", "per_launch": n * (64 + 4) + self.wl.batch * 64, "unit": "GB/s",
-                "kernel": "index_score_kernel<true>: int8 indexer scores + fused radix histogram",
-                "per_unit": "68 B per compressed entry (64 B key read, 4 B score written)"}
+        kb = 32 if self.wl.idx_fp4 else 64
+        fmt = "FP4 (FP4 MFMA)" if self.wl.idx_fp4 else "int8 (v_dot4)"
+        return {"bound": "hbm", "per_launch": n * kb + self.wl.batch * kb, "unit": "GB/s",
+                "kernel": f"ds_index_kernel: {fmt} indexer scores in LDS, per-chunk top-k "
+                          "candidates (no score matrix)",
+                "per_unit": f"{kb} B per compressed entry (indexer key read) + {kb} B per query"}
 
     def cpu_baseline(self, n):
         import oracle
@@ -386,7 +404,7 @@ class CsaDecodeRunner(_Capture):
         n = n or wl.batch
         r = inp["replicas"][0]
         t_tok, spent, calls = 0.0, 0.0, 0
-        with _OneThread():
+        with _HostThreads() as ht:
             for b in range(n):
                 s, e = int(inp["ent_off"][b]), int(inp["ent_off"][b + 1])
                 Kc = oracle.bf16_bits_to_f64(_bits(self.k_cmp[s:e]))
@@ -401,7 +419,7 @@ class CsaDecodeRunner(_Capture):
                 t_tok += mean
                 spent += sp
                 calls += rp
-        return {"value": n / t_tok, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+        return {"value": n / t_tok, "unit": "tokens/s", "cores": ht.cores, "kind": "oracle",
                 "sample": f"{n} of {wl.batch} sequences, one decode token each over the "
                           f"compressed cache; {calls} oracle calls, {spent:.1f} s of oracle time"}
 
@@ -458,7 +476,7 @@ class HcaDecodeRunner(_Capture):
         n = n or wl.batch
         k, v = self.caches[0]
         t_tok, spent, calls = 0.0, 0.0, 0
-        with _OneThread():
+        with _HostThreads() as ht:
             for b in range(n):
                 s, e = int(inp["ent_off"][b]), int(inp["ent_off"][b + 1])
                 Kc, Vc = oracle.bf16_bits_to_f64(_bits(k[s:e])), oracle.bf16_bits_to_f64(_bits(v[s:e]))
@@ -469,7 +487,7 @@ class HcaDecodeRunner(_Capture):
                 t_tok += mean
                 spent += sp
                 calls += rp
-        return {"value": n / t_tok, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+        return {"value": n / t_tok, "unit": "tokens/s", "cores": ht.cores, "kind": "oracle",
                 "sample": f"{n} of {wl.batch} sequences; {calls} oracle calls, {spent:.1f} s "
                           f"of oracle time"}
 
@@ -542,7 +560,7 @@ class PrefillRunner(_Capture):
         # query tokens spread over the chunk, until the budget is spent (or n given)
         order = np.random.default_rng(0).permutation(wl.new_tokens)
         t_or, done = 0.0, 0
-        with _OneThread():
+        with _HostThreads() as ht:
             for i in order:
                 if (n and done >= n) or (not n and t_or >= CPU_BUDGET_S):
                     break
@@ -553,7 +571,7 @@ class PrefillRunner(_Capture):
                 query(q, qi, wl.ctx_len + int(i), Kc, Vc, kidx, wl.c, wl.topk, SCALE)
                 t_or += time.perf_counter() - t0
                 done += 1
-        return {"value": done / t_or, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+        return {"value": done / t_or, "unit": "tokens/s", "cores": ht.cores, "kind": "oracle",
                 "sample": f"{done} of {wl.new_tokens} query tokens (random order) after "
                           f"compression ({t_or:.1f} s of oracle time)"}
 
@@ -575,6 +593,43 @@ def _time(fn, n, stream, torch):
     e1.record(stream)
     torch.cuda.synchronize()
     return e0.elapsed_time(e1) / n
+
+
+def _measure(run, args, stream, torch):
+    """W warm-up steps, then the mean time of K steps (HIP-graph replays unless
+    --no-graph), bracketed by device synchronisations."""
+    torch.cuda.synchronize()
+    if args.no_graph:
+        step_fn = run.step
+    else:
+        graphs = run.capture()
+        step_fn = lambda i: graphs[i % len(graphs)].replay()
+    for i in range(args.warmup):
+        step_fn(i)
+    return _time(step_fn, args.steps, stream, torch)
+
+
+def _extra_csa_1m(args, stream, torch):
+    """The 1M-context CSA decode (4 sequences of 1,048,576 tokens, top-k 2048), timed the
+    same way in the same process: its step time, tokens/s, HBM rate and phases."""
+    import workloads
+    wl = workloads.get("csa_decode_1m")
+    run = make_runner(wl)
+    ms = _measure(run, args, stream, torch)
+    k_ms = run.dominant_ms(args.kernel_reps)
+    u = run.dominant_units()
+    sb = run.step_bytes()
+    out = {"workload": wl.name, "ms_per_step": ms, "tokens_per_s": run.tokens_per_step / (ms * 1e-3),
+           "step_bytes": sb, "hbm_gbs": sb / (ms * 1e-3) / 1e9,
+           "hbm_frac": sb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+           "phases_ms": dict(zip(["index_pass", "selection", "attention"], run.phase_ms)),
+           "index_pass": {"avg_launch_us": k_ms * 1e3, "per_launch": u["per_launch"],
+                          "achieved_gbs": u["per_launch"] / (k_ms * 1e-3) / 1e9,
+                          "frac": u["per_launch"] / (k_ms * 1e-3) / 1e9 / HBM_PEAK_GBS}}
+    del run
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return out
 
 
 def main(argv=None):
@@ -599,15 +654,7 @@ def main(argv=None):
     torch.cuda.init()
     run = make_runner(wl)
     stream = torch.cuda.current_stream()
-    torch.cuda.synchronize()
-    if args.no_graph:
-        step_fn = run.step
-    else:
-        graphs = run.capture()
-        step_fn = lambda i: graphs[i % len(graphs)].replay()
-    for i in range(args.warmup):
-        step_fn(i)
-    ms = _time(step_fn, args.steps, stream, torch)
+    ms = _measure(run, args, stream, torch)
     sb = run.step_bytes()
 
     # dominant kernel: inside the step where the runner can time it there, else alone
@@ -664,16 +711,26 @@ def main(argv=None):
         "step_bytes": sb,
         "roofline": {"kernel": u["kernel"], "bound": u["bound"], "achieved": achieved,
                      "peak": peak, "unit": u["unit"], "frac": achieved / peak,
-                     "avg_launch_us": k_ms * 1e3, "per_launch": u["per_launch"],
+                     "avg_launch_us": k_ms * 1e3,
+                     "avg_launch_source": ("HIP events the library records around the launch "
+                                           "on its stream, eager steps" if hasattr(run, "dominant_ms")
+                                           else "HIP events around repeated launches of the same "
+                                                "shape on the step's stream"),
+                     "per_launch": u["per_launch"],
                      "per_unit": u["per_unit"],
                      "traffic": traffic_from_profile(run.dominant_tag, run.dominant_src,
                                                      wl.name)},
         "cpu_baseline": None,
     }
     if hasattr(run, "phase_ms"):
-        line["phases_ms"] = dict(zip(["csa_scores", "csa_topk", "attention"], run.phase_ms))
+        line["phases_ms"] = dict(zip(["index_pass", "selection", "attention"], run.phase_ms))
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = run.cpu_baseline(args.cpu_sample)
+    if wl.name == "hybrid_decode_1m" and not args.no_extra:
+        del run
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+        line["csa_decode_1m"] = _extra_csa_1m(args, stream, torch)
     print(json.dumps(line), flush=True)
 
 

@@ -59,7 +59,7 @@
 extern "C" {
 #endif
 
-#define LCA_ABI_VERSION 6
+#define LCA_ABI_VERSION 7
 
 enum lca_status {
   LCA_OK = 0,
@@ -118,7 +118,8 @@ int32_t lca_kv_compress_kv8(const lca_bf16* x, const int64_t* tok_off, int32_t b
  * csa_index_score — indexer scores of every query row against its sequence's
  * indexer keys.  Page section 3-2 item 4: CSA's indexer scores entries through
  * a Q.K product of its own.  Here: int8 x int8 products summed exactly in
- * int32 (|score| <= 64 * 127^2 < 2^20).
+ * int32, in [-2^20, 2^20]: 64 * (-128)^2 = 2^20 is reached only by a query and a
+ * key of all -128 codes; every other score is at most 2^20 - 128.
  *
  *   q_idx    [rows, d_idx] int8, one indexer query per query row.
  *   k_idx    [ent_off[B], d_idx] int8 indexer keys, one per compressed entry.
@@ -165,35 +166,46 @@ int32_t lca_csa_index_score_fp4(const uint8_t* q_fp4, const int64_t* q_off, cons
 
 /* ---------------------------------------------------------------------------
  * csa_index_select — csa_index_score and csa_topk_select in one call, without
- * the scores: idx, count and n_vis are exactly what those two calls give.  Page
- * section 3-2 items 2 and 4 (indexer scores, then a sparse top-k).
+ * the score matrix: idx, count and n_vis are exactly what those two calls give.
+ * Page section 3-2 items 2 and 4 (indexer scores, then a sparse top-k).
  *
- * For query batches of max_q >= 16 tokens per sequence (prefill): a work-group
- * owns 16 query tokens of a sequence and all its entries and recomputes the
- * int8 scores (MFMA) in sweeps over the keys: the coarse histogram, then (when
- * every token's threshold bin holds at most 256 entries) one sweep collecting the
- * entries above and inside that bin, resolved in LDS; otherwise the fine histogram
- * of the threshold bin and a third sweep placing the selection in index order.
- * No score matrix is written and no workspace is needed.
+ * Decode-sized batches (max_q < 16 query rows per sequence) take the candidate
+ * path and need a workspace: one work-group per 1024 entries of a row scores them
+ * in LDS and keeps the chunk's top coarse bins (about twice its expected share of
+ * the top-k, in index order); one work-group per row then selects the top-k from
+ * the candidates, exactly.  When a chunk held more than its share at or above the
+ * row's threshold bin (heavy ties, or a top-k bunched in a few chunks), that row's
+ * selection rescans its keys instead: the same result, more time.
+ * Prefill-sized batches (max_q >= 16): a work-group owns 16 query tokens of a
+ * sequence and all its entries and recomputes the int8 scores (MFMA) in sweeps
+ * over the keys: the coarse histogram, then (when every token's threshold bin
+ * holds at most 256 entries) one sweep collecting the entries above and inside
+ * that bin, resolved in LDS; otherwise the fine histogram of the threshold bin and
+ * a third sweep placing the selection in index order.  No workspace.
  *   q_idx, q_off, q_pos, k_idx, ent_off, batch, max_q, max_entries, d_idx, c
  *            as for lca_csa_index_score.
  *   k        entries kept per query row (>= 1).
  *   idx      [rows, k] int32 out: selected entry indices in ascending order,
  *            then -1 padding.    count [rows] int32 out: min(k, n_vis[r]).
  *   n_vis    [rows] int32 out, or NULL: min(floor(q_pos[r] / c), N_b).
- *   LCA_ERR_UNSUPPORTED for max_q < 16 (use the two calls there).
+ *   ws       workspace of lca_csa_index_select_workspace_bytes(batch, max_q,
+ *            max_entries, k) bytes (0 for prefill-sized batches: ws may be NULL);
+ *            zero-filled before first use, returned to zero by every call.
+ *   Decode-sized batches: max_entries <= 4,194,304 (else LCA_ERR_UNSUPPORTED).
  * ------------------------------------------------------------------------- */
+size_t lca_csa_index_select_workspace_bytes(int32_t batch, int32_t max_q, int32_t max_entries,
+                                            int32_t k);
 int32_t lca_csa_index_select(const int8_t* q_idx, const int64_t* q_off, const int64_t* q_pos,
                              const int8_t* k_idx, const int64_t* ent_off, int32_t batch,
                              int32_t max_q, int32_t max_entries, int32_t d_idx, int32_t c,
-                             int32_t k, int32_t* idx, int32_t* count, int32_t* n_vis,
-                             void* stream);
+                             int32_t k, int32_t* idx, int32_t* count, int32_t* n_vis, void* ws,
+                             size_t ws_bytes, void* stream);
 
 /* csa_index_select_fp4 — the same selection over FP4 indexer codes (page section 3-2
  * item 4: the indexer's Q.K path trained with FP4 quantisation-aware training; the code
  * format and score unit as lca_csa_index_score_fp4): exactly what
- * lca_csa_index_score_fp4 followed by lca_csa_topk_select gives.  The sweeps score
- * with the FP4 MFMA (v_mfma_scale_f32_16x16x128_f8f6f4, E2M1 operands, unit scales).
+ * lca_csa_index_score_fp4 followed by lca_csa_topk_select gives.  Scores come from the
+ * FP4 MFMA (E2M1 operands, unit scales); the workspace is the int8 form's.
  *   q_fp4 [rows, 32], k_fp4 [ent_off[B], 32] packed E2M1 codes as for
  *   lca_csa_index_score_fp4; every other argument and error as lca_csa_index_select.
  */
@@ -201,7 +213,7 @@ int32_t lca_csa_index_select_fp4(const uint8_t* q_fp4, const int64_t* q_off, con
                                  const uint8_t* k_fp4, const int64_t* ent_off, int32_t batch,
                                  int32_t max_q, int32_t max_entries, int32_t d_idx, int32_t c,
                                  int32_t k, int32_t* idx, int32_t* count, int32_t* n_vis,
-                                 void* stream);
+                                 void* ws, size_t ws_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------
  * csa_topk_select — per row, the top min(k, n_vis[r]) entries of
@@ -209,8 +221,9 @@ int32_t lca_csa_index_select_fp4(const uint8_t* q_fp4, const int64_t* q_off, con
  * Page section 3-2 item 2 (component table): CSA keeps a sparse top-k of the
  * compressed entries.  The tie rule (lower index first) is this library's.
  *
- *   scores   [rows, ld_scores] int32, values in [-2^20, 2^20) (what the int8
- *            indexer with d_idx = 64 produces; others give unspecified sets).
+ *   scores   [rows, ld_scores] int32, values in [-2^20, 2^20] (what the int8
+ *            indexer with d_idx = 64 produces; others give unspecified sets).  The
+ *            radix key clamps 2^20 to 2^20 - 1, a value no other int8 score reaches.
  *   n_vis    [rows] int32 visible entries per row (<= max_n).
  *   idx      [rows, k] int32 out: selected entry indices in ascending order,
  *            then -1 padding.    count [rows] int32 out: min(k, n_vis[r]).
@@ -331,11 +344,12 @@ int32_t lca_attn_sink(lca_bf16* out, float* lse, const float* sink, int64_t rows
 /* ---------------------------------------------------------------------------
  * hybrid_layer_step — a stack of independent attention layers over the same
  * batch, CSA and HCA interleaved (page section 3-2 item 2).  Each layer has its
- * own cache and queries; a CSA layer runs index_score -> topk_select ->
- * sparse_attn, an HCA layer dense_attn, with the same kernels as the single
- * calls.  Layers are independent and each has its own workspace region.  All
- * work is enqueued on `stream` in three phases: the CSA layers' scores and their
- * top-k selection (up to 8 layers per launch), then the attention of every
+ * own cache and queries; a CSA layer runs the selection of lca_csa_index_select
+ * (its decode form: candidates, then the top-k) -> sparse_attn, an HCA layer
+ * dense_attn, with the same kernels as the single calls.  Layers are independent
+ * and each has its own workspace region.  All work is enqueued on `stream` in
+ * three phases: the CSA layers' candidate index pass and their top-k selection
+ * (up to 8 layers per launch), then the attention of every
  * layer, CSA and HCA in the same launches (up to 8 layers each), followed by the
  * sliding-window branch of every layer that has one (window > 0).  A layer's sink
  * (sink != NULL, as lca_attn_sink) is folded in by the kernel that writes the
@@ -389,8 +403,8 @@ int32_t lca_hybrid_layer_step(const lca_layer* layers, int32_t n_layers, const i
  * caller's stream (not for use under graph capture).
  *   lca_hybrid_timing_enable(1 / 0) switches it on / off for the current device.
  *   lca_hybrid_timing_read(ms, n) waits for the last timed step and writes up to
- *   n durations in milliseconds: [0] indexer scores of the first batch of CSA
- *   layers (one launch), [1] their top-k selection, [2] the attention of all
+ *   n durations in milliseconds: [0] the index pass (scores and candidates) of the
+ *   first batch of CSA layers (one launch), [1] their top-k selection, [2] the attention of all
  *   layers with the split combine and the sliding-window branches (0 for a phase
  *   the step did not have).
  *   LCA_ERR_SHAPE if no timed step ran since enabling.

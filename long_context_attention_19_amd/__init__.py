@@ -54,10 +54,11 @@ _SIGS = {
                                    _i64, _vp, _vp, _sz, _vp]),
     "lca_csa_index_score_fp4": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
                                        _vp, _i64, _vp, _vp, _sz, _vp]),
+    "lca_csa_index_select_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32]),
     "lca_csa_index_select": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32,
-                                    _vp, _vp, _vp, _vp]),
+                                    _vp, _vp, _vp, _vp, _sz, _vp]),
     "lca_csa_index_select_fp4": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
-                                        _i32, _vp, _vp, _vp, _vp]),
+                                        _i32, _vp, _vp, _vp, _vp, _sz, _vp]),
     "lca_window_attn": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
                                _f32, _vp, _vp, _vp]),
     "lca_attn_sink": (_i32, [_vp, _vp, _vp, _i64, _i32, _i32, _vp]),
@@ -170,19 +171,23 @@ def csa_index_score_fp4(q_fp4, q_off, q_pos, k_fp4, ent_off, batch, max_q, max_e
         _s(stream)))
 
 
+def csa_index_select_workspace_bytes(batch, max_q, max_entries, k) -> int:
+    return _lib.lca_csa_index_select_workspace_bytes(batch, max_q, max_entries, k)
+
+
 def csa_index_select(q_idx, q_off, q_pos, k_idx, ent_off, batch, max_q, max_entries, c, k, idx,
-                     count, n_vis=None, stream=None):
+                     count, n_vis=None, ws=None, stream=None):
     _check("lca_csa_index_select", _lib.lca_csa_index_select(
         _p(q_idx), _p(q_off), _p(q_pos), _p(k_idx), _p(ent_off), batch, max_q, max_entries,
-        q_idx.shape[-1], c, k, _p(idx), _p(count), _p(n_vis), _s(stream)))
+        q_idx.shape[-1], c, k, _p(idx), _p(count), _p(n_vis), _p(ws), _nb(ws), _s(stream)))
 
 
 def csa_index_select_fp4(q_fp4, q_off, q_pos, k_fp4, ent_off, batch, max_q, max_entries, c, k,
-                         idx, count, n_vis=None, stream=None):
+                         idx, count, n_vis=None, ws=None, stream=None):
     """q_fp4 [rows, 32] / k_fp4 [entries, 32] uint8 packed E2M1 codes (d_idx = 64)."""
     _check("lca_csa_index_select_fp4", _lib.lca_csa_index_select_fp4(
         _p(q_fp4), _p(q_off), _p(q_pos), _p(k_fp4), _p(ent_off), batch, max_q, max_entries,
-        2 * q_fp4.shape[-1], c, k, _p(idx), _p(count), _p(n_vis), _s(stream)))
+        2 * q_fp4.shape[-1], c, k, _p(idx), _p(count), _p(n_vis), _p(ws), _nb(ws), _s(stream)))
 
 
 def window_attn(q, win_k, win_v, win_off, win_pos0, q_off, q_pos, batch, max_q, window, scale,
@@ -270,7 +275,7 @@ def hybrid_timing_enable(enable: bool = True):
 
 
 def hybrid_timing_read():
-    """[scores, top-k, attention] of the last timed hybrid step, in ms."""
+    """[index pass, top-k selection, attention] of the last timed hybrid step, in ms."""
     buf = (_f32 * LCA_HYBRID_PHASES)()
     _check("lca_hybrid_timing_read", _lib.lca_hybrid_timing_read(buf, LCA_HYBRID_PHASES))
     return [float(x) for x in buf]

@@ -6,6 +6,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
 #include <mutex>
 #include <string>
 #include <vector>
@@ -116,9 +117,15 @@ struct HybridAttnPlan {
   int G = 0;        // persistent work-groups: two per compute unit
   int items = 0;    // largest launch
 };
+// Fewer items than this leave most persistent work-groups a sliver of one item, and the
+// combine then merges ~G / items partials per item in dependent rounds: the per-row
+// split form is faster there (4 items: 12 + 42 us persistent against 8 + 5 us).
+constexpr int kPersistMinItems = 32;
+
 HybridAttnPlan hybrid_attn_plan(const lca_layer* layers, int n_layers, int rows, int heads) {
   HybridAttnPlan p;
   if (heads % 64 != 0 || rows <= 0) return p;
+  if ((int64_t)n_layers * rows * (heads / 64) < kPersistMinItems) return p;
   const int cu = lca_device_cu_count();
   if (cu <= 0) return p;
   const int G = 2 * cu;
@@ -143,12 +150,7 @@ HybridAttnPlan hybrid_attn_plan(const lca_layer* layers, int n_layers, int rows,
 }
 
 size_t csa_layer_bytes(int rows, int max_entries, int topk, int heads, int splits) {
-  const int ld = (max_entries + 3) & ~3;
-  size_t b = lca::align256((size_t)rows * (size_t)std::max(ld, 4) * 4);   // scores
-  b += lca::align256((size_t)rows * 4);                                     // n_vis
-  b += lca::topk_ws_bytes(rows, max_entries, topk);
-  b += lca::attn_ws_bytes(rows, heads, splits);
-  return b;
+  return lca::ds_ws_bytes(rows, max_entries, topk) + lca::attn_ws_bytes(rows, heads, splits);
 }
 
 }  // namespace
@@ -256,44 +258,79 @@ int32_t lca_csa_index_score_fp4(const uint8_t* q_fp4, const int64_t* q_off, cons
 }
 
 // ------------------------------------------------------------------ fused scores + top-k
+size_t lca_csa_index_select_workspace_bytes(int32_t batch, int32_t max_q, int32_t max_entries,
+                                            int32_t k) {
+  if (batch <= 0 || max_q <= 0 || max_entries < 0 || k <= 0) return 0;
+  if (max_q >= lca::SELECT_MIN_Q) return 0;   // the prefill form needs no workspace
+  return lca::ds_ws_bytes(batch * max_q, max_entries, k);
+}
+
 static int32_t index_select_impl(const int8_t* q_idx, const int64_t* q_off, const int64_t* q_pos,
                                  const int8_t* k_idx, const int64_t* ent_off, int32_t batch,
                                  int32_t max_q, int32_t max_entries, int32_t d_idx, int32_t c,
                                  int32_t k, int32_t* idx, int32_t* count, int32_t* n_vis,
-                                 void* stream, bool fp4) {
+                                 void* ws, size_t ws_bytes, void* stream, bool fp4) {
   const char* name = fp4 ? "csa_index_select_fp4" : "csa_index_select";
   if (d_idx != 64) return fail(LCA_ERR_UNSUPPORTED, "%s: d_idx=%d (only 64)", name, d_idx);
   if (batch < 0 || max_q < 0 || max_entries < 0) return fail(LCA_ERR_SHAPE, "%s: negative size", name);
   if (c < 1) return fail(LCA_ERR_SHAPE, "%s: ratio c=%d < 1", name, c);
   if (k <= 0) return fail(LCA_ERR_SHAPE, "%s: k=%d must be positive", name, k);
   if (batch == 0 || max_q == 0) return ok();
-  if (max_q < lca::SELECT_MIN_Q) return fail(LCA_ERR_UNSUPPORTED, "%s: max_q=%d below %d (use the score + csa_topk_select pair)", name, max_q, lca::SELECT_MIN_Q);
   if ((int64_t)batch * max_q > (1 << 30)) return fail(LCA_ERR_SHAPE, "%s: too many rows", name);
   if ((int64_t)batch * max_q * k > ((int64_t)1 << 40)) return fail(LCA_ERR_SHAPE, "%s: output too large", name);
   if (!q_idx || !q_off || !q_pos || !k_idx || !ent_off || !idx || !count) return fail(LCA_ERR_NULL, "%s: NULL pointer", name);
   if (!al16(q_idx) || !al16(k_idx)) return fail(LCA_ERR_ALIGN, "%s: q_idx / k_idx not 16-byte aligned", name);
-  lca::SelectArgs a{q_idx, k_idx, ent_off, q_off, q_pos, idx, count, n_vis, c, max_entries, max_q, k,
-                    fp4 ? 1 : 0};
-  return hip_status(lca::launch_index_select(a, batch, (hipStream_t)stream), name);
+  if (max_q >= lca::SELECT_MIN_Q) {
+    lca::SelectArgs a{q_idx, k_idx, ent_off, q_off, q_pos, idx, count, n_vis, c, max_entries,
+                      max_q, k, fp4 ? 1 : 0};
+    return hip_status(lca::launch_index_select(a, batch, (hipStream_t)stream), name);
+  }
+  // decode-sized batches: the candidate path
+  if ((int64_t)max_entries > (int64_t)lca::DS_MAX_CHUNKS * lca::DS_CHUNK) return fail(LCA_ERR_UNSUPPORTED, "%s: max_entries=%d above %d", name, max_entries, lca::DS_MAX_CHUNKS * lca::DS_CHUNK);
+  const int rows = batch * max_q;
+  const size_t need = lca::ds_ws_bytes(rows, max_entries, k);
+  if (!ws || ws_bytes < need) return fail(LCA_ERR_WORKSPACE, "%s: ws_bytes %zu < %zu", name, ws_bytes, need);
+  if (!al16(ws)) return fail(LCA_ERR_ALIGN, "%s: ws not 16-byte aligned", name);
+  lca::DsBatch db{};
+  db.q_off = q_off;
+  db.q_pos = q_pos;
+  db.max_q = max_q;
+  db.n = 1;
+  db.fp4 = fp4 ? 1 : 0;
+  lca::DsLayer& L = db.layer[0];
+  L.q_idx = q_idx;
+  L.k_idx = k_idx;
+  L.ent_off = ent_off;
+  L.idx = idx;
+  L.count = count;
+  L.c = c;
+  L.max_entries = max_entries;
+  L.k = k;
+  lca::ds_ws_carve(ws, rows, max_entries, k, L);
+  if (n_vis) L.n_vis = n_vis;
+  hipError_t e = lca::launch_ds_chunks(db, batch, (hipStream_t)stream);
+  if (e == hipSuccess) e = lca::launch_ds_select(db, batch, (hipStream_t)stream);
+  return hip_status(e, name);
 }
 
 int32_t lca_csa_index_select(const int8_t* q_idx, const int64_t* q_off, const int64_t* q_pos,
                              const int8_t* k_idx, const int64_t* ent_off, int32_t batch,
                              int32_t max_q, int32_t max_entries, int32_t d_idx, int32_t c,
-                             int32_t k, int32_t* idx, int32_t* count, int32_t* n_vis,
-                             void* stream) {
+                             int32_t k, int32_t* idx, int32_t* count, int32_t* n_vis, void* ws,
+                             size_t ws_bytes, void* stream) {
   return index_select_impl(q_idx, q_off, q_pos, k_idx, ent_off, batch, max_q, max_entries, d_idx,
-                           c, k, idx, count, n_vis, stream, false);
+                           c, k, idx, count, n_vis, ws, ws_bytes, stream, false);
 }
 
 int32_t lca_csa_index_select_fp4(const uint8_t* q_fp4, const int64_t* q_off, const int64_t* q_pos,
                                  const uint8_t* k_fp4, const int64_t* ent_off, int32_t batch,
                                  int32_t max_q, int32_t max_entries, int32_t d_idx, int32_t c,
                                  int32_t k, int32_t* idx, int32_t* count, int32_t* n_vis,
-                                 void* stream) {
+                                 void* ws, size_t ws_bytes, void* stream) {
   return index_select_impl(reinterpret_cast<const int8_t*>(q_fp4), q_off, q_pos,
                            reinterpret_cast<const int8_t*>(k_fp4), ent_off, batch, max_q,
-                           max_entries, d_idx, c, k, idx, count, n_vis, stream, true);
+                           max_entries, d_idx, c, k, idx, count, n_vis, ws, ws_bytes, stream,
+                           true);
 }
 
 // ------------------------------------------------------------------ top-k
@@ -558,7 +595,7 @@ int32_t lca_hybrid_layer_step(const lca_layer* layers, int32_t n_layers, const i
       if (!L.q_idx || !L.k_idx || !L.idx || !L.count) return fail(LCA_ERR_NULL, "hybrid_layer_step: CSA layer %d NULL pointer", l);
       if (!al16(L.q_idx) || !al16(L.k_idx)) return fail(LCA_ERR_ALIGN, "hybrid_layer_step: layer %d indexer not aligned", l);
       if (L.idx_format != LCA_IDX_INT8 && L.idx_format != LCA_IDX_FP4) return fail(LCA_ERR_SHAPE, "hybrid_layer_step: layer %d idx_format=%d", l, L.idx_format);
-      if ((int64_t)L.max_entries > (int64_t)lca::topk_max_chunks() * kTopkChunk) return fail(LCA_ERR_UNSUPPORTED, "hybrid_layer_step: layer %d max_entries too large", l);
+      if ((int64_t)L.max_entries > (int64_t)lca::DS_MAX_CHUNKS * lca::DS_CHUNK) return fail(LCA_ERR_UNSUPPORTED, "hybrid_layer_step: layer %d max_entries too large", l);
     }
     if (head_dim != 128) return fail(LCA_ERR_UNSUPPORTED, "hybrid_layer_step: head_dim=%d (only 128)", head_dim);
     if (!heads_supported(heads)) return fail(LCA_ERR_UNSUPPORTED, "hybrid_layer_step: heads=%d", heads);
@@ -579,8 +616,7 @@ int32_t lca_hybrid_layer_step(const lca_layer* layers, int32_t n_layers, const i
   const float scale_log2 = scale * 1.4426950408889634f;
 
   // carve each layer's workspace region (layer order, as lca_hybrid_workspace_bytes sizes it)
-  std::vector<lca::IndexLayer> il;
-  std::vector<lca::TopkLayer> tl;
+  std::vector<lca::DsLayer> il;
   std::vector<int> il_fp4;   // per CSA layer: FP4 indexer codes
   std::vector<lca::AttnArgs> args((size_t)n_layers);
   bool has_csa = false;
@@ -602,16 +638,18 @@ int32_t lca_hybrid_layer_step(const lca_layer* layers, int32_t n_layers, const i
     a.sink = L.window > 0 ? nullptr : L.sink;   // else the window branch writes last
     a.kv8 = L.kv_format == LCA_KV_MIXED ? 1 : 0;
     if (L.kind == LCA_LAYER_CSA) {
-      const int ld = std::max((L.max_entries + 3) & ~3, 4);
-      int32_t* scores = reinterpret_cast<int32_t*>(p);
-      p += lca::align256((size_t)rows * ld * 4);
-      int32_t* n_vis = reinterpret_cast<int32_t*>(p);
-      p += lca::align256((size_t)rows * 4);
-      lca::TopkWs w = lca::topk_ws_carve(p, rows, L.max_entries, L.topk);
-      p += lca::topk_ws_bytes(rows, L.max_entries, L.topk);
-      il.push_back(lca::IndexLayer{L.q_idx, L.k_idx, L.ent_off, scores, ld, n_vis, w.hist, w.fine,
-                                   L.ratio, L.max_entries});
-      tl.push_back(lca::TopkLayer{scores, ld, n_vis, L.idx, L.count, L.max_entries, L.topk, w});
+      lca::DsLayer d{};
+      d.q_idx = L.q_idx;
+      d.k_idx = L.k_idx;
+      d.ent_off = L.ent_off;
+      d.idx = L.idx;
+      d.count = L.count;
+      d.c = L.ratio;
+      d.max_entries = L.max_entries;
+      d.k = L.topk;
+      lca::ds_ws_carve(p, rows, L.max_entries, L.topk, d);
+      p += lca::ds_ws_bytes(rows, L.max_entries, L.topk);
+      il.push_back(d);
       il_fp4.push_back(L.idx_format == LCA_IDX_FP4 ? 1 : 0);
       a.idx = L.idx;
       a.count = L.count;
@@ -664,23 +702,18 @@ int32_t lca_hybrid_layer_step(const lca_layer* layers, int32_t n_layers, const i
   for (size_t gi = 0; gi < groups.size() && e == hipSuccess; ++gi) {
     const std::vector<int>& grp = groups[gi];
     const int n = (int)grp.size();
-    lca::IndexBatch ib{};
-    ib.q_off = q_off;
-    ib.q_pos = q_pos;
-    ib.max_q = max_q;
-    ib.n = n;
-    ib.fp4 = il_fp4[grp[0]];
-    lca::TopkBatch tb{};
-    tb.n = n;
-    for (int i = 0; i < n; ++i) {
-      ib.layer[i] = il[grp[i]];
-      tb.layer[i] = tl[grp[i]];
-    }
+    lca::DsBatch db{};
+    db.q_off = q_off;
+    db.q_pos = q_pos;
+    db.max_q = max_q;
+    db.n = n;
+    db.fp4 = il_fp4[grp[0]];
+    for (int i = 0; i < n; ++i) db.layer[i] = il[grp[i]];
     const bool first = gi == 0;
     if (first) mark(0);
-    e = lca::launch_index_score(ib, batch, caller);
+    e = lca::launch_ds_chunks(db, batch, caller);
     if (first) mark(1);
-    if (e == hipSuccess) e = lca::launch_topk(tb, rows, true, caller);
+    if (e == hipSuccess) e = lca::launch_ds_select(db, batch, caller);
     if (first) mark(2);
   }
   mark(3);

@@ -107,7 +107,7 @@ __global__ __launch_bounds__(IS_NT) void index_score_kernel(IndexBatch ib) {
       const int64_t j = base + jl;
       const bool vis = j < nv;
       s_sc[jl] = vis ? v : INT32_MIN;
-      if (HIST && vis && j < N) atomicAdd(&lh[(v + KEY_BIAS) >> 10], 1);
+      if (HIST && vis && j < N) atomicAdd(&lh[score_key(v) >> 10], 1);
     }
   }
   // the group's scores leave at the end, 16 bytes per thread per store, 4 KiB
@@ -230,7 +230,7 @@ __global__ __launch_bounds__(IF_NT) void index_score_fp4_kernel(IndexBatch ib) {
         const int32_t v = (int32_t)(acc[0] * 256.0f);   // exact
         const bool vis = j < nv;
         s_sc[jl] = vis ? v : INT32_MIN;
-        if (HIST && vis && j < N) atomicAdd(&lh[(v + KEY_BIAS) >> 10], 1);
+        if (HIST && vis && j < N) atomicAdd(&lh[score_key(v) >> 10], 1);
       }
     }
   }
@@ -352,7 +352,7 @@ __device__ __forceinline__ void ig_round(const i32x4 (&kv)[4], const i32x4& qv, 
     for (int r = 0; r < 4; ++r) {
       const bool vis = j0 + r < nv;
       o[u][r] = vis ? acc[r] : INT32_MIN;
-      if (HIST && vis) atomicAdd(&lh[n * HIST_BINS + (((acc[r] + KEY_BIAS) >> 10) ^ n)], 1);
+      if (HIST && vis) atomicAdd(&lh[n * HIST_BINS + ((score_key(acc[r]) >> 10) ^ n)], 1);
     }
   }
   if (live) {

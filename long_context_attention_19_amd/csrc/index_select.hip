@@ -112,7 +112,7 @@ __device__ __forceinline__ void sl_keys(const i32x4 (&kv)[4], const i32x4& qv, i
     } else {
       const i32x4 acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(kv[u], qv, zero4, 0, 0, 0);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) key[u][r] = acc[r] + KEY_BIAS;
+      for (int r = 0; r < 4; ++r) key[u][r] = score_key(acc[r]);
     }
   }
 }

@@ -11,9 +11,15 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int WAVE = 64;
-constexpr int KEY_BIAS = 1 << 20;        // indexer scores lie in [-2^20, 2^20)
+constexpr int KEY_BIAS = 1 << 20;        // indexer scores lie in [-2^20, 2^20]
 constexpr int HIST_BINS = 2048;          // first radix level: key >> 10
 constexpr int FINE_BINS = 1024;          // second radix level: key & 1023
+
+// The 21-bit radix key of an indexer score.  int8 scores lie in [-2^20, 2^20]; the top
+// value 2^20 = 64 * (-128)^2 needs a query and a key of all -128 codes, and the next
+// reachable score is 63 * 2^14 + 128 * 127 = 2^20 - 128.  Clamping 2^20 to 2^20 - 1
+// therefore keeps every reachable score's rank, and the key stays below 2^21.
+__device__ __forceinline__ int score_key(int32_t s) { return min(s, KEY_BIAS - 1) + KEY_BIAS; }
 
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
 
@@ -44,14 +50,17 @@ __device__ __forceinline__ uint32_t f64_to_bf16_bits(double x) {
 
 // ---------------------------------------------------------------- scans
 
-template <typename T>
-__device__ __forceinline__ T wave_incl_scan(T v) {
-  const int lane = threadIdx.x & (WAVE - 1);
-#pragma unroll
-  for (int d = 1; d < WAVE; d <<= 1) {
-    T o = __shfl_up(v, d, WAVE);
-    if (lane >= d) v += o;
-  }
+// Inclusive prefix sum over the 64 lanes of a wave with DPP: a Hillis-Steele scan
+// inside each row of 16 lanes (row_shr 1, 2, 4, 8; lanes past the row's start read
+// 0), then row 15's lane added into rows 1 and 3 (row_bcast:15) and lane 31 into
+// rows 2 and 3 (row_bcast:31).  Rows left out by the row mask add 0.
+__device__ __forceinline__ int wave_incl_scan(int v) {
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, true);   // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, true);   // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, true);   // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, true);   // row_shr:8
+  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xa, 0xf, false);  // row_bcast:15
+  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xc, 0xf, false);  // row_bcast:31
   return v;
 }
 
@@ -62,28 +71,33 @@ __device__ __forceinline__ T wave_sum(T v) {
   return v;
 }
 
-// Exclusive scan across a work-group of NT threads (NT a multiple of 64, <= 1024).
-// `tmp` is LDS scratch of NT/64 + 1 elements.  Returns the exclusive prefix and
-// writes the total to *total.  Contains __syncthreads(): call from all threads.
-template <int NT, typename T>
-__device__ __forceinline__ T block_excl_scan(T v, T* tmp, T* total) {
+__device__ __forceinline__ int wave_max(int v) {
+#pragma unroll
+  for (int d = WAVE / 2; d >= 1; d >>= 1) v = max(v, __shfl_xor(v, d, WAVE));
+  return v;
+}
+
+// Exclusive prefix sum across a work-group of NT threads (NT a multiple of 64, at most
+// 1024) in thread order.  `tmp` is LDS scratch of NT/64 + 1 ints.  Returns the exclusive
+// prefix and writes the total to *total.  The waves scan their lanes; the first wave
+// scans the wave totals.  Contains __syncthreads(): call from all threads.
+template <int NT>
+__device__ __forceinline__ int block_excl_scan(int v, int* tmp, int* total) {
   constexpr int NW = NT / WAVE;
+  static_assert(NW >= 1 && NW <= WAVE, "work-group size");
   const int lane = threadIdx.x & (WAVE - 1);
   const int w = threadIdx.x / WAVE;
-  T inc = wave_incl_scan(v);
+  const int inc = wave_incl_scan(v);
   if (lane == WAVE - 1) tmp[w] = inc;
   __syncthreads();
-  if (threadIdx.x == 0) {
-    T run = 0;
-    for (int i = 0; i < NW; ++i) {
-      T t = tmp[i];
-      tmp[i] = run;
-      run += t;
-    }
-    tmp[NW] = run;
+  if (w == 0) {
+    const int x = lane < NW ? tmp[lane] : 0;
+    const int xi = wave_incl_scan(x);
+    if (lane < NW) tmp[lane] = xi - x;
+    if (lane == NW - 1) tmp[NW] = xi;
   }
   __syncthreads();
-  T res = inc - v + tmp[w];
+  const int res = inc - v + tmp[w];
   *total = tmp[NW];
   __syncthreads();
   return res;

@@ -63,6 +63,74 @@ struct SelectArgs {
 constexpr int SELECT_MIN_Q = 16;
 hipError_t launch_index_select(const SelectArgs& a, int batch, hipStream_t st);
 
+// ------------------------------------------------------------ decode selection
+// Scores and top-k without the score matrix, for decode-sized query batches: each
+// work-group of a first launch scores DS_CHUNK entries of one row in LDS and keeps only
+// its chunk's candidates (whole coarse bins from the top, about twice the chunk's
+// expected share of the top-k); a second launch picks each row's top-k from the
+// candidates, exactly, or rescans the row's keys when a chunk dropped an entry that
+// could belong to it.
+constexpr int DS_NT = 512;            // threads of a work-group
+constexpr int DS_CHUNK = 2048;        // entries per work-group
+constexpr int DS_MAX_CHUNKS = 2048;   // rows up to 4M entries
+constexpr int DS_SEL_VPT = 29;        // candidate slots per thread and selection round (odd:
+                                      // a thread's run of LDS words starts on its own bank)
+
+// A chunk's candidate budget for a row with nv > k visible entries.  E is the
+// chunk's expected share of the top-k, ceil(k * DS_CHUNK / nv); the chunk keeps the
+// top coarse bins until `target` entries (E plus six standard deviations of a Poisson
+// count, plus 8), and never more than `slot` (target + 16), the chunk's stride in the
+// candidate region.  Host and device share this rule.
+struct DsBudget {
+  int target;
+  int slot;
+};
+constexpr int DS_MIN_SLOT = 31;       // the smallest slot the rule gives (E = 1)
+__host__ __device__ inline DsBudget ds_budget(int64_t nv, int k) {
+  int64_t e = ((int64_t)k * DS_CHUNK + nv - 1) / (nv > 0 ? nv : 1);
+  if (e > DS_CHUNK) e = DS_CHUNK;
+  int sq = 0;
+  while ((int64_t)sq * sq < e) ++sq;
+  int target = (int)e + 6 * sq + 8;
+  if (target > DS_CHUNK) target = DS_CHUNK;
+  int slot = target + 16;
+  if (slot > DS_CHUNK) slot = DS_CHUNK;
+  return DsBudget{target, slot};
+}
+// Candidate slots a row needs for any nv in (k, max_n]: ceil(nv / DS_CHUNK) chunks of
+// ds_budget(nv, k).slot slots each; the bound is taken over every chunk count.
+size_t ds_cand_slots(int max_n, int k);
+
+struct DsLayer {
+  const int8_t* q_idx;   // [rows][64] int8, or [rows][32] packed FP4
+  const int8_t* k_idx;   // [ent_off[B]][64] int8, or [.][32] packed FP4
+  const int64_t* ent_off;
+  int32_t* n_vis;        // [rows] out
+  int32_t* dcut;         // [rows][nch] a chunk's cut bin if it dropped entries, else 0
+  int32_t* cand;         // [rows][cand_slots] per chunk `slot` words: (key << 11 | entry in
+                         // chunk) of the kept entries in index order, then 0
+  int32_t* idx;          // [rows][k] out
+  int32_t* count;        // [rows] out
+  int64_t cand_slots;
+  int32_t nch;           // chunk stride of dcut
+  int32_t c;
+  int32_t max_entries;
+  int32_t k;
+};
+struct DsBatch {
+  const int64_t* q_off;
+  const int64_t* q_pos;
+  int32_t max_q;
+  int32_t n;
+  int32_t fp4;           // q_idx / k_idx hold packed FP4 (E2M1) codes, 32 bytes per vector
+  DsLayer layer[MAX_BATCH_LAYERS];
+};
+size_t ds_ws_bytes(int rows, int max_n, int k);
+// carve one layer's workspace: n_vis, dcut, cand
+void ds_ws_carve(void* ws, int rows, int max_n, int k, DsLayer& L);
+hipError_t launch_ds_chunks(const DsBatch& db, int batch, hipStream_t st);   // candidates
+hipError_t launch_ds_select(const DsBatch& db, int batch, hipStream_t st);   // the top-k
+
 // ------------------------------------------------------------ top-k
 struct TopkWs {
   int32_t* hist;       // [rows][2048] coarse histogram, zero on entry and on exit

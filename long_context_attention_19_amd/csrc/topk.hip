@@ -5,7 +5,8 @@
 // Review", section 3-2 item 2 (component table): CSA keeps a sparse top-k of
 // the compressed entries.  The tie rule (lower index first) is this library's.
 //
-// Scores lie in [-2^20, 2^20), so key = score + 2^20 has 21 bits.  Two radix
+// Scores lie in [-2^20, 2^20], so key = score + 2^20 (2^20 clamped one lower, a rank
+// no other reachable score takes) has 21 bits.  Two radix
 // levels pin the k-th largest key T exactly: 2048 bins of key >> 10 (the coarse
 // histogram), then 1024 bins of key & 1023 among the keys of the threshold bin
 // (the fine histogram).  Every decision is a function of counts, never of the
@@ -158,7 +159,7 @@ __global__ __launch_bounds__(TK_NT) void topk_hist_kernel(TopkBatch tb) {
   load16(scores + (int64_t)row * ld, j0, n, v);
 #pragma unroll
   for (int e = 0; e < 16; ++e)
-    if (j0 + e < n) atomicAdd(&lh[(v[e] + KEY_BIAS) >> 10], 1);
+    if (j0 + e < n) atomicAdd(&lh[score_key(v[e]) >> 10], 1);
   __syncthreads();
   int32_t* gh = hist + (int64_t)row * HIST_BINS;
   for (int b = t; b < HIST_BINS; b += TK_NT)
@@ -194,7 +195,7 @@ __global__ __launch_bounds__(TK_NT) void topk_cand_kernel(TopkBatch tb) {
 #pragma unroll
   for (int e = 0; e < 16; ++e) {
     if (j0 + e < n) {
-      const int bin = (v[e] + KEY_BIAS) >> 10;
+      const int bin = score_key(v[e]) >> 10;
       na += bin > bA ? 1 : 0;
       nb += bin == bA ? 1 : 0;
     }
@@ -210,7 +211,7 @@ __global__ __launch_bounds__(TK_NT) void topk_cand_kernel(TopkBatch tb) {
 #pragma unroll
   for (int e = 0; e < 16; ++e) {
     if (j0 + e < n) {
-      const int key = v[e] + KEY_BIAS;
+      const int key = score_key(v[e]);
       const int li = t * TK_PER_THREAD + e;
       if ((key >> 10) > bA) {
         keys[aoff++] = li;
@@ -355,7 +356,7 @@ __global__ __launch_bounds__(TK_NT) void topk_place_kernel(TopkBatch tb) {
   // this chunk, in index order
   int32_t ne = 0;
 #pragma unroll
-  for (int e = 0; e < 16; ++e) ne += (j0 + e < n && v[e] + KEY_BIAS == T) ? 1 : 0;
+  for (int e = 0; e < 16; ++e) ne += (j0 + e < n && score_key(v[e]) == T) ? 1 : 0;
   int32_t etot;
   int32_t rank = eq_before + block_excl_scan<TK_NT>(ne, s_scan, &etot);
   uint32_t selmask = 0;
@@ -363,7 +364,7 @@ __global__ __launch_bounds__(TK_NT) void topk_place_kernel(TopkBatch tb) {
 #pragma unroll
   for (int e = 0; e < 16; ++e) {
     if (j0 + e < n) {
-      const int key = v[e] + KEY_BIAS;
+      const int key = score_key(v[e]);
       bool sel = key > T;
       if (key == T) sel = rank++ < need_eq;
       if (sel) {

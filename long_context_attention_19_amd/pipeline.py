@@ -1,10 +1,10 @@
 """Composed steps over the C ABI: buffer allocation and call order only.
 
-CsaStep   selection, then csa_sparse_attn.  Selection is csa_index_score (with the
-          fused first radix pass) -> csa_topk_select for decode (fewer than 16
-          queries per sequence), and csa_index_select (scores never written) for
-          chunked prefill (16 or more queries per sequence); the FP4 indexer takes
-          csa_index_score_fp4 and csa_index_select_fp4 in the same places.
+CsaStep   selection, then csa_sparse_attn.  Selection is csa_index_select (scores
+          never written: its candidate form for decode, its sweep form for chunked
+          prefill of 16 or more queries per sequence), or, with fused=False, the pair
+          csa_index_score (with the fused first radix pass) -> csa_topk_select; the
+          FP4 indexer takes the _fp4 forms of the same calls.
 HcaStep   hca_dense_attn.
 HybridStep  hybrid_layer_step over a list of CSA / HCA layers.
 
@@ -17,7 +17,7 @@ import torch
 
 from . import (LCA_IDX_FP4, LCA_IDX_INT8, LCA_KV_BF16, LCA_KV_MIXED, LCA_LAYER_CSA, LCA_LAYER_HCA,
                attn_workspace_bytes, csa_index_score, csa_index_score_fp4, csa_index_select,
-               csa_index_select_fp4,
+               csa_index_select_fp4, csa_index_select_workspace_bytes,
                csa_sparse_attn, csa_sparse_attn_kv8, csa_topk_select, csa_topk_workspace_bytes,
                hca_dense_attn, hca_dense_attn_kv8, hybrid_layer_step, hybrid_workspace_bytes,
                make_layers, workspace)
@@ -31,8 +31,8 @@ def _round4(n: int) -> int:
 
 
 class CsaStep:
-    """fused: None picks csa_index_select when max_q >= 16; True / False force it
-    on / off (the two-call path materialises the scores in self.scores).  fp4: the
+    """fused: True (default) selects with csa_index_select; False with the two-call
+    path, which materialises the scores in self.scores.  fp4: the
     indexer query / keys are packed FP4 codes (the _fp4 scoring and selection calls);
     kv8: the cache holds mixed FP8 / bf16 rows (csa_sparse_attn_kv8)."""
 
@@ -43,11 +43,14 @@ class CsaStep:
         rows = batch * max_q
         self.rows = rows
         self.fp4, self.kv8 = fp4, kv8
-        self.fused = (max_q >= SELECT_MIN_Q) if fused is None else fused
+        self.fused = True if fused is None else fused
         self.n_vis = torch.empty(rows, dtype=torch.int32, device=device)
         self.idx = torch.empty(rows, topk, dtype=torch.int32, device=device)
         self.count = torch.empty(rows, dtype=torch.int32, device=device)
-        if not self.fused:
+        if self.fused:
+            self.sws = workspace(csa_index_select_workspace_bytes(batch, max_q, max_entries, topk),
+                                 device)
+        else:
             self.scores = torch.empty(rows, _round4(max_entries), dtype=torch.int32,
                                       device=device)
             self.tws = workspace(csa_topk_workspace_bytes(rows, max_entries, topk), device)
@@ -57,7 +60,7 @@ class CsaStep:
         if self.fused:
             sel = csa_index_select_fp4 if self.fp4 else csa_index_select
             sel(q_idx, q_off, q_pos, k_idx, ent_off, self.batch, self.max_q, self.max_entries,
-                self.c, self.topk, self.idx, self.count, self.n_vis, stream=stream)
+                self.c, self.topk, self.idx, self.count, self.n_vis, ws=self.sws, stream=stream)
             return
         score = csa_index_score_fp4 if self.fp4 else csa_index_score
         score(q_idx, q_off, q_pos, k_idx, ent_off, self.batch, self.max_q, self.max_entries,

@@ -30,7 +30,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_version_and_struct_layout():
-    assert lca.abi_version() == 6
+    assert lca.abi_version() == 7
     # 4 int32, 10 pointers, 4 window pointers, int32 window (+4 padding), sink pointer,
     # int32 idx_format, int32 kv_format
     assert ctypes.sizeof(lca.LcaLayer) == 16 + 10 * 8 + 4 * 8 + 8 + 8 + 8
@@ -57,13 +57,11 @@ def test_kv_compress_validation():
 @pytest.mark.parametrize("fn", ["lca_csa_index_select", "lca_csa_index_select_fp4"])
 def test_index_select_validation(fn):
     f = getattr(L(), fn)
-    # q, q_off, q_pos, k, ent_off, batch, max_q, max_entries, d_idx, c, k, idx, count, n_vis
-    args = [FAKE] * 5 + [2, 32, 1000, 64, 4, 256, FAKE, FAKE, None, None]
+    # q, q_off, q_pos, k, ent_off, batch, max_q, max_entries, d_idx, c, k, idx, count, n_vis,
+    # ws, ws_bytes, stream
+    args = [FAKE] * 5 + [2, 32, 1000, 64, 4, 256, FAKE, FAKE, None, None, 0, None]
     bad = list(args); bad[8] = 32
     assert f(*bad) == E_UNSUP                          # d_idx other than 64
-    bad = list(args); bad[6] = 8
-    assert f(*bad) == E_UNSUP                          # fewer than 16 query tokens per sequence
-    assert "16" in lca.last_error()
     bad = list(args); bad[10] = 0
     assert f(*bad) == E_SHAPE                          # k = 0
     bad = list(args); bad[9] = 0
@@ -74,6 +72,41 @@ def test_index_select_validation(fn):
     assert f(*bad) == E_ALIGN
     bad = list(args); bad[5] = 0
     assert f(*bad) == OK                               # empty batch: nothing to do
+    # decode-sized batches (fewer than 16 query rows per sequence) need the workspace
+    need = L().lca_csa_index_select_workspace_bytes(2, 8, 1000, 256)
+    assert need > 0
+    assert L().lca_csa_index_select_workspace_bytes(2, 32, 1000, 256) == 0   # prefill form
+    bad = list(args); bad[6] = 8
+    assert f(*bad) == E_WS
+    bad[14] = FAKE; bad[15] = need - 1
+    assert f(*bad) == E_WS
+    bad[15] = need; bad[14] = MIS
+    assert f(*bad) == E_ALIGN
+    bad = list(args); bad[6] = 8; bad[7] = 2048 * 2048 + 1; bad[14] = FAKE; bad[15] = 1 << 40
+    assert f(*bad) == E_UNSUP                          # beyond 4M entries per row
+
+
+def test_index_select_workspace_bounds_the_candidates():
+    """The candidate region holds every row the budget rule allows: for each visible
+    count nv in (k, max_n], ceil(nv / 2048) chunks of the rule's slot size."""
+    import math
+
+    def slot(nv, k):   # the rule as the header states it
+        e = min(2048, -(-k * 2048 // nv))
+        sq = math.isqrt(e - 1) + 1
+        target = min(2048, e + 6 * sq + 8)
+        return min(2048, target + 16)
+
+    f = L().lca_csa_index_select_workspace_bytes
+    for max_n, k in [(5000, 256), (262144, 2048), (70001, 2048), (3000, 2048), (2048, 2048)]:
+        rows = 3
+        need = max((-(-nv // 2048)) * slot(nv, k) for nv in range(k + 1, max_n + 1)) \
+            if max_n > k else 0
+        nch = max(1, -(-max_n // 2048))
+        al = lambda x: (x + 255) // 256 * 256
+        expect = al(rows * 4) + al(rows * nch * 4) + al(rows * max(need, 1) * 4)
+        assert f(rows, 1, max_n, k) == expect, (max_n, k)
+    assert min(slot(nv, 2048) for nv in range(2049, 1 << 22, 997)) >= 31
 
 
 def test_kv_compress_kv8_validation():

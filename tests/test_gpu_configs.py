@@ -54,35 +54,51 @@ def _check_csa_row(q, qidx, pos, k_cmp, v_cmp, kidx_host, c, topk, idx, cnt, out
     assert_lse_close(lse, l, what)
 
 
+def _oracle_cache(raw, tok_off, ent_off, c):
+    """The oracle's compression of every sequence's raw tokens: bf16 bits [entries, 128]."""
+    parts = []
+    for b in range(len(tok_off) - 1):
+        n = int(ent_off[b + 1] - ent_off[b])
+        x = _f64(raw[int(tok_off[b]): int(tok_off[b]) + n * c])
+        parts.append(oracle.csa_hca.compress_to_cache(x, c))
+    return np.concatenate(parts)
+
+
 @pytest.mark.parametrize("name", ["csa_decode_8k", "csa_decode_1m", "csa_decode_1m_fp4"])
 def test_csa_decode_full(name):
+    """The whole compressed cache bit-exact against the oracle's block means of the raw
+    tokens; then, for every sequence of two input replicas, the selection bit-exact and
+    the attention against the oracle's attention over the oracle-compressed rows."""
     step(f"full-size {name}")
     wl = workloads.get(name)
     run = bench.CsaDecodeRunner(wl, replicas=2)
-    run.step(0)
-    torch.cuda.synchronize()
     inp = run.inp
-    _check_compress_sample(inp["raw_k"], inp["tok_off"], inp["ent_off"], run.k_cmp, wl.c, 2048, 1)
-    _check_compress_sample(inp["raw_v"], inp["tok_off"], inp["ent_off"], run.v_cmp, wl.c, 2048, 2)
-    r = inp["replicas"][0]
-    idx, cnt = run.st.idx.cpu().numpy(), run.st.count.cpu().numpy()
-    out, lse = _f64(run.out), run.lse.cpu().numpy()
-    for b in range(wl.batch):
-        s, e = int(inp["ent_off"][b]), int(inp["ent_off"][b + 1])
-        _check_csa_row(_f64(r["q"][b]), r["q_idx"][b].cpu().numpy(), int(inp["L"][b]),
-                       run.k_cmp[s:e], run.v_cmp[s:e], r["k_idx"][s:e].cpu().numpy(), wl.c,
-                       wl.topk, idx[b], cnt[b], out[b], lse[b], f"{name} seq {b}", wl.idx_fp4)
-    # a second replica (different indexer inputs) in the same launch shape
-    run.step(1)
-    torch.cuda.synchronize()
-    r = inp["replicas"][1]
-    idx, cnt = run.st.idx.cpu().numpy(), run.st.count.cpu().numpy()
-    out, lse = _f64(run.out), run.lse.cpu().numpy()
-    b = wl.batch - 1
-    s, e = int(inp["ent_off"][b]), int(inp["ent_off"][b + 1])
-    _check_csa_row(_f64(r["q"][b]), r["q_idx"][b].cpu().numpy(), int(inp["L"][b]),
-                   run.k_cmp[s:e], run.v_cmp[s:e], r["k_idx"][s:e].cpu().numpy(), wl.c, wl.topk,
-                   idx[b], cnt[b], out[b], lse[b], f"{name} replica 1 seq {b}", wl.idx_fp4)
+    Kc = _oracle_cache(inp["raw_k"], inp["tok_off"], inp["ent_off"], wl.c)
+    Vc = _oracle_cache(inp["raw_v"], inp["tok_off"], inp["ent_off"], wl.c)
+    assert np.array_equal(bf16_bits(run.k_cmp), Kc), "compressed K cache"
+    assert np.array_equal(bf16_bits(run.v_cmp), Vc), "compressed V cache"
+    Kf, Vf = oracle.bf16_bits_to_f64(Kc), oracle.bf16_bits_to_f64(Vc)
+    scorer = oracle.index_scores_fp4 if wl.idx_fp4 else oracle.index_scores
+    for rep in range(2):
+        run.step(rep)
+        torch.cuda.synchronize()
+        L = run.layer(rep)
+        idx, cnt = L["idx"].cpu().numpy(), L["count"].cpu().numpy()
+        out, lse = _f64(L["out"]), L["lse"].cpu().numpy()
+        kidx_all = L["k_idx"].cpu().numpy()
+        for b in range(wl.batch):
+            what = f"{name} replica {rep} seq {b}"
+            s, e = int(inp["ent_off"][b]), int(inp["ent_off"][b + 1])
+            pos = int(inp["L"][b])
+            n_vis = oracle.n_visible(pos, wl.c, e - s)
+            sel = oracle.topk_select(scorer(L["q_idx"][b].cpu().numpy(), kidx_all[s:e]), n_vis,
+                                     wl.topk)
+            assert cnt[b] == len(sel), what
+            assert np.array_equal(idx[b, :cnt[b]], sel), what
+            assert np.all(idx[b, cnt[b]:] == -1), what
+            o, lv, _ = oracle.attention(_f64(L["q"][b]), Kf[s:e][sel], Vf[s:e][sel], SCALE)
+            assert_attn_close(out[b], o, what)
+            assert_lse_close(lse[b], lv, what)
 
 
 def test_hca_decode_full():

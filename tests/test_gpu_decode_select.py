@@ -1,0 +1,156 @@
+"""csa_index_select in its decode form (fewer than 16 query rows per sequence: the
+candidate index pass and the per-row selection) against the oracle's scores and
+top-k, bit-exact: ragged and padded batches, rows at and around k, heavy ties and
+top-k sets bunched in a few chunks (which take the rescan path), the extreme int8
+codes including -128, FP4 codes, and repeated calls on one workspace."""
+import numpy as np
+import pytest
+import torch
+
+import long_context_attention_19_amd as lca
+import oracle
+from gpu_util import DEV, i64_dev, i8_dev, offsets, step
+from workloads import fp4_uniform, int8_uniform, rng
+
+pytestmark = pytest.mark.gpu
+
+
+def _positions(g, Ns, nq, c, k):
+    """Query positions per row: mostly the full context, some rows seeing fewer than
+    k entries, exactly k, k + 1, or nothing."""
+    q_pos = []
+    for b, n in enumerate(Ns):
+        for i in range(nq[b]):
+            pick = (b + 3 * i) % 7
+            if pick == 0:
+                q_pos.append(n * c + 3)                 # every entry visible
+            elif pick == 1:
+                q_pos.append(min(n, k) * c)             # at most k visible
+            elif pick == 2:
+                q_pos.append(min(n, k + 1) * c + 1)     # one more than k
+            elif pick == 3:
+                q_pos.append(0)                         # nothing visible
+            else:
+                q_pos.append(int(g.integers(0, n * c + 5)) if n else 7)
+    return q_pos
+
+
+def _run(Ns, nq, k, k_idx, q_idx, q_pos, c=4, fp4=False, reps=2, tag=""):
+    B, max_q = len(Ns), max(nq)
+    assert max_q < 16
+    ent_off, q_off = offsets(Ns), offsets(nq)
+    rows = int(q_off[-1])          # packed rows only: no padding rows in the outputs
+    max_n = max(max(Ns), 1)
+    ws = lca.workspace(lca.csa_index_select_workspace_bytes(B, max_q, max_n, k))
+    idx = torch.full((max(rows, 1), k), -5, dtype=torch.int32, device=DEV)
+    count = torch.full((max(rows, 1),), -5, dtype=torch.int32, device=DEV)
+    n_vis = torch.full((max(rows, 1),), -5, dtype=torch.int32, device=DEV)
+    width = 32 if fp4 else 64
+    kd = i8_dev(k_idx if len(k_idx) else np.zeros((1, width), np.int8))
+    qd = i8_dev(q_idx)
+    sel = lca.csa_index_select_fp4 if fp4 else lca.csa_index_select
+    refs = {}
+    for b in range(B):
+        keys = k_idx[ent_off[b]:ent_off[b + 1]]
+        for i in range(nq[b]):
+            r = int(q_off[b]) + i
+            nv = oracle.n_visible(q_pos[r], c, Ns[b])
+            if Ns[b] == 0:
+                sc = np.zeros(0, np.int64)
+            elif fp4:
+                sc = oracle.index_scores_fp4(q_idx[r], keys)
+            else:
+                sc = oracle.index_scores(q_idx[r], keys)
+            refs[r] = (nv, oracle.topk_select(sc, nv, k))
+    for rep in range(reps):   # nothing carries over between calls on one workspace
+        step(f"csa_index_select decode {tag} rep={rep} B={B} max_q={max_q} k={k} fp4={fp4}")
+        sel(qd, i64_dev(q_off), i64_dev(q_pos), kd, i64_dev(ent_off), B, max_q, max_n, c, k,
+            idx, count, n_vis, ws=ws)
+        torch.cuda.synchronize()
+        I, C, NV = idx.cpu().numpy(), count.cpu().numpy(), n_vis.cpu().numpy()
+        for r, (nv, ref) in refs.items():
+            assert NV[r] == nv, (tag, rep, r)
+            assert C[r] == len(ref), (tag, rep, r, C[r], len(ref))
+            assert np.array_equal(I[r, :len(ref)], ref), (tag, rep, r)
+            assert np.all(I[r, len(ref):] == -1), (tag, rep, r)
+
+
+@pytest.mark.parametrize("k", [256, 2048])
+def test_decode_select_ragged(k):
+    g = rng(600, k, 0)
+    Ns, nq = [70001, 5000, 3000, 0, 2049, 40000], [1, 3, 0, 2, 1, 2]
+    c = 4
+    kk = int8_uniform(g, (sum(Ns), 64))
+    qq = int8_uniform(g, (sum(nq), 64))
+    _run(Ns, nq, k, kk, qq, _positions(g, Ns, nq, c, k), c, tag=f"ragged k={k}")
+
+
+def test_decode_select_one_row_per_sequence_long():
+    # the decode shape: one query row per sequence, 4 rows of 262,144 entries
+    g = rng(600, 1, 1)
+    Ns, nq, k = [262144, 262143, 200000, 131073], [1, 1, 1, 1], 2048
+    kk = int8_uniform(g, (sum(Ns), 64))
+    qq = int8_uniform(g, (4, 64))
+    q_pos = [n * 4 for n in Ns]
+    _run(Ns, nq, k, kk, qq, q_pos, tag="long")
+
+
+@pytest.mark.parametrize("name", ["ties", "all_equal", "sorted", "bunched", "extreme", "k_one"])
+def test_decode_select_hard_cases(name):
+    """Cases where chunks hold far more than their share of the top-k at or above the
+    threshold bin: the selection rescans the row's keys, with the same result."""
+    g = rng(601, 0, ["ties", "all_equal", "sorted", "bunched", "extreme", "k_one"].index(name))
+    Ns, nq, k, c = [30000, 9000], [2, 1], 2048, 4
+    n = sum(Ns)
+    qq = int8_uniform(g, (3, 64))
+    if name == "ties":        # scores in [-64, 64]: each value has hundreds of copies
+        kk = g.integers(-1, 2, (n, 64)).astype(np.int8)
+        qq = g.integers(-1, 2, (3, 64)).astype(np.int8)
+    elif name == "all_equal":
+        kk = np.tile(int8_uniform(g, (1, 64)), (n, 1))
+    elif name == "sorted":    # scores rise with the index: the top-k sits in the last chunks
+        qq = np.ones((3, 64), np.int8)
+        v = np.concatenate([np.floor(-127 + 254.0 * np.arange(m) / m) for m in Ns])
+        kk = np.repeat(v.astype(np.int8)[:, None], 64, axis=1)
+    elif name == "bunched":   # 3000 consecutive entries score near the maximum
+        kk = int8_uniform(g, (n, 64))
+        for b, r in [(0, 0), (1, 2)]:
+            s = int(offsets(Ns)[b]) + 5000
+            kk[s:s + 3000] = np.clip(qq[r].astype(np.int16)[None, :] +
+                                     g.integers(-3, 4, (3000, 64)), -127, 127).astype(np.int8)
+    elif name == "extreme":   # -128 codes: a query and keys of all -128 reach 2^20
+        kk = int8_uniform(g, (n, 64))
+        kk[::97] = -128
+        kk[1::97] = 127
+        kk[2::89] = -127
+        qq = np.full((3, 64), -128, np.int8)
+        qq[1, :32] = 127
+    else:   # k_one
+        kk = int8_uniform(g, (n, 64))
+        k = 1
+    q_pos = [Ns[0] * c, Ns[0] * c - 1, Ns[1] * c + 2]
+    _run(Ns, nq, k, kk, qq, q_pos, c, tag=name)
+
+
+def test_decode_select_max_q_many_rows():
+    """Several query rows per sequence (max_q 7) over ragged sequences: the index pass and
+    the selection skip the padding rows; outputs have exactly q_off[B] rows."""
+    g = rng(602, 0, 0)
+    Ns, nq, k = [9000, 20000, 4000, 12345], [7, 1, 4, 6], 512
+    kk = int8_uniform(g, (sum(Ns), 64))
+    qq = int8_uniform(g, (sum(nq), 64))
+    _run(Ns, nq, k, kk, qq, _positions(g, Ns, nq, 4, k), 4, tag="max_q=7")
+
+
+@pytest.mark.parametrize("name", ["random", "ties"])
+def test_decode_select_fp4(name):
+    g = rng(603, 0, ["random", "ties"].index(name))
+    Ns, nq, k = [50000, 7000, 2100], [1, 2, 1], 2048
+    kk = fp4_uniform(g, (sum(Ns), 32))
+    qq = fp4_uniform(g, (4, 32))
+    if name == "ties":   # codes 0, +-0.5 only: few distinct scores
+        kk = (g.integers(0, 2, (sum(Ns), 32)) * 0x11 + g.integers(0, 2, (sum(Ns), 32)) * 0x88)
+        kk = kk.astype(np.uint8).view(np.int8)
+        qq = np.full((4, 32), 0x11, np.uint8).view(np.int8)
+    _run(Ns, nq, k, kk.view(np.int8), qq.view(np.int8), _positions(g, Ns, nq, 4, k), 4,
+         fp4=True, tag=f"fp4 {name}")

@@ -224,6 +224,7 @@ def test_index_select_bit_exact(name):
     idx = torch.full((rows, k), -5, dtype=torch.int32, device=DEV)
     count = torch.full((rows,), -5, dtype=torch.int32, device=DEV)
     n_vis = torch.full((rows,), -5, dtype=torch.int32, device=DEV)
+    assert lca.csa_index_select_workspace_bytes(B, max_q, max(Ns), k) == 0   # prefill form
     lca.csa_index_select(i8_dev(q_idx), i64_dev(q_off), i64_dev(q_pos),
                          i8_dev(k_idx if len(k_idx) else np.zeros((1, 64), np.int8)),
                          i64_dev(ent_off), B, max_q, max(Ns), c, k, idx, count, n_vis)

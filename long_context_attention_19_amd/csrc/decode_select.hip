@@ -59,6 +59,7 @@ static_assert(DF_ROUNDS * DI_NW * 32 == DS_CHUNK, "FP4 rounds cover the chunk");
 constexpr int DS_VPT = DS_SEL_VPT;
 constexpr int DS_RC = DI_NT * DS_VPT;                            // slots per selection round
 static_assert(DS_RC < (1 << 16), "a round's counts fit 16 bits");
+static_assert(DS_MAX_CHUNKS % DS_NT == 0, "cut marks per selection thread");
 static_assert(DS_VPT <= DS_MIN_SLOT, "a thread's run of slots crosses at most one chunk boundary");
 static_assert(HIST_BINS % DI_NT == 0 && DS_CHUNK % DI_NT == 0, "bins and entries per thread");
 
@@ -80,6 +81,7 @@ size_t ds_cand_slots(int max_n, int k) {
 size_t ds_ws_bytes(int rows, int max_n, int k) {
   const size_t nch = (size_t)std::max(1, (max_n + DS_CHUNK - 1) / DS_CHUNK);
   size_t b = align256((size_t)rows * 4);                         // n_vis
+  b += align256((size_t)rows * 16);                              // row records
   b += align256((size_t)rows * nch * 4);                         // per-chunk cut marks
   b += align256((size_t)rows * std::max<size_t>(ds_cand_slots(max_n, k), 1) * 4);   // candidates
   return b;
@@ -91,6 +93,8 @@ void ds_ws_carve(void* ws, int rows, int max_n, int k, DsLayer& L) {
   char* p = reinterpret_cast<char*>(ws);
   L.n_vis = reinterpret_cast<int32_t*>(p);
   p += align256((size_t)rows * 4);
+  L.rinfo = reinterpret_cast<int4*>(p);
+  p += align256((size_t)rows * 16);
   L.dcut = reinterpret_cast<int32_t*>(p);
   p += align256((size_t)rows * nch * 4);
   L.cand = reinterpret_cast<int32_t*>(p);
@@ -267,11 +271,13 @@ struct DsSmemChunk {
   __attribute__((aligned(16))) int32_t sc[DS_CHUNK];   // keys of the chunk
   int32_t out[DS_CHUNK];                          // kept slot words, compacted
 };
+constexpr int DS_MC = DS_RC / 2;                  // candidates at or above the threshold bin
 struct DsSmemSelect {
   int32_t hist[HIST_BINS];                        // coarse, then fine histogram
   uint32_t c[DS_RC];                              // one round of candidate slots
+  int32_t key[DS_MC];                             // the candidates at or above bin bA, in
+  int32_t ent[DS_MC];                             // index order: key and entry
 };
-
 
 // The selection of one row from its candidates (all DI_NT threads of the work-group).
 template <bool FP4>
@@ -280,6 +286,7 @@ __device__ void ds_select_row(const DsLayer& L, int64_t row, int b, int64_t nv,
   constexpr int NT = DI_NT;
   constexpr int VPT = DS_VPT;
   constexpr int RC = DS_RC;
+  constexpr int DPT = DS_MAX_CHUNKS / NT;         // cut marks per thread
   const int t = threadIdx.x;
   const int lane = t & (WAVE - 1);
   const int k = L.k;
@@ -288,119 +295,133 @@ __device__ void ds_select_row(const DsLayer& L, int64_t row, int b, int64_t nv,
   const DsBudget bud = ds_budget(nv, k);
   const int vs = nch * bud.slot;   // the row's candidate slots
   const int32_t* crow = L.cand + row * L.cand_slots;
-
-  // the highest cut bin of a chunk that dropped entries (0: none)
-  if (t == 0) s_b[2] = 0;
-  int32_t dm = 0;
-  for (int ch = t; ch < nch; ch += NT) dm = max(dm, L.dcut[row * L.nch + ch]);
-  dm = wave_max(dm);
-  __syncthreads();
-  if (lane == 0 && dm > 0) atomicMax(&s_b[2], dm);
-
-  // A round of slots: coalesced loads into LDS, then thread t holds its VPT consecutive
-  // slots in registers (read from LDS at an odd stride: no two lanes of a read share a
-  // bank) for every pass; a slot word is key << 11 | entry within its chunk, 0 empty.
   const int nround = (vs + RC - 1) / RC;
+
+  // A round of slots: coalesced loads, then through LDS thread t holds its VPT
+  // consecutive slots in registers (read at an odd stride: no two lanes of a read share
+  // a bank); a slot word is key << 11 | entry within its chunk, 0 an empty slot.
+  // Threads past the round's end hold empty slots, and their waves skip the passes.
   uint32_t ck[VPT];
-  auto stage = [&](int rd) __attribute__((always_inline)) {
-    const int r0 = rd * RC;
-    const int n_in = min(RC, vs - r0);
+  int n_in = 0;
+  auto issue = [&](int rd) __attribute__((always_inline)) {
+    n_in = min(RC, vs - rd * RC);
     // a buffer view of the round: loads past its end return 0, an empty slot
     const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<int32_t*>(crow + r0), 0, n_in * 4, DS_RSRC_WORD3);
-    // every load in flight before the first is used (into the same registers the
-    // thread's own slots take next)
+        const_cast<int32_t*>(crow + rd * RC), 0, n_in * 4, DS_RSRC_WORD3);
 #pragma unroll
-    for (int u = 0; u < VPT; ++u)
-      ck[u] = __builtin_amdgcn_raw_buffer_load_b32(rs, (t + NT * u) * 4, 0, 0);
+    for (int u = 0; u < VPT; ++u) ck[u] = __builtin_amdgcn_raw_buffer_load_b32(rs, (t + NT * u) * 4, 0, 0);
+  };
+  auto land = [&]() __attribute__((always_inline)) {
     __syncthreads();   // the previous round's slots are no longer read
 #pragma unroll
     for (int u = 0; u < VPT; ++u) sm.c[t + NT * u] = ck[u];
     __syncthreads();
-    const bool mine = VPT * t < n_in;   // threads past the round's end hold empty slots
+    const bool mine = VPT * t < n_in;
 #pragma unroll
     for (int u = 0; u < VPT; ++u) ck[u] = mine ? sm.c[VPT * t + u] : 0u;
   };
+  const bool one = nround == 1;
 
-  if (nround == 1) stage(0);
+  // the chunks' cut marks, loaded beside the first round's slots: the highest cut bin
+  // of a chunk that dropped entries (0: none)
+  int32_t dc[DPT];
+#pragma unroll
+  for (int e = 0; e < DPT; ++e) dc[e] = L.dcut[row * L.nch + min(t + NT * e, nch - 1)];
+  if (one) issue(0);
+  if (t == 0) s_b[2] = 0;
+  int32_t dm = 0;
+#pragma unroll
+  for (int e = 0; e < DPT; ++e) dm = max(dm, t + NT * e < nch ? dc[e] : 0);
+  dm = wave_max(dm);
   for (int i = t; i < HIST_BINS; i += NT) sm.hist[i] = 0;
   __syncthreads();
-  const int dplus = s_b[2];
+  if (lane == 0 && dm > 0) atomicMax(&s_b[2], dm);
+  if (one) land();
+
+  // coarse histogram of the candidates' keys
   for (int rd = 0; rd < nround; ++rd) {
-    if (nround > 1) stage(rd);
-#pragma unroll
-    for (int u = 0; u < VPT; ++u)
-      if (ck[u]) atomicAdd(&sm.hist[ck[u] >> 21], 1);
-  }
-  __syncthreads();
-  int bA, above;
-  ds_threshold<NT, HIST_BINS>(sm.hist, k, s_scan, s_b, bA, above);
-  // Fewer than k candidates, or a chunk cut above the threshold bin: some entry of bin
-  // bA or above may have been dropped.  Otherwise every one is a candidate.
-  const bool fast = s_b[3] >= k && dplus <= bA;
-  if (fast) {
-    for (int i = t; i < FINE_BINS; i += NT) sm.hist[i] = 0;
-    __syncthreads();
-    for (int rd = 0; rd < nround; ++rd) {
-      if (nround > 1) stage(rd);
+    if (!one) {
+      issue(rd);
+      land();
+    }
+    if (VPT * t < n_in) {
 #pragma unroll
       for (int u = 0; u < VPT; ++u)
-        if ((int)(ck[u] >> 21) == bA && ck[u]) atomicAdd(&sm.hist[(ck[u] >> 11) & 1023], 1);
+        if (ck[u]) atomicAdd(&sm.hist[ck[u] >> 21], 1);
     }
+  }
+  __syncthreads();
+  const int dplus = s_b[2];
+  int bA, above;
+  ds_threshold<NT, HIST_BINS>(sm.hist, k, s_scan, s_b, bA, above);
+  const int n_cand = s_b[3];
+  const int m = above + sm.hist[bA];   // candidates at or above bin bA
+  __syncthreads();
+  // Fewer than k candidates, or a chunk cut above the threshold bin: some entry of bin
+  // bA or above may have been dropped.  Otherwise every one is a candidate.  (More
+  // candidates in bin bA and above than the compacted lists hold: heavy ties.)
+  const bool fast = n_cand >= k && dplus <= bA && m <= DS_MC;
+  if (fast) {
+    // the candidates at or above bin bA, compacted in index order as (key, entry)
+    int32_t run = 0;
+    for (int rd = 0; rd < nround; ++rd) {
+      if (!one) {
+        issue(rd);
+        land();
+      }
+      int32_t nk = 0;
+#pragma unroll
+      for (int u = 0; u < VPT; ++u) nk += (int)(ck[u] >> 21) >= bA && ck[u] ? 1 : 0;
+      int32_t tot;
+      int32_t off = run + block_excl_scan<NT>(nk, s_scan, &tot);
+      if (nk) {
+        // this thread's first slot lies in chunk ch0; its run of VPT slots crosses at
+        // most one chunk boundary (a slot region holds at least DS_MIN_SLOT words), at
+        // slot u_next of the run
+        const int v0 = rd * RC + VPT * t;
+        const int ch0 = v0 / bud.slot;
+        const int u_next = (ch0 + 1) * bud.slot - v0;
+#pragma unroll
+        for (int u = 0; u < VPT; ++u)
+          if ((int)(ck[u] >> 21) >= bA && ck[u]) {
+            const int ch = ch0 + (u >= u_next ? 1 : 0);
+            sm.key[off] = (int32_t)(ck[u] >> 11);
+            sm.ent[off] = ch * DS_CHUNK + (int)(ck[u] & 2047);
+            ++off;
+          }
+      }
+      run += tot;
+    }
+    for (int i = t; i < FINE_BINS; i += NT) sm.hist[i] = 0;
+    __syncthreads();
+    // thread t takes compacted candidates [IPT t, IPT t + IPT), in index order
+    const int ipt = (m + NT - 1) / NT;
+    const int i0 = min(ipt * t, m), i1 = min(i0 + ipt, m);
+    for (int i = i0; i < i1; ++i)
+      if ((sm.key[i] >> 10) == bA) atomicAdd(&sm.hist[sm.key[i] & 1023], 1);
     __syncthreads();
     int low_t, gt_in;
     ds_threshold<NT, FINE_BINS>(sm.hist, k - above, s_scan, s_b, low_t, gt_in);
     const int T = (bA << 10) | low_t;
     const int need_eq = k - above - gt_in;   // T-valued keys to keep, lowest indices first
-    // one scan of (above T, equal to T) counts, 16 bits each (a round holds < 2^16 slots):
-    // a selected slot's place is (above-T before it) + min(T-valued before it, need_eq).
-    // The k entries gather in LDS (the round's slots are in registers) and leave in
-    // coalesced stores.
-    int32_t* s_sel = reinterpret_cast<int32_t*>(sm.c);   // free once the slots are in registers
-    const bool staged_out = nround == 1 && k <= RC;
-    int32_t gt_run = 0, eq_run = 0;
-    for (int rd = 0; rd < nround; ++rd) {
-      if (nround > 1) stage(rd);
-      int32_t ngt = 0, neq = 0;
-#pragma unroll
-      for (int u = 0; u < VPT; ++u) {
-        const int key = (int)(ck[u] >> 11);   // 0 for an empty slot, and T > 0
-        ngt += key > T ? 1 : 0;
-        neq += key == T ? 1 : 0;
-      }
-      int32_t tot2;
-      const int32_t pre = block_excl_scan<NT>((ngt << 16) | neq, s_scan, &tot2);
-      int32_t g = gt_run + (pre >> 16), q = eq_run + (pre & 0xffff);
-      // this thread's first slot: its chunk and place in it; a run of VPT slots crosses
-      // at most one chunk boundary (a slot region holds at least DS_MIN_SLOT words)
-      const int v0 = rd * RC + VPT * t;
-      int ch = v0 / bud.slot;
-      int in = v0 - ch * bud.slot;
-#pragma unroll
-      for (int u = 0; u < VPT; ++u) {
-        const int key = (int)(ck[u] >> 11);
-        const bool gt = key > T;
-        const bool eq = key == T;
-        const bool sel = gt || (eq && q < need_eq);
-        const int pos = g + min(q, need_eq);
-        if (sel && pos < k) {
-          const int e = ch * DS_CHUNK + (int)(ck[u] & 2047);
-          if (staged_out) s_sel[pos] = e;
-          else irow[pos] = e;
-        }
-        g += gt ? 1 : 0;
-        q += eq ? 1 : 0;
-        if (++in == bud.slot) {
-          in = 0;
-          ++ch;
-        }
-      }
-      gt_run += tot2 >> 16;
-      eq_run += tot2 & 0xffff;
+    // one scan of (above T, equal to T) counts, 16 bits each (m < 2^16): a selected
+    // candidate's place is (above-T before it) + min(T-valued before it, need_eq)
+    int32_t ngt = 0, neq = 0;
+    for (int i = i0; i < i1; ++i) {
+      ngt += sm.key[i] > T ? 1 : 0;
+      neq += sm.key[i] == T ? 1 : 0;
     }
-    if (staged_out) {   // (otherwise written in place above)
-      __syncthreads();
-      for (int p = t; p < k; p += NT) irow[p] = s_sel[p];
+    int32_t tot2;
+    const int32_t pre = block_excl_scan<NT>((ngt << 16) | neq, s_scan, &tot2);
+    int32_t g = pre >> 16, q = pre & 0xffff;
+    for (int i = i0; i < i1; ++i) {
+      const int key = sm.key[i];
+      const bool gt = key > T;
+      const bool eq = key == T;
+      const int pos = g + min(q, need_eq);
+      if ((gt || (eq && q < need_eq)) && pos < k) irow[pos] = sm.ent[i];
+      g += gt ? 1 : 0;
+      q += eq ? 1 : 0;
     }
   } else {   // uniform: every thread read the same counts and bins
     uint32_t qd[16];
@@ -416,15 +437,21 @@ __global__ __launch_bounds__(DI_NT) void ds_chunk_kernel(DsBatch db) {
   __shared__ int32_t s_scan[DI_NW + 1];
   __shared__ int32_t s_cut;
   const DsLayer& L = db.layer[blockIdx.z];
+  const int t = threadIdx.x;
   int64_t row;
   int b;
-  if (!ds_row(db.q_off, db.max_q, row, b)) return;
+  if (!ds_row(db.q_off, db.max_q, row, b)) {
+    if (blockIdx.x == 0 && t == 0) L.rinfo[blockIdx.y] = make_int4(-1, 0, 0, 0);   // padding
+    return;
+  }
   const int64_t e0 = L.ent_off[b];
   const int64_t N = min(L.ent_off[b + 1] - e0, (int64_t)L.max_entries);
   const int64_t nv = max(min(db.q_pos[row] / L.c, N), (int64_t)0);
-  const int t = threadIdx.x;
   const int k = L.k;
-  if (blockIdx.x == 0 && t == 0) L.n_vis[row] = (int32_t)nv;
+  if (blockIdx.x == 0 && t == 0) {
+    L.n_vis[row] = (int32_t)nv;
+    L.rinfo[blockIdx.y] = make_int4((int)row, (int)nv, b, 0);   // for the select launch
+  }
   if (nv <= k) {   // every visible entry is selected: the first work-group writes the row
     if (blockIdx.x == 0) {
       int32_t* irow = L.idx + row * k;
@@ -566,13 +593,10 @@ __global__ __launch_bounds__(DI_NT) void ds_select_kernel(DsBatch db) {
   __shared__ int32_t s_scan[DI_NW + 1];
   __shared__ int32_t s_b[4];
   const DsLayer& L = db.layer[blockIdx.z];
-  int64_t row;
-  int b;
-  if (!ds_row(db.q_off, db.max_q, row, b)) return;
-  const int64_t e0 = L.ent_off[b];
-  const int64_t N = min(L.ent_off[b + 1] - e0, (int64_t)L.max_entries);
-  const int64_t nv = max(min(db.q_pos[row] / L.c, N), (int64_t)0);
-  if (nv <= L.k) return;   // written by the chunk launch
+  const int4 ri = L.rinfo[blockIdx.y];   // (row, nv, sequence) from the chunk launch
+  if (ri.x < 0 || ri.y <= L.k) return;   // padding, or written by the chunk launch
+  const int64_t row = ri.x, nv = ri.y;
+  const int b = ri.z;
   if (threadIdx.x == 0) L.count[row] = L.k;
   ds_select_row<FP4>(L, row, b, nv, sm, s_scan, s_b);
 }

@@ -106,6 +106,7 @@ struct DsLayer {
   const int8_t* k_idx;   // [ent_off[B]][64] int8, or [.][32] packed FP4
   const int64_t* ent_off;
   int32_t* n_vis;        // [rows] out
+  int4* rinfo;           // [batch * max_q] per grid row: (query row or -1, nv, sequence, 0)
   int32_t* dcut;         // [rows][nch] a chunk's cut bin if it dropped entries, else 0
   int32_t* cand;         // [rows][cand_slots] per chunk `slot` words: (key << 11 | entry in
                          // chunk) of the kept entries in index order, then 0
@@ -126,7 +127,7 @@ struct DsBatch {
   DsLayer layer[MAX_BATCH_LAYERS];
 };
 size_t ds_ws_bytes(int rows, int max_n, int k);
-// carve one layer's workspace: n_vis, dcut, cand
+// carve one layer's workspace: n_vis, rinfo, dcut, cand
 void ds_ws_carve(void* ws, int rows, int max_n, int k, DsLayer& L);
 hipError_t launch_ds_chunks(const DsBatch& db, int batch, hipStream_t st);   // candidates
 hipError_t launch_ds_select(const DsBatch& db, int batch, hipStream_t st);   // the top-k

@@ -104,7 +104,7 @@ def test_index_select_workspace_bounds_the_candidates():
             if max_n > k else 0
         nch = max(1, -(-max_n // 2048))
         al = lambda x: (x + 255) // 256 * 256
-        expect = al(rows * 4) + al(rows * nch * 4) + al(rows * max(need, 1) * 4)
+        expect = al(rows * 4) + al(rows * 16) + al(rows * nch * 4) + al(rows * max(need, 1) * 4)
         assert f(rows, 1, max_n, k) == expect, (max_n, k)
     assert min(slot(nv, 2048) for nv in range(2049, 1 << 22, 997)) >= 31
 

@@ -185,13 +185,17 @@ def _select_case(name):
         Ns, nq, k = [9000], [16], 100
         kk = np.tile(int8_uniform(g, (1, 64)), (9000, 1))
         qq = int8_uniform(g, (16, 64))
-    elif name == "extreme":   # scores up to +-64 * 127^2
+    elif name == "extreme":   # scores up to +-64 * 127^2, and 2^20 from all -128 codes
         Ns, nq, k = [5000], [16], 77
         kk = (127 * np.where(g.random((5000, 64)) < 0.5, -1, 1)).astype(np.int8)
         kk[:3] = 127
         kk[3:6] = -127
+        kk[6:9] = -128
+        kk[9, :] = -128
+        kk[9, 0] = -127   # 2^20 - 128, the next reachable score
         qq = np.full((16, 64), 127, np.int8)
         qq[1::2] = -127
+        qq[2] = -128
     elif name == "k_large":   # k above the LDS-staged rows: rows written in place
         Ns, nq, k = [10001], [20], 3000
         kk = int8_uniform(g, (sum(Ns), 64))
@@ -251,6 +255,11 @@ def _topk_cases():
     big = oracle.index_scores(q, int8_uniform(g, (70001, 64)))
     ext = g.integers(-(1 << 20), 1 << 20, 5000)
     ext[:4] = [-(1 << 20), (1 << 20) - 1, 1032256, -1032256]
+    # 2^20: a query and a key of all -128 codes (the radix key clamps it one lower, a
+    # value no int8 score reaches), beside 2^20 - 128, the next reachable score
+    ext128 = g.integers(-(1 << 20), 1 << 20, 5000)
+    ext128[[7, 900, 4000]] = 1 << 20
+    ext128[[5, 901]] = (1 << 20) - 128
     return {
         "random": (rand, 10001, 256),
         "random_big_k2048": (big, 70001, 2048),
@@ -261,6 +270,7 @@ def _topk_cases():
         "chunk_multiple": (rand, 8192, 4096),
         "k_n_minus_1": (rand, 4097, 4096),
         "extreme": (ext, 5000, 77),
+        "extreme_2pow20": (ext128, 5000, 4),
         "k_one": (rand, 10001, 1),
         "one_candidate_bin": (np.concatenate([np.full(5000, 7), np.arange(10)]), 5010, 3),
         # k above the per-row merge's limit: the chunk-parallel placement

@@ -170,3 +170,21 @@ def test_topk_selects_largest_scores():
     rest = np.setdiff1d(np.arange(5000), sel)
     assert len(sel) == 300 and np.all(np.diff(sel) > 0)
     assert s[sel].min() >= s[rest].max()
+
+
+def test_scores_extreme_int8_codes():
+    """The int8 type's whole range, -128 included: a query and a key of all -128 reach
+    64 * 2^14 = 2^20 exactly (Python integers); no other pair reaches it, the next
+    reachable score being 63 * 2^14 + 128 * 127 = 2^20 - 128; the lowest is
+    64 * (-128) * 127."""
+    q = np.full(64, -128, np.int8)
+    keys = np.full((4, 64), -128, np.int8)
+    keys[1, 0] = -127                      # one product 128 * 127
+    keys[2] = 127                          # the lowest score
+    keys[3, :32] = 127                     # half and half: -2^13 * 128 + ...
+    want = [sum(int(a) * int(b) for a, b in zip(q, k)) for k in keys]
+    assert want[0] == 1 << 20 and want[1] == (1 << 20) - 128 and want[2] == -64 * 128 * 127
+    assert oracle.index_scores(q, keys).tolist() == want
+    # the two top scores keep their order in the selection (ties by index otherwise)
+    assert oracle.topk_select(oracle.index_scores(q, keys), 4, 1).tolist() == [0]
+    assert oracle.topk_select(oracle.index_scores(q, keys[1:]), 3, 1).tolist() == [0]

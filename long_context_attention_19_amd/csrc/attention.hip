@@ -550,30 +550,39 @@ __global__ __launch_bounds__(AT_NT) void attn_dma_kernel(AttnBatch ab) {
     const int id = (MODE != 0 && sparse) ? sm.ids[e - cbase] : e;
     return (uint32_t)min(max(id, 0), id_max);
   };
+  // Every row id of the stage is read first (LDS, one wait), then the DMAs are issued:
+  // the DMA's inline assembly clobbers memory, so an id read placed after one would
+  // wait on its own.
   auto issue = [&](int buf, int tb, int cbase, int e_last) __attribute__((always_inline)) {
     if constexpr (KV) {
-      // FP8 halves: 16 rows of 64 bytes, lane -> (row lane / 4, chunk lane % 4)
+      // FP8 halves: 16 rows of 64 bytes, lane -> (row lane / 4, chunk lane % 4);
+      // bf16 halves: 2 x 8 rows of 128 bytes, lane -> (row lane / 8, slot lane % 8)
+      const uint32_t rid0 = row_id(wrow0 + (lane >> 2), tb, cbase, e_last);
+      uint32_t rid[2];
+#pragma unroll
+      for (int u = 0; u < 2; ++u) rid[u] = row_id(wrow0 + 8 * u + (lane >> 3), tb, cbase, e_last);
       {
-        const int r = wrow0 + (lane >> 2);
-        const uint32_t off = row_id(r, tb, cbase, e_last) * KV8_ROW_BYTES + (uint32_t)(lane & 3) * 16u;
+        const uint32_t off = rid0 * KV8_ROW_BYTES + (uint32_t)(lane & 3) * 16u;
         dma16(kseq, off, k_lds0 + buf * (ST * 64));
         dma16(vseq, off, v_lds0 + buf * (ST * 64));
       }
-      // bf16 halves: 2 x 8 rows of 128 bytes, lane -> (row lane / 8, slot lane % 8)
       const uint32_t khi0 = lds_addr(&sm.khi[buf][0]), vhi0 = lds_addr(&sm.vhi[buf][0]);
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
         const int r = wrow0 + 8 * u + (lane >> 3);
-        const uint32_t base = row_id(r, tb, cbase, e_last) * KV8_ROW_BYTES + 64u;
+        const uint32_t base = rid[u] * KV8_ROW_BYTES + 64u;
         const int sl = lane & 7;
         dma16(kseq, base + kv8_kslot(r, sl) * 16u, khi0 + (uint32_t)(wrow0 + 8 * u) * 128u);
         dma16(vseq, base + kv8_vslot(r, sl) * 16u, vhi0 + (uint32_t)(wrow0 + 8 * u) * 128u);
       }
     } else {
+      uint32_t rid[NU];
+#pragma unroll
+      for (int u = 0; u < NU; ++u) rid[u] = row_id(wrow0 + 4 * u + my_row, tb, cbase, e_last);
 #pragma unroll
       for (int u = 0; u < NU; ++u) {
         const int r = wrow0 + 4 * u + my_row;
-        attn_issue_rows(kseq, vseq, row_id(r, tb, cbase, e_last) * 256u, r, l16,
+        attn_issue_rows(kseq, vseq, rid[u] * 256u, r, l16,
                         k_lds0 + buf * BUF_BYTES + u * 1024, v_lds0 + buf * BUF_BYTES + u * 1024);
       }
     }
@@ -962,32 +971,27 @@ __global__ __launch_bounds__(AT_NT) void attn_persist_kernel(AttnBatch ab, AttnP
   constexpr uint32_t BUF_BYTES = ST * 256;
   constexpr int64_t ROW_BYTES = KV ? KV8_ROW_BYTES : HD * 2;
 
-  bf16x8 qf[4], qn0[4], qn1[4];
+  bf16x8 qf[4], qn[4];
   f32x4 o[8];
 #pragma unroll
   for (int db = 0; db < 8; ++db) o[db] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m_run = -INFINITY, l_run = 0.f;
   int cur = -1;     // item being accumulated
   int nseg = 0;     // items started in this run
-  int nq = 0;       // queries prefetched
   float scale_log2 = 0.f;
 
-  auto load_q = [&](int item) __attribute__((always_inline)) {
+  // this wave's query slice (16 heads) of item `item`; a row of -1 (no such query)
+  // reads row 0, never used
+  auto load_q = [&](bf16x8 (&dst)[4], int item) __attribute__((always_inline)) {
     const AttnArgs& a = ab.a[(item / HB) / R0];
     const int head = (item % HB) * 64 + w * 16 + l16;
-    const i32x4* qp = reinterpret_cast<const i32x4*>(a.q + ((int64_t)s_item[item].w * a.heads + head) * HD);
-    if (nq & 1) {
+    const int64_t qrow = max(s_item[item].w, 0);
+    const i32x4* qp = reinterpret_cast<const i32x4*>(a.q + (qrow * a.heads + head) * HD);
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) qn1[ks] = __builtin_bit_cast(bf16x8, qp[ks * 4 + g]);
-    } else {
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) qn0[ks] = __builtin_bit_cast(bf16x8, qp[ks * 4 + g]);
-    }
-    ++nq;
+    for (int ks = 0; ks < 4; ++ks) dst[ks] = __builtin_bit_cast(bf16x8, qp[ks * 4 + g]);
   };
   // DMA of global stage js into buffer buf (nothing for an empty item); returns
-  // whether anything was issued.  The first stage of an item in this run also
-  // prefetches the item's query.  Stages are issued in order, so the item is
+  // whether anything was issued.  Stages are issued in order, so the item is
   // tracked, and its sequence pointers are kept, instead of looked up per stage.
   int iss_item = ps_item_of(s_pre, W, s0);
   int iss_pre = s_pre[iss_item], iss_next = s_pre[iss_item + 1];
@@ -1007,7 +1011,6 @@ __global__ __launch_bounds__(AT_NT) void attn_persist_kernel(AttnBatch ab, AttnP
       iss_v = reinterpret_cast<const char*>(iss_a->vc) + (int64_t)iss_it.y * ROW_BYTES;
       iss_sparse = iss_a->idx != nullptr;
     }
-    if (js == iss_pre || js == s0) load_q(iss_item);
     if (iss_it.x <= 0) return false;
     const int tb = (js - iss_pre) * ST;
     const int e_last = iss_it.x - 1;
@@ -1017,23 +1020,32 @@ __global__ __launch_bounds__(AT_NT) void attn_persist_kernel(AttnBatch ab, AttnP
       return (uint32_t)min(max(id, 0), iss_it.z - 1);
     };
     if constexpr (KV) {   // as in attn_dma_kernel: FP8 halves, then two runs of bf16 halves
-      const uint32_t off = row_id(wrow0 + (lane >> 2)) * KV8_ROW_BYTES + (uint32_t)(lane & 3) * 16u;
+      const uint32_t rid0 = row_id(wrow0 + (lane >> 2));   // row ids first (see below)
+      uint32_t rid[2];
+#pragma unroll
+      for (int u = 0; u < 2; ++u) rid[u] = row_id(wrow0 + 8 * u + (lane >> 3));
+      const uint32_t off = rid0 * KV8_ROW_BYTES + (uint32_t)(lane & 3) * 16u;
       dma16(iss_k, off, k_lds0 + buf * (ST * 64));
       dma16(iss_v, off, v_lds0 + buf * (ST * 64));
       const uint32_t khi0 = lds_addr(&sm.khi[buf][0]), vhi0 = lds_addr(&sm.vhi[buf][0]);
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
         const int r = wrow0 + 8 * u + (lane >> 3);
-        const uint32_t base = row_id(r) * KV8_ROW_BYTES + 64u;
+        const uint32_t base = rid[u] * KV8_ROW_BYTES + 64u;
         const int sl = lane & 7;
         dma16(iss_k, base + kv8_kslot(r, sl) * 16u, khi0 + (uint32_t)(wrow0 + 8 * u) * 128u);
         dma16(iss_v, base + kv8_vslot(r, sl) * 16u, vhi0 + (uint32_t)(wrow0 + 8 * u) * 128u);
       }
     } else {
+      // every row id first (LDS reads, one wait), then the DMAs: the DMA's inline
+      // assembly clobbers memory, so a read placed after one would wait on its own
+      uint32_t rid[NU];
+#pragma unroll
+      for (int u = 0; u < NU; ++u) rid[u] = row_id(wrow0 + 4 * u + my_row);
 #pragma unroll
       for (int u = 0; u < NU; ++u) {
         const int r = wrow0 + 4 * u + my_row;
-        attn_issue_rows(iss_k, iss_v, row_id(r) * 256u, r, l16,
+        attn_issue_rows(iss_k, iss_v, rid[u] * 256u, r, l16,
                         k_lds0 + buf * BUF_BYTES + u * 1024, v_lds0 + buf * BUF_BYTES + u * 1024);
       }
     }
@@ -1070,23 +1082,32 @@ __global__ __launch_bounds__(AT_NT) void attn_persist_kernel(AttnBatch ab, AttnP
   };
 
   int cmp_item = iss_item, cmp_pre = iss_pre, cmp_next = iss_next, cmp_n = 0;
+  // The query of the run's first item; each later item's query is loaded one stage
+  // ahead into qn (see the stage loop).  A load is waited for only where it is used.
+  load_q(qf, iss_item);
   for (int c0 = s0; c0 < s1; c0 += ATTN_PS_MAX_RUN) {
     const int c1 = min(c0 + ATTN_PS_MAX_RUN, s1);
     const int nst = c1 - c0;
-    // entry ids of the sparse stages of this part of the run (nothing is in flight)
+    // entry ids of the sparse stages of this part of the run: thread t takes entries
+    // t % ST of stages c0 + t / ST + (AT_NT / ST) u; their items follow from one search
+    // and a walk forward; every load is issued before the first is used
     {
+      static_assert(AT_NT % ST == 0, "a thread keeps its place within the stages");
+      constexpr int SPU = AT_NT / ST;   // stages per round of AT_NT ids
       int v[AT_IDS / AT_NT];
+      int js = c0 + t / ST;
+      int item = ps_item_of(s_pre, W, min(js, c1 - 1));
 #pragma unroll
-      for (int u = 0; u < AT_IDS / AT_NT; ++u) {
-        const int f = t + AT_NT * u;
-        const int js = c0 + f / ST;
-        v[u] = 0;
-        if (js < c1) {
-          const int item = ps_item_of(s_pre, W, js);
-          const AttnArgs& a = ab.a[(item / HB) / R0];
-          const int e = (js - s_pre[item]) * ST + f % ST;
-          if (a.idx && e < s_item[item].x) v[u] = a.idx[(int64_t)s_item[item].w * a.k + e];
-        }
+      for (int u = 0; u < AT_IDS / AT_NT; ++u, js += SPU) {
+        while (item + 1 < W && s_pre[item + 1] <= js) ++item;
+        const AttnArgs& a = ab.a[(item / HB) / R0];
+        const int e = (js - s_pre[item]) * ST + t % ST;
+        const bool ok = js < c1 && a.idx != nullptr && e < s_item[item].x;
+        // an address that is always valid (the plan, in the workspace), so the load
+        // can be issued unconditionally; the value of a slot without an entry is 0
+        const int* src = ok ? a.idx + (int64_t)s_item[item].w * a.k + e : pp.plan;
+        const int x = *src;
+        v[u] = ok ? x : 0;
       }
       __syncthreads();   // the previous part's ids are no longer read
 #pragma unroll
@@ -1109,11 +1130,13 @@ __global__ __launch_bounds__(AT_NT) void attn_persist_kernel(AttnBatch ab, AttnP
       }
       const int item = cmp_item;
       if (item != cur) {
-        if (cur >= 0) finish(cur);
-        // the query prefetched when this item's first stage was issued
-        const bool odd = (nseg & 1) != 0;
+        if (cur >= 0) {
+          finish(cur);
+          // qn holds this item's query: loaded at the previous stage, before the DMAs
+          // of the stage after this one, which the wait above left in flight
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) qf[ks] = odd ? qn1[ks] : qn0[ks];
+          for (int ks = 0; ks < 4; ++ks) qf[ks] = qn[ks];
+        }
 #pragma unroll
         for (int db = 0; db < 8; ++db) o[db] = f32x4{0.f, 0.f, 0.f, 0.f};
         m_run = -INFINITY;
@@ -1122,6 +1145,16 @@ __global__ __launch_bounds__(AT_NT) void attn_persist_kernel(AttnBatch ab, AttnP
         cmp_n = s_item[item].x;
         cur = item;
         ++nseg;
+      }
+      {   // the query of the next stage's item (always loaded: a conditional load would be
+          // merged into a select that waits for it)
+        int nit = cmp_item, nnext = cmp_next;
+        const int jn = min(js + 1, s1 - 1);
+        while (jn >= nnext) {
+          ++nit;
+          nnext = s_pre[nit + 1];
+        }
+        load_q(qn, nit);
       }
       if constexpr (KV) {
         // the stage's FP8 halves to bf16 (stale rows of an empty item's stage are harmless)

@@ -59,7 +59,7 @@
 extern "C" {
 #endif
 
-#define LCA_ABI_VERSION 7
+#define LCA_ABI_VERSION 8
 
 enum lca_status {
   LCA_OK = 0,
@@ -170,7 +170,7 @@ int32_t lca_csa_index_score_fp4(const uint8_t* q_fp4, const int64_t* q_off, cons
  * Page section 3-2 items 2 and 4 (indexer scores, then a sparse top-k).
  *
  * Decode-sized batches (max_q < 16 query rows per sequence) take the candidate
- * path and need a workspace: one work-group per 1024 entries of a row scores them
+ * path and need a workspace: one work-group per 2048 entries of a row scores them
  * in LDS and keeps the chunk's top coarse bins (about twice its expected share of
  * the top-k, in index order); one work-group per row then selects the top-k from
  * the candidates, exactly.  When a chunk held more than its share at or above the
@@ -189,8 +189,10 @@ int32_t lca_csa_index_score_fp4(const uint8_t* q_fp4, const int64_t* q_off, cons
  *            then -1 padding.    count [rows] int32 out: min(k, n_vis[r]).
  *   n_vis    [rows] int32 out, or NULL: min(floor(q_pos[r] / c), N_b).
  *   ws       workspace of lca_csa_index_select_workspace_bytes(batch, max_q,
- *            max_entries, k) bytes (0 for prefill-sized batches: ws may be NULL);
- *            zero-filled before first use, returned to zero by every call.
+ *            max_entries, k) bytes (0 for prefill-sized batches: ws may be NULL),
+ *            16-byte aligned; its contents on entry do not matter (every call
+ *            writes whatever it reads back), so calls sharing one ws must not
+ *            overlap in time.
  *   Decode-sized batches: max_entries <= 4,194,304 (else LCA_ERR_UNSUPPORTED).
  * ------------------------------------------------------------------------- */
 size_t lca_csa_index_select_workspace_bytes(int32_t batch, int32_t max_q, int32_t max_entries,
@@ -214,6 +216,29 @@ int32_t lca_csa_index_select_fp4(const uint8_t* q_fp4, const int64_t* q_off, con
                                  int32_t max_q, int32_t max_entries, int32_t d_idx, int32_t c,
                                  int32_t k, int32_t* idx, int32_t* count, int32_t* n_vis,
                                  void* ws, size_t ws_bytes, void* stream);
+
+/* csa_index_select_noalloc — lca_csa_index_select for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc): the same arguments without ws / ws_bytes and the same result.
+ * The workspace of the decode-sized form is a device array inside the library of
+ * LCA_INDEX_SELECT_SCRATCH_BYTES bytes, one per GPU, held until the process ends;
+ * the first call on a GPU looks up that GPU's copy (hipGetSymbolAddress), so make
+ * it before any capture.  The call allocates nothing.
+ *   Errors: as lca_csa_index_select, and LCA_ERR_WORKSPACE when the batch needs
+ *   more than LCA_INDEX_SELECT_SCRATCH_BYTES, i.e. when
+ *   lca_csa_index_select_workspace_bytes(batch, max_q, max_entries, k) exceeds it
+ *   (8 MiB holds 26 rows of 4,194,304 entries, or 227 rows of 262,144, at k 2048).
+ *   Every call on one GPU uses that GPU's one array: calls that overlap in time on
+ *   one GPU (two streams, or two threads) race and give undefined results.  Nothing
+ *   in it needs clearing between calls.
+ */
+#define LCA_INDEX_SELECT_SCRATCH_BYTES ((size_t)8 << 20)
+int32_t lca_csa_index_select_noalloc(const int8_t* q_idx, const int64_t* q_off,
+                                     const int64_t* q_pos, const int8_t* k_idx,
+                                     const int64_t* ent_off, int32_t batch, int32_t max_q,
+                                     int32_t max_entries, int32_t d_idx, int32_t c, int32_t k,
+                                     int32_t* idx, int32_t* count, int32_t* n_vis,
+                                     void* stream);
 
 /* ---------------------------------------------------------------------------
  * csa_topk_select — per row, the top min(k, n_vis[r]) entries of

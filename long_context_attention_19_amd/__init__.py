@@ -59,6 +59,8 @@ _SIGS = {
                                     _vp, _vp, _vp, _vp, _sz, _vp]),
     "lca_csa_index_select_fp4": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
                                         _i32, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "lca_csa_index_select_noalloc": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32,
+                                            _i32, _i32, _vp, _vp, _vp, _vp]),
     "lca_window_attn": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
                                _f32, _vp, _vp, _vp]),
     "lca_attn_sink": (_i32, [_vp, _vp, _vp, _i64, _i32, _i32, _vp]),
@@ -180,6 +182,14 @@ def csa_index_select(q_idx, q_off, q_pos, k_idx, ent_off, batch, max_q, max_entr
     _check("lca_csa_index_select", _lib.lca_csa_index_select(
         _p(q_idx), _p(q_off), _p(q_pos), _p(k_idx), _p(ent_off), batch, max_q, max_entries,
         q_idx.shape[-1], c, k, _p(idx), _p(count), _p(n_vis), _p(ws), _nb(ws), _s(stream)))
+
+
+def csa_index_select_noalloc(q_idx, q_off, q_pos, k_idx, ent_off, batch, max_q, max_entries, c,
+                             k, idx, count, n_vis=None, stream=None):
+    """csa_index_select with the library's own per-device scratch as its workspace."""
+    _check("lca_csa_index_select_noalloc", _lib.lca_csa_index_select_noalloc(
+        _p(q_idx), _p(q_off), _p(q_pos), _p(k_idx), _p(ent_off), batch, max_q, max_entries,
+        q_idx.shape[-1], c, k, _p(idx), _p(count), _p(n_vis), _s(stream)))
 
 
 def csa_index_select_fp4(q_fp4, q_off, q_pos, k_fp4, ent_off, batch, max_q, max_entries, c, k,

@@ -269,8 +269,11 @@ static int32_t index_select_impl(const int8_t* q_idx, const int64_t* q_off, cons
                                  const int8_t* k_idx, const int64_t* ent_off, int32_t batch,
                                  int32_t max_q, int32_t max_entries, int32_t d_idx, int32_t c,
                                  int32_t k, int32_t* idx, int32_t* count, int32_t* n_vis,
-                                 void* ws, size_t ws_bytes, void* stream, bool fp4) {
-  const char* name = fp4 ? "csa_index_select_fp4" : "csa_index_select";
+                                 void* ws, size_t ws_bytes, void* stream, bool fp4,
+                                 bool noalloc = false) {
+  const char* name = noalloc ? "csa_index_select_noalloc"
+                     : fp4   ? "csa_index_select_fp4"
+                             : "csa_index_select";
   if (d_idx != 64) return fail(LCA_ERR_UNSUPPORTED, "%s: d_idx=%d (only 64)", name, d_idx);
   if (batch < 0 || max_q < 0 || max_entries < 0) return fail(LCA_ERR_SHAPE, "%s: negative size", name);
   if (c < 1) return fail(LCA_ERR_SHAPE, "%s: ratio c=%d < 1", name, c);
@@ -289,6 +292,12 @@ static int32_t index_select_impl(const int8_t* q_idx, const int64_t* q_off, cons
   if ((int64_t)max_entries > (int64_t)lca::DS_MAX_CHUNKS * lca::DS_CHUNK) return fail(LCA_ERR_UNSUPPORTED, "%s: max_entries=%d above %d", name, max_entries, lca::DS_MAX_CHUNKS * lca::DS_CHUNK);
   const int rows = batch * max_q;
   const size_t need = lca::ds_ws_bytes(rows, max_entries, k);
+  if (noalloc) {
+    if (need > lca::DS_SCRATCH_BYTES) return fail(LCA_ERR_WORKSPACE, "%s: the batch needs %zu bytes of workspace, above the %zu-byte scratch", name, need, lca::DS_SCRATCH_BYTES);
+    const hipError_t e = lca::ds_scratch(&ws);
+    if (e != hipSuccess) return hip_status(e, name);
+    ws_bytes = lca::DS_SCRATCH_BYTES;
+  }
   if (!ws || ws_bytes < need) return fail(LCA_ERR_WORKSPACE, "%s: ws_bytes %zu < %zu", name, ws_bytes, need);
   if (!al16(ws)) return fail(LCA_ERR_ALIGN, "%s: ws not 16-byte aligned", name);
   lca::DsBatch db{};
@@ -320,6 +329,17 @@ int32_t lca_csa_index_select(const int8_t* q_idx, const int64_t* q_off, const in
                              size_t ws_bytes, void* stream) {
   return index_select_impl(q_idx, q_off, q_pos, k_idx, ent_off, batch, max_q, max_entries, d_idx,
                            c, k, idx, count, n_vis, ws, ws_bytes, stream, false);
+}
+
+int32_t lca_csa_index_select_noalloc(const int8_t* q_idx, const int64_t* q_off,
+                                     const int64_t* q_pos, const int8_t* k_idx,
+                                     const int64_t* ent_off, int32_t batch, int32_t max_q,
+                                     int32_t max_entries, int32_t d_idx, int32_t c, int32_t k,
+                                     int32_t* idx, int32_t* count, int32_t* n_vis,
+                                     void* stream) {
+  static_assert(LCA_INDEX_SELECT_SCRATCH_BYTES == lca::DS_SCRATCH_BYTES, "scratch size");
+  return index_select_impl(q_idx, q_off, q_pos, k_idx, ent_off, batch, max_q, max_entries, d_idx,
+                           c, k, idx, count, n_vis, nullptr, 0, stream, false, true);
 }
 
 int32_t lca_csa_index_select_fp4(const uint8_t* q_fp4, const int64_t* q_off, const int64_t* q_pos,

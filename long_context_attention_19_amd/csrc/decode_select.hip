@@ -44,6 +44,7 @@
 // not depend on the other rows of the batch.  Nothing in the workspace carries over
 // between calls.
 #include <algorithm>
+#include <atomic>
 
 #include "lca_device.h"
 #include "lca_internal.h"
@@ -618,6 +619,30 @@ hipError_t launch_ds_select(const DsBatch& db, int batch, hipStream_t st) {
   if (db.fp4) hipLaunchKernelGGL(ds_select_kernel<true>, grid, dim3(DI_NT), 0, st, db);
   else hipLaunchKernelGGL(ds_select_kernel<false>, grid, dim3(DI_NT), 0, st, db);
   return hipGetLastError();
+}
+
+// The workspace of the allocation-free selection.  In host code `scratch` names a
+// host-side stand-in, never the device copy: host code uses only the address that
+// hipGetSymbolAddress gives for the current device.
+static __device__ __align__(256) uint8_t scratch[DS_SCRATCH_BYTES];
+
+constexpr int DS_MAX_DEVICES = 64;
+
+hipError_t ds_scratch(void** ptr) {
+  static std::atomic<void*> addr[DS_MAX_DEVICES];
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= DS_MAX_DEVICES) return hipErrorInvalidDevice;
+  void* p = addr[dev].load(std::memory_order_acquire);
+  if (!p) {   // two threads may both look it up: they find the same address
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    addr[dev].store(p, std::memory_order_release);
+  }
+  *ptr = p;
+  return hipSuccess;
 }
 
 }  // namespace lca

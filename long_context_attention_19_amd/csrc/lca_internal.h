@@ -131,6 +131,11 @@ size_t ds_ws_bytes(int rows, int max_n, int k);
 void ds_ws_carve(void* ws, int rows, int max_n, int k, DsLayer& L);
 hipError_t launch_ds_chunks(const DsBatch& db, int batch, hipStream_t st);   // candidates
 hipError_t launch_ds_select(const DsBatch& db, int batch, hipStream_t st);   // the top-k
+// The allocation-free form's workspace: a device array of DS_SCRATCH_BYTES, one copy
+// per device.  ds_scratch returns the current device's copy (looked up on the first
+// call on that device).
+constexpr size_t DS_SCRATCH_BYTES = (size_t)8 << 20;
+hipError_t ds_scratch(void** ptr);
 
 // ------------------------------------------------------------ top-k
 struct TopkWs {

@@ -30,7 +30,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_version_and_struct_layout():
-    assert lca.abi_version() == 7
+    assert lca.abi_version() == 8
     # 4 int32, 10 pointers, 4 window pointers, int32 window (+4 padding), sink pointer,
     # int32 idx_format, int32 kv_format
     assert ctypes.sizeof(lca.LcaLayer) == 16 + 10 * 8 + 4 * 8 + 8 + 8 + 8
@@ -83,6 +83,30 @@ def test_index_select_validation(fn):
     bad[15] = need; bad[14] = MIS
     assert f(*bad) == E_ALIGN
     bad = list(args); bad[6] = 8; bad[7] = 2048 * 2048 + 1; bad[14] = FAKE; bad[15] = 1 << 40
+    assert f(*bad) == E_UNSUP                          # beyond 4M entries per row
+
+
+def test_index_select_noalloc_validation():
+    """The allocation-free form rejects, before any HIP call, a batch whose workspace
+    exceeds its fixed scratch; other argument errors are those of the workspace form."""
+    f = L().lca_csa_index_select_noalloc
+    cap = 8 << 20
+    # q, q_off, q_pos, k, ent_off, batch, max_q, max_entries, d_idx, c, k, idx, count, n_vis,
+    # stream
+    args = [FAKE] * 5 + [2, 8, 1000, 64, 4, 256, FAKE, FAKE, None, None]
+    bad = list(args); bad[8] = 32
+    assert f(*bad) == E_UNSUP
+    bad = list(args); bad[3] = None
+    assert f(*bad) == E_NULL
+    bad = list(args); bad[5] = 0
+    assert f(*bad) == OK
+    # 26 rows of 4M entries fit the 8 MiB scratch, 27 do not
+    ws = L().lca_csa_index_select_workspace_bytes
+    assert ws(26, 1, 1 << 22, 2048) <= cap < ws(27, 1, 1 << 22, 2048)
+    bad = list(args); bad[5] = 27; bad[6] = 1; bad[7] = 1 << 22; bad[10] = 2048
+    assert f(*bad) == E_WS
+    assert "scratch" in lca.last_error()
+    bad[7] = (1 << 22) + 1
     assert f(*bad) == E_UNSUP                          # beyond 4M entries per row
 
 

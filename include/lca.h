@@ -46,8 +46,15 @@
  *             clear them), so one zeroed workspace serves any number of calls in
  *             stream order.  Calls that share a workspace must not run
  *             concurrently.  lca_workspace_reset() re-zeroes one on a stream.
- *   Determinism. For a given launch shape every output is bitwise reproducible:
- *             no result depends on the order in which work-groups finish.
+ *   Determinism. Every output is bitwise reproducible: no result depends on the
+ *             order in which work-groups finish.  Batch invariance: a query row's
+ *             result depends only on its own inputs and on the size arguments that
+ *             fix how a row is cut into pieces (the single-layer attention calls:
+ *             splits with k or max_entries; lca_hybrid_layer_step: the layer and
+ *             query counts), never on the other rows of the batch.  So a sequence
+ *             gives the same bits alone or inside any batch of the hybrid step,
+ *             and inside any batch of a single call made with the same splits and
+ *             bound.
  */
 #ifndef LCA_H
 #define LCA_H
@@ -378,10 +385,12 @@ int32_t lca_attn_sink(lca_bf16* out, float* lse, const float* sink, int64_t rows
  * layer, CSA and HCA in the same launches (up to 8 layers each), followed by the
  * sliding-window branch of every layer that has one (window > 0).  A layer's sink
  * (sink != NULL, as lca_attn_sink) is folded in by the kernel that writes the
- * layer's final result, after the window branch.  The attention
- * takes a balanced persistent form when the step fits it (64-head blocks, at most
- * 256 (layer, row) items); otherwise with L layers it uses 32 / min(L, 4) splits
- * per row, a function of the layer count only.
+ * layer's final result, after the window branch.  The attention cuts every
+ * row, CSA or HCA, into pieces of P entries, one work-group each, merged in
+ * piece order: P = 2048 / s rounded up to a multiple of 64, s = max(1, S / min(2L,
+ * 32)) for L layers, where S = 32 for one query row per sequence, 32 / max_q for
+ * up to 31 and 1 from 32 (8 layers of decode: P = 1024).  P depends on L and
+ * max_q only, so the step is batch invariant (see Determinism).
  * ------------------------------------------------------------------------- */
 enum lca_layer_kind { LCA_LAYER_CSA = 0, LCA_LAYER_HCA = 1 };
 enum lca_idx_format { LCA_IDX_INT8 = 0, LCA_IDX_FP4 = 1 };

@@ -74,19 +74,35 @@ HybridTiming* hybrid_timing() {
   return &ht;
 }
 
-// Split count of the hybrid step's attention (the per-row form): the layers of one
-// launch share the chip, so each row needs fewer work-groups, and fewer splits mean
-// fewer partials.  It depends on the layer and query counts only, never on the batch.
-constexpr int kHybridLayerShare = 4;
+// Piece size of the hybrid step's attention: a row's entries are cut into pieces of
+// this many entries (one work-group each), merged in piece order.  It depends on the
+// step's layer and query counts only, never on the batch, the layer's kind or the
+// cache lengths, so a sequence's result is the same alone or inside any batch.  The
+// layers of one launch share the chip, so with more layers a row takes fewer, longer
+// pieces (fewer partials): kPieceRefEntries / splits entries, splits = the per-row
+// split count of a single layer divided by kLayerWeight per layer.
+constexpr int kLayerWeight = 2;
+constexpr int kPieceRefEntries = 2048;
 int hybrid_splits(int n_layers, int max_q) {
   const int base = lca::attn_auto_splits(max_q);
-  const int conc = std::min(std::max(n_layers, 1), kHybridLayerShare);
+  const int conc = std::min(std::max(n_layers, 1) * kLayerWeight, 32);
   return std::max(1, base / conc);
+}
+int hybrid_piece(int n_layers, int max_q) {
+  const int sp = hybrid_splits(n_layers, max_q);
+  const int want = (kPieceRefEntries + sp - 1) / sp;
+  return std::max(64, (want + 63) / 64 * 64);   // a multiple of every stage size
+}
+// Pieces of the layer's longest row (its bound: top-k, or max_entries): the grid and the
+// partial workspace.
+int hybrid_layer_splits(const lca_layer& L, int piece) {
+  const int bound = L.kind == LCA_LAYER_CSA ? std::max(L.topk, 1) : std::max(L.max_entries, 1);
+  return std::max(1, (bound + piece - 1) / piece);
 }
 
 // Attention launches of the hybrid step: up to 8 layers each, one row format per
-// launch, HCA layers first (their rows are the longest, for the per-row form).  The
-// plan below and the step both take the launches from here.
+// launch, HCA layers first (their rows hold the most pieces, so their work-groups are
+// dispatched first).
 std::vector<std::vector<int>> attn_groups(const lca_layer* layers, int n_layers) {
   std::vector<int> order;
   for (int kind : {LCA_LAYER_HCA, LCA_LAYER_CSA})
@@ -106,47 +122,6 @@ std::vector<std::vector<int>> attn_groups(const lca_layer* layers, int n_layers)
     if (!cur.empty()) groups.push_back(cur);
   }
   return groups;
-}
-
-// The hybrid step's attention takes the balanced persistent form when every one of
-// its launches fits it (64-head blocks, at most ATTN_PS_MAX_ITEMS items, and entry
-// bounds that keep the runs short); one partial region serves all launches, which
-// run one after another on the caller's stream.
-struct HybridAttnPlan {
-  bool persist = false;
-  int G = 0;        // persistent work-groups: two per compute unit
-  int items = 0;    // largest launch
-};
-// Fewer items than this leave most persistent work-groups a sliver of one item, and the
-// combine then merges ~G / items partials per item in dependent rounds: the per-row
-// split form is faster there (4 items: 12 + 42 us persistent against 8 + 5 us).
-constexpr int kPersistMinItems = 32;
-
-HybridAttnPlan hybrid_attn_plan(const lca_layer* layers, int n_layers, int rows, int heads) {
-  HybridAttnPlan p;
-  if (heads % 64 != 0 || rows <= 0) return p;
-  if ((int64_t)n_layers * rows * (heads / 64) < kPersistMinItems) return p;
-  const int cu = lca_device_cu_count();
-  if (cu <= 0) return p;
-  const int G = 2 * cu;
-  const int hb = heads / 64;
-  int items_max = 0;
-  for (const std::vector<int>& grp : attn_groups(layers, n_layers)) {
-    const int64_t items = (int64_t)grp.size() * rows * hb;
-    if (items > lca::ATTN_PS_MAX_ITEMS) return p;
-    int64_t stages = 0;
-    for (int l : grp) {
-      const int max_n = layers[l].kind == LCA_LAYER_CSA ? layers[l].topk : layers[l].max_entries;
-      stages += (int64_t)rows * hb *
-                std::max(1, (std::max(max_n, 0) + lca::ATTN_PS_STAGE - 1) / lca::ATTN_PS_STAGE);
-    }
-    if (stages > (int64_t)lca::ATTN_PS_MAX_RUN * G) return p;
-    items_max = std::max(items_max, (int)items);
-  }
-  p.persist = true;
-  p.G = G;
-  p.items = items_max;
-  return p;
 }
 
 size_t csa_layer_bytes(int rows, int max_entries, int topk, int heads, int splits) {
@@ -579,17 +554,15 @@ size_t lca_hybrid_workspace_bytes(const lca_layer* layers, int32_t n_layers, int
                                   int32_t max_q, int32_t heads) {
   if (!layers || n_layers <= 0 || batch <= 0 || max_q <= 0 || heads <= 0) return 0;
   const int rows = batch * max_q;
-  const HybridAttnPlan plan = hybrid_attn_plan(layers, n_layers, rows, heads);
-  const int sp = plan.persist ? 1 : hybrid_splits(n_layers, max_q);
   size_t b = 0;
   for (int l = 0; l < n_layers; ++l) {
+    const int sp = hybrid_layer_splits(layers[l], hybrid_piece(n_layers, max_q));
     if (layers[l].kind == LCA_LAYER_CSA)
       b += csa_layer_bytes(rows, std::max(layers[l].max_entries, 0), std::max(layers[l].topk, 1),
                            heads, sp);
     else
       b += lca::attn_ws_bytes(rows, heads, sp);
   }
-  if (plan.persist) b += lca::attn_persist_ws_bytes(plan.G, plan.items);
   return b;
 }
 
@@ -631,8 +604,6 @@ int32_t lca_hybrid_layer_step(const lca_layer* layers, int32_t n_layers, const i
   if (!std::isfinite(scale)) return fail(LCA_ERR_SHAPE, "hybrid_layer_step: scale not finite");
   const hipStream_t caller = (hipStream_t)stream;
   const int rows = batch * max_q;
-  const HybridAttnPlan plan = hybrid_attn_plan(layers, n_layers, rows, heads);
-  const int sp = plan.persist ? 1 : hybrid_splits(n_layers, max_q);
   const float scale_log2 = scale * 1.4426950408889634f;
 
   // carve each layer's workspace region (layer order, as lca_hybrid_workspace_bytes sizes it)
@@ -643,6 +614,8 @@ int32_t lca_hybrid_layer_step(const lca_layer* layers, int32_t n_layers, const i
   char* p = reinterpret_cast<char*>(ws);
   for (int l = 0; l < n_layers; ++l) {
     const lca_layer& L = layers[l];
+    const int piece = hybrid_piece(n_layers, max_q);
+    const int sp = hybrid_layer_splits(L, piece);
     lca::AttnArgs a{};
     a.q = L.q;
     a.kc = L.k_cmp;
@@ -674,7 +647,7 @@ int32_t lca_hybrid_layer_step(const lca_layer* layers, int32_t n_layers, const i
       a.idx = L.idx;
       a.count = L.count;
       a.k = L.topk;
-      a.max_n = L.topk;
+      a.max_n = piece * sp;   // every row's piece: ceil(max_n / splits) = piece
       a.ratio = 1;
       lca::attn_ws_carve(p, rows, heads, sp, a);
       p += lca::attn_ws_bytes(rows, heads, sp);
@@ -682,7 +655,7 @@ int32_t lca_hybrid_layer_step(const lca_layer* layers, int32_t n_layers, const i
     } else {
       a.q_pos = q_pos;
       a.ratio = L.ratio;
-      a.max_n = L.max_entries;
+      a.max_n = piece * sp;
       lca::attn_ws_carve(p, rows, heads, sp, a);
       p += lca::attn_ws_bytes(rows, heads, sp);
     }
@@ -737,19 +710,13 @@ int32_t lca_hybrid_layer_step(const lca_layer* layers, int32_t n_layers, const i
     if (first) mark(2);
   }
   mark(3);
-  lca::AttnPersist pp{};
-  if (plan.persist) {
-    lca::attn_persist_carve(p, plan.G, plan.items, pp);
-    pp.rows = rows;
-  }
   for (const std::vector<int>& grp : attn_groups(layers, n_layers)) {
     if (e != hipSuccess) break;
     lca::AttnBatch ab{};
     ab.n = (int)grp.size();
     ab.head_blocks = hb;
     for (int i = 0; i < ab.n; ++i) ab.a[i] = args[grp[i]];
-    e = plan.persist ? lca::launch_attention_persist(ab, pp, caller)
-                     : lca::launch_attention(ab, batch, caller);
+    e = lca::launch_attention(ab, batch, caller);
   }
   // sliding-window branches, merged into each layer's result (one launch per 8 layers)
   std::vector<lca::AttnArgs> win_a;

@@ -451,7 +451,15 @@ __device__ __forceinline__ void attn_issue_rows(const char* kseq, const char* vs
 // bf16 in LDS by the whole work-group before the waves use the stage.
 template <int ES, int SUB, int NB, int MODE, int KV>
 __global__ __launch_bounds__(AT_NT) void attn_dma_kernel(AttnBatch ab) {
-  const AttnArgs& a = ab.a[blockIdx.z / ab.head_blocks];   // grid z = layer x head block
+  // grid x = item (query row slot, then layer x head block), padded to an odd count;
+  // grid y = piece.  Consecutive work-groups go to the XCDs in turn, so with an odd
+  // item count the pieces of one item land on different XCDs, and the work-groups of
+  // the first pieces (present in every row) are dispatched before the later ones.
+  const int item = blockIdx.x;
+  if (item >= ab.items) return;
+  const int lz = item / ab.rows_grid;            // layer x head block
+  const int gy = item - lz * ab.rows_grid;       // query row slot
+  const AttnArgs& a = ab.a[lz / ab.head_blocks];
   const bool sparse = MODE == 2 ? a.idx != nullptr : MODE == 1;   // uniform
   constexpr int ST = 32 * ES * SUB;             // entries per super-tile (stage)
   constexpr int HG = 4 / ES;                    // head groups of 16 per work-group
@@ -469,15 +477,15 @@ __global__ __launch_bounds__(AT_NT) void attn_dma_kernel(AttnBatch ab) {
   // the first entry ids and the first stages' rows are issued as soon as their
   // addresses are known, before the row's entry count (and so the exact end of the
   // piece) is back.  Rows past the end are read but masked in the softmax.
-  const int b = blockIdx.y / a.max_q;
-  const int qi = blockIdx.y - b * a.max_q;
+  const int b = gy / a.max_q;
+  const int qi = gy - b * a.max_q;
   const int64_t r0 = a.q_off[b];
   const int64_t nq = a.q_off[b + 1] - r0;
   int64_t e_base = a.ent_off[b];
   int64_t n_seq = a.ent_off[b + 1] - e_base;
   if (qi >= nq) return;
   const int64_t row = r0 + qi;
-  const int s = blockIdx.x;
+  const int s = blockIdx.y;
   // the row's entry count: only needed after the first DMAs are issued
   int n_raw = sparse ? a.count[row] : (int)min(a.q_pos[row] / a.ratio, (int64_t)INT32_MAX);
   if (MODE == 0 && a.win_pos0 != nullptr) {
@@ -493,7 +501,7 @@ __global__ __launch_bounds__(AT_NT) void attn_dma_kernel(AttnBatch ab) {
   const int max_n = a.max_n;
   const int splits = a.splits;
   const int kk = a.k;
-  const int h0 = (blockIdx.z % ab.head_blocks) * 64;
+  const int h0 = (lz % ab.head_blocks) * 64;
   const int t = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(t >> 6);
   const int lane = t & 63;
@@ -866,407 +874,6 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnBatch ab, int sta
   if (a.lse && dg == 0) a.lse[ri.row * a.heads + head] = lse_v;
 }
 
-// ---------------------------------------------------------------------------------
-// Balanced persistent form, for decode over a batch of layers (64-head blocks).
-// An item is (layer, row, 64-head block) with n entries; it takes max(1, ceil(n / 64))
-// stages (an empty item still takes one, to write its zero output).  The stages of
-// all items are laid end to end, S in total, and work-group g of G streams the run
-// [g*S/G, (g+1)*S/G) as one pipeline that crosses item boundaries.  An item that
-// lies wholly inside a run gets its output there; any other item leaves a partial
-// (O, max, sum) in slot 2g (the run's first item) or 2g + 1 (its last item), and the
-// persistent combine merges an item's partials in work-group order.  The split of an
-// item therefore depends on every item's length, unlike the per-row pieces above.
-__device__ __forceinline__ int ps_run_start(int g, int S, int G) {
-  return (int)((int64_t)g * S / G);
-}
-__device__ __forceinline__ int ps_group_of(int p, int S, int G) {   // run holding stage p
-  int g = (int)((int64_t)p * G / S);
-  while (g + 1 < G && ps_run_start(g + 1, S, G) <= p) ++g;
-  while (g > 0 && ps_run_start(g, S, G) > p) --g;
-  return g;
-}
-// last item whose first stage is <= j (items without stages share their successor's
-// offset, so the search lands on the item that owns stage j)
-__device__ __forceinline__ int ps_item_of(const int* pre, int W, int j) {
-  int lo = 0, hi = W;   // pre[lo] <= j < pre[hi]
-  while (hi - lo > 1) {
-    const int mid = (lo + hi) >> 1;
-    if (pre[mid] <= j) lo = mid; else hi = mid;
-  }
-  return lo;
-}
-
-template <int KV>
-__global__ __launch_bounds__(AT_NT) void attn_persist_kernel(AttnBatch ab, AttnPersist pp) {
-  constexpr int ST = ATTN_PS_STAGE, SUB = 2, NU = ST / 16, NB = 2;
-  constexpr int MAXW = ATTN_PS_MAX_ITEMS;
-  static_assert(MAXW <= AT_NT && ATTN_PS_MAX_RUN * ST <= AT_IDS, "persistent sizes");
-  static_assert(KV == 0 || ST == 64, "mixed KV rows: 64-entry stages");
-  constexpr int DPS = KV ? 6 : 2 * NU;   // DMA instructions per wave per stage
-  __shared__ AttnDmaSmem<ST, NB, 0, KV> sm;   // stage buffers (bf16 or mixed rows)
-  __shared__ int s_ids[AT_IDS];
-  __shared__ int s_pre[MAXW + 1];
-  __shared__ int4 s_item[MAXW];   // entries, first entry of the sequence, sequence size, query row
-  __shared__ int s_scan[AT_NT / WAVE + 1];
-
-  const int t = threadIdx.x;
-  const int R0 = pp.rows;
-  const int HB = ab.head_blocks;
-  const int W = ab.n * R0 * HB;   // the host keeps W <= MAXW
-  const int G = pp.G;
-  const int gid = blockIdx.x;
-
-  // ---- the plan: every work-group derives the same item table and stage offsets
-  int my_st = 0;
-  if (t < W) {
-    const int lr = t / HB;
-    const AttnArgs& a = ab.a[lr / R0];
-    const int r = lr % R0;
-    const int b = r / a.max_q;
-    const int qi = r - b * a.max_q;
-    const int64_t r0 = a.q_off[b];
-    int4 it = make_int4(0, 0, 0, -1);   // row -1: no such query
-    if (qi < a.q_off[b + 1] - r0) {
-      const int64_t eb = a.ent_off[b];
-      const int64_t ns = a.ent_off[b + 1] - eb;
-      const int64_t row = r0 + qi;
-      int n = 0;
-      if (ns > 0) n = a.idx ? min(a.count[row], a.k) : (int)min(a.q_pos[row] / a.ratio, ns);
-      n = max(n, 0);
-      it = make_int4(n, (int)eb, (int)min(ns, (int64_t)ATTN_MAX_SEQ), (int)row);
-      my_st = max(1, (n + ST - 1) / ST);
-    }
-    s_item[t] = it;
-  }
-  int S;
-  const int pre = block_excl_scan<AT_NT>(my_st, s_scan, &S);
-  if (t < W) s_pre[t] = pre;
-  if (t == 0) s_pre[W] = S;
-  if (gid == 0) {   // for the combine
-    if (t < W) {
-      pp.plan[t] = pre;
-      pp.plan[W + 1 + t] = s_item[t].w;
-    }
-    if (t == 0) pp.plan[W] = S;
-  }
-  __syncthreads();
-  const int s0 = ps_run_start(gid, S, G);
-  const int s1 = ps_run_start(gid + 1, S, G);
-  if (s0 >= s1) return;
-
-  const int w = __builtin_amdgcn_readfirstlane(t >> 6);   // wave = head group of 16
-  const int lane = t & 63;
-  const int l16 = lane & 15;
-  const int g = lane >> 4;
-  const int my_row = lane >> 4;
-  const int wrow0 = w * (ST / 4);
-  uint32_t k_lds0, v_lds0;
-  if constexpr (KV) {
-    k_lds0 = lds_addr(&sm.k8[0][wrow0 * 4]);
-    v_lds0 = lds_addr(&sm.v8[0][wrow0 * 4]);
-  } else {
-    k_lds0 = lds_addr(&sm.k[0][wrow0 * 16]);
-    v_lds0 = lds_addr(&sm.v[0][wrow0 * 16]);
-  }
-  constexpr uint32_t BUF_BYTES = ST * 256;
-  constexpr int64_t ROW_BYTES = KV ? KV8_ROW_BYTES : HD * 2;
-
-  bf16x8 qf[4], qn[4];
-  f32x4 o[8];
-#pragma unroll
-  for (int db = 0; db < 8; ++db) o[db] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_run = -INFINITY, l_run = 0.f;
-  int cur = -1;     // item being accumulated
-  int nseg = 0;     // items started in this run
-  float scale_log2 = 0.f;
-
-  // this wave's query slice (16 heads) of item `item`; a row of -1 (no such query)
-  // reads row 0, never used
-  auto load_q = [&](bf16x8 (&dst)[4], int item) __attribute__((always_inline)) {
-    const AttnArgs& a = ab.a[(item / HB) / R0];
-    const int head = (item % HB) * 64 + w * 16 + l16;
-    const int64_t qrow = max(s_item[item].w, 0);
-    const i32x4* qp = reinterpret_cast<const i32x4*>(a.q + (qrow * a.heads + head) * HD);
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) dst[ks] = __builtin_bit_cast(bf16x8, qp[ks * 4 + g]);
-  };
-  // DMA of global stage js into buffer buf (nothing for an empty item); returns
-  // whether anything was issued.  Stages are issued in order, so the item is
-  // tracked, and its sequence pointers are kept, instead of looked up per stage.
-  int iss_item = ps_item_of(s_pre, W, s0);
-  int iss_pre = s_pre[iss_item], iss_next = s_pre[iss_item + 1];
-  int4 iss_it = s_item[iss_item];
-  const AttnArgs* iss_a = &ab.a[(iss_item / HB) / R0];
-  const char* iss_k = reinterpret_cast<const char*>(iss_a->kc) + (int64_t)iss_it.y * ROW_BYTES;
-  const char* iss_v = reinterpret_cast<const char*>(iss_a->vc) + (int64_t)iss_it.y * ROW_BYTES;
-  bool iss_sparse = iss_a->idx != nullptr;
-  auto issue = [&](int js, int buf, int c0) __attribute__((always_inline)) -> bool {
-    while (js >= iss_next) {   // next item (items without stages are passed over)
-      ++iss_item;
-      iss_pre = iss_next;
-      iss_next = s_pre[iss_item + 1];
-      iss_it = s_item[iss_item];
-      iss_a = &ab.a[(iss_item / HB) / R0];
-      iss_k = reinterpret_cast<const char*>(iss_a->kc) + (int64_t)iss_it.y * ROW_BYTES;
-      iss_v = reinterpret_cast<const char*>(iss_a->vc) + (int64_t)iss_it.y * ROW_BYTES;
-      iss_sparse = iss_a->idx != nullptr;
-    }
-    if (iss_it.x <= 0) return false;
-    const int tb = (js - iss_pre) * ST;
-    const int e_last = iss_it.x - 1;
-    auto row_id = [&](int r) __attribute__((always_inline)) {
-      const int e = min(tb + r, e_last);
-      const int id = iss_sparse ? s_ids[(js - c0) * ST + (e - tb)] : e;
-      return (uint32_t)min(max(id, 0), iss_it.z - 1);
-    };
-    if constexpr (KV) {   // as in attn_dma_kernel: FP8 halves, then two runs of bf16 halves
-      const uint32_t rid0 = row_id(wrow0 + (lane >> 2));   // row ids first (see below)
-      uint32_t rid[2];
-#pragma unroll
-      for (int u = 0; u < 2; ++u) rid[u] = row_id(wrow0 + 8 * u + (lane >> 3));
-      const uint32_t off = rid0 * KV8_ROW_BYTES + (uint32_t)(lane & 3) * 16u;
-      dma16(iss_k, off, k_lds0 + buf * (ST * 64));
-      dma16(iss_v, off, v_lds0 + buf * (ST * 64));
-      const uint32_t khi0 = lds_addr(&sm.khi[buf][0]), vhi0 = lds_addr(&sm.vhi[buf][0]);
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const int r = wrow0 + 8 * u + (lane >> 3);
-        const uint32_t base = rid[u] * KV8_ROW_BYTES + 64u;
-        const int sl = lane & 7;
-        dma16(iss_k, base + kv8_kslot(r, sl) * 16u, khi0 + (uint32_t)(wrow0 + 8 * u) * 128u);
-        dma16(iss_v, base + kv8_vslot(r, sl) * 16u, vhi0 + (uint32_t)(wrow0 + 8 * u) * 128u);
-      }
-    } else {
-      // every row id first (LDS reads, one wait), then the DMAs: the DMA's inline
-      // assembly clobbers memory, so a read placed after one would wait on its own
-      uint32_t rid[NU];
-#pragma unroll
-      for (int u = 0; u < NU; ++u) rid[u] = row_id(wrow0 + 4 * u + my_row);
-#pragma unroll
-      for (int u = 0; u < NU; ++u) {
-        const int r = wrow0 + 4 * u + my_row;
-        attn_issue_rows(iss_k, iss_v, rid[u] * 256u, r, l16,
-                        k_lds0 + buf * BUF_BYTES + u * 1024, v_lds0 + buf * BUF_BYTES + u * 1024);
-      }
-    }
-    return true;
-  };
-  // output of item `item` from this run: final when the item lies inside the run,
-  // else a partial in slot 2g (first item of the run) or 2g + 1
-  auto finish = [&](int item) __attribute__((always_inline)) {
-    const float l = lanes4_sum(l_run);
-    const AttnArgs& a = ab.a[(item / HB) / R0];
-    const int hl = w * 16 + l16;
-    const int head = (item % HB) * 64 + hl;
-    const int64_t row = s_item[item].w;
-    if (s_pre[item] >= s0 && s_pre[item + 1] <= s1) {
-      float inv = l > 0.f ? 1.f / l : 0.f;
-      float lse_v = l > 0.f ? (m_run + log2f(l)) * 0.69314718055994530942f : -INFINITY;
-      if (a.sink) inv *= sink_fold(lse_v, a.sink[head], &lse_v);
-      uint16_t* op = a.out + (row * a.heads + head) * HD;
-#pragma unroll
-      for (int db = 0; db < 8; ++db) {
-        uint2 pk;
-        pk.x = f32_to_bf16_bits(o[db][0] * inv) | (f32_to_bf16_bits(o[db][1] * inv) << 16);
-        pk.y = f32_to_bf16_bits(o[db][2] * inv) | (f32_to_bf16_bits(o[db][3] * inv) << 16);
-        *reinterpret_cast<uint2*>(op + db * 16 + 4 * g) = pk;
-      }
-      if (a.lse && g == 0) a.lse[row * a.heads + head] = lse_v;
-    } else {
-      const int64_t slot = 2 * (int64_t)gid + (nseg > 1 ? 1 : 0);
-      float* pp_o = pp.part_o + (slot * 64 + hl) * HD;
-#pragma unroll
-      for (int db = 0; db < 8; ++db) *reinterpret_cast<f32x4*>(pp_o + db * 16 + 4 * g) = o[db];
-      if (g == 0) pp.part_ml[slot * 64 + hl] = make_float2(m_run, l);
-    }
-  };
-
-  int cmp_item = iss_item, cmp_pre = iss_pre, cmp_next = iss_next, cmp_n = 0;
-  // The query of the run's first item; each later item's query is loaded one stage
-  // ahead into qn (see the stage loop).  A load is waited for only where it is used.
-  load_q(qf, iss_item);
-  for (int c0 = s0; c0 < s1; c0 += ATTN_PS_MAX_RUN) {
-    const int c1 = min(c0 + ATTN_PS_MAX_RUN, s1);
-    const int nst = c1 - c0;
-    // entry ids of the sparse stages of this part of the run: thread t takes entries
-    // t % ST of stages c0 + t / ST + (AT_NT / ST) u; their items follow from one search
-    // and a walk forward; every load is issued before the first is used
-    {
-      static_assert(AT_NT % ST == 0, "a thread keeps its place within the stages");
-      constexpr int SPU = AT_NT / ST;   // stages per round of AT_NT ids
-      int v[AT_IDS / AT_NT];
-      int js = c0 + t / ST;
-      int item = ps_item_of(s_pre, W, min(js, c1 - 1));
-#pragma unroll
-      for (int u = 0; u < AT_IDS / AT_NT; ++u, js += SPU) {
-        while (item + 1 < W && s_pre[item + 1] <= js) ++item;
-        const AttnArgs& a = ab.a[(item / HB) / R0];
-        const int e = (js - s_pre[item]) * ST + t % ST;
-        const bool ok = js < c1 && a.idx != nullptr && e < s_item[item].x;
-        // an address that is always valid (the plan, in the workspace), so the load
-        // can be issued unconditionally; the value of a slot without an entry is 0
-        const int* src = ok ? a.idx + (int64_t)s_item[item].w * a.k + e : pp.plan;
-        const int x = *src;
-        v[u] = ok ? x : 0;
-      }
-      __syncthreads();   // the previous part's ids are no longer read
-#pragma unroll
-      for (int u = 0; u < AT_IDS / AT_NT; ++u) s_ids[t + AT_NT * u] = v[u];
-      __syncthreads();
-    }
-    bool dma1 = false;                     // whether the stage after the current one fetched rows
-    issue(c0, 0, c0);
-    if (nst > 1) dma1 = issue(c0 + 1, 1, c0);
-    for (int j = 0; j < nst; ++j) {
-      const int js = c0 + j;
-      const int buf = j & 1;
-      if (j + 1 < nst && dma1) wait_vm<DPS>();
-      else wait_vm<0>();
-      lds_barrier();
-      while (js >= cmp_next) {   // the item of stage js
-        ++cmp_item;
-        cmp_pre = cmp_next;
-        cmp_next = s_pre[cmp_item + 1];
-      }
-      const int item = cmp_item;
-      if (item != cur) {
-        if (cur >= 0) {
-          finish(cur);
-          // qn holds this item's query: loaded at the previous stage, before the DMAs
-          // of the stage after this one, which the wait above left in flight
-#pragma unroll
-          for (int ks = 0; ks < 4; ++ks) qf[ks] = qn[ks];
-        }
-#pragma unroll
-        for (int db = 0; db < 8; ++db) o[db] = f32x4{0.f, 0.f, 0.f, 0.f};
-        m_run = -INFINITY;
-        l_run = 0.f;
-        scale_log2 = ab.a[(item / HB) / R0].scale_log2;
-        cmp_n = s_item[item].x;
-        cur = item;
-        ++nseg;
-      }
-      {   // the query of the next stage's item (always loaded: a conditional load would be
-          // merged into a select that waits for it)
-        int nit = cmp_item, nnext = cmp_next;
-        const int jn = min(js + 1, s1 - 1);
-        while (jn >= nnext) {
-          ++nit;
-          nnext = s_pre[nit + 1];
-        }
-        load_q(qn, nit);
-      }
-      if constexpr (KV) {
-        // the stage's FP8 halves to bf16 (stale rows of an empty item's stage are harmless)
-        const int r = t >> 2, ch = t & 3;
-        const i32x4 k8 = sm.k8[buf][r * 4 + ch];
-        const i32x4 v8 = sm.v8[buf][r * 4 + ch];
-        i32x4 klo[2], vlo[2];
-#pragma unroll
-        for (int h = 0; h < 2; ++h)
-#pragma unroll
-          for (int d = 0; d < 2; ++d) {
-            const int word = 2 * h + d;
-            klo[h][2 * d] = __builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(k8[word], 1.f, false));
-            klo[h][2 * d + 1] = __builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(k8[word], 1.f, true));
-            vlo[h][2 * d] = __builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v8[word], 1.f, false));
-            vlo[h][2 * d + 1] = __builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v8[word], 1.f, true));
-          }
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          sm.klo[r * 8 + kv8_kslot(r, 2 * ch + h)] = klo[h];
-          sm.vlo[r * 8 + kv8_vslot(r, 2 * ch + h)] = vlo[h];
-        }
-        lds_barrier();
-        if ((js - cmp_pre) * ST < cmp_n)
-          attn_stage_kv8<SUB>(sm.klo, sm.khi[buf], sm.vlo, sm.vhi[buf], 0, (js - cmp_pre) * ST,
-                              cmp_n, qf, o, m_run, l_run, scale_log2, l16, g);
-      } else {
-        if ((js - cmp_pre) * ST < cmp_n)   // an empty item's stage has nothing to attend
-          attn_stage<SUB>(sm.k[buf], reinterpret_cast<const char*>(sm.v[buf]), 0,
-                          (js - cmp_pre) * ST, cmp_n, qf, o, m_run, l_run, scale_log2, l16, g);
-      }
-      lds_barrier();
-      dma1 = false;
-      if (j + 2 < nst) dma1 = issue(js + 2, buf, c0);
-    }
-    wait_vm<0>();
-  }
-  if (cur >= 0) finish(cur);
-}
-
-// Merge an item's partials from consecutive work-groups, in work-group order.
-// grid (64 / 8, items): a work-group takes 8 heads of one item, 32 threads per head
-// (4 dims each), and loads up to CB pieces per round, all of them in one round for
-// the usual item sizes.
-constexpr int PSC_HEADS = 8;
-__global__ __launch_bounds__(256) void attn_persist_combine_kernel(AttnBatch ab, AttnPersist pp) {
-  constexpr int CB = 8;
-  const int R0 = pp.rows;
-  const int HB = ab.head_blocks;
-  const int W = ab.n * R0 * HB;
-  const int item = blockIdx.y;
-  if (item >= W) return;
-  const int* plan = pp.plan;
-  const int S = plan[W];
-  const int p0 = plan[item], p1 = plan[item + 1];
-  if (p1 <= p0) return;   // no such query row
-  const int G = pp.G;
-  const int g_first = ps_group_of(p0, S, G);
-  const int g_last = ps_group_of(p1 - 1, S, G);
-  if (g_first == g_last) return;   // written whole by its run
-  const int npc = g_last - g_first + 1;
-  const bool first_is_last_slot = p0 > ps_run_start(g_first, S, G);
-  const AttnArgs& a = ab.a[(item / HB) / R0];
-  const int hl = blockIdx.x * PSC_HEADS + (threadIdx.x >> 5);
-  const int head = (item % HB) * 64 + hl;
-  const int dg = threadIdx.x & 31;
-  float mm = -INFINITY, ll = 0.f;
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  for (int c0 = 0; c0 < npc; c0 += CB) {
-    float2 ml[CB];
-    f32x4 ov[CB];
-#pragma unroll
-    for (int u = 0; u < CB; ++u) {
-      const int pc = c0 + u;
-      const int gq = g_first + (pc < npc ? pc : c0);
-      // with fewer stages than work-groups some runs are empty: they wrote no partial,
-      // and their slots hold whatever an earlier launch left there
-      const bool in = pc < npc && ps_run_start(gq, S, G) < ps_run_start(gq + 1, S, G);
-      const int pcc = gq - g_first;
-      const int64_t slot = 2 * (int64_t)gq + ((pcc == 0 && first_is_last_slot) ? 1 : 0);
-      ml[u] = pp.part_ml[slot * 64 + hl];
-      ov[u] = *reinterpret_cast<const f32x4*>(pp.part_o + (slot * 64 + hl) * HD + dg * 4);
-      if (!in) {
-        ml[u] = make_float2(-INFINITY, 0.f);
-        ov[u] = f32x4{0.f, 0.f, 0.f, 0.f};
-      }
-    }
-    float mb = mm;
-#pragma unroll
-    for (int u = 0; u < CB; ++u) mb = fmaxf(mb, ml[u].x);
-    const float r = exp2f(mm - mb);   // 0 on the first round
-    ll *= r;
-    acc *= r;
-#pragma unroll
-    for (int u = 0; u < CB; ++u) {
-      const float f = exp2f(ml[u].x - mb);   // 0 for pieces past the end
-      ll += ml[u].y * f;
-      acc += ov[u] * f;
-    }
-    mm = mb;
-  }
-  const int64_t row = plan[W + 1 + item];
-  float inv = ll > 0.f ? 1.f / ll : 0.f;
-  float lse_v = ll > 0.f ? (mm + log2f(ll)) * 0.69314718055994530942f : -INFINITY;
-  if (a.sink) inv *= sink_fold(lse_v, a.sink[head], &lse_v);
-  uint2 pk;
-  pk.x = f32_to_bf16_bits(acc[0] * inv) | (f32_to_bf16_bits(acc[1] * inv) << 16);
-  pk.y = f32_to_bf16_bits(acc[2] * inv) | (f32_to_bf16_bits(acc[3] * inv) << 16);
-  *reinterpret_cast<uint2*>(a.out + (row * a.heads + head) * HD + dg * 4) = pk;
-  if (a.lse && dg == 0) a.lse[row * a.heads + head] = lse_v;
-}
-
 // lca_attn_sink: the sink folded into a finished result, in place.  A thread takes
 // 8 dims of one (row, head); 16 threads per (row, head).
 __global__ __launch_bounds__(256) void attn_sink_kernel(uint16_t* __restrict__ out,
@@ -1301,56 +908,21 @@ hipError_t launch_attn_sink(uint16_t* out, float* lse, const float* sink, int64_
   return hipGetLastError();
 }
 
-size_t attn_persist_ws_bytes(int G, int items) {
-  return align256((size_t)2 * G * 64 * HD * 4) + align256((size_t)2 * G * 64 * 8) +
-         align256((size_t)(2 * items + 1) * 4);
-}
-
-void attn_persist_carve(void* ws, int G, int items, AttnPersist& pp) {
-  char* p = reinterpret_cast<char*>(ws);
-  pp.part_o = reinterpret_cast<float*>(p);
-  p += align256((size_t)2 * G * 64 * HD * 4);
-  pp.part_ml = reinterpret_cast<float2*>(p);
-  p += align256((size_t)2 * G * 64 * 8);
-  pp.plan = reinterpret_cast<int32_t*>(p);
-  pp.G = G;
-}
-
-bool attn_persist_fits(const AttnBatch& ab, int rows, int G) {
-  if (ab.n == 0 || G <= 0) return false;
-  if (ab.a[0].heads % 64 != 0) return false;
-  const int64_t items = (int64_t)ab.n * rows * ab.head_blocks;
-  if (items > ATTN_PS_MAX_ITEMS) return false;
-  int64_t stages = 0;   // bound on S from the host bounds on the entry counts
-  for (int l = 0; l < ab.n; ++l)
-    stages += (int64_t)rows * ab.head_blocks *
-              max(1, (ab.a[l].max_n + ATTN_PS_STAGE - 1) / ATTN_PS_STAGE);
-  return stages <= (int64_t)ATTN_PS_MAX_RUN * G;
-}
-
-hipError_t launch_attention_persist(const AttnBatch& ab, const AttnPersist& pp, hipStream_t st) {
-  if (ab.n == 0 || pp.rows == 0) return hipSuccess;
-  const int items = ab.n * pp.rows * ab.head_blocks;
-  if (ab.a[0].kv8)   // one row format per launch
-    hipLaunchKernelGGL(attn_persist_kernel<1>, dim3((unsigned)pp.G), dim3(AT_NT), 0, st, ab, pp);
-  else
-    hipLaunchKernelGGL(attn_persist_kernel<0>, dim3((unsigned)pp.G), dim3(AT_NT), 0, st, ab, pp);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(attn_persist_combine_kernel, dim3(64 / PSC_HEADS, (unsigned)items), dim3(256),
-                     0, st, ab, pp);
-  return hipGetLastError();
-}
-
-hipError_t launch_attention(const AttnBatch& ab, int batch, hipStream_t st) {
-  if (batch == 0 || ab.n == 0) return hipSuccess;
+hipError_t launch_attention(const AttnBatch& ab_in, int batch, hipStream_t st) {
+  if (batch == 0 || ab_in.n == 0) return hipSuccess;
+  AttnBatch ab = ab_in;
   const AttnArgs& a0 = ab.a[0];   // heads and max_q are shared by the batch
   if (a0.max_q == 0) return hipSuccess;
   int max_splits = 1;               // each layer has its own split count
   for (int l = 0; l < ab.n; ++l) max_splits = max(max_splits, ab.a[l].splits);
+  if (max_splits > 65535) return hipErrorInvalidValue;
   const int hg = min(a0.heads, 64) / 16;          // 1, 2 or 4
   const unsigned rows_grid = (unsigned)(batch * a0.max_q);
-  dim3 grid((unsigned)max_splits, rows_grid, (unsigned)(ab.n * ab.head_blocks));
+  const int64_t items = (int64_t)rows_grid * ab.n * ab.head_blocks;
+  if (items >= INT32_MAX) return hipErrorInvalidValue;
+  ab.rows_grid = (int)rows_grid;
+  ab.items = (int)items;
+  dim3 grid((unsigned)(items | 1), (unsigned)max_splits, 1u);
   int n_sparse = 0;
   for (int l = 0; l < ab.n; ++l) n_sparse += ab.a[l].idx != nullptr;
   const int mode = n_sparse == 0 ? 0 : n_sparse == ab.n ? 1 : 2;

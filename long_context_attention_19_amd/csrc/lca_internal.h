@@ -210,6 +210,8 @@ hipError_t launch_attn_sink(uint16_t* out, float* lse, const float* sink, int64_
 struct AttnBatch {
   int32_t n;
   int32_t head_blocks;     // ceil(heads / 64)
+  int32_t rows_grid;       // batch * max_q (set at launch)
+  int32_t items;           // rows_grid * n * head_blocks (set at launch)
   AttnArgs a[MAX_BATCH_LAYERS];
 };
 inline AttnBatch attn_batch1(const AttnArgs& a) {
@@ -225,25 +227,6 @@ int attn_auto_splits(int max_q);
 size_t attn_ws_bytes(int rows, int heads, int splits);
 void attn_ws_carve(void* ws, int rows, int heads, int splits, AttnArgs& a);
 hipError_t launch_attention(const AttnBatch& ab, int batch, hipStream_t st);
-
-// Balanced persistent attention over the items (layer, row, 64-head block) of a batch
-// of layers: G work-groups take equal runs of the items' stages end to end.
-struct AttnPersist {
-  int32_t* plan;           // [W + 1] stage offsets of the items, then [W] query rows
-  float* part_o;           // [2G][64][128]
-  float2* part_ml;         // [2G][64]
-  int32_t G;               // persistent work-groups
-  int32_t rows;            // rows per layer (batch * max_q)
-};
-constexpr int ATTN_PS_MAX_ITEMS = 256;   // layers x rows x head blocks per launch
-constexpr int ATTN_PS_STAGE = 64;        // entries per stage
-constexpr int ATTN_PS_MAX_RUN = 32;      // stages per work-group without re-staging ids
-size_t attn_persist_ws_bytes(int G, int items);
-void attn_persist_carve(void* ws, int G, int items, AttnPersist& pp);
-// true when the batch can take the persistent form: 64-head blocks, few enough
-// items, and a stage total (from the host bounds) that keeps runs short
-bool attn_persist_fits(const AttnBatch& ab, int rows, int G);
-hipError_t launch_attention_persist(const AttnBatch& ab, const AttnPersist& pp, hipStream_t st);
 
 // ------------------------------------------------------------ misc
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t st);

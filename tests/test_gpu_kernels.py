@@ -585,10 +585,10 @@ _KIND_PATTERNS = {"alternate": [i % 2 == 0 for i in range(12)],
 
 
 @pytest.mark.parametrize("pattern", list(_KIND_PATTERNS))
-def test_hybrid_two_persistent_launches_few_stages(pattern):
-    """More than 8 layers (two attention launches sharing the partial slots) with fewer
-    stages than work-groups: a launch's merge must not pick up the other launch's
-    partials from the slots of work-groups whose runs hold no stage."""
+def test_hybrid_two_attention_launches_short_rows(pattern):
+    """More than 8 layers (two attention launches, each with its own layers' partial
+    regions) over short rows, run twice over the same workspace: no launch's merge picks
+    up partials of another layer or of the previous step."""
     step(f"HybridStep 12 layers, short rows, {pattern}")
     g = rng(275, list(_KIND_PATTERNS).index(pattern), 0)
     L = [3000, 9000, 20000]

@@ -1,6 +1,6 @@
 """GPU parity of the attention sink: lca_attn_sink on a finished result, and the sink
-folded in by the hybrid step's final writers (persistent attention and its combine,
-the per-row attention and its combine, the window branch's merge), against the
+folded in by the hybrid step's final writers (the attention of a one-piece row, the
+split combine, the window branch's merge), against the
 oracle's softmax with one extra per-head logit and a zero value."""
 import math
 
@@ -147,24 +147,24 @@ def _hybrid_case(g, L, heads, n_layers, windows, sinks_on):
             assert_lse_close(LSE[b], r["lse"], f"layer {li} seq {b}")
 
 
-def test_hybrid_sinks_persistent_split_items():
-    """64 heads, few long rows: every item is split between work-groups, so the
-    persistent combine writes the results (window on some layers, one layer without sink)."""
-    step("HybridStep sinks, persistent form, split items")
+def test_hybrid_sinks_split_rows():
+    """64 heads, few long rows: most rows are cut into several pieces, so the split
+    combine writes the results (window on some layers, one layer without sink)."""
+    step("HybridStep sinks, 64 heads, split rows")
     _hybrid_case(rng(312, 0, 0), [4000, 65537, 1000 * 128 + 77], 64, 4, [0, 0, W, 0],
                  [True, True, True, False])
 
 
-def test_hybrid_sinks_persistent_whole_items():
-    """Many short rows: most items lie inside one work-group's run and are written
-    there; some rows see nothing but their window or nothing at all."""
-    step("HybridStep sinks, persistent form, whole items")
+def test_hybrid_sinks_one_piece_rows():
+    """Many short rows: most rows are one piece, written by their attention work-group;
+    some rows see nothing but their window or nothing at all."""
+    step("HybridStep sinks, 64 heads, one-piece rows")
     g = rng(313, 0, 0)
     L = list(g.integers(0, 700, size=30)) + [2, 0]
     _hybrid_case(g, [int(x) for x in L], 64, 8, [0, W], [True])
 
 
-def test_hybrid_sinks_per_row_form():
-    """16 heads: the per-row attention and its split combine write the results."""
-    step("HybridStep sinks, per-row form")
+def test_hybrid_sinks_16_heads():
+    """16 heads (128-entry stages, four entry sub-groups per work-group)."""
+    step("HybridStep sinks, 16 heads")
     _hybrid_case(rng(314, 0, 0), [4000, 65537, 300], 16, 4, [0, W], [True, True, False, True])

@@ -49,29 +49,23 @@ int attn_auto_splits(int max_q) {
 size_t attn_ws_bytes(int rows, int heads, int splits) {
   if (splits <= 1) return 0;
   return align256((size_t)rows * splits * heads * HD * 4) +
-         align256((size_t)rows * splits * heads * 8);
+         align256((size_t)rows * splits * heads * 8) + align256((size_t)rows * 8);
 }
 
 void attn_ws_carve(void* ws, int rows, int heads, int splits, AttnArgs& a) {
   if (splits <= 1 || ws == nullptr) {
     a.part_o = nullptr;
     a.part_ml = nullptr;
+    a.part_info = nullptr;
     return;
   }
   char* p = reinterpret_cast<char*>(ws);
   a.part_o = reinterpret_cast<float*>(p);
   p += align256((size_t)rows * splits * heads * HD * 4);
   a.part_ml = reinterpret_cast<float2*>(p);
+  p += align256((size_t)rows * splits * heads * 8);
+  a.part_info = reinterpret_cast<int2*>(p);
 }
-
-struct RowInfo {
-  int64_t row;       // global query row
-  int64_t e_base;    // first entry of the sequence
-  int64_t n_seq;     // entries the sequence holds
-  int n;             // entries this row attends
-  int per;           // entries per split piece
-  int nsp;           // split pieces actually used
-};
 
 // One piece size for every row of the launch, from the host's bound on the entry
 // count: shorter rows get proportionally fewer pieces (a row beyond the bound widens
@@ -79,24 +73,6 @@ struct RowInfo {
 __device__ __forceinline__ int piece_size(int n, int max_n, int splits, int stage) {
   const int want = (max(n, max_n) + splits - 1) / splits;
   return max(stage, (want + stage - 1) / stage * stage);
-}
-
-// Shared by the attention and combine kernels so both cut a row identically.
-__device__ __forceinline__ bool row_info(const AttnArgs& a, int supertile, RowInfo& ri) {
-  const int b = blockIdx.y / a.max_q;
-  const int i = blockIdx.y - b * a.max_q;
-  const int64_t r0 = a.q_off[b];
-  if (i >= a.q_off[b + 1] - r0) return false;
-  ri.row = r0 + i;
-  ri.e_base = a.ent_off[b];
-  const int64_t N = a.ent_off[b + 1] - ri.e_base;
-  ri.n_seq = N;
-  if (N <= 0) ri.n = 0;
-  else if (a.idx) ri.n = max(0, min(a.count[ri.row], a.k));
-  else ri.n = (int)min(a.q_pos[ri.row] / a.ratio, N);
-  ri.per = piece_size(ri.n, a.max_n, a.splits, supertile);
-  ri.nsp = ri.n > 0 ? (ri.n + ri.per - 1) / ri.per : 1;
-  return true;
 }
 
 // ---------------------------------------------------------------------------------
@@ -460,6 +436,8 @@ __global__ __launch_bounds__(AT_NT) void attn_dma_kernel(AttnBatch ab) {
   const int lz = item / ab.rows_grid;            // layer x head block
   const int gy = item - lz * ab.rows_grid;       // query row slot
   const AttnArgs& a = ab.a[lz / ab.head_blocks];
+  const int s = blockIdx.y;
+  if (s >= a.splits) return;                     // a layer with fewer pieces per row
   const bool sparse = MODE == 2 ? a.idx != nullptr : MODE == 1;   // uniform
   constexpr int ST = 32 * ES * SUB;             // entries per super-tile (stage)
   constexpr int HG = 4 / ES;                    // head groups of 16 per work-group
@@ -483,9 +461,16 @@ __global__ __launch_bounds__(AT_NT) void attn_dma_kernel(AttnBatch ab) {
   const int64_t nq = a.q_off[b + 1] - r0;
   int64_t e_base = a.ent_off[b];
   int64_t n_seq = a.ent_off[b + 1] - e_base;
-  if (qi >= nq) return;
+  if (qi >= nq) {   // a padding row slot: nothing for the combine either
+    if (s == 0 && threadIdx.x == 0 && a.part_info) a.part_info[gy] = make_int2(-1, 0);
+    return;
+  }
+  // a piece that starts past the sequence's entries (or past k) exists for no row of
+  // the sequence: leave before the row's count is read (pieces only widen beyond the bound)
+  if (s > 0 && (int64_t)s * piece_size(0, a.max_n, a.splits, ST) >=
+                   (sparse ? min(n_seq, (int64_t)a.k) : n_seq))
+    return;
   const int64_t row = r0 + qi;
-  const int s = blockIdx.y;
   // the row's entry count: only needed after the first DMAs are issued
   int n_raw = sparse ? a.count[row] : (int)min(a.q_pos[row] / a.ratio, (int64_t)INT32_MAX);
   if (MODE == 0 && a.win_pos0 != nullptr) {
@@ -630,10 +615,10 @@ __global__ __launch_bounds__(AT_NT) void attn_dma_kernel(AttnBatch ab) {
   // the query is needed now: the compiler's wait for it lands here, behind the DMAs
   asm volatile("" : "+v"(qf[0]), "+v"(qf[1]), "+v"(qf[2]), "+v"(qf[3]));
 
-  // as row_info computes it for the combine kernel
   const int n = n_seq <= 0 ? 0 : sparse ? max(0, min(n_raw, kk)) : (int)min((int64_t)n_raw, n_seq);
   const int per = piece_size(n, max_n, splits, ST);
   const int nsp = n > 0 ? (n + per - 1) / per : 1;
+  if (s == 0 && t == 0 && a.part_info) a.part_info[gy] = make_int2((int)row, nsp);
   if (s >= nsp || per != per_g) {
     // outside the row, or a row beyond the bound: drop what was fetched speculatively
     wait_vm<0>();
@@ -796,82 +781,68 @@ __global__ __launch_bounds__(AT_NT) void attn_dma_kernel(AttnBatch ab) {
   }
 }
 
-// Merge split partials: a work-group takes 2 heads of one row; per head, 32 dim
-// groups (4 dims, one 16-byte load per piece) x 4 piece groups (pieces g, g+4, ...).
-// Each thread merges its pieces in order with a running maximum, up to CB pieces per
-// round of loads, then piece group 0 merges the 4 groups' results in group order.
-// The result therefore does not depend on load timing.
-constexpr int CMB_HEADS = 2;
-constexpr int CMB_PG = 4;
-__global__ __launch_bounds__(256) void attn_combine_kernel(AttnBatch ab, int stage) {
-  const AttnArgs& a = ab.a[blockIdx.z];   // grid z = layer
-  constexpr int CB = 8;
-  __shared__ float red[CMB_HEADS][CMB_PG][32][6];
-  RowInfo ri;
-  if (!row_info(a, stage, ri)) return;
-  if (ri.nsp <= 1) return;
-  const int hl = threadIdx.x >> 7;
-  const int head = blockIdx.x * CMB_HEADS + hl;   // heads is a multiple of CMB_HEADS
-  const int pg = (threadIdx.x >> 5) & (CMB_PG - 1);
-  const int dg = threadIdx.x & 31;
-  const int64_t base = ri.row * a.splits * a.heads + head;
-  float mm = -INFINITY, ll = 0.f;
+// Merge split partials: a work-group per (row slot, layer x head block, 8 heads), the
+// item numbering of the attention grid times the 8-head groups of a block.  The row and
+// its piece count come from the record the attention's piece-0 work-groups wrote (one
+// load).  Thread t takes head t / 32 of the group and dims 4 (t % 32) .. +3, and loads
+// the (max, sum) and O of CMB_U pieces at a time, all in flight together; the pieces
+// are added in piece order against a running maximum, so the result does not depend on
+// load timing.
+constexpr int CMB_H = 8;    // heads per work-group
+constexpr int CMB_U = 8;    // pieces per round of loads
+__global__ __launch_bounds__(256) void attn_combine_kernel(AttnBatch ab, int groups) {
+  const int item = blockIdx.x / groups;
+  const int hgrp = blockIdx.x - item * groups;
+  if (item >= ab.items) return;
+  const int lz = item / ab.rows_grid;
+  const int gy = item - lz * ab.rows_grid;
+  const AttnArgs& a = ab.a[lz / ab.head_blocks];
+  if (a.splits <= 1 || a.part_info == nullptr) return;
+  const int2 info = a.part_info[gy];
+  const int nsp = info.y;
+  if (nsp <= 1) return;
+  const int t = threadIdx.x;
+  const int head = (lz % ab.head_blocks) * 64 + hgrp * CMB_H + t / 32;
+  const int d0 = (t % 32) * 4;
+  const int64_t row = info.x;
+  const int64_t base = row * a.splits * a.heads + head;
+  float mt = -INFINITY, lt = 0.f;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  for (int s0 = pg; s0 < ri.nsp; s0 += CB * CMB_PG) {
-    float2 ml[CB];
-    f32x4 ov[CB];
+  for (int j0 = 0; j0 < nsp; j0 += CMB_U) {
+    float2 ml[CMB_U];
+    f32x4 ov[CMB_U];
 #pragma unroll
-    for (int u = 0; u < CB; ++u) {
-      const int sp = s0 + u * CMB_PG;
-      const bool in = sp < ri.nsp;
-      const int64_t slot = base + (int64_t)(in ? sp : s0) * a.heads;
+    for (int u = 0; u < CMB_U; ++u) {
+      const int j = j0 + u;
+      const int64_t slot = base + (int64_t)(j < nsp ? j : j0) * a.heads;
       ml[u] = a.part_ml[slot];
-      ov[u] = *reinterpret_cast<const f32x4*>(a.part_o + slot * HD + dg * 4);
-      if (!in) ml[u] = make_float2(-INFINITY, 0.f);
+      ov[u] = *reinterpret_cast<const f32x4*>(a.part_o + slot * HD + d0);
     }
-    float mb = mm;
 #pragma unroll
-    for (int u = 0; u < CB; ++u) mb = fmaxf(mb, ml[u].x);
-    const float r = exp2f(mm - mb);   // 0 on the first round
-    ll *= r;
+    for (int u = 0; u < CMB_U; ++u)
+      if (j0 + u >= nsp) ml[u] = make_float2(-INFINITY, 0.f);
+    float mb = mt;   // piece j0 exists and holds an entry: mb is finite
+#pragma unroll
+    for (int u = 0; u < CMB_U; ++u) mb = fmaxf(mb, ml[u].x);
+    const float r = exp2f(mt - mb);   // 0 on the first round
+    lt *= r;
     acc *= r;
 #pragma unroll
-    for (int u = 0; u < CB; ++u) {
+    for (int u = 0; u < CMB_U; ++u) {
       const float f = exp2f(ml[u].x - mb);   // 0 for pieces past the end
-      ll += ml[u].y * f;
+      lt += ml[u].y * f;
       acc += ov[u] * f;
     }
-    mm = mb;
-  }
-  float* my = red[hl][pg][dg];
-  my[0] = mm;
-  my[1] = ll;
-  my[2] = acc[0];
-  my[3] = acc[1];
-  my[4] = acc[2];
-  my[5] = acc[3];
-  __syncthreads();
-  if (pg != 0) return;
-  float mt = -INFINITY;
-#pragma unroll
-  for (int q = 0; q < CMB_PG; ++q) mt = fmaxf(mt, red[hl][q][dg][0]);   // pg 0 holds piece 0
-  float lt = 0.f;
-  f32x4 at = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int q = 0; q < CMB_PG; ++q) {
-    const float* o = red[hl][q][dg];
-    const float f = o[0] == -INFINITY ? 0.f : exp2f(o[0] - mt);
-    lt += o[1] * f;
-    at += f32x4{o[2], o[3], o[4], o[5]} * f;
+    mt = mb;
   }
   float inv = 1.f / lt;
   float lse_v = (mt + log2f(lt)) * 0.69314718055994530942f;
   if (a.sink) inv *= sink_fold(lse_v, a.sink[head], &lse_v);
   uint2 pk;
-  pk.x = f32_to_bf16_bits(at[0] * inv) | (f32_to_bf16_bits(at[1] * inv) << 16);
-  pk.y = f32_to_bf16_bits(at[2] * inv) | (f32_to_bf16_bits(at[3] * inv) << 16);
-  *reinterpret_cast<uint2*>(a.out + (ri.row * a.heads + head) * HD + dg * 4) = pk;
-  if (a.lse && dg == 0) a.lse[ri.row * a.heads + head] = lse_v;
+  pk.x = f32_to_bf16_bits(acc[0] * inv) | (f32_to_bf16_bits(acc[1] * inv) << 16);
+  pk.y = f32_to_bf16_bits(acc[2] * inv) | (f32_to_bf16_bits(acc[3] * inv) << 16);
+  *reinterpret_cast<uint2*>(a.out + (row * a.heads + head) * HD + d0) = pk;
+  if (a.lse && d0 == 0) a.lse[row * a.heads + head] = lse_v;
 }
 
 // lca_attn_sink: the sink folded into a finished result, in place.  A thread takes
@@ -926,13 +897,11 @@ hipError_t launch_attention(const AttnBatch& ab_in, int batch, hipStream_t st) {
   int n_sparse = 0;
   for (int l = 0; l < ab.n; ++l) n_sparse += ab.a[l].idx != nullptr;
   const int mode = n_sparse == 0 ? 0 : n_sparse == ab.n ? 1 : 2;
-  int st_size;
 #define LCA_ATTN_LAUNCH_KV(ES, SUB, NB, KV)                                                   \
   do {                                                                                        \
     if (mode == 0) hipLaunchKernelGGL((attn_dma_kernel<ES, SUB, NB, 0, KV>), grid, dim3(AT_NT), 0, st, ab); \
     else if (mode == 1) hipLaunchKernelGGL((attn_dma_kernel<ES, SUB, NB, 1, KV>), grid, dim3(AT_NT), 0, st, ab); \
     else hipLaunchKernelGGL((attn_dma_kernel<ES, SUB, NB, 2, KV>), grid, dim3(AT_NT), 0, st, ab); \
-    st_size = 32 * ES * SUB;                                                                  \
   } while (0)
 #define LCA_ATTN_LAUNCH(ES, SUB, NB) LCA_ATTN_LAUNCH_KV(ES, SUB, NB, 0)
   // mixed KV rows (every layer of the batch; 64-head blocks): 64-entry stages
@@ -950,8 +919,10 @@ hipError_t launch_attention(const AttnBatch& ab_in, int batch, hipStream_t st) {
 #undef LCA_ATTN_LAUNCH_KV
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || max_splits <= 1) return e;
-  dim3 cgrid((unsigned)((a0.heads + CMB_HEADS - 1) / CMB_HEADS), rows_grid, (unsigned)ab.n);
-  hipLaunchKernelGGL(attn_combine_kernel, cgrid, dim3(256), 0, st, ab, st_size);
+  const int groups = hg * 16 / CMB_H;   // 8-head groups of a 64-head block (or of 16 / 32 heads)
+  if ((int64_t)items * groups >= INT32_MAX) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(attn_combine_kernel, dim3((unsigned)(items * groups)), dim3(256), 0, st, ab,
+                     groups);
   return hipGetLastError();
 }
 

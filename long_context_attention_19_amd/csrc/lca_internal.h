@@ -189,6 +189,8 @@ struct AttnArgs {
   float* lse;
   float* part_o;           // [rows][splits][heads][128]
   float2* part_ml;         // [rows][splits][heads]  (running max in log2 units, sum)
+  int2* part_info;         // [batch * max_q] per row slot: (query row or -1, pieces),
+                           // written by the piece-0 work-groups for the combine
   // Sliding-window form (dense, win_pos0 != nullptr): kc / vc / ent_off describe the
   // state buffers, whose first rows sit at absolute positions win_pos0[b]; a row at
   // position p attends the buffer's tokens at positions [p - window, p).  With

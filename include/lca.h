@@ -346,6 +346,23 @@ int32_t lca_hca_dense_attn_kv8(const lca_bf16* q, const uint8_t* k_cmp, const ui
  *            -inf with out = 0 for a row that attended nothing); out: the result
  *            of one softmax over both key sets (log-sum-exp merge).  lse required.
  *   window >= 0 (0: nothing to do).  No workspace.
+ *
+ * Decode with the state cache (page section 3-2 item 4: the window and the tokens not
+ * yet ready for compression are kept apart from the compressed cache).  Per layer of
+ * compression ratio r and window w, for a sequence of L tokens (query at position L):
+ *   - the compressed cache holds the floor(L / r) complete blocks; it may be laid out
+ *     with room for later entries (ent_off spaced by capacity): the attention and the
+ *     selection see only min(floor(q_pos / r), N_b) entries, so rows not yet written
+ *     are never read;
+ *   - the state buffer holds at least the tokens [min(L - w, floor(L / r) * r), L):
+ *     the window and the incomplete block's tail (up to r - 1 tokens); win_pos0 is
+ *     the position of its row 0, and rows past position L - 1 are never read;
+ *   - after the step the new token (position L) is appended to the buffer; when
+ *     L + 1 is a multiple of r the block [L + 1 - r, L + 1) is complete:
+ *     lca_kv_compress over those r buffered tokens (tok_off {0, r}, batch 1, ent_off
+ *     {0, 1}, y = the sequence's next cache row) appends its entry (for CSA the
+ *     indexer key of the new entry is written beside it), and the buffer may drop
+ *     the tokens before L + 1 - w (moving win_pos0 up).
  * ------------------------------------------------------------------------- */
 int32_t lca_window_attn(const lca_bf16* q, const lca_bf16* win_k, const lca_bf16* win_v,
                         const int64_t* win_off, const int64_t* win_pos0, const int64_t* q_off,

@@ -24,6 +24,9 @@ from .csa_hca import (
     n_visible,
     index_scores,
     topk_select,
+    index_scores_rows,
+    index_scores_fp4_rows,
+    topk_select_rows,
     attention,
     csa_query,
     hca_query,
@@ -52,7 +55,8 @@ from .csa_hca import (
 
 __all__ = [
     "bf16_bits_to_f64", "f64_to_bf16_bits", "kv_compress", "n_visible", "index_scores",
-    "topk_select", "attention", "csa_query", "hca_query", "csa_decode", "hca_decode",
+    "topk_select", "index_scores_rows", "index_scores_fp4_rows", "topk_select_rows",
+    "attention", "csa_query", "hca_query", "csa_decode", "hca_decode",
     "hybrid_decode", "csa_prefill", "window_tokens", "attention_union", "csa_query_swa",
     "hca_query_swa", "attention_sink", "csa_query_sink", "hca_query_sink",
     "fp4_values", "fp4_unpack", "index_scores_fp4", "csa_query_fp4",

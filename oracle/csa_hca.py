@@ -215,6 +215,51 @@ def topk_select(scores, n_vis: int, k: int) -> np.ndarray:
     return np.sort(order[: min(k, n_vis)])
 
 
+def index_scores_rows(q_idx, k_idx) -> np.ndarray:
+    """index_scores of many query rows against one key set: [rows, entries].
+
+    The same integers, from one fp64 matrix product: every product is an integer of
+    magnitude at most 2^14 and every partial sum at most 2^20, far inside fp64's exact
+    integer range (2^53), so the summation order cannot change the result."""
+    q = np.asarray(q_idx, dtype=np.float64)
+    k = np.asarray(k_idx, dtype=np.float64)
+    return np.rint(q @ k.T).astype(np.int64)
+
+
+def index_scores_fp4_rows(q_fp4, k_fp4) -> np.ndarray:
+    """index_scores_fp4 of many query rows: [rows, entries], exactly (products are
+    quarter-multiples of magnitude at most 36, sums at most 2304)."""
+    q = fp4_values(fp4_unpack(q_fp4))
+    k = fp4_values(fp4_unpack(k_fp4))
+    return np.rint(256.0 * (q @ k.T)).astype(np.int64)
+
+
+def topk_select_rows(scores, n_vis, k: int) -> np.ndarray:
+    """topk_select of every row of a score matrix: [rows, k] with row r's
+    min(k, n_vis[r]) selected indices ascending, then -1.
+
+    The ranking is topk_select's, written as one integer key per entry: rank by
+    (score desc, index asc) is rank by (2^21 - score) * N + index ascending (scores
+    lie in [-2^20, 2^20], indices below N), with entries at or past n_vis[r] given
+    the largest key.  The k smallest keys of a row are that row's selection."""
+    s = np.asarray(scores, dtype=np.int64)
+    rows, n = s.shape
+    if n == 0 or k <= 0:
+        return np.full((rows, max(k, 0)), -1, dtype=np.int64)
+    nv = np.minimum(np.asarray(n_vis, dtype=np.int64).reshape(rows), n)
+    j = np.arange(n, dtype=np.int64)[None, :]
+    key = ((1 << 21) - s) * n + j
+    key = np.where(j < nv[:, None], key, np.iinfo(np.int64).max)
+    kk = min(k, n)
+    part = np.argpartition(key, kk - 1, axis=1)[:, :kk] if kk < n else np.tile(j, (rows, 1))
+    out = np.full((rows, k), -1, dtype=np.int64)
+    for r in range(rows):
+        m = int(min(k, nv[r]))
+        pick = part[r][np.argsort(key[r, part[r]], kind="stable")][:m]
+        out[r, :m] = np.sort(pick)
+    return out
+
+
 # --------------------------------------------------------------------------------------
 # attention
 

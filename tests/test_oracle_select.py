@@ -188,3 +188,51 @@ def test_scores_extreme_int8_codes():
     # the two top scores keep their order in the selection (ties by index otherwise)
     assert oracle.topk_select(oracle.index_scores(q, keys), 4, 1).tolist() == [0]
     assert oracle.topk_select(oracle.index_scores(q, keys[1:]), 3, 1).tolist() == [0]
+
+
+# ---------------------------------------------------------------- many-row forms
+
+def test_scores_rows_equal_per_row_scores():
+    """The fp64-product form gives index_scores' exact integers row by row, including
+    the extreme codes (a query and keys of all -128 reach 2^20)."""
+    g = rng(700, 0, 0)
+    K = int8_uniform(g, (3000, 64))
+    Q = int8_uniform(g, (37, 64))
+    K[::50] = -128
+    K[1::50] = 127
+    Q[0] = -128
+    Q[1] = 127
+    S = oracle.index_scores_rows(Q, K)
+    assert S.dtype == np.int64 and S.shape == (37, 3000)
+    for r in range(37):
+        assert np.array_equal(S[r], oracle.index_scores(Q[r], K)), r
+    assert S[0, 0] == 1 << 20
+
+
+def test_scores_fp4_rows_equal_per_row_scores():
+    g = rng(700, 1, 0)
+    K = g.integers(0, 256, (2000, 32)).astype(np.uint8)
+    Q = g.integers(0, 256, (23, 32)).astype(np.uint8)
+    K[0] = 0x77          # +6 in both nibbles
+    Q[0] = 0x77
+    S = oracle.index_scores_fp4_rows(Q, K)
+    for r in range(23):
+        assert np.array_equal(S[r], oracle.index_scores_fp4(Q[r], K)), r
+    assert S[0, 0] == 64 * 36 * 256
+
+
+@pytest.mark.parametrize("spread", [3, 200, 1 << 20])
+def test_topk_rows_equal_per_row_selection(spread):
+    """Row by row the same selection as topk_select, with heavy ties (spread 3), n_vis
+    of 0, below k, exactly k, between k and n, and n, and k above n."""
+    g = rng(701, spread % 97, 0)
+    n, k = 700, 64
+    S = g.integers(-spread, spread + 1, (40, n))
+    nv = np.array([0, 1, k - 1, k, k + 1, n - 1, n] + list(g.integers(0, n + 1, 33)))
+    for kk in (k, 1, n + 5):
+        T = oracle.topk_select_rows(S, nv, kk)
+        assert T.shape == (40, kk)
+        for r in range(40):
+            ref = oracle.topk_select(S[r], int(nv[r]), kk)
+            assert np.array_equal(T[r, :len(ref)], ref), (kk, r)
+            assert np.all(T[r, len(ref):] == -1), (kk, r)

@@ -83,7 +83,7 @@ def traffic_from_profile(tag, src_files, workload):
     if not os.path.exists(path):
         return None
     try:
-        rec = json.load(open(path)).get(tag)
+        rec = json.load(open(path)).get(f"{tag} @ {workload}")
     except Exception:
         return None
     if not rec or rec.get("workload", "").split(" ")[0] != workload:
@@ -105,6 +105,7 @@ def _dtype(wl):
 
 
 CPU_BUDGET_S = 12.0   # oracle time the cpu_baseline leg aims for
+INDEX_REPS = 10       # back-to-back index-pass launches per timed step (its launch duration)
 
 
 def _timed_reps(fn, budget):
@@ -168,7 +169,7 @@ class _Capture:
 
 class HybridRunner(_Capture):
     """8 independent layers, CSA (even) / HCA (odd), one decode token per sequence."""
-    dominant_tag = "ds_index_kernel"
+    dominant_tag = "ds_chunk_kernel"
     dominant_src = ["long_context_attention_19_amd/csrc/decode_select.hip"]
 
     def __init__(self, wl, device="cuda"):
@@ -234,7 +235,7 @@ class HybridRunner(_Capture):
         launch), from HIP events the library records on the stream it runs on, over
         `reps` eager steps of the same configuration."""
         lca, torch = self.lca, self.torch
-        lca.hybrid_timing_enable(True)
+        lca.hybrid_timing_enable(True, index_reps=INDEX_REPS)
         try:
             t = []
             for _ in range(max(1, reps)):
@@ -252,7 +253,7 @@ class HybridRunner(_Capture):
         fmt = "FP4 (FP4 MFMA)" if self.wl.idx_fp4 else "int8 (v_dot4)"
         return {"bound": "hbm", "per_launch": n * kb + len(self._csa) * self.wl.batch * kb,
                 "unit": "GB/s",
-                "kernel": f"ds_index_kernel ({len(self._csa)} CSA layers in one launch): {fmt} "
+                "kernel": f"ds_chunk_kernel ({len(self._csa)} CSA layers in one launch): {fmt} "
                           "indexer scores in LDS, per-chunk top-k candidates (no score matrix)",
                 "per_unit": f"{kb} B per compressed entry (indexer key read) + {kb} B per query"}
 
@@ -321,7 +322,7 @@ class CsaDecodeRunner(_Capture):
     step is the library's layer-stack step with one CSA layer: the candidate index
     pass, the top-k selection and the sparse attention; one step object per input
     replica (distinct indexer keys, queries and outputs)."""
-    dominant_tag = "ds_index_kernel"
+    dominant_tag = "ds_chunk_kernel"
     dominant_src = ["long_context_attention_19_amd/csrc/decode_select.hip"]
 
     def __init__(self, wl, device="cuda", replicas=None):
@@ -377,7 +378,7 @@ class CsaDecodeRunner(_Capture):
         """Average duration of the step's index pass (scores and candidates), from HIP
         events the library records around it on its stream, over `reps` eager steps."""
         lca, torch = self.lca, self.torch
-        lca.hybrid_timing_enable(True)
+        lca.hybrid_timing_enable(True, index_reps=INDEX_REPS)
         try:
             t = []
             for i in range(max(1, reps)):
@@ -394,7 +395,7 @@ class CsaDecodeRunner(_Capture):
         kb = 32 if self.wl.idx_fp4 else 64
         fmt = "FP4 (FP4 MFMA)" if self.wl.idx_fp4 else "int8 (v_dot4)"
         return {"bound": "hbm", "per_launch": n * kb + self.wl.batch * kb, "unit": "GB/s",
-                "kernel": f"ds_index_kernel: {fmt} indexer scores in LDS, per-chunk top-k "
+                "kernel": f"ds_chunk_kernel: {fmt} indexer scores in LDS, per-chunk top-k "
                           "candidates (no score matrix)",
                 "per_unit": f"{kb} B per compressed entry (indexer key read) + {kb} B per query"}
 
@@ -712,8 +713,9 @@ def main(argv=None):
         "roofline": {"kernel": u["kernel"], "bound": u["bound"], "achieved": achieved,
                      "peak": peak, "unit": u["unit"], "frac": achieved / peak,
                      "avg_launch_us": k_ms * 1e3,
-                     "avg_launch_source": ("HIP events the library records around the launch "
-                                           "on its stream, eager steps" if hasattr(run, "dominant_ms")
+                     "avg_launch_source": (f"HIP events the library records on its stream around "
+                                           f"{INDEX_REPS} back-to-back launches of the index pass "
+                                           f"in eager steps, per launch" if hasattr(run, "dominant_ms")
                                            else "HIP events around repeated launches of the same "
                                                 "shape on the step's stream"),
                      "per_launch": u["per_launch"],

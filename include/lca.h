@@ -452,10 +452,14 @@ int32_t lca_hybrid_layer_step(const lca_layer* layers, int32_t n_layers, const i
  * Phase timing of lca_hybrid_layer_step, for measurement.  While enabled, each
  * hybrid step on the current device records HIP events around its phases on the
  * caller's stream (not for use under graph capture).
- *   lca_hybrid_timing_enable(1 / 0) switches it on / off for the current device.
+ *   lca_hybrid_timing_enable(r / 0) switches it on / off for the current device; with
+ *   r > 1 (at most 1000) a timed step launches its first index pass r times back to
+ *   back (the same result each time), so that [0] below is that launch's own
+ *   duration rather than one launch plus the dispatch gap after an event.
  *   lca_hybrid_timing_read(ms, n) waits for the last timed step and writes up to
  *   n durations in milliseconds: [0] the index pass (scores and candidates) of the
- *   first batch of CSA layers (one launch), [1] their top-k selection, [2] the attention of all
+ *   first batch of CSA layers (per launch, the average of the r launches), [1] their
+ *   top-k selection, [2] the attention of all
  *   layers with the split combine and the sliding-window branches (0 for a phase
  *   the step did not have).
  *   LCA_ERR_SHAPE if no timed step ran since enabling.

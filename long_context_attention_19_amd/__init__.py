@@ -279,9 +279,11 @@ def hybrid_layer_step(layer_arr, q_off, q_pos, batch, max_q, heads, head_dim, sc
         _p(ws), _nb(ws), _s(stream)))
 
 
-def hybrid_timing_enable(enable: bool = True):
-    """Record HIP events around the phases of later hybrid steps (not under graph capture)."""
-    _check("lca_hybrid_timing_enable", _lib.lca_hybrid_timing_enable(1 if enable else 0))
+def hybrid_timing_enable(enable: bool = True, index_reps: int = 1):
+    """Record HIP events around the phases of later hybrid steps (not under graph capture);
+    index_reps > 1 repeats the index pass launch back to back inside its timed interval."""
+    _check("lca_hybrid_timing_enable",
+           _lib.lca_hybrid_timing_enable(max(1, int(index_reps)) if enable else 0))
 
 
 def hybrid_timing_read():

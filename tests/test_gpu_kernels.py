@@ -564,7 +564,7 @@ def test_hybrid_step_small():
     # phase timing: a timed eager step gives positive durations for all three phases and
     # the same outputs as the untimed step
     before = [Ld["out"].clone() for Ld in hs.layers]
-    lca.hybrid_timing_enable(True)
+    lca.hybrid_timing_enable(True, index_reps=3)   # the repeated index pass: same result
     try:
         hs.run(i64_dev(np.arange(B + 1)), i64_dev(q_pos), SCALE)
         t = lca.hybrid_timing_read()

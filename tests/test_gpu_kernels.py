@@ -576,6 +576,73 @@ def test_hybrid_step_small():
         assert torch.equal(Ld["out"].view(torch.int16), o.view(torch.int16))
 
 
+def test_hybrid_step_ragged_queries():
+    """Several query rows per sequence (max_q 3, one sequence with none): every output
+    buffer holds exactly q_off[B] packed rows, followed by guard rows that must stay
+    untouched; each row against the oracle at its own position."""
+    step("HybridStep max_q=3 ragged query rows")
+    g = rng(272, 0, 0)
+    L = [40000, 9000, 70001, 128 * 300 + 5]
+    nq = [3, 0, 2, 1]
+    B, max_q, heads, topk, GUARD = len(L), 3, 64, 512, 2
+    q_off = offsets(nq)
+    rows = int(q_off[-1])
+    q_pos = []
+    for b in range(B):
+        for i in range(nq[b]):
+            q_pos.append(L[b] - 2 * i - int(g.integers(0, 3)))
+    layers, refs = [], []
+    for li in range(4):
+        csa = li % 2 == 0
+        ratio = 4 if csa else 128
+        Ns = [x // ratio for x in L]
+        ent_off = offsets(Ns)
+        tot = int(ent_off[-1])
+        Kc = bf16_normal(g, (tot, 128), std=1 / math.sqrt(ratio))
+        Vc = bf16_normal(g, (tot, 128), std=1 / math.sqrt(ratio))
+        q = bf16_normal(g, (rows, heads, 128))
+        out = torch.full((rows + GUARD, heads, 128), 7.0, dtype=torch.bfloat16, device=DEV)
+        lse = torch.full((rows + GUARD, heads), 7.0, dtype=torch.float32, device=DEV)
+        Ld = dict(kind=lca.LCA_LAYER_CSA if csa else lca.LCA_LAYER_HCA, ratio=ratio,
+                  max_entries=max(Ns), q=bf16_dev(q), k_cmp=bf16_dev(Kc), v_cmp=bf16_dev(Vc),
+                  ent_off=i64_dev(ent_off), out=out, lse=lse)
+        host = dict(q=q, Kc=Kc, Vc=Vc, ent_off=ent_off, out=out, lse=lse)
+        if csa:
+            host["k_idx"] = int8_uniform(g, (tot, 64))
+            host["q_idx"] = int8_uniform(g, (rows, 64))
+            host["idx"] = torch.full((rows + GUARD, topk), -7, dtype=torch.int32, device=DEV)
+            host["count"] = torch.full((rows + GUARD,), -7, dtype=torch.int32, device=DEV)
+            Ld.update(topk=topk, k_idx=i8_dev(host["k_idx"]), q_idx=i8_dev(host["q_idx"]),
+                      idx=host["idx"], count=host["count"])
+        layers.append(Ld)
+        refs.append(host)
+    hs = HybridStep(layers, B, max_q, heads)
+    hs.run(i64_dev(q_off), i64_dev(q_pos), SCALE)
+    torch.cuda.synchronize()
+    for li, host in enumerate(refs):
+        O, LSE = bf16_vals(host["out"]), host["lse"].cpu().numpy()
+        assert np.all(O[rows:] == 7.0) and np.all(LSE[rows:] == 7.0), f"layer {li}: guard rows"
+        Kf, Vf = oracle.bf16_bits_to_f64(host["Kc"]), oracle.bf16_bits_to_f64(host["Vc"])
+        qf = oracle.bf16_bits_to_f64(host["q"])
+        if li % 2 == 0:
+            I, C = host["idx"].cpu().numpy(), host["count"].cpu().numpy()
+            assert np.all(I[rows:] == -7) and np.all(C[rows:] == -7), f"layer {li}: guard rows"
+        for b in range(B):
+            sl = slice(host["ent_off"][b], host["ent_off"][b + 1])
+            for i in range(nq[b]):
+                r = int(q_off[b]) + i
+                if li % 2 == 0:
+                    ref = oracle.csa_query(qf[r], host["q_idx"][r], q_pos[r], Kf[sl], Vf[sl],
+                                           host["k_idx"][sl], 4, topk, SCALE)
+                    assert C[r] == len(ref["idx"]) and np.array_equal(I[r, :C[r]], ref["idx"]), \
+                        (li, r)
+                    assert np.all(I[r, C[r]:] == -1), (li, r)
+                else:
+                    ref = oracle.hca_query(qf[r], q_pos[r], Kf[sl], Vf[sl], 128, SCALE)
+                assert_attn_close(O[r], ref["o"], f"layer {li} row {r}")
+                assert_lse_close(LSE[r], ref["lse"], f"layer {li} row {r}")
+
+
 # 12-layer stacks, each attended in two launches of up to 8 layers (HCA layers first):
 # CSA / HCA alternating, HCA-heavy (a launch of HCA layers only) and CSA-heavy (a launch
 # of CSA layers only)

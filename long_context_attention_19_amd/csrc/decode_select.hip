@@ -282,8 +282,8 @@ struct DsSmemSelect {
 
 // The selection of one row from its candidates (all DI_NT threads of the work-group).
 template <bool FP4>
-__device__ void ds_select_row(const DsLayer& L, int64_t row, int b, int64_t nv,
-                              DsSmemSelect& sm, int32_t* s_scan, int32_t* s_b) {
+__device__ void ds_select_row(const DsLayer& L, int gy, DsSmemSelect& sm, int32_t* s_scan,
+                              int32_t* s_b) {
   constexpr int NT = DI_NT;
   constexpr int VPT = DS_VPT;
   constexpr int RC = DS_RC;
@@ -291,12 +291,10 @@ __device__ void ds_select_row(const DsLayer& L, int64_t row, int b, int64_t nv,
   const int t = threadIdx.x;
   const int lane = t & (WAVE - 1);
   const int k = L.k;
-  int32_t* irow = L.idx + row * k;
-  const int nch = (int)((nv + DS_CHUNK - 1) / DS_CHUNK);
-  const DsBudget bud = ds_budget(nv, k);
-  const int vs = nch * bud.slot;   // the row's candidate slots
-  const int32_t* crow = L.cand + row * L.cand_slots;
-  const int nround = (vs + RC - 1) / RC;
+  // The candidate slots and cut marks of grid row gy are where the chunk launch put
+  // them: their first round and the marks are loaded before the row record is back
+  // (the row's own slot count, known from the record, then masks the rest).
+  const int32_t* crow = L.cand + (int64_t)gy * L.cand_slots;
 
   // A round of slots: coalesced loads, then through LDS thread t holds its VPT
   // consecutive slots in registers (read at an odd stride: no two lanes of a read share
@@ -304,7 +302,7 @@ __device__ void ds_select_row(const DsLayer& L, int64_t row, int b, int64_t nv,
   // Threads past the round's end hold empty slots, and their waves skip the passes.
   uint32_t ck[VPT];
   int n_in = 0;
-  auto issue = [&](int rd) __attribute__((always_inline)) {
+  auto issue = [&](int rd, int vs) __attribute__((always_inline)) {
     n_in = min(RC, vs - rd * RC);
     // a buffer view of the round: loads past its end return 0, an empty slot
     const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
@@ -317,18 +315,30 @@ __device__ void ds_select_row(const DsLayer& L, int64_t row, int b, int64_t nv,
 #pragma unroll
     for (int u = 0; u < VPT; ++u) sm.c[t + NT * u] = ck[u];
     __syncthreads();
-    const bool mine = VPT * t < n_in;
 #pragma unroll
-    for (int u = 0; u < VPT; ++u) ck[u] = mine ? sm.c[VPT * t + u] : 0u;
+    for (int u = 0; u < VPT; ++u) ck[u] = VPT * t + u < n_in ? sm.c[VPT * t + u] : 0u;
   };
-  const bool one = nround == 1;
 
-  // the chunks' cut marks, loaded beside the first round's slots: the highest cut bin
-  // of a chunk that dropped entries (0: none)
+  // speculative: the first round of the slot region (all of it that one round holds) and
+  // every cut mark the layer may have, beside the row record
+  issue(0, (int)min((int64_t)RC, L.cand_slots));
   int32_t dc[DPT];
 #pragma unroll
-  for (int e = 0; e < DPT; ++e) dc[e] = L.dcut[row * L.nch + min(t + NT * e, nch - 1)];
-  if (one) issue(0);
+  for (int e = 0; e < DPT; ++e) dc[e] = L.dcut[(int64_t)gy * L.nch + min(t + NT * e, L.nch - 1)];
+  const int4 ri = L.rinfo[gy];   // (row, nv, sequence) from the chunk launch
+  if (ri.x < 0 || ri.y <= k) return;   // padding, or written by the chunk launch
+  const int64_t row = ri.x, nv = ri.y;
+  const int b = ri.z;
+  if (t == 0) L.count[row] = k;
+  int32_t* irow = L.idx + row * k;
+  const int nch = (int)((nv + DS_CHUNK - 1) / DS_CHUNK);
+  const DsBudget bud = ds_budget(nv, k);
+  const int vs = nch * bud.slot;   // the row's candidate slots
+  const int nround = (vs + RC - 1) / RC;
+  const bool one = nround == 1;
+  n_in = min(RC, vs);   // the row's share of the speculative round: slots past it are not its own
+
+  // the chunks' cut marks: the highest cut bin of a chunk that dropped entries (0: none)
   if (t == 0) s_b[2] = 0;
   int32_t dm = 0;
 #pragma unroll
@@ -337,12 +347,12 @@ __device__ void ds_select_row(const DsLayer& L, int64_t row, int b, int64_t nv,
   for (int i = t; i < HIST_BINS; i += NT) sm.hist[i] = 0;
   __syncthreads();
   if (lane == 0 && dm > 0) atomicMax(&s_b[2], dm);
-  if (one) land();
+  land();   // round 0, the speculative one
 
   // coarse histogram of the candidates' keys
   for (int rd = 0; rd < nround; ++rd) {
-    if (!one) {
-      issue(rd);
+    if (rd > 0) {
+      issue(rd, vs);
       land();
     }
     if (VPT * t < n_in) {
@@ -367,7 +377,7 @@ __device__ void ds_select_row(const DsLayer& L, int64_t row, int b, int64_t nv,
     int32_t run = 0;
     for (int rd = 0; rd < nround; ++rd) {
       if (!one) {
-        issue(rd);
+        issue(rd, vs);
         land();
       }
       int32_t nk = 0;
@@ -582,9 +592,9 @@ __global__ __launch_bounds__(DI_NT) void ds_chunk_kernel(DsBatch db) {
     if (EPT * t + e < tot && (kk[e] >> 10) >= cut)
       sm.out[off++] = (int32_t)(((uint32_t)kk[e] << 11) | (uint32_t)(EPT * t + e));
   __syncthreads();
-  int32_t* cdst = L.cand + row * L.cand_slots + blockIdx.x * (int64_t)bud.slot;
+  int32_t* cdst = L.cand + blockIdx.y * L.cand_slots + blockIdx.x * (int64_t)bud.slot;
   for (int i = t; i < bud.slot; i += DI_NT) cdst[i] = i < kept ? sm.out[i] : 0;
-  if (t == 0) L.dcut[row * L.nch + blockIdx.x] = kept < tot ? cut : 0;   // cut >= 1 if dropped
+  if (t == 0) L.dcut[blockIdx.y * L.nch + blockIdx.x] = kept < tot ? cut : 0;   // >= 1 if dropped
 }
 
 // The selection as a kernel of its own: one work-group per row, after the chunk launch.
@@ -594,12 +604,7 @@ __global__ __launch_bounds__(DI_NT) void ds_select_kernel(DsBatch db) {
   __shared__ int32_t s_scan[DI_NW + 1];
   __shared__ int32_t s_b[4];
   const DsLayer& L = db.layer[blockIdx.z];
-  const int4 ri = L.rinfo[blockIdx.y];   // (row, nv, sequence) from the chunk launch
-  if (ri.x < 0 || ri.y <= L.k) return;   // padding, or written by the chunk launch
-  const int64_t row = ri.x, nv = ri.y;
-  const int b = ri.z;
-  if (threadIdx.x == 0) L.count[row] = L.k;
-  ds_select_row<FP4>(L, row, b, nv, sm, s_scan, s_b);
+  ds_select_row<FP4>(L, blockIdx.y, sm, s_scan, s_b);
 }
 
 hipError_t launch_ds_chunks(const DsBatch& db, int batch, hipStream_t st) {

@@ -107,8 +107,10 @@ struct DsLayer {
   const int64_t* ent_off;
   int32_t* n_vis;        // [rows] out
   int4* rinfo;           // [batch * max_q] per grid row: (query row or -1, nv, sequence, 0)
-  int32_t* dcut;         // [rows][nch] a chunk's cut bin if it dropped entries, else 0
-  int32_t* cand;         // [rows][cand_slots] per chunk `slot` words: (key << 11 | entry in
+  int32_t* dcut;         // [batch * max_q][nch] by grid row: a chunk's cut bin if it dropped
+                         // entries, else 0
+  int32_t* cand;         // [batch * max_q][cand_slots] by grid row: per chunk `slot` words:
+                         // (key << 11 | entry in
                          // chunk) of the kept entries in index order, then 0
   int32_t* idx;          // [rows][k] out
   int32_t* count;        // [rows] out

@@ -75,20 +75,29 @@ __device__ __forceinline__ void sl_lds_barrier() {   // LDS traffic only: no mem
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
+// word 3 of a raw buffer resource on gfx950: 32-bit data format, no swizzle
+constexpr int SL_RSRC_WORD3 = 0x00020000;
+
 // Keys of one 64-entry block: tile u, lane l -> entry blk*64 + 16u + l%16, bytes
 // 16 (l/16) ..; entries past N re-read entry N-1 (their scores are never used).
-// Ordinary loads: the keys are shared by every row tile and should stay in L2.
+// Ordinary loads: the keys are shared by every row tile and should stay in L2.  They go
+// through a buffer resource over the sequence's keys: a 32-bit offset per load instead
+// of a 64-bit address (the compiler keeps the first loads' addresses of every sweep
+// live across the whole kernel otherwise, and spills them).
 // FP4 keys are 2 x 16 bytes: lanes 32..63 load nothing and hold zeros.
 template <bool FP4>
-__device__ __forceinline__ void sl_load(i32x4 (&kv)[4], const i32x4* __restrict__ kp, int32_t blk,
+__device__ __forceinline__ void sl_load(i32x4 (&kv)[4], __amdgpu_buffer_rsrc_t rs, int32_t blk,
                                         int32_t N, int lane) {
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
     const int32_t j = min(blk * SL_BLOCK + 16 * u + (lane & 15), N - 1);
     if (FP4)
-      kv[u] = lane < 32 ? kp[j * 2 + (lane >> 4)] : i32x4{0, 0, 0, 0};
+      kv[u] = lane < 32 ? __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                        rs, (j * 2 + (lane >> 4)) * 16, 0, 0))
+                        : i32x4{0, 0, 0, 0};
     else
-      kv[u] = kp[j * 4 + (lane >> 4)];
+      kv[u] = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                            rs, (j * 4 + (lane >> 4)) * 16, 0, 0));
   }
 }
 
@@ -121,12 +130,16 @@ __device__ __forceinline__ void sl_keys(const i32x4 (&kv)[4], const i32x4& qv, i
 // gets (keys, round, block).  Every wave runs every round (a block past the end
 // has no visible entry), so bodies may hold work-group barriers.
 template <bool FP4, class Body>
-__device__ __forceinline__ void sl_sweep(const i32x4* __restrict__ kp, const i32x4& qv, int32_t N,
+__device__ __forceinline__ void sl_sweep(__amdgpu_buffer_rsrc_t kp, const i32x4& qv, int32_t N,
                                          int32_t nround, int w, int lane, Body&& body) {
   i32x4 ka[4], kb[4], kc[4];
   int32_t key[4][4];
-  sl_load<FP4>(ka, kp, w, N, lane);
-  sl_load<FP4>(kb, kp, SL_NW + w, N, lane);
+  // the sweep's first offsets are recomputed here, not kept from an earlier sweep (which
+  // would hold them in registers across the whole kernel)
+  int wv = w;
+  asm volatile("" : "+s"(wv));
+  sl_load<FP4>(ka, kp, wv, N, lane);
+  sl_load<FP4>(kb, kp, SL_NW + wv, N, lane);
   for (int32_t rd = 0; rd < nround; rd += 3) {
     sl_load<FP4>(kc, kp, (rd + 2) * SL_NW + w, N, lane);
     sl_keys<FP4>(ka, qv, key);
@@ -174,7 +187,7 @@ __device__ __forceinline__ void sl_threshold(const int32_t* h, int j, int need, 
 // with a lower index.
 template <bool FP4>
 __device__ __forceinline__ void sl_collect_finalize(
-    const i32x4* __restrict__ kp, const i32x4& qv, int32_t N, int32_t nround, int w, int lane,
+    __amdgpu_buffer_rsrc_t kp, const i32x4& qv, int32_t N, int32_t nround, int w, int lane,
     int n, int grp, int32_t nv, int32_t bA, int k, int nr, int32_t* sm, int32_t* s_tot,
     int32_t* s_na, int32_t* s_nb, int32_t* __restrict__ idx0) {
   int32_t* wt = sm;                                // [2][16][waves] wave totals
@@ -363,7 +376,9 @@ __global__ __launch_bounds__(SL_NT) void index_select_kernel(SelectArgs a, int t
   const int32_t nround = (nblk + SL_NW - 1) / SL_NW;
 
   constexpr int VB = FP4 ? 32 : 64;        // bytes per indexer vector
-  const i32x4* kp = reinterpret_cast<const i32x4*>(a.k_idx + e0 * VB);
+  // the sequence's keys (N entries of VB bytes) as a buffer
+  const __amdgpu_buffer_rsrc_t kp = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<int8_t*>(a.k_idx + e0 * VB), 0, N * VB, SL_RSRC_WORD3);
   const i32x4 zero4 = {0, 0, 0, 0};
   const i32x4 qv = qok && 16 * grp < VB ? *reinterpret_cast<const i32x4*>(a.q_idx + row * VB + 16 * grp)
                                         : zero4;

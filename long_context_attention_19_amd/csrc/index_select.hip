@@ -41,6 +41,8 @@
 // operand; d_idx = 64 fills elements 0..63, so lanes 32..63 supply zeros.  The
 // result has the int8 form's layout; the fp32 sums are exact (quarter multiples far
 // below 2^24) and the score is 256 x the sum, the unit of csa_index_score_fp4.
+#include <type_traits>
+
 #include "lca_device.h"
 #include "lca_internal.h"
 
@@ -104,9 +106,11 @@ __device__ __forceinline__ void sl_load(i32x4 (&kv)[4], __amdgpu_buffer_rsrc_t r
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
-// The block's 16 keys (score + 2^20) of this lane's token: [tile u][r].
+// The block's 16 raw scores of this lane's token: [tile u][r] (int32; the FP4 form in its
+// unit, 256 x the E2M1 dot product).  The sweeps compare raw scores against limits mapped
+// from the 21-bit key space (sl_raw_limit); only the histograms form keys.
 template <bool FP4>
-__device__ __forceinline__ void sl_keys(const i32x4 (&kv)[4], const i32x4& qv, int32_t (&key)[4][4]) {
+__device__ __forceinline__ void sl_scores(const i32x4 (&kv)[4], const i32x4& qv, int32_t (&sc)[4][4]) {
   const i32x4 zero4 = {0, 0, 0, 0};
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
@@ -117,40 +121,60 @@ __device__ __forceinline__ void sl_keys(const i32x4 (&kv)[4], const i32x4& qv, i
       const f32x4_t acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
           ka, qb, f32x4_t{0.f, 0.f, 0.f, 0.f}, FP4_E2M1, FP4_E2M1, 0, UNIT_SCALE, 0, UNIT_SCALE);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) key[u][r] = (int32_t)(acc[r] * 256.f) + KEY_BIAS;
+      for (int r = 0; r < 4; ++r) sc[u][r] = (int32_t)(acc[r] * 256.f);
     } else {
       const i32x4 acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(kv[u], qv, zero4, 0, 0, 0);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) key[u][r] = score_key(acc[r]);
+      for (int r = 0; r < 4; ++r) sc[u][r] = acc[r];
     }
   }
 }
 
-// One sweep over the work-group's blocks, keys loaded two rounds ahead; `body`
-// gets (keys, round, block).  Every wave runs every round (a block past the end
-// has no visible entry), so bodies may hold work-group barriers.
-template <bool FP4, class Body>
-__device__ __forceinline__ void sl_sweep(__amdgpu_buffer_rsrc_t kp, const i32x4& qv, int32_t N,
-                                         int32_t nround, int w, int lane, Body&& body) {
+// score_key(s) >= lim exactly when s >= sl_raw_limit(lim): keys are min(s, 2^20 - 1) + 2^20,
+// so below 2^21 the limit moves down by 2^20, and a limit past the largest key (2^21 - 1)
+// admits no score (not even 2^20, whose key is clamped).
+__device__ __forceinline__ int32_t sl_raw_limit(int32_t lim) {
+  return lim >= (1 << 21) ? INT32_MAX : lim - KEY_BIAS;
+}
+
+// Rounds [r0, r1) of a sweep (and up to two past r1), keys loaded two rounds ahead;
+// `body` gets (ALL, scores, round, block), ALL an integral constant: true when every
+// entry of the round is visible to every token of the group (no per-entry test).
+template <bool FP4, bool ALL, class Body>
+__device__ __forceinline__ void sl_sweep_part(__amdgpu_buffer_rsrc_t kp, const i32x4& qv, int32_t N,
+                                              int32_t r0, int32_t r1, int w, int lane, Body& body) {
   i32x4 ka[4], kb[4], kc[4];
-  int32_t key[4][4];
-  // the sweep's first offsets are recomputed here, not kept from an earlier sweep (which
+  int32_t sc[4][4];
+  const std::integral_constant<bool, ALL> all{};
+  // the part's first offsets are recomputed here, not kept from an earlier sweep (which
   // would hold them in registers across the whole kernel)
   int wv = w;
   asm volatile("" : "+s"(wv));
-  sl_load<FP4>(ka, kp, wv, N, lane);
-  sl_load<FP4>(kb, kp, SL_NW + wv, N, lane);
-  for (int32_t rd = 0; rd < nround; rd += 3) {
+  sl_load<FP4>(ka, kp, r0 * SL_NW + wv, N, lane);
+  sl_load<FP4>(kb, kp, (r0 + 1) * SL_NW + wv, N, lane);
+  for (int32_t rd = r0; rd < r1; rd += 3) {
     sl_load<FP4>(kc, kp, (rd + 2) * SL_NW + w, N, lane);
-    sl_keys<FP4>(ka, qv, key);
-    body(key, rd, rd * SL_NW + w);
+    sl_scores<FP4>(ka, qv, sc);
+    body(all, sc, rd, rd * SL_NW + w);
     sl_load<FP4>(ka, kp, (rd + 3) * SL_NW + w, N, lane);
-    sl_keys<FP4>(kb, qv, key);
-    body(key, rd + 1, (rd + 1) * SL_NW + w);
+    sl_scores<FP4>(kb, qv, sc);
+    body(all, sc, rd + 1, (rd + 1) * SL_NW + w);
     sl_load<FP4>(kb, kp, (rd + 4) * SL_NW + w, N, lane);
-    sl_keys<FP4>(kc, qv, key);
-    body(key, rd + 2, (rd + 2) * SL_NW + w);
+    sl_scores<FP4>(kc, qv, sc);
+    body(all, sc, rd + 2, (rd + 2) * SL_NW + w);
   }
+}
+
+// One sweep over the work-group's blocks: the rounds below every token's visible count
+// (a multiple of 3 of them) without visibility tests, then the rest with them.  Every
+// wave runs every round (a block past the end has no visible entry), so bodies may hold
+// work-group barriers.
+template <bool FP4, class Body>
+__device__ __forceinline__ void sl_sweep(__amdgpu_buffer_rsrc_t kp, const i32x4& qv, int32_t N,
+                                         int32_t nround, int32_t nfull, int w, int lane, Body&& body) {
+  const int32_t nf = min(nfull, nround) / 3 * 3;
+  if (nf > 0) sl_sweep_part<FP4, true>(kp, qv, N, 0, nf, w, lane, body);
+  if (nf < nround) sl_sweep_part<FP4, false>(kp, qv, N, nf, nround, w, lane, body);
 }
 
 // Threshold of one token's histogram (nbins bins, bin b at h[b ^ j]), by one wave:
@@ -187,29 +211,37 @@ __device__ __forceinline__ void sl_threshold(const int32_t* h, int j, int need, 
 // with a lower index.
 template <bool FP4>
 __device__ __forceinline__ void sl_collect_finalize(
-    __amdgpu_buffer_rsrc_t kp, const i32x4& qv, int32_t N, int32_t nround, int w, int lane,
-    int n, int grp, int32_t nv, int32_t bA, int k, int nr, int32_t* sm, int32_t* s_tot,
-    int32_t* s_na, int32_t* s_nb, int32_t* __restrict__ idx0) {
+    __amdgpu_buffer_rsrc_t kp, const i32x4& qv, int32_t N, int32_t nround, int32_t nfull, int w,
+    int lane, int n, int grp, bool qok, int32_t nv, int32_t bA, int k, int nr, int32_t* sm,
+    int32_t* s_tot, int32_t* s_na, int32_t* s_nb, int32_t* __restrict__ idx0) {
   int32_t* wt = sm;                                // [2][16][waves] wave totals
   int32_t* blist = sm + SL_WT;                     // [16][SL_BIN_CAP] (index << 10 | key & 1023)
   int32_t* alist = sm + SL_FRONT;                  // [16][SL_STAGE_K] indices above bA
   int32_t a_base = 0, b_base = 0;
+  // key limits: above the bin is key >= lim_a, inside it lim_b <= key < lim_a (bA = -1:
+  // every key is above); a lane without a token takes no key
+  const int32_t lim_a = sl_raw_limit(qok ? (bA + 1) << 10 : INT32_MAX);
+  const int32_t lim_b = sl_raw_limit(qok ? max(bA, 0) << 10 : INT32_MAX);
   __syncthreads();
-  sl_sweep<FP4>(kp, qv, N, nround, w, lane, [&](const int32_t (&key)[4][4], int32_t rd, int32_t blk) __attribute__((always_inline)) {
+  sl_sweep<FP4>(kp, qv, N, nround, nfull, w, lane, [&](auto all, const int32_t (&sc)[4][4], int32_t rd, int32_t blk) __attribute__((always_inline)) {
+    constexpr bool ALL = decltype(all)::value;
     uint32_t ba[4], bb[4];
     int32_t ex[4];
     int32_t wtot = 0;
+    // entry e_lane + 16 u + r is visible when 16 u + r < vlim
+    const int32_t e_lane = blk * SL_BLOCK + 4 * grp;
+    const int32_t vlim = nv - e_lane;
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      ba[u] = 0;
-      bb[u] = 0;
+      uint32_t a = 0, c = 0;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const bool vis = blk * SL_BLOCK + 16 * u + 4 * grp + r < nv;
-        const int32_t bin = key[u][r] >> 10;
-        ba[u] |= (uint32_t)(vis && bin > bA) << r;
-        bb[u] |= (uint32_t)(vis && bin == bA) << r;
+        const bool vis = ALL || 16 * u + r < vlim;
+        a |= vis && sc[u][r] >= lim_a ? 1u << r : 0u;
+        c |= vis && sc[u][r] >= lim_b ? 1u << r : 0u;
       }
+      ba[u] = a;
+      bb[u] = c & ~a;
       const int32_t cnt = (int32_t)((__builtin_popcount(bb[u]) << 16) | __builtin_popcount(ba[u]));
       const int32_t c1 = sl_partner16(cnt);
       const int32_t pair = cnt + c1;
@@ -228,29 +260,37 @@ __device__ __forceinline__ void sl_collect_finalize(
       pre += i < w ? v : 0;
       tot += v;
     }
-    // entries above bA: walk the set bits
-    uint32_t m = 0;
+    // entries above bA: walk the lane's set bits (tile-major, so in entry order); the
+    // list position is the tile's base (four 16-bit bases in two words) plus the
+    // lane's earlier bits in the same tile
+    {
+      const uint32_t mall = ba[0] | ba[1] << 4 | ba[2] << 8 | ba[3] << 12;
+      uint32_t bw[2];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) m |= ba[u] << (4 * u);
-    while (m) {
-      const int bit = __builtin_ctz(m);
-      m &= m - 1;
-      const int u = bit >> 2, r = bit & 3;
-      const uint32_t bau = u == 0 ? ba[0] : u == 1 ? ba[1] : u == 2 ? ba[2] : ba[3];
-      const int32_t exu = u == 0 ? ex[0] : u == 1 ? ex[1] : u == 2 ? ex[2] : ex[3];
-      const int32_t pos = a_base + ((pre + exu) & 0xffff) + __builtin_popcount(bau & ((1u << r) - 1));
-      if (pos < SL_STAGE_K) alist[n * SL_STAGE_K + pos] = blk * SL_BLOCK + 16 * u + 4 * grp + r;
+      for (int h = 0; h < 2; ++h)
+        bw[h] = (uint32_t)(a_base + ((pre + ex[2 * h]) & 0xffff)) |
+                (uint32_t)(a_base + ((pre + ex[2 * h + 1]) & 0xffff)) << 16;
+      uint32_t m = mall;
+      while (m) {
+        const int bit = __builtin_ctz(m);
+        m &= m - 1;
+        const uint32_t word = (bit & 8) ? bw[1] : bw[0];
+        const int32_t pos = (int32_t)((word >> ((bit & 4) << 2)) & 0xffff) +
+                            __builtin_popcount(__builtin_amdgcn_ubfe(mall, bit & 12, bit & 3));
+        if (pos < SL_STAGE_K) alist[n * SL_STAGE_K + pos] = e_lane + (bit & 12) * 4 + (bit & 3);
+      }
     }
-    // entries inside bA (rare)
+    // entries inside bA (rare: one branch for the wave when there are none)
+    if (bb[0] | bb[1] | bb[2] | bb[3]) {
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      if (bb[u] == 0) continue;
+      for (int u = 0; u < 4; ++u) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        if (bb[u] >> r & 1) {
-          const int32_t pos = b_base + ((pre + ex[u]) >> 16) + __builtin_popcount(bb[u] & ((1u << r) - 1));
-          if (pos < SL_BIN_CAP)
-            blist[n * SL_BIN_CAP + pos] = ((blk * SL_BLOCK + 16 * u + 4 * grp + r) << 10) | (key[u][r] & 1023);
+        for (int r = 0; r < 4; ++r) {
+          if (bb[u] >> r & 1) {
+            const int32_t pos = b_base + ((pre + ex[u]) >> 16) + __builtin_popcount(bb[u] & ((1u << r) - 1));
+            if (pos < SL_BIN_CAP)
+              blist[n * SL_BIN_CAP + pos] = ((e_lane + 16 * u + r) << 10) | (score_key(sc[u][r]) & 1023);
+          }
         }
       }
     }
@@ -363,10 +403,16 @@ __global__ __launch_bounds__(SL_NT) void index_select_kernel(SelectArgs a, int t
     a.count[r0 + q0 + t] = min(v, k);
   }
   if (thr) s_flag = 1;                     // benign race: every writer stores 1
-  // entries visible to some token of the group: the sweeps stop there
-  int32_t mx = nv;
+  // entries visible to some token of the group: the sweeps stop there; the rounds
+  // below the fewest entries visible to a token of the group need no visibility test
+  int32_t mx = nv, mn = qok ? nv : INT32_MAX;
 #pragma unroll
-  for (int d = 1; d < 16; d <<= 1) mx = max(mx, __shfl_xor(mx, d, WAVE));
+  for (int d = 1; d < 16; d <<= 1) {
+    mx = max(mx, __shfl_xor(mx, d, WAVE));
+    mn = min(mn, __shfl_xor(mn, d, WAVE));
+  }
+  // the same in every wave (each wave's lanes n, n + 16, ... cover the group's tokens)
+  const int32_t nfull = __builtin_amdgcn_readfirstlane(mn) / (SL_BLOCK * SL_NW);
   if (lane == 0) s_tot[w] = mx;            // s_tot doubles as scratch here
   __syncthreads();
   int32_t nvmax = 0;
@@ -388,13 +434,15 @@ __global__ __launch_bounds__(SL_NT) void index_select_kernel(SelectArgs a, int t
     for (int i = t; i < SL_ROWS * HIST_BINS; i += SL_NT) sm[i] = 0;
     __syncthreads();
     int32_t* hc = sm + n * HIST_BINS;
-    sl_sweep<FP4>(kp, qv, N, nround, w, lane, [&](const int32_t (&key)[4][4], int32_t, int32_t blk) __attribute__((always_inline)) {
+    sl_sweep<FP4>(kp, qv, N, nround, nfull, w, lane, [&](auto all, const int32_t (&sc)[4][4], int32_t, int32_t blk) __attribute__((always_inline)) {
+      constexpr bool ALL = decltype(all)::value;
+      const int32_t vlim = nv - (blk * SL_BLOCK + 4 * grp);   // visible: 16 u + r < vlim
 #pragma unroll
       for (int u = 0; u < 4; ++u)
 #pragma unroll
         for (int r = 0; r < 4; ++r)
-          if (thr && blk * SL_BLOCK + 16 * u + 4 * grp + r < nv)
-            atomicAdd(&hc[(key[u][r] >> 10) ^ n], 1);
+          if (thr && (ALL || 16 * u + r < vlim))
+            atomicAdd(&hc[(score_key(sc[u][r]) >> 10) ^ n], 1);
     });
     __syncthreads();
     for (int j = w; j < nr; j += SL_NW) {
@@ -410,8 +458,8 @@ __global__ __launch_bounds__(SL_NT) void index_select_kernel(SelectArgs a, int t
     if (t < nr && s_bin[t] >= 0 && sm[t * HIST_BINS + (s_bin[t] ^ t)] > SL_BIN_CAP) s_flag = 0;
     __syncthreads();
     if (s_flag) {
-      sl_collect_finalize<FP4>(kp, qv, N, nround, w, lane, n, grp, nv, thr ? s_bin[n] : -1, k, nr,
-                          sm, s_tot, s_na, s_nb, idx0);
+      sl_collect_finalize<FP4>(kp, qv, N, nround, nfull, w, lane, n, grp, qok, nv,
+                               thr ? s_bin[n] : -1, k, nr, sm, s_tot, s_na, s_nb, idx0);
       return;
     }
     // ---- sweep 2: fine histograms of the threshold bins
@@ -419,13 +467,17 @@ __global__ __launch_bounds__(SL_NT) void index_select_kernel(SelectArgs a, int t
     for (int i = t; i < SL_ROWS * FINE_BINS; i += SL_NT) sm[i] = 0;
     __syncthreads();
     int32_t* hf = sm + n * FINE_BINS;
-    sl_sweep<FP4>(kp, qv, N, nround, w, lane, [&](const int32_t (&key)[4][4], int32_t, int32_t blk) __attribute__((always_inline)) {
+    sl_sweep<FP4>(kp, qv, N, nround, nfull, w, lane, [&](auto all, const int32_t (&sc)[4][4], int32_t, int32_t blk) __attribute__((always_inline)) {
+      constexpr bool ALL = decltype(all)::value;
+      const int32_t vlim = nv - (blk * SL_BLOCK + 4 * grp);   // visible: 16 u + r < vlim
 #pragma unroll
       for (int u = 0; u < 4; ++u)
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-          if (thr && blk * SL_BLOCK + 16 * u + 4 * grp + r < nv && (key[u][r] >> 10) == bA)
-            atomicAdd(&hf[(key[u][r] & 1023) ^ n], 1);
+        for (int r = 0; r < 4; ++r) {
+          const int32_t key = score_key(sc[u][r]);
+          if (thr && (ALL || 16 * u + r < vlim) && (key >> 10) == bA)
+            atomicAdd(&hf[(key & 1023) ^ n], 1);
+        }
     });
     __syncthreads();
     if (t < SL_ROWS) {   // keep bA while the fine threshold overwrites s_bin
@@ -457,7 +509,12 @@ __global__ __launch_bounds__(SL_NT) void index_select_kernel(SelectArgs a, int t
   int32_t a_base = 0, e_base = 0;                 // selected-above / T-valued so far (row n)
   __syncthreads();
   if (nvmax > 0) {
-    sl_sweep<FP4>(kp, qv, N, nround, w, lane, [&](const int32_t (&key)[4][4], int32_t rd, int32_t blk) __attribute__((always_inline)) {
+    // key limits: selected-above is key >= lim_a, T-valued is lim_e <= key < lim_a (a
+    // token without a threshold keeps every visible entry); a lane without a token takes none
+    const int32_t lim_a = sl_raw_limit(!qok ? INT32_MAX : thr ? T + 1 : 0);
+    const int32_t lim_e = sl_raw_limit(!qok ? INT32_MAX : thr ? T : 0);
+    sl_sweep<FP4>(kp, qv, N, nround, nfull, w, lane, [&](auto all, const int32_t (&sc)[4][4], int32_t rd, int32_t blk) __attribute__((always_inline)) {
+      constexpr bool ALL = decltype(all)::value;
       // Counts are packed (T-valued << 16 | above); a round adds at most 1024 to
       // either half.  Within the wave, segment (tile u, lane group g) precedes
       // (u, g') for g < g' and every segment of tiles after u: a scan over the
@@ -465,18 +522,19 @@ __global__ __launch_bounds__(SL_NT) void index_select_kernel(SelectArgs a, int t
       uint32_t ba[4], be[4];
       int32_t ex[4];
       int32_t wtot = 0;
+      const int32_t e_lane = blk * SL_BLOCK + 4 * grp;   // entry e_lane + 16 u + r
+      const int32_t vlim = nv - e_lane;                  // visible when 16 u + r < vlim
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        ba[u] = 0;
-        be[u] = 0;
+        uint32_t x_a = 0, x_c = 0;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const bool vis = blk * SL_BLOCK + 16 * u + 4 * grp + r < nv;
-          const bool above = vis && (!thr || key[u][r] > T);
-          const bool eq = vis && thr && key[u][r] == T;
-          ba[u] |= (uint32_t)above << r;
-          be[u] |= (uint32_t)eq << r;
+          const bool vis = ALL || 16 * u + r < vlim;
+          x_a |= vis && sc[u][r] >= lim_a ? 1u << r : 0u;
+          x_c |= vis && sc[u][r] >= lim_e ? 1u << r : 0u;
         }
+        ba[u] = x_a;
+        be[u] = x_c & ~x_a;
         const int32_t cnt = (int32_t)((__builtin_popcount(be[u]) << 16) | __builtin_popcount(ba[u]));
         // inclusive scan over the lane groups with two lane swaps (no LDS):
         // pair (0,1) and (2,3) sums, then the lower pair's sum for groups 2, 3
@@ -499,25 +557,31 @@ __global__ __launch_bounds__(SL_NT) void index_select_kernel(SelectArgs a, int t
       }
       // Placement: a selected entry's slot is the number of selected entries
       // before it (above-T ones all count, T-valued ones up to the quota).  About
-      // 3% of entries are candidates, so each lane walks only its set bits.
-      uint32_t m = 0;
+      // 3% of entries are candidates, so each lane walks only its set bits, tile-major
+      // (entry order).  The round's offsets of each tile (at most 1088, so 16 bits)
+      // are packed two to a word, above-T and T-valued apart.
+      const uint32_t mA = ba[0] | ba[1] << 4 | ba[2] << 8 | ba[3] << 12;
+      const uint32_t mE = be[0] | be[1] << 4 | be[2] << 8 | be[3] << 12;
+      uint32_t oa[2], oe[2];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) m |= (ba[u] | be[u]) << (4 * u);
+      for (int h = 0; h < 2; ++h) {
+        const uint32_t p0 = (uint32_t)(pre + ex[2 * h]), p1 = (uint32_t)(pre + ex[2 * h + 1]);
+        oa[h] = (p0 & 0xffff) | (p1 << 16);
+        oe[h] = (p0 >> 16) | (p1 & 0xffff0000u);
+      }
+      uint32_t m = mA | mE;
       while (m) {
         const int bit = __builtin_ctz(m);
         m &= m - 1;
-        const int u = bit >> 2, r = bit & 3;
-        const uint32_t bau = u == 0 ? ba[0] : u == 1 ? ba[1] : u == 2 ? ba[2] : ba[3];
-        const uint32_t beu = u == 0 ? be[0] : u == 1 ? be[1] : u == 2 ? be[2] : be[3];
-        const int32_t exu = u == 0 ? ex[0] : u == 1 ? ex[1] : u == 2 ? ex[2] : ex[3];
-        const uint32_t below = (1u << r) - 1;
-        const int32_t p = pre + exu;
-        const int32_t ab = a_base + (p & 0xffff) + __builtin_popcount(bau & below);
-        const int32_t eb = e_base + (p >> 16) + __builtin_popcount(beu & below);
-        const bool isa = bau >> r & 1;
+        const int sh = (bit & 4) << 2;
+        const bool hi = bit & 8;
+        const int32_t ab = a_base + (int32_t)(((hi ? oa[1] : oa[0]) >> sh) & 0xffff) +
+                           __builtin_popcount(__builtin_amdgcn_ubfe(mA, bit & 12, bit & 3));
+        const int32_t eb = e_base + (int32_t)(((hi ? oe[1] : oe[0]) >> sh) & 0xffff) +
+                           __builtin_popcount(__builtin_amdgcn_ubfe(mE, bit & 12, bit & 3));
+        const bool isa = (mA >> bit) & 1;
         const int32_t pos = isa ? ab + min(eb, need_eq) : ab + eb;
-        if (qok && pos < k && (isa || eb < need_eq))
-          orow[pos] = blk * SL_BLOCK + 16 * u + 4 * grp + r;
+        if (pos < k && (isa || eb < need_eq)) orow[pos] = e_lane + (bit & 12) * 4 + (bit & 3);
       }
       a_base += tot & 0xffff;
       e_base += tot >> 16;

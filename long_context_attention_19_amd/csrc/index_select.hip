@@ -205,10 +205,10 @@ __device__ __forceinline__ void sl_threshold(const int32_t* h, int j, int need, 
 // Two-sweep path, second sweep: each token's entries above its threshold bin bA
 // (all of them selected; fewer than k) and inside bA, each list in index order
 // (bA = -1 for a token that keeps every visible entry: they all count as above).
-// Then one wave per token resolves the threshold inside bA by ranking the bin's
-// entries (score desc, index asc), and writes the row: each entry's slot is its
-// rank in its own list plus the number of selected entries of the other list
-// with a lower index.
+// Then one wave per token resolves the threshold inside bA (the bin's largest keys,
+// ties to the lower index) and writes the row: each entry's slot is its position in
+// its own list plus the number of selected entries of the other list with a lower
+// index.
 template <bool FP4>
 __device__ __forceinline__ void sl_collect_finalize(
     __amdgpu_buffer_rsrc_t kp, const i32x4& qv, int32_t N, int32_t nround, int32_t nfull, int w,
@@ -303,58 +303,98 @@ __device__ __forceinline__ void sl_collect_finalize(
   }
   __syncthreads();
   // one wave per token
+  const uint64_t lt_mask = (1ull << lane) - 1;   // lanes below this one
   for (int j = w; j < nr; j += SL_NW) {
     const int32_t na = min(s_na[j], SL_STAGE_K), nb = min(s_nb[j], SL_BIN_CAP);
     const int32_t need = max(0, k - na);                // keys to take from the bin
     int32_t* bl = blist + j * SL_BIN_CAP;
     const int32_t* al = alist + j * SL_STAGE_K;
     constexpr int PB = SL_BIN_CAP / WAVE;
-    int32_t e[PB], rank[PB];
+    int32_t e[PB], kl[PB];
 #pragma unroll
     for (int u = 0; u < PB; ++u) {
-      e[u] = lane + WAVE * u < nb ? bl[lane + WAVE * u] : 0;
-      rank[u] = 0;
+      const bool ok = lane + WAVE * u < nb;
+      e[u] = ok ? bl[lane + WAVE * u] : 0;
+      kl[u] = ok ? (e[u] & 1023) : -1;                // an empty slot takes no threshold
     }
-    for (int q = 0; q < nb; ++q) {   // rank by (key desc, index asc)
-      const int32_t lq = bl[q] & 1023;
+    // The bin's `need` largest keys by (key desc, index asc): the threshold t is the
+    // largest value with at least `need` low key bits >= t (a binary search over the 10
+    // bits, counted by ballots); keys above t are taken, and of the keys equal to t the
+    // first ones in list order (index order) up to the quota.
+    auto count_ge = [&](int32_t v) __attribute__((always_inline)) {
+      int32_t c = 0;
 #pragma unroll
-      for (int u = 0; u < PB; ++u) {
-        const int32_t li = e[u] & 1023;
-        rank[u] += (lq > li || (lq == li && q < lane + WAVE * u)) ? 1 : 0;
+      for (int u = 0; u < PB; ++u) c += __builtin_popcountll(__ballot(kl[u] >= v));
+      return c;
+    };
+    int32_t t, quota;
+    if (need == 0) {               // wave-uniform: nothing from the bin
+      t = 1024;
+      quota = 0;
+    } else if (need >= nb) {       // the whole bin
+      t = 0;
+      quota = nb;
+    } else {
+      int32_t lo = 0, hi = 1023;
+      while (lo < hi) {
+        const int32_t mid = (lo + hi + 1) >> 1;
+        if (count_ge(mid) >= need) lo = mid; else hi = mid - 1;
       }
+      t = lo;
+      quota = need - count_ge(t + 1);
     }
     // selected bin entries, and how many of them precede each list position
-    int32_t run = 0;
+    int32_t run = 0, run_eq = 0;
     int32_t sel_ex[PB];
     bool sel[PB];
 #pragma unroll
     for (int u = 0; u < PB; ++u) {
-      sel[u] = lane + WAVE * u < nb && rank[u] < need;
+      const uint64_t eqb = __ballot(kl[u] == t);
+      const int32_t eq_rank = run_eq + __builtin_popcountll(eqb & lt_mask);
+      run_eq += __builtin_popcountll(eqb);
+      sel[u] = kl[u] > t || (kl[u] == t && eq_rank < quota);
       const uint64_t bal = __ballot(sel[u]);
-      sel_ex[u] = run + __builtin_popcountll(bal & ((1ull << lane) - 1));
+      sel_ex[u] = run + __builtin_popcountll(bal & lt_mask);
       run += __builtin_popcountll(bal);
     }
     const int32_t nsel = run;
+    // the selected bin entries' indices, compacted in order into the list's front, then
+    // one per lane (nsel <= 256: up to four registers)
 #pragma unroll
-    for (int u = 0; u < PB; ++u)   // keep the index, replace the key bits by the count
-      if (lane + WAVE * u < nb) bl[lane + WAVE * u] = (e[u] & ~1023) | sel_ex[u];
+    for (int u = 0; u < PB; ++u)
+      if (sel[u]) bl[sel_ex[u]] = e[u] >> 10;
+    int32_t sv[PB];
+#pragma unroll
+    for (int u = 0; u < PB; ++u) sv[u] = lane + WAVE * u < nsel ? bl[lane + WAVE * u] : INT32_MAX;
     int32_t* orow = idx0 + (int64_t)j * k;
-    for (int p = lane; p < na; p += WAVE) {   // above-bA entries
-      const int32_t x = al[p];
-      int lo = 0, hi = nb;                     // bin entries with a lower index
-      while (lo < hi) {
-        const int mid = (lo + hi) >> 1;
-        if ((bl[mid] >> 10) < x) lo = mid + 1; else hi = mid;
+    // above-bA entries, 64 at a time: each one's slot is its list position plus the
+    // selected bin entries with a lower index, counted with ballots: those below the
+    // chunk's first entry at once, the few between its first and last one by one
+    for (int p0 = 0; p0 < na; p0 += WAVE) {
+      const int p = p0 + lane;
+      const int32_t x = p < na ? al[p] : INT32_MAX;
+      const int32_t x0 = __builtin_amdgcn_readfirstlane(x);
+      const int32_t xl = __builtin_amdgcn_readlane(x, min(WAVE, na - p0) - 1);
+      int32_t c = 0;
+#pragma unroll
+      for (int u = 0; u < PB; ++u) {
+        if (WAVE * u >= nsel) break;
+        c += __builtin_popcountll(__ballot(sv[u] < x0));
+        uint64_t inr = __ballot(sv[u] > x0 && sv[u] < xl);
+        while (inr) {
+          const int l = __builtin_ctzll(inr);
+          inr &= inr - 1;
+          c += x > __builtin_amdgcn_readlane(sv[u], l) ? 1 : 0;
+        }
       }
-      const int32_t before = lo < nb ? (bl[lo] & 1023) : nsel;
-      const int32_t pos = p + before;
-      if (pos < k) orow[pos] = x;
+      const int32_t pos = p + c;
+      if (p < na && pos < k) orow[pos] = x;
     }
 #pragma unroll
     for (int u = 0; u < PB; ++u) {            // selected bin entries
       if (!sel[u]) continue;
       const int32_t y = e[u] >> 10;
-      int lo = 0, hi = na;
+      int lo = 0, hi = na;                     // above-bA entries with a lower index
       while (lo < hi) {
         const int mid = (lo + hi) >> 1;
         if (al[mid] < y) lo = mid + 1; else hi = mid;

@@ -482,12 +482,16 @@ __global__ __launch_bounds__(DI_NT) void ds_chunk_kernel(DsBatch db) {
     // lane t: the 16-byte piece t % 4 of key t / 4 of each 128-key round
     const int piece = t & 3;
     const i32x4 qv = *reinterpret_cast<const i32x4*>(L.q_idx + row * 64 + piece * 16);
-    const i32x4* kp = reinterpret_cast<const i32x4*>(L.k_idx + e0 * 64);
+    // the chunk's visible keys as a buffer: a load past them returns zeros, so the loads
+    // carry no branches (a branch per load made the compiler wait for the first ones
+    // before issuing the rest)
+    const __amdgpu_buffer_rsrc_t kr = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<int8_t*>(L.k_idx + (e0 + base) * 64), 0, tot * 64, BUF_RSRC_WORD3);
     i32x4 kv[DI_ROUNDS];
 #pragma unroll
     for (int u = 0; u < DI_ROUNDS; ++u) {
       const int jl = u * (DI_NT / 4) + (t >> 2);
-      kv[u] = jl < tot ? __builtin_nontemporal_load(kp + (base + jl) * 4 + piece) : i32x4{0, 0, 0, 0};
+      kv[u] = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(kr, jl * 64 + piece * 16, 0, BUF_NT));
     }
     int32_t pd[DI_ROUNDS];
 #pragma unroll
@@ -523,13 +527,14 @@ __global__ __launch_bounds__(DI_NT) void ds_chunk_kernel(DsBatch db) {
     const int kl = lane & 31;
     const i32x4 qv = *reinterpret_cast<const i32x4*>(L.q_idx + row * 32 + half * 16);
     const i32x8 qa = {qv[0], qv[1], qv[2], qv[3], 0, 0, 0, 0};
-    const i32x4* kp = reinterpret_cast<const i32x4*>(L.k_idx + e0 * 32);
+    const __amdgpu_buffer_rsrc_t kr = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<int8_t*>(L.k_idx + (e0 + base) * 32), 0, tot * 32, BUF_RSRC_WORD3);
     const f32x16 zero16 = {};
     i32x4 kv[DF_ROUNDS];
 #pragma unroll
     for (int u = 0; u < DF_ROUNDS; ++u) {
       const int jl = u * (DI_NT / WAVE * 32) + w * 32 + kl;
-      kv[u] = jl < tot ? __builtin_nontemporal_load(kp + (base + jl) * 2 + half) : i32x4{0, 0, 0, 0};
+      kv[u] = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(kr, jl * 32 + half * 16, 0, BUF_NT));
     }
 #pragma unroll
     for (int u = 0; u < DF_ROUNDS; ++u) {

@@ -77,9 +77,6 @@ __device__ __forceinline__ void sl_lds_barrier() {   // LDS traffic only: no mem
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
-// word 3 of a raw buffer resource on gfx950: 32-bit data format, no swizzle
-constexpr int SL_RSRC_WORD3 = 0x00020000;
-
 // Keys of one 64-entry block: tile u, lane l -> entry blk*64 + 16u + l%16, bytes
 // 16 (l/16) ..; entries past N re-read entry N-1 (their scores are never used).
 // Ordinary loads: the keys are shared by every row tile and should stay in L2.  They go
@@ -464,7 +461,7 @@ __global__ __launch_bounds__(SL_NT) void index_select_kernel(SelectArgs a, int t
   constexpr int VB = FP4 ? 32 : 64;        // bytes per indexer vector
   // the sequence's keys (N entries of VB bytes) as a buffer
   const __amdgpu_buffer_rsrc_t kp = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<int8_t*>(a.k_idx + e0 * VB), 0, N * VB, SL_RSRC_WORD3);
+      const_cast<int8_t*>(a.k_idx + e0 * VB), 0, N * VB, BUF_RSRC_WORD3);
   const i32x4 zero4 = {0, 0, 0, 0};
   const i32x4 qv = qok && 16 * grp < VB ? *reinterpret_cast<const i32x4*>(a.q_idx + row * VB + 16 * grp)
                                         : zero4;

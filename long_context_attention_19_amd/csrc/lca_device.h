@@ -12,6 +12,10 @@ typedef int i32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int WAVE = 64;
 constexpr int KEY_BIAS = 1 << 20;        // indexer scores lie in [-2^20, 2^20]
+// word 3 of a raw buffer resource on gfx950: 32-bit data format, no swizzle (loads past
+// the resource's byte range return zeros)
+constexpr int BUF_RSRC_WORD3 = 0x00020000;
+constexpr int BUF_NT = 2;                  // cache-policy bit of a buffer load: nontemporal
 constexpr int HIST_BINS = 2048;          // first radix level: key >> 10
 constexpr int FINE_BINS = 1024;          // second radix level: key & 1023
 

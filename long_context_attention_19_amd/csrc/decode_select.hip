@@ -105,11 +105,18 @@ void ds_ws_carve(void* ws, int rows, int max_n, int k, DsLayer& L) {
 
 // the query row of this grid row, or false for a padding row (i beyond the sequence's
 // query count)
+// A value no kernel of the launch writes, read through the constant address space:
+// a scalar load for a uniform address, whose wait does not hold the in-order vector loads.
+template <class T>
+__device__ __forceinline__ T ld_const(const T* p) {
+  return *(const __attribute__((address_space(4))) T*)(size_t)p;
+}
+
 __device__ __forceinline__ bool ds_row(const int64_t* q_off, int max_q, int64_t& row, int& b) {
   b = blockIdx.y / max_q;
   const int i = blockIdx.y - b * max_q;
-  const int64_t r0 = q_off[b];
-  if (i >= q_off[b + 1] - r0) return false;
+  const int64_t r0 = ld_const(q_off + b);
+  if (i >= ld_const(q_off + b + 1) - r0) return false;
   row = r0 + i;
   return true;
 }
@@ -449,15 +456,43 @@ __global__ __launch_bounds__(DI_NT) void ds_chunk_kernel(DsBatch db) {
   __shared__ int32_t s_cut;
   const DsLayer& L = db.layer[blockIdx.z];
   const int t = threadIdx.x;
+  // The chunk's keys are requested first, over the entries the sequence holds: the
+  // row's position, and so its visible count, is two dependent loads further (the
+  // query offsets, then the position).  Keys past the visible count are fetched but
+  // never counted.
+  const int bs = blockIdx.y / db.max_q;
+  const int64_t e0 = ld_const(L.ent_off + bs);
+  const int64_t N = min(ld_const(L.ent_off + bs + 1) - e0, (int64_t)L.max_entries);
+  const int64_t base = (int64_t)blockIdx.x * DS_CHUNK;
+  if (blockIdx.x > 0 && base >= N) return;   // no entry of the sequence (chunk 0 writes the row records)
+  const int navail = (int)max(min((int64_t)DS_CHUNK, N - base), (int64_t)0);
+  constexpr int VB = FP4 ? 32 : 64;          // bytes per key
+  constexpr int NR = FP4 ? DF_ROUNDS : DI_ROUNDS;
+  // int8: lane t takes the 16-byte piece t % 4 of key t / 4 of each 128-key round;
+  // FP4: lane l of wave w takes half l / 32 of key w * 32 + l % 32 of each round
+  const int w = __builtin_amdgcn_readfirstlane(t / WAVE);
+  const int lane = t & (WAVE - 1);
+  const int piece = FP4 ? lane >> 5 : t & 3;
+  // a buffer over the chunk's keys: a load past them returns zeros, so the loads carry
+  // no branches (a branch per load made the compiler wait for the first ones before
+  // issuing the rest)
+  const __amdgpu_buffer_rsrc_t kr = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<int8_t*>(L.k_idx + (e0 + base) * VB), 0, navail * VB, BUF_RSRC_WORD3);
+  i32x4 kv[NR];
+#pragma unroll
+  for (int u = 0; u < NR; ++u) {
+    const int jl = FP4 ? u * (DI_NT / WAVE * 32) + w * 32 + (lane & 31) : u * (DI_NT / 4) + (t >> 2);
+    kv[u] = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(kr, jl * VB + piece * 16, 0, BUF_NT));
+  }
+  asm volatile("" ::: "memory");   // the row's loads below stay behind the key requests
+
   int64_t row;
   int b;
   if (!ds_row(db.q_off, db.max_q, row, b)) {
     if (blockIdx.x == 0 && t == 0) L.rinfo[blockIdx.y] = make_int4(-1, 0, 0, 0);   // padding
     return;
   }
-  const int64_t e0 = L.ent_off[b];
-  const int64_t N = min(L.ent_off[b + 1] - e0, (int64_t)L.max_entries);
-  const int64_t nv = max(min(db.q_pos[row] / L.c, N), (int64_t)0);
+  const int64_t nv = max(min(ld_const(db.q_pos + row) / L.c, N), (int64_t)0);
   const int k = L.k;
   if (blockIdx.x == 0 && t == 0) {
     L.n_vis[row] = (int32_t)nv;
@@ -471,28 +506,25 @@ __global__ __launch_bounds__(DI_NT) void ds_chunk_kernel(DsBatch db) {
     }
     return;
   }
-  const int64_t base = (int64_t)blockIdx.x * DS_CHUNK;
   if (base >= nv) return;
   const int tot = (int)min((int64_t)DS_CHUNK, nv - base);   // visible entries of the chunk
+
+  // The query through the constant address space: scalar loads, whose wait does not
+  // hold the (in-order) key loads issued above.  Each lane keeps its 16-byte piece.
+  const i32x4* qc = reinterpret_cast<const i32x4*>(L.q_idx + row * VB);
+  i32x4 qv;
+  if constexpr (FP4) {
+    const i32x4 q0 = ld_const(qc), q1 = ld_const(qc + 1);
+    qv = piece ? q1 : q0;
+  } else {
+    const i32x4 q0 = ld_const(qc), q1 = ld_const(qc + 1), q2 = ld_const(qc + 2), q3 = ld_const(qc + 3);
+    qv = piece == 0 ? q0 : piece == 1 ? q1 : piece == 2 ? q2 : q3;
+  }
 
   for (int i = t; i < HIST_BINS; i += DI_NT) sm.lh[i] = 0;
   __syncthreads();
 
   if constexpr (!FP4) {
-    // lane t: the 16-byte piece t % 4 of key t / 4 of each 128-key round
-    const int piece = t & 3;
-    const i32x4 qv = *reinterpret_cast<const i32x4*>(L.q_idx + row * 64 + piece * 16);
-    // the chunk's visible keys as a buffer: a load past them returns zeros, so the loads
-    // carry no branches (a branch per load made the compiler wait for the first ones
-    // before issuing the rest)
-    const __amdgpu_buffer_rsrc_t kr = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<int8_t*>(L.k_idx + (e0 + base) * 64), 0, tot * 64, BUF_RSRC_WORD3);
-    i32x4 kv[DI_ROUNDS];
-#pragma unroll
-    for (int u = 0; u < DI_ROUNDS; ++u) {
-      const int jl = u * (DI_NT / 4) + (t >> 2);
-      kv[u] = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(kr, jl * 64 + piece * 16, 0, BUF_NT));
-    }
     int32_t pd[DI_ROUNDS];
 #pragma unroll
     for (int u = 0; u < DI_ROUNDS; ++u) {
@@ -505,12 +537,12 @@ __global__ __launch_bounds__(DI_NT) void ds_chunk_kernel(DsBatch db) {
     // score of round 4w + piece
     const bool b0 = piece & 1, b1 = piece & 2;
 #pragma unroll
-    for (int w = 0; w < DI_ROUNDS / 4; ++w) {
-      const int p0 = pd[4 * w], p1 = pd[4 * w + 1], p2 = pd[4 * w + 2], p3 = pd[4 * w + 3];
+    for (int w4 = 0; w4 < DI_ROUNDS / 4; ++w4) {
+      const int p0 = pd[4 * w4], p1 = pd[4 * w4 + 1], p2 = pd[4 * w4 + 2], p3 = pd[4 * w4 + 3];
       const int q0 = (b0 ? p1 : p0) + __shfl_xor(b0 ? p0 : p1, 1, WAVE);
       const int q1 = (b0 ? p3 : p2) + __shfl_xor(b0 ? p2 : p3, 1, WAVE);
       const int32_t v = (b1 ? q1 : q0) + __shfl_xor(b1 ? q0 : q1, 2, WAVE);
-      const int jl = (4 * w + piece) * (DI_NT / 4) + (t >> 2);
+      const int jl = (4 * w4 + piece) * (DI_NT / 4) + (t >> 2);
       const int key = score_key(v);
       sm.sc[jl] = key;
       if (jl < tot) atomicAdd(&sm.lh[key >> 10], 1);
@@ -521,28 +553,15 @@ __global__ __launch_bounds__(DI_NT) void ds_chunk_kernel(DsBatch db) {
     // the product, register 0 of lanes 0..31, holds the 32 scores (exact in fp32)
     constexpr int FP4_E2M1 = 4;
     constexpr int UNIT_SCALE = 127;   // E8M0 2^0
-    const int w = __builtin_amdgcn_readfirstlane(t / WAVE);
-    const int lane = t & (WAVE - 1);
-    const int half = lane >> 5;
-    const int kl = lane & 31;
-    const i32x4 qv = *reinterpret_cast<const i32x4*>(L.q_idx + row * 32 + half * 16);
     const i32x8 qa = {qv[0], qv[1], qv[2], qv[3], 0, 0, 0, 0};
-    const __amdgpu_buffer_rsrc_t kr = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<int8_t*>(L.k_idx + (e0 + base) * 32), 0, tot * 32, BUF_RSRC_WORD3);
     const f32x16 zero16 = {};
-    i32x4 kv[DF_ROUNDS];
-#pragma unroll
-    for (int u = 0; u < DF_ROUNDS; ++u) {
-      const int jl = u * (DI_NT / WAVE * 32) + w * 32 + kl;
-      kv[u] = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(kr, jl * 32 + half * 16, 0, BUF_NT));
-    }
 #pragma unroll
     for (int u = 0; u < DF_ROUNDS; ++u) {
       const i32x8 kb = {kv[u][0], kv[u][1], kv[u][2], kv[u][3], 0, 0, 0, 0};
       const f32x16 acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
           qa, kb, zero16, FP4_E2M1, FP4_E2M1, 0, UNIT_SCALE, 0, UNIT_SCALE);
-      if (half == 0) {
-        const int jl = u * (DI_NT / WAVE * 32) + w * 32 + kl;
+      if (piece == 0) {
+        const int jl = u * (DI_NT / WAVE * 32) + w * 32 + (lane & 31);
         const int key = score_key((int32_t)(acc[0] * 256.0f));
         sm.sc[jl] = key;
         if (jl < tot) atomicAdd(&sm.lh[key >> 10], 1);

@@ -457,10 +457,16 @@ __global__ __launch_bounds__(AT_NT) void attn_dma_kernel(AttnBatch ab) {
   // piece) is back.  Rows past the end are read but masked in the softmax.
   const int b = gy / a.max_q;
   const int qi = gy - b * a.max_q;
-  const int64_t r0 = a.q_off[b];
-  const int64_t nq = a.q_off[b + 1] - r0;
-  int64_t e_base = a.ent_off[b];
-  int64_t n_seq = a.ent_off[b + 1] - e_base;
+  // row bounds and counts as scalar loads: a vector load here would be waited for
+  // with the entry ids and the query
+  const int64_t r0 = ld_const(a.q_off + b), r1 = ld_const(a.q_off + b + 1);
+  int64_t e_base = ld_const(a.ent_off + b);
+  const int64_t e_end = ld_const(a.ent_off + b + 1);
+  // both pairs in flight together (otherwise the entry range is requested only after
+  // the padding test below)
+  asm volatile("" ::"s"(r0), "s"(r1), "s"(e_base), "s"(e_end));
+  const int64_t nq = r1 - r0;
+  int64_t n_seq = e_end - e_base;
   if (qi >= nq) {   // a padding row slot: nothing for the combine either
     if (s == 0 && threadIdx.x == 0 && a.part_info) a.part_info[gy] = make_int2(-1, 0);
     return;
@@ -472,11 +478,11 @@ __global__ __launch_bounds__(AT_NT) void attn_dma_kernel(AttnBatch ab) {
     return;
   const int64_t row = r0 + qi;
   // the row's entry count: only needed after the first DMAs are issued
-  int n_raw = sparse ? a.count[row] : (int)min(a.q_pos[row] / a.ratio, (int64_t)INT32_MAX);
+  int n_raw = sparse ? ld_const(a.count + row) : (int)min(ld_const(a.q_pos + row) / a.ratio, (int64_t)INT32_MAX);
   if (MODE == 0 && a.win_pos0 != nullptr) {
     // sliding window: the buffer's tokens at positions [p - window, p), as buffer
     // rows [lo, hi); the rows before lo are skipped by moving the sequence base
-    const int64_t p = a.q_pos[row], pos0 = a.win_pos0[b];
+    const int64_t p = ld_const(a.q_pos + row), pos0 = ld_const(a.win_pos0 + b);
     const int64_t lo = min(max(p - a.window, pos0) - pos0, max(n_seq, (int64_t)0));
     const int64_t hi = max(min(p, pos0 + n_seq) - pos0, lo);
     e_base += lo;

@@ -105,13 +105,6 @@ void ds_ws_carve(void* ws, int rows, int max_n, int k, DsLayer& L) {
 
 // the query row of this grid row, or false for a padding row (i beyond the sequence's
 // query count)
-// A value no kernel of the launch writes, read through the constant address space:
-// a scalar load for a uniform address, whose wait does not hold the in-order vector loads.
-template <class T>
-__device__ __forceinline__ T ld_const(const T* p) {
-  return *(const __attribute__((address_space(4))) T*)(size_t)p;
-}
-
 __device__ __forceinline__ bool ds_row(const int64_t* q_off, int max_q, int64_t& row, int& b) {
   b = blockIdx.y / max_q;
   const int i = blockIdx.y - b * max_q;

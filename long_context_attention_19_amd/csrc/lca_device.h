@@ -16,6 +16,13 @@ constexpr int KEY_BIAS = 1 << 20;        // indexer scores lie in [-2^20, 2^20]
 // the resource's byte range return zeros)
 constexpr int BUF_RSRC_WORD3 = 0x00020000;
 constexpr int BUF_NT = 2;                  // cache-policy bit of a buffer load: nontemporal
+
+// A value no kernel of the launch writes, read through the constant address space: a
+// scalar load for a uniform address, whose wait does not hold the in-order vector loads.
+template <class T>
+__device__ __forceinline__ T ld_const(const T* p) {
+  return *(const __attribute__((address_space(4))) T*)(size_t)p;
+}
 constexpr int HIST_BINS = 2048;          // first radix level: key >> 10
 constexpr int FINE_BINS = 1024;          // second radix level: key & 1023
 

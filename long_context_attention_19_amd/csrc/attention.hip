@@ -545,9 +545,9 @@ __global__ __launch_bounds__(AT_NT) void attn_dma_kernel(AttnBatch ab) {
   // issue the DMA of the stage starting at entry tb into buffer buf; rows past
   // e_last repeat row e_last (cached, and masked in the softmax)
   auto row_id = [&](int r, int tb, int cbase, int e_last) __attribute__((always_inline)) {
-    const int e = min(tb + r, e_last);
-    const int id = (MODE != 0 && sparse) ? sm.ids[e - cbase] : e;
-    return (uint32_t)min(max(id, 0), id_max);
+    // sparse: the staged ids are clamped and run on past the chunk's end (load_ids)
+    if (MODE != 0 && sparse) return (uint32_t)sm.ids[tb + r - cbase];
+    return (uint32_t)min(max(min(tb + r, e_last), 0), id_max);
   };
   // Every row id of the stage is read first (LDS, one wait), then the DMAs are issued:
   // the DMA's inline assembly clobbers memory, so an id read placed after one would
@@ -586,16 +586,20 @@ __global__ __launch_bounds__(AT_NT) void attn_dma_kernel(AttnBatch ab) {
       }
     }
   };
-  // copy the entry ids [cbase, cend) to LDS (sparse form; nothing else in flight)
+  // copy the entry ids [cbase, cend) to LDS (sparse form; nothing else in flight),
+  // clamped to the sequence's rows (a padding id reads row 0, masked in the softmax),
+  // and the slots past cend repeat the last id: a stage's rows then need no clamp
   auto load_ids = [&](int cbase, int cend) __attribute__((always_inline)) {
     const int* src = a.idx + row * kk + cbase;
-    const int cnt = cend - cbase;
+    const int cnt = cend - cbase;   // >= 1
     int v[AT_IDS / AT_NT];
 #pragma unroll
     for (int u = 0; u < AT_IDS / AT_NT; ++u) {   // all loads in flight, then the stores
       const int j = t + AT_NT * u;
-      v[u] = j < cnt ? src[j] : 0;
+      v[u] = src[min(j, cnt - 1)];
     }
+#pragma unroll
+    for (int u = 0; u < AT_IDS / AT_NT; ++u) v[u] = min(max(v[u], 0), id_max);
     __syncthreads();   // the previous chunk's ids are no longer read
 #pragma unroll
     for (int u = 0; u < AT_IDS / AT_NT; ++u) sm.ids[t + AT_NT * u] = v[u];
@@ -681,21 +685,27 @@ __global__ __launch_bounds__(AT_NT) void attn_dma_kernel(AttnBatch ab) {
       issued = prologue(cbase, cend);
       cb0 = cbase;
     }
-    int buf = 0;
-    for (int j = 0; j < nst; ++j) {
-      const int ahead = issued - 1 - j;   // stages issued after stage j
-      if (NB > 3 && ahead >= 3) wait_vm<(NB > 3 ? 3 : 0) * DPS>();
-      else if (NB > 2 && ahead == 2) wait_vm<(NB > 2 ? 2 : 0) * DPS>();
-      else if (ahead == 1) wait_vm<DPS>();
-      else wait_vm<0>();
-      lds_barrier();
-      compute(buf, cbase + j * ST);
-      lds_barrier();
-      if (j + NB < nst) {
-        issue(buf, cbase + (j + NB) * ST, cbase, cend - 1);
-        issued = j + NB + 1;
+    // stage j uses buffer j % NB; unrolled by NB so that the buffer (and with it every
+    // LDS address of the stage) is a compile-time constant
+    for (int j0 = 0; j0 < nst; j0 += NB) {
+#pragma unroll
+      for (int buf = 0; buf < NB; ++buf) {
+        const int j = j0 + buf;
+        if (j < nst) {
+          const int ahead = issued - 1 - j;   // stages issued after stage j
+          if (NB > 3 && ahead >= 3) wait_vm<(NB > 3 ? 3 : 0) * DPS>();
+          else if (NB > 2 && ahead == 2) wait_vm<(NB > 2 ? 2 : 0) * DPS>();
+          else if (ahead == 1) wait_vm<DPS>();
+          else wait_vm<0>();
+          lds_barrier();
+          compute(buf, cbase + j * ST);
+          lds_barrier();
+          if (j + NB < nst) {
+            issue(buf, cbase + (j + NB) * ST, cbase, cend - 1);
+            issued = j + NB + 1;
+          }
+        }
       }
-      buf = buf + 1 == NB ? 0 : buf + 1;
     }
   }
   wait_vm<0>();   // stages fetched past the end

@@ -247,6 +247,44 @@ def test_index_select_bit_exact(name):
             assert np.all(I[r, len(ref):] == -1), (b, i)
 
 
+@pytest.mark.parametrize("name", ["random", "ties", "front_aligned", "front_opposed"])
+def test_index_select_full_rounds(name):
+    """csa_index_select on row tiles whose tokens all see the whole sequence (30,000
+    entries: the sweeps' rounds below every token's visible count run without visibility
+    tests), with random keys, heavy ties (k = 512), or the first 6144 keys aligned with
+    (every token's top k among them) or opposed to the queries.  Bit-exact against the
+    oracle's scores + top-k for every row."""
+    step(f"csa_index_select full rounds {name}")
+    g = rng(213, 0, ["random", "ties", "front_aligned", "front_opposed"].index(name))
+    N, nq, c = 30000, 32, 4
+    k = 512 if name == "ties" else 2048
+    if name == "ties":
+        kk = g.integers(-1, 2, (N, 64)).astype(np.int8)
+        qq = g.integers(-1, 2, (nq, 64)).astype(np.int8)
+    else:
+        kk = int8_uniform(g, (N, 64))
+        base = int8_uniform(g, (1, 64)).astype(np.int32)
+        qq = np.clip(base + g.integers(-8, 9, (nq, 64)), -127, 127).astype(np.int8)
+        if name != "random":   # the first 6144 entries (6 rounds) aligned with, or against, the queries
+            sgn = 1 if name == "front_aligned" else -1
+            kk[:6144] = np.clip(sgn * base + g.integers(-20, 21, (6144, 64)), -127, 127).astype(np.int8)
+    q_pos = [N * c + i for i in range(nq)]   # every entry visible to every token
+    idx = torch.full((nq, k), -5, dtype=torch.int32, device=DEV)
+    count = torch.full((nq,), -5, dtype=torch.int32, device=DEV)
+    n_vis = torch.full((nq,), -5, dtype=torch.int32, device=DEV)
+    lca.csa_index_select(i8_dev(qq), i64_dev([0, nq]), i64_dev(q_pos), i8_dev(kk), i64_dev([0, N]),
+                         1, nq, N, c, k, idx, count, n_vis)
+    torch.cuda.synchronize()
+    I, C, NV = idx.cpu().numpy(), count.cpu().numpy(), n_vis.cpu().numpy()
+    for r in range(nq):
+        sc = oracle.index_scores(qq[r], kk)
+        ref = oracle.topk_select(sc, N, k)
+        assert NV[r] == N and C[r] == k, r
+        assert np.array_equal(I[r], ref), r
+    if name == "front_aligned":   # every row's top k lie among the first 6144 keys
+        assert np.all(I < 6144)
+
+
 # ------------------------------------------------------------------ top-k
 def _topk_cases():
     g = rng(220, 0, 0)

@@ -53,7 +53,7 @@ constexpr int SL_NW = SL_NT / WAVE;
 constexpr int SL_ROWS = 16;                   // query tokens per work-group (MFMA N)
 constexpr int SL_BLOCK = 64;                  // entries per wave and round: 4 MFMA tiles
 constexpr int SL_STAGE_K = 2048;              // k up to this: rows are staged in LDS
-constexpr int SL_BIN_CAP = 256;              // threshold-bin entries per token, two-sweep path
+constexpr int SL_BIN_CAP = 448;              // threshold-bin entries per token, two-sweep path
 constexpr int SL_WT = 2 * SL_ROWS * (SL_NT / WAVE);   // wave totals, two round parities
 constexpr int SL_FRONT = SL_WT + SL_ROWS * SL_BIN_CAP;   // words ahead of the staged rows
 constexpr int SL_LDS = SL_FRONT + SL_ROWS * SL_STAGE_K;   // words; >= 16 x 2048 coarse bins
@@ -356,7 +356,7 @@ __device__ __forceinline__ void sl_collect_finalize(
     }
     const int32_t nsel = run;
     // the selected bin entries' indices, compacted in order into the list's front, then
-    // one per lane (nsel <= 256: up to four registers)
+    // one per lane (nsel <= SL_BIN_CAP: up to SL_BIN_CAP / 64 registers)
 #pragma unroll
     for (int u = 0; u < PB; ++u)
       if (sel[u]) bl[sel_ex[u]] = e[u] >> 10;

@@ -186,7 +186,7 @@ int32_t lca_csa_index_score_fp4(const uint8_t* q_fp4, const int64_t* q_off, cons
  * Prefill-sized batches (max_q >= 16): a work-group owns 16 query tokens of a
  * sequence and all its entries and recomputes the int8 scores (MFMA) in sweeps
  * over the keys: the coarse histogram, then (when every token's threshold bin
- * holds at most 256 entries) one sweep collecting the entries above and inside
+ * holds at most 448 entries) one sweep collecting the entries above and inside
  * that bin, resolved in LDS; otherwise the fine histogram of the threshold bin and
  * a third sweep placing the selection in index order.  No workspace.
  *   q_idx, q_off, q_pos, k_idx, ent_off, batch, max_q, max_entries, d_idx, c

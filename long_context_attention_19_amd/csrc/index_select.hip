@@ -223,8 +223,6 @@ __device__ __forceinline__ void sl_collect_finalize(
   sl_sweep<FP4>(kp, qv, N, nround, nfull, w, lane, [&](auto all, const int32_t (&sc)[4][4], int32_t rd, int32_t blk) __attribute__((always_inline)) {
     constexpr bool ALL = decltype(all)::value;
     uint32_t ba[4], bb[4];
-    int32_t ex[4];
-    int32_t wtot = 0;
     // entry e_lane + 16 u + r is visible when 16 u + r < vlim
     const int32_t e_lane = blk * SL_BLOCK + 4 * grp;
     const int32_t vlim = nv - e_lane;
@@ -239,16 +237,31 @@ __device__ __forceinline__ void sl_collect_finalize(
       }
       ba[u] = a;
       bb[u] = c & ~a;
-      const int32_t cnt = (int32_t)((__builtin_popcount(bb[u]) << 16) | __builtin_popcount(ba[u]));
-      const int32_t c1 = sl_partner16(cnt);
-      const int32_t pair = cnt + c1;
-      const int32_t x = (grp & 1) ? pair : cnt;
-      const int32_t lowpair = sl_partner32(pair);
-      ex[u] = wtot + ((grp & 2) ? x + lowpair : x) - cnt;
-      wtot += pair + lowpair;
     }
+    // List offsets within the wave: segment (tile u, lane group g) precedes (u, g') for
+    // g < g' and every segment of later tiles.  The lane's four tile counts are packed one
+    // byte each (at most 4); a butterfly over the token's 4 lanes (two lane swaps) gives
+    // every tile's total and the lane's count of lower groups at once, and the earlier
+    // tiles' totals are byte shifts of the totals: every byte stays below 64, no carries.
+    auto wave_offsets = [&](const uint32_t (&m)[4], uint32_t& off, uint32_t& wsum) __attribute__((always_inline)) {
+      uint32_t pk = __builtin_popcount(m[3]);
+      pk = (pk << 8) + __builtin_popcount(m[2]);
+      pk = (pk << 8) + __builtin_popcount(m[1]);
+      pk = (pk << 8) + __builtin_popcount(m[0]);
+      const uint32_t s16 = (uint32_t)sl_partner16((int32_t)pk);
+      const uint32_t t1 = pk + s16;
+      const uint32_t s32 = (uint32_t)sl_partner32((int32_t)t1);
+      const uint32_t tall = t1 + s32;                                   // tile totals
+      const uint32_t tp = (tall << 8) + (tall << 16) + (tall << 24);   // earlier tiles
+      off = ((grp & 1) ? s16 : 0u) + ((grp & 2) ? s32 : 0u) + tp;
+      wsum = (tp >> 24) + (tall >> 24);
+    };
+    uint32_t off_a, wsum_a, off_b = 0, wsum_b = 0;
+    wave_offsets(ba, off_a, wsum_a);
+    const bool any_b = (bb[0] | bb[1] | bb[2] | bb[3]) != 0;
+    if (__builtin_amdgcn_ballot_w64(any_b)) wave_offsets(bb, off_b, wsum_b);   // rare
     int32_t* wr = wt + (rd & 1) * (SL_ROWS * SL_NW) + n * SL_NW;
-    if (grp == 0) wr[w] = wtot;
+    if (grp == 0) wr[w] = (int32_t)(wsum_a | wsum_b << 16);
     sl_lds_barrier();
     int32_t pre = 0, tot = 0;
 #pragma unroll
@@ -258,33 +271,32 @@ __device__ __forceinline__ void sl_collect_finalize(
       tot += v;
     }
     // entries above bA: walk the lane's set bits (tile-major, so in entry order); the
-    // list position is the tile's base (four 16-bit bases in two words) plus the
-    // lane's earlier bits in the same tile
+    // list position is the tile's base plus the lane's earlier bits in the same tile.
+    // Tile bases, 16 bits each: tiles 0 and 2 in one word, 1 and 3 in the other.
     {
       const uint32_t mall = ba[0] | ba[1] << 4 | ba[2] << 8 | ba[3] << 12;
-      uint32_t bw[2];
-#pragma unroll
-      for (int h = 0; h < 2; ++h)
-        bw[h] = (uint32_t)(a_base + ((pre + ex[2 * h]) & 0xffff)) |
-                (uint32_t)(a_base + ((pre + ex[2 * h + 1]) & 0xffff)) << 16;
+      const uint32_t base = (uint32_t)(a_base + (pre & 0xffff));
+      const uint32_t base2 = base | base << 16;
+      const uint32_t bw02 = (off_a & 0x00ff00ffu) + base2, bw13 = ((off_a >> 8) & 0x00ff00ffu) + base2;
       uint32_t m = mall;
       while (m) {
         const int bit = __builtin_ctz(m);
         m &= m - 1;
-        const uint32_t word = (bit & 8) ? bw[1] : bw[0];
-        const int32_t pos = (int32_t)((word >> ((bit & 4) << 2)) & 0xffff) +
+        const uint32_t word = (bit & 4) ? bw13 : bw02;
+        const int32_t pos = (int32_t)((word >> ((bit & 8) << 1)) & 0xffff) +
                             __builtin_popcount(__builtin_amdgcn_ubfe(mall, bit & 12, bit & 3));
         if (pos < SL_STAGE_K) alist[n * SL_STAGE_K + pos] = e_lane + (bit & 12) * 4 + (bit & 3);
       }
     }
     // entries inside bA (rare: one branch for the wave when there are none)
-    if (bb[0] | bb[1] | bb[2] | bb[3]) {
+    if (any_b) {
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           if (bb[u] >> r & 1) {
-            const int32_t pos = b_base + ((pre + ex[u]) >> 16) + __builtin_popcount(bb[u] & ((1u << r) - 1));
+            const int32_t pos = b_base + (pre >> 16) + (int32_t)((off_b >> (8 * u)) & 0xff) +
+                                __builtin_popcount(bb[u] & ((1u << r) - 1));
             if (pos < SL_BIN_CAP)
               blist[n * SL_BIN_CAP + pos] = ((e_lane + 16 * u + r) << 10) | (score_key(sc[u][r]) & 1023);
           }

@@ -1,8 +1,8 @@
 """csa_index_select_noalloc (the library's own per-device scratch as the workspace)
 against csa_index_select with a caller workspace: bit-exact idx, count and n_vis, on
-two calls in a row, the second with a smaller batch, fewer entries and a smaller k,
-so that whatever the first call left in the scratch must not reach the second's
-result."""
+calls in a row, the second with a smaller batch, fewer entries and a smaller k, so that
+whatever the first call left in the scratch must not reach the second's result, and a
+third in the prefill form (16 or more query rows per sequence, no workspace)."""
 import numpy as np
 import pytest
 import torch
@@ -34,7 +34,8 @@ def test_noalloc_matches_workspace_form():
     g = rng(700, 0, 0)
     c = 4
     calls = [([120000, 70001, 0, 5000, 2049, 300000], [2, 1, 1, 3, 1, 2], 2048),
-             ([9000, 2100], [1, 1], 256)]
+             ([9000, 2100], [1, 1], 256),
+             ([30000, 7000], [20, 33], 512)]   # the prefill form (16 or more query rows)
     for n_call, (Ns, nq, k) in enumerate(calls):
         kk, qq, q_pos = _case(g, Ns, nq, c)
         B, max_q, max_n = len(Ns), max(nq), max(max(Ns), 1)

@@ -125,8 +125,11 @@ std::vector<std::vector<int>> attn_groups(const lca_layer* layers, int n_layers)
   return groups;
 }
 
+// A CSA layer of the hybrid step: the selection's workspace, the selected ids by grid
+// row (read by the attention launch before it knows the row), the attention partials.
 size_t csa_layer_bytes(int rows, int max_entries, int topk, int heads, int splits) {
-  return lca::ds_ws_bytes(rows, max_entries, topk) + lca::attn_ws_bytes(rows, heads, splits);
+  return lca::ds_ws_bytes(rows, max_entries, topk) + lca::align256((size_t)rows * topk * 4) +
+         lca::attn_ws_bytes(rows, heads, splits);
 }
 
 }  // namespace
@@ -643,9 +646,12 @@ int32_t lca_hybrid_layer_step(const lca_layer* layers, int32_t n_layers, const i
       d.k = L.topk;
       lca::ds_ws_carve(p, rows, L.max_entries, L.topk, d);
       p += lca::ds_ws_bytes(rows, L.max_entries, L.topk);
+      d.idx_gy = reinterpret_cast<int32_t*>(p);
+      p += lca::align256((size_t)rows * L.topk * 4);
       il.push_back(d);
       il_fp4.push_back(L.idx_format == LCA_IDX_FP4 ? 1 : 0);
       a.idx = L.idx;
+      a.idx_gy = d.idx_gy;
       a.count = L.count;
       a.k = L.topk;
       a.max_n = piece * sp;   // every row's piece: ceil(max_n / splits) = piece

@@ -440,6 +440,25 @@ __global__ __launch_bounds__(AT_NT) void attn_dma_kernel(AttnBatch ab) {
   if (s >= a.splits) return;                     // a layer with fewer pieces per row
   const bool sparse = MODE == 2 ? a.idx != nullptr : MODE == 1;   // uniform
   constexpr int ST = 32 * ES * SUB;             // entries per super-tile (stage)
+  constexpr int IPT = AT_IDS / AT_NT;           // entry ids per thread and chunk
+  const int t = threadIdx.x;
+  const int kk = a.k;
+  // the piece as far as it is known before the entry count: exact when the count is
+  // within the bound (always for the sparse form)
+  const int per_g = piece_size(0, a.max_n, a.splits, ST);
+  const int e0_g = s * per_g;
+  // Sparse rows whose ids are also stored by grid row: the first chunk of ids is
+  // requested now, before the row bounds (a row's ids by row would wait for them).
+  int idv[MODE != 0 ? IPT : 1];
+  const bool ids_gy = MODE != 0 && sparse && a.idx_gy != nullptr;   // uniform
+  if (ids_gy) {
+    const int cnt = min(min(e0_g + per_g, kk), e0_g + AT_IDS) - e0_g;
+    const int* src = a.idx_gy + (int64_t)gy * kk + e0_g;
+    if (cnt > 0) {
+#pragma unroll
+      for (int u = 0; u < IPT; ++u) idv[u] = src[min(t + AT_NT * u, cnt - 1)];
+    }
+  }
   constexpr int HG = 4 / ES;                    // head groups of 16 per work-group
   constexpr int NU = ST / 16;                   // DMA instructions per wave per matrix
   static_assert(NU >= 1 && NU <= 8 && AT_IDS % ST == 0, "stage size");
@@ -491,9 +510,7 @@ __global__ __launch_bounds__(AT_NT) void attn_dma_kernel(AttnBatch ab) {
   }
   const int max_n = a.max_n;
   const int splits = a.splits;
-  const int kk = a.k;
   const int h0 = (lz % ab.head_blocks) * 64;
-  const int t = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(t >> 6);
   const int lane = t & 63;
   const int hg = w % HG;
@@ -534,10 +551,8 @@ __global__ __launch_bounds__(AT_NT) void attn_dma_kernel(AttnBatch ab) {
   }
   constexpr uint32_t BUF_BYTES = ST * 256;
 
-  // the piece as far as it is known before the entry count: exact when the count is
-  // within the bound (always for the sparse form); its end is where reads stay valid
-  const int per_g = piece_size(0, max_n, splits, ST);
-  const int e0_g = s * per_g;
+  // the end of the piece as far as it is known before the entry count: where reads
+  // stay valid
   const int end_g = n_seq <= 0 ? e0_g   // an empty sequence: nothing to fetch
                     : sparse ? min(e0_g + per_g, kk)
                              : (int)min((int64_t)e0_g + per_g, (int64_t)id_max + 1);
@@ -589,21 +604,21 @@ __global__ __launch_bounds__(AT_NT) void attn_dma_kernel(AttnBatch ab) {
   // copy the entry ids [cbase, cend) to LDS (sparse form; nothing else in flight),
   // clamped to the sequence's rows (a padding id reads row 0, masked in the softmax),
   // and the slots past cend repeat the last id: a stage's rows then need no clamp
-  auto load_ids = [&](int cbase, int cend) __attribute__((always_inline)) {
-    const int* src = a.idx + row * kk + cbase;
-    const int cnt = cend - cbase;   // >= 1
-    int v[AT_IDS / AT_NT];
+  auto store_ids = [&](int (&v)[MODE != 0 ? IPT : 1]) __attribute__((always_inline)) {
 #pragma unroll
-    for (int u = 0; u < AT_IDS / AT_NT; ++u) {   // all loads in flight, then the stores
-      const int j = t + AT_NT * u;
-      v[u] = src[min(j, cnt - 1)];
-    }
-#pragma unroll
-    for (int u = 0; u < AT_IDS / AT_NT; ++u) v[u] = min(max(v[u], 0), id_max);
+    for (int u = 0; u < IPT; ++u) v[u] = min(max(v[u], 0), id_max);
     __syncthreads();   // the previous chunk's ids are no longer read
 #pragma unroll
-    for (int u = 0; u < AT_IDS / AT_NT; ++u) sm.ids[t + AT_NT * u] = v[u];
+    for (int u = 0; u < IPT; ++u) sm.ids[t + AT_NT * u] = v[u];
     __syncthreads();
+  };
+  auto load_ids = [&](int cbase, int cend) __attribute__((always_inline)) {
+    const int* src = ids_gy ? a.idx_gy + (int64_t)gy * kk + cbase : a.idx + row * kk + cbase;
+    const int cnt = cend - cbase;   // >= 1
+    int v[MODE != 0 ? IPT : 1];
+#pragma unroll
+    for (int u = 0; u < IPT; ++u) v[u] = src[min(t + AT_NT * u, cnt - 1)];   // all in flight
+    store_ids(v);
   };
   // first stages of a chunk, one per buffer; returns the number issued
   auto prologue = [&](int cbase, int cend) __attribute__((always_inline)) {
@@ -619,7 +634,10 @@ __global__ __launch_bounds__(AT_NT) void attn_dma_kernel(AttnBatch ab) {
   int cb0 = e0_g;
   const int cend0 = sparse ? min(end_g, e0_g + AT_IDS) : end_g;
   if (cend0 > e0_g) {
-    if (MODE != 0 && sparse) load_ids(e0_g, cend0);
+    if (MODE != 0 && sparse) {
+      if (ids_gy) store_ids(idv);   // requested at the start
+      else load_ids(e0_g, cend0);
+    }
     issued = prologue(e0_g, cend0);
   }
   // the query is needed now: the compiler's wait for it lands here, behind the DMAs
@@ -789,7 +807,7 @@ __global__ __launch_bounds__(AT_NT) void attn_dma_kernel(AttnBatch ab) {
     }
     if (a.lse && g == 0) a.lse[row * a.heads + head] = lse_v;
   } else {
-    const int64_t slot = (row * a.splits + s) * a.heads + head;
+    const int64_t slot = ((int64_t)gy * a.splits + s) * a.heads + head;   // by grid row
     float* pp = a.part_o + slot * HD;
 #pragma unroll
     for (int db = 0; db < 8; ++db) *reinterpret_cast<f32x4*>(pp + db * 16 + 4 * g) = o[db];
@@ -798,12 +816,13 @@ __global__ __launch_bounds__(AT_NT) void attn_dma_kernel(AttnBatch ab) {
 }
 
 // Merge split partials: a work-group per (row slot, layer x head block, 8 heads), the
-// item numbering of the attention grid times the 8-head groups of a block.  The row and
-// its piece count come from the record the attention's piece-0 work-groups wrote (one
-// load).  Thread t takes head t / 32 of the group and dims 4 (t % 32) .. +3, and loads
-// the (max, sum) and O of CMB_U pieces at a time, all in flight together; the pieces
-// are added in piece order against a running maximum, so the result does not depend on
-// load timing.
+// item numbering of the attention grid times the 8-head groups of a block.  The
+// partials sit by grid row, so the first CMB_U pieces' loads go out beside the load of
+// the record the attention's piece-0 work-groups wrote (the row and its piece count);
+// pieces past the count are then masked out.  Thread t takes head t / 32 of the group
+// and dims 4 (t % 32) .. +3, and loads the (max, sum) and O of CMB_U pieces at a time,
+// all in flight together; the pieces are added in piece order against a running
+// maximum, so the result does not depend on load timing.
 constexpr int CMB_H = 8;    // heads per work-group
 constexpr int CMB_U = 8;    // pieces per round of loads
 __global__ __launch_bounds__(256) void attn_combine_kernel(AttnBatch ab, int groups) {
@@ -814,29 +833,37 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnBatch ab, int gro
   const int gy = item - lz * ab.rows_grid;
   const AttnArgs& a = ab.a[lz / ab.head_blocks];
   if (a.splits <= 1 || a.part_info == nullptr) return;
-  const int2 info = a.part_info[gy];
-  const int nsp = info.y;
-  if (nsp <= 1) return;
   const int t = threadIdx.x;
   const int head = (lz % ab.head_blocks) * 64 + hgrp * CMB_H + t / 32;
   const int d0 = (t % 32) * 4;
-  const int64_t row = info.x;
-  const int64_t base = row * a.splits * a.heads + head;
-  float mt = -INFINITY, lt = 0.f;
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  for (int j0 = 0; j0 < nsp; j0 += CMB_U) {
-    float2 ml[CMB_U];
-    f32x4 ov[CMB_U];
+  const int64_t base = (int64_t)gy * a.splits * a.heads + head;
+  float2 ml[CMB_U];
+  f32x4 ov[CMB_U];
+  // pieces j0 .. j0 + CMB_U - 1 of the launch's `splits` (a piece past the row's count
+  // holds whatever an earlier launch left: loaded, then masked)
+  auto fetch = [&](int j0) __attribute__((always_inline)) {
 #pragma unroll
     for (int u = 0; u < CMB_U; ++u) {
-      const int j = j0 + u;
-      const int64_t slot = base + (int64_t)(j < nsp ? j : j0) * a.heads;
+      const int64_t slot = base + (int64_t)min(j0 + u, a.splits - 1) * a.heads;
       ml[u] = a.part_ml[slot];
       ov[u] = *reinterpret_cast<const f32x4*>(a.part_o + slot * HD + d0);
     }
+  };
+  fetch(0);
+  const int2 info = a.part_info[gy];
+  const int nsp = info.y;
+  if (nsp <= 1) return;
+  const int64_t row = info.x;
+  float mt = -INFINITY, lt = 0.f;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  for (int j0 = 0; j0 < nsp; j0 += CMB_U) {
+    if (j0 > 0) fetch(j0);
 #pragma unroll
     for (int u = 0; u < CMB_U; ++u)
-      if (j0 + u >= nsp) ml[u] = make_float2(-INFINITY, 0.f);
+      if (j0 + u >= nsp) {
+        ml[u] = make_float2(-INFINITY, 0.f);
+        ov[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
     float mb = mt;   // piece j0 exists and holds an entry: mb is finite
 #pragma unroll
     for (int u = 0; u < CMB_U; ++u) mb = fmaxf(mb, ml[u].x);

@@ -20,7 +20,7 @@
 //                  int8 score, -64 * 128 * 127, has key 8192, the lowest FP4 score key
 //                  458752).  A group that drops entries records its cut bin.
 //   select launch  a work-group per row reads the row's slot regions with coalesced
-//                  loads into LDS; each thread then holds 29 consecutive slots in
+//                  loads into LDS; each thread then holds 9 consecutive slots in
 //                  registers (read at an odd stride, so a thread's run starts on its
 //                  own bank; longer rows in rounds) for the passes: the k-th largest
 //                  key T among the candidates from the two radix levels (2048 coarse
@@ -58,9 +58,9 @@ static_assert(DI_NT / 4 * DI_ROUNDS == DS_CHUNK, "int8 rounds cover the chunk");
 constexpr int DF_ROUNDS = DS_CHUNK / (DI_NW * 32);              // FP4: 32 keys per wave and round
 static_assert(DF_ROUNDS * DI_NW * 32 == DS_CHUNK, "FP4 rounds cover the chunk");
 constexpr int DS_VPT = DS_SEL_VPT;
-constexpr int DS_RC = DI_NT * DS_VPT;                            // slots per selection round
+constexpr int DS_RC = DS_SEL_NT * DS_VPT;                        // slots per selection round
 static_assert(DS_RC < (1 << 16), "a round's counts fit 16 bits");
-static_assert(DS_MAX_CHUNKS % DS_NT == 0, "cut marks per selection thread");
+static_assert(DS_MAX_CHUNKS % DS_SEL_NT == 0, "cut marks per selection thread");
 static_assert(DS_VPT <= DS_MIN_SLOT, "a thread's run of slots crosses at most one chunk boundary");
 static_assert(HIST_BINS % DI_NT == 0 && DS_CHUNK % DI_NT == 0, "bins and entries per thread");
 
@@ -227,11 +227,12 @@ __device__ __forceinline__ int32_t ds_score(const int8_t* kbase, int64_t j, cons
 
 // The exact selection over every visible entry's score, recomputed from the keys in
 // three sweeps (coarse histogram, fine histogram of the threshold bin, placement in
-// index order).  nv > k.  Writes k indices.
+// index order).  nv > k.  Writes k indices to irow (and to grow unless null).
 template <bool FP4>
 __device__ void ds_rescan(const int8_t* kbase, const uint32_t (&qd)[16], int64_t nv, int k,
-                          int32_t* irow, int32_t* s_hist, int32_t* s_scan, int32_t* s_b) {
-  constexpr int NT = DI_NT;
+                          int32_t* irow, int32_t* grow, int32_t* s_hist, int32_t* s_scan,
+                          int32_t* s_b) {
+  constexpr int NT = DS_SEL_NT;
   const int t = threadIdx.x;
   for (int i = t; i < HIST_BINS; i += NT) s_hist[i] = 0;
   __syncthreads();
@@ -260,7 +261,10 @@ __device__ void ds_rescan(const int8_t* kbase, const uint32_t (&qd)[16], int64_t
     const bool sel = key > T || (eq && eq_rank < need_eq);
     int32_t sel_n;
     const int32_t pos = sel_run + block_excl_scan<NT>(sel ? 1 : 0, s_scan, &sel_n);
-    if (sel && pos < k) irow[pos] = (int32_t)j;
+    if (sel && pos < k) {
+      irow[pos] = (int32_t)j;
+      if (grow) grow[pos] = (int32_t)j;
+    }
     eq_run += eq_n;
     sel_run += sel_n;
   }
@@ -280,11 +284,11 @@ struct DsSmemSelect {
   int32_t ent[DS_MC];                             // index order: key and entry
 };
 
-// The selection of one row from its candidates (all DI_NT threads of the work-group).
+// The selection of one row from its candidates (all DS_SEL_NT threads of the work-group).
 template <bool FP4>
 __device__ void ds_select_row(const DsLayer& L, int gy, DsSmemSelect& sm, int32_t* s_scan,
                               int32_t* s_b) {
-  constexpr int NT = DI_NT;
+  constexpr int NT = DS_SEL_NT;
   constexpr int VPT = DS_VPT;
   constexpr int RC = DS_RC;
   constexpr int DPT = DS_MAX_CHUNKS / NT;         // cut marks per thread
@@ -331,6 +335,7 @@ __device__ void ds_select_row(const DsLayer& L, int gy, DsSmemSelect& sm, int32_
   const int b = ri.z;
   if (t == 0) L.count[row] = k;
   int32_t* irow = L.idx + row * k;
+  int32_t* grow = L.idx_gy ? L.idx_gy + (int64_t)gy * k : nullptr;
   const int nch = (int)((nv + DS_CHUNK - 1) / DS_CHUNK);
   const DsBudget bud = ds_budget(nv, k);
   const int vs = nch * bud.slot;   // the row's candidate slots
@@ -430,7 +435,10 @@ __device__ void ds_select_row(const DsLayer& L, int gy, DsSmemSelect& sm, int32_
       const bool gt = key > T;
       const bool eq = key == T;
       const int pos = g + min(q, need_eq);
-      if ((gt || (eq && q < need_eq)) && pos < k) irow[pos] = sm.ent[i];
+      if ((gt || (eq && q < need_eq)) && pos < k) {
+        irow[pos] = sm.ent[i];
+        if (grow) grow[pos] = sm.ent[i];
+      }
       g += gt ? 1 : 0;
       q += eq ? 1 : 0;
     }
@@ -438,7 +446,7 @@ __device__ void ds_select_row(const DsLayer& L, int gy, DsSmemSelect& sm, int32_
     uint32_t qd[16];
     ds_query_words<FP4>(L.q_idx, row, qd);
     const int8_t* kbase = L.k_idx + L.ent_off[b] * (FP4 ? 32 : 64);
-    ds_rescan<FP4>(kbase, qd, nv, k, irow, sm.hist, s_scan, s_b);
+    ds_rescan<FP4>(kbase, qd, nv, k, irow, grow, sm.hist, s_scan, s_b);
   }
 }
 
@@ -494,7 +502,11 @@ __global__ __launch_bounds__(DI_NT) void ds_chunk_kernel(DsBatch db) {
   if (nv <= k) {   // every visible entry is selected: the first work-group writes the row
     if (blockIdx.x == 0) {
       int32_t* irow = L.idx + row * k;
-      for (int p = t; p < k; p += DI_NT) irow[p] = p < nv ? p : -1;
+      int32_t* grow = L.idx_gy ? L.idx_gy + (int64_t)blockIdx.y * k : nullptr;
+      for (int p = t; p < k; p += DI_NT) {
+        irow[p] = p < nv ? p : -1;
+        if (grow) grow[p] = p < nv ? p : -1;
+      }
       if (t == 0) L.count[row] = (int32_t)nv;
     }
     return;
@@ -616,9 +628,9 @@ __global__ __launch_bounds__(DI_NT) void ds_chunk_kernel(DsBatch db) {
 
 // The selection as a kernel of its own: one work-group per row, after the chunk launch.
 template <bool FP4>
-__global__ __launch_bounds__(DI_NT) void ds_select_kernel(DsBatch db) {
+__global__ __launch_bounds__(DS_SEL_NT) void ds_select_kernel(DsBatch db) {
   __shared__ DsSmemSelect sm;
-  __shared__ int32_t s_scan[DI_NW + 1];
+  __shared__ int32_t s_scan[DS_SEL_NT / WAVE + 1];
   __shared__ int32_t s_b[4];
   const DsLayer& L = db.layer[blockIdx.z];
   ds_select_row<FP4>(L, blockIdx.y, sm, s_scan, s_b);
@@ -638,8 +650,8 @@ hipError_t launch_ds_chunks(const DsBatch& db, int batch, hipStream_t st) {
 hipError_t launch_ds_select(const DsBatch& db, int batch, hipStream_t st) {
   if (batch == 0 || db.max_q == 0 || db.n == 0) return hipSuccess;
   dim3 grid(1u, (unsigned)(batch * db.max_q), (unsigned)db.n);
-  if (db.fp4) hipLaunchKernelGGL(ds_select_kernel<true>, grid, dim3(DI_NT), 0, st, db);
-  else hipLaunchKernelGGL(ds_select_kernel<false>, grid, dim3(DI_NT), 0, st, db);
+  if (db.fp4) hipLaunchKernelGGL(ds_select_kernel<true>, grid, dim3(DS_SEL_NT), 0, st, db);
+  else hipLaunchKernelGGL(ds_select_kernel<false>, grid, dim3(DS_SEL_NT), 0, st, db);
   return hipGetLastError();
 }
 

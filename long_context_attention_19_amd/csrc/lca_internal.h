@@ -70,11 +70,14 @@ hipError_t launch_index_select(const SelectArgs& a, int batch, hipStream_t st);
 // expected share of the top-k); a second launch picks each row's top-k from the
 // candidates, exactly, or rescans the row's keys when a chunk dropped an entry that
 // could belong to it.
-constexpr int DS_NT = 512;            // threads of a work-group
+constexpr int DS_NT = 512;            // threads of a chunk work-group
 constexpr int DS_CHUNK = 2048;        // entries per work-group
 constexpr int DS_MAX_CHUNKS = 2048;   // rows up to 4M entries
-constexpr int DS_SEL_VPT = 29;        // candidate slots per thread and selection round (odd:
-                                      // a thread's run of LDS words starts on its own bank)
+constexpr int DS_SEL_NT = 1024;       // threads of a selection work-group (one per row)
+constexpr int DS_SEL_VPT = 9;         // candidate slots per thread and selection round (odd:
+                                      // a thread's run of LDS words starts on its own bank);
+                                      // a round (9216 slots) holds a whole row up to 2^18
+                                      // entries at k 2048
 
 // A chunk's candidate budget for a row with nv > k visible entries.  E is the
 // chunk's expected share of the top-k, ceil(k * DS_CHUNK / nv); the chunk keeps the
@@ -114,6 +117,9 @@ struct DsLayer {
                          // chunk) of the kept entries in index order, then 0
   int32_t* idx;          // [rows][k] out
   int32_t* count;        // [rows] out
+  int32_t* idx_gy;       // null, or [batch * max_q][k] out: idx by grid row (for the
+                         // attention launch that follows, which reads it before it
+                         // knows the row)
   int64_t cand_slots;
   int32_t nch;           // chunk stride of dcut
   int32_t c;
@@ -180,6 +186,8 @@ struct AttnArgs {
   const int64_t* q_pos;    // dense only
   const int32_t* idx;      // sparse: [rows][k]; nullptr selects the dense form
   const int32_t* count;    // sparse
+  const int32_t* idx_gy;   // sparse, may be null: the same ids by grid row,
+                           // [batch * max_q][k], read before the row is known
   int32_t k;
   int32_t ratio;           // dense visibility ratio
   int32_t max_q;
@@ -189,8 +197,8 @@ struct AttnArgs {
   float scale_log2;        // scale * log2(e)
   uint16_t* out;
   float* lse;
-  float* part_o;           // [rows][splits][heads][128]
-  float2* part_ml;         // [rows][splits][heads]  (running max in log2 units, sum)
+  float* part_o;           // [batch * max_q][splits][heads][128] by grid row
+  float2* part_ml;         // [batch * max_q][splits][heads]  (running max in log2 units, sum)
   int2* part_info;         // [batch * max_q] per row slot: (query row or -1, pieces),
                            // written by the piece-0 work-groups for the combine
   // Sliding-window form (dense, win_pos0 != nullptr): kc / vc / ent_off describe the

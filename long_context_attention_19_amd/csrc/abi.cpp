@@ -676,7 +676,7 @@ int32_t lca_hybrid_layer_step(const lca_layer* layers, int32_t n_layers, const i
   // drain once instead of per kind.
   HybridTiming* ls = hybrid_timing();
   hipError_t e = hipSuccess;
-  const int hb = (heads + 63) / 64;
+  const int hb64 = (heads + 63) / 64;   // 64-head blocks
   const bool timing = ls && ls->timing;
   if (timing) {
     ls->has_csa = has_csa;
@@ -726,7 +726,8 @@ int32_t lca_hybrid_layer_step(const lca_layer* layers, int32_t n_layers, const i
     if (e != hipSuccess) break;
     lca::AttnBatch ab{};
     ab.n = (int)grp.size();
-    ab.head_blocks = hb;
+    ab.hpb = std::min(heads, 64);
+    ab.head_blocks = hb64;
     for (int i = 0; i < ab.n; ++i) ab.a[i] = args[grp[i]];
     e = lca::launch_attention(ab, batch, caller);
   }
@@ -744,7 +745,8 @@ int32_t lca_hybrid_layer_step(const lca_layer* layers, int32_t n_layers, const i
     const int n = (int)std::min<size_t>(lca::MAX_BATCH_LAYERS, win_a.size() - c0);
     lca::AttnBatch ab{};
     ab.n = n;
-    ab.head_blocks = hb;
+    ab.hpb = std::min(heads, 64);
+    ab.head_blocks = hb64;
     for (int i = 0; i < n; ++i) ab.a[i] = win_a[c0 + i];
     e = lca::launch_attention(ab, batch, caller);
   }

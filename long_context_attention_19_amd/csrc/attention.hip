@@ -510,7 +510,7 @@ __global__ __launch_bounds__(AT_NT) void attn_dma_kernel(AttnBatch ab) {
   }
   const int max_n = a.max_n;
   const int splits = a.splits;
-  const int h0 = (lz % ab.head_blocks) * 64;
+  const int h0 = (lz % ab.head_blocks) * ab.hpb;
   const int w = __builtin_amdgcn_readfirstlane(t >> 6);
   const int lane = t & 63;
   const int hg = w % HG;
@@ -816,15 +816,17 @@ __global__ __launch_bounds__(AT_NT) void attn_dma_kernel(AttnBatch ab) {
 }
 
 // Merge split partials: a work-group per (row slot, layer x head block, 8 heads), the
-// item numbering of the attention grid times the 8-head groups of a block.  The
-// partials sit by grid row, so the first CMB_U pieces' loads go out beside the load of
-// the record the attention's piece-0 work-groups wrote (the row and its piece count);
-// pieces past the count are then masked out.  Thread t takes head t / 32 of the group
-// and dims 4 (t % 32) .. +3, and loads the (max, sum) and O of CMB_U pieces at a time,
-// all in flight together; the pieces are added in piece order against a running
-// maximum, so the result does not depend on load timing.
+// item numbering of the attention grid times the 8-head groups of a block.  The row and
+// its piece count come from a record the attention's piece-0 work-groups wrote.  The
+// partials sit by grid row, so a sparse layer's pieces (as many as its launch has, up to
+// U; a full row has them all) are requested beside the record; a dense layer's rows
+// hold fewer pieces the shorter they are, so its pieces are requested once the count is
+// known.  Thread t takes head t / 32 of the group and dims 4 (t % 32) .. +3, and loads
+// the (max, sum) and O of U pieces at a time, all in flight together; the pieces are
+// added in piece order against a running maximum, so the result does not depend on
+// load timing.
 constexpr int CMB_H = 8;    // heads per work-group
-constexpr int CMB_U = 8;    // pieces per round of loads
+template <int U>
 __global__ __launch_bounds__(256) void attn_combine_kernel(AttnBatch ab, int groups) {
   const int item = blockIdx.x / groups;
   const int hgrp = blockIdx.x - item * groups;
@@ -834,44 +836,46 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnBatch ab, int gro
   const AttnArgs& a = ab.a[lz / ab.head_blocks];
   if (a.splits <= 1 || a.part_info == nullptr) return;
   const int t = threadIdx.x;
-  const int head = (lz % ab.head_blocks) * 64 + hgrp * CMB_H + t / 32;
+  const int head = (lz % ab.head_blocks) * ab.hpb + hgrp * CMB_H + t / 32;
   const int d0 = (t % 32) * 4;
   const int64_t base = (int64_t)gy * a.splits * a.heads + head;
-  float2 ml[CMB_U];
-  f32x4 ov[CMB_U];
-  // pieces j0 .. j0 + CMB_U - 1 of the launch's `splits` (a piece past the row's count
-  // holds whatever an earlier launch left: loaded, then masked)
-  auto fetch = [&](int j0) __attribute__((always_inline)) {
+  float2 ml[U];
+  f32x4 ov[U];
+  // pieces j0 .. j0 + U - 1, those below `lim` (past it: not loaded, masked below)
+  auto fetch = [&](int j0, int lim) __attribute__((always_inline)) {
 #pragma unroll
-    for (int u = 0; u < CMB_U; ++u) {
-      const int64_t slot = base + (int64_t)min(j0 + u, a.splits - 1) * a.heads;
-      ml[u] = a.part_ml[slot];
-      ov[u] = *reinterpret_cast<const f32x4*>(a.part_o + slot * HD + d0);
+    for (int u = 0; u < U; ++u) {
+      if (j0 + u < lim) {
+        const int64_t slot = base + (int64_t)(j0 + u) * a.heads;
+        ml[u] = a.part_ml[slot];
+        ov[u] = *reinterpret_cast<const f32x4*>(a.part_o + slot * HD + d0);
+      }
     }
   };
-  fetch(0);
+  const bool spec = a.idx != nullptr;   // uniform
+  if (spec) fetch(0, a.splits);
   const int2 info = a.part_info[gy];
   const int nsp = info.y;
   if (nsp <= 1) return;
   const int64_t row = info.x;
   float mt = -INFINITY, lt = 0.f;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  for (int j0 = 0; j0 < nsp; j0 += CMB_U) {
-    if (j0 > 0) fetch(j0);
+  for (int j0 = 0; j0 < nsp; j0 += U) {
+    if (j0 > 0 || !spec) fetch(j0, nsp);
 #pragma unroll
-    for (int u = 0; u < CMB_U; ++u)
-      if (j0 + u >= nsp) {
+    for (int u = 0; u < U; ++u)
+      if (j0 + u >= nsp) {   // a piece the row does not have
         ml[u] = make_float2(-INFINITY, 0.f);
         ov[u] = f32x4{0.f, 0.f, 0.f, 0.f};
       }
     float mb = mt;   // piece j0 exists and holds an entry: mb is finite
 #pragma unroll
-    for (int u = 0; u < CMB_U; ++u) mb = fmaxf(mb, ml[u].x);
+    for (int u = 0; u < U; ++u) mb = fmaxf(mb, ml[u].x);
     const float r = exp2f(mt - mb);   // 0 on the first round
     lt *= r;
     acc *= r;
 #pragma unroll
-    for (int u = 0; u < CMB_U; ++u) {
+    for (int u = 0; u < U; ++u) {
       const float f = exp2f(ml[u].x - mb);   // 0 for pieces past the end
       lt += ml[u].y * f;
       acc += ov[u] * f;
@@ -930,7 +934,7 @@ hipError_t launch_attention(const AttnBatch& ab_in, int batch, hipStream_t st) {
   int max_splits = 1;               // each layer has its own split count
   for (int l = 0; l < ab.n; ++l) max_splits = max(max_splits, ab.a[l].splits);
   if (max_splits > 65535) return hipErrorInvalidValue;
-  const int hg = min(a0.heads, 64) / 16;          // 1, 2 or 4
+  const int hg = ab.hpb / 16;                     // 1, 2 or 4
   const unsigned rows_grid = (unsigned)(batch * a0.max_q);
   const int64_t items = (int64_t)rows_grid * ab.n * ab.head_blocks;
   if (items >= INT32_MAX) return hipErrorInvalidValue;
@@ -962,10 +966,16 @@ hipError_t launch_attention(const AttnBatch& ab_in, int batch, hipStream_t st) {
 #undef LCA_ATTN_LAUNCH_KV
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || max_splits <= 1) return e;
-  const int groups = hg * 16 / CMB_H;   // 8-head groups of a 64-head block (or of 16 / 32 heads)
+  const int groups = ab.hpb / CMB_H;   // 8-head groups of a block of 16, 32 or 64 heads
   if ((int64_t)items * groups >= INT32_MAX) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(attn_combine_kernel, dim3((unsigned)(items * groups)), dim3(256), 0, st, ab,
-                     groups);
+  // rounds of 16 pieces for launches of sparse layers only with more than 8 pieces per
+  // row (one round for a 16-piece row), else of 8
+  if (mode == 1 && max_splits > 8)
+    hipLaunchKernelGGL(attn_combine_kernel<16>, dim3((unsigned)(items * groups)), dim3(256), 0, st,
+                       ab, groups);
+  else
+    hipLaunchKernelGGL(attn_combine_kernel<8>, dim3((unsigned)(items * groups)), dim3(256), 0, st,
+                       ab, groups);
   return hipGetLastError();
 }
 

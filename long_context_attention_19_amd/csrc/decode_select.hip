@@ -329,7 +329,10 @@ __device__ void ds_select_row(const DsLayer& L, int gy, DsSmemSelect& sm, int32_
   int32_t dc[DPT];
 #pragma unroll
   for (int e = 0; e < DPT; ++e) dc[e] = L.dcut[(int64_t)gy * L.nch + min(t + NT * e, L.nch - 1)];
-  const int4 ri = L.rinfo[gy];   // (row, nv, sequence) from the chunk launch
+  // (row, nv, sequence) from the chunk launch, as scalars: the passes below branch and
+  // size their loops on it
+  const int* rip = reinterpret_cast<const int*>(L.rinfo + gy);
+  const int4 ri = make_int4(ld_const(rip), ld_const(rip + 1), ld_const(rip + 2), 0);
   if (ri.x < 0 || ri.y <= k) return;   // padding, or written by the chunk launch
   const int64_t row = ri.x, nv = ri.y;
   const int b = ri.z;
@@ -513,6 +516,9 @@ __global__ __launch_bounds__(DI_NT) void ds_chunk_kernel(DsBatch db) {
   }
   if (base >= nv) return;
   const int tot = (int)min((int64_t)DS_CHUNK, nv - base);   // visible entries of the chunk
+  // the chunk's candidate budget (a 64-bit division and a square root: worked out while
+  // the keys are in flight, not after the scores)
+  const DsBudget bud = ds_budget(nv, k);
 
   // The query through the constant address space: scalar loads, whose wait does not
   // hold the (in-order) key loads issued above.  Each lane keeps its 16-byte piece.
@@ -579,7 +585,6 @@ __global__ __launch_bounds__(DI_NT) void ds_chunk_kernel(DsBatch db) {
   // would take the count past `slot` is left out (then fewer than target are kept).
   // Thread t owns bins 2047 - BPT t .. 2048 - BPT (t + 1), highest first.
   constexpr int BPT = HIST_BINS / DI_NT;
-  const DsBudget bud = ds_budget(nv, k);
   {
     int32_t hv[BPT];
     int32_t hs = 0;

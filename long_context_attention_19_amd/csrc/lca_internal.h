@@ -221,7 +221,8 @@ hipError_t launch_attn_sink(uint16_t* out, float* lse, const float* sink, int64_
                             hipStream_t st);
 struct AttnBatch {
   int32_t n;
-  int32_t head_blocks;     // ceil(heads / 64)
+  int32_t hpb;             // heads per block (one work-group's heads): 16, 32 or 64
+  int32_t head_blocks;     // heads / hpb
   int32_t rows_grid;       // batch * max_q (set at launch)
   int32_t items;           // rows_grid * n * head_blocks (set at launch)
   AttnArgs a[MAX_BATCH_LAYERS];
@@ -229,7 +230,8 @@ struct AttnBatch {
 inline AttnBatch attn_batch1(const AttnArgs& a) {
   AttnBatch b{};
   b.n = 1;
-  b.head_blocks = (a.heads + 63) / 64;
+  b.hpb = a.heads < 64 ? a.heads : 64;
+  b.head_blocks = a.heads / b.hpb;
   b.a[0] = a;
   return b;
 }

@@ -821,13 +821,14 @@ __global__ __launch_bounds__(AT_NT) void attn_dma_kernel(AttnBatch ab) {
 // partials sit by grid row, so a sparse layer's pieces (as many as its launch has, up to
 // U; a full row has them all) are requested beside the record; a dense layer's rows
 // hold fewer pieces the shorter they are, so its pieces are requested once the count is
-// known.  Thread t takes head t / 32 of the group and dims 4 (t % 32) .. +3, and loads
+// known.  A work-group takes H heads (8, or 2 when the launch has few rows, so that
+// its groups spread over more CUs: each group's loads are then a quarter as many).
+// Thread t takes head t / 32 of the group and dims 4 (t % 32) .. +3, and loads
 // the (max, sum) and O of U pieces at a time, all in flight together; the pieces are
 // added in piece order against a running maximum, so the result does not depend on
-// load timing.
-constexpr int CMB_H = 8;    // heads per work-group
-template <int U>
-__global__ __launch_bounds__(256) void attn_combine_kernel(AttnBatch ab, int groups) {
+// load timing, nor on H.
+template <int U, int H>
+__global__ __launch_bounds__(32 * H) void attn_combine_kernel(AttnBatch ab, int groups) {
   const int item = blockIdx.x / groups;
   const int hgrp = blockIdx.x - item * groups;
   if (item >= ab.items) return;
@@ -836,7 +837,7 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnBatch ab, int gro
   const AttnArgs& a = ab.a[lz / ab.head_blocks];
   if (a.splits <= 1 || a.part_info == nullptr) return;
   const int t = threadIdx.x;
-  const int head = (lz % ab.head_blocks) * ab.hpb + hgrp * CMB_H + t / 32;
+  const int head = (lz % ab.head_blocks) * ab.hpb + hgrp * H + t / 32;
   const int d0 = (t % 32) * 4;
   const int64_t base = (int64_t)gy * a.splits * a.heads + head;
   float2 ml[U];
@@ -966,16 +967,19 @@ hipError_t launch_attention(const AttnBatch& ab_in, int batch, hipStream_t st) {
 #undef LCA_ATTN_LAUNCH_KV
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || max_splits <= 1) return e;
-  const int groups = ab.hpb / CMB_H;   // 8-head groups of a block of 16, 32 or 64 heads
+  // 8-head groups of a block of 16, 32 or 64 heads; 2-head groups when 8-head ones
+  // would not give every CU a group
+  const bool narrow = items * (ab.hpb / 8) < 256;
+  const int groups = ab.hpb / (narrow ? 2 : 8);
   if ((int64_t)items * groups >= INT32_MAX) return hipErrorInvalidValue;
+  const dim3 cgrid((unsigned)(items * groups));
   // rounds of 16 pieces for launches of sparse layers only with more than 8 pieces per
   // row (one round for a 16-piece row), else of 8
-  if (mode == 1 && max_splits > 8)
-    hipLaunchKernelGGL(attn_combine_kernel<16>, dim3((unsigned)(items * groups)), dim3(256), 0, st,
-                       ab, groups);
-  else
-    hipLaunchKernelGGL(attn_combine_kernel<8>, dim3((unsigned)(items * groups)), dim3(256), 0, st,
-                       ab, groups);
+  const bool u16 = mode == 1 && max_splits > 8;
+  if (narrow && u16) hipLaunchKernelGGL((attn_combine_kernel<16, 2>), cgrid, dim3(64), 0, st, ab, groups);
+  else if (narrow) hipLaunchKernelGGL((attn_combine_kernel<8, 2>), cgrid, dim3(64), 0, st, ab, groups);
+  else if (u16) hipLaunchKernelGGL((attn_combine_kernel<16, 8>), cgrid, dim3(256), 0, st, ab, groups);
+  else hipLaunchKernelGGL((attn_combine_kernel<8, 8>), cgrid, dim3(256), 0, st, ab, groups);
   return hipGetLastError();
 }
 

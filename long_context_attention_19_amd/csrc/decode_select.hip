@@ -353,6 +353,8 @@ __device__ void ds_select_row(const DsLayer& L, int gy, DsSmemSelect& sm, int32_
   for (int e = 0; e < DPT; ++e) dm = max(dm, t + NT * e < nch ? dc[e] : 0);
   dm = wave_max(dm);
   for (int i = t; i < HIST_BINS; i += NT) sm.hist[i] = 0;
+  if (one)   // the fine histogram of a one-round row, in the (then unused) key list
+    for (int i = t; i < FINE_BINS; i += NT) sm.key[i] = 0;
   __syncthreads();
   if (lane == 0 && dm > 0) atomicMax(&s_b[2], dm);
   land();   // round 0, the speculative one
@@ -380,7 +382,52 @@ __device__ void ds_select_row(const DsLayer& L, int gy, DsSmemSelect& sm, int32_
   // bA or above may have been dropped.  Otherwise every one is a candidate.  (More
   // candidates in bin bA and above than the compacted lists hold: heavy ties.)
   const bool fast = n_cand >= k && dplus <= bA && m <= DS_MC;
-  if (fast) {
+  if (fast && one) {
+    // A row in one round: each thread's VPT slots stay in registers for the fine
+    // histogram of bin bA and for the placement (no compacted list).  Empty slots (0)
+    // and threads past the round hold keys below any threshold.
+    int32_t* fine = sm.key;
+    if (VPT * t < n_in) {
+#pragma unroll
+      for (int u = 0; u < VPT; ++u)
+        if ((int)(ck[u] >> 21) == bA && ck[u]) atomicAdd(&fine[(ck[u] >> 11) & 1023], 1);
+    }
+    __syncthreads();
+    int low_t, gt_in;
+    ds_threshold<NT, FINE_BINS>(fine, k - above, s_scan, s_b, low_t, gt_in);
+    const int T = (bA << 10) | low_t;
+    const int need_eq = k - above - gt_in;   // T-valued keys to keep, lowest indices first
+    int32_t ngt = 0, neq = 0;
+#pragma unroll
+    for (int u = 0; u < VPT; ++u) {
+      const int key = (int)(ck[u] >> 11);
+      ngt += key > T ? 1 : 0;
+      neq += key == T ? 1 : 0;
+    }
+    int32_t tot2;
+    const int32_t pre = block_excl_scan<NT>((ngt << 16) | neq, s_scan, &tot2);
+    if (ngt + neq) {
+      int32_t g = pre >> 16, q = pre & 0xffff;
+      // this thread's run of slots crosses at most one chunk boundary, at slot u_next
+      const int v0 = VPT * t;
+      const int ch0 = v0 / bud.slot;
+      const int u_next = (ch0 + 1) * bud.slot - v0;
+#pragma unroll
+      for (int u = 0; u < VPT; ++u) {
+        const int key = (int)(ck[u] >> 11);
+        const bool gt = key > T;
+        const bool eq = key == T;
+        const int pos = g + min(q, need_eq);
+        if ((gt || (eq && q < need_eq)) && pos < k) {
+          const int ent = (ch0 + (u >= u_next ? 1 : 0)) * DS_CHUNK + (int)(ck[u] & 2047);
+          irow[pos] = ent;
+          if (grow) grow[pos] = ent;
+        }
+        g += gt ? 1 : 0;
+        q += eq ? 1 : 0;
+      }
+    }
+  } else if (fast) {
     // the candidates at or above bin bA, compacted in index order as (key, entry)
     int32_t run = 0;
     for (int rd = 0; rd < nround; ++rd) {

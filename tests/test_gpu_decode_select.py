@@ -95,6 +95,20 @@ def test_decode_select_one_row_per_sequence_long():
     _run(Ns, nq, k, kk, qq, q_pos, tag="long")
 
 
+@pytest.mark.parametrize("k", [2048, 4096])
+def test_decode_select_multi_round(k):
+    """Rows whose candidate slots take more than one selection round (600,000 entries at
+    k 2048: 293 chunks of 49 slots; 262,144 entries at k 4096: 128 chunks of 92 slots),
+    which compact their candidates at or above the threshold bin, beside one-round rows
+    that keep their slots in registers, in one launch."""
+    g = rng(600, k, 2)
+    Ns, nq = [600000, 262144, 9000, 70001], [1, 2, 1, 1]
+    kk = int8_uniform(g, (sum(Ns), 64))
+    qq = int8_uniform(g, (sum(nq), 64))
+    q_pos = [Ns[0] * 4, Ns[1] * 4 + 1, 200000 * 4, Ns[2] * 4, Ns[3] * 4 + 3]
+    _run(Ns, nq, k, kk, qq, q_pos, tag=f"multi-round k={k}")
+
+
 @pytest.mark.parametrize("name", ["ties", "all_equal", "sorted", "bunched", "extreme", "k_one"])
 def test_decode_select_hard_cases(name):
     """Cases where chunks hold far more than their share of the top-k at or above the

@@ -60,6 +60,12 @@ constexpr int SL_LDS = SL_FRONT + SL_ROWS * SL_STAGE_K;   // words; >= 16 x 2048
 static_assert(SL_LDS >= SL_ROWS * HIST_BINS, "LDS region must hold the coarse histograms");
 static_assert(SL_LDS >= SL_ROWS * FINE_BINS + SL_ROWS, "fine histograms and their counts");
 static_assert(SL_NW <= SL_ROWS, "s_tot holds one value per wave");
+// Bitmap path: after the threshold-bin lists, one bit per entry for each token
+// (entries above the bin, then the bin's selected ones), in the rest of the region.
+constexpr int SL_BM_WORDS = (SL_LDS - SL_ROWS * SL_BIN_CAP) / SL_ROWS;   // per token
+constexpr int SL_BM_MAX = SL_BM_WORDS * 32;                               // entries
+static_assert(SL_BM_WORDS % 16 == 0, "a word index XOR a token (< 16) stays in the bitmap");
+static_assert(SL_ROWS * SL_BIN_CAP + SL_ROWS * SL_BM_WORDS <= SL_LDS, "bitmaps fit the region");
 
 // The value of lane l ^ 16 (l ^ 32): v_permlane16_swap (v_permlane32_swap) of a
 // register with itself returns the lane's own value and its partner's, ordered by
@@ -415,6 +421,160 @@ __device__ __forceinline__ void sl_collect_finalize(
   }
 }
 
+// Two-sweep path over a bitmap (every token of the group sees at most SL_BM_MAX entries):
+// the second sweep sets one bit per entry above each token's threshold bin bA, word
+// e / 32 of the token's bitmap (bA = -1: every visible entry), and appends the bin's
+// entries, unordered, to the token's list.  No order is kept during the sweep: a 64-entry
+// block belongs to one wave and one round, so its two words per token are written once,
+// with no barrier and no scan.  Then one wave per token resolves the threshold inside bA
+// (the bin's largest keys; of the keys equal to the threshold, the lowest indices), sets
+// those entries' bits, and writes the row by reading the bitmap in entry order.
+template <bool FP4>
+__device__ __forceinline__ void sl_bitmap_finalize(
+    __amdgpu_buffer_rsrc_t kp, const i32x4& qv, int32_t N, int32_t nround, int32_t nfull, int w,
+    int lane, int n, int grp, bool qok, int32_t nv, int32_t bA, int k, int nr, int32_t* sm,
+    const int32_t* s_above, int32_t* s_nb, const int32_t* s_nv, int32_t* __restrict__ idx0) {
+  int32_t* blist = sm;                                     // [16][SL_BIN_CAP] (index << 10 | key & 1023)
+  uint32_t* bm = reinterpret_cast<uint32_t*>(sm + SL_ROWS * SL_BIN_CAP);   // [16][SL_BM_WORDS]
+  // word i of token j sits at j * SL_BM_WORDS + (i ^ j): the 16 tokens' words of one block
+  // fall in different banks
+  const int32_t lim_a = sl_raw_limit(qok ? (bA + 1) << 10 : INT32_MAX);
+  const int32_t lim_b = sl_raw_limit(qok ? max(bA, 0) << 10 : INT32_MAX);
+  if (threadIdx.x < SL_ROWS) s_nb[threadIdx.x] = 0;
+  __syncthreads();
+  uint32_t* bmn = bm + n * SL_BM_WORDS;
+  int32_t* bln = blist + n * SL_BIN_CAP;
+  sl_sweep<FP4>(kp, qv, N, nround, nfull, w, lane, [&](auto all, const int32_t (&sc)[4][4], int32_t, int32_t blk) __attribute__((always_inline)) {
+    constexpr bool ALL = decltype(all)::value;
+    uint32_t ba[4], bb[4];
+    // entry e_lane + 16 u + r is visible when 16 u + r < vlim
+    const int32_t e_lane = blk * SL_BLOCK + 4 * grp;
+    const int32_t vlim = nv - e_lane;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      uint32_t a = 0, c = 0;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const bool vis = ALL || 16 * u + r < vlim;
+        a |= vis && sc[u][r] >= lim_a ? 1u << r : 0u;
+        c |= vis && sc[u][r] >= lim_b ? 1u << r : 0u;
+      }
+      ba[u] = a;
+      bb[u] = c & ~a;
+    }
+    // the block's two words of this lane's token: entry 16 u + 4 g + r of the block is bit
+    // (16 u + 4 g + r) % 32 of word (16 u + 4 g + r) / 32; the token's 4 lane groups OR
+    // their nibbles together with two lane swaps
+    const int sh = 4 * grp;
+    uint32_t w0 = (ba[0] << sh) | (ba[1] << (16 + sh));
+    uint32_t w1 = (ba[2] << sh) | (ba[3] << (16 + sh));
+    w0 |= (uint32_t)sl_partner16((int32_t)w0);
+    w1 |= (uint32_t)sl_partner16((int32_t)w1);
+    w0 |= (uint32_t)sl_partner32((int32_t)w0);
+    w1 |= (uint32_t)sl_partner32((int32_t)w1);
+    // (the sweep runs up to two rounds past the last block, whose words would lie past
+    // the bitmap: they hold no visible entry and are not stored)
+    if (grp == 0 && 2 * blk < SL_BM_WORDS) {
+      bmn[(2 * blk) ^ n] = w0;
+      bmn[(2 * blk + 1) ^ n] = w1;
+    }
+    // entries inside bA (a few per wave and round): appended in any order
+    if (__builtin_amdgcn_ballot_w64((bb[0] | bb[1] | bb[2] | bb[3]) != 0)) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const i32x4 su = {sc[u][0], sc[u][1], sc[u][2], sc[u][3]};
+        uint32_t m = bb[u];
+        while (m) {
+          const int r = __builtin_ctz(m);
+          m &= m - 1;
+          const int32_t pos = atomicAdd(&s_nb[n], 1);
+          if (pos < SL_BIN_CAP) bln[pos] = ((e_lane + 16 * u + r) << 10) | (score_key(su[r]) & 1023);
+        }
+      }
+    }
+  });
+  __syncthreads();
+  // one wave per token
+  for (int j = w; j < nr; j += SL_NW) {
+    const int32_t vj = s_nv[j];
+    uint32_t* bmj = bm + j * SL_BM_WORDS;
+    if (vj > k) {   // wave-uniform: the token has a threshold bin
+      const int32_t nb = min(s_nb[j], SL_BIN_CAP);
+      const int32_t need = k - s_above[j];   // keys to take from the bin, 1..nb
+      const int32_t* bl = blist + j * SL_BIN_CAP;
+      constexpr int PB = SL_BIN_CAP / WAVE;
+      int32_t e[PB], kl[PB];
+#pragma unroll
+      for (int u = 0; u < PB; ++u) {
+        const bool ok = lane + WAVE * u < nb;
+        e[u] = ok ? bl[lane + WAVE * u] >> 10 : 0;
+        kl[u] = ok ? (bl[lane + WAVE * u] & 1023) : -1;   // an empty slot takes no threshold
+      }
+      // the threshold t: the largest value with at least `need` low key bits >= t (a
+      // binary search over the 10 bits, counted by ballots)
+      auto count_ge = [&](int32_t v) __attribute__((always_inline)) {
+        int32_t c = 0;
+#pragma unroll
+        for (int u = 0; u < PB; ++u) c += __builtin_popcountll(__ballot(kl[u] >= v));
+        return c;
+      };
+      int32_t lo = 0, hi = 1023;
+      while (lo < hi) {
+        const int32_t mid = (lo + hi + 1) >> 1;
+        if (count_ge(mid) >= need) lo = mid; else hi = mid - 1;
+      }
+      const int32_t t = lo;
+      const int32_t quota = need - count_ge(t + 1);   // t-valued keys to take, lowest indices
+      int32_t n_eq = 0;
+#pragma unroll
+      for (int u = 0; u < PB; ++u) n_eq += __builtin_popcountll(__ballot(kl[u] == t));
+      // a t-valued entry's rank among the t-valued ones by index (the list is unordered):
+      // only needed when some of them are left out
+      int32_t rank[PB];
+#pragma unroll
+      for (int u = 0; u < PB; ++u) rank[u] = 0;
+      if (quota < n_eq) {
+#pragma unroll
+        for (int v = 0; v < PB; ++v) {
+          uint64_t eqb = __ballot(kl[v] == t);
+          while (eqb) {
+            const int l = __builtin_ctzll(eqb);
+            eqb &= eqb - 1;
+            const int32_t y = __builtin_amdgcn_readlane(e[v], l);
+#pragma unroll
+            for (int u = 0; u < PB; ++u) rank[u] += (kl[u] == t && y < e[u]) ? 1 : 0;
+          }
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < PB; ++u)
+        if (kl[u] > t || (kl[u] == t && rank[u] < quota))
+          atomicOr(&bmj[(e[u] >> 5) ^ j], 1u << (e[u] & 31));
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // the bits are in before the reads below
+    }
+    // the row: the set bits in entry order.  Lane l takes words [l * wpl, l * wpl + wpl).
+    const int32_t nw = (vj + 31) >> 5;
+    const int32_t wpl = (nw + WAVE - 1) / WAVE;
+    const int32_t w0 = min(lane * wpl, nw), w1 = min(w0 + wpl, nw);
+    int32_t cnt = 0;
+    for (int i = w0; i < w1; ++i) cnt += __builtin_popcount(bmj[i ^ j]);
+    const int32_t incl = wave_incl_scan(cnt);
+    const int32_t total = __shfl(incl, WAVE - 1, WAVE);
+    int32_t pos = incl - cnt;
+    int32_t* orow = idx0 + (int64_t)j * k;
+    for (int i = w0; i < w1; ++i) {
+      uint32_t x = bmj[i ^ j];
+      while (x) {
+        const int bit = __builtin_ctz(x);
+        x &= x - 1;
+        if (pos < k) orow[pos] = (i << 5) | bit;
+        ++pos;
+      }
+    }
+    for (int p = min(total, k) + lane; p < k; p += WAVE) orow[p] = -1;
+  }
+}
+
 template <bool STAGE, bool FP4>
 __global__ __launch_bounds__(SL_NT) void index_select_kernel(SelectArgs a, int tiles_per_seq) {
   __shared__ __attribute__((aligned(16))) int32_t sm[SL_LDS];
@@ -506,6 +666,12 @@ __global__ __launch_bounds__(SL_NT) void index_select_kernel(SelectArgs a, int t
     __syncthreads();
     if (t < nr && s_bin[t] >= 0 && sm[t * HIST_BINS + (s_bin[t] ^ t)] > SL_BIN_CAP) s_flag = 0;
     __syncthreads();
+    if (s_flag && nvmax <= SL_BM_MAX) {
+      if (t < nr) s_tot[t] = (int32_t)min(a.q_pos[r0 + q0 + t] / a.c, (int64_t)N);   // visible counts
+      sl_bitmap_finalize<FP4>(kp, qv, N, nround, nfull, w, lane, n, grp, qok, nv,
+                              thr ? s_bin[n] : -1, k, nr, sm, s_above, s_nb, s_tot, idx0);
+      return;
+    }
     if (s_flag) {
       sl_collect_finalize<FP4>(kp, qv, N, nround, nfull, w, lane, n, grp, qok, nv,
                                thr ? s_bin[n] : -1, k, nr, sm, s_tot, s_na, s_nb, idx0);

@@ -552,18 +552,18 @@ __device__ __forceinline__ void sl_bitmap_finalize(
           atomicOr(&bmj[(e[u] >> 5) ^ j], 1u << (e[u] & 31));
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // the bits are in before the reads below
     }
-    // the row: the set bits in entry order.  Lane l takes words [l * wpl, l * wpl + wpl).
+    // the row: the set bits in entry order, 64 words at a time (lane l takes word
+    // c0 + l), so the entries a round of stores writes lie close together in the row
     const int32_t nw = (vj + 31) >> 5;
-    const int32_t wpl = (nw + WAVE - 1) / WAVE;
-    const int32_t w0 = min(lane * wpl, nw), w1 = min(w0 + wpl, nw);
-    int32_t cnt = 0;
-    for (int i = w0; i < w1; ++i) cnt += __builtin_popcount(bmj[i ^ j]);
-    const int32_t incl = wave_incl_scan(cnt);
-    const int32_t total = __shfl(incl, WAVE - 1, WAVE);
-    int32_t pos = incl - cnt;
     int32_t* orow = idx0 + (int64_t)j * k;
-    for (int i = w0; i < w1; ++i) {
-      uint32_t x = bmj[i ^ j];
+    int32_t base = 0;
+    for (int32_t c0 = 0; c0 < nw; c0 += WAVE) {
+      const int32_t i = c0 + lane;
+      uint32_t x = i < nw ? bmj[i ^ j] : 0u;
+      const int32_t cnt = __builtin_popcount(x);
+      const int32_t incl = wave_incl_scan(cnt);
+      int32_t pos = base + incl - cnt;
+      base += __builtin_amdgcn_readlane(incl, WAVE - 1);
       while (x) {
         const int bit = __builtin_ctz(x);
         x &= x - 1;
@@ -571,7 +571,7 @@ __device__ __forceinline__ void sl_bitmap_finalize(
         ++pos;
       }
     }
-    for (int p = min(total, k) + lane; p < k; p += WAVE) orow[p] = -1;
+    for (int p = min(base, k) + lane; p < k; p += WAVE) orow[p] = -1;
   }
 }
 

@@ -610,14 +610,14 @@ __global__ __launch_bounds__(DI_NT) void ds_chunk_kernel(DsBatch db) {
     // brings elements 32 (l / 32) .. + 31), 32 keys as the columns of B; row 0 of
     // the product, register 0 of lanes 0..31, holds the 32 scores (exact in fp32)
     constexpr int FP4_E2M1 = 4;
-    constexpr int UNIT_SCALE = 127;   // E8M0 2^0
+    const int us = e8m0_unit_vgpr();   // the E8M0 unit scale, one VGPR
     const i32x8 qa = {qv[0], qv[1], qv[2], qv[3], 0, 0, 0, 0};
     const f32x16 zero16 = {};
 #pragma unroll
     for (int u = 0; u < DF_ROUNDS; ++u) {
       const i32x8 kb = {kv[u][0], kv[u][1], kv[u][2], kv[u][3], 0, 0, 0, 0};
       const f32x16 acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-          qa, kb, zero16, FP4_E2M1, FP4_E2M1, 0, UNIT_SCALE, 0, UNIT_SCALE);
+          qa, kb, zero16, FP4_E2M1, FP4_E2M1, 0, us, 0, us);
       if (piece == 0) {
         const int jl = u * (DI_NT / WAVE * 32) + w * 32 + (lane & 31);
         const int key = score_key((int32_t)(acc[0] * 256.0f));
@@ -625,6 +625,7 @@ __global__ __launch_bounds__(DI_NT) void ds_chunk_kernel(DsBatch db) {
         if (jl < tot) atomicAdd(&sm.lh[key >> 10], 1);
       }
     }
+    e8m0_keep(us);
   }
   __syncthreads();
 

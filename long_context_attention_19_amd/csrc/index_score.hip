@@ -169,7 +169,6 @@ template <bool HIST, int PASSES>
 __global__ __launch_bounds__(IF_NT) void index_score_fp4_kernel(IndexBatch ib) {
   constexpr int CHUNK = IF_KEYS_PER_PASS * PASSES;
   constexpr int FP4_E2M1 = 4;   // MFMA operand format code
-  constexpr int UNIT_SCALE = 127;   // E8M0 2^0
   __shared__ int32_t lh[HIST ? HIST_BINS : 1];
   __shared__ __attribute__((aligned(16))) int32_t s_sc[CHUNK];
   const IndexLayer& L = ib.layer[blockIdx.z];
@@ -209,6 +208,7 @@ __global__ __launch_bounds__(IF_NT) void index_score_fp4_kernel(IndexBatch ib) {
   const i32x4* kp = reinterpret_cast<const i32x4*>(k_fp4 + e0 * 32);   // 2 pieces per key
   int32_t* srow = scores + row * ld;
   const f32x16 zero16 = {};
+  const int us = e8m0_unit_vgpr();   // the E8M0 unit scale, one VGPR for the kernel
 
   for (int pass = 0; pass < PASSES; ++pass) {
     const int64_t pb = base + pass * IF_KEYS_PER_PASS;
@@ -223,7 +223,7 @@ __global__ __launch_bounds__(IF_NT) void index_score_fp4_kernel(IndexBatch ib) {
     for (int u = 0; u < IF_ROUNDS; ++u) {
       const i32x8 kb = {kv[u][0], kv[u][1], kv[u][2], kv[u][3], 0, 0, 0, 0};
       const f32x16 acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-          qa, kb, zero16, FP4_E2M1, FP4_E2M1, 0, UNIT_SCALE, 0, UNIT_SCALE);
+          qa, kb, zero16, FP4_E2M1, FP4_E2M1, 0, us, 0, us);
       if (half == 0) {   // row 0 of the product: lane kl holds key kl's score
         const int jl = pass * IF_KEYS_PER_PASS + u * (IF_NW * 32) + w * 32 + kl;
         const int64_t j = base + jl;
@@ -234,6 +234,7 @@ __global__ __launch_bounds__(IF_NT) void index_score_fp4_kernel(IndexBatch ib) {
       }
     }
   }
+  e8m0_keep(us);
   __syncthreads();
   {
     const int64_t cnt = min((int64_t)CHUNK, N - base);

@@ -113,16 +113,16 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 // unit, 256 x the E2M1 dot product).  The sweeps compare raw scores against limits mapped
 // from the 21-bit key space (sl_raw_limit); only the histograms form keys.
 template <bool FP4>
-__device__ __forceinline__ void sl_scores(const i32x4 (&kv)[4], const i32x4& qv, int32_t (&sc)[4][4]) {
+__device__ __forceinline__ void sl_scores(const i32x4 (&kv)[4], const i32x4& qv, int us, int32_t (&sc)[4][4]) {
   const i32x4 zero4 = {0, 0, 0, 0};
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
     if (FP4) {
-      constexpr int FP4_E2M1 = 4, UNIT_SCALE = 127;   // operand format code, E8M0 2^0
+      constexpr int FP4_E2M1 = 4;   // operand format code; `us` holds the E8M0 unit scale 2^0
       const i32x8 ka = {kv[u][0], kv[u][1], kv[u][2], kv[u][3], 0, 0, 0, 0};
       const i32x8 qb = {qv[0], qv[1], qv[2], qv[3], 0, 0, 0, 0};
       const f32x4_t acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-          ka, qb, f32x4_t{0.f, 0.f, 0.f, 0.f}, FP4_E2M1, FP4_E2M1, 0, UNIT_SCALE, 0, UNIT_SCALE);
+          ka, qb, f32x4_t{0.f, 0.f, 0.f, 0.f}, FP4_E2M1, FP4_E2M1, 0, us, 0, us);
 #pragma unroll
       for (int r = 0; r < 4; ++r) sc[u][r] = (int32_t)(acc[r] * 256.f);
     } else {
@@ -144,7 +144,7 @@ __device__ __forceinline__ int32_t sl_raw_limit(int32_t lim) {
 // `body` gets (ALL, scores, round, block), ALL an integral constant: true when every
 // entry of the round is visible to every token of the group (no per-entry test).
 template <bool FP4, bool ALL, class Body>
-__device__ __forceinline__ void sl_sweep_part(__amdgpu_buffer_rsrc_t kp, const i32x4& qv, int32_t N,
+__device__ __forceinline__ void sl_sweep_part(__amdgpu_buffer_rsrc_t kp, const i32x4& qv, int us, int32_t N,
                                               int32_t r0, int32_t r1, int w, int lane, Body& body) {
   i32x4 ka[4], kb[4], kc[4];
   int32_t sc[4][4];
@@ -157,13 +157,13 @@ __device__ __forceinline__ void sl_sweep_part(__amdgpu_buffer_rsrc_t kp, const i
   sl_load<FP4>(kb, kp, (r0 + 1) * SL_NW + wv, N, lane);
   for (int32_t rd = r0; rd < r1; rd += 3) {
     sl_load<FP4>(kc, kp, (rd + 2) * SL_NW + w, N, lane);
-    sl_scores<FP4>(ka, qv, sc);
+    sl_scores<FP4>(ka, qv, us, sc);
     body(all, sc, rd, rd * SL_NW + w);
     sl_load<FP4>(ka, kp, (rd + 3) * SL_NW + w, N, lane);
-    sl_scores<FP4>(kb, qv, sc);
+    sl_scores<FP4>(kb, qv, us, sc);
     body(all, sc, rd + 1, (rd + 1) * SL_NW + w);
     sl_load<FP4>(kb, kp, (rd + 4) * SL_NW + w, N, lane);
-    sl_scores<FP4>(kc, qv, sc);
+    sl_scores<FP4>(kc, qv, us, sc);
     body(all, sc, rd + 2, (rd + 2) * SL_NW + w);
   }
 }
@@ -173,11 +173,11 @@ __device__ __forceinline__ void sl_sweep_part(__amdgpu_buffer_rsrc_t kp, const i
 // wave runs every round (a block past the end has no visible entry), so bodies may hold
 // work-group barriers.
 template <bool FP4, class Body>
-__device__ __forceinline__ void sl_sweep(__amdgpu_buffer_rsrc_t kp, const i32x4& qv, int32_t N,
+__device__ __forceinline__ void sl_sweep(__amdgpu_buffer_rsrc_t kp, const i32x4& qv, int us, int32_t N,
                                          int32_t nround, int32_t nfull, int w, int lane, Body&& body) {
   const int32_t nf = min(nfull, nround) / 3 * 3;
-  if (nf > 0) sl_sweep_part<FP4, true>(kp, qv, N, 0, nf, w, lane, body);
-  if (nf < nround) sl_sweep_part<FP4, false>(kp, qv, N, nf, nround, w, lane, body);
+  if (nf > 0) sl_sweep_part<FP4, true>(kp, qv, us, N, 0, nf, w, lane, body);
+  if (nf < nround) sl_sweep_part<FP4, false>(kp, qv, us, N, nf, nround, w, lane, body);
 }
 
 // Threshold of one token's histogram (nbins bins, bin b at h[b ^ j]), by one wave:
@@ -214,7 +214,7 @@ __device__ __forceinline__ void sl_threshold(const int32_t* h, int j, int need, 
 // index.
 template <bool FP4>
 __device__ __forceinline__ void sl_collect_finalize(
-    __amdgpu_buffer_rsrc_t kp, const i32x4& qv, int32_t N, int32_t nround, int32_t nfull, int w,
+    __amdgpu_buffer_rsrc_t kp, const i32x4& qv, int us, int32_t N, int32_t nround, int32_t nfull, int w,
     int lane, int n, int grp, bool qok, int32_t nv, int32_t bA, int k, int nr, int32_t* sm,
     int32_t* s_tot, int32_t* s_na, int32_t* s_nb, int32_t* __restrict__ idx0) {
   int32_t* wt = sm;                                // [2][16][waves] wave totals
@@ -226,7 +226,7 @@ __device__ __forceinline__ void sl_collect_finalize(
   const int32_t lim_a = sl_raw_limit(qok ? (bA + 1) << 10 : INT32_MAX);
   const int32_t lim_b = sl_raw_limit(qok ? max(bA, 0) << 10 : INT32_MAX);
   __syncthreads();
-  sl_sweep<FP4>(kp, qv, N, nround, nfull, w, lane, [&](auto all, const int32_t (&sc)[4][4], int32_t rd, int32_t blk) __attribute__((always_inline)) {
+  sl_sweep<FP4>(kp, qv, us, N, nround, nfull, w, lane, [&](auto all, const int32_t (&sc)[4][4], int32_t rd, int32_t blk) __attribute__((always_inline)) {
     constexpr bool ALL = decltype(all)::value;
     uint32_t ba[4], bb[4];
     // entry e_lane + 16 u + r is visible when 16 u + r < vlim
@@ -431,7 +431,7 @@ __device__ __forceinline__ void sl_collect_finalize(
 // those entries' bits, and writes the row by reading the bitmap in entry order.
 template <bool FP4>
 __device__ __forceinline__ void sl_bitmap_finalize(
-    __amdgpu_buffer_rsrc_t kp, const i32x4& qv, int32_t N, int32_t nround, int32_t nfull, int w,
+    __amdgpu_buffer_rsrc_t kp, const i32x4& qv, int us, int32_t N, int32_t nround, int32_t nfull, int w,
     int lane, int n, int grp, bool qok, int32_t nv, int32_t bA, int k, int nr, int32_t* sm,
     const int32_t* s_above, int32_t* s_nb, const int32_t* s_nv, int32_t* __restrict__ idx0) {
   int32_t* blist = sm;                                     // [16][SL_BIN_CAP] (index << 10 | key & 1023)
@@ -444,7 +444,7 @@ __device__ __forceinline__ void sl_bitmap_finalize(
   __syncthreads();
   uint32_t* bmn = bm + n * SL_BM_WORDS;
   int32_t* bln = blist + n * SL_BIN_CAP;
-  sl_sweep<FP4>(kp, qv, N, nround, nfull, w, lane, [&](auto all, const int32_t (&sc)[4][4], int32_t, int32_t blk) __attribute__((always_inline)) {
+  sl_sweep<FP4>(kp, qv, us, N, nround, nfull, w, lane, [&](auto all, const int32_t (&sc)[4][4], int32_t, int32_t blk) __attribute__((always_inline)) {
     constexpr bool ALL = decltype(all)::value;
     uint32_t ba[4], bb[4];
     // entry e_lane + 16 u + r is visible when 16 u + r < vlim
@@ -637,13 +637,15 @@ __global__ __launch_bounds__(SL_NT) void index_select_kernel(SelectArgs a, int t
   const i32x4 zero4 = {0, 0, 0, 0};
   const i32x4 qv = qok && 16 * grp < VB ? *reinterpret_cast<const i32x4*>(a.q_idx + row * VB + 16 * grp)
                                         : zero4;
+  // The E8M0 unit scale of the FP4 MFMAs in one VGPR for the whole kernel (e8m0_unit_vgpr).
+  const int us = FP4 ? e8m0_unit_vgpr() : 127;
 
   if (nvmax > 0 && any_thr) {
     // ---- sweep 1: coarse histograms
     for (int i = t; i < SL_ROWS * HIST_BINS; i += SL_NT) sm[i] = 0;
     __syncthreads();
     int32_t* hc = sm + n * HIST_BINS;
-    sl_sweep<FP4>(kp, qv, N, nround, nfull, w, lane, [&](auto all, const int32_t (&sc)[4][4], int32_t, int32_t blk) __attribute__((always_inline)) {
+    sl_sweep<FP4>(kp, qv, us, N, nround, nfull, w, lane, [&](auto all, const int32_t (&sc)[4][4], int32_t, int32_t blk) __attribute__((always_inline)) {
       constexpr bool ALL = decltype(all)::value;
       const int32_t vlim = nv - (blk * SL_BLOCK + 4 * grp);   // visible: 16 u + r < vlim
 #pragma unroll
@@ -668,13 +670,15 @@ __global__ __launch_bounds__(SL_NT) void index_select_kernel(SelectArgs a, int t
     __syncthreads();
     if (s_flag && nvmax <= SL_BM_MAX) {
       if (t < nr) s_tot[t] = (int32_t)min(a.q_pos[r0 + q0 + t] / a.c, (int64_t)N);   // visible counts
-      sl_bitmap_finalize<FP4>(kp, qv, N, nround, nfull, w, lane, n, grp, qok, nv,
+      sl_bitmap_finalize<FP4>(kp, qv, us, N, nround, nfull, w, lane, n, grp, qok, nv,
                               thr ? s_bin[n] : -1, k, nr, sm, s_above, s_nb, s_tot, idx0);
+      e8m0_keep(us);
       return;
     }
     if (s_flag) {
-      sl_collect_finalize<FP4>(kp, qv, N, nround, nfull, w, lane, n, grp, qok, nv,
+      sl_collect_finalize<FP4>(kp, qv, us, N, nround, nfull, w, lane, n, grp, qok, nv,
                                thr ? s_bin[n] : -1, k, nr, sm, s_tot, s_na, s_nb, idx0);
+      e8m0_keep(us);
       return;
     }
     // ---- sweep 2: fine histograms of the threshold bins
@@ -682,7 +686,7 @@ __global__ __launch_bounds__(SL_NT) void index_select_kernel(SelectArgs a, int t
     for (int i = t; i < SL_ROWS * FINE_BINS; i += SL_NT) sm[i] = 0;
     __syncthreads();
     int32_t* hf = sm + n * FINE_BINS;
-    sl_sweep<FP4>(kp, qv, N, nround, nfull, w, lane, [&](auto all, const int32_t (&sc)[4][4], int32_t, int32_t blk) __attribute__((always_inline)) {
+    sl_sweep<FP4>(kp, qv, us, N, nround, nfull, w, lane, [&](auto all, const int32_t (&sc)[4][4], int32_t, int32_t blk) __attribute__((always_inline)) {
       constexpr bool ALL = decltype(all)::value;
       const int32_t vlim = nv - (blk * SL_BLOCK + 4 * grp);   // visible: 16 u + r < vlim
 #pragma unroll
@@ -728,7 +732,7 @@ __global__ __launch_bounds__(SL_NT) void index_select_kernel(SelectArgs a, int t
     // token without a threshold keeps every visible entry); a lane without a token takes none
     const int32_t lim_a = sl_raw_limit(!qok ? INT32_MAX : thr ? T + 1 : 0);
     const int32_t lim_e = sl_raw_limit(!qok ? INT32_MAX : thr ? T : 0);
-    sl_sweep<FP4>(kp, qv, N, nround, nfull, w, lane, [&](auto all, const int32_t (&sc)[4][4], int32_t rd, int32_t blk) __attribute__((always_inline)) {
+    sl_sweep<FP4>(kp, qv, us, N, nround, nfull, w, lane, [&](auto all, const int32_t (&sc)[4][4], int32_t rd, int32_t blk) __attribute__((always_inline)) {
       constexpr bool ALL = decltype(all)::value;
       // Counts are packed (T-valued << 16 | above); a round adds at most 1024 to
       // either half.  Within the wave, segment (tile u, lane group g) precedes
@@ -818,6 +822,7 @@ __global__ __launch_bounds__(SL_NT) void index_select_kernel(SelectArgs a, int t
       if (p >= min(vj, k)) idx0[i] = -1;
     }
   }
+  e8m0_keep(us);
 }
 
 hipError_t launch_index_select(const SelectArgs& a, int batch, hipStream_t st) {

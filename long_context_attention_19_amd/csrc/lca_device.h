@@ -59,6 +59,19 @@ __device__ __forceinline__ uint32_t f64_to_bf16_bits(double x) {
   return __float_as_uint((float)__longlong_as_double((long long)u)) >> 16;   // >= 2^128 -> inf
 }
 
+// The E8M0 unit scale (2^0, code 127) of the scaled (FP4) MFMAs, held in one VGPR that a
+// kernel defines once and keeps to its end (e8m0_keep after its last MFMA).  Left to the
+// compiler, the constant is rematerialised into a short-lived VGPR that the very next VALU
+// instruction may overwrite while the multi-pass MFMA reading it as its scale is still in
+// flight; rows of huge scores were seen with such code.  An asm definition cannot be
+// rematerialised, and while it is live no other value is allocated to it.
+__device__ __forceinline__ int e8m0_unit_vgpr() {
+  int s;
+  asm volatile("v_mov_b32 %0, 127" : "=v"(s));
+  return s;
+}
+__device__ __forceinline__ void e8m0_keep(int s) { asm volatile("" ::"v"(s)); }
+
 // ---------------------------------------------------------------- scans
 
 // Inclusive prefix sum over the 64 lanes of a wave with DPP: a Hillis-Steele scan

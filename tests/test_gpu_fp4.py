@@ -94,9 +94,11 @@ def test_index_score_fp4_extremes():
 
 
 def _select_fp4_case(name):
-    g = rng(325, ["ragged", "prefill_tile", "k_large", "ties", "extremes"].index(name), 0)
+    g = rng(325, ["ragged", "prefill_tile", "k_large", "ties", "extremes", "long"].index(name), 0)
     if name == "ragged":          # an empty sequence, one shorter than k, rows at position 0
         Ns, nq, k = [3000, 0, 70, 20000], [16, 20, 17, 40], 256
+    elif name == "long":          # tokens seeing more than 66,560 entries: the ordered lists
+        Ns, nq, k = [90000], [20], 2048
     elif name == "prefill_tile":  # the prefill shape: 66,560 entries, several row tiles
         Ns, nq, k = [66560], [64], 2048
     elif name == "k_large":       # k above the LDS-staged rows: rows written in place
@@ -113,7 +115,7 @@ def _select_fp4_case(name):
     return Ns, nq, k, kk, qq
 
 
-@pytest.mark.parametrize("name", ["ragged", "prefill_tile", "k_large", "ties", "extremes"])
+@pytest.mark.parametrize("name", ["ragged", "prefill_tile", "k_large", "ties", "extremes", "long"])
 def test_index_select_fp4_bit_exact(name):
     """csa_index_select_fp4 (scores never written) against the oracle's FP4 scores and
     top-k."""

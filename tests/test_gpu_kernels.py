@@ -172,7 +172,7 @@ def test_index_score_gemm_bit_exact(fused, case):
 def _select_case(name):
     """(Ns, nq, k, k_idx, q_idx) for csa_index_select: 16+ query tokens per sequence."""
     g = rng(212, 0, ["ragged", "ties", "all_equal", "extreme", "k_large", "k_one",
-                     "tiles"].index(name))
+                     "tiles", "long"].index(name))
     if name == "ragged":
         Ns, nq, k = [3000, 10001, 0, 700, 64], [16, 37, 5, 50, 17], 256
         kk = int8_uniform(g, (sum(Ns), 64))
@@ -204,6 +204,10 @@ def _select_case(name):
         Ns, nq, k = [5000, 300], [16, 33], 1
         kk = int8_uniform(g, (sum(Ns), 64))
         qq = int8_uniform(g, (sum(nq), 64))
+    elif name == "long":   # tokens seeing more than 66,560 entries: the ordered-list collection
+        Ns, nq, k = [90000], [20], 2048
+        kk = int8_uniform(g, (sum(Ns), 64))
+        qq = int8_uniform(g, (sum(nq), 64))
     else:   # "tiles": several row tiles of one sequence, k = 2048
         Ns, nq, k = [20000], [64], 2048
         kk = int8_uniform(g, (sum(Ns), 64))
@@ -212,7 +216,7 @@ def _select_case(name):
 
 
 @pytest.mark.parametrize("name", ["ragged", "ties", "all_equal", "extreme", "k_large", "k_one",
-                                  "tiles"])
+                                  "tiles", "long"])
 def test_index_select_bit_exact(name):
     """csa_index_select (scores never written) against the oracle's scores + top-k."""
     step(f"csa_index_select {name}")
